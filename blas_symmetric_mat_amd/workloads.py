@@ -1,0 +1,253 @@
+"""Seeded synthetic inputs for y := alpha*S*x + beta*y.
+
+This module only draws numbers and lays them out; it holds none of the
+product's arithmetic.  Both the GPU path's tests/benchmark and the CPU
+oracle take their inputs from here, so the two always see the same data.
+
+Layout (the BLAS layout of the CUDA-xSYMV report, §2.2 Fig. 5): A is a flat
+column-major array of ``lda * n`` elements, element (i, j) at ``i + j*lda``.
+Only the stored triangle (``uplo``) is drawn; the other strict triangle and
+the padding rows ``n .. lda-1`` are filled with NaN, so that any read of them
+would show in the result.
+
+Element storage per precision code:
+  's' float32, 'd' float64, 'c' complex64, 'z' complex128 (interleaved re, im),
+  'w' double-double: float64 array with a trailing axis of 2 holding (hi, lo).
+
+Drawing order for one problem, from ``numpy.random.Generator(PCG64(seed))``:
+  1. the stored triangle, column by column (column-major), top to bottom;
+  2. x (n values); 3. y (n values);
+  4. Hermitian problems with diagonal garbage: n values that overwrite the
+     imaginary words of the diagonal.
+A complex value takes two consecutive draws (re, im).  A double-double value
+takes two consecutive draws (r, r') and is hi = 2r-1, lo = hi*(2r'-1)*2^-53.
+uniform[-1,1] is ``2*rng.random(dtype) - 1`` (exact in the element type);
+normal is ``rng.standard_normal(dtype)``.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Any
+
+import numpy as np
+
+PRECISIONS = ("s", "d", "c", "z", "w")
+
+# element dtype, real dtype, bytes per element
+_DTYPE = {
+    "s": (np.float32, np.float32, 4),
+    "d": (np.float64, np.float64, 8),
+    "c": (np.complex64, np.float32, 8),
+    "z": (np.complex128, np.float64, 16),
+    "w": (np.float64, np.float64, 16),
+}
+
+
+def elem_bytes(prec: str) -> int:
+    return _DTYPE[prec][2]
+
+
+def real_dtype(prec: str):
+    return _DTYPE[prec][1]
+
+
+def empty(prec: str, count: int, fill: float = np.nan) -> np.ndarray:
+    """Array of ``count`` elements of type ``prec`` filled with ``fill``."""
+    if prec == "w":
+        return np.full((count, 2), fill, dtype=np.float64)
+    if prec in ("c", "z"):
+        return np.full(count, complex(fill, fill), dtype=_DTYPE[prec][0])
+    return np.full(count, fill, dtype=_DTYPE[prec][0])
+
+
+def _flat_real(a: np.ndarray) -> np.ndarray:
+    """Contiguous real view of an element array (complex: (re, im) words;
+    double-double: (hi, lo) words)."""
+    if a.dtype in (np.complex64, np.complex128):
+        return a.view(a.real.dtype)
+    return a.reshape(-1)
+
+
+def draw_into(rng: np.random.Generator, prec: str, out: np.ndarray,
+              dist: str = "uniform", scale: float = 1.0) -> np.ndarray:
+    """Fill the contiguous element array ``out`` with draws from ``dist``
+    ('uniform' on [-scale, scale] or 'normal'), in place."""
+    rdt = _DTYPE[prec][1]
+    raw = _flat_real(out)
+    if dist == "uniform":
+        rng.random(out=raw, dtype=rdt)
+        raw *= rdt(2)
+        raw -= rdt(1)
+    elif dist == "normal":
+        rng.standard_normal(out=raw, dtype=rdt)
+    else:
+        raise ValueError(f"unknown distribution {dist!r}")
+    if scale != 1.0:
+        raw *= rdt(scale)
+    if prec == "w":
+        # pairs (hi, u) -> (hi, hi*u*2^-53)
+        out[:, 1] *= out[:, 0]
+        out[:, 1] *= 2.0 ** -53
+    return out
+
+
+def draw(rng: np.random.Generator, prec: str, count: int, dist: str = "uniform",
+         scale: float = 1.0) -> np.ndarray:
+    """``count`` fresh elements of type ``prec`` from ``dist``."""
+    return draw_into(rng, prec, empty(prec, count, 0.0), dist, scale)
+
+
+def draw_integers(rng: np.random.Generator, prec: str, count: int, lo: int, hi: int) -> np.ndarray:
+    """Integer-valued elements in [lo, hi] (complex: both parts; double-double:
+    lo word zero).  Sums of such values stay exact in every type as long as
+    they stay below 2^24 in magnitude."""
+    ncomp = 1 if prec in ("s", "d", "w") else 2
+    raw = rng.integers(lo, hi + 1, size=count * ncomp).astype(_DTYPE[prec][1])
+    if prec in ("s", "d"):
+        return raw
+    if prec in ("c", "z"):
+        return raw.view(_DTYPE[prec][0])
+    out = np.zeros((count, 2), dtype=np.float64)
+    out[:, 0] = raw
+    return out
+
+
+def place_triangle(prec: str, uplo: str, n: int, lda: int, tri: np.ndarray,
+                   fill: float = np.nan) -> np.ndarray:
+    """Column-major ``lda x n`` array holding ``tri`` (the stored triangle in
+    column-major order) with everything else set to ``fill``."""
+    if lda < max(1, n):
+        raise ValueError("lda < max(1, n)")
+    A = empty(prec, lda * n, fill)
+    off = 0
+    upper = uplo in ("U", "u")
+    for j in range(n):
+        r0, r1 = (0, j + 1) if upper else (j, n)
+        ln = r1 - r0
+        A[j * lda + r0: j * lda + r1] = tri[off: off + ln]
+        off += ln
+    return A
+
+
+def diag_index(n: int, lda: int) -> np.ndarray:
+    return np.arange(n, dtype=np.int64) * (lda + 1)
+
+
+@dataclasses.dataclass
+class Problem:
+    """One call's worth of arguments (host arrays)."""
+    prec: str
+    uplo: str
+    n: int
+    lda: int
+    alpha: Any
+    beta: Any
+    A: np.ndarray
+    x: np.ndarray
+    y: np.ndarray
+    incx: int = 1
+    incy: int = 1
+    name: str = ""
+
+    @property
+    def elem_bytes(self) -> int:
+        return elem_bytes(self.prec)
+
+
+def make_problem(prec: str, uplo: str, n: int, lda: int | None = None, *,
+                 alpha: Any = 1.0, beta: Any = 1.0, seed: int = 0,
+                 a_dist: str = "uniform", xy_dist: str = "uniform",
+                 diag_imag_scale: float | None = None,
+                 fill: float = np.nan, name: str = "") -> Problem:
+    """Draw a problem in the documented order.  ``diag_imag_scale`` (Hermitian
+    only) overwrites the imaginary words of the diagonal with uniform values on
+    [-scale, scale], drawn last."""
+    if prec not in PRECISIONS:
+        raise ValueError(prec)
+    lda = n if lda is None else lda
+    if lda < max(1, n):
+        raise ValueError("lda < max(1, n)")
+    rng = np.random.Generator(np.random.PCG64(seed))
+    # the stored triangle, column by column, drawn straight into place
+    A = np.empty((lda * n, 2), dtype=np.float64) if prec == "w" else \
+        np.empty(lda * n, dtype=_DTYPE[prec][0])
+    fillv = complex(fill, fill) if prec in ("c", "z") else fill
+    upper = uplo in ("U", "u")
+    for j in range(n):
+        r0, r1 = (0, j + 1) if upper else (j, n)
+        col = A[j * lda: (j + 1) * lda]
+        col[:r0] = fillv
+        col[r1:] = fillv
+        draw_into(rng, prec, col[r0:r1], a_dist)
+    x = draw(rng, prec, n, xy_dist)
+    y = draw(rng, prec, n, xy_dist)
+    if diag_imag_scale is not None:
+        if prec not in ("c", "z"):
+            raise ValueError("diagonal garbage only applies to Hermitian types")
+        g = draw(rng, "s" if prec == "c" else "d", n, "uniform", diag_imag_scale)
+        A.imag[diag_index(n, lda)] = g
+    return Problem(prec, uplo, n, lda, alpha, beta, A, x, y, name=name)
+
+
+def make_integer_problem(prec: str, uplo: str, n: int, lda: int | None = None, *,
+                         alpha: Any = 1.5, beta: Any = -0.5, seed: int = 0,
+                         lo: int = -3, hi: int = 3, fill: float = np.nan) -> Problem:
+    """Integer-valued A, x, y (entries in [lo, hi]); with alpha = 1.5 and
+    beta = -0.5 every intermediate of any summation order is exact while
+    n*hi*hi stays below 2^23."""
+    lda = n if lda is None else lda
+    rng = np.random.Generator(np.random.PCG64(seed))
+    tri = draw_integers(rng, prec, n * (n + 1) // 2, lo, hi)
+    A = place_triangle(prec, uplo, n, lda, tri, fill)
+    x = draw_integers(rng, prec, n, lo, hi)
+    y = draw_integers(rng, prec, n, lo, hi)
+    if prec == "w":
+        alpha = alpha if isinstance(alpha, tuple) else (float(alpha), 0.0)
+        beta = beta if isinstance(beta, tuple) else (float(beta), 0.0)
+    return Problem(prec, uplo, n, lda, alpha, beta, A, x, y, name="integer")
+
+
+# --------------------------------------------------------------------------
+# The benchmark workloads, named by what they are.
+# --------------------------------------------------------------------------
+
+SWEEP_N = (2048, 4096, 8192, 16384, 24576, 32768, 10007, 32767)
+
+
+def ssymv_lower_n1024() -> Problem:
+    """SSYMV, uplo=L, n=lda=1024, uniform A, x, y; alpha=1.5, beta=-0.5; seed 0."""
+    return make_problem("s", "L", 1024, 1024, alpha=1.5, beta=-0.5, seed=0,
+                        name="ssymv-L-n1024")
+
+
+def dsymv_upper_n8192_lda8200_beta0() -> Problem:
+    """DSYMV, uplo=U, n=8192, lda=8200, uniform A, normal x, y; alpha=1,
+    beta=0 (y is ignored); seed 1."""
+    return make_problem("d", "U", 8192, 8200, alpha=1.0, beta=0.0, seed=1,
+                        xy_dist="normal", name="dsymv-U-n8192-lda8200-beta0")
+
+
+def symv_sweep(prec: str, uplo: str, n: int) -> Problem:
+    """[SD]SYMV size sweep: lda=n, uniform A, x, y; alpha=beta=1; seed=n."""
+    if prec not in ("s", "d"):
+        raise ValueError(prec)
+    return make_problem(prec, uplo, n, n, alpha=1.0, beta=1.0, seed=n,
+                        name=f"{prec}symv-{uplo}-n{n}")
+
+
+def hemv_lower_n16384(prec: str, n: int = 16384) -> Problem:
+    """[CZ]HEMV, uplo=L, n=16384, uniform A, x, y, diagonal imaginary words
+    uniform[-1e3, 1e3] (must be ignored); alpha=(0.75,0.25), beta=(0.5,-1);
+    seed 3."""
+    if prec not in ("c", "z"):
+        raise ValueError(prec)
+    return make_problem(prec, "L", n, n, alpha=complex(0.75, 0.25),
+                        beta=complex(0.5, -1.0), seed=3, diag_imag_scale=1e3,
+                        name=f"{prec}hemv-L-n{n}")
+
+
+def wsymv_lower_n8192(n: int = 8192) -> Problem:
+    """WSYMV (double-double), uplo=L, n=8192, (hi, lo) with hi uniform[-1,1]
+    and lo = hi*u*2^-53; alpha = beta = (1, 0); seed 4."""
+    return make_problem("w", "L", n, n, alpha=(1.0, 0.0), beta=(1.0, 0.0),
+                        seed=4, name=f"wsymv-L-n{n}")

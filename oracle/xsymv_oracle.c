@@ -1,0 +1,317 @@
+/*
+ * xsymv_oracle.c -- CPU oracle for the symmetric / Hermitian matrix-vector
+ * product y := alpha*S*x + beta*y in five element types.
+ *
+ * TEST INFRASTRUCTURE ONLY: called by the test suite, the packaged smoke
+ * check and the benchmark's CPU-baseline leg, never by the product path.
+ * It shares no source with the GPU library (no common headers, helpers or
+ * tables).  Build: gcc -O2 -ffp-contract=off -std=c99 -fPIC -shared -lm, so
+ * that every product and sum is rounded exactly as written (no contraction
+ * into fused multiply-adds except where fma() is called by name).
+ *
+ * What it computes.  The CUDA-xSYMV report (IPSJ SIG Technical Report
+ * 2014-HPC-146 No.14), §1 eq.(1): y := alpha*A_{U or L}*x + beta*y with
+ * A = A^T, where only the upper (U) or lower (L) triangle is stored and
+ * referenced.  S below is the full matrix that triangle implies:
+ *   S(i,j) = A(i,j) where (i,j) is stored, conj(A(j,i)) across the diagonal,
+ *   and for Hermitian matrices S(i,i) = Re A(i,i) (the imaginary word of a
+ *   diagonal element is never read).  conj() is the identity for the real
+ *   and double-double types.
+ *
+ * How.  The report's sequential algorithm (§2.1 Fig. 1), taken step by step:
+ *   v := 0 and y := beta*y;
+ *   part one: for every column j, every stored off-diagonal a = A(i,j) is
+ *     used twice -- v(i) += a*x(j) (its row's share) and t += conj(a)*x(i)
+ *     (its column's share, the transpose) -- and then y(j) += alpha*t;
+ *   part two: y(i) += alpha*S(i,i)*x(i);
+ *   part three: y += alpha*v.
+ * Fig. 1 prints the U case; for L only the range of i within a column
+ * changes (i > j instead of i < j).  Scaling y by beta follows BLAS: with
+ * beta == 0 the old y is not read (it may hold NaN), and alpha == 0 leaves
+ * y := beta*y without touching A or x.
+ *
+ * Double-double arithmetic (report §2.2, which takes Bailey's double-double
+ * format [14]: a value is the unevaluated sum hi + lo of two doubles):
+ *   TwoSum (Knuth) and FastTwoSum (Dekker) give a sum and its exact error;
+ *   TwoProd gives a product and its exact error with one fma;
+ *   dd_add is the accurate ("IEEE") double-double addition of Hida, Li and
+ *     Bailey -- both hi and lo parts are summed with TwoSum and the result
+ *     is renormalised twice;
+ *   dd_mul is their multiplication: TwoProd of the high parts plus the two
+ *     cross products, then renormalised.
+ */
+#include "xsymv_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+
+/* ----------------------------------------------------------------- checks */
+
+/* BLAS argument checks, in the order of the report's argument list
+ * (§2.2 Fig. 5: uplo, n, alpha, a, lda, x, incx, beta, y, incy). */
+static int check_args(char uplo, int n, const void *A, int lda,
+                      const void *x, int incx, const void *y, int incy,
+                      int *upper)
+{
+    if (uplo == 'U' || uplo == 'u')
+        *upper = 1;
+    else if (uplo == 'L' || uplo == 'l')
+        *upper = 0;
+    else
+        return -1;
+    if (n < 0) return -2;
+    if (n > 0 && A == NULL) return -4;
+    if (lda < (n > 1 ? n : 1)) return -5;
+    if (n > 0 && x == NULL) return -6;
+    if (incx == 0) return -7;
+    if (n > 0 && y == NULL) return -9;
+    if (incy == 0) return -10;
+    return 0;
+}
+
+/* Position of logical element k of a strided vector (BLAS convention). */
+static long long vpos(int n, int inc, int k)
+{
+    long long start = inc > 0 ? 0 : (long long)(1 - n) * inc;
+    return start + (long long)k * inc;
+}
+
+/* ------------------------------------------------------- element types */
+
+/* real single */
+static float s_add(float a, float b) { return a + b; }
+static float s_mul(float a, float b) { return a * b; }
+static float s_conj(float a) { return a; }
+static float s_diag(const float *p) { return *p; }
+static int s_is_zero(float a) { return a == 0.0f; }
+static int s_is_one(float a) { return a == 1.0f; }
+static float s_zero(void) { return 0.0f; }
+
+/* real double */
+static double d_add(double a, double b) { return a + b; }
+static double d_mul(double a, double b) { return a * b; }
+static double d_conj(double a) { return a; }
+static double d_diag(const double *p) { return *p; }
+static int d_is_zero(double a) { return a == 0.0; }
+static int d_is_one(double a) { return a == 1.0; }
+static double d_zero(void) { return 0.0; }
+
+/* complex single: textbook product, four products and two sums */
+static ocplx_f c_add(ocplx_f a, ocplx_f b)
+{
+    ocplx_f r;
+    r.re = a.re + b.re;
+    r.im = a.im + b.im;
+    return r;
+}
+static ocplx_f c_mul(ocplx_f a, ocplx_f b)
+{
+    ocplx_f r;
+    r.re = a.re * b.re - a.im * b.im;
+    r.im = a.re * b.im + a.im * b.re;
+    return r;
+}
+static ocplx_f c_conj(ocplx_f a)
+{
+    a.im = -a.im;
+    return a;
+}
+/* Hermitian diagonal: only the real word is read. */
+static ocplx_f c_diag(const ocplx_f *p)
+{
+    ocplx_f r;
+    r.re = p->re;
+    r.im = 0.0f;
+    return r;
+}
+static int c_is_zero(ocplx_f a) { return a.re == 0.0f && a.im == 0.0f; }
+static int c_is_one(ocplx_f a) { return a.re == 1.0f && a.im == 0.0f; }
+static ocplx_f c_zero(void)
+{
+    ocplx_f r = {0.0f, 0.0f};
+    return r;
+}
+
+/* complex double */
+static ocplx_d z_add(ocplx_d a, ocplx_d b)
+{
+    ocplx_d r;
+    r.re = a.re + b.re;
+    r.im = a.im + b.im;
+    return r;
+}
+static ocplx_d z_mul(ocplx_d a, ocplx_d b)
+{
+    ocplx_d r;
+    r.re = a.re * b.re - a.im * b.im;
+    r.im = a.re * b.im + a.im * b.re;
+    return r;
+}
+static ocplx_d z_conj(ocplx_d a)
+{
+    a.im = -a.im;
+    return a;
+}
+static ocplx_d z_diag(const ocplx_d *p)
+{
+    ocplx_d r;
+    r.re = p->re;
+    r.im = 0.0;
+    return r;
+}
+static int z_is_zero(ocplx_d a) { return a.re == 0.0 && a.im == 0.0; }
+static int z_is_one(ocplx_d a) { return a.re == 1.0 && a.im == 0.0; }
+static ocplx_d z_zero(void)
+{
+    ocplx_d r = {0.0, 0.0};
+    return r;
+}
+
+/* double-double */
+static odd two_sum(double a, double b)          /* Knuth: any a, b */
+{
+    odd r;
+    double s = a + b;
+    double bb = s - a;
+    r.hi = s;
+    r.lo = (a - (s - bb)) + (b - bb);
+    return r;
+}
+static odd fast_two_sum(double a, double b)     /* Dekker: |a| >= |b| */
+{
+    odd r;
+    double s = a + b;
+    r.hi = s;
+    r.lo = b - (s - a);
+    return r;
+}
+static odd two_prod(double a, double b)         /* exact via one fma */
+{
+    odd r;
+    double p = a * b;
+    r.hi = p;
+    r.lo = fma(a, b, -p);
+    return r;
+}
+odd oracle_dd_add(odd a, odd b)
+{
+    odd s = two_sum(a.hi, b.hi);
+    odd t = two_sum(a.lo, b.lo);
+    s.lo = s.lo + t.hi;
+    s = fast_two_sum(s.hi, s.lo);
+    s.lo = s.lo + t.lo;
+    return fast_two_sum(s.hi, s.lo);
+}
+odd oracle_dd_mul(odd a, odd b)
+{
+    odd p = two_prod(a.hi, b.hi);
+    p.lo = p.lo + (a.hi * b.lo + a.lo * b.hi);
+    return fast_two_sum(p.hi, p.lo);
+}
+static odd w_add(odd a, odd b) { return oracle_dd_add(a, b); }
+static odd w_mul(odd a, odd b) { return oracle_dd_mul(a, b); }
+static odd w_conj(odd a) { return a; }
+static odd w_diag(const odd *p) { return *p; }
+static int w_is_zero(odd a) { return a.hi == 0.0 && a.lo == 0.0; }
+static int w_is_one(odd a) { return a.hi == 1.0 && a.lo == 0.0; }
+static odd w_zero(void)
+{
+    odd r = {0.0, 0.0};
+    return r;
+}
+
+/* ------------------------------------------------------------ algorithm */
+
+/* One definition per element type; P is the prefix of its operations. */
+#define DEFINE_ORACLE(NAME, ROWS_NAME, T, P)                                   \
+int NAME(char uplo, int n, T alpha, const T *A, int lda, const T *x,           \
+         int incx, T beta, T *y, int incy)                                     \
+{                                                                              \
+    int upper, i, j;                                                           \
+    int rc = check_args(uplo, n, A, lda, x, incx, y, incy, &upper);            \
+    T *v;                                                                      \
+    if (rc) return rc;                                                         \
+    if (n == 0 || (P##_is_zero(alpha) && P##_is_one(beta))) return 0;          \
+    /* y := beta*y (BLAS: beta == 0 writes zeros without reading y) */         \
+    if (!P##_is_one(beta)) {                                                   \
+        for (i = 0; i < n; ++i) {                                              \
+            T *yi = &y[vpos(n, incy, i)];                                      \
+            *yi = P##_is_zero(beta) ? P##_zero() : P##_mul(beta, *yi);         \
+        }                                                                      \
+    }                                                                          \
+    if (P##_is_zero(alpha)) return 0;                                          \
+    v = (T *)malloc(sizeof(T) * (size_t)n);                                    \
+    if (v == NULL) return -100;                                                \
+    for (i = 0; i < n; ++i) v[i] = P##_zero();                                 \
+    /* part one: each stored off-diagonal element, read once, used twice */    \
+    for (j = 0; j < n; ++j) {                                                  \
+        T xj = x[vpos(n, incx, j)];                                            \
+        T t = P##_zero();                                                      \
+        int lo = upper ? 0 : j + 1;                                            \
+        int hi = upper ? j : n;                                                \
+        T *yj = &y[vpos(n, incy, j)];                                          \
+        for (i = lo; i < hi; ++i) {                                            \
+            T a = A[(long long)i + (long long)j * lda];                        \
+            T xi = x[vpos(n, incx, i)];                                        \
+            v[i] = P##_add(v[i], P##_mul(a, xj));                              \
+            t = P##_add(t, P##_mul(P##_conj(a), xi));                          \
+        }                                                                      \
+        *yj = P##_add(*yj, P##_mul(alpha, t));                                 \
+    }                                                                          \
+    /* part two: the diagonal */                                               \
+    for (i = 0; i < n; ++i) {                                                  \
+        T d = P##_diag(&A[(long long)i + (long long)i * lda]);                 \
+        T *yi = &y[vpos(n, incy, i)];                                          \
+        *yi = P##_add(*yi, P##_mul(P##_mul(alpha, d), x[vpos(n, incx, i)]));   \
+    }                                                                          \
+    /* part three: y += alpha*v */                                             \
+    for (i = 0; i < n; ++i) {                                                  \
+        T *yi = &y[vpos(n, incy, i)];                                          \
+        *yi = P##_add(*yi, P##_mul(alpha, v[i]));                              \
+    }                                                                          \
+    free(v);                                                                   \
+    return 0;                                                                  \
+}                                                                              \
+                                                                               \
+int ROWS_NAME(char uplo, int n, T alpha, const T *A, int lda, const T *x,      \
+              int incx, T beta, const T *y, int incy, const long long *rows,   \
+              int nrows, T *out)                                               \
+{                                                                              \
+    int upper, r, j;                                                           \
+    int rc = check_args(uplo, n, A, lda, x, incx, y, incy, &upper);            \
+    if (rc) return rc;                                                         \
+    for (r = 0; r < nrows; ++r)                                                \
+        if (rows[r] < 0 || rows[r] >= n) return -11;                           \
+    for (r = 0; r < nrows; ++r) {                                              \
+        long long i = rows[r];                                                 \
+        T yi = y[vpos(n, incy, (int)i)];                                       \
+        T sum = P##_zero();                                                    \
+        T res;                                                                 \
+        if (P##_is_zero(alpha) && P##_is_one(beta)) {                          \
+            out[r] = yi;                                                       \
+            continue;                                                          \
+        }                                                                      \
+        res = P##_is_zero(beta) ? P##_zero() : P##_mul(beta, yi);              \
+        if (!P##_is_zero(alpha)) {                                             \
+            for (j = 0; j < n; ++j) {                                          \
+                T s;                                                           \
+                if (i == j)                                                    \
+                    s = P##_diag(&A[i + (long long)i * lda]);                  \
+                else if (upper ? (i < j) : (i > j))                            \
+                    s = A[i + (long long)j * lda];                             \
+                else                                                           \
+                    s = P##_conj(A[(long long)j + i * lda]);                   \
+                sum = P##_add(sum, P##_mul(s, x[vpos(n, incx, j)]));           \
+            }                                                                  \
+            res = P##_add(res, P##_mul(alpha, sum));                           \
+        }                                                                      \
+        out[r] = res;                                                          \
+    }                                                                          \
+    return 0;                                                                  \
+}
+
+DEFINE_ORACLE(oracle_ssymv, oracle_ssymv_rows, float, s)
+DEFINE_ORACLE(oracle_dsymv, oracle_dsymv_rows, double, d)
+DEFINE_ORACLE(oracle_chemv, oracle_chemv_rows, ocplx_f, c)
+DEFINE_ORACLE(oracle_zhemv, oracle_zhemv_rows, ocplx_d, z)
+DEFINE_ORACLE(oracle_wsymv, oracle_wsymv_rows, odd, w)

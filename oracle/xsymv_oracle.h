@@ -1,0 +1,80 @@
+/*
+ * xsymv_oracle.h -- interface of the CPU oracle for y := alpha*S*x + beta*y.
+ *
+ * TEST INFRASTRUCTURE ONLY.  The oracle is a plain, slow, sequential C
+ * implementation used by the test suite, by the packaged smoke check and by
+ * the benchmark's CPU-baseline leg.  No product code path may call it.  It
+ * shares no source with the GPU library.
+ *
+ * Source of the method: Imamura, Mukunoki, Yamada, Machida, "CUDA-xSYMV no
+ * jisso to hyoka" (Implementation and evaluation of CUDA-xSYMV), IPSJ SIG
+ * Technical Report 2014-HPC-146 No.14 -- cited below as "the CUDA-xSYMV
+ * report".  Problem statement: §1 eq.(1); sequential three-part algorithm:
+ * §2.1 Fig. 1; BLAS-style argument list: §2.2 Fig. 5; element types
+ * (float2 / double2 complex, double2 double-double): §2.2.
+ *
+ * Matrices are column-major: element (i, j) of A lives at A[i + j*lda],
+ * 0-based.  Vectors use BLAS increments: X(k) = x[kx + k*incx] with
+ * kx = 0 for incx > 0 and kx = (1-n)*incx for incx < 0.
+ *
+ * Return codes (same numbering as the product library, BLAS xerbla order):
+ *   0 ok, -1 bad uplo, -2 n < 0, -4 A NULL, -5 lda < max(1,n),
+ *   -6 x NULL, -7 incx == 0, -9 y NULL, -10 incy == 0.
+ */
+#ifndef XSYMV_ORACLE_H
+#define XSYMV_ORACLE_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct { float re, im; } ocplx_f;    /* interleaved, like float2  */
+typedef struct { double re, im; } ocplx_d;   /* interleaved, like double2 */
+typedef struct { double hi, lo; } odd;       /* value = hi + lo exactly   */
+
+/* Full result by the three-part algorithm of §2.1 Fig. 1 (part one: the
+ * off-diagonal elements used twice; part two: the diagonal; part three:
+ * the row-role vector v added in), extended to uplo = 'L', to Hermitian
+ * matrices and to BLAS increments. */
+int oracle_ssymv(char uplo, int n, float alpha, const float *A, int lda,
+                 const float *x, int incx, float beta, float *y, int incy);
+int oracle_dsymv(char uplo, int n, double alpha, const double *A, int lda,
+                 const double *x, int incx, double beta, double *y, int incy);
+int oracle_chemv(char uplo, int n, ocplx_f alpha, const ocplx_f *A, int lda,
+                 const ocplx_f *x, int incx, ocplx_f beta, ocplx_f *y, int incy);
+int oracle_zhemv(char uplo, int n, ocplx_d alpha, const ocplx_d *A, int lda,
+                 const ocplx_d *x, int incx, ocplx_d beta, ocplx_d *y, int incy);
+int oracle_wsymv(char uplo, int n, odd alpha, const odd *A, int lda,
+                 const odd *x, int incx, odd beta, odd *y, int incy);
+
+/* Selected rows only, straight from the definition of eq.(1):
+ *   out[r] = beta*y(rows[r]) + alpha * sum_{j ascending} S(rows[r], j)*x(j)
+ * where S is the full matrix implied by the stored triangle.  y is read
+ * (not written); results go to out[0..nrows).  Used to check very large
+ * problems on a sample of rows.  Same argument checks as above, plus
+ * -11 for a row index outside [0, n). */
+int oracle_ssymv_rows(char uplo, int n, float alpha, const float *A, int lda,
+                      const float *x, int incx, float beta, const float *y,
+                      int incy, const long long *rows, int nrows, float *out);
+int oracle_dsymv_rows(char uplo, int n, double alpha, const double *A, int lda,
+                      const double *x, int incx, double beta, const double *y,
+                      int incy, const long long *rows, int nrows, double *out);
+int oracle_chemv_rows(char uplo, int n, ocplx_f alpha, const ocplx_f *A, int lda,
+                      const ocplx_f *x, int incx, ocplx_f beta, const ocplx_f *y,
+                      int incy, const long long *rows, int nrows, ocplx_f *out);
+int oracle_zhemv_rows(char uplo, int n, ocplx_d alpha, const ocplx_d *A, int lda,
+                      const ocplx_d *x, int incx, ocplx_d beta, const ocplx_d *y,
+                      int incy, const long long *rows, int nrows, ocplx_d *out);
+int oracle_wsymv_rows(char uplo, int n, odd alpha, const odd *A, int lda,
+                      const odd *x, int incx, odd beta, const odd *y,
+                      int incy, const long long *rows, int nrows, odd *out);
+
+/* The double-double primitives, exported so that the tests can pin them
+ * one by one against exact rational arithmetic. */
+odd oracle_dd_add(odd a, odd b);
+odd oracle_dd_mul(odd a, odd b);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

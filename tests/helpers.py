@@ -1,0 +1,287 @@
+"""Checkers shared by the tests: explicit symmetrisation, exact products,
+the componentwise error bound, comparisons.
+
+They are written from the definition of the product (the CUDA-xSYMV report,
+§1 eq.(1)) and share nothing with either the oracle or the GPU library.
+"""
+from __future__ import annotations
+
+from fractions import Fraction
+
+import numpy as np
+
+# unit roundoff per element type (2^-24, 2^-53; double-double 2^-104)
+EPS = {"s": 2.0 ** -24, "c": 2.0 ** -24, "d": 2.0 ** -53, "z": 2.0 ** -53,
+       "w": 2.0 ** -104}
+
+
+def is_upper(uplo: str) -> bool:
+    return uplo in ("U", "u")
+
+
+def stored(uplo: str, i: int, j: int) -> bool:
+    return i <= j if is_upper(uplo) else i >= j
+
+
+def vec_index(n: int, inc: int) -> np.ndarray:
+    """Storage positions of logical elements 0..n-1 of a strided vector."""
+    start = 0 if inc > 0 else (1 - n) * inc
+    return start + np.arange(n, dtype=np.int64) * inc
+
+
+def dense_matrix(p, dtype=None) -> np.ndarray:
+    """Full n x n matrix implied by the stored triangle (conjugate mirror and
+    real diagonal for Hermitian types), as complex128/float64 (double-double:
+    hi + lo rounded to float64)."""
+    n, lda = p.n, p.lda
+    if p.prec == "w":
+        A = p.A[:, 0].astype(np.float64) + p.A[:, 1]
+    else:
+        A = p.A
+    M = A[: lda * n].reshape(n, lda).T[:n, :n]  # column-major -> [i, j]
+    dt = dtype or (np.complex128 if p.prec in ("c", "z") else np.float64)
+    M = M.astype(dt)
+    low = np.tril(np.ones((n, n), dtype=bool), -1)
+    if is_upper(p.uplo):
+        S = np.where(low, np.conj(M.T), M)
+    else:
+        S = np.where(low.T, np.conj(M.T), M)
+    S = np.array(S)
+    d = np.arange(n)
+    if p.prec in ("c", "z"):
+        S[d, d] = M[d, d].real
+    return S
+
+
+def _frac(v) -> Fraction:
+    return Fraction(float(v))
+
+
+def exact_elements(p):
+    """Stored elements as exact values: Fraction (real, double-double) or a
+    pair of Fractions (complex)."""
+    n, lda = p.n, p.lda
+
+    def get(i, j):
+        k = i + j * lda
+        if p.prec == "w":
+            return Fraction(float(p.A[k, 0])) + Fraction(float(p.A[k, 1]))
+        if p.prec in ("c", "z"):
+            return (_frac(p.A[k].real), _frac(p.A[k].imag))
+        return _frac(p.A[k])
+
+    return get
+
+
+def exact_vector(p, v, inc):
+    idx = vec_index(p.n, inc)
+    if p.prec == "w":
+        return [Fraction(float(v[k, 0])) + Fraction(float(v[k, 1])) for k in idx]
+    if p.prec in ("c", "z"):
+        return [(_frac(v[k].real), _frac(v[k].imag)) for k in idx]
+    return [_frac(v[k]) for k in idx]
+
+
+def exact_scalar(prec, s):
+    if prec == "w":
+        return Fraction(float(s[0])) + Fraction(float(s[1]))
+    if prec in ("c", "z"):
+        c = complex(s)
+        return (Fraction(c.real), Fraction(c.imag))
+    return Fraction(float(s))
+
+
+def _cmul(a, b):
+    return (a[0] * b[0] - a[1] * b[1], a[0] * b[1] + a[1] * b[0])
+
+
+def _cadd(a, b):
+    return (a[0] + b[0], a[1] + b[1])
+
+
+def exact_result(p):
+    """Exact alpha*S*x + beta*y (y ignored when beta == 0), as a list of
+    Fractions or (re, im) Fraction pairs, in logical order."""
+    n = p.n
+    get = exact_elements(p)
+    cplx = p.prec in ("c", "z")
+    x = exact_vector(p, p.x, p.incx)
+    al = exact_scalar(p.prec, p.alpha)
+    be = exact_scalar(p.prec, p.beta)
+    beta_zero = be == (0, 0) if cplx else be == 0
+    y = None if beta_zero else exact_vector(p, p.y, p.incy)
+    out = []
+    zero = (Fraction(0), Fraction(0)) if cplx else Fraction(0)
+    for i in range(n):
+        s = zero
+        for j in range(n):
+            if i == j:
+                a = get(i, i)
+                if cplx:
+                    a = (a[0], Fraction(0))
+            elif stored(p.uplo, i, j):
+                a = get(i, j)
+            else:
+                a = get(j, i)
+                if cplx:
+                    a = (a[0], -a[1])
+            s = _cadd(s, _cmul(a, x[j])) if cplx else s + a * x[j]
+        if cplx:
+            r = _cmul(al, s)
+            if not beta_zero:
+                r = _cadd(r, _cmul(be, y[i]))
+        else:
+            r = al * s
+            if not beta_zero:
+                r = r + be * y[i]
+        out.append(r)
+    return out
+
+
+def abs_bound_terms(p):
+    """(|alpha|*(|S||x|)_i + |beta|*|y_i|) in float64, logical order."""
+    S = np.abs(dense_matrix(p))
+    xi = vec_index(p.n, p.incx)
+    yi = vec_index(p.n, p.incy)
+    if p.prec == "w":
+        x = np.abs(p.x[xi, 0] + p.x[xi, 1])
+        y = np.abs(p.y[yi, 0] + p.y[yi, 1])
+        al = abs(p.alpha[0] + p.alpha[1])
+        be = abs(p.beta[0] + p.beta[1])
+    else:
+        x = np.abs(p.x[xi]).astype(np.float64)
+        y = np.abs(p.y[yi]).astype(np.float64)
+        al = abs(complex(p.alpha))
+        be = abs(complex(p.beta))
+    t = al * (S @ x)
+    if be != 0:
+        t = t + be * np.where(np.isfinite(y), y, 0.0)
+    return t
+
+
+def tolerance(p, rows=None):
+    """Componentwise bound 4*n*eps*(|alpha|*(|S||x|)_i + |beta|*|y_i|), for all
+    rows or for the logical rows ``rows`` only (then without forming S)."""
+    if rows is None:
+        return 4.0 * max(p.n, 1) * EPS[p.prec] * abs_bound_terms(p)
+    return 4.0 * max(p.n, 1) * EPS[p.prec] * abs_bound_rows(p, rows)
+
+
+def _magnitude(p, v):
+    if p.prec == "w":
+        return np.abs(v[..., 0] + v[..., 1])
+    return np.abs(v).astype(np.float64)
+
+
+def abs_bound_rows(p, rows):
+    """(|alpha|*(|S||x|)_i + |beta|*|y_i|) for logical rows ``rows``, read
+    straight from the stored triangle (unit increments only)."""
+    assert p.incx == 1 and p.incy == 1
+    n, lda = p.n, p.lda
+    ax = _magnitude(p, p.x)
+    ay = _magnitude(p, p.y)
+    if p.prec == "w":
+        al = abs(p.alpha[0] + p.alpha[1])
+        be = abs(p.beta[0] + p.beta[1])
+    else:
+        al = abs(complex(p.alpha))
+        be = abs(complex(p.beta))
+    out = np.empty(len(rows))
+    j = np.arange(n, dtype=np.int64)
+    for k, i in enumerate(rows):
+        st = (j >= i) if is_upper(p.uplo) else (j <= i)
+        idx = np.where(st, i + j * lda, j + i * lda)
+        a = _magnitude(p, p.A[idx])
+        if p.prec in ("c", "z"):
+            a[i] = abs(float(p.A[i + i * lda].real))
+        t = al * float(a @ ax)
+        if be != 0 and np.isfinite(ay[i]):
+            t += be * ay[i]
+        out[k] = t
+    return out
+
+
+def exact_errors(p, y_out, exact=None):
+    """|y_out - exact| per logical element, as float64 (exact subtraction in
+    rationals, then rounded)."""
+    ex = exact_result(p) if exact is None else exact
+    idx = vec_index(p.n, p.incy)
+    errs = np.empty(p.n)
+    for k, i in enumerate(idx):
+        e = ex[k]
+        if p.prec == "w":
+            v = Fraction(float(y_out[i, 0])) + Fraction(float(y_out[i, 1]))
+            errs[k] = abs(float(v - e))
+        elif p.prec in ("c", "z"):
+            re = _frac(y_out[i].real) - e[0]
+            im = _frac(y_out[i].imag) - e[1]
+            errs[k] = abs(complex(float(re), float(im)))
+        else:
+            errs[k] = abs(float(_frac(y_out[i]) - e))
+    return errs
+
+
+def diff(prec, a, b):
+    """|a - b| elementwise in float64; double-double as (hi-hi) + (lo-lo)."""
+    if prec == "w":
+        return np.abs((a[..., 0] - b[..., 0]) + (a[..., 1] - b[..., 1]))
+    return np.abs(a.astype(np.complex128) - b.astype(np.complex128)) \
+        if prec in ("c", "z") else np.abs(a.astype(np.float64) - b.astype(np.float64))
+
+
+def integer_expected(p):
+    """Exact result for integer-valued problems via int64 dense products, in
+    the element type (every value involved is exactly representable)."""
+    n = p.n
+    M = dense_matrix(p)
+    xi = vec_index(n, p.incx)
+    yi = vec_index(n, p.incy)
+    if p.prec in ("c", "z"):
+        Sr = np.rint(M.real).astype(np.int64)
+        Si = np.rint(M.imag).astype(np.int64)
+        xr = np.rint(p.x[xi].real).astype(np.int64)
+        xim = np.rint(p.x[xi].imag).astype(np.int64)
+        sr = Sr @ xr - Si @ xim
+        si = Sr @ xim + Si @ xr
+        s = sr.astype(np.complex128) + 1j * si.astype(np.complex128)
+        al = complex(p.alpha)
+        be = complex(p.beta)
+        y = p.y[yi].astype(np.complex128)
+        out = al * s + (be * y if be != 0 else 0)
+        return out.astype(p.y.dtype)
+    S = np.rint(M).astype(np.int64)
+    if p.prec == "w":
+        x = np.rint(p.x[xi, 0]).astype(np.int64)
+        y = p.y[yi, 0]
+        al, be = p.alpha[0], p.beta[0]
+    else:
+        x = np.rint(p.x[xi]).astype(np.int64)
+        y = p.y[yi].astype(np.float64)
+        al, be = float(p.alpha), float(p.beta)
+    s = (S @ x).astype(np.float64)
+    out = al * s + (be * y if be != 0 else 0.0)
+    if p.prec == "w":
+        r = np.zeros((n, 2))
+        r[:, 0] = out
+        return r
+    return out.astype(p.y.dtype)
+
+
+def np_mul(a, b):
+    """Elementwise product in the element type with one rounding per real
+    operation (complex: textbook formula, each real product and sum rounded
+    separately), independent of how numpy implements complex multiply."""
+    if np.iscomplexobj(a) or np.iscomplexobj(b):
+        dt = np.result_type(a, b)
+        rt = np.float32 if dt == np.complex64 else np.float64
+        a = np.asarray(a, dtype=dt)
+        b = np.asarray(b, dtype=dt)
+        ar, ai = a.real.astype(rt), a.imag.astype(rt)
+        br, bi = b.real.astype(rt), b.imag.astype(rt)
+        re = np.subtract(np.multiply(ar, br), np.multiply(ai, bi))
+        im = np.add(np.multiply(ar, bi), np.multiply(ai, br))
+        out = np.empty(np.broadcast(re, im).shape, dtype=dt)
+        out.real = re
+        out.imag = im
+        return out
+    return np.multiply(a, b)

@@ -1,0 +1,114 @@
+"""The pins have teeth: plant plausible mistakes in a copy of the oracle's
+source (on the CPU only), build each copy, and check that the pin battery of
+``test_oracle_pins`` rejects every one of them.
+"""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from tests import test_oracle_pins as P
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "xsymv_oracle.c")
+
+# (name, text in the oracle, replacement, occurrence to change or None = all)
+MUTANTS = [
+    ("column role without conjugate",
+     "t = P##_add(t, P##_mul(P##_conj(a), xi));",
+     "t = P##_add(t, P##_mul(a, xi));", None),
+    ("row role with x(i)",
+     "v[i] = P##_add(v[i], P##_mul(a, xj));",
+     "v[i] = P##_add(v[i], P##_mul(a, xi));", None),
+    ("part two dropped",
+     "*yi = P##_add(*yi, P##_mul(P##_mul(alpha, d), x[vpos(n, incx, i)]));",
+     "(void)d;", None),
+    ("part three dropped",
+     "*yi = P##_add(*yi, P##_mul(alpha, v[i]));",
+     "(void)yi;", None),
+    ("upper loop includes the diagonal",
+     "int hi = upper ? j : n;", "int hi = upper ? j + 1 : n;", None),
+    ("lower loop includes the diagonal",
+     "int lo = upper ? 0 : j + 1;", "int lo = upper ? 0 : j;", None),
+    ("transposed read",
+     "T a = A[(long long)i + (long long)j * lda];",
+     "T a = A[(long long)j + (long long)i * lda];", None),
+    ("beta = 0 multiplies y",
+     "*yi = P##_is_zero(beta) ? P##_zero() : P##_mul(beta, *yi);",
+     "*yi = P##_mul(beta, *yi);", None),
+    ("Hermitian diagonal keeps the imaginary word (single)",
+     "r.im = 0.0f;", "r.im = p->im;", None),
+    ("Hermitian diagonal keeps the imaginary word (double)",
+     "r.im = 0.0;\n    return r;\n}\nstatic int z_is_zero",
+     "r.im = p->im;\n    return r;\n}\nstatic int z_is_zero", None),
+    ("complex product sign",
+     "r.re = a.re * b.re - a.im * b.im;", "r.re = a.re * b.re + a.im * b.im;", 1),
+    ("double complex product sign",
+     "r.re = a.re * b.re - a.im * b.im;", "r.re = a.re * b.re + a.im * b.im;", 2),
+    ("sloppy double-double add",
+     "    s.lo = s.lo + t.hi;\n    s = fast_two_sum(s.hi, s.lo);\n    s.lo = s.lo + t.lo;",
+     "    s.lo = s.lo + (a.lo + b.lo);", None),
+    ("double-double product drops cross terms",
+     "p.lo = p.lo + (a.hi * b.lo + a.lo * b.hi);", "p.lo = p.lo;", None),
+    ("TwoProd without its error term",
+     "r.lo = fma(a, b, -p);", "r.lo = 0.0;", None),
+    ("increments ignored",
+     "return start + (long long)k * inc;", "return (long long)k;", None),
+    ("rows: mirrored element not conjugated",
+     "s = P##_conj(A[(long long)j + i * lda]);",
+     "s = A[(long long)j + i * lda];", None),
+    ("rows: alpha dropped",
+     "res = P##_add(res, P##_mul(alpha, sum));", "res = P##_add(res, sum);", None),
+]
+
+# pin battery: (test function, parameter sets)
+BATTERY = [
+    (P.test_exact_bruteforce, [dict(prec=pr, uplo=u, n=17, pad=3)
+                               for pr in P.PRECS for u in "LU"]),
+    (P.test_integer_inputs_bitwise, [dict(prec=pr, uplo=u, n=64, pad=5)
+                                     for pr in P.PRECS for u in "LU"]),
+    (P.test_hermitian_diagonal_imaginary_ignored, [dict(prec=pr, uplo=u)
+                                                   for pr in "cz" for u in "LU"]),
+    (P.test_beta_zero_ignores_nan_y, [dict(prec=pr) for pr in P.PRECS]),
+    (P.test_increments, [dict(prec=pr, incx=-3, incy=-2) for pr in P.PRECS]),
+    (P.test_dd_add_mul_exact_cases, [dict()]),
+    (P.test_dd_add_mul_relative_error, [dict()]),
+]
+
+
+def build_mutant(tmp_path, old, new, occurrence):
+    src = open(SRC).read()
+    assert old in src, f"mutation anchor not found: {old!r}"
+    if occurrence is None:
+        mutated = src.replace(old, new)
+    else:
+        parts = src.split(old)
+        assert len(parts) > occurrence
+        mutated = old.join(parts[:occurrence]) + new + old.join(parts[occurrence:])
+    assert mutated != src
+    c = tmp_path / "mutant.c"
+    c.write_text(mutated)
+    so = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", *oracle.CFLAGS, "-I", os.path.dirname(SRC), "-o", str(so),
+                    str(c), "-lm"], check=True, capture_output=True)
+    return oracle.OracleLib(str(so))
+
+
+@pytest.mark.parametrize("name,old,new,occ", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_reject_mutant(name, old, new, occ, tmp_path):
+    lib = build_mutant(tmp_path, old, new, occ)
+    for fn, params in BATTERY:
+        for kw in params:
+            try:
+                fn(oracle_lib=lib, **kw)
+            except (AssertionError, ValueError):
+                return  # killed
+    pytest.fail(f"no pin rejects the mutant '{name}'")
+
+
+def test_unmutated_copy_passes(tmp_path):
+    """The battery itself passes on an unmodified copy of the oracle."""
+    lib = oracle.OracleLib(oracle.default().path)
+    for fn, params in BATTERY:
+        for kw in params:
+            fn(oracle_lib=lib, **kw)
