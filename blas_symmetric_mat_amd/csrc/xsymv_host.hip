@@ -1,0 +1,308 @@
+// xsymv_host.hip -- state shared by all precisions of libxsymv (selection
+// rules, tile plans, per-stream workspaces, timing) and the precision-generic
+// C ABI calls of include/xsymv.h.
+#include "xsymv_host.hpp"
+
+namespace xsymv {
+
+namespace {
+struct Rule {
+    int n_lo, n_hi, idx;
+};
+std::mutex g_rules_mu;
+std::vector<Rule> g_rules[5][2];
+
+std::mutex g_time_mu;
+bool g_timing = false;
+std::vector<TimedCall> g_timed;
+
+std::mutex g_dev_mu;
+}  // namespace
+
+using PlanKey = std::tuple<int, int, int, int, int>;  // upper, n, NB, R, device
+
+struct DeviceState {
+    std::mutex mu;
+    std::map<PlanKey, std::unique_ptr<Plan>> plans;
+    std::map<hipStream_t, std::pair<void*, size_t>> workspaces;
+};
+
+namespace {
+std::map<int, std::unique_ptr<DeviceState>> g_dev;
+}
+
+int pick_config(int prec, bool upper, int n)
+{
+    std::lock_guard<std::mutex> lk(g_rules_mu);
+    const auto& rs = g_rules[prec][upper ? 1 : 0];
+    for (auto it = rs.rbegin(); it != rs.rend(); ++it)
+        if (n >= it->n_lo && n <= it->n_hi) return it->idx;
+    return 0;
+}
+
+void build_plan_host(bool upper, int n, int NB, int R, std::vector<TileDesc>& tiles,
+                     std::vector<int>& slot_base, int& P)
+{
+    P = (n + NB - 1) / NB;
+    std::vector<TileDesc> full, masked;
+    slot_base.assign(P + 1, 0);
+    int slot = 0;
+    for (int p = 0; p < P; ++p) {
+        const int c0 = p * NB;
+        const int cend = std::min(n, c0 + NB);
+        const bool ragged_cols = (cend - c0) != NB;
+        slot_base[p] = slot;
+        masked.push_back(TileDesc{p, c0, cend, (slot++ << 2) | TILE_MASKED});
+        const int lo = upper ? 0 : cend;
+        const int hi = upper ? c0 : n;
+        for (int r0 = lo; r0 < hi; r0 += R) {
+            const int r1 = std::min(hi, r0 + R);
+            const bool m = ragged_cols || (r1 - r0) != R;
+            TileDesc t{p, r0, r1, (slot++ << 2) | (m ? TILE_MASKED : 0)};
+            (m ? masked : full).push_back(t);
+        }
+    }
+    slot_base[P] = slot;
+    tiles = full;
+    tiles.insert(tiles.end(), masked.begin(), masked.end());
+}
+
+DeviceState* device_state(int dev)
+{
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    auto& p = g_dev[dev];
+    if (!p) p.reset(new DeviceState());
+    return p.get();
+}
+
+std::mutex& device_mutex(DeviceState* ds) { return ds->mu; }
+
+int get_plan(DeviceState* ds, int dev, bool upper, int n, int NB, int R, hipStream_t stream,
+             const Plan** out)
+{
+    PlanKey key{upper ? 1 : 0, n, NB, R, dev};
+    auto it = ds->plans.find(key);
+    if (it != ds->plans.end()) {
+        *out = it->second.get();
+        return 0;
+    }
+    std::vector<TileDesc> tiles;
+    std::vector<int> slot_base;
+    int P = 0;
+    build_plan_host(upper, n, NB, R, tiles, slot_base, P);
+    std::unique_ptr<Plan> plan(new Plan());
+    plan->P = P;
+    plan->NB = NB;
+    plan->ntiles = (int)tiles.size();
+    plan->nslots = slot_base[P];
+    const size_t tb = tiles.size() * sizeof(TileDesc);
+    const size_t sb = slot_base.size() * sizeof(int);
+    XSYMV_HIP(hipHostMalloc((void**)&plan->h_tiles, tb, hipHostMallocDefault));
+    XSYMV_HIP(hipHostMalloc((void**)&plan->h_slot_base, sb, hipHostMallocDefault));
+    std::copy(tiles.begin(), tiles.end(), plan->h_tiles);
+    std::copy(slot_base.begin(), slot_base.end(), plan->h_slot_base);
+    XSYMV_HIP(hipMalloc((void**)&plan->d_tiles, tb));
+    XSYMV_HIP(hipMalloc((void**)&plan->d_slot_base, sb));
+    XSYMV_HIP(hipMemcpyAsync(plan->d_tiles, plan->h_tiles, tb, hipMemcpyHostToDevice, stream));
+    XSYMV_HIP(hipMemcpyAsync(plan->d_slot_base, plan->h_slot_base, sb, hipMemcpyHostToDevice,
+                             stream));
+    // A plan may later be used from other streams: finish the upload now.
+    XSYMV_HIP(hipStreamSynchronize(stream));
+    *out = plan.get();
+    ds->plans[key] = std::move(plan);
+    return 0;
+}
+
+int get_workspace(DeviceState* ds, hipStream_t stream, size_t bytes, void** out)
+{
+    auto& ws = ds->workspaces[stream];
+    if (ws.second < bytes) {
+        if (ws.first) {
+            // the old buffer may still be in use by work queued on this stream
+            XSYMV_HIP(hipStreamSynchronize(stream));
+            XSYMV_HIP(hipFree(ws.first));
+            ws.first = nullptr;
+            ws.second = 0;
+        }
+        const size_t grown = std::max(bytes, (size_t)1 << 20);
+        XSYMV_HIP(hipMalloc(&ws.first, grown));
+        ws.second = grown;
+    }
+    *out = ws.first;
+    return 0;
+}
+
+bool timing_enabled()
+{
+    std::lock_guard<std::mutex> tl(g_time_mu);
+    return g_timing;
+}
+
+void timing_push(const TimedCall& c)
+{
+    std::lock_guard<std::mutex> tl(g_time_mu);
+    g_timed.push_back(c);
+}
+
+int check_args(char uplo, int n, const void* A, int lda, const void* x, int incx,
+               const void* y, int incy, bool* upper)
+{
+    if (uplo == 'U' || uplo == 'u')
+        *upper = true;
+    else if (uplo == 'L' || uplo == 'l')
+        *upper = false;
+    else
+        return -1;
+    if (n < 0) return -2;
+    if (n > 0 && A == nullptr) return -4;
+    if (lda < std::max(1, n)) return -5;
+    if (n > 0 && x == nullptr) return -6;
+    if (incx == 0) return -7;
+    if (n > 0 && y == nullptr) return -9;
+    if (incy == 0) return -10;
+    return 0;
+}
+
+namespace {
+int num_configs(int prec)
+{
+    switch (prec) {
+    case XSYMV_S: return (int)kernel_sets<float>().size();
+    case XSYMV_D: return (int)kernel_sets<double>().size();
+    case XSYMV_C: return (int)kernel_sets<cf32>().size();
+    case XSYMV_Z: return (int)kernel_sets<cf64>().size();
+    case XSYMV_W: return (int)kernel_sets<ddreal>().size();
+    default: return -1;
+    }
+}
+
+bool config_info(int prec, int idx, ConfigInfo* out)
+{
+    if (idx < 0 || idx >= num_configs(prec)) return false;
+    switch (prec) {
+    case XSYMV_S: *out = kernel_sets<float>()[idx].info; return true;
+    case XSYMV_D: *out = kernel_sets<double>()[idx].info; return true;
+    case XSYMV_C: *out = kernel_sets<cf32>()[idx].info; return true;
+    case XSYMV_Z: *out = kernel_sets<cf64>()[idx].info; return true;
+    case XSYMV_W: *out = kernel_sets<ddreal>()[idx].info; return true;
+    default: return false;
+    }
+}
+}  // namespace
+
+}  // namespace xsymv
+
+using namespace xsymv;
+
+extern "C" {
+
+size_t xsymv_workspace_bytes(int prec, char uplo, int n)
+{
+    switch (prec) {
+    case XSYMV_S: return ws_bytes<float>(uplo, n);
+    case XSYMV_D: return ws_bytes<double>(uplo, n);
+    case XSYMV_C: return ws_bytes<cf32>(uplo, n);
+    case XSYMV_Z: return ws_bytes<cf64>(uplo, n);
+    case XSYMV_W: return ws_bytes<ddreal>(uplo, n);
+    default: return (size_t)-1;
+    }
+}
+
+int xsymv_release(void)
+{
+    int dev = 0;
+    XSYMV_HIP(hipGetDevice(&dev));
+    XSYMV_HIP(hipDeviceSynchronize());
+    DeviceState* ds = device_state(dev);
+    std::lock_guard<std::mutex> lk(ds->mu);
+    for (auto& kv : ds->workspaces)
+        if (kv.second.first) XSYMV_HIP(hipFree(kv.second.first));
+    ds->workspaces.clear();
+    for (auto& kv : ds->plans) {
+        Plan* p = kv.second.get();
+        XSYMV_HIP(hipFree(p->d_tiles));
+        XSYMV_HIP(hipFree(p->d_slot_base));
+        XSYMV_HIP(hipHostFree(p->h_tiles));
+        XSYMV_HIP(hipHostFree(p->h_slot_base));
+    }
+    ds->plans.clear();
+    return 0;
+}
+
+int xsymv_num_configs(int prec) { return num_configs(prec); }
+
+int xsymv_config_info(int prec, int idx, int* waves, int* cols_per_wave, int* stripes,
+                      int* rows_per_stripe, int* nontemporal)
+{
+    ConfigInfo ci;
+    if (!config_info(prec, idx, &ci)) return -1;
+    if (waves) *waves = ci.W;
+    if (cols_per_wave) *cols_per_wave = ci.CW;
+    if (stripes) *stripes = ci.S;
+    if (rows_per_stripe) *rows_per_stripe = ci.H;
+    if (nontemporal) *nontemporal = ci.NT;
+    return 0;
+}
+
+int xsymv_select_config(int prec, char uplo, int n_lo, int n_hi, int idx)
+{
+    if (prec < 0 || prec > 4) return -1;
+    bool upper;
+    if (uplo == 'U' || uplo == 'u')
+        upper = true;
+    else if (uplo == 'L' || uplo == 'l')
+        upper = false;
+    else
+        return -1;
+    if (idx < -1 || idx >= num_configs(prec) || n_lo > n_hi) return -1;
+    std::lock_guard<std::mutex> lk(g_rules_mu);
+    g_rules[prec][upper ? 1 : 0].push_back(Rule{n_lo, n_hi, idx < 0 ? 0 : idx});
+    return 0;
+}
+
+int xsymv_current_config(int prec, char uplo, int n)
+{
+    if (prec < 0 || prec > 4) return -1;
+    return pick_config(prec, uplo == 'U' || uplo == 'u', n);
+}
+
+int xsymv_timing_enable(int on)
+{
+    std::lock_guard<std::mutex> tl(g_time_mu);
+    g_timing = on != 0;
+    return 0;
+}
+
+int xsymv_timing_read(float* main_ms, float* merge_ms, int max)
+{
+    std::vector<TimedCall> calls;
+    {
+        std::lock_guard<std::mutex> tl(g_time_mu);
+        calls.swap(g_timed);
+    }
+    int k = 0;
+    int err = 0;
+    for (auto& c : calls) {
+        if (!err) {
+            hipError_t e = hipEventSynchronize(c.e2);
+            float a = 0.f, b = 0.f;
+            if (e == hipSuccess) e = hipEventElapsedTime(&a, c.e0, c.e1);
+            if (e == hipSuccess) e = hipEventElapsedTime(&b, c.e1, c.e2);
+            if (e != hipSuccess) {
+                err = ERR_HIP + (int)e;
+            } else if (k < max) {
+                if (main_ms) main_ms[k] = a;
+                if (merge_ms) merge_ms[k] = b;
+                ++k;
+            }
+        }
+        (void)hipEventDestroy(c.e0);
+        (void)hipEventDestroy(c.e1);
+        (void)hipEventDestroy(c.e2);
+    }
+    return err ? err : k;
+}
+
+const char* xsymv_version(void) { return "xsymv-gfx950 0.1"; }
+
+}  // extern "C"

@@ -1,0 +1,223 @@
+// xsymv_host.hpp -- host-side machinery shared by the per-precision
+// translation units of libxsymv: tile configurations, tile plans, per-stream
+// workspaces, kernel timing and the call driver symv_impl<T>.
+//
+// Call flow of one product y := alpha*S*x + beta*y (the CUDA-xSYMV report,
+// §1 eq.(1), with the BLAS argument list of §2.2 Fig. 5): check the
+// arguments before touching the device; quick returns; pick the tile
+// configuration for (precision, uplo, n); fetch or build the tile plan;
+// enqueue symv_tiles (every stored element read once, used twice) and then
+// symv_merge (fixed-order sum of the partials, alpha/beta epilogue) on the
+// caller's stream.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <map>
+#include <memory>
+#include <mutex>
+#include <tuple>
+#include <vector>
+
+#include "../../include/xsymv.h"
+#include "xsymv_kernels.hpp"
+
+namespace xsymv {
+
+constexpr int ERR_HIP = 1000;
+
+#define XSYMV_HIP(expr)                                 \
+    do {                                                \
+        hipError_t e_ = (expr);                         \
+        if (e_ != hipSuccess) return ERR_HIP + (int)e_; \
+    } while (0)
+
+// ------------------------------------------------------------ configurations
+struct ConfigInfo {
+    int W, CW, S, H, NT;
+    int NB() const { return W * CW; }
+    int R() const { return S * H; }
+};
+
+template <class T>
+struct KernelSet {
+    void (*lower)(SymvArgs<T>);
+    void (*upper)(SymvArgs<T>);
+    ConfigInfo info;
+};
+
+template <class T, int W, int CW, int S, bool NT>
+KernelSet<T> make_set()
+{
+    return KernelSet<T>{&symv_tiles<T, false, W, CW, S, NT>, &symv_tiles<T, true, W, CW, S, NT>,
+                        ConfigInfo{W, CW, S, 64 * Elem<T>::VEC, NT ? 1 : 0}};
+}
+
+// Defined in the per-precision translation units.
+template <class T> const std::vector<KernelSet<T>>& kernel_sets();
+template <> const std::vector<KernelSet<float>>& kernel_sets<float>();
+template <> const std::vector<KernelSet<double>>& kernel_sets<double>();
+template <> const std::vector<KernelSet<cf32>>& kernel_sets<cf32>();
+template <> const std::vector<KernelSet<cf64>>& kernel_sets<cf64>();
+template <> const std::vector<KernelSet<ddreal>>& kernel_sets<ddreal>();
+
+template <class T> constexpr int prec_code();
+template <> constexpr int prec_code<float>() { return XSYMV_S; }
+template <> constexpr int prec_code<double>() { return XSYMV_D; }
+template <> constexpr int prec_code<cf32>() { return XSYMV_C; }
+template <> constexpr int prec_code<cf64>() { return XSYMV_Z; }
+template <> constexpr int prec_code<ddreal>() { return XSYMV_W; }
+
+// Configuration index for (prec, upper, n): the last matching selection
+// rule, else the built-in default.
+int pick_config(int prec, bool upper, int n);
+
+// --------------------------------------------------------------- tile plans
+struct Plan {
+    int P = 0, NB = 0, ntiles = 0, nslots = 0;
+    TileDesc* d_tiles = nullptr;
+    int* d_slot_base = nullptr;
+    TileDesc* h_tiles = nullptr;  // pinned source of the one upload
+    int* h_slot_base = nullptr;
+};
+
+// Tiles of the panel decomposition (see xsymv_kernels.hpp).  For every panel:
+// the diagonal tile, then the off-diagonal tiles in row order; that is the
+// slot order the merge uses.  Dispatch order: full tiles first, masked
+// (diagonal, ragged) tiles last.
+void build_plan_host(bool upper, int n, int NB, int R, std::vector<TileDesc>& tiles,
+                     std::vector<int>& slot_base, int& P);
+
+struct DeviceState;
+DeviceState* device_state(int dev);
+// Both return 0 or ERR_HIP + hipError_t; the caller holds the state's lock.
+int get_plan(DeviceState* ds, int dev, bool upper, int n, int NB, int R, hipStream_t stream,
+             const Plan** out);
+int get_workspace(DeviceState* ds, hipStream_t stream, size_t bytes, void** out);
+std::mutex& device_mutex(DeviceState* ds);
+
+inline size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Workspace layout: [rowpart P*n][colpart nslots*NB][x gathered, n]
+template <class T>
+size_t workspace_bytes_for(int P, int n, int nslots, int NB)
+{
+    return align_up((size_t)P * n * sizeof(T)) + align_up((size_t)nslots * NB * sizeof(T)) +
+           align_up((size_t)n * sizeof(T));
+}
+
+// ------------------------------------------------------------------- timing
+struct TimedCall {
+    hipEvent_t e0, e1, e2;
+};
+bool timing_enabled();
+void timing_push(const TimedCall& c);
+
+// ---------------------------------------------------------------- checking
+int check_args(char uplo, int n, const void* A, int lda, const void* x, int incx,
+               const void* y, int incy, bool* upper);
+
+inline bool host_is_zero(float a) { return a == 0.0f; }
+inline bool host_is_zero(double a) { return a == 0.0; }
+inline bool host_is_zero(cf32 a) { return a.re == 0.0f && a.im == 0.0f; }
+inline bool host_is_zero(cf64 a) { return a.re == 0.0 && a.im == 0.0; }
+inline bool host_is_zero(ddreal a) { return a.hi == 0.0 && a.lo == 0.0; }
+inline bool host_is_one(float a) { return a == 1.0f; }
+inline bool host_is_one(double a) { return a == 1.0; }
+inline bool host_is_one(cf32 a) { return a.re == 1.0f && a.im == 0.0f; }
+inline bool host_is_one(cf64 a) { return a.re == 1.0 && a.im == 0.0; }
+inline bool host_is_one(ddreal a) { return a.hi == 1.0 && a.lo == 0.0; }
+
+inline unsigned blocks_for(long long n, int per) { return (unsigned)((n + per - 1) / per); }
+
+// --------------------------------------------------------------- the driver
+template <class T>
+int symv_impl(char uplo, int n, T alpha, const T* A, int lda, const T* x, int incx, T beta,
+              T* y, int incy, hipStream_t stream)
+{
+    bool upper = false;
+    int rc = check_args(uplo, n, A, lda, x, incx, y, incy, &upper);
+    if (rc) return rc;
+    if (n == 0 || (host_is_zero(alpha) && host_is_one(beta))) return 0;
+    const long long ky = incy > 0 ? 0 : (long long)(1 - n) * incy;
+    const long long kx = incx > 0 ? 0 : (long long)(1 - n) * incx;
+    const int beta_zero = host_is_zero(beta) ? 1 : 0;
+    if (host_is_zero(alpha)) {
+        symv_scale<T><<<blocks_for(n, 256), 256, 0, stream>>>(y, incy, ky, n, beta, beta_zero);
+        XSYMV_HIP(hipGetLastError());
+        return 0;
+    }
+
+    const int idx = pick_config(prec_code<T>(), upper, n);
+    const KernelSet<T>& ks = kernel_sets<T>()[idx];
+    const int NB = ks.info.NB();
+    const int R = ks.info.R();
+
+    int dev = 0;
+    XSYMV_HIP(hipGetDevice(&dev));
+    DeviceState* ds = device_state(dev);
+    std::lock_guard<std::mutex> lk(device_mutex(ds));
+    const Plan* plan = nullptr;
+    rc = get_plan(ds, dev, upper, n, NB, R, stream, &plan);
+    if (rc) return rc;
+    void* ws = nullptr;
+    rc = get_workspace(ds, stream, workspace_bytes_for<T>(plan->P, n, plan->nslots, NB), &ws);
+    if (rc) return rc;
+    char* base = static_cast<char*>(ws);
+    const size_t off_col = align_up((size_t)plan->P * n * sizeof(T));
+    const size_t off_x = off_col + align_up((size_t)plan->nslots * NB * sizeof(T));
+    T* rowpart = reinterpret_cast<T*>(base);
+    T* colpart = reinterpret_cast<T*>(base + off_col);
+    T* xg = reinterpret_cast<T*>(base + off_x);
+
+    const T* xin = x;
+    if (incx != 1) {
+        symv_gather<T><<<blocks_for(n, 256), 256, 0, stream>>>(x, incx, kx, n, xg);
+        XSYMV_HIP(hipGetLastError());
+        xin = xg;
+    }
+
+    TimedCall tc{};
+    const bool timing = timing_enabled();
+    if (timing) {
+        XSYMV_HIP(hipEventCreate(&tc.e0));
+        XSYMV_HIP(hipEventCreate(&tc.e1));
+        XSYMV_HIP(hipEventCreate(&tc.e2));
+        XSYMV_HIP(hipEventRecord(tc.e0, stream));
+    }
+
+    SymvArgs<T> sa{A, xin, rowpart, colpart, plan->d_tiles, (long long)lda, n};
+    const int threads = 64 * ks.info.W;
+    if (upper)
+        ks.upper<<<plan->ntiles, threads, 0, stream>>>(sa);
+    else
+        ks.lower<<<plan->ntiles, threads, 0, stream>>>(sa);
+    XSYMV_HIP(hipGetLastError());
+    if (timing) XSYMV_HIP(hipEventRecord(tc.e1, stream));
+
+    MergeArgs<T> ma{rowpart, colpart, plan->d_slot_base, y, (long long)incy, ky, alpha, beta,
+                    n, plan->P, NB, upper ? 1 : 0, beta_zero};
+    symv_merge<T><<<blocks_for(n, 64), 256, 0, stream>>>(ma);
+    XSYMV_HIP(hipGetLastError());
+    if (timing) {
+        XSYMV_HIP(hipEventRecord(tc.e2, stream));
+        timing_push(tc);
+    }
+    return 0;
+}
+
+template <class T>
+size_t ws_bytes(char uplo, int n)
+{
+    if (n <= 0) return 0;
+    const bool upper = (uplo == 'U' || uplo == 'u');
+    const ConfigInfo& ci = kernel_sets<T>()[pick_config(prec_code<T>(), upper, n)].info;
+    std::vector<TileDesc> tiles;
+    std::vector<int> sb;
+    int P = 0;
+    build_plan_host(upper, n, ci.NB(), ci.R(), tiles, sb, P);
+    return workspace_bytes_for<T>(P, n, sb[P], ci.NB());
+}
+
+}  // namespace xsymv

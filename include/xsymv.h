@@ -1,0 +1,135 @@
+/*
+ * xsymv.h -- C ABI of the MI355X (gfx950) symmetric / Hermitian matrix-vector
+ * product library (libxsymv.so).
+ *
+ *   y := alpha*S*x + beta*y
+ *
+ * S is an n x n symmetric matrix (xsymv_s, xsymv_d, xsymv_w) or Hermitian
+ * matrix (xhemv_c, xhemv_z) of which only one triangle is stored and read.
+ * The operation is eq.(1) of the CUDA-xSYMV report (Imamura, Mukunoki,
+ * Yamada, Machida; IPSJ SIG Technical Report 2014-HPC-146 No.14, §1), and the
+ * argument list is the BLAS one the report gives for its API (§2.2 Fig. 5),
+ * with the HIP stream appended.  Element types: §2.2 (interleaved complex
+ * pairs for [CZ]HEMV, double-double pairs for WSYMV).
+ *
+ * Arguments (all calls):
+ *   uplo   'U'/'u': the upper triangle of A is stored; 'L'/'l': the lower.
+ *          The other strict triangle is never read (it may hold anything).
+ *   n      order of S, n >= 0.
+ *   alpha, beta  host scalars, by value.
+ *   A      DEVICE pointer, column-major, element (i, j) at A[i + j*lda];
+ *          read only.  For the Hermitian calls the imaginary word of a
+ *          diagonal element is never read (it is taken as zero).
+ *   lda    leading dimension, lda >= max(1, n).
+ *   x      DEVICE pointer, n elements with stride incx (incx != 0; a
+ *          negative stride walks the vector backwards, as in BLAS); read only.
+ *   y      DEVICE pointer, n elements with stride incy (incy != 0); updated
+ *          in place.  With beta == 0 the old y is not read (may hold NaN).
+ *   stream a hipStream_t (NULL = the default stream).
+ *
+ * Ownership: A, x and y belong to the caller and must stay valid until the
+ * work enqueued on `stream` has finished.  The library keeps a device
+ * workspace per (device, stream), allocated on first use and grown as needed
+ * (hipMalloc), never exposed in results.  Calls on one stream are ordered;
+ * calls on different streams use different workspaces.
+ *
+ * Behaviour: every call is asynchronous on `stream` (it enqueues kernels and
+ * returns).  Results are bitwise identical from run to run for the same
+ * inputs, n, uplo and tile configuration: no floating-point atomics are used
+ * and partial sums are combined in a fixed order.  n == 0, or alpha == 0 with
+ * beta == 1, returns without touching y.  alpha == 0 scales y by beta only
+ * (A and x are not read).
+ *
+ * Return codes (checked before any device work; numbering follows the
+ * argument positions, as BLAS xerbla does):
+ *    0  success
+ *   -1  uplo is not one of U, u, L, l
+ *   -2  n < 0
+ *   -4  A is NULL and n > 0
+ *   -5  lda < max(1, n)
+ *   -6  x is NULL and n > 0
+ *   -7  incx == 0
+ *   -9  y is NULL and n > 0
+ *  -10  incy == 0
+ *  1000 + e  the HIP runtime returned error e (hipError_t) on allocation,
+ *            copy or launch.
+ */
+#ifndef XSYMV_H
+#define XSYMV_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct { float re, im; } xcomplex64;   /* layout of float2 */
+typedef struct { double re, im; } xcomplex128; /* layout of double2 */
+typedef struct { double hi, lo; } xdd;         /* value = hi + lo */
+
+/* Precision codes for the helper calls below. */
+enum { XSYMV_S = 0, XSYMV_D = 1, XSYMV_C = 2, XSYMV_Z = 3, XSYMV_W = 4 };
+
+/* SSYMV, DSYMV: real symmetric, float / double (report §2.2 Fig. 5). */
+int xsymv_s(char uplo, int n, float alpha, const float *A, int lda,
+            const float *x, int incx, float beta, float *y, int incy,
+            void *stream);
+int xsymv_d(char uplo, int n, double alpha, const double *A, int lda,
+            const double *x, int incx, double beta, double *y, int incy,
+            void *stream);
+
+/* CHEMV, ZHEMV: complex Hermitian (report §2.2 Fig. 5).  The mirrored
+ * element is the conjugate: S(j,i) = conj(A(i,j)). */
+int xhemv_c(char uplo, int n, xcomplex64 alpha, const xcomplex64 *A, int lda,
+            const xcomplex64 *x, int incx, xcomplex64 beta, xcomplex64 *y,
+            int incy, void *stream);
+int xhemv_z(char uplo, int n, xcomplex128 alpha, const xcomplex128 *A, int lda,
+            const xcomplex128 *x, int incx, xcomplex128 beta, xcomplex128 *y,
+            int incy, void *stream);
+
+/* WSYMV: double-double symmetric (report §2.2 Fig. 4 and Fig. 5).  Inputs
+ * need not be normalised; outputs are (hi, lo) with hi = RN(hi + lo). */
+int xsymv_w(char uplo, int n, xdd alpha, const xdd *A, int lda,
+            const xdd *x, int incx, xdd beta, xdd *y, int incy,
+            void *stream);
+
+/* Bytes of device workspace one call of precision `prec` and order n uses
+ * with the currently selected tile configuration (0 for n == 0; -1 cast to
+ * size_t for a bad precision code). */
+size_t xsymv_workspace_bytes(int prec, char uplo, int n);
+
+/* Release every workspace and cached tile plan of the current device
+ * (synchronises the device first).  Returns 0 or 1000 + hipError_t. */
+int xsymv_release(void);
+
+/* Tile configurations (the autotuner's search space, report §3 Table 1
+ * plays this role for the report's CUDA kernels).  Each precision has a
+ * fixed list of compiled configurations; xsymv_config_info describes entry
+ * `idx`: waves per workgroup, columns per wave, stripes per tile, rows per
+ * stripe, non-temporal loads (0/1).  Returns 0, or -1 for a bad index. */
+int xsymv_num_configs(int prec);
+int xsymv_config_info(int prec, int idx, int *waves, int *cols_per_wave,
+                      int *stripes, int *rows_per_stripe, int *nontemporal);
+
+/* Select the configuration used for precision `prec`, uplo and every n in
+ * [n_lo, n_hi] (later selections take precedence).  idx = -1 restores the
+ * built-in default.  Returns 0 or -1 for bad arguments. */
+int xsymv_select_config(int prec, char uplo, int n_lo, int n_hi, int idx);
+/* Configuration index that a call (prec, uplo, n) would use now. */
+int xsymv_current_config(int prec, char uplo, int n);
+
+/* Kernel timing for measurement: while enabled, every call records HIP
+ * events around its main (tile streaming) kernel and its merge kernel on
+ * its stream.  xsymv_timing_read waits for the recorded events, writes up to
+ * `max` (main_ms, merge_ms) pairs, clears the record and returns how many it
+ * wrote (or 1000 + hipError_t on failure). */
+int xsymv_timing_enable(int on);
+int xsymv_timing_read(float *main_ms, float *merge_ms, int max);
+
+/* Library version string. */
+const char *xsymv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

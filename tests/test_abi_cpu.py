@@ -1,0 +1,82 @@
+"""The C ABI library on the CPU: it loads, exports every function that
+include/xsymv.h declares, and its host logic (argument checks, quick
+returns, configuration tables, tile plans) behaves -- no device work."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import blas_symmetric_mat_amd as X
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "xsymv.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(x(?:symv|hemv)_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    lib = ctypes.CDLL(X.LIB_PATH)
+    names = declared_functions()
+    assert {"xsymv_s", "xsymv_d", "xhemv_c", "xhemv_z", "xsymv_w"} <= set(names)
+    for nm in names:
+        assert hasattr(lib, nm), nm
+
+
+@pytest.mark.parametrize("prec", ["s", "d", "c", "z", "w"])
+def test_argument_errors_before_device_work(prec):
+    f = getattr(X, {"s": "xsymv_s", "d": "xsymv_d", "c": "xhemv_c", "z": "xhemv_z",
+                    "w": "xsymv_w"}[prec])
+    one = (1.0, 0.0) if prec == "w" else 1.0
+    zero = (0.0, 0.0) if prec == "w" else 0.0
+    cases = [(("Q", 4, one, 8, 4, 8, 1, zero, 8, 1), -1),
+             (("L", -3, one, 8, 4, 8, 1, zero, 8, 1), -2),
+             (("U", 4, one, None, 4, 8, 1, zero, 8, 1), -4),
+             (("U", 4, one, 8, 2, 8, 1, zero, 8, 1), -5),
+             (("l", 4, one, 8, 4, None, 1, zero, 8, 1), -6),
+             (("u", 4, one, 8, 4, 8, 0, zero, 8, 1), -7),
+             (("L", 4, one, 8, 4, 8, 1, zero, None, 1), -9),
+             (("L", 4, one, 8, 4, 8, 1, zero, 8, 0), -10),
+             (("L", 0, one, 8, 0, 8, 1, zero, 8, 1), -5)]
+    for args, code in cases:
+        with pytest.raises(X.XsymvError) as e:
+            f(*args, stream=0)
+        assert e.value.code == code
+    # quick returns: n == 0; alpha == 0 and beta == 1 (pointers never touched)
+    f("L", 0, one, None, 1, None, 1, zero, None, 1, stream=0)
+    f("L", 5, zero, 8, 5, 8, 1, one, 8, 1, stream=0)
+
+
+def test_config_tables():
+    for p in "sdczw":
+        k = X.num_configs(p)
+        assert k >= 1
+        for i in range(k):
+            ci = X.config_info(p, i)
+            assert ci["panel"] & (ci["panel"] - 1) == 0
+            assert 64 % ci["cols_per_wave"] == 0
+        with pytest.raises(IndexError):
+            X.config_info(p, k)
+        assert X.current_config(p, "L", 1000) == 0
+    X.select_config("d", "U", 100, 200, 1)
+    assert X.current_config("d", "U", 150) == 1
+    assert X.current_config("d", "U", 201) == 0
+    assert X.current_config("d", "L", 150) == 0
+    X.select_config("d", "U", 100, 200, -1)
+    assert X.current_config("d", "U", 150) == 0
+    with pytest.raises(ValueError):
+        X.select_config("d", "U", 0, 10, 99)
+
+
+def test_workspace_bytes_grow_with_n():
+    a = X.workspace_bytes("d", "L", 1000)
+    b = X.workspace_bytes("d", "L", 4000)
+    assert 0 < a < b
+    assert X.workspace_bytes("d", "L", 0) == 0
+    ci = X.config_info("d", 0)
+    P = (4000 + ci["panel"] - 1) // ci["panel"]
+    assert b >= P * 4000 * 8
