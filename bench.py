@@ -1,0 +1,304 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X SYMV/HEMV/WSYMV library (one GPU).
+
+A step is one call y := alpha*S*x + beta*y of the headline workload: SSYMV,
+uplo = L, n = lda = 32768, A's lower triangle, x and y uniform[-1, 1],
+alpha = beta = 1, seed 32768 (the largest size of the [SD]SYMV sweep).  The
+inputs are resident in HBM before timing starts.  `value` is GFLOPS counted
+as 2n^2 per call, over K timed steps between two device synchronisations.
+
+Printed as one JSON line, with:
+  roofline      the streaming kernel's algorithmic bytes (stored triangle + x)
+                over its average duration, timed with HIP events recorded by
+                the library on the launch stream, against the 8 TB/s HBM peak;
+                `traffic` comes from committed rocprofv3 counter summaries when
+                they were taken on the current kernel source, else null;
+  cpu_baseline  the CPU oracle (single thread) on the same problem;
+  detail        the other workloads (fp64 n = 32768, both triangles, the small
+                and padded cases, CHEMV/ZHEMV n = 16384, WSYMV n = 8192), each
+                timed per call with the library's events and a cache flush
+                between calls when the matrix is below 1 GiB.
+
+Only one GPU is used: --gpus N with N > 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "SYMV GFLOPS (2n^2) and % of peak HBM GB/s at n=32768, fp32/fp64/c/z/DD"
+KERNEL_SOURCES = ["blas_symmetric_mat_amd/csrc/xsymv_kernels.hpp",
+                  "blas_symmetric_mat_amd/csrc/xsymv_arith.hpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+ENTRY = {"s": "xsymv_s", "d": "xsymv_d", "c": "xhemv_c", "z": "xhemv_z", "w": "xsymv_w"}
+DTYPE_NAME = {"s": "f32", "d": "f64", "c": "c64", "z": "c128", "w": "dd (f64 pairs)"}
+
+
+def log(msg):
+    sys.stderr.write(msg + "\n")
+    sys.stderr.flush()
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+class Dev:
+    """A problem resident on the device."""
+
+    def __init__(self, p):
+        import numpy as np
+        import torch
+        self.p = p
+        self.A = torch.from_numpy(np.ascontiguousarray(p.A)).to("cuda")
+        self.x = torch.from_numpy(np.ascontiguousarray(p.x)).to("cuda")
+        self.y0 = torch.from_numpy(np.ascontiguousarray(p.y)).to("cuda")
+        self.y = self.y0.clone()
+        import blas_symmetric_mat_amd as X
+        self.f = getattr(X, ENTRY[p.prec])
+
+    def call(self):
+        p = self.p
+        self.f(p.uplo, p.n, p.alpha, self.A, p.lda, self.x, p.incx, p.beta, self.y, p.incy)
+
+    def reset_y(self):
+        self.y.copy_(self.y0)
+
+
+def beta_is_zero(p):
+    b = p.beta
+    return (b[0] == 0 and b[1] == 0) if isinstance(b, tuple) else complex(b) == 0
+
+
+def time_kernels(d: Dev, reps: int, flush=None):
+    """Per-call (main kernel ms, merge kernel ms) from the library's events."""
+    import torch
+    import blas_symmetric_mat_amd as X
+    torch.cuda.synchronize()
+    X.timing_read()  # drop stale records
+    X.timing_enable(True)
+    try:
+        for _ in range(reps):
+            if flush is not None:
+                flush()
+            d.call()
+        torch.cuda.synchronize()
+        rec = X.timing_read()
+    finally:
+        X.timing_enable(False)
+    return rec
+
+
+def cpu_baseline(p, seconds: float):
+    """The oracle (plain C, one thread) on the same problem, repeated until
+    about ``seconds`` of CPU work."""
+    import oracle
+    from blas_symmetric_mat_amd import roofline as R
+    reps, t_total = 0, 0.0
+    while t_total < seconds or reps == 0:
+        t0 = time.perf_counter()
+        oracle.symv_problem(p)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    t = t_total / reps
+    return {"value": round(R.gflops_2n2(p.n, t), 3), "unit": "GFLOPS", "cores": 1,
+            "kind": "oracle",
+            "sample": f"the full {p.name} problem (same inputs as the GPU run), "
+                      f"{reps} calls, {t:.3f} s each, single-threaded C",
+            "cpu": cpu_model()}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def traffic_record(workload: str):
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = json.load(open(TRAFFIC_FILE)).get(workload)
+    if not rec or rec.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    return rec
+
+
+def measure_detail(name, p, reps, flush):
+    from blas_symmetric_mat_amd import roofline as R
+    import torch
+    log(f"detail: {name}")
+    d = Dev(p)
+    for _ in range(2):
+        d.call()
+    torch.cuda.synchronize()
+    small = p.A.nbytes < (1 << 30)
+    rec = time_kernels(d, reps, flush if small else None)
+    main = sorted(r[0] for r in rec)
+    tot = sorted(r[0] + r[1] for r in rec)
+    t_main = main[len(main) // 2] * 1e-3
+    t_call = tot[len(tot) // 2] * 1e-3
+    bz = beta_is_zero(p)
+    call_b = R.call_bytes(p.prec, p.n, bz)
+    out = {"prec": p.prec, "uplo": p.uplo, "n": p.n, "lda": p.lda,
+           "ms_per_call_median": round(t_call * 1e3, 4),
+           "gflops_2n2": round(R.gflops_2n2(p.n, t_call), 2),
+           "hbm_gbps_algorithmic": round(call_b / t_call / 1e9, 1),
+           "pct_peak_hbm": round(100 * call_b / t_call / 1e9 / R.HBM_PEAK_GBPS, 1),
+           "tile_kernel_gbps": round(R.tile_kernel_bytes(p.prec, p.n) / t_main / 1e9, 1),
+           "flushed_between_calls": small,
+           "calls": reps}
+    if p.prec in ("c", "z"):
+        out["gflops_8n2_real"] = round(4 * R.gflops_2n2(p.n, t_call), 2)
+    del d
+    torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-detail", action="store_true", help="headline workload only")
+    ap.add_argument("--detail-reps", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--pmc-calibrate", action="store_true",
+                    help="also run a plain 1 GiB elementwise copy, for scaling "
+                         "rocprofv3 FETCH_SIZE/WRITE_SIZE readings")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); "
+              f"asked for --gpus {args.gpus}, WORLD_SIZE={world}", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import blas_symmetric_mat_amd as X
+    from blas_symmetric_mat_amd import roofline as R
+    from blas_symmetric_mat_amd import workloads as W
+
+    if not os.path.exists(X.LIB_PATH):
+        from blas_symmetric_mat_amd import build as B
+        B.build()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    props = torch.cuda.get_device_properties(0)
+    log(f"device: {props.name}, {props.multi_processor_count} CUs, {X.version()}")
+
+    # ------------------------------------------------------------- headline
+    t0 = time.perf_counter()
+    p = W.symv_sweep("s", "L", 32768)
+    log(f"headline inputs generated in {time.perf_counter() - t0:.1f} s")
+    d = Dev(p)
+    cfg_idx = X.current_config("s", "L", p.n)
+    for _ in range(args.warmup):
+        d.call()
+    torch.cuda.synchronize()
+    # timed region: K steps between two synchronisations
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        d.call()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    value = R.gflops_2n2(p.n, ms_per_step * 1e-3)
+    call_b = R.call_bytes("s", p.n, False)
+    log(f"headline: {ms_per_step:.4f} ms/step, {value:.1f} GFLOPS, wall {wall:.3f} s")
+
+    # per-kernel durations from the library's events (same stream)
+    rec = time_kernels(d, args.steps)
+    main_ms = float(np.mean([r[0] for r in rec]))
+    merge_ms = float(np.mean([r[1] for r in rec]))
+    kb = R.tile_kernel_bytes("s", p.n)
+    achieved = kb / (main_ms * 1e-3) / 1e9
+    workload = f"ssymv-L-n{p.n}"
+    tr = traffic_record(workload)
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": R.HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(achieved / R.HBM_PEAK_GBPS, 4),
+            "traffic": tr["bytes_per_launch"] if tr else None,
+            "kernel": "symv_tiles<float, lower>", "launch_ms_mean": round(main_ms, 4),
+            "merge_ms_mean": round(merge_ms, 4),
+            "algorithmic_bytes_per_launch": kb}
+    del d
+    torch.cuda.empty_cache()
+
+    out = {"metric": METRIC, "value": round(value, 2), "unit": "GFLOPS", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "f32", "data": "synthetic",
+           "config": {"workload": workload, "n": p.n, "lda": p.lda, "uplo": "L",
+                      "alpha": 1.0, "beta": 1.0, "seed": p.n, "distribution": "uniform[-1,1]",
+                      "tile_config": X.config_info("s", cfg_idx)},
+           "hbm_gbps_algorithmic": round(call_b / (ms_per_step * 1e-3) / 1e9, 1),
+           "pct_peak_hbm": round(100 * call_b / (ms_per_step * 1e-3) / 1e9 / R.HBM_PEAK_GBPS, 2),
+           "roofline": roof}
+
+    # -------------------------------------------------------------- CPU leg
+    if not args.no_cpu:
+        log("cpu baseline (oracle) ...")
+        out["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    del p
+
+    # ------------------------------------------------------------ the rest
+    if not args.no_detail:
+        flush_buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+
+        def flush():
+            flush_buf.fill_(1.0)
+
+        detail = {}
+        cases = [("ssymv-U-n32768", lambda: W.symv_sweep("s", "U", 32768)),
+                 ("dsymv-L-n32768", lambda: W.symv_sweep("d", "L", 32768)),
+                 ("dsymv-U-n32768", lambda: W.symv_sweep("d", "U", 32768)),
+                 ("ssymv-L-n1024", W.ssymv_lower_n1024),
+                 ("dsymv-U-n8192-lda8200-beta0", W.dsymv_upper_n8192_lda8200_beta0),
+                 ("chemv-L-n16384", lambda: W.hemv_lower_n16384("c")),
+                 ("zhemv-L-n16384", lambda: W.hemv_lower_n16384("z")),
+                 ("wsymv-L-n8192", W.wsymv_lower_n8192)]
+        for name, make in cases:
+            detail[name] = measure_detail(name, make(), args.detail_reps, flush)
+        out["detail"] = detail
+        del flush_buf
+
+    if args.pmc_calibrate:
+        # a plain elementwise kernel of known traffic: reads 1 GiB, writes 1 GiB
+        a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        torch.neg(a, out=b)
+        torch.cuda.synchronize()
+        out["pmc_calibration"] = {"kernel": "torch.neg float32", "bytes_read": a.nbytes,
+                                  "bytes_written": b.nbytes}
+
+    out["kernel_source_digest"] = kernel_source_digest()
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -15,6 +15,9 @@
 //   load16(p, out)  VEC consecutive elements, one 16-byte load, dword aligned
 //   shfl_xor(v, m)  exchange with lane ^ m inside a wave64
 //   sel(c, a, b)    c ? a : b, word by word (keeps values in registers)
+//   load_any(p, diag) the element at p; if `diag`, the diagonal value
+//                   (Hermitian: the real word, twice read, never the
+//                   imaginary word) -- branch-free, so loads can be batched
 //
 // Double-double arithmetic is written from the published error-free
 // transformations: Knuth's TwoSum, Dekker's FastTwoSum, TwoProd with one
@@ -72,6 +75,7 @@ template <> struct Elem<float> {
     }
     __device__ static float shfl_xor(float v, int m) { return shfl_xor_f(v, m); }
     __device__ static float sel(bool c, float a, float b) { return c ? a : b; }
+    __device__ static float load_any(const float* p, bool) { return *p; }
     __device__ static bool is_zero(float a) { return a == 0.0f; }
     __device__ static bool is_one(float a) { return a == 1.0f; }
 };
@@ -94,6 +98,7 @@ template <> struct Elem<double> {
     }
     __device__ static double shfl_xor(double v, int m) { return shfl_xor_d(v, m); }
     __device__ static double sel(bool c, double a, double b) { return c ? a : b; }
+    __device__ static double load_any(const double* p, bool) { return *p; }
     __device__ static bool is_zero(double a) { return a == 0.0; }
     __device__ static bool is_one(double a) { return a == 1.0; }
 };
@@ -141,6 +146,12 @@ template <> struct Elem<cf32> {
     {
         return {c ? a.re : b.re, c ? a.im : b.im};
     }
+    __device__ static cf32 load_any(const cf32* p, bool diag)
+    {
+        const float re = p->re;
+        const float im = *(diag ? &p->re : &p->im);
+        return {re, diag ? 0.0f : im};
+    }
     __device__ static bool is_zero(cf32 a) { return a.re == 0.0f && a.im == 0.0f; }
     __device__ static bool is_one(cf32 a) { return a.re == 1.0f && a.im == 0.0f; }
 };
@@ -184,6 +195,12 @@ template <> struct Elem<cf64> {
     __device__ static cf64 sel(bool c, cf64 a, cf64 b)
     {
         return {c ? a.re : b.re, c ? a.im : b.im};
+    }
+    __device__ static cf64 load_any(const cf64* p, bool diag)
+    {
+        const double re = p->re;
+        const double im = *(diag ? &p->re : &p->im);
+        return {re, diag ? 0.0 : im};
     }
     __device__ static bool is_zero(cf64 a) { return a.re == 0.0 && a.im == 0.0; }
     __device__ static bool is_one(cf64 a) { return a.re == 1.0 && a.im == 0.0; }
@@ -245,6 +262,7 @@ template <> struct Elem<ddreal> {
     {
         return {c ? a.hi : b.hi, c ? a.lo : b.lo};
     }
+    __device__ static ddreal load_any(const ddreal* p, bool) { return *p; }
     __device__ static bool is_zero(ddreal a) { return a.hi == 0.0 && a.lo == 0.0; }
     __device__ static bool is_one(ddreal a) { return a.hi == 1.0 && a.lo == 0.0; }
 };

@@ -44,7 +44,7 @@ void build_plan_host(bool upper, int n, int NB, int R, std::vector<TileDesc>& ti
                      std::vector<int>& slot_base, int& P)
 {
     P = (n + NB - 1) / NB;
-    std::vector<TileDesc> full, masked;
+    std::vector<TileDesc> full, other;
     slot_base.assign(P + 1, 0);
     int slot = 0;
     for (int p = 0; p < P; ++p) {
@@ -52,19 +52,21 @@ void build_plan_host(bool upper, int n, int NB, int R, std::vector<TileDesc>& ti
         const int cend = std::min(n, c0 + NB);
         const bool ragged_cols = (cend - c0) != NB;
         slot_base[p] = slot;
-        masked.push_back(TileDesc{p, c0, cend, (slot++ << 2) | TILE_MASKED});
+        other.push_back(TileDesc{p, c0, cend, (slot++ << 2) | TILE_DIAG});
         const int lo = upper ? 0 : cend;
         const int hi = upper ? c0 : n;
         for (int r0 = lo; r0 < hi; r0 += R) {
             const int r1 = std::min(hi, r0 + R);
-            const bool m = ragged_cols || (r1 - r0) != R;
-            TileDesc t{p, r0, r1, (slot++ << 2) | (m ? TILE_MASKED : 0)};
-            (m ? masked : full).push_back(t);
+            const bool rag = ragged_cols || (r1 - r0) != R;
+            TileDesc t{p, r0, r1, (slot++ << 2) | (rag ? TILE_RAGGED : TILE_FULL)};
+            (rag ? other : full).push_back(t);
         }
     }
     slot_base[P] = slot;
-    tiles = full;
-    tiles.insert(tiles.end(), masked.begin(), masked.end());
+    // the short diagonal and ragged tiles first, so that their latency
+    // overlaps the streaming of the full tiles
+    tiles = other;
+    tiles.insert(tiles.end(), full.begin(), full.end());
 }
 
 DeviceState* device_state(int dev)

@@ -26,6 +26,7 @@
 namespace xsymv {
 
 constexpr int ERR_HIP = 1000;
+constexpr int MERGE_SPLIT = 16;  // waves sharing one 64-row block of the merge
 
 #define XSYMV_HIP(expr)                                 \
     do {                                                \
@@ -84,8 +85,8 @@ struct Plan {
 
 // Tiles of the panel decomposition (see xsymv_kernels.hpp).  For every panel:
 // the diagonal tile, then the off-diagonal tiles in row order; that is the
-// slot order the merge uses.  Dispatch order: full tiles first, masked
-// (diagonal, ragged) tiles last.
+// slot order the merge uses.  Dispatch order: diagonal and ragged tiles
+// first, then the full tiles.
 void build_plan_host(bool upper, int n, int NB, int R, std::vector<TileDesc>& tiles,
                      std::vector<int>& slot_base, int& P);
 
@@ -198,7 +199,7 @@ int symv_impl(char uplo, int n, T alpha, const T* A, int lda, const T* x, int in
 
     MergeArgs<T> ma{rowpart, colpart, plan->d_slot_base, y, (long long)incy, ky, alpha, beta,
                     n, plan->P, NB, upper ? 1 : 0, beta_zero};
-    symv_merge<T><<<blocks_for(n, 64), 256, 0, stream>>>(ma);
+    symv_merge<T, MERGE_SPLIT><<<blocks_for(n, 64), 64 * MERGE_SPLIT, 0, stream>>>(ma);
     XSYMV_HIP(hipGetLastError());
     if (timing) {
         XSYMV_HIP(hipEventRecord(tc.e2, stream));

@@ -34,14 +34,16 @@
 
 namespace xsymv {
 
-// One workgroup's tile.  rows [r0, r1), panel p, colpart slot, flags.
+// One workgroup's tile.  rows [r0, r1), panel p, colpart slot, kind.
 struct TileDesc {
     int p;
     int r0;
     int r1;
-    int slot_flags;  // slot << 2 | flags
+    int slot_flags;  // slot << 2 | kind
 };
-enum : int { TILE_MASKED = 1 };
+// Tile kinds: full (R rows, NB columns, strictly off the diagonal), the
+// diagonal block of a panel, or ragged (fewer rows or columns than the shape).
+enum : int { TILE_FULL = 0, TILE_DIAG = 1, TILE_RAGGED = 2 };
 
 template <class T>
 struct SymvArgs {
@@ -118,6 +120,10 @@ __device__ __forceinline__ int wave_transpose_index(int lane)
 //   W      waves per workgroup; CW columns per wave (NB = W*CW)
 //   S      stripes of H = 64*VEC rows per tile (R = S*H)
 //   NT     non-temporal loads for A (streamed once)
+// Every load of A is issued without a data-dependent branch, so the compiler
+// can keep many 16-byte loads in flight per wave.  Elements outside the
+// stored triangle are never loaded: predicated-off lanes load a stored
+// element instead (the diagonal of a valid column) and discard it.
 template <class T, bool UPPER, int W, int CW, int S, bool NT>
 __global__ __launch_bounds__(64 * W) void symv_tiles(SymvArgs<T> args)
 {
@@ -134,7 +140,7 @@ __global__ __launch_bounds__(64 * W) void symv_tiles(SymvArgs<T> args)
     const int r0 = d.r0;
     const int r1 = d.r1;
     const int slot = d.slot_flags >> 2;
-    const bool masked = (d.slot_flags & TILE_MASKED) != 0;
+    const int kind = d.slot_flags & 3;
     const int n = args.n;
     const long long lda = args.lda;
     const int lane = threadIdx.x & 63;
@@ -151,7 +157,9 @@ __global__ __launch_bounds__(64 * W) void symv_tiles(SymvArgs<T> args)
 #pragma unroll
     for (int c = 0; c < CW; ++c) {
         cacc[c] = E::zero();
-        xc[c] = (cw0 + c < n) ? x[cw0 + c] : E::zero();
+        const int col = cw0 + c;
+        const T v = x[col < n ? col : n - 1];
+        xc[c] = E::sel(col < n, v, E::zero());
     }
 #pragma unroll
     for (int s = 0; s < S; ++s) {
@@ -159,12 +167,13 @@ __global__ __launch_bounds__(64 * W) void symv_tiles(SymvArgs<T> args)
         for (int k = 0; k < V; ++k) {
             racc[s][k] = E::zero();
             const int r = r0 + s * H + lane * V + k;
-            xr[s][k] = (r < r1) ? x[r] : E::zero();
+            const T v = x[r < r1 ? r : r1 - 1];
+            xr[s][k] = E::sel(r < r1, v, E::zero());
         }
     }
 
-    if (!masked) {
-        // Full tile: R rows, all NB columns stored, strictly off the diagonal.
+    if (kind == TILE_FULL) {
+        // R rows, all NB columns stored, strictly off the diagonal.
         const T* __restrict__ Ab = A + (long long)cw0 * lda + r0 + lane * V;
 #pragma unroll
         for (int c = 0; c < CW; ++c) {
@@ -179,38 +188,64 @@ __global__ __launch_bounds__(64 * W) void symv_tiles(SymvArgs<T> args)
                 }
             }
         }
-    } else {
-        // Diagonal or ragged tile: element-wise predicates; elements outside
-        // the stored triangle or beyond n are never loaded.  The column loop
-        // is not unrolled (this path is a small share of the work).
-#pragma nounroll
+    } else if (kind == TILE_RAGGED) {
+        // Off the diagonal, but fewer rows than R and/or columns past n.
+        // Whole stripes use 16-byte loads; the one partial stripe uses
+        // element loads at clamped addresses.
+#pragma unroll
         for (int c = 0; c < CW; ++c) {
             const int col = cw0 + c;
-            if (col >= n) break;  // wave-uniform
-            const T* __restrict__ Ac = A + (long long)col * lda;
-            const T xcol = x[col];
-            T csum = E::zero();
+            if (col < n) {  // wave-uniform
+                const T* __restrict__ Ac = A + (long long)col * lda;
+#pragma unroll
+                for (int s = 0; s < S; ++s) {
+                    const int rs = r0 + s * H;
+                    if (rs + H <= r1) {  // workgroup-uniform: a whole stripe
+                        T a[V];
+                        E::template load16<NT>(Ac + rs + lane * V, a);
+#pragma unroll
+                        for (int k = 0; k < V; ++k) {
+                            racc[s][k] = E::mac(racc[s][k], a[k], xc[c]);
+                            cacc[c] = E::macc(cacc[c], a[k], xr[s][k]);
+                        }
+                    } else if (rs < r1) {  // workgroup-uniform: the partial stripe
+#pragma unroll
+                        for (int k = 0; k < V; ++k) {
+                            const int r = rs + lane * V + k;
+                            const T v = Ac[r < r1 ? r : r1 - 1];
+                            const T a = E::sel(r < r1, v, E::zero());
+                            racc[s][k] = E::mac(racc[s][k], a, xc[c]);
+                            cacc[c] = E::macc(cacc[c], a, xr[s][k]);
+                        }
+                    }
+                }
+            }
+        }
+    } else {
+        // The panel's diagonal block: rows and columns [c0, min(n, c0+NB)).
+        // Element (r, col) is stored when r >= col (L) or r <= col (U); the
+        // diagonal element counts once (row role only; Hermitian: real part).
+#pragma unroll
+        for (int c = 0; c < CW; ++c) {
+            const int col = cw0 + c;
+            const bool colok = col < n;               // wave-uniform
+            const int cc = colok ? col : c0;          // a valid column
+            const T* __restrict__ Ac = A + (long long)cc * lda;
 #pragma unroll
             for (int s = 0; s < S; ++s) {
                 if (r0 + s * H < r1) {  // workgroup-uniform
 #pragma unroll
                     for (int k = 0; k < V; ++k) {
                         const int r = r0 + s * H + lane * V + k;
-                        const bool st = (r < r1) && (UPPER ? (r <= col) : (r >= col));
-                        if (st) {
-                            if (r == col) {
-                                racc[s][k] = E::mac(racc[s][k], E::diag_load(Ac + r), xcol);
-                            } else {
-                                const T a = Ac[r];
-                                racc[s][k] = E::mac(racc[s][k], a, xcol);
-                                csum = E::macc(csum, a, xr[s][k]);
-                            }
-                        }
+                        const bool st = colok && r < r1 && (UPPER ? (r <= col) : (r >= col));
+                        const bool dg = (r == col);
+                        const T v = E::load_any(Ac + (st ? r : cc), dg || !st);
+                        const T a = E::sel(st, v, E::zero());
+                        racc[s][k] = E::mac(racc[s][k], a, xc[c]);
+                        cacc[c] = E::macc(cacc[c], E::sel(dg, E::zero(), a), xr[s][k]);
                     }
                 }
             }
-#pragma unroll
-            for (int cc = 0; cc < CW; ++cc) cacc[cc] = E::sel(cc == c, csum, cacc[cc]);
         }
     }
 
@@ -246,9 +281,10 @@ __global__ __launch_bounds__(64 * W) void symv_tiles(SymvArgs<T> args)
 // ---------------------------------------------------------------------------
 // Ordered merge and epilogue: y_i := beta*y_i + alpha*total_i, where total_i
 // adds the row partials of row i in ascending panel order, then the column
-// partials of column i in ascending slot order.  Four waves share a row block:
-// wave g sums the partials k with k % 4 == g (same fixed sequence every run);
-// the four subtotals are then added in wave order.  beta == 0 never reads y.
+// partials of column i in ascending slot order.  SPLIT waves share a block
+// of 64 rows: wave g sums the partials k with k % SPLIT == g (the same fixed
+// sequence every run), and the SPLIT subtotals are then added by a fixed
+// pairwise tree.  beta == 0 never reads y.
 template <class T>
 struct MergeArgs {
     const T* rowpart;
@@ -266,11 +302,11 @@ struct MergeArgs {
     int beta_zero;
 };
 
-template <class T>
-__global__ __launch_bounds__(256) void symv_merge(MergeArgs<T> a)
+template <class T, int SPLIT>
+__global__ __launch_bounds__(64 * SPLIT) void symv_merge(MergeArgs<T> a)
 {
     using E = Elem<T>;
-    __shared__ T part[4][64];
+    __shared__ T part[SPLIT][64];
     const int lane = threadIdx.x & 63;
     const int g = threadIdx.x >> 6;
     const int i = blockIdx.x * 64 + lane;
@@ -284,19 +320,23 @@ __global__ __launch_bounds__(256) void symv_merge(MergeArgs<T> a)
         const int nrow = p_hi - p_lo + 1;
         const int ntot = nrow + (s_hi - s_lo);
         const int ci = i - pi * a.NB;
-        for (int k = g; k < ntot; k += 4) {
-            T v;
-            if (k < nrow)
-                v = a.rowpart[(long long)(p_lo + k) * a.n + i];
-            else
-                v = a.colpart[(long long)(s_lo + k - nrow) * a.NB + ci];
+        const T* __restrict__ rp = a.rowpart + (long long)p_lo * a.n + i;
+        const T* __restrict__ cp = a.colpart + (long long)s_lo * a.NB + ci;
+#pragma unroll 4
+        for (int k = g; k < ntot; k += SPLIT) {
+            const T v = (k < nrow) ? rp[(long long)k * a.n] : cp[(long long)(k - nrow) * a.NB];
             acc = E::add(acc, v);
         }
     }
     part[g][lane] = acc;
     __syncthreads();
+#pragma unroll
+    for (int w = SPLIT / 2; w >= 1; w >>= 1) {
+        if (g < w) part[g][lane] = E::add(part[g][lane], part[g + w][lane]);
+        __syncthreads();
+    }
     if (g == 0 && i < a.n) {
-        T tot = E::add(E::add(part[0][lane], part[1][lane]), E::add(part[2][lane], part[3][lane]));
+        const T tot = part[0][lane];
         T* yp = a.y + a.ky + (long long)i * a.incy;
         T r = E::mul(a.alpha, tot);
         if (!a.beta_zero) r = E::add(r, E::mul(a.beta, *yp));
