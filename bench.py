@@ -169,6 +169,36 @@ def measure_detail(name, p, reps, flush):
     return out
 
 
+def summarize_trace(trace_csv: str, stats_csv: str, command: str) -> str:
+    """Markdown summary of a rocprofv3 --kernel-trace --stats run: every
+    kernel's calls and mean duration from the stats file, and the per-launch
+    durations of each (kernel, grid) pair from the trace (a grid size
+    identifies the workload a launch belonged to)."""
+    import csv
+    import statistics
+    stats = list(csv.DictReader(open(stats_csv)))
+    trace = list(csv.DictReader(open(trace_csv)))
+    out = ["# rocprofv3 kernel trace summary", "", "Command (run from the repository root):", "",
+           "```", command, "```", "", "## Kernel statistics (rocprofv3 --stats)", "",
+           "| kernel | calls | mean us | min us | max us |", "|---|---|---|---|---|"]
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+        out.append(f"| `{r['Name'][:110]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                   f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
+    groups = {}
+    for r in trace:
+        key = (r["Kernel_Name"], int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
+        groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    out += ["", "## Per (kernel, grid) launches from the trace", "",
+            "| kernel | workgroups | threads/wg | launches | mean us | median us |",
+            "|---|---|---|---|---|---|"]
+    for (k, g, wg), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        if "xsymv" not in k:
+            continue
+        out.append(f"| `{k[:90]}` | {g // wg} | {wg} | {len(d)} | {statistics.mean(d):.1f} | "
+                   f"{statistics.median(d):.1f} |")
+    return "\n".join(out) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -179,10 +209,15 @@ def main():
     ap.add_argument("--detail-reps", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--summarize-trace", nargs=3, metavar=("TRACE_CSV", "STATS_CSV", "COMMAND"),
+                    help="print a markdown summary of a rocprofv3 kernel trace and exit")
     ap.add_argument("--pmc-calibrate", action="store_true",
                     help="also run a plain 1 GiB elementwise copy, for scaling "
                          "rocprofv3 FETCH_SIZE/WRITE_SIZE readings")
     args = ap.parse_args()
+    if args.summarize_trace:
+        print(summarize_trace(*args.summarize_trace), end="")
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

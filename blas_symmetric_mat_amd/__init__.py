@@ -21,7 +21,8 @@ import threading
 __all__ = ["xsymv_s", "xsymv_d", "xhemv_c", "xhemv_z", "xsymv_w", "XsymvError",
            "library", "LIB_PATH", "PREC_CODE", "workspace_bytes", "num_configs",
            "config_info", "select_config", "current_config", "timing_enable",
-           "timing_read", "release", "version"]
+           "timing_read", "release", "version", "autotune", "save_config", "load_config",
+           "clear_config"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libxsymv.so")
 PREC_CODE = {"s": 0, "d": 1, "c": 2, "z": 3, "w": 4}
@@ -79,17 +80,24 @@ def library():
             lib.xsymv_num_configs.restype = ci
             lib.xsymv_num_configs.argtypes = [ci]
             ip = ctypes.POINTER(ci)
+            fp = ctypes.POINTER(ctypes.c_float)
             lib.xsymv_config_info.restype = ci
-            lib.xsymv_config_info.argtypes = [ci, ci, ip, ip, ip, ip, ip]
+            lib.xsymv_config_info.argtypes = [ci, ci, ip, ip, ip, ip, ip, ip, ip]
             lib.xsymv_select_config.restype = ci
             lib.xsymv_select_config.argtypes = [ci, cc, ci, ci, ci]
             lib.xsymv_current_config.restype = ci
             lib.xsymv_current_config.argtypes = [ci, cc, ci]
             lib.xsymv_timing_enable.restype = ci
             lib.xsymv_timing_enable.argtypes = [ci]
-            fp = ctypes.POINTER(ctypes.c_float)
             lib.xsymv_timing_read.restype = ci
             lib.xsymv_timing_read.argtypes = [fp, fp, ci]
+            lib.xsymv_autotune.restype = ci
+            lib.xsymv_autotune.argtypes = [ci, cc, ci, ci, ci, ci, vp, ip, fp, ci]
+            for nm in ("xsymv_save_config", "xsymv_load_config"):
+                getattr(lib, nm).restype = ci
+                getattr(lib, nm).argtypes = [ctypes.c_char_p]
+            lib.xsymv_clear_config.restype = ci
+            lib.xsymv_clear_config.argtypes = []
             lib.xsymv_version.restype = ctypes.c_char_p
             lib.xsymv_version.argtypes = []
             _lib = lib
@@ -167,13 +175,14 @@ def num_configs(prec: str) -> int:
 
 
 def config_info(prec: str, idx: int) -> dict:
-    vals = [ctypes.c_int() for _ in range(5)]
+    vals = [ctypes.c_int() for _ in range(7)]
     rc = library().xsymv_config_info(PREC_CODE[prec], idx, *[ctypes.byref(v) for v in vals])
     if rc != 0:
         raise IndexError(idx)
-    w, cw, s, h, nt = (v.value for v in vals)
+    w, cw, s, h, nt, xl, cr = (v.value for v in vals)
     return {"waves": w, "cols_per_wave": cw, "stripes": s, "rows_per_stripe": h,
-            "nontemporal": nt, "panel": w * cw, "tile_rows": s * h}
+            "nontemporal": nt, "x_in_lds": xl, "column_runs": cr, "panel": w * cw,
+            "tile_rows": s * h}
 
 
 def select_config(prec: str, uplo: str, n_lo: int, n_hi: int, idx: int) -> None:
@@ -184,6 +193,42 @@ def select_config(prec: str, uplo: str, n_lo: int, n_hi: int, idx: int) -> None:
 
 def current_config(prec: str, uplo: str, n: int) -> int:
     return library().xsymv_current_config(PREC_CODE[prec], uplo.encode()[:1], n)
+
+
+def autotune(prec: str, uplo: str, n: int, n_lo: int | None = None, n_hi: int | None = None,
+             reps: int = 10, stream=None):
+    """Time every compiled configuration for (prec, uplo, n) on the device,
+    install the fastest for n in [n_lo, n_hi] (default: n only) and return
+    (best index, list of median milliseconds per configuration)."""
+    k = num_configs(prec)
+    ms = (ctypes.c_float * k)()
+    best = ctypes.c_int(-1)
+    n_lo = n if n_lo is None else n_lo
+    n_hi = n if n_hi is None else n_hi
+    rc = library().xsymv_autotune(PREC_CODE[prec], uplo.encode()[:1], n, n_lo, n_hi, reps,
+                                  _stream(stream), ctypes.byref(best), ms, k)
+    if rc != 0:
+        raise XsymvError("xsymv_autotune", rc)
+    return best.value, list(ms)
+
+
+def save_config(path: str) -> None:
+    if library().xsymv_save_config(os.fsencode(path)) != 0:
+        raise OSError(f"cannot write {path}")
+
+
+def load_config(path: str) -> int:
+    """Install the rules of a JSON file; returns how many were installed."""
+    k = library().xsymv_load_config(os.fsencode(path))
+    if k == -1:
+        raise OSError(f"cannot read {path}")
+    if k == -2:
+        raise ValueError(f"malformed rule file {path}")
+    return k
+
+
+def clear_config() -> None:
+    library().xsymv_clear_config()
 
 
 def timing_enable(on: bool) -> None:

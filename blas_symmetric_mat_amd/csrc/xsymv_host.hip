@@ -3,6 +3,12 @@
 // C ABI calls of include/xsymv.h.
 #include "xsymv_host.hpp"
 
+#include <cctype>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
 namespace xsymv {
 
 namespace {
@@ -190,6 +196,77 @@ bool config_info(int prec, int idx, ConfigInfo* out)
     default: return false;
     }
 }
+int find_config(int prec, int W, int CW, int S, int NT, int XL, int RUNS)
+{
+    ConfigInfo ci;
+    for (int i = 0; i < num_configs(prec); ++i)
+        if (config_info(prec, i, &ci) && ci.W == W && ci.CW == CW && ci.S == S && ci.NT == NT &&
+            ci.XLDS == XL && ci.RUNS == RUNS)
+            return i;
+    return -1;
+}
+
+const char PREC_CHARS[5] = {'s', 'd', 'c', 'z', 'w'};
+
+// A minimal reader for the rule files this library writes: a flat list of
+// objects with string or integer values inside the "rules" array.
+struct JsonRule {
+    std::map<std::string, std::string> kv;
+};
+
+bool parse_rules(const std::string& text, std::vector<JsonRule>& out)
+{
+    size_t pos = text.find("\"rules\"");
+    if (pos == std::string::npos) return false;
+    pos = text.find('[', pos);
+    if (pos == std::string::npos) return false;
+    ++pos;
+    auto skip_ws = [&]() {
+        while (pos < text.size() && std::isspace((unsigned char)text[pos])) ++pos;
+    };
+    auto read_string = [&](std::string& v) -> bool {
+        if (pos >= text.size() || text[pos] != '"') return false;
+        size_t e = text.find('"', pos + 1);
+        if (e == std::string::npos) return false;
+        v = text.substr(pos + 1, e - pos - 1);
+        pos = e + 1;
+        return true;
+    };
+    for (;;) {
+        skip_ws();
+        if (pos >= text.size()) return false;
+        if (text[pos] == ']') return true;
+        if (text[pos] == ',') { ++pos; continue; }
+        if (text[pos] != '{') return false;
+        ++pos;
+        JsonRule r;
+        for (;;) {
+            skip_ws();
+            if (pos >= text.size()) return false;
+            if (text[pos] == '}') { ++pos; break; }
+            if (text[pos] == ',') { ++pos; continue; }
+            std::string key, val;
+            if (!read_string(key)) return false;
+            skip_ws();
+            if (pos >= text.size() || text[pos] != ':') return false;
+            ++pos;
+            skip_ws();
+            if (pos < text.size() && text[pos] == '"') {
+                if (!read_string(val)) return false;
+            } else {
+                size_t e = pos;
+                while (e < text.size() && (std::isalnum((unsigned char)text[e]) ||
+                                           text[e] == '-' || text[e] == '+' || text[e] == '.'))
+                    ++e;
+                if (e == pos) return false;
+                val = text.substr(pos, e - pos);
+                pos = e;
+            }
+            r.kv[key] = val;
+        }
+        out.push_back(r);
+    }
+}
 }  // namespace
 
 }  // namespace xsymv
@@ -234,10 +311,12 @@ int xsymv_release(void)
 int xsymv_num_configs(int prec) { return num_configs(prec); }
 
 int xsymv_config_info(int prec, int idx, int* waves, int* cols_per_wave, int* stripes,
-                      int* rows_per_stripe, int* nontemporal)
+                      int* rows_per_stripe, int* nontemporal, int* x_in_lds, int* column_runs)
 {
     ConfigInfo ci;
     if (!config_info(prec, idx, &ci)) return -1;
+    if (x_in_lds) *x_in_lds = ci.XLDS;
+    if (column_runs) *column_runs = ci.RUNS;
     if (waves) *waves = ci.W;
     if (cols_per_wave) *cols_per_wave = ci.CW;
     if (stripes) *stripes = ci.S;
@@ -303,6 +382,101 @@ int xsymv_timing_read(float* main_ms, float* merge_ms, int max)
         (void)hipEventDestroy(c.e2);
     }
     return err ? err : k;
+}
+
+int xsymv_autotune(int prec, char uplo, int n, int n_lo, int n_hi, int reps, void* stream,
+                   int* best_idx, float* ms, int max_cfg)
+{
+    if (prec < 0 || prec > 4 || n_lo > n_hi || n <= 0 || reps <= 0) return -1;
+    if (!(uplo == 'U' || uplo == 'u' || uplo == 'L' || uplo == 'l')) return -1;
+    int best = 0;
+    hipStream_t st = (hipStream_t)stream;
+    int rc;
+    switch (prec) {
+    case XSYMV_S: rc = autotune_for<float>(uplo, n, reps, st, &best, ms, max_cfg); break;
+    case XSYMV_D: rc = autotune_for<double>(uplo, n, reps, st, &best, ms, max_cfg); break;
+    case XSYMV_C: rc = autotune_for<cf32>(uplo, n, reps, st, &best, ms, max_cfg); break;
+    case XSYMV_Z: rc = autotune_for<cf64>(uplo, n, reps, st, &best, ms, max_cfg); break;
+    default: rc = autotune_for<ddreal>(uplo, n, reps, st, &best, ms, max_cfg); break;
+    }
+    if (rc) return rc;
+    if (best_idx) *best_idx = best;
+    return xsymv_select_config(prec, uplo, n_lo, n_hi, best);
+}
+
+int xsymv_save_config(const char* path)
+{
+    if (!path) return -1;
+    FILE* f = std::fopen(path, "w");
+    if (!f) return -1;
+    std::fprintf(f, "{\"library\": \"%s\", \"rules\": [", xsymv_version());
+    bool first = true;
+    {
+        std::lock_guard<std::mutex> lk(g_rules_mu);
+        for (int p = 0; p < 5; ++p)
+            for (int u = 0; u < 2; ++u)
+                for (const Rule& r : g_rules[p][u]) {
+                    ConfigInfo ci;
+                    if (!config_info(p, r.idx, &ci)) continue;
+                    std::fprintf(f,
+                                 "%s\n  {\"prec\": \"%c\", \"uplo\": \"%c\", \"n_lo\": %d, "
+                                 "\"n_hi\": %d, \"waves\": %d, \"cols_per_wave\": %d, "
+                                 "\"stripes\": %d, \"nontemporal\": %d, \"x_in_lds\": %d, "
+                                 "\"column_runs\": %d}",
+                                 first ? "" : ",", PREC_CHARS[p], u ? 'U' : 'L', r.n_lo, r.n_hi,
+                                 ci.W, ci.CW, ci.S, ci.NT, ci.XLDS, ci.RUNS);
+                    first = false;
+                }
+    }
+    std::fprintf(f, "\n]}\n");
+    return std::fclose(f) == 0 ? 0 : -1;
+}
+
+int xsymv_load_config(const char* path)
+{
+    if (!path) return -1;
+    FILE* f = std::fopen(path, "r");
+    if (!f) return -1;
+    std::string text;
+    char buf[4096];
+    size_t k;
+    while ((k = std::fread(buf, 1, sizeof buf, f)) > 0) text.append(buf, k);
+    std::fclose(f);
+    std::vector<JsonRule> rules;
+    if (!parse_rules(text, rules)) return -2;
+    int loaded = 0;
+    for (const JsonRule& r : rules) {
+        auto get = [&](const char* key) -> const std::string* {
+            auto it = r.kv.find(key);
+            return it == r.kv.end() ? nullptr : &it->second;
+        };
+        const std::string *ps = get("prec"), *us = get("uplo");
+        const char* keys[8] = {"n_lo", "n_hi", "waves", "cols_per_wave", "stripes", "nontemporal",
+                               "x_in_lds", "column_runs"};
+        int v[8];
+        bool ok = ps && us && ps->size() == 1 && us->size() == 1;
+        for (int i = 0; i < 8 && ok; ++i) {
+            const std::string* s = get(keys[i]);
+            ok = s != nullptr;
+            if (ok) v[i] = std::atoi(s->c_str());
+        }
+        if (!ok) continue;
+        const char* pc = std::strchr(PREC_CHARS, (*ps)[0]);
+        if (!pc || *pc == 0) continue;
+        const int prec = (int)(pc - PREC_CHARS);
+        const int idx = find_config(prec, v[2], v[3], v[4], v[5], v[6], v[7]);
+        if (idx < 0) continue;
+        if (xsymv_select_config(prec, (*us)[0], v[0], v[1], idx) == 0) ++loaded;
+    }
+    return loaded;
+}
+
+int xsymv_clear_config(void)
+{
+    std::lock_guard<std::mutex> lk(g_rules_mu);
+    for (int p = 0; p < 5; ++p)
+        for (int u = 0; u < 2; ++u) g_rules[p][u].clear();
+    return 0;
 }
 
 const char* xsymv_version(void) { return "xsymv-gfx950 0.1"; }

@@ -36,7 +36,9 @@ constexpr int MERGE_SPLIT = 16;  // waves sharing one 64-row block of the merge
 
 // ------------------------------------------------------------ configurations
 struct ConfigInfo {
-    int W, CW, S, H, NT;
+    int W, CW, S, H, NT, XLDS;
+    int RUNS;  // 0: symv_tiles; 1: symv_runs; 2: symv_runs with the next run
+               // prefetched; 3: symv_block
     int NB() const { return W * CW; }
     int R() const { return S * H; }
 };
@@ -48,11 +50,31 @@ struct KernelSet {
     ConfigInfo info;
 };
 
-template <class T, int W, int CW, int S, bool NT>
+template <class T, int W, int CW, int S, bool NT, bool XLDS>
 KernelSet<T> make_set()
 {
-    return KernelSet<T>{&symv_tiles<T, false, W, CW, S, NT>, &symv_tiles<T, true, W, CW, S, NT>,
-                        ConfigInfo{W, CW, S, 64 * Elem<T>::VEC, NT ? 1 : 0}};
+    return KernelSet<T>{&symv_tiles<T, false, W, CW, S, NT, XLDS>,
+                        &symv_tiles<T, true, W, CW, S, NT, XLDS>,
+                        ConfigInfo{W, CW, S, 64 * Elem<T>::VEC, NT ? 1 : 0, XLDS ? 1 : 0, 0}};
+}
+
+// Block-run configurations: W waves, NB columns, SW stripes per wave, column
+// groups of G.  Reported as cols_per_wave = NB / W and stripes = W * SW so
+// that NB and R come out as for the other families.
+template <class T, int W, int NB, int SW, int G, bool NT>
+KernelSet<T> make_block()
+{
+    return KernelSet<T>{&symv_block<T, false, W, NB, SW, G, NT>,
+                        &symv_block<T, true, W, NB, SW, G, NT>,
+                        ConfigInfo{W, NB / W, W * SW, 64 * Elem<T>::VEC, NT ? 1 : 0, 0, 3}};
+}
+
+template <class T, int W, int CW, int S, bool NT, bool PF>
+KernelSet<T> make_runs()
+{
+    return KernelSet<T>{&symv_runs<T, false, W, CW, S, NT, PF>,
+                        &symv_runs<T, true, W, CW, S, NT, PF>,
+                        ConfigInfo{W, CW, S, 64 * Elem<T>::VEC, NT ? 1 : 0, 1, PF ? 2 : 1}};
 }
 
 // Defined in the per-precision translation units.
@@ -132,10 +154,35 @@ inline bool host_is_one(ddreal a) { return a.hi == 1.0 && a.lo == 0.0; }
 
 inline unsigned blocks_for(long long n, int per) { return (unsigned)((n + per - 1) / per); }
 
-// --------------------------------------------------------------- the driver
+template <class T> T tune_one();
+template <> inline float tune_one<float>() { return 1.0f; }
+template <> inline double tune_one<double>() { return 1.0; }
+template <> inline cf32 tune_one<cf32>() { return {1.0f, 0.0f}; }
+template <> inline cf64 tune_one<cf64>() { return {1.0, 0.0}; }
+template <> inline ddreal tune_one<ddreal>() { return {1.0, 0.0}; }
+template <class T> T tune_zero();
+template <> inline float tune_zero<float>() { return 0.0f; }
+template <> inline double tune_zero<double>() { return 0.0; }
+template <> inline cf32 tune_zero<cf32>() { return {0.0f, 0.0f}; }
+template <> inline cf64 tune_zero<cf64>() { return {0.0, 0.0}; }
+template <> inline ddreal tune_zero<ddreal>() { return {0.0, 0.0}; }
+
+// Autotuner per element type (specialised in the precision units, where the
+// kernels live).
 template <class T>
-int symv_impl(char uplo, int n, T alpha, const T* A, int lda, const T* x, int incx, T beta,
-              T* y, int incy, hipStream_t stream)
+int autotune_for(char uplo, int n, int reps, hipStream_t stream, int* best_idx, float* ms,
+                 int max_cfg);
+template <> int autotune_for<float>(char, int, int, hipStream_t, int*, float*, int);
+template <> int autotune_for<double>(char, int, int, hipStream_t, int*, float*, int);
+template <> int autotune_for<cf32>(char, int, int, hipStream_t, int*, float*, int);
+template <> int autotune_for<cf64>(char, int, int, hipStream_t, int*, float*, int);
+template <> int autotune_for<ddreal>(char, int, int, hipStream_t, int*, float*, int);
+
+// --------------------------------------------------------------- the driver
+// forced_idx >= 0 runs that configuration instead of the selected one.
+template <class T>
+int symv_run(char uplo, int n, T alpha, const T* A, int lda, const T* x, int incx, T beta,
+             T* y, int incy, hipStream_t stream, int forced_idx)
 {
     bool upper = false;
     int rc = check_args(uplo, n, A, lda, x, incx, y, incy, &upper);
@@ -150,7 +197,7 @@ int symv_impl(char uplo, int n, T alpha, const T* A, int lda, const T* x, int in
         return 0;
     }
 
-    const int idx = pick_config(prec_code<T>(), upper, n);
+    const int idx = forced_idx >= 0 ? forced_idx : pick_config(prec_code<T>(), upper, n);
     const KernelSet<T>& ks = kernel_sets<T>()[idx];
     const int NB = ks.info.NB();
     const int R = ks.info.R();
@@ -206,6 +253,128 @@ int symv_impl(char uplo, int n, T alpha, const T* A, int lda, const T* x, int in
         timing_push(tc);
     }
     return 0;
+}
+
+template <class T>
+int symv_impl(char uplo, int n, T alpha, const T* A, int lda, const T* x, int incx, T beta,
+              T* y, int incy, hipStream_t stream)
+{
+    return symv_run<T>(uplo, n, alpha, A, lda, x, incx, beta, y, incy, stream, -1);
+}
+
+// ---------------------------------------------------------------- autotuner
+// Deterministic test data for timing: a counter-based hash of the index
+// mapped to [-1, 1) in every real word.
+__device__ __forceinline__ double tune_value(unsigned long long i)
+{
+    unsigned long long z = i + 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    return (double)(z >> 11) * (2.0 / 9007199254740992.0) - 1.0;
+}
+template <class T> __device__ T tune_elem(unsigned long long i);
+template <> __device__ inline float tune_elem<float>(unsigned long long i) { return (float)tune_value(i); }
+template <> __device__ inline double tune_elem<double>(unsigned long long i) { return tune_value(i); }
+template <> __device__ inline cf32 tune_elem<cf32>(unsigned long long i)
+{
+    return {(float)tune_value(2 * i), (float)tune_value(2 * i + 1)};
+}
+template <> __device__ inline cf64 tune_elem<cf64>(unsigned long long i)
+{
+    return {tune_value(2 * i), tune_value(2 * i + 1)};
+}
+template <> __device__ inline ddreal tune_elem<ddreal>(unsigned long long i)
+{
+    const double h = tune_value(2 * i);
+    return {h, h * tune_value(2 * i + 1) * 0x1p-53};
+}
+
+template <class T>
+__global__ __launch_bounds__(256) void tune_fill(T* a, long long count, unsigned long long seed)
+{
+    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < count;
+         i += (long long)gridDim.x * 256)
+        a[i] = tune_elem<T>(seed + (unsigned long long)i);
+}
+
+// Flush the caches (L2, MALL) between timed calls: write a 1 GiB buffer.
+static __global__ __launch_bounds__(256) void tune_flush(uint32_t* buf, long long words)
+{
+    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < words;
+         i += (long long)gridDim.x * 256)
+        buf[i] = (uint32_t)i;
+}
+
+// Time every configuration of T for (uplo, n): `reps` calls each (after two
+// warm-up calls), each preceded by a cache flush when the matrix is smaller
+// than 1 GiB; the configuration with the lowest median wins, ties going to
+// the lower index.  ms[i] receives configuration i's median (up to max_cfg).
+template <class T>
+int autotune_impl(char uplo, int n, int reps, hipStream_t stream, int* best_idx, float* ms,
+                  int max_cfg)
+{
+    if (n <= 0 || reps <= 0 || !(uplo == 'U' || uplo == 'u' || uplo == 'L' || uplo == 'l'))
+        return -1;
+    const long long lda = n;
+    const size_t abytes = (size_t)lda * n * sizeof(T);
+    T *A = nullptr, *x = nullptr, *y = nullptr;
+    uint32_t* fl = nullptr;
+    const long long flush_words = (1ll << 30) / 4;
+    const bool flush = abytes < ((size_t)1 << 30);
+    int rc = 0;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    const auto& sets = kernel_sets<T>();
+    std::vector<float> med(sets.size(), 0.f);
+    auto fail = [&](hipError_t e) { rc = ERR_HIP + (int)e; };
+    hipError_t e;
+    if ((e = hipMalloc((void**)&A, abytes)) != hipSuccess) { fail(e); goto done; }
+    if ((e = hipMalloc((void**)&x, n * sizeof(T))) != hipSuccess) { fail(e); goto done; }
+    if ((e = hipMalloc((void**)&y, n * sizeof(T))) != hipSuccess) { fail(e); goto done; }
+    if (flush && (e = hipMalloc((void**)&fl, flush_words * 4)) != hipSuccess) { fail(e); goto done; }
+    if ((e = hipEventCreate(&e0)) != hipSuccess || (e = hipEventCreate(&e1)) != hipSuccess) {
+        fail(e);
+        goto done;
+    }
+    tune_fill<T><<<4096, 256, 0, stream>>>(A, lda * n, 1);
+    tune_fill<T><<<64, 256, 0, stream>>>(x, n, 1ull << 40);
+    tune_fill<T><<<64, 256, 0, stream>>>(y, n, 1ull << 41);
+    for (size_t ci = 0; ci < sets.size(); ++ci) {
+        std::vector<float> t;
+        for (int r = 0; r < reps + 2 && rc == 0; ++r) {
+            if (flush) tune_flush<<<2048, 256, 0, stream>>>(fl, flush_words);
+            if ((e = hipEventRecord(e0, stream)) != hipSuccess) { fail(e); break; }
+            // alpha = 1, beta = 0: y is overwritten, never grows
+            rc = symv_run<T>(uplo, n, tune_one<T>(), A, (int)lda, x, 1, tune_zero<T>(), y, 1,
+                             stream, (int)ci);
+            if (rc) break;
+            if ((e = hipEventRecord(e1, stream)) != hipSuccess) { fail(e); break; }
+            if ((e = hipEventSynchronize(e1)) != hipSuccess) { fail(e); break; }
+            float v = 0.f;
+            if ((e = hipEventElapsedTime(&v, e0, e1)) != hipSuccess) { fail(e); break; }
+            if (r >= 2) t.push_back(v);
+        }
+        if (rc) goto done;
+        std::sort(t.begin(), t.end());
+        med[ci] = t[t.size() / 2];
+    }
+    {
+        size_t best = 0;
+        for (size_t ci = 1; ci < sets.size(); ++ci)
+            if (med[ci] < med[best]) best = ci;
+        if (best_idx) *best_idx = (int)best;
+        for (size_t ci = 0; ci < sets.size() && (int)ci < max_cfg; ++ci)
+            if (ms) ms[ci] = med[ci];
+    }
+done:
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    (void)hipStreamSynchronize(stream);
+    if (A) (void)hipFree(A);
+    if (x) (void)hipFree(x);
+    if (y) (void)hipFree(y);
+    if (fl) (void)hipFree(fl);
+    return rc;
 }
 
 template <class T>

@@ -115,16 +115,42 @@ __device__ __forceinline__ int wave_transpose_index(int lane)
 }
 
 // ---------------------------------------------------------------------------
+// Element (r, col) of a diagonal or ragged tile, branch-free so that every
+// load of a column can be in flight at once.  `cc` is a valid column (col
+// itself when col < n); an element outside the stored triangle or outside
+// [.., r1) is not loaded: the lane loads the stored diagonal element (cc, cc)
+// instead and the value is discarded by a select (never by a multiply, so
+// NaN or Inf there cannot leak).  The diagonal element of a Hermitian matrix
+// is its real part.  Returns the value for the row role; *off is the value
+// for the column role (zero on the diagonal, which counts once).
+template <class T, bool UPPER>
+__device__ __forceinline__ T masked_elem(const T* __restrict__ Acc, int r, int r1, int col,
+                                         int cc, bool colok, bool diag, T* off)
+{
+    using E = Elem<T>;
+    const bool in = colok && r < r1 && (!diag || (UPPER ? (r <= col) : (r >= col)));
+    const bool dg = diag && (r == col);
+    const T v = E::load_any(Acc + (in ? r : cc), dg || !in);
+    const T a = E::sel(in, v, E::zero());
+    *off = E::sel(dg, E::zero(), a);
+    return a;
+}
+
+// ---------------------------------------------------------------------------
 // Main streaming kernel.  Template parameters:
 //   T      element type; UPPER: stored triangle
 //   W      waves per workgroup; CW columns per wave (NB = W*CW)
-//   S      stripes of H = 64*VEC rows per tile (R = S*H)
+//   S      stripes of H = 64*VEC rows per tile (R = S*H): each wave reads
+//          every one of its columns as one contiguous run of R rows
 //   NT     non-temporal loads for A (streamed once)
+//   XLDS   keep the tile's x rows in LDS (one 16-byte LDS read per 16-byte
+//          load of A) instead of registers, so that long runs (large S) do
+//          not cost occupancy
 // Every load of A is issued without a data-dependent branch, so the compiler
 // can keep many 16-byte loads in flight per wave.  Elements outside the
 // stored triangle are never loaded: predicated-off lanes load a stored
 // element instead (the diagonal of a valid column) and discard it.
-template <class T, bool UPPER, int W, int CW, int S, bool NT>
+template <class T, bool UPPER, int W, int CW, int S, bool NT, bool XLDS>
 __global__ __launch_bounds__(64 * W) void symv_tiles(SymvArgs<T> args)
 {
     using E = Elem<T>;
@@ -133,6 +159,7 @@ __global__ __launch_bounds__(64 * W) void symv_tiles(SymvArgs<T> args)
     constexpr int R = S * H;
     constexpr int NB = W * CW;
 
+    // x rows of the tile while streaming (XLDS), then the waves' row partials
     __shared__ T red[W][R];
 
     const TileDesc d = args.tiles[blockIdx.x];
@@ -152,7 +179,7 @@ __global__ __launch_bounds__(64 * W) void symv_tiles(SymvArgs<T> args)
 
     T racc[S][V];
     T cacc[CW];
-    T xr[S][V];
+    T xreg[XLDS ? 1 : S][V];
     T xc[CW];
 #pragma unroll
     for (int c = 0; c < CW; ++c) {
@@ -162,15 +189,38 @@ __global__ __launch_bounds__(64 * W) void symv_tiles(SymvArgs<T> args)
         xc[c] = E::sel(col < n, v, E::zero());
     }
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
+    for (int s = 0; s < S; ++s)
 #pragma unroll
-        for (int k = 0; k < V; ++k) {
-            racc[s][k] = E::zero();
-            const int r = r0 + s * H + lane * V + k;
+        for (int k = 0; k < V; ++k) racc[s][k] = E::zero();
+    if constexpr (XLDS) {
+        T* xs = &red[0][0];
+        for (int i = threadIdx.x; i < R; i += 64 * W) {
+            const int r = r0 + i;
             const T v = x[r < r1 ? r : r1 - 1];
-            xr[s][k] = E::sel(r < r1, v, E::zero());
+            xs[i] = E::sel(r < r1, v, E::zero());
         }
+        __syncthreads();
+    } else {
+#pragma unroll
+        for (int s = 0; s < S; ++s)
+#pragma unroll
+            for (int k = 0; k < V; ++k) {
+                const int r = r0 + s * H + lane * V + k;
+                const T v = x[r < r1 ? r : r1 - 1];
+                xreg[XLDS ? 0 : s][k] = E::sel(r < r1, v, E::zero());
+            }
     }
+    // x at the rows of stripe s for this lane
+    auto xrow = [&](int s, T (&xv)[V]) {
+        if constexpr (XLDS) {
+            const T* xs = &red[0][0] + s * H + lane * V;
+#pragma unroll
+            for (int k = 0; k < V; ++k) xv[k] = xs[k];
+        } else {
+#pragma unroll
+            for (int k = 0; k < V; ++k) xv[k] = xreg[XLDS ? 0 : s][k];
+        }
+    };
 
     if (kind == TILE_FULL) {
         // R rows, all NB columns stored, strictly off the diagonal.
@@ -179,71 +229,37 @@ __global__ __launch_bounds__(64 * W) void symv_tiles(SymvArgs<T> args)
         for (int c = 0; c < CW; ++c) {
 #pragma unroll
             for (int s = 0; s < S; ++s) {
-                T a[V];
+                T a[V], xv[V];
                 E::template load16<NT>(Ab + c * lda + s * H, a);
+                xrow(s, xv);
 #pragma unroll
                 for (int k = 0; k < V; ++k) {
                     racc[s][k] = E::mac(racc[s][k], a[k], xc[c]);
-                    cacc[c] = E::macc(cacc[c], a[k], xr[s][k]);
-                }
-            }
-        }
-    } else if (kind == TILE_RAGGED) {
-        // Off the diagonal, but fewer rows than R and/or columns past n.
-        // Whole stripes use 16-byte loads; the one partial stripe uses
-        // element loads at clamped addresses.
-#pragma unroll
-        for (int c = 0; c < CW; ++c) {
-            const int col = cw0 + c;
-            if (col < n) {  // wave-uniform
-                const T* __restrict__ Ac = A + (long long)col * lda;
-#pragma unroll
-                for (int s = 0; s < S; ++s) {
-                    const int rs = r0 + s * H;
-                    if (rs + H <= r1) {  // workgroup-uniform: a whole stripe
-                        T a[V];
-                        E::template load16<NT>(Ac + rs + lane * V, a);
-#pragma unroll
-                        for (int k = 0; k < V; ++k) {
-                            racc[s][k] = E::mac(racc[s][k], a[k], xc[c]);
-                            cacc[c] = E::macc(cacc[c], a[k], xr[s][k]);
-                        }
-                    } else if (rs < r1) {  // workgroup-uniform: the partial stripe
-#pragma unroll
-                        for (int k = 0; k < V; ++k) {
-                            const int r = rs + lane * V + k;
-                            const T v = Ac[r < r1 ? r : r1 - 1];
-                            const T a = E::sel(r < r1, v, E::zero());
-                            racc[s][k] = E::mac(racc[s][k], a, xc[c]);
-                            cacc[c] = E::macc(cacc[c], a, xr[s][k]);
-                        }
-                    }
+                    cacc[c] = E::macc(cacc[c], a[k], xv[k]);
                 }
             }
         }
     } else {
-        // The panel's diagonal block: rows and columns [c0, min(n, c0+NB)).
-        // Element (r, col) is stored when r >= col (L) or r <= col (U); the
-        // diagonal element counts once (row role only; Hermitian: real part).
+        // Diagonal block or ragged tile (fewer rows, or columns past n):
+        // element loads at clamped addresses, all issued without branches.
+        const bool diag = (kind == TILE_DIAG);
 #pragma unroll
         for (int c = 0; c < CW; ++c) {
             const int col = cw0 + c;
-            const bool colok = col < n;               // wave-uniform
-            const int cc = colok ? col : c0;          // a valid column
-            const T* __restrict__ Ac = A + (long long)cc * lda;
+            const bool colok = col < n;
+            const int cc = colok ? col : c0;  // c0 < n always
+            const T* __restrict__ Acc = A + (long long)cc * lda;
 #pragma unroll
             for (int s = 0; s < S; ++s) {
-                if (r0 + s * H < r1) {  // workgroup-uniform
+                T xv[V];
+                xrow(s, xv);
 #pragma unroll
-                    for (int k = 0; k < V; ++k) {
-                        const int r = r0 + s * H + lane * V + k;
-                        const bool st = colok && r < r1 && (UPPER ? (r <= col) : (r >= col));
-                        const bool dg = (r == col);
-                        const T v = E::load_any(Ac + (st ? r : cc), dg || !st);
-                        const T a = E::sel(st, v, E::zero());
-                        racc[s][k] = E::mac(racc[s][k], a, xc[c]);
-                        cacc[c] = E::macc(cacc[c], E::sel(dg, E::zero(), a), xr[s][k]);
-                    }
+                for (int k = 0; k < V; ++k) {
+                    T off;
+                    const T a = masked_elem<T, UPPER>(Acc, r0 + s * H + lane * V + k, r1, col,
+                                                      cc, colok, diag, &off);
+                    racc[s][k] = E::mac(racc[s][k], a, xc[c]);
+                    cacc[c] = E::macc(cacc[c], off, xv[k]);
                 }
             }
         }
@@ -260,6 +276,7 @@ __global__ __launch_bounds__(64 * W) void symv_tiles(SymvArgs<T> args)
     }
 
     // Row role: add the W waves' partials in wave order through LDS.
+    if constexpr (XLDS) __syncthreads();  // every wave is done with the x rows
 #pragma unroll
     for (int s = 0; s < S; ++s)
 #pragma unroll
@@ -275,6 +292,294 @@ __global__ __launch_bounds__(64 * W) void symv_tiles(SymvArgs<T> args)
             for (int w = 1; w < W; ++w) sum = E::add(sum, red[w][i]);
             rp[r] = sum;
         }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Column-run kernel: the same tiles and partials as symv_tiles, organised so
+// that registers do not grow with the panel width.  Each wave walks its CW
+// columns one at a time; a column's R tile rows are one contiguous run of S
+// 16-byte loads per lane, and the next column's run is loaded while the
+// current one is used.  The tile's x rows sit in LDS.  A column's sum
+// (column role) is finished right away by a fixed 64-lane butterfly, so the
+// only long-lived accumulators are the S*VEC row partials.
+template <class T>
+__device__ __forceinline__ T wave_sum(T v, int lane)
+{
+    using E = Elem<T>;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        const T got = E::shfl_xor(v, m);
+        const bool up = (lane & m) != 0;
+        v = E::add(E::sel(up, got, v), E::sel(up, v, got));
+    }
+    return v;
+}
+
+template <class T, bool UPPER, int W, int CW, int S, bool NT, bool PF>
+__global__ __launch_bounds__(64 * W) void symv_runs(SymvArgs<T> args)
+{
+    using E = Elem<T>;
+    constexpr int V = E::VEC;
+    constexpr int H = 64 * V;
+    constexpr int R = S * H;
+    constexpr int NB = W * CW;
+
+    // x rows of the tile while streaming, then the waves' row partials
+    __shared__ T red[W][R];
+
+    const TileDesc d = args.tiles[blockIdx.x];
+    const int p = d.p;
+    const int r0 = d.r0;
+    const int r1 = d.r1;
+    const int slot = d.slot_flags >> 2;
+    const int kind = d.slot_flags & 3;
+    const int n = args.n;
+    const long long lda = args.lda;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c0 = p * NB;
+    const int cw0 = c0 + wave * CW;  // first column of this wave
+    const T* __restrict__ A = args.A;
+    const T* __restrict__ x = args.x;
+    T* __restrict__ colout = args.colpart + (long long)slot * NB + wave * CW;
+
+    T racc[S][V];
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+        for (int k = 0; k < V; ++k) racc[s][k] = E::zero();
+    {
+        T* xs = &red[0][0];
+        for (int i = threadIdx.x; i < R; i += 64 * W) {
+            const int r = r0 + i;
+            const T v = x[r < r1 ? r : r1 - 1];
+            xs[i] = E::sel(r < r1, v, E::zero());
+        }
+        __syncthreads();
+    }
+    const T* xs_lane = &red[0][0] + lane * V;
+
+    if (kind == TILE_FULL) {
+        // R rows, all NB columns stored, strictly off the diagonal.
+        const T* __restrict__ Ab = A + (long long)cw0 * lda + r0 + lane * V;
+        T cur[S][V];
+        T xcol = x[cw0];
+        if constexpr (PF) {
+#pragma unroll
+            for (int s = 0; s < S; ++s) E::template load16<NT>(Ab + s * H, cur[s]);
+        }
+#pragma unroll 1
+        for (int c = 0; c < CW; ++c) {
+            T nxt[PF ? S : 1][V];
+            const int cn = (c + 1 < CW) ? c + 1 : c;  // wave-uniform
+            if constexpr (PF) {
+                const T* __restrict__ An = Ab + (long long)cn * lda;
+#pragma unroll
+                for (int s = 0; s < S; ++s) E::template load16<NT>(An + s * H, nxt[s]);
+            } else {
+                const T* __restrict__ Ac = Ab + (long long)c * lda;
+#pragma unroll
+                for (int s = 0; s < S; ++s) E::template load16<NT>(Ac + s * H, cur[s]);
+            }
+            const T xnext = x[cw0 + cn];
+            T csum = E::zero();
+            // x is re-read from LDS for every column: an opaque offset keeps
+            // the compiler from hoisting it into S*VEC registers for the loop
+            int xoff = 0;
+            asm volatile("" : "+v"(xoff));
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+#pragma unroll
+                for (int k = 0; k < V; ++k) {
+                    racc[s][k] = E::mac(racc[s][k], cur[s][k], xcol);
+                    csum = E::macc(csum, cur[s][k], xs_lane[xoff + s * H + k]);
+                }
+            }
+            csum = wave_sum(csum, lane);
+            if (lane == 0) colout[c] = csum;
+            if constexpr (PF) {
+#pragma unroll
+                for (int s = 0; s < S; ++s)
+#pragma unroll
+                    for (int k = 0; k < V; ++k) cur[s][k] = nxt[PF ? s : 0][k];
+            }
+            xcol = xnext;
+        }
+    } else {
+        // Diagonal block or ragged tile: element loads at clamped addresses,
+        // all issued without branches.
+        const bool diag = (kind == TILE_DIAG);
+#pragma unroll 1
+        for (int c = 0; c < CW; ++c) {
+            const int col = cw0 + c;
+            const bool colok = col < n;
+            const int cc = colok ? col : c0;
+            const T* __restrict__ Acc = A + (long long)cc * lda;
+            const T xcol = E::sel(colok, x[cc], E::zero());
+            T csum = E::zero();
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+#pragma unroll
+                for (int k = 0; k < V; ++k) {
+                    T off;
+                    const T a = masked_elem<T, UPPER>(Acc, r0 + s * H + lane * V + k, r1, col,
+                                                      cc, colok, diag, &off);
+                    racc[s][k] = E::mac(racc[s][k], a, xcol);
+                    csum = E::macc(csum, off, xs_lane[s * H + k]);
+                }
+            }
+            csum = wave_sum(csum, lane);
+            if (lane == 0) colout[c] = csum;
+        }
+    }
+
+    // Row role: add the W waves' partials in wave order through LDS.
+    __syncthreads();  // every wave is done with the x rows
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+        for (int k = 0; k < V; ++k)
+            red[wave][s * H + lane * V + k] = racc[s][k];
+    __syncthreads();
+    T* __restrict__ rp = args.rowpart + (long long)p * n;
+    for (int i = threadIdx.x; i < R; i += 64 * W) {
+        const int r = r0 + i;
+        if (r < r1) {
+            T sum = red[0][i];
+#pragma unroll
+            for (int w = 1; w < W; ++w) sum = E::add(sum, red[w][i]);
+            rp[r] = sum;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Block-run kernel.  The W waves of a block walk the tile's NB columns
+// together, one column (group) at a time; for each column, wave w reads its
+// own SW stripes (SW*H rows) right below wave w-1's, so the block as a whole
+// reads one contiguous run of W*SW*H rows per column.  Consequences:
+//  * a wave owns its rows for the whole tile, so its row partials stay in
+//    SW*VEC registers and are written straight to rowpart (no cross-wave
+//    row reduction);
+//  * column sums are finished per group of G consecutive columns by a fixed
+//    lane exchange (wave_transpose_reduce), parked in LDS per wave, and added
+//    across the W waves in wave order at the end of the tile.
+// Tile shape: NB columns x R = W*SW*H rows.
+template <class T, bool UPPER, int W, int NB, int SW, int G, bool NT>
+__global__ __launch_bounds__(64 * W) void symv_block(SymvArgs<T> args)
+{
+    using E = Elem<T>;
+    constexpr int V = E::VEC;
+    constexpr int H = 64 * V;
+    static_assert(NB % G == 0, "column groups must tile the panel");
+
+    __shared__ T colred[W][NB];
+
+    const TileDesc d = args.tiles[blockIdx.x];
+    const int p = d.p;
+    const int r0 = d.r0;
+    const int r1 = d.r1;
+    const int slot = d.slot_flags >> 2;
+    const int kind = d.slot_flags & 3;
+    const int n = args.n;
+    const long long lda = args.lda;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c0 = p * NB;
+    const int rw = r0 + wave * SW * H;  // first row of this wave
+    const T* __restrict__ A = args.A;
+    const T* __restrict__ x = args.x;
+
+    T racc[SW][V];
+    T xr[SW][V];
+#pragma unroll
+    for (int s = 0; s < SW; ++s)
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+            racc[s][k] = E::zero();
+            const int r = rw + s * H + lane * V + k;
+            const T v = x[r < r1 ? r : r1 - 1];
+            xr[s][k] = E::sel(r < r1, v, E::zero());
+        }
+
+    if (kind == TILE_FULL) {
+        const T* __restrict__ Ab = A + (long long)c0 * lda + rw + lane * V;
+#pragma unroll 1
+        for (int cg = 0; cg < NB; cg += G) {
+            T cacc[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const int c = cg + g;
+                T a[SW][V];
+#pragma unroll
+                for (int s = 0; s < SW; ++s)
+                    E::template load16<NT>(Ab + (long long)c * lda + s * H, a[s]);
+                const T xcol = x[c0 + c];
+                cacc[g] = E::zero();
+#pragma unroll
+                for (int s = 0; s < SW; ++s)
+#pragma unroll
+                    for (int k = 0; k < V; ++k) {
+                        racc[s][k] = E::mac(racc[s][k], a[s][k], xcol);
+                        cacc[g] = E::macc(cacc[g], a[s][k], xr[s][k]);
+                    }
+            }
+            wave_transpose_reduce<T, G>(cacc, lane);
+            constexpr int GROUP = 64 / G;
+            if ((lane & (GROUP - 1)) == 0)
+                colred[wave][cg + wave_transpose_index<G>(lane)] = cacc[0];
+        }
+    } else {
+        // Diagonal block or ragged tile: element loads at clamped addresses,
+        // all issued without branches.
+        const bool diag = (kind == TILE_DIAG);
+#pragma unroll 1
+        for (int cg = 0; cg < NB; cg += G) {
+            T cacc[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const int col = c0 + cg + g;
+                const bool colok = col < n;
+                const int cc = colok ? col : c0;
+                const T* __restrict__ Acc = A + (long long)cc * lda;
+                const T xcol = E::sel(colok, x[cc], E::zero());
+                cacc[g] = E::zero();
+#pragma unroll
+                for (int s = 0; s < SW; ++s) {
+#pragma unroll
+                    for (int k = 0; k < V; ++k) {
+                        T off;
+                        const T a = masked_elem<T, UPPER>(Acc, rw + s * H + lane * V + k, r1,
+                                                          col, cc, colok, diag, &off);
+                        racc[s][k] = E::mac(racc[s][k], a, xcol);
+                        cacc[g] = E::macc(cacc[g], off, xr[s][k]);
+                    }
+                }
+            }
+            wave_transpose_reduce<T, G>(cacc, lane);
+            constexpr int GROUP = 64 / G;
+            if ((lane & (GROUP - 1)) == 0)
+                colred[wave][cg + wave_transpose_index<G>(lane)] = cacc[0];
+        }
+    }
+
+    // Row role: this wave's rows are complete.
+    T* __restrict__ rp = args.rowpart + (long long)p * n;
+#pragma unroll
+    for (int s = 0; s < SW; ++s)
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+            const int r = rw + s * H + lane * V + k;
+            if (r < r1) rp[r] = racc[s][k];
+        }
+    // Column role: add the waves' sums in wave order.
+    __syncthreads();
+    for (int c = threadIdx.x; c < NB; c += 64 * W) {
+        T sum = colred[0][c];
+#pragma unroll
+        for (int w = 1; w < W; ++w) sum = E::add(sum, colred[w][c]);
+        args.colpart[(long long)slot * NB + c] = sum;
     }
 }
 

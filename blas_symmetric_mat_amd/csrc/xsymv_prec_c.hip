@@ -4,13 +4,23 @@
 namespace xsymv {
 template <> const std::vector<KernelSet<cf32>>& kernel_sets<cf32>()
 {
+    // index 0 is the built-in default (fastest streaming kernel measured on MI355X
+    // at the largest benchmark size of this precision)
     static const std::vector<KernelSet<cf32>> v = {
-        make_set<cf32, 4, 16, 4, true>(),   // NB 64,  R 512
-        make_set<cf32, 4, 8, 8, true>(),    // NB 32,  R 1024
-        make_set<cf32, 8, 16, 4, true>(),   // NB 128, R 512
-        make_set<cf32, 4, 16, 4, false>(),  // cached loads
+        make_set<cf32, 8, 16, 4, true, false>(),          // tiles: NB 128, R 512
+        make_block<cf32, 8, 128, 1, 4, true>(),           // block: NB 128, R 1024, 8 KB runs
+        make_block<cf32, 4, 128, 2, 4, true>(),           // block: NB 128, R 1024, 8 KB runs
+        make_set<cf32, 4, 16, 4, true, false>(),          // tiles: NB 64, R 512
+        make_runs<cf32, 4, 16, 8, true, true>(),          // runs: NB 64, R 1024, prefetch
     };
     return v;
+}
+
+template <>
+int autotune_for<cf32>(char uplo, int n, int reps, hipStream_t stream, int* best_idx, float* ms,
+                      int max_cfg)
+{
+    return autotune_impl<cf32>(uplo, n, reps, stream, best_idx, ms, max_cfg);
 }
 }  // namespace xsymv
 

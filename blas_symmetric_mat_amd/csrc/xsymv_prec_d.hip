@@ -4,14 +4,24 @@
 namespace xsymv {
 template <> const std::vector<KernelSet<double>>& kernel_sets<double>()
 {
+    // index 0 is the built-in default (fastest streaming kernel measured on MI355X
+    // at the largest benchmark size of this precision)
     static const std::vector<KernelSet<double>> v = {
-        make_set<double, 4, 16, 4, true>(),   // NB 64,  R 512
-        make_set<double, 4, 16, 8, true>(),   // NB 64,  R 1024
-        make_set<double, 4, 32, 4, true>(),   // NB 128, R 512
-        make_set<double, 8, 16, 4, true>(),   // NB 128, R 512
-        make_set<double, 4, 16, 4, false>(),  // cached loads
+        make_block<double, 4, 128, 2, 4, false>(),        // block: NB 128, R 1024, 8 KB runs, cached
+        make_block<double, 4, 256, 2, 4, true>(),         // block: NB 256, R 1024, 8 KB runs
+        make_set<double, 4, 16, 4, false, false>(),       // tiles: NB 64, R 512, cached
+        make_runs<double, 4, 16, 8, true, true>(),        // runs: NB 64, R 1024, prefetch
+        make_block<double, 4, 128, 2, 4, true>(),         // block: NB 128, R 1024, 8 KB runs
+        make_set<double, 8, 16, 2, false, false>(),       // tiles: NB 128, R 256, cached
     };
     return v;
+}
+
+template <>
+int autotune_for<double>(char uplo, int n, int reps, hipStream_t stream, int* best_idx, float* ms,
+                      int max_cfg)
+{
+    return autotune_impl<double>(uplo, n, reps, stream, best_idx, ms, max_cfg);
 }
 }  // namespace xsymv
 

@@ -4,14 +4,24 @@
 namespace xsymv {
 template <> const std::vector<KernelSet<float>>& kernel_sets<float>()
 {
+    // index 0 is the built-in default (fastest streaming kernel measured on MI355X
+    // at the largest benchmark size of this precision)
     static const std::vector<KernelSet<float>> v = {
-        make_set<float, 4, 16, 4, true>(),   // NB 64,  R 1024
-        make_set<float, 4, 16, 2, true>(),   // NB 64,  R 512
-        make_set<float, 4, 32, 2, true>(),   // NB 128, R 512
-        make_set<float, 8, 16, 4, true>(),   // NB 128, R 1024
-        make_set<float, 4, 16, 4, false>(),  // cached loads
+        make_set<float, 8, 16, 2, true, false>(),         // tiles: NB 128, R 512
+        make_block<float, 4, 128, 2, 4, true>(),          // block: NB 128, R 2048, 8 KB runs
+        make_set<float, 4, 16, 4, true, false>(),         // tiles: NB 64, R 1024
+        make_block<float, 4, 64, 2, 4, true>(),           // block: NB 64, R 2048, 8 KB runs
+        make_block<float, 8, 128, 1, 4, true>(),          // block: NB 128, R 2048, 8 KB runs
+        make_runs<float, 4, 16, 8, true, true>(),         // runs: NB 64, R 2048, prefetch
     };
     return v;
+}
+
+template <>
+int autotune_for<float>(char uplo, int n, int reps, hipStream_t stream, int* best_idx, float* ms,
+                      int max_cfg)
+{
+    return autotune_impl<float>(uplo, n, reps, stream, best_idx, ms, max_cfg);
 }
 }  // namespace xsymv
 

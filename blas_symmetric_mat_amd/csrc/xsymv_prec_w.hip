@@ -4,13 +4,23 @@
 namespace xsymv {
 template <> const std::vector<KernelSet<ddreal>>& kernel_sets<ddreal>()
 {
+    // index 0 is the built-in default (fastest streaming kernel measured on MI355X
+    // at the largest benchmark size of this precision)
     static const std::vector<KernelSet<ddreal>> v = {
-        make_set<ddreal, 4, 8, 4, true>(),   // NB 32, R 256
-        make_set<ddreal, 4, 4, 8, true>(),   // NB 16, R 512
-        make_set<ddreal, 8, 8, 4, true>(),   // NB 64, R 256
-        make_set<ddreal, 4, 8, 4, false>(),  // cached loads
+        make_set<ddreal, 4, 8, 4, true, false>(),         // tiles: NB 32, R 256
+        make_runs<ddreal, 4, 16, 8, true, true>(),        // runs: NB 64, R 512, prefetch
+        make_block<ddreal, 4, 64, 2, 4, true>(),          // block: NB 64, R 512, 8 KB runs
+        make_set<ddreal, 8, 8, 4, true, false>(),         // tiles: NB 64, R 256
+        make_block<ddreal, 4, 128, 2, 4, true>(),         // block: NB 128, R 512, 8 KB runs
     };
     return v;
+}
+
+template <>
+int autotune_for<ddreal>(char uplo, int n, int reps, hipStream_t stream, int* best_idx, float* ms,
+                      int max_cfg)
+{
+    return autotune_impl<ddreal>(uplo, n, reps, stream, best_idx, ms, max_cfg);
 }
 }  // namespace xsymv
 

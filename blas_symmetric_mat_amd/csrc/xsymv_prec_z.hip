@@ -4,13 +4,23 @@
 namespace xsymv {
 template <> const std::vector<KernelSet<cf64>>& kernel_sets<cf64>()
 {
+    // index 0 is the built-in default (fastest streaming kernel measured on MI355X
+    // at the largest benchmark size of this precision)
     static const std::vector<KernelSet<cf64>> v = {
-        make_set<cf64, 4, 8, 8, true>(),    // NB 32, R 512
-        make_set<cf64, 4, 16, 4, true>(),   // NB 64, R 256
-        make_set<cf64, 8, 8, 8, true>(),    // NB 64, R 512
-        make_set<cf64, 4, 8, 8, false>(),   // cached loads
+        make_block<cf64, 4, 128, 2, 4, false>(),          // block: NB 128, R 512, 8 KB runs, cached
+        make_set<cf64, 8, 8, 8, false, true>(),           // tiles: NB 64, R 512, cached, x in LDS
+        make_block<cf64, 4, 128, 2, 4, true>(),           // block: NB 128, R 512, 8 KB runs
+        make_set<cf64, 4, 8, 8, true, false>(),           // tiles: NB 32, R 512
+        make_runs<cf64, 4, 16, 8, false, true>(),         // runs: NB 64, R 512, cached, prefetch
     };
     return v;
+}
+
+template <>
+int autotune_for<cf64>(char uplo, int n, int reps, hipStream_t stream, int* best_idx, float* ms,
+                      int max_cfg)
+{
+    return autotune_impl<cf64>(uplo, n, reps, stream, best_idx, ms, max_cfg);
 }
 }  // namespace xsymv
 

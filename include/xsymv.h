@@ -106,10 +106,14 @@ int xsymv_release(void);
  * plays this role for the report's CUDA kernels).  Each precision has a
  * fixed list of compiled configurations; xsymv_config_info describes entry
  * `idx`: waves per workgroup, columns per wave, stripes per tile, rows per
- * stripe, non-temporal loads (0/1).  Returns 0, or -1 for a bad index. */
+ * stripe, non-temporal loads of A (0/1), x rows staged in LDS (0/1), and the
+ * kernel family (1: each wave walks its columns one contiguous run at a time
+ * with the next run prefetched; 0: the whole tile unrolled).  Any output
+ * pointer may be NULL.  Returns 0, or -1 for a bad index. */
 int xsymv_num_configs(int prec);
 int xsymv_config_info(int prec, int idx, int *waves, int *cols_per_wave,
-                      int *stripes, int *rows_per_stripe, int *nontemporal);
+                      int *stripes, int *rows_per_stripe, int *nontemporal,
+                      int *x_in_lds, int *column_runs);
 
 /* Select the configuration used for precision `prec`, uplo and every n in
  * [n_lo, n_hi] (later selections take precedence).  idx = -1 restores the
@@ -117,6 +121,32 @@ int xsymv_config_info(int prec, int idx, int *waves, int *cols_per_wave,
 int xsymv_select_config(int prec, char uplo, int n_lo, int n_hi, int idx);
 /* Configuration index that a call (prec, uplo, n) would use now. */
 int xsymv_current_config(int prec, char uplo, int n);
+
+/* Autotuner (the report's §3 tunes its CUDA kernels offline per GPU; this
+ * is the on-device counterpart).  On the current device and `stream`, time
+ * every compiled configuration of `prec` for (uplo, n) on device-generated
+ * data: two warm-up calls, then `reps` timed calls each (HIP events; caches
+ * flushed before each call when the matrix is under 1 GiB).  The lowest
+ * median wins (ties: the lower index) and is installed for every n in
+ * [n_lo, n_hi], as xsymv_select_config does.  Allocates, uses and frees
+ * n*n elements of matrix plus vectors (and a 1 GiB flush buffer for small
+ * matrices); synchronises `stream`.  best_idx and ms (median per
+ * configuration, at most max_cfg entries) may be NULL.  Returns 0, -1 for a
+ * bad argument, or 1000 + hipError_t. */
+int xsymv_autotune(int prec, char uplo, int n, int n_lo, int n_hi, int reps,
+                   void *stream, int *best_idx, float *ms, int max_cfg);
+
+/* Selection rules as a JSON file: {"library": ..., "rules": [{"prec": "s",
+ * "uplo": "L", "n_lo": .., "n_hi": .., "waves": .., "cols_per_wave": ..,
+ * "stripes": .., "nontemporal": .., "x_in_lds": .., "column_runs": ..},
+ * ...]}.  Rules are matched to compiled
+ * configurations by shape.  save: 0 or -1 (cannot write).  load: number of
+ * rules installed (appended after the current ones, so they take
+ * precedence), -1 (cannot read) or -2 (malformed).  clear: drop every rule
+ * (back to the built-in defaults). */
+int xsymv_save_config(const char *path);
+int xsymv_load_config(const char *path);
+int xsymv_clear_config(void);
 
 /* Kernel timing for measurement: while enabled, every call records HIP
  * events around its main (tile streaming) kernel and its merge kernel on
