@@ -199,6 +199,40 @@ def summarize_trace(trace_csv: str, stats_csv: str, command: str) -> str:
     return "\n".join(out) + "\n"
 
 
+def summarize_pmc(fetch_csv: str, write_csv: str, command: str, workload: str) -> dict:
+    """Per-launch HBM traffic of the streaming kernel from two rocprofv3 --pmc
+    runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what
+    the same counter reads for the plain 1 GiB elementwise kernel that
+    `--pmc-calibrate` runs (1 GiB read + 1 GiB written)."""
+    import csv
+    import statistics
+
+    def per_kernel(path):
+        agg = {}
+        for r in csv.DictReader(open(path)):
+            agg.setdefault((r["Kernel_Name"], int(r["Grid_Size"])), []).append(
+                float(r["Counter_Value"]))
+        return agg
+
+    f, w = per_kernel(fetch_csv), per_kernel(write_csv)
+    calib = [k for k in f if "neg_kernel" in k[0]]
+    if len(calib) != 1:
+        raise ValueError("calibration kernel not found exactly once")
+    gib = float(1 << 30)
+    fetch_scale = gib / (statistics.mean(f[calib[0]]) * 1024)
+    write_scale = gib / (statistics.mean(w[calib[0]]) * 1024)
+    mains = [k for k in f if "xsymv::symv_" in k[0] and "merge" not in k[0]]
+    main = max(mains, key=lambda k: statistics.mean(f[k]))
+    fb = statistics.mean(f[main]) * 1024 * fetch_scale
+    wb = statistics.mean(w[main]) * 1024 * write_scale
+    return {workload: {"kernel": main[0], "grid_threads": main[1],
+                       "fetch_bytes_per_launch": round(fb), "write_bytes_per_launch": round(wb),
+                       "bytes_per_launch": round(fb + wb),
+                       "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4),
+                       "launches": len(f[main]), "kernel_source_digest": kernel_source_digest(),
+                       "command": command}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -211,12 +245,24 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--summarize-trace", nargs=3, metavar=("TRACE_CSV", "STATS_CSV", "COMMAND"),
                     help="print a markdown summary of a rocprofv3 kernel trace and exit")
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"),
+                    help="write profiles/traffic_counters.json from two rocprofv3 --pmc "
+                         "runs of the headline workload and exit")
     ap.add_argument("--pmc-calibrate", action="store_true",
                     help="also run a plain 1 GiB elementwise copy, for scaling "
                          "rocprofv3 FETCH_SIZE/WRITE_SIZE readings")
     args = ap.parse_args()
     if args.summarize_trace:
         print(summarize_trace(*args.summarize_trace), end="")
+        return
+    if args.summarize_pmc:
+        rec = summarize_pmc(*args.summarize_pmc, workload="ssymv-L-n32768")
+        old = json.load(open(TRAFFIC_FILE)) if os.path.exists(TRAFFIC_FILE) else {}
+        old.update(rec)
+        with open(TRAFFIC_FILE, "w") as fh:
+            json.dump(old, fh, indent=1)
+            fh.write("\n")
+        print(json.dumps(rec, indent=1))
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
