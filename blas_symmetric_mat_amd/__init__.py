@@ -22,7 +22,7 @@ __all__ = ["xsymv_s", "xsymv_d", "xhemv_c", "xhemv_z", "xsymv_w", "XsymvError",
            "library", "LIB_PATH", "PREC_CODE", "workspace_bytes", "num_configs",
            "config_info", "select_config", "current_config", "timing_enable",
            "timing_read", "release", "version", "autotune", "save_config", "load_config",
-           "clear_config"]
+           "clear_config", "strip_plan", "config_workgroups"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libxsymv.so")
 PREC_CODE = {"s": 0, "d": 1, "c": 2, "z": 3, "w": 4}
@@ -98,6 +98,10 @@ def library():
                 getattr(lib, nm).argtypes = [ctypes.c_char_p]
             lib.xsymv_clear_config.restype = ci
             lib.xsymv_clear_config.argtypes = []
+            lib.xsymv_config_workgroups.restype = ci
+            lib.xsymv_config_workgroups.argtypes = [ci, ci, cc]
+            lib.xsymv_strip_plan.restype = ci
+            lib.xsymv_strip_plan.argtypes = [cc, ci, ci, ci, ip, ci, ip, ip, ci]
             lib.xsymv_version.restype = ctypes.c_char_p
             lib.xsymv_version.argtypes = []
             _lib = lib
@@ -244,6 +248,27 @@ def timing_read(max_calls: int = 4096):
     if k >= 1000:
         raise XsymvError("xsymv_timing_read", k)
     return [(a[i], b[i]) for i in range(k)]
+
+
+def config_workgroups(prec: str, idx: int, uplo: str = "L") -> int:
+    """Workgroups a row-strip configuration is launched with (0 otherwise)."""
+    return library().xsymv_config_workgroups(PREC_CODE[prec], idx, uplo.encode()[:1])
+
+
+def strip_plan(uplo: str, n: int, R: int, G: int):
+    """The row-strip work split (host computation): (blocks [G x 4]:
+    first, end, first slot, first strip), strip_base [NS+1], seg_base [NS+1]."""
+    import numpy as np
+    ns = (n + R - 1) // R
+    blocks = np.zeros((G, 4), dtype=np.int32)
+    sb = np.zeros(ns + 1, dtype=np.int32)
+    segb = np.zeros(ns + 1, dtype=np.int32)
+    ip = ctypes.POINTER(ctypes.c_int)
+    k = library().xsymv_strip_plan(uplo.encode()[:1], n, R, G, blocks.ctypes.data_as(ip), G,
+                                    sb.ctypes.data_as(ip), segb.ctypes.data_as(ip), ns + 1)
+    if k < 0:
+        raise ValueError(f"xsymv_strip_plan failed ({k})")
+    return blocks[:k], sb, segb
 
 
 def release() -> None:

@@ -27,10 +27,14 @@ std::mutex g_dev_mu;
 
 using PlanKey = std::tuple<int, int, int, int, int>;  // upper, n, NB, R, device
 
+using StripKey = std::tuple<int, int, int, int>;  // upper, n, R, G
+
 struct DeviceState {
     std::mutex mu;
     std::map<PlanKey, std::unique_ptr<Plan>> plans;
+    std::map<StripKey, std::unique_ptr<StripPlan>> strip_plans;
     std::map<hipStream_t, std::pair<void*, size_t>> workspaces;
+    std::map<std::pair<const void*, int>, int> resident;  // (kernel, threads) -> blocks
 };
 
 namespace {
@@ -73,6 +77,66 @@ void build_plan_host(bool upper, int n, int NB, int R, std::vector<TileDesc>& ti
     // overlaps the streaming of the full tiles
     tiles = other;
     tiles.insert(tiles.end(), full.begin(), full.end());
+}
+
+void build_strip_plan_host(bool upper, int n, int R, int G, std::vector<StripBlock>& blocks,
+                           std::vector<int>& strip_base, std::vector<int>& seg_base, int& NS)
+{
+    NS = (n + R - 1) / R;
+    strip_base.assign(NS + 1, 0);
+    for (int i = 0; i < NS; ++i) {
+        const int width = upper ? n - i * R : std::min(n, (i + 1) * R);
+        strip_base[i + 1] = strip_base[i] + width;
+    }
+    const long long total_pos = strip_base[NS];
+    // cost of one column of a strip: the strip's rows (a workgroup's waves
+    // each read their own rows of the column), with columns of the diagonal
+    // triangle weighted by DIAG_COST/4 (one wave there takes the element-load
+    // path), plus a fixed per-column share for the reductions
+    const long long OVH = 16;
+    const long long DIAG_COST = 8;
+    std::vector<long long> prefix(total_pos + 1, 0);
+    long long pos = 0;
+    for (int i = 0; i < NS; ++i) {
+        const int rs0 = i * R, rs1 = std::min(n, rs0 + R), rows = rs1 - rs0;
+        const int cfirst = upper ? rs0 : 0;
+        for (int t = 0; t < strip_base[i + 1] - strip_base[i]; ++t, ++pos) {
+            const int j = cfirst + t;
+            const bool tri = upper ? (j < rs1) : (j >= rs0);
+            const long long c = tri ? rows * DIAG_COST / 4 : rows;
+            prefix[pos + 1] = prefix[pos] + c + OVH;
+        }
+    }
+    const long long C = prefix[total_pos];
+    G = std::max(1, (int)std::min<long long>(G, total_pos));
+    blocks.assign(G, StripBlock{0, 0, 0, 0});
+    std::vector<long long> bound(G + 1, 0);
+    bound[G] = total_pos;
+    for (int b = 1; b < G; ++b) {
+        // first position whose prefix cost reaches b*C/G
+        const long long target = (C * (long long)b) / G;
+        bound[b] = std::lower_bound(prefix.begin(), prefix.end(), target) - prefix.begin();
+        bound[b] = std::max(bound[b], bound[b - 1]);
+        bound[b] = std::min(bound[b], total_pos);
+    }
+    seg_base.assign(NS + 1, 0);
+    int slot = 0;
+    int strip = 0;
+    std::vector<int> first_slot(NS, -1);
+    for (int b = 0; b < G; ++b) {
+        const int u0 = (int)bound[b], u1 = (int)bound[b + 1];
+        while (strip < NS - 1 && strip_base[strip + 1] <= u0) ++strip;
+        blocks[b] = StripBlock{u0, u1, slot, strip};
+        int u = u0, st = strip;
+        while (u < u1) {
+            if (first_slot[st] < 0) first_slot[st] = slot;
+            u = std::min(u1, strip_base[st + 1]);
+            ++slot;
+            ++st;
+        }
+    }
+    for (int i = 0; i < NS; ++i) seg_base[i] = first_slot[i];
+    seg_base[NS] = slot;
 }
 
 DeviceState* device_state(int dev)
@@ -118,6 +182,65 @@ int get_plan(DeviceState* ds, int dev, bool upper, int n, int NB, int R, hipStre
     XSYMV_HIP(hipStreamSynchronize(stream));
     *out = plan.get();
     ds->plans[key] = std::move(plan);
+    return 0;
+}
+
+int resident_blocks(const void* kernel, int threads, int* out)
+{
+    int dev = 0;
+    XSYMV_HIP(hipGetDevice(&dev));
+    DeviceState* ds = device_state(dev);
+    auto key = std::make_pair(kernel, threads);
+    auto it = ds->resident.find(key);
+    if (it != ds->resident.end()) {
+        *out = it->second;
+        return 0;
+    }
+    int per_cu = 0, cus = 0;
+    XSYMV_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0));
+    XSYMV_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+    *out = std::max(1, per_cu) * std::max(1, cus);
+    ds->resident[key] = *out;
+    return 0;
+}
+
+int get_strip_plan(DeviceState* ds, int dev, bool upper, int n, int R, int G, hipStream_t stream,
+                   const StripPlan** out)
+{
+    (void)dev;
+    StripKey key{upper ? 1 : 0, n, R, G};
+    auto it = ds->strip_plans.find(key);
+    if (it != ds->strip_plans.end()) {
+        *out = it->second.get();
+        return 0;
+    }
+    std::vector<StripBlock> blocks;
+    std::vector<int> sb, segb;
+    int NS = 0;
+    int g = G;
+    build_strip_plan_host(upper, n, R, g, blocks, sb, segb, NS);
+    std::unique_ptr<StripPlan> plan(new StripPlan());
+    plan->NS = NS;
+    plan->G = (int)blocks.size();
+    plan->nseg = segb[NS];
+    plan->R = R;
+    const size_t bb = blocks.size() * sizeof(StripBlock);
+    const size_t ib = sb.size() * sizeof(int);
+    char* h = nullptr;
+    XSYMV_HIP(hipHostMalloc((void**)&h, bb + 2 * ib, hipHostMallocDefault));
+    plan->h_pinned = h;
+    std::copy(blocks.begin(), blocks.end(), reinterpret_cast<StripBlock*>(h));
+    std::copy(sb.begin(), sb.end(), reinterpret_cast<int*>(h + bb));
+    std::copy(segb.begin(), segb.end(), reinterpret_cast<int*>(h + bb + ib));
+    char* d = nullptr;
+    XSYMV_HIP(hipMalloc((void**)&d, bb + 2 * ib));
+    XSYMV_HIP(hipMemcpyAsync(d, h, bb + 2 * ib, hipMemcpyHostToDevice, stream));
+    XSYMV_HIP(hipStreamSynchronize(stream));
+    plan->d_blocks = reinterpret_cast<StripBlock*>(d);
+    plan->d_strip_base = reinterpret_cast<int*>(d + bb);
+    plan->d_seg_base = reinterpret_cast<int*>(d + bb + ib);
+    *out = plan.get();
+    ds->strip_plans[key] = std::move(plan);
     return 0;
 }
 
@@ -305,6 +428,11 @@ int xsymv_release(void)
         XSYMV_HIP(hipHostFree(p->h_slot_base));
     }
     ds->plans.clear();
+    for (auto& kv : ds->strip_plans) {
+        XSYMV_HIP(hipFree(kv.second->d_blocks));
+        XSYMV_HIP(hipHostFree(kv.second->h_pinned));
+    }
+    ds->strip_plans.clear();
     return 0;
 }
 
@@ -477,6 +605,56 @@ int xsymv_clear_config(void)
     for (int p = 0; p < 5; ++p)
         for (int u = 0; u < 2; ++u) g_rules[p][u].clear();
     return 0;
+}
+
+int xsymv_config_workgroups(int prec, int idx, char uplo)
+{
+    const bool upper = (uplo == 'U' || uplo == 'u');
+    const void* k = nullptr;
+    int threads = 0;
+    switch (prec) {
+#define XSYMV_K(T)                                                                       \
+    {                                                                                    \
+        if (idx < 0 || idx >= (int)kernel_sets<T>().size()) return -1;                   \
+        const auto& ks = kernel_sets<T>()[idx];                                          \
+        if (ks.info.RUNS != 4) return 0;                                                 \
+        k = (const void*)(upper ? ks.strip_upper : ks.strip_lower);                      \
+        threads = 64 * ks.info.W;                                                        \
+        break;                                                                           \
+    }
+    case XSYMV_S: XSYMV_K(float)
+    case XSYMV_D: XSYMV_K(double)
+    case XSYMV_C: XSYMV_K(cf32)
+    case XSYMV_Z: XSYMV_K(cf64)
+    case XSYMV_W: XSYMV_K(ddreal)
+#undef XSYMV_K
+    default: return -1;
+    }
+    int G = 0;
+    const int rc = resident_blocks(k, threads, &G);
+    return rc ? -rc : G;
+}
+
+int xsymv_strip_plan(char uplo, int n, int R, int G, int* blocks4, int max_blocks,
+                     int* strip_base, int* seg_base, int max_strips)
+{
+    if (!(uplo == 'U' || uplo == 'u' || uplo == 'L' || uplo == 'l') || n <= 0 || R <= 0 ||
+        G <= 0)
+        return -1;
+    std::vector<StripBlock> blocks;
+    std::vector<int> sb, segb;
+    int NS = 0;
+    build_strip_plan_host(uplo == 'U' || uplo == 'u', n, R, G, blocks, sb, segb, NS);
+    if ((int)blocks.size() > max_blocks || NS + 1 > max_strips) return -2;
+    for (size_t b = 0; b < blocks.size(); ++b) {
+        blocks4[4 * b + 0] = blocks[b].u0;
+        blocks4[4 * b + 1] = blocks[b].u1;
+        blocks4[4 * b + 2] = blocks[b].slot0;
+        blocks4[4 * b + 3] = blocks[b].strip0;
+    }
+    std::copy(sb.begin(), sb.end(), strip_base);
+    std::copy(segb.begin(), segb.end(), seg_base);
+    return (int)blocks.size();
 }
 
 const char* xsymv_version(void) { return "xsymv-gfx950 0.1"; }

@@ -22,11 +22,13 @@
 
 #include "../../include/xsymv.h"
 #include "xsymv_kernels.hpp"
+#include "xsymv_strip.hpp"
 
 namespace xsymv {
 
 constexpr int ERR_HIP = 1000;
 constexpr int MERGE_SPLIT = 16;  // waves sharing one 64-row block of the merge
+constexpr int STRIP_CBUF = 256;  // columns a strip workgroup buffers before adding waves
 
 #define XSYMV_HIP(expr)                                 \
     do {                                                \
@@ -38,7 +40,8 @@ constexpr int MERGE_SPLIT = 16;  // waves sharing one 64-row block of the merge
 struct ConfigInfo {
     int W, CW, S, H, NT, XLDS;
     int RUNS;  // 0: symv_tiles; 1: symv_runs; 2: symv_runs with the next run
-               // prefetched; 3: symv_block
+               // prefetched; 3: symv_block; 4: symv_strip (CW = column group,
+               // S = W * stripes per wave)
     int NB() const { return W * CW; }
     int R() const { return S * H; }
 };
@@ -48,6 +51,8 @@ struct KernelSet {
     void (*lower)(SymvArgs<T>);
     void (*upper)(SymvArgs<T>);
     ConfigInfo info;
+    void (*strip_lower)(StripArgs<T>) = nullptr;  // strip family only
+    void (*strip_upper)(StripArgs<T>) = nullptr;
 };
 
 template <class T, int W, int CW, int S, bool NT, bool XLDS>
@@ -67,6 +72,17 @@ KernelSet<T> make_block()
     return KernelSet<T>{&symv_block<T, false, W, NB, SW, G, NT>,
                         &symv_block<T, true, W, NB, SW, G, NT>,
                         ConfigInfo{W, NB / W, W * SW, 64 * Elem<T>::VEC, NT ? 1 : 0, 0, 3}};
+}
+
+// Row-strip, evenly split configurations: W waves, SW stripes per wave,
+// column groups of G.
+template <class T, int W, int SW, int G, bool NT>
+KernelSet<T> make_strip()
+{
+    KernelSet<T> k{nullptr, nullptr, ConfigInfo{W, G, W * SW, 64 * Elem<T>::VEC, NT ? 1 : 0, 0, 4}};
+    k.strip_lower = &symv_strip<T, false, W, SW, G, NT, STRIP_CBUF>;
+    k.strip_upper = &symv_strip<T, true, W, SW, G, NT, STRIP_CBUF>;
+    return k;
 }
 
 template <class T, int W, int CW, int S, bool NT, bool PF>
@@ -112,8 +128,24 @@ struct Plan {
 void build_plan_host(bool upper, int n, int NB, int R, std::vector<TileDesc>& tiles,
                      std::vector<int>& slot_base, int& P);
 
+// Row-strip plan: R-row strips, the column sequence split evenly over G
+// workgroups (see xsymv_strip.hpp).
+struct StripPlan {
+    int NS = 0, G = 0, nseg = 0, R = 0;
+    StripBlock* d_blocks = nullptr;
+    int* d_strip_base = nullptr;
+    int* d_seg_base = nullptr;
+    void* h_pinned = nullptr;  // pinned source of the one upload
+};
+void build_strip_plan_host(bool upper, int n, int R, int G, std::vector<StripBlock>& blocks,
+                           std::vector<int>& strip_base, std::vector<int>& seg_base, int& NS);
+
 struct DeviceState;
 DeviceState* device_state(int dev);
+int get_strip_plan(DeviceState* ds, int dev, bool upper, int n, int R, int G, hipStream_t stream,
+                   const StripPlan** out);
+// Workgroups of `kernel` (block size `threads`) the current device holds at once.
+int resident_blocks(const void* kernel, int threads, int* out);
 // Both return 0 or ERR_HIP + hipError_t; the caller holds the state's lock.
 int get_plan(DeviceState* ds, int dev, bool upper, int n, int NB, int R, hipStream_t stream,
              const Plan** out);
@@ -121,6 +153,14 @@ int get_workspace(DeviceState* ds, hipStream_t stream, size_t bytes, void** out)
 std::mutex& device_mutex(DeviceState* ds);
 
 inline size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Strip workspace layout: [rowpart nseg*R][colpart NS*n][x gathered, n]
+template <class T>
+size_t strip_workspace_bytes(int nseg, int R, int NS, int n)
+{
+    return align_up((size_t)nseg * R * sizeof(T)) + align_up((size_t)NS * n * sizeof(T)) +
+           align_up((size_t)n * sizeof(T));
+}
 
 // Workspace layout: [rowpart P*n][colpart nslots*NB][x gathered, n]
 template <class T>
@@ -179,6 +219,60 @@ template <> int autotune_for<cf64>(char, int, int, hipStream_t, int*, float*, in
 template <> int autotune_for<ddreal>(char, int, int, hipStream_t, int*, float*, int);
 
 // --------------------------------------------------------------- the driver
+// The strip family's half of a call (the caller holds the device lock).
+template <class T>
+int strip_run(const KernelSet<T>& ks, bool upper, int n, T alpha, const T* A, int lda,
+              const T* x, int incx, long long kx, T beta, int beta_zero, T* y, int incy,
+              long long ky, hipStream_t stream, DeviceState* ds, int dev)
+{
+    const int R = ks.info.R();
+    const int threads = 64 * ks.info.W;
+    auto kern = upper ? ks.strip_upper : ks.strip_lower;
+    int G = 0;
+    int rc = resident_blocks((const void*)kern, threads, &G);
+    if (rc) return rc;
+    const StripPlan* plan = nullptr;
+    rc = get_strip_plan(ds, dev, upper, n, R, G, stream, &plan);
+    if (rc) return rc;
+    void* ws = nullptr;
+    rc = get_workspace(ds, stream, strip_workspace_bytes<T>(plan->nseg, R, plan->NS, n), &ws);
+    if (rc) return rc;
+    char* base = static_cast<char*>(ws);
+    const size_t off_col = align_up((size_t)plan->nseg * R * sizeof(T));
+    const size_t off_x = off_col + align_up((size_t)plan->NS * n * sizeof(T));
+    T* rowpart = reinterpret_cast<T*>(base);
+    T* colpart = reinterpret_cast<T*>(base + off_col);
+    T* xg = reinterpret_cast<T*>(base + off_x);
+    const T* xin = x;
+    if (incx != 1) {
+        symv_gather<T><<<blocks_for(n, 256), 256, 0, stream>>>(x, incx, kx, n, xg);
+        XSYMV_HIP(hipGetLastError());
+        xin = xg;
+    }
+    TimedCall tc{};
+    const bool timing = timing_enabled();
+    if (timing) {
+        XSYMV_HIP(hipEventCreate(&tc.e0));
+        XSYMV_HIP(hipEventCreate(&tc.e1));
+        XSYMV_HIP(hipEventCreate(&tc.e2));
+        XSYMV_HIP(hipEventRecord(tc.e0, stream));
+    }
+    StripArgs<T> sa{A, xin, rowpart, colpart, plan->d_blocks, plan->d_strip_base,
+                    (long long)lda, n};
+    kern<<<plan->G, threads, 0, stream>>>(sa);
+    XSYMV_HIP(hipGetLastError());
+    if (timing) XSYMV_HIP(hipEventRecord(tc.e1, stream));
+    StripMergeArgs<T> ma{rowpart, colpart, plan->d_seg_base, y, (long long)incy, ky, alpha, beta,
+                         n, plan->NS, R, upper ? 1 : 0, beta_zero};
+    symv_strip_merge<T, MERGE_SPLIT><<<blocks_for(n, 64), 64 * MERGE_SPLIT, 0, stream>>>(ma);
+    XSYMV_HIP(hipGetLastError());
+    if (timing) {
+        XSYMV_HIP(hipEventRecord(tc.e2, stream));
+        timing_push(tc);
+    }
+    return 0;
+}
+
 // forced_idx >= 0 runs that configuration instead of the selected one.
 template <class T>
 int symv_run(char uplo, int n, T alpha, const T* A, int lda, const T* x, int incx, T beta,
@@ -206,6 +300,9 @@ int symv_run(char uplo, int n, T alpha, const T* A, int lda, const T* x, int inc
     XSYMV_HIP(hipGetDevice(&dev));
     DeviceState* ds = device_state(dev);
     std::lock_guard<std::mutex> lk(device_mutex(ds));
+    if (ks.info.RUNS == 4)
+        return strip_run<T>(ks, upper, n, alpha, A, lda, x, incx, kx, beta, beta_zero, y, incy,
+                            ky, stream, ds, dev);
     const Plan* plan = nullptr;
     rc = get_plan(ds, dev, upper, n, NB, R, stream, &plan);
     if (rc) return rc;
@@ -382,7 +479,19 @@ size_t ws_bytes(char uplo, int n)
 {
     if (n <= 0) return 0;
     const bool upper = (uplo == 'U' || uplo == 'u');
-    const ConfigInfo& ci = kernel_sets<T>()[pick_config(prec_code<T>(), upper, n)].info;
+    const KernelSet<T>& ks = kernel_sets<T>()[pick_config(prec_code<T>(), upper, n)];
+    const ConfigInfo& ci = ks.info;
+    if (ci.RUNS == 4) {
+        int G = 0;
+        if (resident_blocks((const void*)(upper ? ks.strip_upper : ks.strip_lower), 64 * ci.W,
+                            &G))
+            return (size_t)-1;
+        std::vector<StripBlock> blocks;
+        std::vector<int> sb, segb;
+        int NS = 0;
+        build_strip_plan_host(upper, n, ci.R(), G, blocks, sb, segb, NS);
+        return strip_workspace_bytes<T>(segb[NS], ci.R(), NS, n);
+    }
     std::vector<TileDesc> tiles;
     std::vector<int> sb;
     int P = 0;

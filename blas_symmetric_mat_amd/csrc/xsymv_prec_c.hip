@@ -12,6 +12,10 @@ template <> const std::vector<KernelSet<cf32>>& kernel_sets<cf32>()
         make_block<cf32, 4, 128, 2, 4, true>(),           // block: NB 128, R 1024, 8 KB runs
         make_set<cf32, 4, 16, 4, true, false>(),          // tiles: NB 64, R 512
         make_runs<cf32, 4, 16, 8, true, true>(),          // runs: NB 64, R 1024, prefetch
+        make_strip<cf32, 4, 2, 4, true>(),                // strip: R 1024, 8 KB runs, G 4
+        make_strip<cf32, 4, 2, 4, false>(),               // strip: R 1024, 8 KB runs, G 4, cached
+        make_strip<cf32, 8, 1, 4, true>(),                // strip: R 1024, 8 KB runs, G 4
+        make_strip<cf32, 4, 1, 4, true>(),                // strip: R 512, 4 KB runs, G 4
     };
     return v;
 }

@@ -13,6 +13,12 @@ template <> const std::vector<KernelSet<double>>& kernel_sets<double>()
         make_runs<double, 4, 16, 8, true, true>(),        // runs: NB 64, R 1024, prefetch
         make_block<double, 4, 128, 2, 4, true>(),         // block: NB 128, R 1024, 8 KB runs
         make_set<double, 8, 16, 2, false, false>(),       // tiles: NB 128, R 256, cached
+        make_strip<double, 4, 2, 4, true>(),              // strip: R 1024, 8 KB runs, G 4
+        make_strip<double, 4, 2, 4, false>(),             // strip: R 1024, 8 KB runs, G 4, cached
+        make_strip<double, 4, 2, 8, true>(),              // strip: R 1024, 8 KB runs, G 8
+        make_strip<double, 8, 1, 4, true>(),              // strip: R 1024, 8 KB runs, G 4
+        make_strip<double, 4, 1, 4, true>(),              // strip: R 512, 4 KB runs, G 4
+        make_strip<double, 4, 4, 4, false>(),             // strip: R 2048, 16 KB runs, G 4, cached
     };
     return v;
 }

@@ -13,6 +13,12 @@ template <> const std::vector<KernelSet<float>>& kernel_sets<float>()
         make_block<float, 4, 64, 2, 4, true>(),           // block: NB 64, R 2048, 8 KB runs
         make_block<float, 8, 128, 1, 4, true>(),          // block: NB 128, R 2048, 8 KB runs
         make_runs<float, 4, 16, 8, true, true>(),         // runs: NB 64, R 2048, prefetch
+        make_strip<float, 4, 2, 4, true>(),               // strip: R 2048, 8 KB runs, G 4
+        make_strip<float, 4, 2, 4, false>(),              // strip: R 2048, 8 KB runs, G 4, cached
+        make_strip<float, 4, 2, 8, true>(),               // strip: R 2048, 8 KB runs, G 8
+        make_strip<float, 8, 1, 4, true>(),               // strip: R 2048, 8 KB runs, G 4
+        make_strip<float, 4, 1, 4, true>(),               // strip: R 1024, 4 KB runs, G 4
+        make_strip<float, 4, 4, 4, true>(),               // strip: R 4096, 16 KB runs, G 4
     };
     return v;
 }

@@ -12,6 +12,11 @@ template <> const std::vector<KernelSet<ddreal>>& kernel_sets<ddreal>()
         make_block<ddreal, 4, 64, 2, 4, true>(),          // block: NB 64, R 512, 8 KB runs
         make_set<ddreal, 8, 8, 4, true, false>(),         // tiles: NB 64, R 256
         make_block<ddreal, 4, 128, 2, 4, true>(),         // block: NB 128, R 512, 8 KB runs
+        make_strip<ddreal, 4, 2, 4, true>(),              // strip: R 512, 8 KB runs, G 4
+        make_strip<ddreal, 4, 2, 4, false>(),             // strip: R 512, 8 KB runs, G 4, cached
+        make_strip<ddreal, 8, 1, 4, true>(),              // strip: R 512, 8 KB runs, G 4
+        make_strip<ddreal, 4, 1, 4, true>(),              // strip: R 256, 4 KB runs, G 4
+        make_strip<ddreal, 4, 2, 2, true>(),              // strip: R 512, 8 KB runs, G 2
     };
     return v;
 }

@@ -12,6 +12,11 @@ template <> const std::vector<KernelSet<cf64>>& kernel_sets<cf64>()
         make_block<cf64, 4, 128, 2, 4, true>(),           // block: NB 128, R 512, 8 KB runs
         make_set<cf64, 4, 8, 8, true, false>(),           // tiles: NB 32, R 512
         make_runs<cf64, 4, 16, 8, false, true>(),         // runs: NB 64, R 512, cached, prefetch
+        make_strip<cf64, 4, 2, 4, true>(),                // strip: R 512, 8 KB runs, G 4
+        make_strip<cf64, 4, 2, 4, false>(),               // strip: R 512, 8 KB runs, G 4, cached
+        make_strip<cf64, 8, 1, 4, true>(),                // strip: R 512, 8 KB runs, G 4
+        make_strip<cf64, 4, 1, 4, true>(),                // strip: R 256, 4 KB runs, G 4
+        make_strip<cf64, 4, 4, 4, false>(),               // strip: R 1024, 16 KB runs, G 4, cached
     };
     return v;
 }

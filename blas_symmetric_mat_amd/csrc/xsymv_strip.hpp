@@ -1,0 +1,257 @@
+// xsymv_strip.hpp -- row-strip, evenly split kernels for y := alpha*S*x + beta*y
+// on gfx950 (only one triangle of S stored, column-major).
+//
+// Each stored off-diagonal element is read once and used twice (its own row
+// and, conjugated, the mirrored element's row), as in the CUDA-xSYMV report's
+// algorithm (§2.1 Fig. 1); partial sums are combined in a fixed order, with no
+// floating-point atomics, so results are bitwise identical from run to run
+// (the report's aim, §2.1; it used an atomic ticket lock instead).
+//
+// Decomposition (gfx950-specific):
+//  * Rows are cut into strips of R = W*SW*64*VEC rows.  Strip i stores, for
+//    uplo = L, the columns [0, iR) in full plus the diagonal triangle of
+//    columns [iR, iR+R); for U, the columns [iR+R, n) in full plus its
+//    diagonal triangle.
+//  * The strips' columns, concatenated in strip order, form one sequence.  It
+//    is cut into G ranges of equal cost (stored elements), G = the number of
+//    workgroups the GPU holds at once, so every workgroup streams the same
+//    number of bytes and they all finish together.  A range may span strips;
+//    its piece in one strip is a segment.
+//  * A workgroup walks its columns in order.  For each column, wave w reads
+//    its own SW stripes right below wave w-1's, so the workgroup reads one
+//    contiguous run of R rows per column (long runs keep HBM efficient even
+//    when the leading dimension is a power of two).
+//  * Row role: each lane keeps SW*VEC row partials in registers for the whole
+//    segment and writes them once to rowpart[segment][row].
+//  * Column role: a column's sum over the strip's rows is finished inside the
+//    workgroup (lane exchange per group of G columns, then the W waves added
+//    in wave order through LDS) and written to colpart[strip][column].
+//  * symv_strip_merge: y_r = beta*y_r + alpha*(sum of the row partials of r's
+//    strip in segment order + sum of colpart[i][r] in strip order).
+#pragma once
+
+#include "xsymv_kernels.hpp"
+
+namespace xsymv {
+
+// Per workgroup: [u0, u1) in the column sequence, first segment slot, strip
+// of u0.
+struct StripBlock {
+    int u0;
+    int u1;
+    int slot0;
+    int strip0;
+};
+
+template <class T>
+struct StripArgs {
+    const T* A;
+    const T* x;           // contiguous
+    T* rowpart;           // [nseg][R]
+    T* colpart;           // [NS][n]
+    const StripBlock* blocks;
+    const int* strip_base;  // [NS+1]: first sequence position of strip i
+    long long lda;
+    int n;
+};
+
+template <class T, bool UPPER, int W, int SW, int G, bool NT, int CBUF>
+__global__ __launch_bounds__(64 * W) void symv_strip(StripArgs<T> a)
+{
+    using E = Elem<T>;
+    constexpr int V = E::VEC;
+    constexpr int H = 64 * V;
+    constexpr int R = W * SW * H;
+    static_assert(CBUF % G == 0, "column buffer holds whole groups");
+
+    __shared__ T colred[W][CBUF];
+
+    const StripBlock bd = a.blocks[blockIdx.x];
+    const int n = a.n;
+    const long long lda = a.lda;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const T* __restrict__ A = a.A;
+    const T* __restrict__ x = a.x;
+
+    int u = bd.u0;
+    int slot = bd.slot0;
+    int strip = bd.strip0;
+    while (u < bd.u1) {  // workgroup-uniform: one segment per iteration
+        const int sb0 = a.strip_base[strip];
+        const int useg = min(bd.u1, a.strip_base[strip + 1]);
+        const int rs0 = strip * R;
+        const int rs1 = min(n, rs0 + R);
+        const int cfirst = UPPER ? rs0 : 0;  // the strip's first column
+        const int rw = rs0 + wave * SW * H;  // this wave's first row
+
+        T racc[SW][V];
+        T xr[SW][V];
+#pragma unroll
+        for (int s = 0; s < SW; ++s)
+#pragma unroll
+            for (int k = 0; k < V; ++k) {
+                racc[s][k] = E::zero();
+                const int r = rw + s * H + lane * V + k;
+                const T v = x[r < rs1 ? r : rs1 - 1];
+                xr[s][k] = E::sel(r < rs1, v, E::zero());
+            }
+        // this wave's rows are all inside the strip (wave-uniform)
+        const bool rows_whole = rw + SW * H <= rs1;
+
+        int jbuf = cfirst + (u - sb0);  // first column held in colred
+        int nbuf = 0;                   // columns held in colred
+#pragma unroll 1
+        for (int g0 = u; g0 < useg; g0 += G) {
+            const int jg = cfirst + (g0 - sb0);  // first column of the group
+            const int ng = min(G, useg - g0);    // real columns in the group
+            // every element of the group in this wave's rows is stored and
+            // strictly off the diagonal: 16-byte loads, no masks
+            const bool fullv = ng == G && rows_whole && jg + G <= n &&
+                               (UPPER ? (rw + SW * H <= jg) : (rw >= jg + G));
+            // no element of the group in this wave's rows is stored
+            const bool empty = rw >= rs1 || (UPPER ? (rw > jg + ng - 1) : (rw + SW * H <= jg));
+            T cacc[G];
+            if (empty) {
+#pragma unroll
+                for (int g = 0; g < G; ++g) cacc[g] = E::zero();
+            } else if (fullv) {
+                const T* __restrict__ Ab = A + (long long)jg * lda + rw + lane * V;
+                T av[G][SW][V];
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+#pragma unroll
+                    for (int s = 0; s < SW; ++s)
+                        E::template load16<NT>(Ab + (long long)g * lda + s * H, av[g][s]);
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const T xcol = x[jg + g];
+                    cacc[g] = E::zero();
+#pragma unroll
+                    for (int s = 0; s < SW; ++s)
+#pragma unroll
+                        for (int k = 0; k < V; ++k) {
+                            racc[s][k] = E::mac(racc[s][k], av[g][s][k], xcol);
+                            cacc[g] = E::macc(cacc[g], av[g][s][k], xr[s][k]);
+                        }
+                }
+            } else {
+                // element loads at clamped addresses, branch-free
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const int col = jg + g;
+                    const bool colok = g < ng && col < n;
+                    const int cc = colok ? col : jg;  // jg is a real column
+                    const T* __restrict__ Acc = A + (long long)cc * lda;
+                    const T xcol = E::sel(colok, x[cc], E::zero());
+                    cacc[g] = E::zero();
+#pragma unroll
+                    for (int s = 0; s < SW; ++s)
+#pragma unroll
+                        for (int k = 0; k < V; ++k) {
+                            T off;
+                            const T av = masked_elem<T, UPPER>(Acc, rw + s * H + lane * V + k,
+                                                               rs1, col, cc, colok, true, &off);
+                            racc[s][k] = E::mac(racc[s][k], av, xcol);
+                            cacc[g] = E::macc(cacc[g], off, xr[s][k]);
+                        }
+                }
+            }
+            wave_transpose_reduce<T, G>(cacc, lane);
+            constexpr int GROUP = 64 / G;
+            if ((lane & (GROUP - 1)) == 0)
+                colred[wave][nbuf + wave_transpose_index<G>(lane)] = cacc[0];
+            nbuf += G;
+            const bool last = g0 + G >= useg;
+            if (nbuf == CBUF || last) {  // workgroup-uniform
+                __syncthreads();
+                const int nreal = last ? (useg - g0) + nbuf - G : nbuf;
+                for (int c = threadIdx.x; c < nreal; c += 64 * W) {
+                    T sum = colred[0][c];
+#pragma unroll
+                    for (int w = 1; w < W; ++w) sum = E::add(sum, colred[w][c]);
+                    a.colpart[(long long)strip * n + jbuf + c] = sum;
+                }
+                __syncthreads();
+                jbuf += nreal;
+                nbuf = 0;
+            }
+        }
+        // this wave's row partials for the segment
+        T* __restrict__ rp = a.rowpart + (long long)slot * R;
+#pragma unroll
+        for (int s = 0; s < SW; ++s)
+#pragma unroll
+            for (int k = 0; k < V; ++k) {
+                const int r = rw + s * H + lane * V + k;
+                if (r < rs1) rp[r - rs0] = racc[s][k];
+            }
+        u = useg;
+        ++slot;
+        ++strip;
+    }
+}
+
+// Ordered merge for the strip decomposition: row r of strip I adds its row
+// partials slot by slot (segments of strip I in order), then the column
+// partials colpart[i][r] of the strips that hold column r (L: i >= I,
+// U: i <= I) in ascending i.  SPLIT waves share 64 rows; wave g takes the
+// terms k with k % SPLIT == g; the subtotals meet in a fixed pairwise tree.
+template <class T>
+struct StripMergeArgs {
+    const T* rowpart;
+    const T* colpart;
+    const int* seg_base;  // [NS+1]: segments of strip i are [seg_base[i], seg_base[i+1])
+    T* y;
+    long long incy;
+    long long ky;
+    T alpha;
+    T beta;
+    int n;
+    int NS;
+    int R;
+    int upper;
+    int beta_zero;
+};
+
+template <class T, int SPLIT>
+__global__ __launch_bounds__(64 * SPLIT) void symv_strip_merge(StripMergeArgs<T> a)
+{
+    using E = Elem<T>;
+    __shared__ T part[SPLIT][64];
+    const int lane = threadIdx.x & 63;
+    const int g = threadIdx.x >> 6;
+    const int i = blockIdx.x * 64 + lane;
+    T acc = E::zero();
+    if (i < a.n) {
+        const int I = i / a.R;
+        const int s_lo = a.seg_base[I];
+        const int nrow = a.seg_base[I + 1] - s_lo;
+        const int c_lo = a.upper ? 0 : I;
+        const int ncol = a.upper ? I + 1 : a.NS - I;
+        const int ntot = nrow + ncol;
+        const T* __restrict__ rp = a.rowpart + (long long)s_lo * a.R + (i - I * a.R);
+        const T* __restrict__ cp = a.colpart + (long long)c_lo * a.n + i;
+#pragma unroll 4
+        for (int k = g; k < ntot; k += SPLIT) {
+            const T v = (k < nrow) ? rp[(long long)k * a.R] : cp[(long long)(k - nrow) * a.n];
+            acc = E::add(acc, v);
+        }
+    }
+    part[g][lane] = acc;
+    __syncthreads();
+#pragma unroll
+    for (int w = SPLIT / 2; w >= 1; w >>= 1) {
+        if (g < w) part[g][lane] = E::add(part[g][lane], part[g + w][lane]);
+        __syncthreads();
+    }
+    if (g == 0 && i < a.n) {
+        const T tot = part[0][lane];
+        T* yp = a.y + a.ky + (long long)i * a.incy;
+        T r = E::mul(a.alpha, tot);
+        if (!a.beta_zero) r = E::add(r, E::mul(a.beta, *yp));
+        *yp = r;
+    }
+}
+
+}  // namespace xsymv

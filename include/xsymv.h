@@ -156,6 +156,23 @@ int xsymv_clear_config(void);
 int xsymv_timing_enable(int on);
 int xsymv_timing_read(float *main_ms, float *merge_ms, int max);
 
+/* Workgroups a row-strip configuration (column_runs == 4) is launched with
+ * on the current device: the number of its workgroups the device holds at
+ * once.  0 for other families, -1 for a bad index, -(1000 + hipError_t) on a
+ * runtime error. */
+int xsymv_config_workgroups(int prec, int idx, char uplo);
+
+/* The row-strip work split the library uses for order n, strips of R rows
+ * and G workgroups (host computation, no device work): writes per workgroup
+ * {first, end} of its range in the strips' concatenated column sequence,
+ * its first segment slot and the strip of `first` into blocks4 (4 ints per
+ * workgroup), the sequence position where each strip starts (NS+1 entries)
+ * into strip_base and each strip's first segment slot (NS+1 entries, the
+ * last = total segments) into seg_base.  Returns the number of workgroups
+ * used, -1 for bad arguments, -2 if an output is too small. */
+int xsymv_strip_plan(char uplo, int n, int R, int G, int *blocks4, int max_blocks,
+                     int *strip_base, int *seg_base, int max_strips);
+
 /* Library version string. */
 const char *xsymv_version(void);
 

@@ -80,3 +80,52 @@ def test_workspace_bytes_grow_with_n():
     ci = X.config_info("d", 0)
     P = (4000 + ci["panel"] - 1) // ci["panel"]
     assert b >= P * 4000 * 8
+
+
+@pytest.mark.parametrize("uplo", ["L", "U"])
+@pytest.mark.parametrize("n,R,G", [(1, 64, 7), (100, 64, 3), (1000, 256, 37), (1031, 128, 200),
+                                   (4096, 1024, 1792), (10007, 2048, 1792), (5000, 512, 1)])
+def test_strip_plan_covers_triangle_once(uplo, n, R, G):
+    """Emulate the strip kernel's walk: every stored element (i, j) is visited
+    by exactly one workgroup, every (strip, column) sum is written once, and
+    the segments of each strip are the slots the merge reads."""
+    blocks, sb, segb = X.strip_plan(uplo, n, R, G)
+    NS = (n + R - 1) // R
+    assert sb[0] == 0 and segb[0] == 0
+    upper = uplo == "U"
+    visits = np.zeros((n, n), dtype=np.int32)
+    colsum_writes = {}
+    slots_of_strip = {}
+    prev_end = 0
+    for u0, u1, slot, strip in blocks:
+        assert u0 == prev_end and u1 >= u0
+        prev_end = u1
+        u = u0
+        while u < u1:
+            assert sb[strip] <= u < sb[strip + 1]
+            end = min(u1, sb[strip + 1])
+            rs0, rs1 = strip * R, min(n, strip * R + R)
+            cfirst = rs0 if upper else 0
+            for pos in range(u, end):
+                j = cfirst + pos - sb[strip]
+                assert 0 <= j < n
+                rows = np.arange(rs0, rs1)
+                st = rows[rows <= j] if upper else rows[rows >= j]
+                visits[st, j] += 1
+                key = (strip, j)
+                colsum_writes[key] = colsum_writes.get(key, 0) + 1
+            slots_of_strip.setdefault(strip, []).append(slot)
+            u = end
+            slot += 1
+            strip += 1
+    assert prev_end == sb[NS]
+    stored = np.triu(np.ones((n, n), bool)) if upper else np.tril(np.ones((n, n), bool))
+    assert np.all(visits[stored] == 1) and np.all(visits[~stored] == 0)
+    assert all(v == 1 for v in colsum_writes.values())
+    for i in range(NS):
+        assert slots_of_strip[i] == list(range(segb[i], segb[i + 1]))
+    # every column j is summed in exactly the strips the merge reads
+    for j in range(0, n, max(1, n // 50)):
+        strips = sorted(i for (i, jj) in colsum_writes if jj == j)
+        I = j // R
+        assert strips == (list(range(0, I + 1)) if upper else list(range(I, NS)))
