@@ -46,6 +46,30 @@ __device__ __forceinline__ u32x4 ld16(const void* p)
         return *q;
 }
 
+// 16 bytes at byte offset `off` of a raw buffer: dwords at or past the
+// buffer's byte count read as zero and touch no memory (range checked per
+// dword on gfx950), so one 16-byte load can end exactly at a row bound.
+constexpr int BUF_DWORD3 = 0x00020000;  // raw buffer, 32-bit data format
+
+// Buffer descriptor of `bytes` bytes at `base`; both must be the same in
+// every lane of the wave (they are read from the first active lane, so the
+// descriptor lives in scalar registers).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes)
+{
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+    void* q = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(q, (short)0, __builtin_amdgcn_readfirstlane(bytes),
+                                             BUF_DWORD3);
+}
+
+template <bool NT>
+__device__ __forceinline__ u32x4 bld16(__amdgpu_buffer_rsrc_t r, int off)
+{
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, NT ? 2 : 0));
+}
+
 __device__ __forceinline__ float shfl_xor_f(float v, int m)
 {
     return __shfl_xor(v, m, 64);
@@ -66,12 +90,17 @@ template <> struct Elem<float> {
     __device__ static float add(float a, float b) { return a + b; }
     __device__ static float mul(float a, float b) { return a * b; }
     __device__ static float diag_load(const float* p) { return *p; }
-    template <bool NT>
-    __device__ static void load16(const float* p, float (&o)[VEC])
+    __device__ static void unpack(u32x4 v, float (&o)[VEC])
     {
-        u32x4 v = ld16<NT>(p);
         o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y);
         o[2] = __uint_as_float(v.z); o[3] = __uint_as_float(v.w);
+    }
+    template <bool NT>
+    __device__ static void load16(const float* p, float (&o)[VEC]) { unpack(ld16<NT>(p), o); }
+    template <bool NT>
+    __device__ static void bload16(__amdgpu_buffer_rsrc_t r, int off, float (&o)[VEC])
+    {
+        unpack(bld16<NT>(r, off), o);
     }
     __device__ static float shfl_xor(float v, int m) { return shfl_xor_f(v, m); }
     __device__ static float sel(bool c, float a, float b) { return c ? a : b; }
@@ -89,12 +118,17 @@ template <> struct Elem<double> {
     __device__ static double add(double a, double b) { return a + b; }
     __device__ static double mul(double a, double b) { return a * b; }
     __device__ static double diag_load(const double* p) { return *p; }
-    template <bool NT>
-    __device__ static void load16(const double* p, double (&o)[VEC])
+    __device__ static void unpack(u32x4 v, double (&o)[VEC])
     {
-        u32x4 v = ld16<NT>(p);
         o[0] = __hiloint2double((int)v.y, (int)v.x);
         o[1] = __hiloint2double((int)v.w, (int)v.z);
+    }
+    template <bool NT>
+    __device__ static void load16(const double* p, double (&o)[VEC]) { unpack(ld16<NT>(p), o); }
+    template <bool NT>
+    __device__ static void bload16(__amdgpu_buffer_rsrc_t r, int off, double (&o)[VEC])
+    {
+        unpack(bld16<NT>(r, off), o);
     }
     __device__ static double shfl_xor(double v, int m) { return shfl_xor_d(v, m); }
     __device__ static double sel(bool c, double a, double b) { return c ? a : b; }
@@ -131,12 +165,17 @@ template <> struct Elem<cf32> {
         return {a.re * b.re - a.im * b.im, a.re * b.im + a.im * b.re};
     }
     __device__ static cf32 diag_load(const cf32* p) { return {p->re, 0.0f}; }
-    template <bool NT>
-    __device__ static void load16(const cf32* p, cf32 (&o)[VEC])
+    __device__ static void unpack(u32x4 v, cf32 (&o)[VEC])
     {
-        u32x4 v = ld16<NT>(p);
         o[0] = {__uint_as_float(v.x), __uint_as_float(v.y)};
         o[1] = {__uint_as_float(v.z), __uint_as_float(v.w)};
+    }
+    template <bool NT>
+    __device__ static void load16(const cf32* p, cf32 (&o)[VEC]) { unpack(ld16<NT>(p), o); }
+    template <bool NT>
+    __device__ static void bload16(__amdgpu_buffer_rsrc_t r, int off, cf32 (&o)[VEC])
+    {
+        unpack(bld16<NT>(r, off), o);
     }
     __device__ static cf32 shfl_xor(cf32 v, int m)
     {
@@ -182,11 +221,16 @@ template <> struct Elem<cf64> {
         return {a.re * b.re - a.im * b.im, a.re * b.im + a.im * b.re};
     }
     __device__ static cf64 diag_load(const cf64* p) { return {p->re, 0.0}; }
-    template <bool NT>
-    __device__ static void load16(const cf64* p, cf64 (&o)[VEC])
+    __device__ static void unpack(u32x4 v, cf64 (&o)[VEC])
     {
-        u32x4 v = ld16<NT>(p);
         o[0] = {__hiloint2double((int)v.y, (int)v.x), __hiloint2double((int)v.w, (int)v.z)};
+    }
+    template <bool NT>
+    __device__ static void load16(const cf64* p, cf64 (&o)[VEC]) { unpack(ld16<NT>(p), o); }
+    template <bool NT>
+    __device__ static void bload16(__amdgpu_buffer_rsrc_t r, int off, cf64 (&o)[VEC])
+    {
+        unpack(bld16<NT>(r, off), o);
     }
     __device__ static cf64 shfl_xor(cf64 v, int m)
     {
@@ -248,11 +292,16 @@ template <> struct Elem<ddreal> {
     __device__ static ddreal add(ddreal a, ddreal b) { return dd_add(a, b); }
     __device__ static ddreal mul(ddreal a, ddreal b) { return dd_mul(a, b); }
     __device__ static ddreal diag_load(const ddreal* p) { return *p; }
-    template <bool NT>
-    __device__ static void load16(const ddreal* p, ddreal (&o)[VEC])
+    __device__ static void unpack(u32x4 v, ddreal (&o)[VEC])
     {
-        u32x4 v = ld16<NT>(p);
         o[0] = {__hiloint2double((int)v.y, (int)v.x), __hiloint2double((int)v.w, (int)v.z)};
+    }
+    template <bool NT>
+    __device__ static void load16(const ddreal* p, ddreal (&o)[VEC]) { unpack(ld16<NT>(p), o); }
+    template <bool NT>
+    __device__ static void bload16(__amdgpu_buffer_rsrc_t r, int off, ddreal (&o)[VEC])
+    {
+        unpack(bld16<NT>(r, off), o);
     }
     __device__ static ddreal shfl_xor(ddreal v, int m)
     {

@@ -617,7 +617,7 @@ int xsymv_config_workgroups(int prec, int idx, char uplo)
     {                                                                                    \
         if (idx < 0 || idx >= (int)kernel_sets<T>().size()) return -1;                   \
         const auto& ks = kernel_sets<T>()[idx];                                          \
-        if (ks.info.RUNS != 4) return 0;                                                 \
+        if (!ks.info.strip()) return 0;                                                  \
         k = (const void*)(upper ? ks.strip_upper : ks.strip_lower);                      \
         threads = 64 * ks.info.W;                                                        \
         break;                                                                           \

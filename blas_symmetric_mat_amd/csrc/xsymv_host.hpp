@@ -43,6 +43,7 @@ struct ConfigInfo {
                // prefetched; 3: symv_block; 4: symv_strip (CW = column group,
                // S = W * stripes per wave)
     int NB() const { return W * CW; }
+    bool strip() const { return RUNS >= 4; }
     int R() const { return S * H; }
 };
 
@@ -300,7 +301,7 @@ int symv_run(char uplo, int n, T alpha, const T* A, int lda, const T* x, int inc
     XSYMV_HIP(hipGetDevice(&dev));
     DeviceState* ds = device_state(dev);
     std::lock_guard<std::mutex> lk(device_mutex(ds));
-    if (ks.info.RUNS == 4)
+    if (ks.info.strip())
         return strip_run<T>(ks, upper, n, alpha, A, lda, x, incx, kx, beta, beta_zero, y, incy,
                             ky, stream, ds, dev);
     const Plan* plan = nullptr;
@@ -481,7 +482,7 @@ size_t ws_bytes(char uplo, int n)
     const bool upper = (uplo == 'U' || uplo == 'u');
     const KernelSet<T>& ks = kernel_sets<T>()[pick_config(prec_code<T>(), upper, n)];
     const ConfigInfo& ci = ks.info;
-    if (ci.RUNS == 4) {
+    if (ci.strip()) {
         int G = 0;
         if (resident_blocks((const void*)(upper ? ks.strip_upper : ks.strip_lower), 64 * ci.W,
                             &G))

@@ -55,13 +55,25 @@ struct StripArgs {
     int n;
 };
 
+// Reads of A.  A wave's rows of column j are one run of SW*H elements
+// starting at row rw.  Stored rows of column j: L: j < r < n (strictly below
+// the diagonal), U: 0 <= r < j.  Both are "rows below an upper bound" once
+// r > j is known, so whole groups are read with 16-byte raw-buffer loads whose
+// byte count ends at that bound: rows at or past it read as zero without a
+// memory access.  That covers the ragged last strip (L and U) and, for U, the
+// diagonal band.  For L the band (rows around the diagonal) needs a lower
+// bound, so those few groups take element loads at clamped addresses.  The
+// diagonal itself counts once, in the row role: L takes it in the band, U
+// adds d_r * x_r at the end of the segment that holds column r.
 template <class T, bool UPPER, int W, int SW, int G, bool NT, int CBUF>
 __global__ __launch_bounds__(64 * W) void symv_strip(StripArgs<T> a)
 {
     using E = Elem<T>;
     constexpr int V = E::VEC;
     constexpr int H = 64 * V;
-    constexpr int R = W * SW * H;
+    constexpr int RW = SW * H;  // rows per wave
+    constexpr int R = W * RW;
+    constexpr int GROUP = 64 / G;
     static_assert(CBUF % G == 0, "column buffer holds whole groups");
 
     __shared__ T colred[W][CBUF];
@@ -82,8 +94,9 @@ __global__ __launch_bounds__(64 * W) void symv_strip(StripArgs<T> a)
         const int useg = min(bd.u1, a.strip_base[strip + 1]);
         const int rs0 = strip * R;
         const int rs1 = min(n, rs0 + R);
-        const int cfirst = UPPER ? rs0 : 0;  // the strip's first column
-        const int rw = rs0 + wave * SW * H;  // this wave's first row
+        const int coff = (UPPER ? rs0 : 0) - sb0;  // column = sequence position + coff
+        const int rw = rs0 + wave * RW;            // this wave's first row
+        const bool wave_empty = rw >= rs1;
 
         T racc[SW][V];
         T xr[SW][V];
@@ -96,51 +109,56 @@ __global__ __launch_bounds__(64 * W) void symv_strip(StripArgs<T> a)
                 const T v = x[r < rs1 ? r : rs1 - 1];
                 xr[s][k] = E::sel(r < rs1, v, E::zero());
             }
-        // this wave's rows are all inside the strip (wave-uniform)
-        const bool rows_whole = rw + SW * H <= rs1;
 
-        int jbuf = cfirst + (u - sb0);  // first column held in colred
-        int nbuf = 0;                   // columns held in colred
+        int jbuf = u + coff;  // first column held in colred
+        int nbuf = 0;         // columns held in colred
 #pragma unroll 1
         for (int g0 = u; g0 < useg; g0 += G) {
-            const int jg = cfirst + (g0 - sb0);  // first column of the group
-            const int ng = min(G, useg - g0);    // real columns in the group
-            // every element of the group in this wave's rows is stored and
-            // strictly off the diagonal: 16-byte loads, no masks
-            const bool fullv = ng == G && rows_whole && jg + G <= n &&
-                               (UPPER ? (rw + SW * H <= jg) : (rw >= jg + G));
-            // no element of the group in this wave's rows is stored
-            const bool empty = rw >= rs1 || (UPPER ? (rw > jg + ng - 1) : (rw + SW * H <= jg));
+            const int jg = g0 + coff;          // first column of the group
+            const int ng = min(G, useg - g0);  // real columns in the group
+            // no stored element of the group in this wave's rows
+            const bool empty =
+                wave_empty || (UPPER ? (rw >= jg + ng - 1) : (rw + RW <= jg));
+            // every real column of the group is left of this wave's rows (L)
+            const bool band = !UPPER && !empty && rw < jg + ng;
             T cacc[G];
             if (empty) {
 #pragma unroll
                 for (int g = 0; g < G; ++g) cacc[g] = E::zero();
-            } else if (fullv) {
-                const T* __restrict__ Ab = A + (long long)jg * lda + rw + lane * V;
+            } else if (!band) {
                 T av[G][SW][V];
-#pragma unroll
-                for (int g = 0; g < G; ++g)
-#pragma unroll
-                    for (int s = 0; s < SW; ++s)
-                        E::template load16<NT>(Ab + (long long)g * lda + s * H, av[g][s]);
+                T xcol[G];
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
-                    const T xcol = x[jg + g];
+                    const bool real = g < ng;
+                    const int cc = real ? jg + g : jg;
+                    // stored rows of this wave in column cc: [rw, bound)
+                    const int bound = UPPER ? cc : n;
+                    const int rows = real ? min(RW, max(0, bound - rw)) : 0;
+                    const auto rs = make_rsrc(A + (long long)cc * lda + rw, rows * (int)sizeof(T));
+#pragma unroll
+                    for (int s = 0; s < SW; ++s)
+                        E::template bload16<NT>(rs, (s * H + lane * V) * (int)sizeof(T), av[g][s]);
+                    xcol[g] = E::sel(real, x[cc], E::zero());
+                }
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
                     cacc[g] = E::zero();
 #pragma unroll
                     for (int s = 0; s < SW; ++s)
 #pragma unroll
                         for (int k = 0; k < V; ++k) {
-                            racc[s][k] = E::mac(racc[s][k], av[g][s][k], xcol);
+                            racc[s][k] = E::mac(racc[s][k], av[g][s][k], xcol[g]);
                             cacc[g] = E::macc(cacc[g], av[g][s][k], xr[s][k]);
                         }
                 }
             } else {
-                // element loads at clamped addresses, branch-free
+                // L diagonal band: element loads at clamped addresses,
+                // branch-free; the diagonal counts once (row role)
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
                     const int col = jg + g;
-                    const bool colok = g < ng && col < n;
+                    const bool colok = g < ng;
                     const int cc = colok ? col : jg;  // jg is a real column
                     const T* __restrict__ Acc = A + (long long)cc * lda;
                     const T xcol = E::sel(colok, x[cc], E::zero());
@@ -150,7 +168,7 @@ __global__ __launch_bounds__(64 * W) void symv_strip(StripArgs<T> a)
 #pragma unroll
                         for (int k = 0; k < V; ++k) {
                             T off;
-                            const T av = masked_elem<T, UPPER>(Acc, rw + s * H + lane * V + k,
+                            const T av = masked_elem<T, false>(Acc, rw + s * H + lane * V + k,
                                                                rs1, col, cc, colok, true, &off);
                             racc[s][k] = E::mac(racc[s][k], av, xcol);
                             cacc[g] = E::macc(cacc[g], off, xr[s][k]);
@@ -158,7 +176,6 @@ __global__ __launch_bounds__(64 * W) void symv_strip(StripArgs<T> a)
                 }
             }
             wave_transpose_reduce<T, G>(cacc, lane);
-            constexpr int GROUP = 64 / G;
             if ((lane & (GROUP - 1)) == 0)
                 colred[wave][nbuf + wave_transpose_index<G>(lane)] = cacc[0];
             nbuf += G;
@@ -176,6 +193,20 @@ __global__ __launch_bounds__(64 * W) void symv_strip(StripArgs<T> a)
                 jbuf += nreal;
                 nbuf = 0;
             }
+        }
+        if (UPPER) {
+            // diagonal of the rows whose column is in this segment
+            const int c0 = u + coff, c1 = useg + coff;
+#pragma unroll
+            for (int s = 0; s < SW; ++s)
+#pragma unroll
+                for (int k = 0; k < V; ++k) {
+                    const int r = rw + s * H + lane * V + k;
+                    const bool in = r >= c0 && r < c1 && r < rs1;
+                    const long long rr = in ? r : c0;  // c0 < n is a real column
+                    const T d = E::diag_load(A + rr * lda + rr);
+                    racc[s][k] = E::mac(racc[s][k], E::sel(in, d, E::zero()), xr[s][k]);
+                }
         }
         // this wave's row partials for the segment
         T* __restrict__ rp = a.rowpart + (long long)slot * R;
