@@ -36,10 +36,28 @@ if ROOT not in sys.path:
 
 METRIC = "SYMV GFLOPS (2n^2) and % of peak HBM GB/s at n=32768, fp32/fp64/c/z/DD"
 KERNEL_SOURCES = ["blas_symmetric_mat_amd/csrc/xsymv_kernels.hpp",
+                  "blas_symmetric_mat_amd/csrc/xsymv_strip.hpp",
                   "blas_symmetric_mat_amd/csrc/xsymv_arith.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 ENTRY = {"s": "xsymv_s", "d": "xsymv_d", "c": "xhemv_c", "z": "xhemv_z", "w": "xsymv_w"}
 DTYPE_NAME = {"s": "f32", "d": "f64", "c": "c64", "z": "c128", "w": "dd (f64 pairs)"}
+
+
+CTYPE = {"s": "float", "d": "double", "c": "cf32", "z": "cf64", "w": "ddreal"}
+
+
+def kernel_label(X, prec: str, uplo: str, idx: int) -> str:
+    """The streaming kernel a configuration launches, with its shape."""
+    ci = X.config_info(prec, idx)
+    tri = "upper" if uplo == "U" else "lower"
+    load = "nt" if ci["nontemporal"] else "cached"
+    fam = ci["column_runs"]
+    if fam == 4:
+        return (f"symv_strip<{CTYPE[prec]}, {tri}, W={ci['waves']}, "
+                f"SW={ci['stripes'] // ci['waves']}, G={ci['cols_per_wave']}, {load}>")
+    name = {0: "symv_tiles", 1: "symv_runs", 2: "symv_runs", 3: "symv_block"}[fam]
+    return (f"{name}<{CTYPE[prec]}, {tri}, W={ci['waves']}, CW={ci['cols_per_wave']}, "
+            f"S={ci['stripes']}, {load}>")
 
 
 def log(msg):
@@ -129,11 +147,15 @@ def cpu_model():
     return None
 
 
-def traffic_record(workload: str):
+def traffic_record(workload: str, kernel: str):
+    """The committed counter record of `workload`, if it was taken on the
+    current kernel source and the same kernel configuration."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     rec = json.load(open(TRAFFIC_FILE)).get(workload)
     if not rec or rec.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    if rec.get("kernel_config") != kernel:
         return None
     return rec
 
@@ -154,7 +176,9 @@ def measure_detail(name, p, reps, flush):
     t_call = tot[len(tot) // 2] * 1e-3
     bz = beta_is_zero(p)
     call_b = R.call_bytes(p.prec, p.n, bz)
+    import blas_symmetric_mat_amd as X
     out = {"prec": p.prec, "uplo": p.uplo, "n": p.n, "lda": p.lda,
+           "kernel": kernel_label(X, p.prec, p.uplo, X.current_config(p.prec, p.uplo, p.n)),
            "ms_per_call_median": round(t_call * 1e3, 4),
            "gflops_2n2": round(R.gflops_2n2(p.n, t_call), 2),
            "hbm_gbps_algorithmic": round(call_b / t_call / 1e9, 1),
@@ -225,7 +249,10 @@ def summarize_pmc(fetch_csv: str, write_csv: str, command: str, workload: str) -
     main = max(mains, key=lambda k: statistics.mean(f[k]))
     fb = statistics.mean(f[main]) * 1024 * fetch_scale
     wb = statistics.mean(w[main]) * 1024 * write_scale
-    return {workload: {"kernel": main[0], "grid_threads": main[1],
+    import blas_symmetric_mat_amd as X
+    prec, uplo, n = workload[0], workload.split("-")[1], int(workload.split("-n")[-1])
+    kcfg = kernel_label(X, prec, uplo, X.current_config(prec, uplo, n))
+    return {workload: {"kernel": main[0], "kernel_config": kcfg, "grid_threads": main[1],
                        "fetch_bytes_per_launch": round(fb), "write_bytes_per_launch": round(wb),
                        "bytes_per_launch": round(fb + wb),
                        "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4),
@@ -318,11 +345,12 @@ def main():
     kb = R.tile_kernel_bytes("s", p.n)
     achieved = kb / (main_ms * 1e-3) / 1e9
     workload = f"ssymv-L-n{p.n}"
-    tr = traffic_record(workload)
+    kname = kernel_label(X, "s", "L", cfg_idx)
+    tr = traffic_record(workload, kname)
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": R.HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": round(achieved / R.HBM_PEAK_GBPS, 4),
             "traffic": tr["bytes_per_launch"] if tr else None,
-            "kernel": "symv_tiles<float, lower>", "launch_ms_mean": round(main_ms, 4),
+            "kernel": kname, "launch_ms_mean": round(main_ms, 4),
             "merge_ms_mean": round(merge_ms, 4),
             "algorithmic_bytes_per_launch": kb}
     del d

@@ -41,14 +41,6 @@ namespace {
 std::map<int, std::unique_ptr<DeviceState>> g_dev;
 }
 
-int pick_config(int prec, bool upper, int n)
-{
-    std::lock_guard<std::mutex> lk(g_rules_mu);
-    const auto& rs = g_rules[prec][upper ? 1 : 0];
-    for (auto it = rs.rbegin(); it != rs.rend(); ++it)
-        if (n >= it->n_lo && n <= it->n_hi) return it->idx;
-    return 0;
-}
 
 void build_plan_host(bool upper, int n, int NB, int R, std::vector<TileDesc>& tiles,
                      std::vector<int>& slot_base, int& P)
@@ -331,6 +323,72 @@ int find_config(int prec, int W, int CW, int S, int NT, int XL, int RUNS)
 
 const char PREC_CHARS[5] = {'s', 'd', 'c', 'z', 'w'};
 
+// Precision code of a precision letter, or -1.
+int prec_of_char(char c)
+{
+    for (int p = 0; p < 5; ++p)
+        if (PREC_CHARS[p] == c) return p;
+    return -1;
+}
+
+}  // namespace
+
+// Built-in selection rules measured on MI355X by the on-device autotuner over
+// a grid of orders (the counterpart of the report's per-size rules, §3
+// Table 3).  Kernels are named by shape, so the table survives reordering of
+// the configuration lists; rows whose shape is not compiled are ignored.
+struct TunedRule {
+    char prec, uplo;
+    int n_lo, n_hi;
+    int W, CW, S, NT, XLDS, RUNS;
+};
+static const TunedRule TUNED_RULES[] = {
+#include "xsymv_tuned.inc"
+};
+
+namespace {
+std::once_flag g_builtin_once;
+std::vector<Rule> g_builtin[5][2];
+
+void init_builtin_rules()
+{
+    for (const TunedRule& t : TUNED_RULES) {
+        const int prec = prec_of_char(t.prec);
+        if (prec < 0) continue;
+        const int idx = find_config(prec, t.W, t.CW, t.S, t.NT, t.XLDS, t.RUNS);
+        if (idx < 0) continue;
+        g_builtin[prec][t.uplo == 'U' ? 1 : 0].push_back(Rule{t.n_lo, t.n_hi, idx});
+    }
+}
+}  // namespace
+
+int builtin_config(int prec, bool upper, int n)
+{
+    std::call_once(g_builtin_once, init_builtin_rules);
+    for (const Rule& r : g_builtin[prec][upper ? 1 : 0])
+        if (n >= r.n_lo && n <= r.n_hi) return r.idx;
+    return 0;
+}
+
+// Caller rules first (the latest matching one; idx -1 defers to the built-in
+// choice), then the built-in rules, then entry 0.
+int pick_config(int prec, bool upper, int n)
+{
+    {
+        std::lock_guard<std::mutex> lk(g_rules_mu);
+        const auto& rs = g_rules[prec][upper ? 1 : 0];
+        for (auto it = rs.rbegin(); it != rs.rend(); ++it)
+            if (n >= it->n_lo && n <= it->n_hi) {
+                if (it->idx >= 0) return it->idx;
+                break;
+            }
+    }
+    return builtin_config(prec, upper, n);
+}
+
+namespace {
+
+
 // A minimal reader for the rule files this library writes: a flat list of
 // objects with string or integer values inside the "rules" array.
 struct JsonRule {
@@ -465,7 +523,7 @@ int xsymv_select_config(int prec, char uplo, int n_lo, int n_hi, int idx)
         return -1;
     if (idx < -1 || idx >= num_configs(prec) || n_lo > n_hi) return -1;
     std::lock_guard<std::mutex> lk(g_rules_mu);
-    g_rules[prec][upper ? 1 : 0].push_back(Rule{n_lo, n_hi, idx < 0 ? 0 : idx});
+    g_rules[prec][upper ? 1 : 0].push_back(Rule{n_lo, n_hi, idx});
     return 0;
 }
 
@@ -545,7 +603,7 @@ int xsymv_save_config(const char* path)
             for (int u = 0; u < 2; ++u)
                 for (const Rule& r : g_rules[p][u]) {
                     ConfigInfo ci;
-                    if (!config_info(p, r.idx, &ci)) continue;
+                    if (r.idx < 0 || !config_info(p, r.idx, &ci)) continue;
                     std::fprintf(f,
                                  "%s\n  {\"prec\": \"%c\", \"uplo\": \"%c\", \"n_lo\": %d, "
                                  "\"n_hi\": %d, \"waves\": %d, \"cols_per_wave\": %d, "
@@ -589,9 +647,8 @@ int xsymv_load_config(const char* path)
             if (ok) v[i] = std::atoi(s->c_str());
         }
         if (!ok) continue;
-        const char* pc = std::strchr(PREC_CHARS, (*ps)[0]);
-        if (!pc || *pc == 0) continue;
-        const int prec = (int)(pc - PREC_CHARS);
+        const int prec = prec_of_char((*ps)[0]);
+        if (prec < 0) continue;
         const int idx = find_config(prec, v[2], v[3], v[4], v[5], v[6], v[7]);
         if (idx < 0) continue;
         if (xsymv_select_config(prec, (*us)[0], v[0], v[1], idx) == 0) ++loaded;

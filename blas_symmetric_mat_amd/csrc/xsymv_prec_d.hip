@@ -20,6 +20,8 @@ template <> const std::vector<KernelSet<double>>& kernel_sets<double>()
         make_strip<double, 4, 1, 4, true>(),              // strip: R 512, 4 KB runs, G 4
         make_strip<double, 4, 4, 4, false>(),             // strip: R 2048, 16 KB runs, G 4, cached
         make_strip<double, 4, 2, 8, false>(),             // strip: R 1024, 8 KB runs, G 8, cached
+        make_strip<double, 8, 2, 4, true>(),              // strip: R 2048, 16 KB runs, G 4
+        make_strip<double, 8, 1, 8, true>(),              // strip: R 1024, 8 KB runs, G 8
     };
     return v;
 }

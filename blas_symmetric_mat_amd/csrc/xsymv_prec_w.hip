@@ -17,6 +17,8 @@ template <> const std::vector<KernelSet<ddreal>>& kernel_sets<ddreal>()
         make_strip<ddreal, 8, 1, 4, true>(),              // strip: R 512, 8 KB runs, G 4
         make_strip<ddreal, 4, 1, 4, true>(),              // strip: R 256, 4 KB runs, G 4
         make_strip<ddreal, 4, 2, 2, true>(),              // strip: R 512, 8 KB runs, G 2
+        make_strip<ddreal, 8, 2, 4, true>(),              // strip: R 1024, 16 KB runs, G 4
+        make_strip<ddreal, 4, 4, 4, true>(),              // strip: R 1024, 16 KB runs, G 4
     };
     return v;
 }

@@ -17,6 +17,8 @@ template <> const std::vector<KernelSet<cf64>>& kernel_sets<cf64>()
         make_strip<cf64, 8, 1, 4, true>(),                // strip: R 512, 8 KB runs, G 4
         make_strip<cf64, 4, 1, 4, true>(),                // strip: R 256, 4 KB runs, G 4
         make_strip<cf64, 4, 4, 4, false>(),               // strip: R 1024, 16 KB runs, G 4, cached
+        make_strip<cf64, 8, 2, 4, true>(),                // strip: R 1024, 16 KB runs, G 4
+        make_strip<cf64, 4, 4, 4, true>(),                // strip: R 1024, 16 KB runs, G 4
     };
     return v;
 }

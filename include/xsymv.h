@@ -94,8 +94,10 @@ int xsymv_w(char uplo, int n, xdd alpha, const xdd *A, int lda,
             void *stream);
 
 /* Bytes of device workspace one call of precision `prec` and order n uses
- * with the currently selected tile configuration (0 for n == 0; -1 cast to
- * size_t for a bad precision code). */
+ * with the configuration selected for it now, on the current device (0 for
+ * n == 0; -1 cast to size_t for a bad precision code, or when the device
+ * cannot be queried: the row-strip family's split depends on how many of
+ * its workgroups the device holds at once). */
 size_t xsymv_workspace_bytes(int prec, char uplo, int n);
 
 /* Release every workspace and cached tile plan of the current device
@@ -117,7 +119,13 @@ int xsymv_config_info(int prec, int idx, int *waves, int *cols_per_wave,
 
 /* Select the configuration used for precision `prec`, uplo and every n in
  * [n_lo, n_hi] (later selections take precedence).  idx = -1 restores the
- * built-in default.  Returns 0 or -1 for bad arguments. */
+ * built-in choice for that range.  Returns 0 or -1 for bad arguments.
+ *
+ * Built-in choice: per (precision, uplo, range of n), the configuration the
+ * on-device autotuner measured fastest on MI355X over a grid of orders from
+ * 64 to 32768 (the counterpart of the report's per-size rules, §3 Table 3);
+ * entry 0 where no rule applies.  Caller selections (this call, autotune,
+ * load_config) take precedence over it. */
 int xsymv_select_config(int prec, char uplo, int n_lo, int n_hi, int idx);
 /* Configuration index that a call (prec, uplo, n) would use now. */
 int xsymv_current_config(int prec, char uplo, int n);
@@ -142,8 +150,8 @@ int xsymv_autotune(int prec, char uplo, int n, int n_lo, int n_hi, int reps,
  * ...]}.  Rules are matched to compiled
  * configurations by shape.  save: 0 or -1 (cannot write).  load: number of
  * rules installed (appended after the current ones, so they take
- * precedence), -1 (cannot read) or -2 (malformed).  clear: drop every rule
- * (back to the built-in defaults). */
+ * precedence), -1 (cannot read) or -2 (malformed).  clear: drop every caller
+ * rule (back to the built-in choice).  save writes the caller rules only. */
 int xsymv_save_config(const char *path);
 int xsymv_load_config(const char *path);
 int xsymv_clear_config(void);

@@ -61,25 +61,57 @@ def test_config_tables():
             assert 64 % ci["cols_per_wave"] == 0
         with pytest.raises(IndexError):
             X.config_info(p, k)
-        assert X.current_config(p, "L", 1000) == 0
+    X.clear_config()
+    builtin = {u: [X.current_config("d", u, n) for n in (150, 201)] for u in "LU"}
     X.select_config("d", "U", 100, 200, 1)
     assert X.current_config("d", "U", 150) == 1
-    assert X.current_config("d", "U", 201) == 0
-    assert X.current_config("d", "L", 150) == 0
-    X.select_config("d", "U", 100, 200, -1)
-    assert X.current_config("d", "U", 150) == 0
+    assert X.current_config("d", "U", 201) == builtin["U"][1]
+    assert X.current_config("d", "L", 150) == builtin["L"][0]
+    X.select_config("d", "U", 100, 200, -1)  # back to the built-in choice
+    assert X.current_config("d", "U", 150) == builtin["U"][0]
     with pytest.raises(ValueError):
         X.select_config("d", "U", 0, 10, 99)
+    X.clear_config()
+
+
+def test_builtin_rules_match_sweep_record():
+    """The rules compiled into the library are the ones the committed sweep
+    record yields (csrc/xsymv_tuned.inc regenerated from it), and they cover
+    every order."""
+    import json
+    from blas_symmetric_mat_amd import tune_sweep
+    here = os.path.dirname(X.LIB_PATH)
+    with open(os.path.join(here, "tuned", "mi355x_sweep.json")) as f:
+        record = json.load(f)
+    rows = tune_sweep.rules_from_record(record)
+    assert rows
+    X.clear_config()
+    for r in rows:
+        for n in {r["n_lo"], r["n_hi"], (r["n_lo"] + r["n_hi"]) // 2}:
+            ci = X.config_info(r["prec"], X.current_config(r["prec"], r["uplo"], n))
+            assert all(ci[k] == r[k] for k in tune_sweep.SHAPE_KEYS), (r, n)
+    for p in "sdczw":
+        for u in "LU":
+            spans = sorted((r["n_lo"], r["n_hi"]) for r in rows if r["prec"] == p and r["uplo"] == u)
+            assert spans[0][0] == 0 and spans[-1][1] == 2**31 - 1
+            assert all(a[1] + 1 == b[0] for a, b in zip(spans, spans[1:]))
 
 
 def test_workspace_bytes_grow_with_n():
-    a = X.workspace_bytes("d", "L", 1000)
-    b = X.workspace_bytes("d", "L", 4000)
-    assert 0 < a < b
-    assert X.workspace_bytes("d", "L", 0) == 0
-    ci = X.config_info("d", 0)
-    P = (4000 + ci["panel"] - 1) // ci["panel"]
-    assert b >= P * 4000 * 8
+    # a tile-family configuration: its workspace needs no device query (the
+    # strip family's depends on how many workgroups the device holds)
+    idx = next(i for i in range(X.num_configs("d")) if X.config_info("d", i)["column_runs"] < 4)
+    X.select_config("d", "L", 0, 1 << 30, idx)
+    try:
+        a = X.workspace_bytes("d", "L", 1000)
+        b = X.workspace_bytes("d", "L", 4000)
+        assert 0 < a < b
+        assert X.workspace_bytes("d", "L", 0) == 0
+        ci = X.config_info("d", idx)
+        P = (4000 + ci["panel"] - 1) // ci["panel"]
+        assert b >= P * 4000 * 8
+    finally:
+        X.clear_config()
 
 
 @pytest.mark.parametrize("uplo", ["L", "U"])
