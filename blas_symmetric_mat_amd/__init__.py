@@ -101,7 +101,7 @@ def library():
             lib.xsymv_config_workgroups.restype = ci
             lib.xsymv_config_workgroups.argtypes = [ci, ci, cc]
             lib.xsymv_strip_plan.restype = ci
-            lib.xsymv_strip_plan.argtypes = [cc, ci, ci, ci, ip, ci, ip, ip, ci]
+            lib.xsymv_strip_plan.argtypes = [cc, ci, ci, ci, ci, ip, ci, ip, ip, ci]
             lib.xsymv_version.restype = ctypes.c_char_p
             lib.xsymv_version.argtypes = []
             _lib = lib
@@ -255,16 +255,18 @@ def config_workgroups(prec: str, idx: int, uplo: str = "L") -> int:
     return library().xsymv_config_workgroups(PREC_CODE[prec], idx, uplo.encode()[:1])
 
 
-def strip_plan(uplo: str, n: int, R: int, G: int):
-    """The row-strip work split (host computation): (blocks [G x 4]:
-    first, end, first slot, first strip), strip_base [NS+1], seg_base [NS+1]."""
+def strip_plan(uplo: str, n: int, R: int, G: int, split: int = 0):
+    """The row-strip work split (host computation) under cost model `split`
+    (0: strip height per column, doubled in the triangle; 1: stored rows plus
+    strip height): (blocks [G x 4]: first, end, first slot, first strip),
+    strip_base [NS+1], seg_base [NS+1]."""
     import numpy as np
     ns = (n + R - 1) // R
     blocks = np.zeros((G, 4), dtype=np.int32)
     sb = np.zeros(ns + 1, dtype=np.int32)
     segb = np.zeros(ns + 1, dtype=np.int32)
     ip = ctypes.POINTER(ctypes.c_int)
-    k = library().xsymv_strip_plan(uplo.encode()[:1], n, R, G, blocks.ctypes.data_as(ip), G,
+    k = library().xsymv_strip_plan(uplo.encode()[:1], n, R, G, split, blocks.ctypes.data_as(ip), G,
                                     sb.ctypes.data_as(ip), segb.ctypes.data_as(ip), ns + 1)
     if k < 0:
         raise ValueError(f"xsymv_strip_plan failed ({k})")

@@ -27,7 +27,7 @@ std::mutex g_dev_mu;
 
 using PlanKey = std::tuple<int, int, int, int, int>;  // upper, n, NB, R, device
 
-using StripKey = std::tuple<int, int, int, int>;  // upper, n, R, G
+using StripKey = std::tuple<int, int, int, int, int>;  // upper, n, R, G, split
 
 struct DeviceState {
     std::mutex mu;
@@ -71,8 +71,9 @@ void build_plan_host(bool upper, int n, int NB, int R, std::vector<TileDesc>& ti
     tiles.insert(tiles.end(), full.begin(), full.end());
 }
 
-void build_strip_plan_host(bool upper, int n, int R, int G, std::vector<StripBlock>& blocks,
-                           std::vector<int>& strip_base, std::vector<int>& seg_base, int& NS)
+void build_strip_plan_host(bool upper, int n, int R, int G, int split,
+                           std::vector<StripBlock>& blocks, std::vector<int>& strip_base,
+                           std::vector<int>& seg_base, int& NS)
 {
     NS = (n + R - 1) / R;
     strip_base.assign(NS + 1, 0);
@@ -81,12 +82,16 @@ void build_strip_plan_host(bool upper, int n, int R, int G, std::vector<StripBlo
         strip_base[i + 1] = strip_base[i] + width;
     }
     const long long total_pos = strip_base[NS];
-    // cost of one column of a strip: the strip's rows (a workgroup's waves
-    // each read their own rows of the column), with columns of the diagonal
-    // triangle weighted by DIAG_COST/4 (one wave there takes the element-load
-    // path), plus a fixed per-column share for the reductions
+    // Cost of one column of a strip, plus a fixed per-column share OVH for
+    // the reductions.  A workgroup's time per column is set mostly by its
+    // waves' per-column latency, not by how many of the column's rows are
+    // stored, so
+    //   split 0: the strip's height R per column, doubled in the diagonal
+    //            triangle (the wave holding the diagonal takes element loads
+    //            there, up to VEC of them per 16 bytes);
+    //   split 1: the stored rows of the column plus R (suits element types of
+    //            one or two elements per 16 bytes, whose band costs less).
     const long long OVH = 16;
-    const long long DIAG_COST = 8;
     std::vector<long long> prefix(total_pos + 1, 0);
     long long pos = 0;
     for (int i = 0; i < NS; ++i) {
@@ -95,7 +100,13 @@ void build_strip_plan_host(bool upper, int n, int R, int G, std::vector<StripBlo
         for (int t = 0; t < strip_base[i + 1] - strip_base[i]; ++t, ++pos) {
             const int j = cfirst + t;
             const bool tri = upper ? (j < rs1) : (j >= rs0);
-            const long long c = tri ? rows * DIAG_COST / 4 : rows;
+            long long c;
+            if (split == 0) {
+                c = tri ? 2ll * rows : rows;
+            } else {
+                const long long stored = !tri ? rows : (upper ? (j - rs0 + 1) : (rs1 - j));
+                c = stored + R;
+            }
             prefix[pos + 1] = prefix[pos] + c + OVH;
         }
     }
@@ -196,11 +207,11 @@ int resident_blocks(const void* kernel, int threads, int* out)
     return 0;
 }
 
-int get_strip_plan(DeviceState* ds, int dev, bool upper, int n, int R, int G, hipStream_t stream,
-                   const StripPlan** out)
+int get_strip_plan(DeviceState* ds, int dev, bool upper, int n, int R, int G, int split,
+                   hipStream_t stream, const StripPlan** out)
 {
     (void)dev;
-    StripKey key{upper ? 1 : 0, n, R, G};
+    StripKey key{upper ? 1 : 0, n, R, G, split};
     auto it = ds->strip_plans.find(key);
     if (it != ds->strip_plans.end()) {
         *out = it->second.get();
@@ -210,7 +221,7 @@ int get_strip_plan(DeviceState* ds, int dev, bool upper, int n, int R, int G, hi
     std::vector<int> sb, segb;
     int NS = 0;
     int g = G;
-    build_strip_plan_host(upper, n, R, g, blocks, sb, segb, NS);
+    build_strip_plan_host(upper, n, R, g, split, blocks, sb, segb, NS);
     std::unique_ptr<StripPlan> plan(new StripPlan());
     plan->NS = NS;
     plan->G = (int)blocks.size();
@@ -692,16 +703,16 @@ int xsymv_config_workgroups(int prec, int idx, char uplo)
     return rc ? -rc : G;
 }
 
-int xsymv_strip_plan(char uplo, int n, int R, int G, int* blocks4, int max_blocks,
+int xsymv_strip_plan(char uplo, int n, int R, int G, int split, int* blocks4, int max_blocks,
                      int* strip_base, int* seg_base, int max_strips)
 {
     if (!(uplo == 'U' || uplo == 'u' || uplo == 'L' || uplo == 'l') || n <= 0 || R <= 0 ||
-        G <= 0)
+        G <= 0 || split < 0 || split > 1)
         return -1;
     std::vector<StripBlock> blocks;
     std::vector<int> sb, segb;
     int NS = 0;
-    build_strip_plan_host(uplo == 'U' || uplo == 'u', n, R, G, blocks, sb, segb, NS);
+    build_strip_plan_host(uplo == 'U' || uplo == 'u', n, R, G, split, blocks, sb, segb, NS);
     if ((int)blocks.size() > max_blocks || NS + 1 > max_strips) return -2;
     for (size_t b = 0; b < blocks.size(); ++b) {
         blocks4[4 * b + 0] = blocks[b].u0;

@@ -41,7 +41,8 @@ struct ConfigInfo {
     int W, CW, S, H, NT, XLDS;
     int RUNS;  // 0: symv_tiles; 1: symv_runs; 2: symv_runs with the next run
                // prefetched; 3: symv_block; 4: symv_strip (CW = column group,
-               // S = W * stripes per wave)
+               // S = W * stripes per wave, work split by strip height);
+               // 5: symv_strip, work split by stored rows + strip height
     int NB() const { return W * CW; }
     bool strip() const { return RUNS >= 4; }
     int R() const { return S * H; }
@@ -77,10 +78,11 @@ KernelSet<T> make_block()
 
 // Row-strip, evenly split configurations: W waves, SW stripes per wave,
 // column groups of G.
-template <class T, int W, int SW, int G, bool NT>
+template <class T, int W, int SW, int G, bool NT, int SPLIT = 0>
 KernelSet<T> make_strip()
 {
-    KernelSet<T> k{nullptr, nullptr, ConfigInfo{W, G, W * SW, 64 * Elem<T>::VEC, NT ? 1 : 0, 0, 4}};
+    KernelSet<T> k{nullptr, nullptr,
+                   ConfigInfo{W, G, W * SW, 64 * Elem<T>::VEC, NT ? 1 : 0, 0, 4 + SPLIT}};
     k.strip_lower = &symv_strip<T, false, W, SW, G, NT, STRIP_CBUF>;
     k.strip_upper = &symv_strip<T, true, W, SW, G, NT, STRIP_CBUF>;
     return k;
@@ -138,12 +140,12 @@ struct StripPlan {
     int* d_seg_base = nullptr;
     void* h_pinned = nullptr;  // pinned source of the one upload
 };
-void build_strip_plan_host(bool upper, int n, int R, int G, std::vector<StripBlock>& blocks,
+void build_strip_plan_host(bool upper, int n, int R, int G, int split, std::vector<StripBlock>& blocks,
                            std::vector<int>& strip_base, std::vector<int>& seg_base, int& NS);
 
 struct DeviceState;
 DeviceState* device_state(int dev);
-int get_strip_plan(DeviceState* ds, int dev, bool upper, int n, int R, int G, hipStream_t stream,
+int get_strip_plan(DeviceState* ds, int dev, bool upper, int n, int R, int G, int split, hipStream_t stream,
                    const StripPlan** out);
 // Workgroups of `kernel` (block size `threads`) the current device holds at once.
 int resident_blocks(const void* kernel, int threads, int* out);
@@ -233,7 +235,7 @@ int strip_run(const KernelSet<T>& ks, bool upper, int n, T alpha, const T* A, in
     int rc = resident_blocks((const void*)kern, threads, &G);
     if (rc) return rc;
     const StripPlan* plan = nullptr;
-    rc = get_strip_plan(ds, dev, upper, n, R, G, stream, &plan);
+    rc = get_strip_plan(ds, dev, upper, n, R, G, ks.info.RUNS - 4, stream, &plan);
     if (rc) return rc;
     void* ws = nullptr;
     rc = get_workspace(ds, stream, strip_workspace_bytes<T>(plan->nseg, R, plan->NS, n), &ws);
@@ -490,7 +492,7 @@ size_t ws_bytes(char uplo, int n)
         std::vector<StripBlock> blocks;
         std::vector<int> sb, segb;
         int NS = 0;
-        build_strip_plan_host(upper, n, ci.R(), G, blocks, sb, segb, NS);
+        build_strip_plan_host(upper, n, ci.R(), G, ci.RUNS - 4, blocks, sb, segb, NS);
         return strip_workspace_bytes<T>(segb[NS], ci.R(), NS, n);
     }
     std::vector<TileDesc> tiles;

@@ -107,11 +107,15 @@ int xsymv_release(void);
 /* Tile configurations (the autotuner's search space, report §3 Table 1
  * plays this role for the report's CUDA kernels).  Each precision has a
  * fixed list of compiled configurations; xsymv_config_info describes entry
- * `idx`: waves per workgroup, columns per wave, stripes per tile, rows per
- * stripe, non-temporal loads of A (0/1), x rows staged in LDS (0/1), and the
- * kernel family (1: each wave walks its columns one contiguous run at a time
- * with the next run prefetched; 0: the whole tile unrolled).  Any output
- * pointer may be NULL.  Returns 0, or -1 for a bad index. */
+ * `idx`: waves per workgroup, columns per wave (row-strip family: columns
+ * per group), stripes per tile (row-strip: waves x stripes per wave), rows
+ * per stripe, non-temporal loads of A (0/1), x rows staged in LDS (0/1), and
+ * the kernel family: 0 tiles, whole tile unrolled; 1 tiles, each wave walks
+ * its columns one contiguous run at a time; 2 the same with the next run
+ * prefetched; 3 tiles, all waves of a workgroup on one column; 4 row strips,
+ * work split by strip height; 5 row strips, work split by stored rows plus
+ * strip height.  Any output pointer may be NULL.  Returns 0, or -1 for a bad
+ * index. */
 int xsymv_num_configs(int prec);
 int xsymv_config_info(int prec, int idx, int *waves, int *cols_per_wave,
                       int *stripes, int *rows_per_stripe, int *nontemporal,
@@ -164,22 +168,25 @@ int xsymv_clear_config(void);
 int xsymv_timing_enable(int on);
 int xsymv_timing_read(float *main_ms, float *merge_ms, int max);
 
-/* Workgroups a row-strip configuration (column_runs == 4) is launched with
+/* Workgroups a row-strip configuration (column_runs 4 or 5) is launched with
  * on the current device: the number of its workgroups the device holds at
  * once.  0 for other families, -1 for a bad index, -(1000 + hipError_t) on a
  * runtime error. */
 int xsymv_config_workgroups(int prec, int idx, char uplo);
 
-/* The row-strip work split the library uses for order n, strips of R rows
- * and G workgroups (host computation, no device work): writes per workgroup
+/* The row-strip work split the library uses for order n, strips of R rows,
+ * G workgroups and cost model `split` (0: every column of a strip costs the
+ * strip's height, doubled in its diagonal triangle -- family 4; 1: a column
+ * costs its stored rows plus the strip's height -- family 5), a host
+ * computation with no device work: writes per workgroup
  * {first, end} of its range in the strips' concatenated column sequence,
  * its first segment slot and the strip of `first` into blocks4 (4 ints per
  * workgroup), the sequence position where each strip starts (NS+1 entries)
  * into strip_base and each strip's first segment slot (NS+1 entries, the
  * last = total segments) into seg_base.  Returns the number of workgroups
  * used, -1 for bad arguments, -2 if an output is too small. */
-int xsymv_strip_plan(char uplo, int n, int R, int G, int *blocks4, int max_blocks,
-                     int *strip_base, int *seg_base, int max_strips);
+int xsymv_strip_plan(char uplo, int n, int R, int G, int split, int *blocks4,
+                     int max_blocks, int *strip_base, int *seg_base, int max_strips);
 
 /* Library version string. */
 const char *xsymv_version(void);

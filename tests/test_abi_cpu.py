@@ -114,14 +114,15 @@ def test_workspace_bytes_grow_with_n():
         X.clear_config()
 
 
+@pytest.mark.parametrize("split", [0, 1])
 @pytest.mark.parametrize("uplo", ["L", "U"])
 @pytest.mark.parametrize("n,R,G", [(1, 64, 7), (100, 64, 3), (1000, 256, 37), (1031, 128, 200),
                                    (4096, 1024, 1792), (10007, 2048, 1792), (5000, 512, 1)])
-def test_strip_plan_covers_triangle_once(uplo, n, R, G):
+def test_strip_plan_covers_triangle_once(uplo, n, R, G, split):
     """Emulate the strip kernel's walk: every stored element (i, j) is visited
     by exactly one workgroup, every (strip, column) sum is written once, and
     the segments of each strip are the slots the merge reads."""
-    blocks, sb, segb = X.strip_plan(uplo, n, R, G)
+    blocks, sb, segb = X.strip_plan(uplo, n, R, G, split)
     NS = (n + R - 1) // R
     assert sb[0] == 0 and segb[0] == 0
     upper = uplo == "U"
@@ -161,3 +162,16 @@ def test_strip_plan_covers_triangle_once(uplo, n, R, G):
         strips = sorted(i for (i, jj) in colsum_writes if jj == j)
         I = j // R
         assert strips == (list(range(0, I + 1)) if upper else list(range(I, NS)))
+
+
+def test_bench_labels_every_configuration():
+    """bench.py names the kernel of whatever configuration runs."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "bench", os.path.join(os.path.dirname(os.path.dirname(X.LIB_PATH)), "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    for p in "sdczw":
+        for i in range(X.num_configs(p)):
+            for u in "LU":
+                assert bench.kernel_label(X, p, u, i).startswith("symv_")
