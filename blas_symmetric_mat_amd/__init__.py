@@ -22,7 +22,7 @@ __all__ = ["xsymv_s", "xsymv_d", "xhemv_c", "xhemv_z", "xsymv_w", "XsymvError",
            "library", "LIB_PATH", "PREC_CODE", "workspace_bytes", "num_configs",
            "config_info", "select_config", "current_config", "timing_enable",
            "timing_read", "release", "version", "autotune", "save_config", "load_config",
-           "clear_config", "strip_plan", "config_workgroups"]
+           "clear_config", "strip_plan", "config_workgroups", "set_workspace"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libxsymv.so")
 PREC_CODE = {"s": 0, "d": 1, "c": 2, "z": 3, "w": 4}
@@ -31,7 +31,9 @@ PREC_CODE = {"s": 0, "d": 1, "c": 2, "z": 3, "w": 4}
 class XsymvError(RuntimeError):
     def __init__(self, name, code):
         self.code = code
-        if code >= 1000:
+        if code == 2000:
+            msg = f"{name}: the workspace installed for this stream is too small"
+        elif code >= 1000:
             msg = f"{name}: HIP runtime error {code - 1000}"
         else:
             msg = f"{name}: illegal value of argument {-code}"
@@ -77,6 +79,8 @@ def library():
             lib.xsymv_workspace_bytes.argtypes = [ci, cc, ci]
             lib.xsymv_release.restype = ci
             lib.xsymv_release.argtypes = []
+            lib.xsymv_set_workspace.restype = ci
+            lib.xsymv_set_workspace.argtypes = [vp, ctypes.c_size_t, vp]
             lib.xsymv_num_configs.restype = ci
             lib.xsymv_num_configs.argtypes = [ci]
             ip = ctypes.POINTER(ci)
@@ -271,6 +275,21 @@ def strip_plan(uplo: str, n: int, R: int, G: int, split: int = 0):
     if k < 0:
         raise ValueError(f"xsymv_strip_plan failed ({k})")
     return blocks[:k], sb, segb
+
+
+def set_workspace(buf, nbytes: int | None = None, stream=None) -> None:
+    """Install a caller-owned device buffer (a torch tensor or an address) as
+    the workspace of `stream`; ``None`` removes it.  ``nbytes`` defaults to
+    the tensor's size in bytes."""
+    if buf is None:
+        ptr, nbytes = None, 0
+    else:
+        ptr = _addr(buf)
+        if nbytes is None:
+            nbytes = buf.numel() * buf.element_size()
+    rc = library().xsymv_set_workspace(ptr, nbytes, _stream(stream))
+    if rc != 0:
+        raise XsymvError("xsymv_set_workspace", rc)
 
 
 def release() -> None:

@@ -33,7 +33,7 @@ struct DeviceState {
     std::mutex mu;
     std::map<PlanKey, std::unique_ptr<Plan>> plans;
     std::map<StripKey, std::unique_ptr<StripPlan>> strip_plans;
-    std::map<hipStream_t, std::pair<void*, size_t>> workspaces;
+    std::map<hipStream_t, Workspace> workspaces;
     std::map<std::pair<const void*, int>, int> resident;  // (kernel, threads) -> blocks
 };
 
@@ -250,19 +250,20 @@ int get_strip_plan(DeviceState* ds, int dev, bool upper, int n, int R, int G, in
 int get_workspace(DeviceState* ds, hipStream_t stream, size_t bytes, void** out)
 {
     auto& ws = ds->workspaces[stream];
-    if (ws.second < bytes) {
-        if (ws.first) {
+    if (ws.bytes < bytes) {
+        if (!ws.owned) return ERR_WORKSPACE;  // the caller's buffer is too small
+        if (ws.ptr) {
             // the old buffer may still be in use by work queued on this stream
             XSYMV_HIP(hipStreamSynchronize(stream));
-            XSYMV_HIP(hipFree(ws.first));
-            ws.first = nullptr;
-            ws.second = 0;
+            XSYMV_HIP(hipFree(ws.ptr));
+            ws.ptr = nullptr;
+            ws.bytes = 0;
         }
         const size_t grown = std::max(bytes, (size_t)1 << 20);
-        XSYMV_HIP(hipMalloc(&ws.first, grown));
-        ws.second = grown;
+        XSYMV_HIP(hipMalloc(&ws.ptr, grown));
+        ws.bytes = grown;
     }
-    *out = ws.first;
+    *out = ws.ptr;
     return 0;
 }
 
@@ -479,6 +480,25 @@ size_t xsymv_workspace_bytes(int prec, char uplo, int n)
     }
 }
 
+int xsymv_set_workspace(void* dev_ptr, size_t bytes, void* stream)
+{
+    if (!dev_ptr && bytes != 0) return -2;
+    int dev = 0;
+    XSYMV_HIP(hipGetDevice(&dev));
+    DeviceState* ds = device_state(dev);
+    std::lock_guard<std::mutex> lk(ds->mu);
+    const hipStream_t st = (hipStream_t)stream;
+    auto it = ds->workspaces.find(st);
+    if (it != ds->workspaces.end()) {
+        // the previous buffer may still be in use by work queued on this stream
+        XSYMV_HIP(hipStreamSynchronize(st));
+        if (it->second.owned && it->second.ptr) XSYMV_HIP(hipFree(it->second.ptr));
+        ds->workspaces.erase(it);
+    }
+    if (dev_ptr) ds->workspaces[st] = Workspace{dev_ptr, bytes, false};
+    return 0;
+}
+
 int xsymv_release(void)
 {
     int dev = 0;
@@ -487,7 +507,7 @@ int xsymv_release(void)
     DeviceState* ds = device_state(dev);
     std::lock_guard<std::mutex> lk(ds->mu);
     for (auto& kv : ds->workspaces)
-        if (kv.second.first) XSYMV_HIP(hipFree(kv.second.first));
+        if (kv.second.owned && kv.second.ptr) XSYMV_HIP(hipFree(kv.second.ptr));
     ds->workspaces.clear();
     for (auto& kv : ds->plans) {
         Plan* p = kv.second.get();

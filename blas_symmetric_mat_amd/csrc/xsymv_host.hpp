@@ -27,6 +27,15 @@
 namespace xsymv {
 
 constexpr int ERR_HIP = 1000;
+constexpr int ERR_WORKSPACE = 2000;  // a caller-installed workspace is too small
+
+// Device workspace of one (device, stream): library-owned (grown with
+// hipMalloc on demand) or installed by the caller (never freed here).
+struct Workspace {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+    bool owned = true;
+};
 constexpr int MERGE_SPLIT = 16;  // waves sharing one 64-row block of the merge
 constexpr int STRIP_CBUF = 256;  // columns a strip workgroup buffers before adding waves
 

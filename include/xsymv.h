@@ -30,8 +30,9 @@
  * Ownership: A, x and y belong to the caller and must stay valid until the
  * work enqueued on `stream` has finished.  The library keeps a device
  * workspace per (device, stream), allocated on first use and grown as needed
- * (hipMalloc), never exposed in results.  Calls on one stream are ordered;
- * calls on different streams use different workspaces.
+ * (hipMalloc), never exposed in results, unless the caller installs one with
+ * xsymv_set_workspace.  Calls on one stream are ordered; calls on different
+ * streams use different workspaces.
  *
  * Behaviour: every call is asynchronous on `stream` (it enqueues kernels and
  * returns).  Results are bitwise identical from run to run for the same
@@ -53,6 +54,9 @@
  *  -10  incy == 0
  *  1000 + e  the HIP runtime returned error e (hipError_t) on allocation,
  *            copy or launch.
+ *  2000      the workspace the caller installed for this stream
+ *            (xsymv_set_workspace) is smaller than the call needs; nothing
+ *            was enqueued.
  */
 #ifndef XSYMV_H
 #define XSYMV_H
@@ -100,8 +104,22 @@ int xsymv_w(char uplo, int n, xdd alpha, const xdd *A, int lda,
  * its workgroups the device holds at once). */
 size_t xsymv_workspace_bytes(int prec, char uplo, int n);
 
-/* Release every workspace and cached tile plan of the current device
- * (synchronises the device first).  Returns 0 or 1000 + hipError_t. */
+/* Install a caller-owned device buffer of `bytes` bytes as the workspace of
+ * `stream` on the current device (the optional caller-owned workspace of the
+ * boundary; size it with xsymv_workspace_bytes).  Calls on that stream then
+ * use it and never allocate a workspace; a call that needs more than `bytes`
+ * returns 2000.  The buffer must stay valid, and must not be used by anything
+ * else, while calls on the stream may still run; the library never frees it.
+ * dev_ptr = NULL (with bytes = 0) removes an installed buffer, so the
+ * library owns the stream's workspace again.  Replacing or removing waits for
+ * the work queued on `stream` and frees a library-owned buffer of it.
+ * Returns 0, -2 (NULL with bytes > 0) or 1000 + hipError_t.  Cached plans
+ * (a few KB per order and configuration) are still allocated by the library. */
+int xsymv_set_workspace(void *dev_ptr, size_t bytes, void *stream);
+
+/* Release every library-owned workspace and cached tile plan of the current
+ * device and forget installed workspaces (synchronises the device first).
+ * Returns 0 or 1000 + hipError_t. */
 int xsymv_release(void);
 
 /* Tile configurations (the autotuner's search space, report §3 Table 1

@@ -175,3 +175,8 @@ def test_bench_labels_every_configuration():
         for i in range(X.num_configs(p)):
             for u in "LU":
                 assert bench.kernel_label(X, p, u, i).startswith("symv_")
+
+
+def test_set_workspace_argument_check():
+    # a NULL buffer with a size is refused before any device query
+    assert X.library().xsymv_set_workspace(None, 64, None) == -2

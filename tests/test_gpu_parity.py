@@ -205,3 +205,43 @@ def test_bitwise_repeatable(prec):
         dp = G.DeviceProblem(p)
         digests = {G.digest(dp.run()) for _ in range(10)}
         assert len(digests) == 1
+
+
+# ------------------------------------------------- caller-installed workspace
+
+@pytest.mark.parametrize("prec", PRECS)
+@pytest.mark.parametrize("uplo", ["L", "U"])
+def test_installed_workspace(prec, uplo):
+    """A workspace installed with xsymv_set_workspace gives bit-identical
+    results to the library-owned one; one that is too small is refused with
+    2000 before any device work (y untouched); removing it restores the
+    library-owned workspace."""
+    import torch
+    import blas_symmetric_mat_amd as X
+    n = 1500
+    G.log(f"installed workspace {prec} {uplo} n={n}")
+    p = problem(prec, uplo, n, 3, seed=77)
+    d = G.DeviceProblem(p)
+    ref = d.run()
+    stream = torch.cuda.Stream()
+    need = X.workspace_bytes(prec, uplo, n)
+    assert 0 < need < 1 << 40
+    buf = torch.empty(need, dtype=torch.uint8, device="cuda")
+    small = torch.empty(need // 2, dtype=torch.uint8, device="cuda")
+    try:
+        with torch.cuda.stream(stream):
+            X.set_workspace(buf, stream=stream)
+            got = d.run()
+            y0 = G.to_device(p.y)
+            X.set_workspace(small, stream=stream)
+            with pytest.raises(X.XsymvError) as e:
+                d.run_device(y0)
+            assert e.value.code == 2000
+            torch.cuda.synchronize()
+            assert G.digest(y0.cpu().numpy()) == G.digest(p.y)
+            X.set_workspace(None, stream=stream)
+            again = d.run()
+    finally:
+        X.set_workspace(None, stream=stream)
+    assert G.digest(got) == G.digest(ref)
+    assert G.digest(again) == G.digest(ref)
