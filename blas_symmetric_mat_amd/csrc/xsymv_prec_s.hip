@@ -24,6 +24,9 @@ template <> const std::vector<KernelSet<float>>& kernel_sets<float>()
         make_strip<float, 16, 1, 4, true, 1>(),           // strip: R 4096, 16 KB runs, G 4, split by stored rows
         make_strip<float, 8, 1, 4, true, 1>(),            // strip: R 2048, 8 KB runs, G 4, split by stored rows
         make_strip<float, 4, 2, 8, true, 1>(),            // strip: R 2048, 8 KB runs, G 8, split by stored rows
+        make_strip<float, 16, 1, 16, true>(),             // strip: R 4096, 16 KB runs, G 16
+        make_strip<float, 16, 1, 16, true, 1>(),          // strip: R 4096, 16 KB runs, G 16, split by stored rows
+        make_strip<float, 16, 1, 8, true>(),              // strip: R 4096, 16 KB runs, G 8
     };
     return v;
 }
