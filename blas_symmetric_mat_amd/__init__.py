@@ -22,7 +22,7 @@ __all__ = ["xsymv_s", "xsymv_d", "xhemv_c", "xhemv_z", "xsymv_w", "XsymvError",
            "library", "LIB_PATH", "PREC_CODE", "workspace_bytes", "num_configs",
            "config_info", "select_config", "current_config", "timing_enable",
            "timing_read", "release", "version", "autotune", "save_config", "load_config",
-           "clear_config", "strip_plan", "config_workgroups", "set_workspace"]
+           "clear_config", "strip_plan", "config_workgroups", "set_workspace", "read_bandwidth"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libxsymv.so")
 PREC_CODE = {"s": 0, "d": 1, "c": 2, "z": 3, "w": 4}
@@ -106,6 +106,8 @@ def library():
             lib.xsymv_config_workgroups.argtypes = [ci, ci, cc]
             lib.xsymv_strip_plan.restype = ci
             lib.xsymv_strip_plan.argtypes = [cc, ci, ci, ci, ci, ip, ci, ip, ip, ci]
+            lib.xsymv_read_bandwidth.restype = ci
+            lib.xsymv_read_bandwidth.argtypes = [ctypes.c_size_t, ci, vp, fp, fp]
             lib.xsymv_version.restype = ctypes.c_char_p
             lib.xsymv_version.argtypes = []
             _lib = lib
@@ -290,6 +292,17 @@ def set_workspace(buf, nbytes: int | None = None, stream=None) -> None:
     rc = library().xsymv_set_workspace(ptr, nbytes, _stream(stream))
     if rc != 0:
         raise XsymvError("xsymv_set_workspace", rc)
+
+
+def read_bandwidth(nbytes: int = 4 << 30, reps: int = 10, stream=None):
+    """(median, best) GB/s of a plain streaming read of ``nbytes`` on the device."""
+    med = ctypes.c_float()
+    best = ctypes.c_float()
+    rc = library().xsymv_read_bandwidth(nbytes, reps, _stream(stream), ctypes.byref(med),
+                                        ctypes.byref(best))
+    if rc != 0:
+        raise XsymvError("xsymv_read_bandwidth", rc)
+    return med.value, best.value
 
 
 def release() -> None:

@@ -3,6 +3,7 @@
 // C ABI calls of include/xsymv.h.
 #include "xsymv_host.hpp"
 
+#include <algorithm>
 #include <cctype>
 #include <cstdio>
 #include <cstdlib>
@@ -466,6 +467,41 @@ bool parse_rules(const std::string& text, std::vector<JsonRule>& out)
 
 using namespace xsymv;
 
+// Plain streaming read, the reference point for "% of a measured
+// stream-read peak": workgroup b reads its own contiguous chunk of `per`
+// 16-byte vectors (non-temporal loads, U in flight per lane; `per` is a
+// multiple of 256*U, so no load is guarded).  Each workgroup writes one word
+// so the loads are not removed.
+template <int U>
+static __global__ __launch_bounds__(256) void read_probe(const xsymv::u32x4* __restrict__ a,
+                                                           long long per, uint32_t* out)
+{
+    const xsymv::u32x4* __restrict__ p = a + (long long)blockIdx.x * per;
+    uint32_t acc = 0;
+    for (long long i = threadIdx.x; i < per; i += 256 * U) {
+        xsymv::u32x4 v[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) v[k] = __builtin_nontemporal_load(p + i + k * 256);
+#pragma unroll
+        for (int k = 0; k < U; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+    }
+    __shared__ uint32_t red[256];
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t t = 0;
+        for (int k = 0; k < 256; ++k) t ^= red[k];
+        out[blockIdx.x] = t;
+    }
+}
+
+static __global__ __launch_bounds__(256) void fill_probe(uint32_t* buf, long long words)
+{
+    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < words;
+         i += (long long)gridDim.x * 256)
+        buf[i] = (uint32_t)(i * 2654435761u);
+}
+
 extern "C" {
 
 size_t xsymv_workspace_bytes(int prec, char uplo, int n)
@@ -478,6 +514,64 @@ size_t xsymv_workspace_bytes(int prec, char uplo, int n)
     case XSYMV_W: return ws_bytes<ddreal>(uplo, n);
     default: return (size_t)-1;
     }
+}
+
+int xsymv_read_bandwidth(size_t bytes, int reps, void* stream, float* gbps, float* best_gbps)
+{
+    if (bytes < ((size_t)64 << 20) || reps <= 0) return -1;
+    const hipStream_t st = (hipStream_t)stream;
+    const long long vecs = (long long)(bytes / 16);
+    constexpr int MAXB = 32768;
+    char* buf = nullptr;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    int rc = 0;
+    float best_med = 0.f, best_any = 0.f;
+    auto fail = [&](hipError_t e) { rc = ERR_HIP + (int)e; };
+    hipError_t e;
+    if ((e = hipMalloc((void**)&buf, (size_t)vecs * 16 + MAXB * 4)) != hipSuccess)
+        return ERR_HIP + (int)e;
+    uint32_t* out = reinterpret_cast<uint32_t*>(buf + (size_t)vecs * 16);
+    const auto* a = reinterpret_cast<const xsymv::u32x4*>(buf);
+    fill_probe<<<4096, 256, 0, st>>>(reinterpret_cast<uint32_t*>(buf), vecs * 4);
+    if ((e = hipGetLastError()) != hipSuccess) { fail(e); goto done; }
+    if ((e = hipEventCreate(&e0)) != hipSuccess || (e = hipEventCreate(&e1)) != hipSuccess) {
+        fail(e);
+        goto done;
+    }
+    // a few layouts (workgroups x loads in flight per lane); the best median wins
+    for (int blocks : {2048, 8192, MAXB}) {
+        for (int u : {4, 8}) {
+            const long long per = vecs / blocks / (256 * u) * (256 * u);
+            if (per == 0) continue;
+            std::vector<float> t;
+            for (int r = 0; r < reps + 1 && rc == 0; ++r) {
+                if ((e = hipEventRecord(e0, st)) != hipSuccess) { fail(e); break; }
+                if (u == 4)
+                    read_probe<4><<<blocks, 256, 0, st>>>(a, per, out);
+                else
+                    read_probe<8><<<blocks, 256, 0, st>>>(a, per, out);
+                if ((e = hipGetLastError()) != hipSuccess) { fail(e); break; }
+                if ((e = hipEventRecord(e1, st)) != hipSuccess) { fail(e); break; }
+                if ((e = hipEventSynchronize(e1)) != hipSuccess) { fail(e); break; }
+                float ms = 0.f;
+                if ((e = hipEventElapsedTime(&ms, e0, e1)) != hipSuccess) { fail(e); break; }
+                if (r >= 1) t.push_back(ms);
+            }
+            if (rc) goto done;
+            std::sort(t.begin(), t.end());
+            const double b = (double)per * blocks * 16;
+            best_med = std::max(best_med, (float)(b / (t[t.size() / 2] * 1e-3) / 1e9));
+            best_any = std::max(best_any, (float)(b / (t[0] * 1e-3) / 1e9));
+        }
+    }
+    if (gbps) *gbps = best_med;
+    if (best_gbps) *best_gbps = best_any;
+done:
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    (void)hipStreamSynchronize(st);
+    (void)hipFree(buf);
+    return rc;
 }
 
 int xsymv_set_workspace(void* dev_ptr, size_t bytes, void* stream)

@@ -206,6 +206,19 @@ int xsymv_config_workgroups(int prec, int idx, char uplo);
 int xsymv_strip_plan(char uplo, int n, int R, int G, int split, int *blocks4,
                      int max_blocks, int *strip_base, int *seg_base, int max_strips);
 
+/* Measurement helper: the device's plain streaming-read bandwidth, the
+ * reference for "% of a measured stream-read peak" (the report puts its
+ * results against both the specification and a measured bandwidth, §4).
+ * Allocates `bytes` (>= 64 MiB) of device memory, fills it, then, for each
+ * of a few layouts (2048, 8192 or 32768 workgroups of 256 lanes, each
+ * reading its own contiguous chunk with 4 or 8 non-temporal 16-byte loads in
+ * flight per lane), times `reps` launches (after one warm-up) on `stream`;
+ * frees the buffer and synchronises the stream.  Writes the best layout's
+ * median rate and the best single launch in GB/s (either may be NULL).
+ * Returns 0, -1 for bad arguments or 1000 + hipError_t. */
+int xsymv_read_bandwidth(size_t bytes, int reps, void *stream, float *gbps,
+                         float *best_gbps);
+
 /* Library version string. */
 const char *xsymv_version(void);
 
