@@ -207,6 +207,71 @@ def make_integer_problem(prec: str, uplo: str, n: int, lda: int | None = None, *
     return Problem(prec, uplo, n, lda, alpha, beta, A, x, y, name="integer")
 
 
+@dataclasses.dataclass
+class GemvProblem:
+    """One general matrix-vector call's arguments (host arrays): A is m x n
+    column-major with leading dimension lda; x has n elements for trans 'N'
+    and m otherwise, y the other length."""
+    prec: str
+    trans: str
+    m: int
+    n: int
+    lda: int
+    alpha: Any
+    beta: Any
+    A: np.ndarray
+    x: np.ndarray
+    y: np.ndarray
+    incx: int = 1
+    incy: int = 1
+    name: str = ""
+
+    @property
+    def lenx(self) -> int:
+        return self.n if self.trans in ("N", "n") else self.m
+
+    @property
+    def leny(self) -> int:
+        return self.m if self.trans in ("N", "n") else self.n
+
+
+def make_gemv_problem(prec: str, trans: str, m: int, n: int, lda: int | None = None, *,
+                      alpha: Any = 1.0, beta: Any = 1.0, seed: int = 0,
+                      a_dist: str = "uniform", xy_dist: str = "uniform",
+                      fill: float = np.nan, integer: tuple[int, int] | None = None,
+                      name: str = "") -> GemvProblem:
+    """Draw a general problem: A column by column (rows 0..m-1; padding rows
+    hold `fill`), then x, then y.  ``integer = (lo, hi)`` draws integers
+    instead."""
+    if prec not in PRECISIONS:
+        raise ValueError(prec)
+    lda = m if lda is None else lda
+    if lda < max(1, m):
+        raise ValueError("lda < max(1, m)")
+    rng = np.random.Generator(np.random.PCG64(seed))
+    A = np.empty((lda * n, 2), dtype=np.float64) if prec == "w" else \
+        np.empty(lda * n, dtype=_DTYPE[prec][0])
+    fillv = complex(fill, fill) if prec in ("c", "z") else fill
+    for j in range(n):
+        col = A[j * lda: (j + 1) * lda]
+        col[m:] = fillv
+        if integer is None:
+            draw_into(rng, prec, col[:m], a_dist)
+        else:
+            col[:m] = draw_integers(rng, prec, m, *integer)
+    lx, ly = (n, m) if trans in ("N", "n") else (m, n)
+    if integer is None:
+        x = draw(rng, prec, lx, xy_dist)
+        y = draw(rng, prec, ly, xy_dist)
+    else:
+        x = draw_integers(rng, prec, lx, *integer)
+        y = draw_integers(rng, prec, ly, *integer)
+        if prec == "w":
+            alpha = alpha if isinstance(alpha, tuple) else (float(alpha), 0.0)
+            beta = beta if isinstance(beta, tuple) else (float(beta), 0.0)
+    return GemvProblem(prec, trans, m, n, lda, alpha, beta, A, x, y, name=name)
+
+
 # --------------------------------------------------------------------------
 # The benchmark workloads, named by what they are.
 # --------------------------------------------------------------------------
@@ -251,3 +316,11 @@ def wsymv_lower_n8192(n: int = 8192) -> Problem:
     and lo = hi*u*2^-53; alpha = beta = (1, 0); seed 4."""
     return make_problem("w", "L", n, n, alpha=(1.0, 0.0), beta=(1.0, 0.0),
                         seed=4, name=f"wsymv-L-n{n}")
+
+
+def gemv_square(prec: str, trans: str, n: int) -> GemvProblem:
+    """xGEMV beside the [SD]SYMV sweep: m = n = lda, uniform A, x, y;
+    alpha = beta = 1; seed = n (the same draws as the full matrix a SYMV
+    problem of order n would need)."""
+    return make_gemv_problem(prec, trans, n, n, n, alpha=1.0, beta=1.0, seed=n,
+                             name=f"{prec}gemv-{trans}-n{n}")

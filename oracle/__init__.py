@@ -49,6 +49,7 @@ class _DD(ctypes.Structure):
 
 _SCALAR = {"s": ctypes.c_float, "d": ctypes.c_double, "c": _CF, "z": _CD, "w": _DD}
 _NAME = {"s": "ssymv", "d": "dsymv", "c": "chemv", "z": "zhemv", "w": "wsymv"}
+_GNAME = {"s": "sgemv", "d": "dgemv", "c": "cgemv", "z": "zgemv", "w": "wgemv"}
 _NP = {"s": np.float32, "d": np.float64, "c": np.complex64, "z": np.complex128,
        "w": np.float64}
 
@@ -63,6 +64,15 @@ def _declare(lib):
         g = getattr(lib, "oracle_" + nm + "_rows")
         g.restype = ci
         g.argtypes = [ctypes.c_char, ci, st, vp, ci, vp, ci, st, vp, ci,
+                      vp, ci, vp]
+    for p, nm in _GNAME.items():
+        st = _SCALAR[p]
+        f = getattr(lib, "oracle_" + nm)
+        f.restype = ci
+        f.argtypes = [ctypes.c_char, ci, ci, st, vp, ci, vp, ci, st, vp, ci]
+        g = getattr(lib, "oracle_" + nm + "_rows")
+        g.restype = ci
+        g.argtypes = [ctypes.c_char, ci, ci, st, vp, ci, vp, ci, st, vp, ci,
                       vp, ci, vp]
     for nm in ("oracle_dd_add", "oracle_dd_mul"):
         f = getattr(lib, nm)
@@ -148,6 +158,44 @@ class OracleLib:
         return self.symv_rows(p.prec, p.uplo, p.n, p.alpha, p.A, p.lda, p.x,
                               p.incx, p.beta, p.y, p.incy, rows)
 
+    def gemv(self, prec: str, trans: str, m: int, n: int, alpha, A, lda: int, x,
+             incx: int, beta, y, incy: int) -> int:
+        """y := alpha*op(A)*x + beta*y in place, from the definition.
+        Returns the status code (0 = ok, negative = bad argument)."""
+        _check_dtype(prec, A, x, y)
+        f = getattr(self._lib, "oracle_" + _GNAME[prec])
+        return f(_uplo(trans), m, n, scalar(prec, alpha), _ptr(A), lda, _ptr(x),
+                 incx, scalar(prec, beta), _ptr(y), incy)
+
+    def gemv_rows(self, prec: str, trans: str, m: int, n: int, alpha, A, lda: int,
+                  x, incx: int, beta, y, incy: int, rows) -> np.ndarray:
+        """Output elements ``rows`` of alpha*op(A)*x + beta*y (y not modified)."""
+        _check_dtype(prec, A, x, y)
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        shape = (len(rows), 2) if prec == "w" else (len(rows),)
+        out = np.empty(shape, dtype=_NP[prec])
+        f = getattr(self._lib, "oracle_" + _GNAME[prec] + "_rows")
+        rc = f(_uplo(trans), m, n, scalar(prec, alpha), _ptr(A), lda, _ptr(x),
+               incx, scalar(prec, beta), _ptr(y), incy, _ptr(rows), len(rows),
+               _ptr(out))
+        if rc != 0:
+            raise ValueError(f"oracle gemv rows call failed with status {rc}")
+        return out
+
+    def gemv_problem(self, p, y=None):
+        """Run on a ``workloads.GemvProblem``; returns the new y (a copy)."""
+        y = (p.y if y is None else y).copy()
+        rc = self.gemv(p.prec, p.trans, p.m, p.n, p.alpha, p.A, p.lda, p.x, p.incx,
+                       p.beta, y, p.incy)
+        if rc != 0:
+            raise ValueError(f"oracle gemv call failed with status {rc}")
+        return y
+
+    def gemv_rows_problem(self, p, rows=None):
+        rows = np.arange(p.leny) if rows is None else rows
+        return self.gemv_rows(p.prec, p.trans, p.m, p.n, p.alpha, p.A, p.lda, p.x,
+                              p.incx, p.beta, p.y, p.incy, rows)
+
     def dd_add(self, a, b):
         r = self._lib.oracle_dd_add(_DD(*a), _DD(*b))
         return (r.hi, r.lo)
@@ -194,3 +242,19 @@ def dd_add(a, b):
 
 def dd_mul(a, b):
     return default().dd_mul(a, b)
+
+
+def gemv(*a, **k):
+    return default().gemv(*a, **k)
+
+
+def gemv_rows(*a, **k):
+    return default().gemv_rows(*a, **k)
+
+
+def gemv_problem(p, y=None):
+    return default().gemv_problem(p, y)
+
+
+def gemv_rows_problem(p, rows=None):
+    return default().gemv_rows_problem(p, rows)

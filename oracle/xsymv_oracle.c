@@ -30,6 +30,14 @@
  * beta == 0 the old y is not read (it may hold NaN), and alpha == 0 leaves
  * y := beta*y without touching A or x.
  *
+ * General matrix-vector product (the report's point of comparison: SYMV
+ * reads one triangle, GEMV the whole matrix, §1 and §2.1), BLAS xGEMV:
+ *   y := alpha*op(A)*x + beta*y, op(A) = A ('N'), A^T ('T') or A^H ('C'),
+ * A m x n column-major.  Written out from the definition, one output element
+ * at a time: y(i) := beta*y(i) + alpha * sum over the inner index k,
+ * ascending, of op(A)(i,k)*x(k), in the working precision.  Same BLAS rules
+ * for beta == 0 (y not read), alpha == 0 and the quick return.
+ *
  * Double-double arithmetic (report §2.2, which takes Bailey's double-double
  * format [14]: a value is the unevaluated sum hi + lo of two doubles):
  *   TwoSum (Knuth) and FastTwoSum (Dekker) give a sum and its exact error;
@@ -315,3 +323,100 @@ DEFINE_ORACLE(oracle_dsymv, oracle_dsymv_rows, double, d)
 DEFINE_ORACLE(oracle_chemv, oracle_chemv_rows, ocplx_f, c)
 DEFINE_ORACLE(oracle_zhemv, oracle_zhemv_rows, ocplx_d, z)
 DEFINE_ORACLE(oracle_wsymv, oracle_wsymv_rows, odd, w)
+
+/* ------------------------------------------------------------- xGEMV */
+
+/* BLAS xGEMV argument checks (xerbla positions: trans, m, n, alpha, a, lda,
+ * x, incx, beta, y, incy). */
+static int gemv_check(char trans, int m, int n, const void *A, int lda,
+                      const void *x, int incx, const void *y, int incy,
+                      int *tr)
+{
+    if (trans == 'N' || trans == 'n')
+        *tr = 0;
+    else if (trans == 'T' || trans == 't')
+        *tr = 1;
+    else if (trans == 'C' || trans == 'c')
+        *tr = 2;
+    else
+        return -1;
+    if (m < 0) return -2;
+    if (n < 0) return -3;
+    if (m > 0 && n > 0 && A == NULL) return -5;
+    if (lda < (m > 1 ? m : 1)) return -6;
+    if (m > 0 && n > 0 && x == NULL) return -7;
+    if (incx == 0) return -8;
+    if (m > 0 && n > 0 && y == NULL) return -10;
+    if (incy == 0) return -11;
+    return 0;
+}
+
+/* One output element of op(A)*x: output index `o`, inner length `kl`. */
+#define DEFINE_GEMV(NAME, ROWS_NAME, T, P)                                      \
+static T P##_gemv_dot(int tr, int o, int kl, int lenx, const T *A, int lda,     \
+                      const T *x, int incx)                                     \
+{                                                                               \
+    T sum = P##_zero();                                                         \
+    int k;                                                                      \
+    for (k = 0; k < kl; ++k) {                                                  \
+        T a = tr == 0 ? A[(long long)o + (long long)k * lda]                    \
+                      : A[(long long)k + (long long)o * lda];                   \
+        if (tr == 2) a = P##_conj(a);                                           \
+        sum = P##_add(sum, P##_mul(a, x[vpos(lenx, incx, k)]));                 \
+    }                                                                           \
+    return sum;                                                                 \
+}                                                                               \
+                                                                                \
+int NAME(char trans, int m, int n, T alpha, const T *A, int lda, const T *x,    \
+         int incx, T beta, T *y, int incy)                                      \
+{                                                                               \
+    int tr, i, leny, lenx;                                                      \
+    int rc = gemv_check(trans, m, n, A, lda, x, incx, y, incy, &tr);            \
+    if (rc) return rc;                                                          \
+    if (m == 0 || n == 0 || (P##_is_zero(alpha) && P##_is_one(beta))) return 0; \
+    leny = tr == 0 ? m : n;                                                     \
+    lenx = tr == 0 ? n : m;                                                     \
+    for (i = 0; i < leny; ++i) {                                                \
+        T *yi = &y[vpos(leny, incy, i)];                                        \
+        T res = P##_is_zero(beta) ? P##_zero() : P##_mul(beta, *yi);            \
+        if (!P##_is_zero(alpha))                                                \
+            res = P##_add(res, P##_mul(alpha, P##_gemv_dot(tr, i, lenx, lenx,   \
+                                                           A, lda, x, incx)));  \
+        *yi = res;                                                              \
+    }                                                                           \
+    return 0;                                                                   \
+}                                                                               \
+                                                                                \
+int ROWS_NAME(char trans, int m, int n, T alpha, const T *A, int lda,           \
+              const T *x, int incx, T beta, const T *y, int incy,               \
+              const long long *rows, int nrows, T *out)                         \
+{                                                                               \
+    int tr, r, leny, lenx;                                                      \
+    int rc = gemv_check(trans, m, n, A, lda, x, incx, y, incy, &tr);            \
+    if (rc) return rc;                                                          \
+    leny = tr == 0 ? m : n;                                                     \
+    lenx = tr == 0 ? n : m;                                                     \
+    for (r = 0; r < nrows; ++r)                                                 \
+        if (rows[r] < 0 || rows[r] >= leny) return -12;                         \
+    for (r = 0; r < nrows; ++r) {                                               \
+        int i = (int)rows[r];                                                   \
+        T yi = y[vpos(leny, incy, i)];                                          \
+        T res;                                                                  \
+        if (m == 0 || n == 0 || (P##_is_zero(alpha) && P##_is_one(beta))) {     \
+            out[r] = yi;                                                        \
+            continue;                                                           \
+        }                                                                       \
+        res = P##_is_zero(beta) ? P##_zero() : P##_mul(beta, yi);               \
+        if (!P##_is_zero(alpha))                                                \
+            res = P##_add(res, P##_mul(alpha, P##_gemv_dot(tr, i, lenx, lenx,   \
+                                                           A, lda, x, incx)));  \
+        out[r] = res;                                                           \
+    }                                                                           \
+    return 0;                                                                   \
+}
+
+DEFINE_GEMV(oracle_sgemv, oracle_sgemv_rows, float, s)
+DEFINE_GEMV(oracle_dgemv, oracle_dgemv_rows, double, d)
+DEFINE_GEMV(oracle_cgemv, oracle_cgemv_rows, ocplx_f, c)
+DEFINE_GEMV(oracle_zgemv, oracle_zgemv_rows, ocplx_d, z)
+DEFINE_GEMV(oracle_wgemv, oracle_wgemv_rows, odd, w)

@@ -69,6 +69,42 @@ int oracle_wsymv_rows(char uplo, int n, odd alpha, const odd *A, int lda,
                       const odd *x, int incx, odd beta, const odd *y,
                       int incy, const long long *rows, int nrows, odd *out);
 
+/* General matrix-vector product, BLAS xGEMV: y := alpha*op(A)*x + beta*y
+ * with op(A) = A ('N'), A^T ('T') or A^H ('C'; 'T' for the real and
+ * double-double types), A m x n.  x has n elements for 'N' and m otherwise,
+ * y the other length.  Every output element from the definition (inner index
+ * ascending).  Return codes (BLAS xerbla positions): -1 trans, -2 m < 0,
+ * -3 n < 0, -5 A NULL, -6 lda < max(1,m), -7 x NULL, -8 incx == 0,
+ * -10 y NULL, -11 incy == 0.  The _rows variants write outputs rows[] to out
+ * (y is read, not written; -12 for an index outside y). */
+int oracle_sgemv(char trans, int m, int n, float alpha, const float *A, int lda,
+                 const float *x, int incx, float beta, float *y, int incy);
+int oracle_dgemv(char trans, int m, int n, double alpha, const double *A, int lda,
+                 const double *x, int incx, double beta, double *y, int incy);
+int oracle_cgemv(char trans, int m, int n, ocplx_f alpha, const ocplx_f *A, int lda,
+                 const ocplx_f *x, int incx, ocplx_f beta, ocplx_f *y, int incy);
+int oracle_zgemv(char trans, int m, int n, ocplx_d alpha, const ocplx_d *A, int lda,
+                 const ocplx_d *x, int incx, ocplx_d beta, ocplx_d *y, int incy);
+int oracle_wgemv(char trans, int m, int n, odd alpha, const odd *A, int lda,
+                 const odd *x, int incx, odd beta, odd *y, int incy);
+int oracle_sgemv_rows(char trans, int m, int n, float alpha, const float *A, int lda,
+                      const float *x, int incx, float beta, const float *y, int incy,
+                      const long long *rows, int nrows, float *out);
+int oracle_dgemv_rows(char trans, int m, int n, double alpha, const double *A, int lda,
+                      const double *x, int incx, double beta, const double *y, int incy,
+                      const long long *rows, int nrows, double *out);
+int oracle_cgemv_rows(char trans, int m, int n, ocplx_f alpha, const ocplx_f *A,
+                      int lda, const ocplx_f *x, int incx, ocplx_f beta,
+                      const ocplx_f *y, int incy, const long long *rows, int nrows,
+                      ocplx_f *out);
+int oracle_zgemv_rows(char trans, int m, int n, ocplx_d alpha, const ocplx_d *A,
+                      int lda, const ocplx_d *x, int incx, ocplx_d beta,
+                      const ocplx_d *y, int incy, const long long *rows, int nrows,
+                      ocplx_d *out);
+int oracle_wgemv_rows(char trans, int m, int n, odd alpha, const odd *A, int lda,
+                      const odd *x, int incx, odd beta, const odd *y, int incy,
+                      const long long *rows, int nrows, odd *out);
+
 /* The double-double primitives, exported so that the tests can pin them
  * one by one against exact rational arithmetic. */
 odd oracle_dd_add(odd a, odd b);

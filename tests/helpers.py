@@ -285,3 +285,152 @@ def np_mul(a, b):
         out.imag = im
         return out
     return np.multiply(a, b)
+
+
+# ------------------------------------------------------------------ xGEMV
+
+def gemv_vec_index(length: int, inc: int) -> np.ndarray:
+    return vec_index(length, inc)
+
+
+def gemv_op_dense(p) -> np.ndarray:
+    """op(A) as a dense (leny x lenx) float64/complex128 array (double-double:
+    hi + lo rounded to float64)."""
+    A = p.A[:, 0].astype(np.float64) + p.A[:, 1] if p.prec == "w" else p.A
+    M = A[: p.lda * p.n].reshape(p.n, p.lda).T[: p.m, :]  # [i, j], m x n
+    dt = np.complex128 if p.prec in ("c", "z") else np.float64
+    M = M.astype(dt)
+    if p.trans in ("N", "n"):
+        return M
+    return np.conj(M.T) if p.trans in ("C", "c") else M.T.copy()
+
+
+def _gemv_exact_vec(p, v, length, inc):
+    idx = vec_index(length, inc)
+    if p.prec == "w":
+        return [Fraction(float(v[k, 0])) + Fraction(float(v[k, 1])) for k in idx]
+    if p.prec in ("c", "z"):
+        return [(_frac(v[k].real), _frac(v[k].imag)) for k in idx]
+    return [_frac(v[k]) for k in idx]
+
+
+def gemv_exact(p):
+    """Exact alpha*op(A)*x + beta*y in logical order (y ignored if beta == 0)."""
+    cplx = p.prec in ("c", "z")
+    tr = p.trans not in ("N", "n")
+    conj = p.trans in ("C", "c")
+
+    def get(i, j):
+        k = i + j * p.lda
+        if p.prec == "w":
+            return Fraction(float(p.A[k, 0])) + Fraction(float(p.A[k, 1]))
+        if cplx:
+            return (_frac(p.A[k].real), _frac(p.A[k].imag))
+        return _frac(p.A[k])
+
+    x = _gemv_exact_vec(p, p.x, p.lenx, p.incx)
+    al = exact_scalar(p.prec, p.alpha)
+    be = exact_scalar(p.prec, p.beta)
+    beta_zero = be == (0, 0) if cplx else be == 0
+    y = None if beta_zero else _gemv_exact_vec(p, p.y, p.leny, p.incy)
+    zero = (Fraction(0), Fraction(0)) if cplx else Fraction(0)
+    out = []
+    for o in range(p.leny):
+        s = zero
+        for k in range(p.lenx):
+            a = get(k, o) if tr else get(o, k)
+            if cplx:
+                if conj:
+                    a = (a[0], -a[1])
+                s = _cadd(s, _cmul(a, x[k]))
+            else:
+                s = s + a * x[k]
+        if cplx:
+            r = _cmul(al, s)
+            if not beta_zero:
+                r = _cadd(r, _cmul(be, y[o]))
+        else:
+            r = al * s
+            if not beta_zero:
+                r = r + be * y[o]
+        out.append(r)
+    return out
+
+
+def gemv_exact_errors(p, y_out, exact=None):
+    ex = gemv_exact(p) if exact is None else exact
+    idx = vec_index(p.leny, p.incy)
+    errs = np.empty(p.leny)
+    for k, i in enumerate(idx):
+        e = ex[k]
+        if p.prec == "w":
+            v = Fraction(float(y_out[i, 0])) + Fraction(float(y_out[i, 1]))
+            errs[k] = abs(float(v - e))
+        elif p.prec in ("c", "z"):
+            errs[k] = abs(complex(float(_frac(y_out[i].real) - e[0]),
+                                  float(_frac(y_out[i].imag) - e[1])))
+        else:
+            errs[k] = abs(float(_frac(y_out[i]) - e))
+    return errs
+
+
+def gemv_tolerance(p, rows=None):
+    """4*k*eps*(|alpha|*(|op(A)||x|)_i + |beta|*|y_i|), k = the inner length,
+    for all outputs (logical order) or for the outputs ``rows`` only (unit
+    increments, read column by column without forming op(A))."""
+    k = max(p.lenx, 1)
+    if p.prec == "w":
+        al = abs(p.alpha[0] + p.alpha[1])
+        be = abs(p.beta[0] + p.beta[1])
+    else:
+        al = abs(complex(p.alpha))
+        be = abs(complex(p.beta))
+    if rows is None:
+        x = _magnitude(p, p.x[vec_index(p.lenx, p.incx)])
+        y = _magnitude(p, p.y[vec_index(p.leny, p.incy)])
+        t = al * (np.abs(gemv_op_dense(p)) @ x)
+    else:
+        assert p.incx == 1 and p.incy == 1
+        rows = np.asarray(rows, dtype=np.int64)
+        x = _magnitude(p, p.x)
+        y = _magnitude(p, p.y)[rows]
+        t = np.empty(len(rows))
+        kk = np.arange(p.lenx, dtype=np.int64)
+        for r, o in enumerate(rows):
+            idx = (kk + o * p.lda) if p.trans not in ("N", "n") else (o + kk * p.lda)
+            t[r] = al * float(_magnitude(p, p.A[idx]) @ x)
+    if be != 0:
+        t = t + be * np.where(np.isfinite(y), y, 0.0)
+    return 4.0 * k * EPS[p.prec] * t
+
+
+def gemv_integer_expected(p):
+    """Exact result of an integer-valued GemvProblem via int64 products, in
+    the element type."""
+    M = gemv_op_dense(p)
+    xi = vec_index(p.lenx, p.incx)
+    yi = vec_index(p.leny, p.incy)
+    if p.prec in ("c", "z"):
+        Mr = np.rint(M.real).astype(np.int64)
+        Mi = np.rint(M.imag).astype(np.int64)
+        xr = np.rint(p.x[xi].real).astype(np.int64)
+        xim = np.rint(p.x[xi].imag).astype(np.int64)
+        s = (Mr @ xr - Mi @ xim).astype(np.complex128) + 1j * (Mr @ xim + Mi @ xr)
+        al, be = complex(p.alpha), complex(p.beta)
+        out = al * s + (be * p.y[yi].astype(np.complex128) if be != 0 else 0)
+        return out.astype(p.y.dtype)
+    Mi = np.rint(M).astype(np.int64)
+    if p.prec == "w":
+        x = np.rint(p.x[xi, 0]).astype(np.int64)
+        y = p.y[yi, 0]
+        al, be = p.alpha[0], p.beta[0]
+    else:
+        x = np.rint(p.x[xi]).astype(np.int64)
+        y = p.y[yi].astype(np.float64)
+        al, be = float(p.alpha), float(p.beta)
+    out = al * (Mi @ x).astype(np.float64) + (be * y if be != 0 else 0.0)
+    if p.prec == "w":
+        r = np.zeros((p.leny, 2))
+        r[:, 0] = out
+        return r
+    return out.astype(p.y.dtype)

@@ -26,6 +26,10 @@ def quad_lib():
             f = getattr(lib, nm)
             f.restype = ci
             f.argtypes = [ctypes.c_char, ci, vp, vp, ci, vp, vp, vp, vp, ci, vp, vp]
+        for nm in ("quad_wgemv_rows", "quad_dgemv_rows"):
+            f = getattr(lib, nm)
+            f.restype = ci
+            f.argtypes = [ctypes.c_char, ci, ci, vp, vp, ci, vp, vp, vp, vp, ci, vp, vp]
         _lib = lib
     return _lib
 
@@ -49,6 +53,31 @@ def quad_rows(p, rows):
     x = np.ascontiguousarray(p.x)
     y = np.ascontiguousarray(p.y)
     rc = f(p.uplo.encode(), p.n, al.ctypes.data, A.ctypes.data, p.lda,
+           x.ctypes.data, be.ctypes.data, y.ctypes.data, rows.ctypes.data,
+           len(rows), hi.ctypes.data, lo.ctypes.data)
+    assert rc == 0
+    return np.stack([hi, lo], axis=1)
+
+
+def quad_gemv_rows(p, rows):
+    """binary128 output elements ``rows`` of alpha*op(A)*x + beta*y for a 'w'
+    or 'd' GemvProblem with unit increments; (nrows, 2) float64 (hi, lo)."""
+    assert p.incx == 1 and p.incy == 1
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    hi = np.empty(len(rows))
+    lo = np.empty(len(rows))
+    if p.prec == "w":
+        al = np.array(p.alpha, dtype=np.float64)
+        be = np.array(p.beta, dtype=np.float64)
+        f = quad_lib().quad_wgemv_rows
+    else:
+        al = np.array([p.alpha], dtype=np.float64)
+        be = np.array([p.beta], dtype=np.float64)
+        f = quad_lib().quad_dgemv_rows
+    A = np.ascontiguousarray(p.A)
+    x = np.ascontiguousarray(p.x)
+    y = np.ascontiguousarray(p.y)
+    rc = f(p.trans.encode(), p.m, p.n, al.ctypes.data, A.ctypes.data, p.lda,
            x.ctypes.data, be.ctypes.data, y.ctypes.data, rows.ctypes.data,
            len(rows), hi.ctypes.data, lo.ctypes.data)
     assert rc == 0

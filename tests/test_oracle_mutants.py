@@ -8,6 +8,7 @@ import subprocess
 import pytest
 
 import oracle
+from tests import test_oracle_gemv as G
 from tests import test_oracle_pins as P
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "xsymv_oracle.c")
@@ -59,6 +60,22 @@ MUTANTS = [
      "s = A[(long long)j + i * lda];", None),
     ("rows: alpha dropped",
      "res = P##_add(res, P##_mul(alpha, sum));", "res = P##_add(res, sum);", None),
+    ("gemv: 'N' reads the transposed element",
+     "T a = tr == 0 ? A[(long long)o + (long long)k * lda]",
+     "T a = tr == 0 ? A[(long long)k + (long long)o * lda]", None),
+    ("gemv: 'C' without conjugate",
+     "if (tr == 2) a = P##_conj(a);", "(void)0;", None),
+    ("gemv: beta = 0 multiplies y",
+     "T res = P##_is_zero(beta) ? P##_zero() : P##_mul(beta, *yi);",
+     "T res = P##_mul(beta, *yi);", None),
+    ("gemv: alpha dropped",
+     "res = P##_add(res, P##_mul(alpha, P##_gemv_dot(",
+     "res = P##_add(res, (P##_gemv_dot(", 1),
+    ("gemv: inner loop one short",
+     "for (k = 0; k < kl; ++k) {", "for (k = 0; k < kl - 1; ++k) {", None),
+    ("gemv: x walked with y's increment",
+     "sum = P##_add(sum, P##_mul(a, x[vpos(lenx, incx, k)]));",
+     "sum = P##_add(sum, P##_mul(a, x[vpos(lenx, 1, k)]));", None),
 ]
 
 # pin battery: (test function, parameter sets)
@@ -73,6 +90,13 @@ BATTERY = [
     (P.test_increments, [dict(prec=pr, incx=-3, incy=-2) for pr in P.PRECS]),
     (P.test_dd_add_mul_exact_cases, [dict()]),
     (P.test_dd_add_mul_relative_error, [dict()]),
+    (G.test_gemv_exact_bruteforce, [dict(prec=pr, trans=t, m=13, n=11, pad=3)
+                                    for pr in G.PRECS for t in G.TRANS]),
+    (G.test_gemv_integer_bitwise, [dict(prec=pr, trans=t, m=64, n=48, pad=5)
+                                   for pr in G.PRECS for t in G.TRANS]),
+    (G.test_gemv_beta_zero_ignores_nan_y, [dict(prec=pr, trans=t)
+                                           for pr in G.PRECS for t in "NT"]),
+    (G.test_gemv_increments, [dict(prec=pr, trans="N", incx=2, incy=-3) for pr in G.PRECS]),
 ]
 
 
