@@ -22,7 +22,10 @@ __all__ = ["xsymv_s", "xsymv_d", "xhemv_c", "xhemv_z", "xsymv_w", "XsymvError",
            "library", "LIB_PATH", "PREC_CODE", "workspace_bytes", "num_configs",
            "config_info", "select_config", "current_config", "timing_enable",
            "timing_read", "release", "version", "autotune", "save_config", "load_config",
-           "clear_config", "strip_plan", "config_workgroups", "set_workspace", "read_bandwidth"]
+           "clear_config", "strip_plan", "config_workgroups", "set_workspace", "read_bandwidth",
+           "xgemv_s", "xgemv_d", "xgemv_c", "xgemv_z", "xgemv_w", "gemv_num_configs",
+           "gemv_config_info", "gemv_select_config", "gemv_current_config",
+           "gemv_workspace_bytes", "gemv_plan"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libxsymv.so")
 PREC_CODE = {"s": 0, "d": 1, "c": 2, "z": 3, "w": 4}
@@ -54,6 +57,7 @@ class _DD(ctypes.Structure):
 
 _SCALAR = {"s": ctypes.c_float, "d": ctypes.c_double, "c": _C64, "z": _C128, "w": _DD}
 _ENTRY = {"s": "xsymv_s", "d": "xsymv_d", "c": "xhemv_c", "z": "xhemv_z", "w": "xsymv_w"}
+_GENTRY = {"s": "xgemv_s", "d": "xgemv_d", "c": "xgemv_c", "z": "xgemv_z", "w": "xgemv_w"}
 
 _lib = None
 _lock = threading.Lock()
@@ -75,6 +79,11 @@ def library():
                 st = _SCALAR[p]
                 f.restype = ci
                 f.argtypes = [cc, ci, st, vp, ci, vp, ci, st, vp, ci, vp]
+            for p, nm in _GENTRY.items():
+                f = getattr(lib, nm)
+                st = _SCALAR[p]
+                f.restype = ci
+                f.argtypes = [cc, ci, ci, st, vp, ci, vp, ci, st, vp, ci, vp]
             lib.xsymv_workspace_bytes.restype = ctypes.c_size_t
             lib.xsymv_workspace_bytes.argtypes = [ci, cc, ci]
             lib.xsymv_release.restype = ci
@@ -106,6 +115,18 @@ def library():
             lib.xsymv_config_workgroups.argtypes = [ci, ci, cc]
             lib.xsymv_strip_plan.restype = ci
             lib.xsymv_strip_plan.argtypes = [cc, ci, ci, ci, ci, ip, ci, ip, ip, ci]
+            lib.xgemv_num_configs.restype = ci
+            lib.xgemv_num_configs.argtypes = [ci]
+            lib.xgemv_config_info.restype = ci
+            lib.xgemv_config_info.argtypes = [ci, ci, ip, ip, ip, ip, ip]
+            lib.xgemv_select_config.restype = ci
+            lib.xgemv_select_config.argtypes = [ci, ci]
+            lib.xgemv_current_config.restype = ci
+            lib.xgemv_current_config.argtypes = [ci]
+            lib.xgemv_workspace_bytes.restype = ctypes.c_size_t
+            lib.xgemv_workspace_bytes.argtypes = [ci, cc, ci, ci]
+            lib.xgemv_plan.restype = ci
+            lib.xgemv_plan.argtypes = [ci, ci, ci, ci, ip, ci, ip, ci]
             lib.xsymv_read_bandwidth.restype = ci
             lib.xsymv_read_bandwidth.argtypes = [ctypes.c_size_t, ci, vp, fp, fp]
             lib.xsymv_version.restype = ctypes.c_char_p
@@ -174,6 +195,80 @@ def xhemv_z(uplo, n, alpha, A, lda, x, incx, beta, y, incy, stream=None):
 def xsymv_w(uplo, n, alpha, A, lda, x, incx, beta, y, incy, stream=None):
     """WSYMV: double-double (hi, lo pairs); alpha, beta are (hi, lo) tuples."""
     _call("w", uplo, n, alpha, A, lda, x, incx, beta, y, incy, stream)
+
+
+def _gcall(prec, trans, m, n, alpha, A, lda, x, incx, beta, y, incy, stream):
+    f = getattr(library(), _GENTRY[prec])
+    t = trans.encode()[:1] if isinstance(trans, str) else trans
+    rc = f(t, m, n, _scalar(prec, alpha), _addr(A), lda, _addr(x), incx,
+           _scalar(prec, beta), _addr(y), incy, _stream(stream))
+    if rc != 0:
+        raise XsymvError(_GENTRY[prec], rc)
+
+
+def xgemv_s(trans, m, n, alpha, A, lda, x, incx, beta, y, incy, stream=None):
+    """SGEMV: y := alpha*op(A)*x + beta*y, float32, A m x n."""
+    _gcall("s", trans, m, n, alpha, A, lda, x, incx, beta, y, incy, stream)
+
+
+def xgemv_d(trans, m, n, alpha, A, lda, x, incx, beta, y, incy, stream=None):
+    """DGEMV: float64."""
+    _gcall("d", trans, m, n, alpha, A, lda, x, incx, beta, y, incy, stream)
+
+
+def xgemv_c(trans, m, n, alpha, A, lda, x, incx, beta, y, incy, stream=None):
+    """CGEMV: complex64 ('C' conjugates)."""
+    _gcall("c", trans, m, n, alpha, A, lda, x, incx, beta, y, incy, stream)
+
+
+def xgemv_z(trans, m, n, alpha, A, lda, x, incx, beta, y, incy, stream=None):
+    """ZGEMV: complex128."""
+    _gcall("z", trans, m, n, alpha, A, lda, x, incx, beta, y, incy, stream)
+
+
+def xgemv_w(trans, m, n, alpha, A, lda, x, incx, beta, y, incy, stream=None):
+    """WGEMV: double-double (hi, lo) pairs; alpha, beta are (hi, lo) tuples."""
+    _gcall("w", trans, m, n, alpha, A, lda, x, incx, beta, y, incy, stream)
+
+
+def gemv_num_configs(prec: str) -> int:
+    return library().xgemv_num_configs(PREC_CODE[prec])
+
+
+def gemv_config_info(prec: str, idx: int) -> dict:
+    vals = [ctypes.c_int() for _ in range(5)]
+    if library().xgemv_config_info(PREC_CODE[prec], idx, *[ctypes.byref(v) for v in vals]) != 0:
+        raise IndexError(idx)
+    w, sw, g, nt, r = (v.value for v in vals)
+    return {"waves": w, "stripes_per_wave": sw, "cols_per_group": g, "nontemporal": nt,
+            "rows_per_strip": r}
+
+
+def gemv_select_config(prec: str, idx: int) -> None:
+    if library().xgemv_select_config(PREC_CODE[prec], idx) != 0:
+        raise ValueError("bad gemv configuration selection")
+
+
+def gemv_current_config(prec: str) -> int:
+    return library().xgemv_current_config(PREC_CODE[prec])
+
+
+def gemv_workspace_bytes(prec: str, trans: str, m: int, n: int) -> int:
+    return library().xgemv_workspace_bytes(PREC_CODE[prec], trans.encode()[:1], m, n)
+
+
+def gemv_plan(m: int, n: int, R: int, G: int):
+    """The xGEMV work split (host computation): (blocks [G x 4], seg_base [NS+1])."""
+    import numpy as np
+    ns = (m + R - 1) // R
+    blocks = np.zeros((G, 4), dtype=np.int32)
+    segb = np.zeros(ns + 1, dtype=np.int32)
+    ip = ctypes.POINTER(ctypes.c_int)
+    k = library().xgemv_plan(m, n, R, G, blocks.ctypes.data_as(ip), G,
+                             segb.ctypes.data_as(ip), ns + 1)
+    if k < 0:
+        raise ValueError(f"xgemv_plan failed ({k})")
+    return blocks[:k], segb
 
 
 def workspace_bytes(prec: str, uplo: str, n: int) -> int:

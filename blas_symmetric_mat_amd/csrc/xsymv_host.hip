@@ -4,6 +4,7 @@
 #include "xsymv_host.hpp"
 
 #include <algorithm>
+#include <atomic>
 #include <cctype>
 #include <cstdio>
 #include <cstdlib>
@@ -34,6 +35,7 @@ struct DeviceState {
     std::mutex mu;
     std::map<PlanKey, std::unique_ptr<Plan>> plans;
     std::map<StripKey, std::unique_ptr<StripPlan>> strip_plans;
+    std::map<std::tuple<int, int, int, int>, std::unique_ptr<StripPlan>> gemv_plans;  // m, n, R, G
     std::map<hipStream_t, Workspace> workspaces;
     std::map<std::pair<const void*, int>, int> resident;  // (kernel, threads) -> blocks
 };
@@ -207,6 +209,125 @@ int resident_blocks(const void* kernel, int threads, int* out)
     ds->resident[key] = *out;
     return 0;
 }
+
+void build_gemv_plan_host(int m, int n, int R, int G, std::vector<StripBlock>& blocks,
+                          std::vector<int>& seg_base, int& NS)
+{
+    NS = (m + R - 1) / R;
+    const long long total = (long long)NS * n;
+    const long long OVH = 16;
+    // cost of one column of strip i: its rows + OVH; prefix over strips
+    auto cost_before = [&](long long pos) {  // cost of positions [0, pos)
+        const long long full = pos / n, rem = pos % n;
+        long long c = 0;
+        const long long rows_full = (long long)R + OVH;
+        const long long last_rows = (long long)(m - (NS - 1) * R) + OVH;
+        if (full >= NS) return (NS - 1) * n * rows_full + n * last_rows;
+        c = full * n * rows_full;
+        c += rem * (full == NS - 1 ? last_rows : rows_full);
+        return c;
+    };
+    const long long C = cost_before(total);
+    G = std::max(1, (int)std::min<long long>(G, total));
+    blocks.assign(G, StripBlock{0, 0, 0, 0});
+    std::vector<long long> bound(G + 1, 0);
+    bound[G] = total;
+    for (int b = 1; b < G; ++b) {
+        const long long target = (C * (long long)b) / G;
+        long long lo = bound[b - 1], hi = total;  // first pos with cost_before >= target
+        while (lo < hi) {
+            const long long mid = (lo + hi) / 2;
+            if (cost_before(mid) < target)
+                lo = mid + 1;
+            else
+                hi = mid;
+        }
+        bound[b] = lo;
+    }
+    seg_base.assign(NS + 1, 0);
+    std::vector<int> first_slot(NS, -1);
+    int slot = 0;
+    for (int b = 0; b < G; ++b) {
+        const int u0 = (int)bound[b], u1 = (int)bound[b + 1];
+        const int strip = std::min(NS - 1, u0 / std::max(n, 1));
+        blocks[b] = StripBlock{u0, u1, slot, strip};
+        int u = u0, st = strip;
+        while (u < u1) {
+            if (first_slot[st] < 0) first_slot[st] = slot;
+            u = std::min(u1, (st + 1) * n);
+            ++slot;
+            ++st;
+        }
+    }
+    // a strip none of whose positions is in a non-empty range cannot occur
+    // (every position belongs to one range); keep seg_base monotone anyway
+    for (int i = 0; i < NS; ++i) seg_base[i] = first_slot[i] < 0 ? slot : first_slot[i];
+    seg_base[NS] = slot;
+}
+
+int get_gemv_plan(DeviceState* ds, int m, int n, int R, int G, hipStream_t stream,
+                  const StripPlan** out)
+{
+    auto key = std::make_tuple(m, n, R, G);
+    auto it = ds->gemv_plans.find(key);
+    if (it != ds->gemv_plans.end()) {
+        *out = it->second.get();
+        return 0;
+    }
+    std::vector<StripBlock> blocks;
+    std::vector<int> segb;
+    int NS = 0;
+    build_gemv_plan_host(m, n, R, G, blocks, segb, NS);
+    std::unique_ptr<StripPlan> plan(new StripPlan());
+    plan->NS = NS;
+    plan->G = (int)blocks.size();
+    plan->nseg = segb[NS];
+    plan->R = R;
+    const size_t bb = blocks.size() * sizeof(StripBlock);
+    const size_t ib = segb.size() * sizeof(int);
+    char* h = nullptr;
+    XSYMV_HIP(hipHostMalloc((void**)&h, bb + ib, hipHostMallocDefault));
+    plan->h_pinned = h;
+    std::copy(blocks.begin(), blocks.end(), reinterpret_cast<StripBlock*>(h));
+    std::copy(segb.begin(), segb.end(), reinterpret_cast<int*>(h + bb));
+    char* d = nullptr;
+    XSYMV_HIP(hipMalloc((void**)&d, bb + ib));
+    XSYMV_HIP(hipMemcpyAsync(d, h, bb + ib, hipMemcpyHostToDevice, stream));
+    XSYMV_HIP(hipStreamSynchronize(stream));
+    plan->d_blocks = reinterpret_cast<StripBlock*>(d);
+    plan->d_seg_base = reinterpret_cast<int*>(d + bb);
+    *out = plan.get();
+    ds->gemv_plans[key] = std::move(plan);
+    return 0;
+}
+
+int check_gemv_args(char trans, int m, int n, const void* A, int lda, const void* x, int incx,
+                    const void* y, int incy, int* tr)
+{
+    if (trans == 'N' || trans == 'n')
+        *tr = 0;
+    else if (trans == 'T' || trans == 't')
+        *tr = 1;
+    else if (trans == 'C' || trans == 'c')
+        *tr = 2;
+    else
+        return -1;
+    if (m < 0) return -2;
+    if (n < 0) return -3;
+    if (m > 0 && n > 0 && A == nullptr) return -5;
+    if (lda < std::max(1, m)) return -6;
+    if (m > 0 && n > 0 && x == nullptr) return -7;
+    if (incx == 0) return -8;
+    if (m > 0 && n > 0 && y == nullptr) return -10;
+    if (incy == 0) return -11;
+    return 0;
+}
+
+namespace {
+std::atomic<int> g_gemv_idx[5];
+}
+
+int gemv_selected(int prec) { return g_gemv_idx[prec].load(); }
 
 int get_strip_plan(DeviceState* ds, int dev, bool upper, int n, int R, int G, int split,
                    hipStream_t stream, const StripPlan** out)
@@ -616,6 +737,11 @@ int xsymv_release(void)
         XSYMV_HIP(hipHostFree(kv.second->h_pinned));
     }
     ds->strip_plans.clear();
+    for (auto& kv : ds->gemv_plans) {
+        XSYMV_HIP(hipFree(kv.second->d_blocks));
+        XSYMV_HIP(hipHostFree(kv.second->h_pinned));
+    }
+    ds->gemv_plans.clear();
     return 0;
 }
 
@@ -835,6 +961,89 @@ int xsymv_strip_plan(char uplo, int n, int R, int G, int split, int* blocks4, in
         blocks4[4 * b + 3] = blocks[b].strip0;
     }
     std::copy(sb.begin(), sb.end(), strip_base);
+    std::copy(segb.begin(), segb.end(), seg_base);
+    return (int)blocks.size();
+}
+
+int xgemv_num_configs(int prec)
+{
+    switch (prec) {
+    case XSYMV_S: return (int)gemv_kernel_sets<float>().size();
+    case XSYMV_D: return (int)gemv_kernel_sets<double>().size();
+    case XSYMV_C: return (int)gemv_kernel_sets<cf32>().size();
+    case XSYMV_Z: return (int)gemv_kernel_sets<cf64>().size();
+    case XSYMV_W: return (int)gemv_kernel_sets<ddreal>().size();
+    default: return -1;
+    }
+}
+
+int xgemv_config_info(int prec, int idx, int* waves, int* stripes_per_wave, int* cols_per_group,
+                      int* nontemporal, int* rows_per_strip)
+{
+    if (idx < 0 || idx >= xgemv_num_configs(prec)) return -1;
+    int W = 0, SW = 0, G = 0, NT = 0, R = 0;
+    switch (prec) {
+#define XSYMV_K(T)                                                                       \
+    {                                                                                    \
+        const auto& k = gemv_kernel_sets<T>()[idx];                                      \
+        W = k.W; SW = k.SW; G = k.G; NT = k.NT; R = k.R();                               \
+        break;                                                                           \
+    }
+    case XSYMV_S: XSYMV_K(float)
+    case XSYMV_D: XSYMV_K(double)
+    case XSYMV_C: XSYMV_K(cf32)
+    case XSYMV_Z: XSYMV_K(cf64)
+    default: XSYMV_K(ddreal)
+#undef XSYMV_K
+    }
+    if (waves) *waves = W;
+    if (stripes_per_wave) *stripes_per_wave = SW;
+    if (cols_per_group) *cols_per_group = G;
+    if (nontemporal) *nontemporal = NT;
+    if (rows_per_strip) *rows_per_strip = R;
+    return 0;
+}
+
+int xgemv_select_config(int prec, int idx)
+{
+    if (prec < 0 || prec > 4 || idx < -1 || idx >= xgemv_num_configs(prec)) return -1;
+    g_gemv_idx[prec].store(idx < 0 ? 0 : idx);
+    return 0;
+}
+
+int xgemv_current_config(int prec)
+{
+    if (prec < 0 || prec > 4) return -1;
+    return gemv_selected(prec);
+}
+
+size_t xgemv_workspace_bytes(int prec, char trans, int m, int n)
+{
+    switch (prec) {
+    case XSYMV_S: return gemv_ws_bytes<float>(trans, m, n);
+    case XSYMV_D: return gemv_ws_bytes<double>(trans, m, n);
+    case XSYMV_C: return gemv_ws_bytes<cf32>(trans, m, n);
+    case XSYMV_Z: return gemv_ws_bytes<cf64>(trans, m, n);
+    case XSYMV_W: return gemv_ws_bytes<ddreal>(trans, m, n);
+    default: return (size_t)-1;
+    }
+}
+
+int xgemv_plan(int m, int n, int R, int G, int* blocks4, int max_blocks, int* seg_base,
+               int max_strips)
+{
+    if (m <= 0 || n <= 0 || R <= 0 || G <= 0) return -1;
+    std::vector<StripBlock> blocks;
+    std::vector<int> segb;
+    int NS = 0;
+    build_gemv_plan_host(m, n, R, G, blocks, segb, NS);
+    if ((int)blocks.size() > max_blocks || NS + 1 > max_strips) return -2;
+    for (size_t b = 0; b < blocks.size(); ++b) {
+        blocks4[4 * b + 0] = blocks[b].u0;
+        blocks4[4 * b + 1] = blocks[b].u1;
+        blocks4[4 * b + 2] = blocks[b].slot0;
+        blocks4[4 * b + 3] = blocks[b].strip0;
+    }
     std::copy(segb.begin(), segb.end(), seg_base);
     return (int)blocks.size();
 }

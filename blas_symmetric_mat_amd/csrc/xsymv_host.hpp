@@ -17,12 +17,14 @@
 #include <map>
 #include <memory>
 #include <mutex>
+#include <type_traits>
 #include <tuple>
 #include <vector>
 
 #include "../../include/xsymv.h"
 #include "xsymv_kernels.hpp"
 #include "xsymv_strip.hpp"
+#include "xgemv_strip.hpp"
 
 namespace xsymv {
 
@@ -152,8 +154,15 @@ struct StripPlan {
 void build_strip_plan_host(bool upper, int n, int R, int G, int split, std::vector<StripBlock>& blocks,
                            std::vector<int>& strip_base, std::vector<int>& seg_base, int& NS);
 
+// xGEMV: (strip, column) sequence of NS strips x n columns, equal pieces
+// (per-column cost: the strip's rows plus a fixed share).
+void build_gemv_plan_host(int m, int n, int R, int G, std::vector<StripBlock>& blocks,
+                          std::vector<int>& seg_base, int& NS);
+
 struct DeviceState;
 DeviceState* device_state(int dev);
+int get_gemv_plan(DeviceState* ds, int m, int n, int R, int G, hipStream_t stream,
+                  const StripPlan** out);
 int get_strip_plan(DeviceState* ds, int dev, bool upper, int n, int R, int G, int split, hipStream_t stream,
                    const StripPlan** out);
 // Workgroups of `kernel` (block size `threads`) the current device holds at once.
@@ -369,6 +378,127 @@ int symv_impl(char uplo, int n, T alpha, const T* A, int lda, const T* x, int in
               T* y, int incy, hipStream_t stream)
 {
     return symv_run<T>(uplo, n, alpha, A, lda, x, incx, beta, y, incy, stream, -1);
+}
+
+// ------------------------------------------------------------------ xGEMV
+template <class T>
+struct GemvKernelSet {
+    int W, SW, G, NT;
+    void (*k[3])(GemvArgs<T>);  // 'N', 'T', 'C'
+    int R() const { return W * SW * 64 * Elem<T>::VEC; }
+};
+
+template <class T, int W, int SW, int G, bool NT>
+GemvKernelSet<T> make_gemv()
+{
+    constexpr bool cplx = std::is_same<T, cf32>::value || std::is_same<T, cf64>::value;
+    GemvKernelSet<T> k{W, SW, G, NT ? 1 : 0, {}};
+    k.k[0] = &gemv_strip<T, 0, W, SW, G, NT, STRIP_CBUF>;
+    k.k[1] = &gemv_strip<T, 1, W, SW, G, NT, STRIP_CBUF>;
+    k.k[2] = cplx ? &gemv_strip<T, 2, W, SW, G, NT, STRIP_CBUF> : k.k[1];
+    return k;
+}
+
+template <class T> const std::vector<GemvKernelSet<T>>& gemv_kernel_sets();
+int gemv_selected(int prec);
+
+int check_gemv_args(char trans, int m, int n, const void* A, int lda, const void* x, int incx,
+                    const void* y, int incy, int* tr);
+
+// Workspace of a GEMV call: [partials][x gathered]
+template <class T>
+size_t gemv_workspace_bytes(int tr, int nseg, int R, int NS, int n, int lenx)
+{
+    const size_t part = tr == 0 ? (size_t)nseg * R : (size_t)NS * n;
+    return align_up(part * sizeof(T)) + align_up((size_t)lenx * sizeof(T));
+}
+
+template <class T>
+int gemv_run(char trans, int m, int n, T alpha, const T* A, int lda, const T* x, int incx,
+             T beta, T* y, int incy, hipStream_t stream, int forced_idx)
+{
+    int tr = 0;
+    int rc = check_gemv_args(trans, m, n, A, lda, x, incx, y, incy, &tr);
+    if (rc) return rc;
+    if (m == 0 || n == 0 || (host_is_zero(alpha) && host_is_one(beta))) return 0;
+    const int leny = tr == 0 ? m : n, lenx = tr == 0 ? n : m;
+    const long long ky = incy > 0 ? 0 : (long long)(1 - leny) * incy;
+    const long long kx = incx > 0 ? 0 : (long long)(1 - lenx) * incx;
+    const int beta_zero = host_is_zero(beta) ? 1 : 0;
+    if (host_is_zero(alpha)) {
+        symv_scale<T><<<blocks_for(leny, 256), 256, 0, stream>>>(y, incy, ky, leny, beta,
+                                                                 beta_zero);
+        XSYMV_HIP(hipGetLastError());
+        return 0;
+    }
+    const auto& sets = gemv_kernel_sets<T>();
+    const int idx = forced_idx >= 0 ? forced_idx : gemv_selected(prec_code<T>());
+    const GemvKernelSet<T>& ks = sets[idx];
+    const int R = ks.R();
+    const int threads = 64 * ks.W;
+    auto kern = ks.k[tr];
+
+    int dev = 0;
+    XSYMV_HIP(hipGetDevice(&dev));
+    DeviceState* ds = device_state(dev);
+    std::lock_guard<std::mutex> lk(device_mutex(ds));
+    int G = 0;
+    rc = resident_blocks((const void*)kern, threads, &G);
+    if (rc) return rc;
+    const StripPlan* plan = nullptr;
+    rc = get_gemv_plan(ds, m, n, R, G, stream, &plan);
+    if (rc) return rc;
+    void* ws = nullptr;
+    rc = get_workspace(ds, stream, gemv_workspace_bytes<T>(tr, plan->nseg, R, plan->NS, n, lenx),
+                       &ws);
+    if (rc) return rc;
+    char* base = static_cast<char*>(ws);
+    const size_t part_bytes = align_up((tr == 0 ? (size_t)plan->nseg * R : (size_t)plan->NS * n) *
+                                       sizeof(T));
+    T* part = reinterpret_cast<T*>(base);
+    T* xg = reinterpret_cast<T*>(base + part_bytes);
+    const T* xin = x;
+    if (incx != 1) {
+        symv_gather<T><<<blocks_for(lenx, 256), 256, 0, stream>>>(x, incx, kx, lenx, xg);
+        XSYMV_HIP(hipGetLastError());
+        xin = xg;
+    }
+    TimedCall tc{};
+    const bool timing = timing_enabled();
+    if (timing) {
+        XSYMV_HIP(hipEventCreate(&tc.e0));
+        XSYMV_HIP(hipEventCreate(&tc.e1));
+        XSYMV_HIP(hipEventCreate(&tc.e2));
+        XSYMV_HIP(hipEventRecord(tc.e0, stream));
+    }
+    GemvArgs<T> ga{A, xin, part, part, plan->d_blocks, (long long)lda, m, n};
+    kern<<<plan->G, threads, 0, stream>>>(ga);
+    XSYMV_HIP(hipGetLastError());
+    if (timing) XSYMV_HIP(hipEventRecord(tc.e1, stream));
+    GemvMergeArgs<T> ma{part, plan->d_seg_base, y, (long long)incy, ky, alpha, beta, leny,
+                        plan->NS, R, n, tr, beta_zero};
+    gemv_merge<T, MERGE_SPLIT><<<blocks_for(leny, 64), 64 * MERGE_SPLIT, 0, stream>>>(ma);
+    XSYMV_HIP(hipGetLastError());
+    if (timing) {
+        XSYMV_HIP(hipEventRecord(tc.e2, stream));
+        timing_push(tc);
+    }
+    return 0;
+}
+
+template <class T>
+size_t gemv_ws_bytes(char trans, int m, int n)
+{
+    const int tr = (trans == 'N' || trans == 'n') ? 0 : 1;
+    if (m <= 0 || n <= 0) return 0;
+    const auto& ks = gemv_kernel_sets<T>()[gemv_selected(prec_code<T>())];
+    int G = 0;
+    if (resident_blocks((const void*)ks.k[tr], 64 * ks.W, &G)) return (size_t)-1;
+    std::vector<StripBlock> blocks;
+    std::vector<int> segb;
+    int NS = 0;
+    build_gemv_plan_host(m, n, ks.R(), G, blocks, segb, NS);
+    return gemv_workspace_bytes<T>(tr, segb[NS], ks.R(), NS, n, tr == 0 ? n : m);
 }
 
 // ---------------------------------------------------------------- autotuner

@@ -32,6 +32,17 @@ int autotune_for<cf32>(char uplo, int n, int reps, hipStream_t stream, int* best
 {
     return autotune_impl<cf32>(uplo, n, reps, stream, best_idx, ms, max_cfg);
 }
+
+// xGEMV configurations (index 0 is the default; xgemv_select_config chooses)
+template <> const std::vector<GemvKernelSet<cf32>>& gemv_kernel_sets<cf32>()
+{
+    static const std::vector<GemvKernelSet<cf32>> v = {
+        make_gemv<cf32, 16, 1, 8, true>(),                 // R 2048, 16 KB runs, G 8
+        make_gemv<cf32, 16, 2, 4, true>(),                 // R 4096, 32 KB runs, G 4
+        make_gemv<cf32, 8, 2, 8, true>(),                  // R 2048, 16 KB runs, G 8
+    };
+    return v;
+}
 }  // namespace xsymv
 
 extern "C" int xhemv_c(char uplo, int n, xcomplex64 alpha, const xcomplex64* A, int lda,
@@ -42,4 +53,15 @@ extern "C" int xhemv_c(char uplo, int n, xcomplex64 alpha, const xcomplex64* A, 
     return xsymv::symv_impl<cf32>(uplo, n, cf32{alpha.re, alpha.im}, (const cf32*)A, lda,
                                   (const cf32*)x, incx, cf32{beta.re, beta.im}, (cf32*)y, incy,
                                   (hipStream_t)stream);
+}
+
+extern "C" int xgemv_c(char trans, int m, int n, xcomplex64 alpha, const xcomplex64* A, int lda,
+                       const xcomplex64* x, int incx, xcomplex64 beta, xcomplex64* y, int incy,
+                       void* stream)
+{
+    using xsymv::cf32;
+    return xsymv::gemv_run<cf32>(trans, m, n, cf32{alpha.re, alpha.im},
+                               reinterpret_cast<const cf32*>(A), lda,
+                               reinterpret_cast<const cf32*>(x), incx, cf32{beta.re, beta.im},
+                               reinterpret_cast<cf32*>(y), incy, (hipStream_t)stream, -1);
 }

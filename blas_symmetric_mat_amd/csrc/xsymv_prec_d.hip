@@ -39,6 +39,18 @@ int autotune_for<double>(char uplo, int n, int reps, hipStream_t stream, int* be
 {
     return autotune_impl<double>(uplo, n, reps, stream, best_idx, ms, max_cfg);
 }
+
+// xGEMV configurations (index 0 is the default; xgemv_select_config chooses)
+template <> const std::vector<GemvKernelSet<double>>& gemv_kernel_sets<double>()
+{
+    static const std::vector<GemvKernelSet<double>> v = {
+        make_gemv<double, 16, 2, 4, true>(),               // R 4096, 32 KB runs, G 4
+        make_gemv<double, 16, 1, 8, true>(),               // R 2048, 16 KB runs, G 8
+        make_gemv<double, 16, 1, 16, true>(),              // R 2048, 16 KB runs, G 16
+        make_gemv<double, 8, 2, 8, true>(),                // R 2048, 16 KB runs, G 8
+    };
+    return v;
+}
 }  // namespace xsymv
 
 extern "C" int xsymv_d(char uplo, int n, double alpha, const double* A, int lda,
@@ -47,4 +59,11 @@ extern "C" int xsymv_d(char uplo, int n, double alpha, const double* A, int lda,
 {
     return xsymv::symv_impl<double>(uplo, n, alpha, A, lda, x, incx, beta, y, incy,
                                     (hipStream_t)stream);
+}
+
+extern "C" int xgemv_d(char trans, int m, int n, double alpha, const double* A, int lda,
+                       const double* x, int incx, double beta, double* y, int incy, void* stream)
+{
+    return xsymv::gemv_run<double>(trans, m, n, alpha, A, lda, x, incx, beta, y, incy,
+                               (hipStream_t)stream, -1);
 }

@@ -37,6 +37,18 @@ int autotune_for<float>(char uplo, int n, int reps, hipStream_t stream, int* bes
 {
     return autotune_impl<float>(uplo, n, reps, stream, best_idx, ms, max_cfg);
 }
+
+// xGEMV configurations (index 0 is the default; xgemv_select_config chooses)
+template <> const std::vector<GemvKernelSet<float>>& gemv_kernel_sets<float>()
+{
+    static const std::vector<GemvKernelSet<float>> v = {
+        make_gemv<float, 16, 1, 8, true>(),                // R 4096, 16 KB runs, G 8
+        make_gemv<float, 16, 1, 16, true>(),               // R 4096, 16 KB runs, G 16
+        make_gemv<float, 8, 2, 8, true>(),                 // R 4096, 16 KB runs, G 8
+        make_gemv<float, 16, 2, 4, true>(),                // R 8192, 32 KB runs, G 4
+    };
+    return v;
+}
 }  // namespace xsymv
 
 extern "C" int xsymv_s(char uplo, int n, float alpha, const float* A, int lda, const float* x,
@@ -44,4 +56,11 @@ extern "C" int xsymv_s(char uplo, int n, float alpha, const float* A, int lda, c
 {
     return xsymv::symv_impl<float>(uplo, n, alpha, A, lda, x, incx, beta, y, incy,
                                    (hipStream_t)stream);
+}
+
+extern "C" int xgemv_s(char trans, int m, int n, float alpha, const float* A, int lda,
+                       const float* x, int incx, float beta, float* y, int incy, void* stream)
+{
+    return xsymv::gemv_run<float>(trans, m, n, alpha, A, lda, x, incx, beta, y, incy,
+                               (hipStream_t)stream, -1);
 }

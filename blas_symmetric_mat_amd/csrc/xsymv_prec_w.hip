@@ -33,13 +33,36 @@ int autotune_for<ddreal>(char uplo, int n, int reps, hipStream_t stream, int* be
 {
     return autotune_impl<ddreal>(uplo, n, reps, stream, best_idx, ms, max_cfg);
 }
+
+// xGEMV configurations (index 0 is the default; xgemv_select_config chooses)
+template <> const std::vector<GemvKernelSet<ddreal>>& gemv_kernel_sets<ddreal>()
+{
+    static const std::vector<GemvKernelSet<ddreal>> v = {
+        make_gemv<ddreal, 4, 4, 4, true>(),                // R 1024, 16 KB runs, G 4
+        make_gemv<ddreal, 16, 1, 4, true>(),               // R 1024, 16 KB runs, G 4
+        make_gemv<ddreal, 8, 2, 4, true>(),                // R 1024, 16 KB runs, G 4
+    };
+    return v;
+}
 }  // namespace xsymv
 
 extern "C" int xsymv_w(char uplo, int n, xdd alpha, const xdd* A, int lda, const xdd* x,
-                       int incx, xdd beta, xdd* y, int incy, void* stream)
+                       int incx, xdd beta, xdd* y, int incy,
+                       void* stream)
 {
     using xsymv::ddreal;
     return xsymv::symv_impl<ddreal>(uplo, n, ddreal{alpha.hi, alpha.lo}, (const ddreal*)A, lda,
                                     (const ddreal*)x, incx, ddreal{beta.hi, beta.lo},
                                     (ddreal*)y, incy, (hipStream_t)stream);
+}
+
+extern "C" int xgemv_w(char trans, int m, int n, xdd alpha, const xdd* A, int lda,
+                       const xdd* x, int incx, xdd beta, xdd* y, int incy,
+                       void* stream)
+{
+    using xsymv::ddreal;
+    return xsymv::gemv_run<ddreal>(trans, m, n, ddreal{alpha.hi, alpha.lo},
+                               reinterpret_cast<const ddreal*>(A), lda,
+                               reinterpret_cast<const ddreal*>(x), incx, ddreal{beta.hi, beta.lo},
+                               reinterpret_cast<ddreal*>(y), incy, (hipStream_t)stream, -1);
 }

@@ -32,14 +32,37 @@ int autotune_for<cf64>(char uplo, int n, int reps, hipStream_t stream, int* best
 {
     return autotune_impl<cf64>(uplo, n, reps, stream, best_idx, ms, max_cfg);
 }
+
+// xGEMV configurations (index 0 is the default; xgemv_select_config chooses)
+template <> const std::vector<GemvKernelSet<cf64>>& gemv_kernel_sets<cf64>()
+{
+    static const std::vector<GemvKernelSet<cf64>> v = {
+        make_gemv<cf64, 16, 2, 4, true>(),                 // R 2048, 32 KB runs, G 4
+        make_gemv<cf64, 16, 1, 8, true>(),                 // R 1024, 16 KB runs, G 8
+        make_gemv<cf64, 8, 2, 4, true>(),                  // R 1024, 16 KB runs, G 4
+    };
+    return v;
+}
 }  // namespace xsymv
 
 extern "C" int xhemv_z(char uplo, int n, xcomplex128 alpha, const xcomplex128* A, int lda,
                        const xcomplex128* x, int incx, xcomplex128 beta, xcomplex128* y,
-                       int incy, void* stream)
+                       int incy,
+                       void* stream)
 {
     using xsymv::cf64;
     return xsymv::symv_impl<cf64>(uplo, n, cf64{alpha.re, alpha.im}, (const cf64*)A, lda,
                                   (const cf64*)x, incx, cf64{beta.re, beta.im}, (cf64*)y, incy,
                                   (hipStream_t)stream);
+}
+
+extern "C" int xgemv_z(char trans, int m, int n, xcomplex128 alpha, const xcomplex128* A, int lda,
+                       const xcomplex128* x, int incx, xcomplex128 beta, xcomplex128* y, int incy,
+                       void* stream)
+{
+    using xsymv::cf64;
+    return xsymv::gemv_run<cf64>(trans, m, n, cf64{alpha.re, alpha.im},
+                               reinterpret_cast<const cf64*>(A), lda,
+                               reinterpret_cast<const cf64*>(x), incx, cf64{beta.re, beta.im},
+                               reinterpret_cast<cf64*>(y), incy, (hipStream_t)stream, -1);
 }

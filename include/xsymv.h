@@ -97,6 +97,59 @@ int xsymv_w(char uplo, int n, xdd alpha, const xdd *A, int lda,
             const xdd *x, int incx, xdd beta, xdd *y, int incy,
             void *stream);
 
+/* xGEMV, the general product the report sets SYMV against (a general matrix
+ * is read whole and each element used once; the symmetric product reads one
+ * triangle and uses each element twice, so it moves half the bytes -- report
+ * §1, §2.1):
+ *
+ *   y := alpha*op(A)*x + beta*y,  op(A) = A (trans 'N'/'n'), A^T ('T'/'t')
+ *                                or A^H ('C'/'c'; the same as 'T' for the
+ *                                real and double-double types)
+ *
+ * BLAS xGEMV arguments: A is m x n, column-major, DEVICE pointer, element
+ * (i, j) at A[i + j*lda], rows m..lda-1 never read; x has n elements for 'N'
+ * and m otherwise, y the other length (DEVICE pointers, strides incx/incy as
+ * for the symmetric calls).  Same ownership, asynchrony, determinism,
+ * workspace (per device and stream, or installed with xsymv_set_workspace)
+ * and beta == 0 / alpha == 0 rules as the symmetric calls.  m == 0, n == 0,
+ * or alpha == 0 with beta == 1 return without touching y.
+ *
+ * Return codes (BLAS xerbla positions, checked before any device work):
+ *   -1 trans not N/T/C (either case), -2 m < 0, -3 n < 0, -5 A NULL with
+ *   m, n > 0, -6 lda < max(1, m), -7 x NULL, -8 incx == 0, -10 y NULL,
+ *   -11 incy == 0; 1000 + hipError_t; 2000 installed workspace too small. */
+int xgemv_s(char trans, int m, int n, float alpha, const float *A, int lda,
+            const float *x, int incx, float beta, float *y, int incy, void *stream);
+int xgemv_d(char trans, int m, int n, double alpha, const double *A, int lda,
+            const double *x, int incx, double beta, double *y, int incy, void *stream);
+int xgemv_c(char trans, int m, int n, xcomplex64 alpha, const xcomplex64 *A, int lda,
+            const xcomplex64 *x, int incx, xcomplex64 beta, xcomplex64 *y, int incy,
+            void *stream);
+int xgemv_z(char trans, int m, int n, xcomplex128 alpha, const xcomplex128 *A, int lda,
+            const xcomplex128 *x, int incx, xcomplex128 beta, xcomplex128 *y, int incy,
+            void *stream);
+int xgemv_w(char trans, int m, int n, xdd alpha, const xdd *A, int lda, const xdd *x,
+            int incx, xdd beta, xdd *y, int incy, void *stream);
+
+/* xGEMV configurations: each precision has a compiled list (entry 0 the
+ * default); info gives waves per workgroup, stripes per wave, columns per
+ * group, non-temporal loads (0/1) and rows per strip (outputs may be NULL;
+ * returns 0 or -1 for a bad index).  select installs entry idx (-1: entry 0)
+ * for every later call of that precision (0 or -1); current returns it.
+ * workspace_bytes: device workspace of one call on the current device with
+ * the selected entry (-1 cast to size_t on a bad code or when the device
+ * cannot be queried).  xgemv_plan: the work split for m x n, strips of R
+ * rows and G workgroups (host computation; blocks4 as for xsymv_strip_plan,
+ * seg_base[NS+1]); returns the number of workgroups, -1 or -2. */
+int xgemv_num_configs(int prec);
+int xgemv_config_info(int prec, int idx, int *waves, int *stripes_per_wave,
+                      int *cols_per_group, int *nontemporal, int *rows_per_strip);
+int xgemv_select_config(int prec, int idx);
+int xgemv_current_config(int prec);
+size_t xgemv_workspace_bytes(int prec, char trans, int m, int n);
+int xgemv_plan(int m, int n, int R, int G, int *blocks4, int max_blocks, int *seg_base,
+               int max_strips);
+
 /* Bytes of device workspace one call of precision `prec` and order n uses
  * with the configuration selected for it now, on the current device (0 for
  * n == 0; -1 cast to size_t for a bad precision code, or when the device

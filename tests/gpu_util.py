@@ -72,3 +72,41 @@ def assert_close(p, got, ref, rows=None, label=""):
     bad = np.nonzero(~(d <= tol))[0]
     assert bad.size == 0, (f"{label}: {bad.size} rows beyond the bound, worst ratio "
                            f"{np.max(d / np.maximum(tol, 1e-300)):.3g} at row {bad[0]}")
+
+
+GENTRY = {"s": "xgemv_s", "d": "xgemv_d", "c": "xgemv_c", "z": "xgemv_z", "w": "xgemv_w"}
+
+
+class GemvDevice:
+    """A general problem's A and x on the device; y is uploaded per call."""
+
+    def __init__(self, p):
+        self.p = p
+        self.A = to_device(p.A)
+        self.x = to_device(p.x)
+
+    def run(self, y_host=None):
+        import blas_symmetric_mat_amd as X
+        torch = torch_dev()
+        p = self.p
+        y = to_device(p.y if y_host is None else y_host)
+        getattr(X, GENTRY[p.prec])(p.trans, p.m, p.n, p.alpha, self.A, p.lda, self.x, p.incx,
+                                   p.beta, y, p.incy)
+        torch.cuda.synchronize()
+        return y.cpu().numpy()
+
+
+def assert_close_gemv(p, got, ref, rows=None, label=""):
+    """|got - ref| <= 4*k*eps*(|alpha||op(A)||x| + |beta||y|) per output (k the
+    inner length), on all outputs or on ``rows`` (got/ref then hold those)."""
+    if rows is None:
+        tol = H.gemv_tolerance(p)
+        idx = H.vec_index(p.leny, p.incy)
+        d = H.diff(p.prec, got[idx], ref[idx])
+    else:
+        tol = H.gemv_tolerance(p, rows)
+        d = H.diff(p.prec, got, ref)
+    assert np.all(np.isfinite(d)), f"{label}: non-finite result"
+    bad = np.nonzero(~(d <= tol))[0]
+    assert bad.size == 0, (f"{label}: {bad.size} outputs beyond the bound, worst ratio "
+                           f"{np.max(d / np.maximum(tol, 1e-300)):.3g} at {bad[0]}")

@@ -16,13 +16,14 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def declared_functions():
     text = open(os.path.join(ROOT, "include", "xsymv.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(x(?:symv|hemv)_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(x(?:symv|hemv|gemv)_\w+)\s*\(", text)))
 
 
 def test_exports_every_declared_function():
     lib = ctypes.CDLL(X.LIB_PATH)
     names = declared_functions()
-    assert {"xsymv_s", "xsymv_d", "xhemv_c", "xhemv_z", "xsymv_w"} <= set(names)
+    assert {"xsymv_s", "xsymv_d", "xhemv_c", "xhemv_z", "xsymv_w", "xgemv_s", "xgemv_d",
+            "xgemv_c", "xgemv_z", "xgemv_w", "xsymv_set_workspace"} <= set(names)
     for nm in names:
         assert hasattr(lib, nm), nm
 
@@ -180,3 +181,82 @@ def test_bench_labels_every_configuration():
 def test_set_workspace_argument_check():
     # a NULL buffer with a size is refused before any device query
     assert X.library().xsymv_set_workspace(None, 64, None) == -2
+
+
+@pytest.mark.parametrize("prec", ["s", "d", "c", "z", "w"])
+def test_gemv_argument_errors_before_device_work(prec):
+    f = getattr(X, "xgemv_" + prec)
+    one = (1.0, 0.0) if prec == "w" else 1.0
+    zero = (0.0, 0.0) if prec == "w" else 0.0
+    # (trans, m, n, alpha, A, lda, x, incx, beta, y, incy); pointers are never touched
+    cases = [(("Q", 4, 3, one, 8, 4, 8, 1, zero, 8, 1), -1),
+             (("N", -1, 3, one, 8, 4, 8, 1, zero, 8, 1), -2),
+             (("T", 4, -1, one, 8, 4, 8, 1, zero, 8, 1), -3),
+             (("C", 4, 3, one, None, 4, 8, 1, zero, 8, 1), -5),
+             (("n", 4, 3, one, 8, 3, 8, 1, zero, 8, 1), -6),
+             (("t", 4, 3, one, 8, 4, None, 1, zero, 8, 1), -7),
+             (("c", 4, 3, one, 8, 4, 8, 0, zero, 8, 1), -8),
+             (("N", 4, 3, one, 8, 4, 8, 1, zero, None, 1), -10),
+             (("N", 4, 3, one, 8, 4, 8, 1, zero, 8, 0), -11),
+             (("N", 0, 3, one, 8, 0, 8, 1, zero, 8, 1), -6)]
+    for args, code in cases:
+        with pytest.raises(X.XsymvError) as e:
+            f(*args, stream=0)
+        assert e.value.code == code, (args, e.value.code)
+    # quick returns: m == 0 or n == 0 (lda >= 1), alpha == 0 and beta == 1
+    f("N", 0, 5, one, None, 1, None, 1, zero, None, 1, stream=0)
+    f("T", 5, 0, one, None, 5, None, 1, zero, None, 1, stream=0)
+    f("N", 5, 4, zero, 8, 5, 8, 1, one, 8, 1, stream=0)
+
+
+def test_gemv_config_tables():
+    for p in "sdczw":
+        k = X.gemv_num_configs(p)
+        assert k >= 1
+        for i in range(k):
+            ci = X.gemv_config_info(p, i)
+            assert ci["rows_per_strip"] == ci["waves"] * ci["stripes_per_wave"] * 64 * \
+                {"s": 4, "d": 2, "c": 2, "z": 1, "w": 1}[p]
+        with pytest.raises(IndexError):
+            X.gemv_config_info(p, k)
+        assert X.gemv_current_config(p) == 0
+    X.gemv_select_config("d", 1)
+    assert X.gemv_current_config("d") == 1
+    X.gemv_select_config("d", -1)
+    assert X.gemv_current_config("d") == 0
+    with pytest.raises(ValueError):
+        X.gemv_select_config("s", 99)
+
+
+@pytest.mark.parametrize("m,n,R,G", [(1, 1, 64, 5), (100, 7, 64, 3), (1000, 77, 256, 37),
+                                     (4096, 4096, 1024, 1024), (10007, 333, 2048, 256),
+                                     (300, 5000, 512, 1)])
+def test_gemv_plan_covers_every_column_once(m, n, R, G):
+    """Every (strip, column) pair is in exactly one workgroup's range, each
+    range's pieces get consecutive slots, and seg_base lists each strip's
+    slots in order (the order the merge reads)."""
+    blocks, segb = X.gemv_plan(m, n, R, G)
+    NS = (m + R - 1) // R
+    seen = np.zeros(NS * n, dtype=np.int32)
+    slots_of_strip = {}
+    prev_end = 0
+    slot_expect = 0
+    for u0, u1, slot, strip in blocks:
+        assert u0 == prev_end and u1 >= u0
+        prev_end = u1
+        assert slot == slot_expect
+        u, st = u0, strip
+        if u0 < u1:
+            assert st == u0 // n
+        while u < u1:
+            e = min(u1, (st + 1) * n)
+            seen[u:e] += 1
+            slots_of_strip.setdefault(st, []).append(slot_expect)
+            slot_expect += 1
+            u = e
+            st += 1
+    assert prev_end == NS * n
+    assert np.all(seen == 1)
+    assert segb[NS] == slot_expect
+    for st in range(NS):
+        assert slots_of_strip[st] == list(range(segb[st], segb[st + 1]))
