@@ -17,6 +17,10 @@ Printed as one JSON line, with:
                 (xsymv_read_bandwidth), the secondary reference: every rate
                 is also given as % of it (`pct_measured_read_peak`);
   cpu_baseline  the CPU oracle (single thread) on the same problem;
+  symv_over_gemv_time  the symmetric call's time over the general one's on
+                the same order (GEMV detail rows: SGEMV 'N' and 'T', DGEMV
+                'N', n = 32768) -- the report's claim that SYMV, reading one
+                triangle, takes about half of GEMV's time;
   detail        the other workloads (fp64 n = 32768, both triangles, the small
                 and padded cases, CHEMV/ZHEMV n = 16384, WSYMV n = 8192), each
                 timed per call (20 calls, median and min) with the library's
@@ -98,6 +102,62 @@ class Dev:
 
     def reset_y(self):
         self.y.copy_(self.y0)
+
+
+class GemvDev:
+    """A general problem resident on the device."""
+
+    def __init__(self, p):
+        import numpy as np
+        import torch
+        import blas_symmetric_mat_amd as X
+        self.p = p
+        self.A = torch.from_numpy(np.ascontiguousarray(p.A)).to("cuda")
+        self.x = torch.from_numpy(np.ascontiguousarray(p.x)).to("cuda")
+        self.y = torch.from_numpy(np.ascontiguousarray(p.y)).to("cuda")
+        self.f = getattr(X, "xgemv_" + p.prec)
+
+    def call(self):
+        p = self.p
+        self.f(p.trans, p.m, p.n, p.alpha, self.A, p.lda, self.x, p.incx, p.beta, self.y,
+               p.incy)
+
+
+def measure_gemv_detail(name, p, reps, read_peak=None):
+    """The general product beside the symmetric one (the report's comparison:
+    same streaming machinery, twice the bytes)."""
+    from blas_symmetric_mat_amd import roofline as R
+    import torch
+    import blas_symmetric_mat_amd as X
+    log(f"detail: {name}")
+    d = GemvDev(p)
+    for _ in range(2):
+        d.call()
+    rec = time_kernels(d, reps)
+    main = sorted(r[0] for r in rec)
+    tot = sorted(r[0] + r[1] for r in rec)
+    t_main = main[len(main) // 2] * 1e-3
+    t_call = tot[len(tot) // 2] * 1e-3
+    bz = beta_is_zero(p)
+    call_b = R.gemv_call_bytes(p.prec, p.m, p.n, p.trans, bz)
+    ci = X.gemv_config_info(p.prec, X.gemv_current_config(p.prec))
+    out = {"prec": p.prec, "trans": p.trans, "m": p.m, "n": p.n, "lda": p.lda,
+           "kernel": (f"gemv_strip<{CTYPE[p.prec]}, {p.trans}, W={ci['waves']}, "
+                      f"SW={ci['stripes_per_wave']}, G={ci['cols_per_group']}, "
+                      f"{'nt' if ci['nontemporal'] else 'cached'}>"),
+           "ms_per_call_median": round(t_call * 1e3, 4),
+           "ms_per_call_min": round(tot[0], 4),
+           "gflops_2mn": round(2.0 * p.m * p.n / t_call / 1e9, 2),
+           "hbm_gbps_algorithmic": round(call_b / t_call / 1e9, 1),
+           "pct_peak_hbm": round(100 * call_b / t_call / 1e9 / R.HBM_PEAK_GBPS, 1),
+           "tile_kernel_gbps": round(R.gemv_kernel_bytes(p.prec, p.m, p.n, p.trans) / t_main
+                                     / 1e9, 1),
+           "flushed_between_calls": False, "calls": reps}
+    if read_peak:
+        out["pct_measured_read_peak"] = round(100 * call_b / t_call / 1e9 / read_peak, 1)
+    del d
+    torch.cuda.empty_cache()
+    return out
 
 
 def beta_is_zero(p):
@@ -435,7 +495,19 @@ def main():
                  ("wsymv-L-n8192", W.wsymv_lower_n8192)]
         for name, make in cases:
             detail[name] = measure_detail(name, make(), args.detail_reps, flush, rd_med)
+        gcases = [("sgemv-N-n32768", lambda: W.gemv_square("s", "N", 32768)),
+                  ("sgemv-T-n32768", lambda: W.gemv_square("s", "T", 32768)),
+                  ("dgemv-N-n32768", lambda: W.gemv_square("d", "N", 32768))]
+        for name, make in gcases:
+            detail[name] = measure_gemv_detail(name, make(), args.detail_reps, rd_med)
         out["detail"] = detail
+        # the report's point: SYMV reads half the bytes of GEMV on the same
+        # order, so takes about half the time
+        out["symv_over_gemv_time"] = {
+            "sgemv-N-n32768": round(ms_per_step / detail["sgemv-N-n32768"]["ms_per_call_median"],
+                                    3),
+            "dsymv-L/dgemv-N-n32768": round(detail["dsymv-L-n32768"]["ms_per_call_median"] /
+                                            detail["dgemv-N-n32768"]["ms_per_call_median"], 3)}
         del flush_buf
 
     if args.pmc_calibrate:

@@ -33,13 +33,15 @@ int autotune_for<cf32>(char uplo, int n, int reps, hipStream_t stream, int* best
     return autotune_impl<cf32>(uplo, n, reps, stream, best_idx, ms, max_cfg);
 }
 
-// xGEMV configurations (index 0 is the default; xgemv_select_config chooses)
+// xGEMV configurations (index 0 is the default -- the fastest for both
+// 'N' and 'T' at the largest size measured on MI355X; xgemv_select_config
+// chooses another)
 template <> const std::vector<GemvKernelSet<cf32>>& gemv_kernel_sets<cf32>()
 {
     static const std::vector<GemvKernelSet<cf32>> v = {
+        make_gemv<cf32, 8, 2, 8, true>(),                  // R 2048, 16 KB runs, G 8
         make_gemv<cf32, 16, 1, 8, true>(),                 // R 2048, 16 KB runs, G 8
         make_gemv<cf32, 16, 2, 4, true>(),                 // R 4096, 32 KB runs, G 4
-        make_gemv<cf32, 8, 2, 8, true>(),                  // R 2048, 16 KB runs, G 8
     };
     return v;
 }

@@ -40,12 +40,14 @@ int autotune_for<double>(char uplo, int n, int reps, hipStream_t stream, int* be
     return autotune_impl<double>(uplo, n, reps, stream, best_idx, ms, max_cfg);
 }
 
-// xGEMV configurations (index 0 is the default; xgemv_select_config chooses)
+// xGEMV configurations (index 0 is the default -- the fastest for both
+// 'N' and 'T' at the largest size measured on MI355X; xgemv_select_config
+// chooses another)
 template <> const std::vector<GemvKernelSet<double>>& gemv_kernel_sets<double>()
 {
     static const std::vector<GemvKernelSet<double>> v = {
-        make_gemv<double, 16, 2, 4, true>(),               // R 4096, 32 KB runs, G 4
         make_gemv<double, 16, 1, 8, true>(),               // R 2048, 16 KB runs, G 8
+        make_gemv<double, 16, 2, 4, true>(),               // R 4096, 32 KB runs, G 4
         make_gemv<double, 16, 1, 16, true>(),              // R 2048, 16 KB runs, G 16
         make_gemv<double, 8, 2, 8, true>(),                // R 2048, 16 KB runs, G 8
     };

@@ -38,14 +38,16 @@ int autotune_for<float>(char uplo, int n, int reps, hipStream_t stream, int* bes
     return autotune_impl<float>(uplo, n, reps, stream, best_idx, ms, max_cfg);
 }
 
-// xGEMV configurations (index 0 is the default; xgemv_select_config chooses)
+// xGEMV configurations (index 0 is the default -- the fastest for both
+// 'N' and 'T' at the largest size measured on MI355X; xgemv_select_config
+// chooses another)
 template <> const std::vector<GemvKernelSet<float>>& gemv_kernel_sets<float>()
 {
     static const std::vector<GemvKernelSet<float>> v = {
+        make_gemv<float, 16, 2, 4, true>(),                // R 8192, 32 KB runs, G 4
         make_gemv<float, 16, 1, 8, true>(),                // R 4096, 16 KB runs, G 8
         make_gemv<float, 16, 1, 16, true>(),               // R 4096, 16 KB runs, G 16
         make_gemv<float, 8, 2, 8, true>(),                 // R 4096, 16 KB runs, G 8
-        make_gemv<float, 16, 2, 4, true>(),                // R 8192, 32 KB runs, G 4
     };
     return v;
 }

@@ -34,13 +34,15 @@ int autotune_for<ddreal>(char uplo, int n, int reps, hipStream_t stream, int* be
     return autotune_impl<ddreal>(uplo, n, reps, stream, best_idx, ms, max_cfg);
 }
 
-// xGEMV configurations (index 0 is the default; xgemv_select_config chooses)
+// xGEMV configurations (index 0 is the default -- the fastest for both
+// 'N' and 'T' at the largest size measured on MI355X; xgemv_select_config
+// chooses another)
 template <> const std::vector<GemvKernelSet<ddreal>>& gemv_kernel_sets<ddreal>()
 {
     static const std::vector<GemvKernelSet<ddreal>> v = {
+        make_gemv<ddreal, 8, 2, 4, true>(),                // R 1024, 16 KB runs, G 4
         make_gemv<ddreal, 4, 4, 4, true>(),                // R 1024, 16 KB runs, G 4
         make_gemv<ddreal, 16, 1, 4, true>(),               // R 1024, 16 KB runs, G 4
-        make_gemv<ddreal, 8, 2, 4, true>(),                // R 1024, 16 KB runs, G 4
     };
     return v;
 }

@@ -52,3 +52,20 @@ def tile_kernel_bytes(prec: str, n: int) -> int:
     """Algorithmic bytes of the streaming kernel of one call: the stored
     triangle and x."""
     return ELEM_BYTES[prec] * (stored_elements(n) + n)
+
+
+# ------------------------------------------------------------------ xGEMV
+# A general m x n matrix is read whole and each element feeds one
+# multiply-add (2 real flops; 8 for complex): the report's comparison point.
+
+def gemv_call_bytes(prec: str, m: int, n: int, trans: str, beta_zero: bool) -> int:
+    """Algorithmic bytes of one GEMV call: A (m*n), x, y read (unless
+    beta == 0) and y written."""
+    lenx, leny = (n, m) if trans in ("N", "n") else (m, n)
+    return ELEM_BYTES[prec] * (m * n + lenx + leny * (1 if beta_zero else 2))
+
+
+def gemv_kernel_bytes(prec: str, m: int, n: int, trans: str) -> int:
+    """Algorithmic bytes of the GEMV streaming kernel: A and x."""
+    lenx = n if trans in ("N", "n") else m
+    return ELEM_BYTES[prec] * (m * n + lenx)

@@ -320,7 +320,6 @@ def wsymv_lower_n8192(n: int = 8192) -> Problem:
 
 def gemv_square(prec: str, trans: str, n: int) -> GemvProblem:
     """xGEMV beside the [SD]SYMV sweep: m = n = lda, uniform A, x, y;
-    alpha = beta = 1; seed = n (the same draws as the full matrix a SYMV
-    problem of order n would need)."""
+    alpha = beta = 1; seed = n."""
     return make_gemv_problem(prec, trans, n, n, n, alpha=1.0, beta=1.0, seed=n,
                              name=f"{prec}gemv-{trans}-n{n}")

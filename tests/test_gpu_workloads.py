@@ -83,3 +83,22 @@ def test_hemv_lower_n16384(prec):
 
 def test_wsymv_lower_n8192():
     check(W.wsymv_lower_n8192(), full=True)
+
+
+# ------------------------------------------- xGEMV beside the symmetric sweep
+
+@pytest.mark.parametrize("prec,trans,n", [("s", "N", 32768), ("s", "T", 32768),
+                                          ("d", "N", 32768), ("d", "C", 16384),
+                                          ("s", "N", 10007)])
+def test_gemv_square(prec, trans, n):
+    """The general products the benchmark times beside the symmetric ones,
+    at full size: sampled outputs against the oracle, ten identical runs."""
+    p = W.gemv_square(prec, trans, n)
+    G.log(f"workload {p.name}: m=n={n}")
+    d = G.GemvDevice(p)
+    outs = [d.run() for _ in range(10)]
+    assert len({G.digest(o) for o in outs}) == 1, "results differ between runs"
+    rows = sample_rows(p.leny, seed=n + 1)
+    ref = oracle.gemv_rows_problem(p, rows)
+    G.assert_close_gemv(p, outs[0][rows], ref, rows=rows, label=p.name)
+    G.log(f"  ok ({len(rows)} sampled outputs)")
