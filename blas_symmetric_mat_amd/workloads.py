@@ -272,6 +272,39 @@ def make_gemv_problem(prec: str, trans: str, m: int, n: int, lda: int | None = N
     return GemvProblem(prec, trans, m, n, lda, alpha, beta, A, x, y, name=name)
 
 
+@dataclasses.dataclass
+class Syr2Problem:
+    """One rank-2 update's arguments (host arrays): A holds the stored
+    triangle (the other triangle and padding hold `fill`)."""
+    prec: str
+    uplo: str
+    n: int
+    lda: int
+    alpha: Any
+    x: np.ndarray
+    y: np.ndarray
+    A: np.ndarray
+    incx: int = 1
+    incy: int = 1
+    name: str = ""
+
+
+def make_syr2_problem(prec: str, uplo: str, n: int, lda: int | None = None, *,
+                      alpha: Any = 1.0, seed: int = 0, fill: float = np.nan,
+                      diag_imag_scale: float | None = None,
+                      integer: tuple[int, int] | None = None, name: str = "") -> Syr2Problem:
+    """Draw a rank-2 update: the stored triangle column by column (as
+    make_problem does), then x, then y, then (Hermitian) the diagonal's
+    imaginary words, which the update must overwrite with zero."""
+    if integer is None:
+        p = make_problem(prec, uplo, n, lda, alpha=alpha, beta=alpha, seed=seed, fill=fill,
+                         diag_imag_scale=diag_imag_scale)
+        return Syr2Problem(prec, uplo, n, p.lda, alpha, p.x, p.y, p.A, name=name)
+    p = make_integer_problem(prec, uplo, n, lda, alpha=alpha, beta=alpha, seed=seed,
+                             lo=integer[0], hi=integer[1], fill=fill)
+    return Syr2Problem(prec, uplo, n, p.lda, p.alpha, p.x, p.y, p.A, name=name)
+
+
 # --------------------------------------------------------------------------
 # The benchmark workloads, named by what they are.
 # --------------------------------------------------------------------------

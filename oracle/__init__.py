@@ -50,6 +50,7 @@ class _DD(ctypes.Structure):
 _SCALAR = {"s": ctypes.c_float, "d": ctypes.c_double, "c": _CF, "z": _CD, "w": _DD}
 _NAME = {"s": "ssymv", "d": "dsymv", "c": "chemv", "z": "zhemv", "w": "wsymv"}
 _GNAME = {"s": "sgemv", "d": "dgemv", "c": "cgemv", "z": "zgemv", "w": "wgemv"}
+_RNAME = {"s": "ssyr2", "d": "dsyr2", "c": "cher2", "z": "zher2", "w": "wsyr2"}
 _NP = {"s": np.float32, "d": np.float64, "c": np.complex64, "z": np.complex128,
        "w": np.float64}
 
@@ -74,6 +75,10 @@ def _declare(lib):
         g.restype = ci
         g.argtypes = [ctypes.c_char, ci, ci, st, vp, ci, vp, ci, st, vp, ci,
                       vp, ci, vp]
+    for p, nm in _RNAME.items():
+        f = getattr(lib, "oracle_" + nm)
+        f.restype = ci
+        f.argtypes = [ctypes.c_char, ci, _SCALAR[p], vp, ci, vp, ci, vp, ci]
     for nm in ("oracle_dd_add", "oracle_dd_mul"):
         f = getattr(lib, nm)
         f.restype = _DD
@@ -196,6 +201,23 @@ class OracleLib:
         return self.gemv_rows(p.prec, p.trans, p.m, p.n, p.alpha, p.A, p.lda, p.x,
                               p.incx, p.beta, p.y, p.incy, rows)
 
+    def syr2(self, prec: str, uplo: str, n: int, alpha, x, incx: int, y, incy: int, A,
+             lda: int) -> int:
+        """A := alpha*x*y^H + conj(alpha)*y*x^H + A on the stored triangle, in
+        place.  Returns the status code."""
+        _check_dtype(prec, A, x, y)
+        f = getattr(self._lib, "oracle_" + _RNAME[prec])
+        return f(_uplo(uplo), n, scalar(prec, alpha), _ptr(x), incx, _ptr(y), incy,
+                 _ptr(A), lda)
+
+    def syr2_problem(self, p, A=None):
+        """Run on a ``workloads.Syr2Problem``; returns the new A (a copy)."""
+        A = (p.A if A is None else A).copy()
+        rc = self.syr2(p.prec, p.uplo, p.n, p.alpha, p.x, p.incx, p.y, p.incy, A, p.lda)
+        if rc != 0:
+            raise ValueError(f"oracle syr2 call failed with status {rc}")
+        return A
+
     def dd_add(self, a, b):
         r = self._lib.oracle_dd_add(_DD(*a), _DD(*b))
         return (r.hi, r.lo)
@@ -258,3 +280,11 @@ def gemv_problem(p, y=None):
 
 def gemv_rows_problem(p, rows=None):
     return default().gemv_rows_problem(p, rows)
+
+
+def syr2(*a, **k):
+    return default().syr2(*a, **k)
+
+
+def syr2_problem(p, A=None):
+    return default().syr2_problem(p, A)

@@ -38,6 +38,15 @@
  * ascending, of op(A)(i,k)*x(k), in the working precision.  Same BLAS rules
  * for beta == 0 (y not read), alpha == 0 and the quick return.
  *
+ * Symmetric / Hermitian rank-2 update (the report's §5 extends the approach
+ * to other Level-2 BLAS), BLAS xSYR2 / xHER2 on the stored triangle:
+ *   A := alpha*x*y^H + conj(alpha)*y*x^H + A  (real: alpha*x*y^T + alpha*y*x^T)
+ * in the BLAS reference order: for each column j, t1 = alpha*conj(y(j)),
+ * t2 = conj(alpha*x(j)), and every stored A(i,j) := (A(i,j) + x(i)*t1) +
+ * y(i)*t2; a Hermitian diagonal element becomes Re(A(j,j)) +
+ * Re(x(j)*t1 + y(j)*t2) with a zero imaginary part.  The other triangle is
+ * neither read nor written.
+ *
  * Double-double arithmetic (report §2.2, which takes Bailey's double-double
  * format [14]: a value is the unevaluated sum hi + lo of two doubles):
  *   TwoSum (Knuth) and FastTwoSum (Dekker) give a sum and its exact error;
@@ -420,3 +429,78 @@ DEFINE_GEMV(oracle_dgemv, oracle_dgemv_rows, double, d)
 DEFINE_GEMV(oracle_cgemv, oracle_cgemv_rows, ocplx_f, c)
 DEFINE_GEMV(oracle_zgemv, oracle_zgemv_rows, ocplx_d, z)
 DEFINE_GEMV(oracle_wgemv, oracle_wgemv_rows, odd, w)
+
+/* ------------------------------------------------------- xSYR2 / xHER2 */
+
+/* BLAS xSYR2 / xHER2 argument checks (xerbla positions: uplo, n, alpha, x,
+ * incx, y, incy, a, lda). */
+static int syr2_check(char uplo, int n, const void *x, int incx, const void *y,
+                      int incy, const void *A, int lda, int *upper)
+{
+    if (uplo == 'U' || uplo == 'u')
+        *upper = 1;
+    else if (uplo == 'L' || uplo == 'l')
+        *upper = 0;
+    else
+        return -1;
+    if (n < 0) return -2;
+    if (n > 0 && x == NULL) return -4;
+    if (incx == 0) return -5;
+    if (n > 0 && y == NULL) return -6;
+    if (incy == 0) return -7;
+    if (n > 0 && A == NULL) return -8;
+    if (lda < (n > 1 ? n : 1)) return -9;
+    return 0;
+}
+
+/* HERM = 1 for the Hermitian update (complex types): conjugates and the real
+ * diagonal; 0 for the symmetric one. */
+#define DEFINE_SYR2(NAME, T, P, HERM, REALPART)                                 \
+int NAME(char uplo, int n, T alpha, const T *x, int incx, const T *y,          \
+         int incy, T *A, int lda)                                               \
+{                                                                               \
+    int upper, i, j;                                                            \
+    int rc = syr2_check(uplo, n, x, incx, y, incy, A, lda, &upper);             \
+    if (rc) return rc;                                                          \
+    if (n == 0 || P##_is_zero(alpha)) return 0;                                 \
+    for (j = 0; j < n; ++j) {                                                   \
+        T xj = x[vpos(n, incx, j)], yj = y[vpos(n, incy, j)];                   \
+        T t1 = P##_mul(alpha, HERM ? P##_conj(yj) : yj);                        \
+        T t2 = HERM ? P##_conj(P##_mul(alpha, xj)) : P##_mul(alpha, xj);        \
+        int lo = upper ? 0 : j, hi = upper ? j + 1 : n;                         \
+        for (i = lo; i < hi; ++i) {                                             \
+            T *a = &A[(long long)i + (long long)j * lda];                       \
+            T xi = x[vpos(n, incx, i)], yi = y[vpos(n, incy, i)];               \
+            if (HERM && i == j) {                                               \
+                T s = P##_add(P##_mul(xi, t1), P##_mul(yi, t2));                \
+                *a = REALPART(*a, s);                                           \
+            } else {                                                            \
+                *a = P##_add(P##_add(*a, P##_mul(xi, t1)), P##_mul(yi, t2));    \
+            }                                                                   \
+        }                                                                       \
+    }                                                                           \
+    return 0;                                                                   \
+}
+
+/* Re(a) + Re(s), imaginary part zero (the Hermitian diagonal) */
+static ocplx_f c_herm_diag(ocplx_f a, ocplx_f s)
+{
+    ocplx_f r;
+    r.re = a.re + s.re;
+    r.im = 0.0f;
+    return r;
+}
+static ocplx_d z_herm_diag(ocplx_d a, ocplx_d s)
+{
+    ocplx_d r;
+    r.re = a.re + s.re;
+    r.im = 0.0;
+    return r;
+}
+#define NO_REALPART(a, s) ((void)(s), (a))
+
+DEFINE_SYR2(oracle_ssyr2, float, s, 0, NO_REALPART)
+DEFINE_SYR2(oracle_dsyr2, double, d, 0, NO_REALPART)
+DEFINE_SYR2(oracle_cher2, ocplx_f, c, 1, c_herm_diag)
+DEFINE_SYR2(oracle_zher2, ocplx_d, z, 1, z_herm_diag)
+DEFINE_SYR2(oracle_wsyr2, odd, w, 0, NO_REALPART)

@@ -105,6 +105,26 @@ int oracle_wgemv_rows(char trans, int m, int n, odd alpha, const odd *A, int lda
                       const odd *x, int incx, odd beta, const odd *y, int incy,
                       const long long *rows, int nrows, odd *out);
 
+/* Symmetric / Hermitian rank-2 update on the stored triangle, BLAS xSYR2 /
+ * xHER2: A := alpha*x*y^T + alpha*y*x^T + A (real, double-double) or
+ * A := alpha*x*y^H + conj(alpha)*y*x^H + A (complex; the diagonal stays real,
+ * its imaginary word is set to zero).  BLAS reference order per column j:
+ * t1 = alpha*conj(y(j)), t2 = conj(alpha*x(j)), A(i,j) := (A(i,j) +
+ * x(i)*t1) + y(i)*t2.  The other triangle is neither read nor written.
+ * Return codes: -1 uplo, -2 n < 0, -4 x NULL, -5 incx == 0, -6 y NULL,
+ * -7 incy == 0, -8 A NULL, -9 lda < max(1,n).  n == 0 or alpha == 0: no
+ * change. */
+int oracle_ssyr2(char uplo, int n, float alpha, const float *x, int incx,
+                 const float *y, int incy, float *A, int lda);
+int oracle_dsyr2(char uplo, int n, double alpha, const double *x, int incx,
+                 const double *y, int incy, double *A, int lda);
+int oracle_cher2(char uplo, int n, ocplx_f alpha, const ocplx_f *x, int incx,
+                 const ocplx_f *y, int incy, ocplx_f *A, int lda);
+int oracle_zher2(char uplo, int n, ocplx_d alpha, const ocplx_d *x, int incx,
+                 const ocplx_d *y, int incy, ocplx_d *A, int lda);
+int oracle_wsyr2(char uplo, int n, odd alpha, const odd *x, int incx,
+                 const odd *y, int incy, odd *A, int lda);
+
 /* The double-double primitives, exported so that the tests can pin them
  * one by one against exact rational arithmetic. */
 odd oracle_dd_add(odd a, odd b);

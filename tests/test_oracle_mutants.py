@@ -9,6 +9,7 @@ import pytest
 
 import oracle
 from tests import test_oracle_gemv as G
+from tests import test_oracle_syr2 as R2
 from tests import test_oracle_pins as P
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "xsymv_oracle.c")
@@ -38,7 +39,7 @@ MUTANTS = [
      "*yi = P##_is_zero(beta) ? P##_zero() : P##_mul(beta, *yi);",
      "*yi = P##_mul(beta, *yi);", None),
     ("Hermitian diagonal keeps the imaginary word (single)",
-     "r.im = 0.0f;", "r.im = p->im;", None),
+     "r.im = 0.0f;", "r.im = p->im;", 1),
     ("Hermitian diagonal keeps the imaginary word (double)",
      "r.im = 0.0;\n    return r;\n}\nstatic int z_is_zero",
      "r.im = p->im;\n    return r;\n}\nstatic int z_is_zero", None),
@@ -73,6 +74,20 @@ MUTANTS = [
      "res = P##_add(res, (P##_gemv_dot(", 1),
     ("gemv: inner loop one short",
      "for (k = 0; k < kl; ++k) {", "for (k = 0; k < kl - 1; ++k) {", None),
+    ("syr2: t2 built from y",
+     "T t2 = HERM ? P##_conj(P##_mul(alpha, xj)) : P##_mul(alpha, xj);",
+     "T t2 = HERM ? P##_conj(P##_mul(alpha, yj)) : P##_mul(alpha, yj);", None),
+    ("her2: t1 without conjugate",
+     "T t1 = P##_mul(alpha, HERM ? P##_conj(yj) : yj);",
+     "T t1 = P##_mul(alpha, yj);", None),
+    ("her2: diagonal keeps its imaginary part",
+     "r.re = a.re + s.re;\n    r.im = 0.0f;", "r.re = a.re + s.re;\n    r.im = a.im;", None),
+    ("syr2: lower update also writes the diagonal's upper neighbour",
+     "int lo = upper ? 0 : j, hi = upper ? j + 1 : n;",
+     "int lo = upper ? 0 : (j > 0 ? j - 1 : 0), hi = upper ? j + 1 : n;", None),
+    ("syr2: upper update skips the diagonal",
+     "int lo = upper ? 0 : j, hi = upper ? j + 1 : n;",
+     "int lo = upper ? 0 : j, hi = upper ? j : n;", None),
     ("gemv: x walked with y's increment",
      "sum = P##_add(sum, P##_mul(a, x[vpos(lenx, incx, k)]));",
      "sum = P##_add(sum, P##_mul(a, x[vpos(lenx, 1, k)]));", None),
@@ -97,6 +112,11 @@ BATTERY = [
     (G.test_gemv_beta_zero_ignores_nan_y, [dict(prec=pr, trans=t)
                                            for pr in G.PRECS for t in "NT"]),
     (G.test_gemv_increments, [dict(prec=pr, trans="N", incx=2, incy=-3) for pr in G.PRECS]),
+    (R2.test_syr2_exact_bruteforce, [dict(prec=pr, uplo=u, n=6, pad=2)
+                                     for pr in R2.PRECS for u in "LU"]),
+    (R2.test_syr2_other_triangle_and_padding_untouched, [dict(prec=pr, uplo=u)
+                                                         for pr in R2.PRECS for u in "LU"]),
+    (R2.test_her2_diagonal_real, [dict(prec=pr, uplo=u) for pr in "cz" for u in "LU"]),
 ]
 
 
