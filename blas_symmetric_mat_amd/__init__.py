@@ -25,7 +25,9 @@ __all__ = ["xsymv_s", "xsymv_d", "xhemv_c", "xhemv_z", "xsymv_w", "XsymvError",
            "clear_config", "strip_plan", "config_workgroups", "set_workspace", "read_bandwidth",
            "xgemv_s", "xgemv_d", "xgemv_c", "xgemv_z", "xgemv_w", "gemv_num_configs",
            "gemv_config_info", "gemv_select_config", "gemv_current_config",
-           "gemv_workspace_bytes", "gemv_plan"]
+           "gemv_workspace_bytes", "gemv_plan", "xsyr2_s", "xsyr2_d", "xher2_c", "xher2_z",
+           "xsyr2_w", "syr2_num_configs", "syr2_config_info", "syr2_select_config",
+           "syr2_current_config"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libxsymv.so")
 PREC_CODE = {"s": 0, "d": 1, "c": 2, "z": 3, "w": 4}
@@ -58,6 +60,7 @@ class _DD(ctypes.Structure):
 _SCALAR = {"s": ctypes.c_float, "d": ctypes.c_double, "c": _C64, "z": _C128, "w": _DD}
 _ENTRY = {"s": "xsymv_s", "d": "xsymv_d", "c": "xhemv_c", "z": "xhemv_z", "w": "xsymv_w"}
 _GENTRY = {"s": "xgemv_s", "d": "xgemv_d", "c": "xgemv_c", "z": "xgemv_z", "w": "xgemv_w"}
+_RENTRY = {"s": "xsyr2_s", "d": "xsyr2_d", "c": "xher2_c", "z": "xher2_z", "w": "xsyr2_w"}
 
 _lib = None
 _lock = threading.Lock()
@@ -84,6 +87,10 @@ def library():
                 st = _SCALAR[p]
                 f.restype = ci
                 f.argtypes = [cc, ci, ci, st, vp, ci, vp, ci, st, vp, ci, vp]
+            for p, nm in _RENTRY.items():
+                f = getattr(lib, nm)
+                f.restype = ci
+                f.argtypes = [cc, ci, _SCALAR[p], vp, ci, vp, ci, vp, ci, vp]
             lib.xsymv_workspace_bytes.restype = ctypes.c_size_t
             lib.xsymv_workspace_bytes.argtypes = [ci, cc, ci]
             lib.xsymv_release.restype = ci
@@ -115,6 +122,14 @@ def library():
             lib.xsymv_config_workgroups.argtypes = [ci, ci, cc]
             lib.xsymv_strip_plan.restype = ci
             lib.xsymv_strip_plan.argtypes = [cc, ci, ci, ci, ci, ip, ci, ip, ip, ci]
+            lib.xsyr2_num_configs.restype = ci
+            lib.xsyr2_num_configs.argtypes = [ci]
+            lib.xsyr2_config_info.restype = ci
+            lib.xsyr2_config_info.argtypes = [ci, ci, ip, ip, ip, ip, ip, ip]
+            lib.xsyr2_select_config.restype = ci
+            lib.xsyr2_select_config.argtypes = [ci, ci]
+            lib.xsyr2_current_config.restype = ci
+            lib.xsyr2_current_config.argtypes = [ci]
             lib.xgemv_num_configs.restype = ci
             lib.xgemv_num_configs.argtypes = [ci]
             lib.xgemv_config_info.restype = ci
@@ -229,6 +244,62 @@ def xgemv_z(trans, m, n, alpha, A, lda, x, incx, beta, y, incy, stream=None):
 def xgemv_w(trans, m, n, alpha, A, lda, x, incx, beta, y, incy, stream=None):
     """WGEMV: double-double (hi, lo) pairs; alpha, beta are (hi, lo) tuples."""
     _gcall("w", trans, m, n, alpha, A, lda, x, incx, beta, y, incy, stream)
+
+
+def _rcall(prec, uplo, n, alpha, x, incx, y, incy, A, lda, stream):
+    f = getattr(library(), _RENTRY[prec])
+    u = uplo.encode()[:1] if isinstance(uplo, str) else uplo
+    rc = f(u, n, _scalar(prec, alpha), _addr(x), incx, _addr(y), incy, _addr(A), lda,
+           _stream(stream))
+    if rc != 0:
+        raise XsymvError(_RENTRY[prec], rc)
+
+
+def xsyr2_s(uplo, n, alpha, x, incx, y, incy, A, lda, stream=None):
+    """SSYR2: A := alpha*x*y^T + alpha*y*x^T + A on the stored triangle, float32."""
+    _rcall("s", uplo, n, alpha, x, incx, y, incy, A, lda, stream)
+
+
+def xsyr2_d(uplo, n, alpha, x, incx, y, incy, A, lda, stream=None):
+    """DSYR2: float64."""
+    _rcall("d", uplo, n, alpha, x, incx, y, incy, A, lda, stream)
+
+
+def xher2_c(uplo, n, alpha, x, incx, y, incy, A, lda, stream=None):
+    """CHER2: A := alpha*x*y^H + conj(alpha)*y*x^H + A, complex64."""
+    _rcall("c", uplo, n, alpha, x, incx, y, incy, A, lda, stream)
+
+
+def xher2_z(uplo, n, alpha, x, incx, y, incy, A, lda, stream=None):
+    """ZHER2: complex128."""
+    _rcall("z", uplo, n, alpha, x, incx, y, incy, A, lda, stream)
+
+
+def xsyr2_w(uplo, n, alpha, x, incx, y, incy, A, lda, stream=None):
+    """WSYR2: double-double; alpha is a (hi, lo) tuple."""
+    _rcall("w", uplo, n, alpha, x, incx, y, incy, A, lda, stream)
+
+
+def syr2_num_configs(prec: str) -> int:
+    return library().xsyr2_num_configs(PREC_CODE[prec])
+
+
+def syr2_config_info(prec: str, idx: int) -> dict:
+    vals = [ctypes.c_int() for _ in range(6)]
+    if library().xsyr2_config_info(PREC_CODE[prec], idx, *[ctypes.byref(v) for v in vals]) != 0:
+        raise IndexError(idx)
+    w, sw, g, nt, sp, r = (v.value for v in vals)
+    return {"waves": w, "stripes_per_wave": sw, "cols_per_group": g, "nontemporal": nt,
+            "split": sp, "rows_per_strip": r}
+
+
+def syr2_select_config(prec: str, idx: int) -> None:
+    if library().xsyr2_select_config(PREC_CODE[prec], idx) != 0:
+        raise ValueError("bad syr2 configuration selection")
+
+
+def syr2_current_config(prec: str) -> int:
+    return library().xsyr2_current_config(PREC_CODE[prec])
 
 
 def gemv_num_configs(prec: str) -> int:

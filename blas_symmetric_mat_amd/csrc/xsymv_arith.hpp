@@ -316,4 +316,54 @@ template <> struct Elem<ddreal> {
     __device__ static bool is_one(ddreal a) { return a.hi == 1.0 && a.lo == 0.0; }
 };
 
+// ---------------------------------------------------- buffer stores, conj
+// One element at byte offset `off` of a raw buffer (4, 8 or 16 bytes);
+// offsets at or past the buffer's byte count load zero / store nothing.
+template <class T>
+__device__ __forceinline__ T bload1(__amdgpu_buffer_rsrc_t r, int off)
+{
+    if constexpr (sizeof(T) == 4)
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+    else if constexpr (sizeof(T) == 8)
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+    else
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+template <class T, bool NT>
+__device__ __forceinline__ void bstore1(__amdgpu_buffer_rsrc_t r, int off, T v)
+{
+    typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+    typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+    if constexpr (sizeof(T) == 4)
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, v), r, off, 0,
+                                              NT ? 2 : 0);
+    else if constexpr (sizeof(T) == 8)
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, v), r, off, 0, NT ? 2 : 0);
+    else
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), r, off, 0, NT ? 2 : 0);
+}
+
+// 16 bytes (VEC consecutive elements) stored at byte offset `off`; dwords at
+// or past the buffer's byte count are dropped.
+template <class T, bool NT>
+__device__ __forceinline__ void bstore16(__amdgpu_buffer_rsrc_t r, int off,
+                                         const T (&o)[Elem<T>::VEC])
+{
+    typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+    struct Pack {
+        T v[Elem<T>::VEC];
+    } pk;
+    static_assert(sizeof(Pack) == 16, "16-byte vector");
+#pragma unroll
+    for (int k = 0; k < Elem<T>::VEC; ++k) pk.v[k] = o[k];
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, pk), r, off, 0, NT ? 2 : 0);
+}
+
+__device__ __forceinline__ float elem_conj(float a) { return a; }
+__device__ __forceinline__ double elem_conj(double a) { return a; }
+__device__ __forceinline__ ddreal elem_conj(ddreal a) { return a; }
+__device__ __forceinline__ cf32 elem_conj(cf32 a) { return {a.re, -a.im}; }
+__device__ __forceinline__ cf64 elem_conj(cf64 a) { return {a.re, -a.im}; }
+
 }  // namespace xsymv

@@ -325,9 +325,30 @@ int check_gemv_args(char trans, int m, int n, const void* A, int lda, const void
 
 namespace {
 std::atomic<int> g_gemv_idx[5];
+std::atomic<int> g_syr2_idx[5];
 }
 
 int gemv_selected(int prec) { return g_gemv_idx[prec].load(); }
+int syr2_selected(int prec) { return g_syr2_idx[prec].load(); }
+
+int check_syr2_args(char uplo, int n, const void* x, int incx, const void* y, int incy,
+                    const void* A, int lda, bool* upper)
+{
+    if (uplo == 'U' || uplo == 'u')
+        *upper = true;
+    else if (uplo == 'L' || uplo == 'l')
+        *upper = false;
+    else
+        return -1;
+    if (n < 0) return -2;
+    if (n > 0 && x == nullptr) return -4;
+    if (incx == 0) return -5;
+    if (n > 0 && y == nullptr) return -6;
+    if (incy == 0) return -7;
+    if (n > 0 && A == nullptr) return -8;
+    if (lda < std::max(1, n)) return -9;
+    return 0;
+}
 
 int get_strip_plan(DeviceState* ds, int dev, bool upper, int n, int R, int G, int split,
                    hipStream_t stream, const StripPlan** out)
@@ -1046,6 +1067,59 @@ int xgemv_plan(int m, int n, int R, int G, int* blocks4, int max_blocks, int* se
     }
     std::copy(segb.begin(), segb.end(), seg_base);
     return (int)blocks.size();
+}
+
+int xsyr2_num_configs(int prec)
+{
+    switch (prec) {
+    case XSYMV_S: return (int)syr2_kernel_sets<float>().size();
+    case XSYMV_D: return (int)syr2_kernel_sets<double>().size();
+    case XSYMV_C: return (int)syr2_kernel_sets<cf32>().size();
+    case XSYMV_Z: return (int)syr2_kernel_sets<cf64>().size();
+    case XSYMV_W: return (int)syr2_kernel_sets<ddreal>().size();
+    default: return -1;
+    }
+}
+
+int xsyr2_config_info(int prec, int idx, int* waves, int* stripes_per_wave, int* cols_per_group,
+                      int* nontemporal, int* split, int* rows_per_strip)
+{
+    if (idx < 0 || idx >= xsyr2_num_configs(prec)) return -1;
+    int W = 0, SW = 0, G = 0, NT = 0, SP = 0, R = 0;
+    switch (prec) {
+#define XSYMV_K(T)                                                                       \
+    {                                                                                    \
+        const auto& k = syr2_kernel_sets<T>()[idx];                                      \
+        W = k.W; SW = k.SW; G = k.G; NT = k.NT; SP = k.split; R = k.R();                 \
+        break;                                                                           \
+    }
+    case XSYMV_S: XSYMV_K(float)
+    case XSYMV_D: XSYMV_K(double)
+    case XSYMV_C: XSYMV_K(cf32)
+    case XSYMV_Z: XSYMV_K(cf64)
+    default: XSYMV_K(ddreal)
+#undef XSYMV_K
+    }
+    if (waves) *waves = W;
+    if (stripes_per_wave) *stripes_per_wave = SW;
+    if (cols_per_group) *cols_per_group = G;
+    if (nontemporal) *nontemporal = NT;
+    if (split) *split = SP;
+    if (rows_per_strip) *rows_per_strip = R;
+    return 0;
+}
+
+int xsyr2_select_config(int prec, int idx)
+{
+    if (prec < 0 || prec > 4 || idx < -1 || idx >= xsyr2_num_configs(prec)) return -1;
+    g_syr2_idx[prec].store(idx < 0 ? 0 : idx);
+    return 0;
+}
+
+int xsyr2_current_config(int prec)
+{
+    if (prec < 0 || prec > 4) return -1;
+    return syr2_selected(prec);
 }
 
 const char* xsymv_version(void) { return "xsymv-gfx950 0.1"; }

@@ -25,6 +25,7 @@
 #include "xsymv_kernels.hpp"
 #include "xsymv_strip.hpp"
 #include "xgemv_strip.hpp"
+#include "xsyr2_strip.hpp"
 
 namespace xsymv {
 
@@ -499,6 +500,91 @@ size_t gemv_ws_bytes(char trans, int m, int n)
     int NS = 0;
     build_gemv_plan_host(m, n, ks.R(), G, blocks, segb, NS);
     return gemv_workspace_bytes<T>(tr, segb[NS], ks.R(), NS, n, tr == 0 ? n : m);
+}
+
+// ------------------------------------------------------------ xSYR2 / xHER2
+template <class T>
+struct Syr2KernelSet {
+    int W, SW, G, NT, split;
+    void (*k[2])(Syr2Args<T>);  // lower, upper
+    int R() const { return W * SW * 64 * Elem<T>::VEC; }
+};
+
+template <class T, int W, int SW, int G, bool NT, int SPLIT>
+Syr2KernelSet<T> make_syr2()
+{
+    constexpr bool herm = std::is_same<T, cf32>::value || std::is_same<T, cf64>::value;
+    return Syr2KernelSet<T>{W, SW, G, NT ? 1 : 0, SPLIT,
+                            {&syr2_strip<T, false, herm, W, SW, G, NT>,
+                             &syr2_strip<T, true, herm, W, SW, G, NT>}};
+}
+
+template <class T> const std::vector<Syr2KernelSet<T>>& syr2_kernel_sets();
+int syr2_selected(int prec);
+int check_syr2_args(char uplo, int n, const void* x, int incx, const void* y, int incy,
+                    const void* A, int lda, bool* upper);
+
+template <class T>
+int syr2_run(char uplo, int n, T alpha, const T* x, int incx, const T* y, int incy, T* A,
+             int lda, hipStream_t stream, int forced_idx)
+{
+    bool upper = false;
+    int rc = check_syr2_args(uplo, n, x, incx, y, incy, A, lda, &upper);
+    if (rc) return rc;
+    if (n == 0 || host_is_zero(alpha)) return 0;
+    const auto& ks = syr2_kernel_sets<T>()[forced_idx >= 0 ? forced_idx
+                                                              : syr2_selected(prec_code<T>())];
+    const int R = ks.R();
+    const int threads = 64 * ks.W;
+    auto kern = ks.k[upper ? 1 : 0];
+    int dev = 0;
+    XSYMV_HIP(hipGetDevice(&dev));
+    DeviceState* ds = device_state(dev);
+    std::lock_guard<std::mutex> lk(device_mutex(ds));
+    int G = 0;
+    rc = resident_blocks((const void*)kern, threads, &G);
+    if (rc) return rc;
+    const StripPlan* plan = nullptr;
+    rc = get_strip_plan(ds, dev, upper, n, R, G, ks.split, stream, &plan);
+    if (rc) return rc;
+    const T* xin = x;
+    const T* yin = y;
+    if (incx != 1 || incy != 1) {
+        void* ws = nullptr;
+        rc = get_workspace(ds, stream, 2 * align_up((size_t)n * sizeof(T)), &ws);
+        if (rc) return rc;
+        T* xg = static_cast<T*>(ws);
+        T* yg = reinterpret_cast<T*>(static_cast<char*>(ws) + align_up((size_t)n * sizeof(T)));
+        if (incx != 1) {
+            const long long kx = incx > 0 ? 0 : (long long)(1 - n) * incx;
+            symv_gather<T><<<blocks_for(n, 256), 256, 0, stream>>>(x, incx, kx, n, xg);
+            XSYMV_HIP(hipGetLastError());
+            xin = xg;
+        }
+        if (incy != 1) {
+            const long long ky = incy > 0 ? 0 : (long long)(1 - n) * incy;
+            symv_gather<T><<<blocks_for(n, 256), 256, 0, stream>>>(y, incy, ky, n, yg);
+            XSYMV_HIP(hipGetLastError());
+            yin = yg;
+        }
+    }
+    TimedCall tc{};
+    const bool timing = timing_enabled();
+    if (timing) {
+        XSYMV_HIP(hipEventCreate(&tc.e0));
+        XSYMV_HIP(hipEventCreate(&tc.e1));
+        XSYMV_HIP(hipEventCreate(&tc.e2));
+        XSYMV_HIP(hipEventRecord(tc.e0, stream));
+    }
+    Syr2Args<T> sa{A, xin, yin, plan->d_blocks, plan->d_strip_base, (long long)lda, alpha, n};
+    kern<<<plan->G, threads, 0, stream>>>(sa);
+    XSYMV_HIP(hipGetLastError());
+    if (timing) {
+        XSYMV_HIP(hipEventRecord(tc.e1, stream));
+        XSYMV_HIP(hipEventRecord(tc.e2, stream));  // no merge step
+        timing_push(tc);
+    }
+    return 0;
 }
 
 // ---------------------------------------------------------------- autotuner

@@ -45,6 +45,18 @@ template <> const std::vector<GemvKernelSet<cf32>>& gemv_kernel_sets<cf32>()
     };
     return v;
 }
+
+// xSYR2 / xHER2 configurations (index 0 is the default; xsyr2_select_config
+// chooses another)
+template <> const std::vector<Syr2KernelSet<cf32>>& syr2_kernel_sets<cf32>()
+{
+    static const std::vector<Syr2KernelSet<cf32>> v = {
+        make_syr2<cf32, 16, 1, 4, true, 1>(),              // R 2048, 16 KB runs, G 4
+        make_syr2<cf32, 8, 2, 4, true, 1>(),               // R 2048, 16 KB runs, G 4
+        make_syr2<cf32, 4, 2, 4, true, 0>(),               // R 1024, 8 KB runs, G 4
+    };
+    return v;
+}
 }  // namespace xsymv
 
 extern "C" int xhemv_c(char uplo, int n, xcomplex64 alpha, const xcomplex64* A, int lda,
@@ -66,4 +78,12 @@ extern "C" int xgemv_c(char trans, int m, int n, xcomplex64 alpha, const xcomple
                                reinterpret_cast<const cf32*>(A), lda,
                                reinterpret_cast<const cf32*>(x), incx, cf32{beta.re, beta.im},
                                reinterpret_cast<cf32*>(y), incy, (hipStream_t)stream, -1);
+}
+
+extern "C" int xher2_c(char uplo, int n, xcomplex64 alpha, const xcomplex64* x, int incx, const xcomplex64* y,
+                       int incy, xcomplex64* A, int lda, void* stream)
+{
+    using xsymv::cf32;
+    return xsymv::syr2_run<cf32>(uplo, n, cf32{alpha.re, alpha.im}, (const cf32*)x, incx,
+                               (const cf32*)y, incy, (cf32*)A, lda, (hipStream_t)stream, -1);
 }

@@ -53,6 +53,19 @@ template <> const std::vector<GemvKernelSet<double>>& gemv_kernel_sets<double>()
     };
     return v;
 }
+
+// xSYR2 / xHER2 configurations (index 0 is the default; xsyr2_select_config
+// chooses another)
+template <> const std::vector<Syr2KernelSet<double>>& syr2_kernel_sets<double>()
+{
+    static const std::vector<Syr2KernelSet<double>> v = {
+        make_syr2<double, 16, 1, 4, true, 1>(),            // R 2048, 16 KB runs, G 4
+        make_syr2<double, 16, 2, 4, true, 1>(),            // R 4096, 32 KB runs, G 4
+        make_syr2<double, 8, 2, 4, true, 1>(),             // R 2048, 16 KB runs, G 4
+        make_syr2<double, 4, 2, 4, true, 0>(),             // R 1024, 8 KB runs, G 4
+    };
+    return v;
+}
 }  // namespace xsymv
 
 extern "C" int xsymv_d(char uplo, int n, double alpha, const double* A, int lda,
@@ -68,4 +81,11 @@ extern "C" int xgemv_d(char trans, int m, int n, double alpha, const double* A, 
 {
     return xsymv::gemv_run<double>(trans, m, n, alpha, A, lda, x, incx, beta, y, incy,
                                (hipStream_t)stream, -1);
+}
+
+extern "C" int xsyr2_d(char uplo, int n, double alpha, const double* x, int incx, const double* y,
+                       int incy, double* A, int lda, void* stream)
+{
+    return xsymv::syr2_run<double>(uplo, n, alpha, x, incx, y, incy, A, lda, (hipStream_t)stream,
+                               -1);
 }

@@ -51,6 +51,19 @@ template <> const std::vector<GemvKernelSet<float>>& gemv_kernel_sets<float>()
     };
     return v;
 }
+
+// xSYR2 / xHER2 configurations (index 0 is the default; xsyr2_select_config
+// chooses another)
+template <> const std::vector<Syr2KernelSet<float>>& syr2_kernel_sets<float>()
+{
+    static const std::vector<Syr2KernelSet<float>> v = {
+        make_syr2<float, 16, 1, 4, true, 1>(),             // R 4096, 16 KB runs, G 4
+        make_syr2<float, 8, 2, 4, true, 1>(),              // R 4096, 16 KB runs, G 4
+        make_syr2<float, 16, 1, 8, true, 1>(),             // R 4096, 16 KB runs, G 8
+        make_syr2<float, 4, 2, 4, true, 0>(),              // R 2048, 8 KB runs, G 4
+    };
+    return v;
+}
 }  // namespace xsymv
 
 extern "C" int xsymv_s(char uplo, int n, float alpha, const float* A, int lda, const float* x,
@@ -65,4 +78,11 @@ extern "C" int xgemv_s(char trans, int m, int n, float alpha, const float* A, in
 {
     return xsymv::gemv_run<float>(trans, m, n, alpha, A, lda, x, incx, beta, y, incy,
                                (hipStream_t)stream, -1);
+}
+
+extern "C" int xsyr2_s(char uplo, int n, float alpha, const float* x, int incx, const float* y,
+                       int incy, float* A, int lda, void* stream)
+{
+    return xsymv::syr2_run<float>(uplo, n, alpha, x, incx, y, incy, A, lda, (hipStream_t)stream,
+                               -1);
 }

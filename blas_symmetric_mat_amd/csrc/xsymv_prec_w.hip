@@ -46,6 +46,18 @@ template <> const std::vector<GemvKernelSet<ddreal>>& gemv_kernel_sets<ddreal>()
     };
     return v;
 }
+
+// xSYR2 / xHER2 configurations (index 0 is the default; xsyr2_select_config
+// chooses another)
+template <> const std::vector<Syr2KernelSet<ddreal>>& syr2_kernel_sets<ddreal>()
+{
+    static const std::vector<Syr2KernelSet<ddreal>> v = {
+        make_syr2<ddreal, 16, 1, 4, true, 1>(),            // R 1024, 16 KB runs, G 4
+        make_syr2<ddreal, 8, 2, 4, true, 1>(),             // R 1024, 16 KB runs, G 4
+        make_syr2<ddreal, 4, 2, 4, true, 0>(),             // R 512, 8 KB runs, G 4
+    };
+    return v;
+}
 }  // namespace xsymv
 
 extern "C" int xsymv_w(char uplo, int n, xdd alpha, const xdd* A, int lda, const xdd* x,
@@ -67,4 +79,12 @@ extern "C" int xgemv_w(char trans, int m, int n, xdd alpha, const xdd* A, int ld
                                reinterpret_cast<const ddreal*>(A), lda,
                                reinterpret_cast<const ddreal*>(x), incx, ddreal{beta.hi, beta.lo},
                                reinterpret_cast<ddreal*>(y), incy, (hipStream_t)stream, -1);
+}
+
+extern "C" int xsyr2_w(char uplo, int n, xdd alpha, const xdd* x, int incx, const xdd* y,
+                       int incy, xdd* A, int lda, void* stream)
+{
+    using xsymv::ddreal;
+    return xsymv::syr2_run<ddreal>(uplo, n, ddreal{alpha.hi, alpha.lo}, (const ddreal*)x, incx,
+                               (const ddreal*)y, incy, (ddreal*)A, lda, (hipStream_t)stream, -1);
 }

@@ -45,6 +45,18 @@ template <> const std::vector<GemvKernelSet<cf64>>& gemv_kernel_sets<cf64>()
     };
     return v;
 }
+
+// xSYR2 / xHER2 configurations (index 0 is the default; xsyr2_select_config
+// chooses another)
+template <> const std::vector<Syr2KernelSet<cf64>>& syr2_kernel_sets<cf64>()
+{
+    static const std::vector<Syr2KernelSet<cf64>> v = {
+        make_syr2<cf64, 16, 1, 4, true, 1>(),              // R 1024, 16 KB runs, G 4
+        make_syr2<cf64, 8, 2, 4, true, 1>(),               // R 1024, 16 KB runs, G 4
+        make_syr2<cf64, 4, 2, 4, true, 0>(),               // R 512, 8 KB runs, G 4
+    };
+    return v;
+}
 }  // namespace xsymv
 
 extern "C" int xhemv_z(char uplo, int n, xcomplex128 alpha, const xcomplex128* A, int lda,
@@ -67,4 +79,12 @@ extern "C" int xgemv_z(char trans, int m, int n, xcomplex128 alpha, const xcompl
                                reinterpret_cast<const cf64*>(A), lda,
                                reinterpret_cast<const cf64*>(x), incx, cf64{beta.re, beta.im},
                                reinterpret_cast<cf64*>(y), incy, (hipStream_t)stream, -1);
+}
+
+extern "C" int xher2_z(char uplo, int n, xcomplex128 alpha, const xcomplex128* x, int incx, const xcomplex128* y,
+                       int incy, xcomplex128* A, int lda, void* stream)
+{
+    using xsymv::cf64;
+    return xsymv::syr2_run<cf64>(uplo, n, cf64{alpha.re, alpha.im}, (const cf64*)x, incx,
+                               (const cf64*)y, incy, (cf64*)A, lda, (hipStream_t)stream, -1);
 }

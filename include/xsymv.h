@@ -150,6 +150,49 @@ size_t xgemv_workspace_bytes(int prec, char trans, int m, int n);
 int xgemv_plan(int m, int n, int R, int G, int *blocks4, int max_blocks, int *seg_base,
                int max_strips);
 
+/* Symmetric / Hermitian rank-2 update on the stored triangle (the report's
+ * §5 carries the approach to other Level-2 BLAS; this is SYMV's partner in
+ * reductions to tridiagonal form), BLAS xSYR2 / xHER2:
+ *
+ *   xsyr2_s/d/w:  A := alpha*x*y^T + alpha*y*x^T + A
+ *   xher2_c/z:    A := alpha*x*y^H + conj(alpha)*y*x^H + A  (the diagonal
+ *                 stays real: its imaginary word is written as zero)
+ *
+ * uplo as for the symmetric product; only the stored triangle of A (DEVICE
+ * pointer, column-major, lda >= max(1, n)) is read and written -- the other
+ * triangle and rows n..lda-1 are never touched.  x, y: DEVICE pointers, n
+ * elements with strides incx, incy (!= 0; negative walks backwards).
+ * Every stored element is updated by one lane in the BLAS reference order
+ * (per column j: t1 = alpha*conj(y_j), t2 = conj(alpha*x_j),
+ * a := (a + x_i*t1) + y_i*t2; Hermitian diagonal: Re(a) + Re(x_j*t1 +
+ * y_j*t2)), without fused multiply-adds, so the results do not depend on the
+ * work split.  n == 0 or alpha == 0: nothing is done.  Asynchronous on
+ * `stream`; a workspace (2n elements) is used only for non-unit strides.
+ * Return codes (BLAS xerbla positions): -1 uplo, -2 n < 0, -4 x NULL,
+ * -5 incx == 0, -6 y NULL, -7 incy == 0, -8 A NULL, -9 lda < max(1, n);
+ * 1000 + hipError_t; 2000 installed workspace too small. */
+int xsyr2_s(char uplo, int n, float alpha, const float *x, int incx, const float *y,
+            int incy, float *A, int lda, void *stream);
+int xsyr2_d(char uplo, int n, double alpha, const double *x, int incx, const double *y,
+            int incy, double *A, int lda, void *stream);
+int xher2_c(char uplo, int n, xcomplex64 alpha, const xcomplex64 *x, int incx,
+            const xcomplex64 *y, int incy, xcomplex64 *A, int lda, void *stream);
+int xher2_z(char uplo, int n, xcomplex128 alpha, const xcomplex128 *x, int incx,
+            const xcomplex128 *y, int incy, xcomplex128 *A, int lda, void *stream);
+int xsyr2_w(char uplo, int n, xdd alpha, const xdd *x, int incx, const xdd *y, int incy,
+            xdd *A, int lda, void *stream);
+
+/* Rank-2 update configurations (entry 0 the default): waves per workgroup,
+ * stripes per wave, columns per group, non-temporal access (0/1), work split
+ * (0: strip height per column, 1: stored rows plus strip height) and rows per
+ * strip.  Same conventions as the xGEMV configuration calls. */
+int xsyr2_num_configs(int prec);
+int xsyr2_config_info(int prec, int idx, int *waves, int *stripes_per_wave,
+                      int *cols_per_group, int *nontemporal, int *split,
+                      int *rows_per_strip);
+int xsyr2_select_config(int prec, int idx);
+int xsyr2_current_config(int prec);
+
 /* Bytes of device workspace one call of precision `prec` and order n uses
  * with the configuration selected for it now, on the current device (0 for
  * n == 0; -1 cast to size_t for a bad precision code, or when the device

@@ -110,3 +110,18 @@ def assert_close_gemv(p, got, ref, rows=None, label=""):
     bad = np.nonzero(~(d <= tol))[0]
     assert bad.size == 0, (f"{label}: {bad.size} outputs beyond the bound, worst ratio "
                            f"{np.max(d / np.maximum(tol, 1e-300)):.3g} at {bad[0]}")
+
+
+RENTRY = {"s": "xsyr2_s", "d": "xsyr2_d", "c": "xher2_c", "z": "xher2_z", "w": "xsyr2_w"}
+
+
+def run_syr2(p):
+    """Upload A, x, y of a Syr2Problem, update on the device, return A."""
+    import blas_symmetric_mat_amd as X
+    torch = torch_dev()
+    A = to_device(p.A)
+    x = to_device(p.x)
+    y = to_device(p.y)
+    getattr(X, RENTRY[p.prec])(p.uplo, p.n, p.alpha, x, p.incx, y, p.incy, A, p.lda)
+    torch.cuda.synchronize()
+    return A.cpu().numpy()

@@ -16,14 +16,15 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def declared_functions():
     text = open(os.path.join(ROOT, "include", "xsymv.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(x(?:symv|hemv|gemv)_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(x(?:symv|hemv|gemv|syr2|her2)_\w+)\s*\(", text)))
 
 
 def test_exports_every_declared_function():
     lib = ctypes.CDLL(X.LIB_PATH)
     names = declared_functions()
     assert {"xsymv_s", "xsymv_d", "xhemv_c", "xhemv_z", "xsymv_w", "xgemv_s", "xgemv_d",
-            "xgemv_c", "xgemv_z", "xgemv_w", "xsymv_set_workspace"} <= set(names)
+            "xgemv_c", "xgemv_z", "xgemv_w", "xsymv_set_workspace", "xsyr2_s", "xsyr2_d",
+            "xher2_c", "xher2_z", "xsyr2_w"} <= set(names)
     for nm in names:
         assert hasattr(lib, nm), nm
 
@@ -260,3 +261,37 @@ def test_gemv_plan_covers_every_column_once(m, n, R, G):
     assert segb[NS] == slot_expect
     for st in range(NS):
         assert slots_of_strip[st] == list(range(segb[st], segb[st + 1]))
+
+
+@pytest.mark.parametrize("prec", ["s", "d", "c", "z", "w"])
+def test_syr2_argument_errors_before_device_work(prec):
+    f = getattr(X, {"s": "xsyr2_s", "d": "xsyr2_d", "c": "xher2_c", "z": "xher2_z",
+                    "w": "xsyr2_w"}[prec])
+    one = (1.0, 0.0) if prec == "w" else 1.0
+    zero = (0.0, 0.0) if prec == "w" else 0.0
+    # (uplo, n, alpha, x, incx, y, incy, A, lda); pointers are never touched
+    cases = [(("Q", 4, one, 8, 1, 8, 1, 8, 4), -1), (("L", -1, one, 8, 1, 8, 1, 8, 4), -2),
+             (("U", 4, one, None, 1, 8, 1, 8, 4), -4), (("u", 4, one, 8, 0, 8, 1, 8, 4), -5),
+             (("l", 4, one, 8, 1, None, 1, 8, 4), -6), (("L", 4, one, 8, 1, 8, 0, 8, 4), -7),
+             (("L", 4, one, 8, 1, 8, 1, None, 4), -8), (("L", 4, one, 8, 1, 8, 1, 8, 3), -9)]
+    for args, code in cases:
+        with pytest.raises(X.XsymvError) as e:
+            f(*args, stream=0)
+        assert e.value.code == code, (args, e.value.code)
+    f("L", 0, one, None, 1, None, 1, None, 1, stream=0)   # n == 0
+    f("U", 4, zero, 8, 1, 8, 1, 8, 4, stream=0)           # alpha == 0
+
+
+def test_syr2_config_tables():
+    for p in "sdczw":
+        k = X.syr2_num_configs(p)
+        assert k >= 1
+        for i in range(k):
+            ci = X.syr2_config_info(p, i)
+            assert ci["split"] in (0, 1)
+        assert X.syr2_current_config(p) == 0
+    X.syr2_select_config("s", 1)
+    assert X.syr2_current_config("s") == 1
+    X.syr2_select_config("s", -1)
+    with pytest.raises(ValueError):
+        X.syr2_select_config("s", 99)
