@@ -17,6 +17,9 @@ Printed as one JSON line, with:
                 (xsymv_read_bandwidth), the secondary reference: every rate
                 is also given as % of it (`pct_measured_read_peak`);
   cpu_baseline  the CPU oracle (single thread) on the same problem;
+  ssyr2/dsyr2   the rank-2 update A := alpha*x*y^T + alpha*y*x^T + A on the
+                stored triangle (n = 32768), its bytes the triangle read and
+                written once;
   symv_over_gemv_time  the symmetric call's time over the general one's on
                 the same order (GEMV detail rows: SGEMV 'N' and 'T', DGEMV
                 'N', n = 32768) -- the report's claim that SYMV, reading one
@@ -156,6 +159,45 @@ def measure_gemv_detail(name, p, reps, read_peak=None):
     if read_peak:
         out["pct_measured_read_peak"] = round(100 * call_b / t_call / 1e9 / read_peak, 1)
     del d
+    torch.cuda.empty_cache()
+    return out
+
+
+def measure_syr2_detail(name, p, reps, read_peak=None):
+    """The rank-2 update: the stored triangle read and written once."""
+    from blas_symmetric_mat_amd import roofline as R
+    import numpy as np
+    import torch
+    import blas_symmetric_mat_amd as X
+    log(f"detail: {name}")
+    A = torch.from_numpy(np.ascontiguousarray(p.A)).to("cuda")
+    x = torch.from_numpy(np.ascontiguousarray(p.x)).to("cuda")
+    y = torch.from_numpy(np.ascontiguousarray(p.y)).to("cuda")
+    f = getattr(X, {"s": "xsyr2_s", "d": "xsyr2_d", "c": "xher2_c", "z": "xher2_z",
+                    "w": "xsyr2_w"}[p.prec])
+
+    class _D:
+        def call(self):
+            f(p.uplo, p.n, p.alpha, x, p.incx, y, p.incy, A, p.lda)
+
+    d = _D()
+    for _ in range(2):
+        d.call()
+    rec = time_kernels(d, reps)
+    tot = sorted(r[0] + r[1] for r in rec)
+    t_call = tot[len(tot) // 2] * 1e-3
+    b = R.syr2_call_bytes(p.prec, p.n)
+    ci = X.syr2_config_info(p.prec, X.syr2_current_config(p.prec))
+    out = {"prec": p.prec, "uplo": p.uplo, "n": p.n, "lda": p.lda,
+           "kernel": (f"syr2_strip<{CTYPE[p.prec]}, {'upper' if p.uplo == 'U' else 'lower'}, "
+                      f"W={ci['waves']}, SW={ci['stripes_per_wave']}, G={ci['cols_per_group']}, "
+                      f"{'nt' if ci['nontemporal'] else 'cached'}>"),
+           "ms_per_call_median": round(t_call * 1e3, 4),
+           "ms_per_call_min": round(tot[0], 4),
+           "hbm_gbps_algorithmic": round(b / t_call / 1e9, 1),
+           "pct_peak_hbm": round(100 * b / t_call / 1e9 / R.HBM_PEAK_GBPS, 1),
+           "bytes": "triangle read + written, x and y", "calls": reps}
+    del A
     torch.cuda.empty_cache()
     return out
 
@@ -500,6 +542,10 @@ def main():
                   ("dgemv-N-n32768", lambda: W.gemv_square("d", "N", 32768))]
         for name, make in gcases:
             detail[name] = measure_gemv_detail(name, make(), args.detail_reps, rd_med)
+        for name, make in [
+                ("ssyr2-L-n32768", lambda: W.make_syr2_problem("s", "L", 32768, seed=32768)),
+                ("dsyr2-U-n32768", lambda: W.make_syr2_problem("d", "U", 32768, seed=32768))]:
+            detail[name] = measure_syr2_detail(name, make(), args.detail_reps, rd_med)
         out["detail"] = detail
         # the report's point: SYMV reads half the bytes of GEMV on the same
         # order, so takes about half the time

@@ -57,9 +57,9 @@ template <> const std::vector<GemvKernelSet<float>>& gemv_kernel_sets<float>()
 template <> const std::vector<Syr2KernelSet<float>>& syr2_kernel_sets<float>()
 {
     static const std::vector<Syr2KernelSet<float>> v = {
+        make_syr2<float, 16, 1, 8, true, 1>(),             // R 4096, 16 KB runs, G 8
         make_syr2<float, 16, 1, 4, true, 1>(),             // R 4096, 16 KB runs, G 4
         make_syr2<float, 8, 2, 4, true, 1>(),              // R 4096, 16 KB runs, G 4
-        make_syr2<float, 16, 1, 8, true, 1>(),             // R 4096, 16 KB runs, G 8
         make_syr2<float, 4, 2, 4, true, 0>(),              // R 2048, 8 KB runs, G 4
     };
     return v;

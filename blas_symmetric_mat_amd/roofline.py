@@ -69,3 +69,10 @@ def gemv_kernel_bytes(prec: str, m: int, n: int, trans: str) -> int:
     """Algorithmic bytes of the GEMV streaming kernel: A and x."""
     lenx = n if trans in ("N", "n") else m
     return ELEM_BYTES[prec] * (m * n + lenx)
+
+
+# ------------------------------------------------------------ xSYR2 / xHER2
+def syr2_call_bytes(prec: str, n: int) -> int:
+    """Algorithmic bytes of one rank-2 update: the stored triangle read and
+    written once, x and y read."""
+    return ELEM_BYTES[prec] * (2 * stored_elements(n) + 2 * n)

@@ -102,3 +102,18 @@ def test_gemv_square(prec, trans, n):
     ref = oracle.gemv_rows_problem(p, rows)
     G.assert_close_gemv(p, outs[0][rows], ref, rows=rows, label=p.name)
     G.log(f"  ok ({len(rows)} sampled outputs)")
+
+
+# ------------------------------------------------------- rank-2 update
+
+@pytest.mark.parametrize("prec,uplo,n", [("s", "L", 16384), ("d", "U", 8192),
+                                         ("c", "L", 8192)])
+def test_syr2_full(prec, uplo, n):
+    """The rank-2 update at sizes the oracle finishes in seconds, the whole
+    updated array against the oracle byte for byte, three identical runs."""
+    from tests import test_oracle_syr2 as R2
+    p = R2.problem(prec, uplo, n, 0, seed=n)
+    G.log(f"workload syr2 {prec}{uplo} n={n}")
+    outs = {G.digest(G.run_syr2(p)) for _ in range(3)}
+    assert len(outs) == 1
+    assert outs.pop() == G.digest(oracle.syr2_problem(p))
