@@ -305,6 +305,36 @@ def make_syr2_problem(prec: str, uplo: str, n: int, lda: int | None = None, *,
     return Syr2Problem(prec, uplo, n, p.lda, p.alpha, p.x, p.y, p.A, name=name)
 
 
+@dataclasses.dataclass
+class TrmvProblem:
+    """One triangular product's arguments (host arrays): A holds the stored
+    triangle (diagonal included; the other triangle and padding hold `fill`)."""
+    prec: str
+    uplo: str
+    trans: str
+    diag: str
+    n: int
+    lda: int
+    A: np.ndarray
+    x: np.ndarray
+    incx: int = 1
+    name: str = ""
+
+
+def make_trmv_problem(prec: str, uplo: str, trans: str, diag: str, n: int,
+                      lda: int | None = None, *, seed: int = 0, fill: float = np.nan,
+                      integer: tuple[int, int] | None = None,
+                      name: str = "") -> TrmvProblem:
+    """Draw a triangular product: the stored triangle column by column (as
+    make_problem does), then x (the same draws as a symmetric problem's)."""
+    if integer is None:
+        p = make_problem(prec, uplo, n, lda, seed=seed, fill=fill)
+    else:
+        p = make_integer_problem(prec, uplo, n, lda, seed=seed, lo=integer[0], hi=integer[1],
+                                 fill=fill)
+    return TrmvProblem(prec, uplo, trans, diag, n, p.lda, p.A, p.x, name=name)
+
+
 # --------------------------------------------------------------------------
 # The benchmark workloads, named by what they are.
 # --------------------------------------------------------------------------

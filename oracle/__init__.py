@@ -51,6 +51,7 @@ _SCALAR = {"s": ctypes.c_float, "d": ctypes.c_double, "c": _CF, "z": _CD, "w": _
 _NAME = {"s": "ssymv", "d": "dsymv", "c": "chemv", "z": "zhemv", "w": "wsymv"}
 _GNAME = {"s": "sgemv", "d": "dgemv", "c": "cgemv", "z": "zgemv", "w": "wgemv"}
 _RNAME = {"s": "ssyr2", "d": "dsyr2", "c": "cher2", "z": "zher2", "w": "wsyr2"}
+_TNAME = {"s": "strmv", "d": "dtrmv", "c": "ctrmv", "z": "ztrmv", "w": "wtrmv"}
 _NP = {"s": np.float32, "d": np.float64, "c": np.complex64, "z": np.complex128,
        "w": np.float64}
 
@@ -79,6 +80,10 @@ def _declare(lib):
         f = getattr(lib, "oracle_" + nm)
         f.restype = ci
         f.argtypes = [ctypes.c_char, ci, _SCALAR[p], vp, ci, vp, ci, vp, ci]
+    for p, nm in _TNAME.items():
+        f = getattr(lib, "oracle_" + nm)
+        f.restype = ci
+        f.argtypes = [ctypes.c_char, ctypes.c_char, ctypes.c_char, ci, vp, ci, vp, ci]
     for nm in ("oracle_dd_add", "oracle_dd_mul"):
         f = getattr(lib, nm)
         f.restype = _DD
@@ -218,6 +223,21 @@ class OracleLib:
             raise ValueError(f"oracle syr2 call failed with status {rc}")
         return A
 
+    def trmv(self, prec: str, uplo: str, trans: str, diag: str, n: int, A, lda: int, x,
+             incx: int) -> int:
+        """x := op(T)*x in place; returns the status code."""
+        _check_dtype(prec, A, x)
+        f = getattr(self._lib, "oracle_" + _TNAME[prec])
+        return f(_uplo(uplo), _uplo(trans), _uplo(diag), n, _ptr(A), lda, _ptr(x), incx)
+
+    def trmv_problem(self, p, x=None):
+        """Run on a ``workloads.TrmvProblem``; returns the new x (a copy)."""
+        x = (p.x if x is None else x).copy()
+        rc = self.trmv(p.prec, p.uplo, p.trans, p.diag, p.n, p.A, p.lda, x, p.incx)
+        if rc != 0:
+            raise ValueError(f"oracle trmv call failed with status {rc}")
+        return x
+
     def dd_add(self, a, b):
         r = self._lib.oracle_dd_add(_DD(*a), _DD(*b))
         return (r.hi, r.lo)
@@ -288,3 +308,11 @@ def syr2(*a, **k):
 
 def syr2_problem(p, A=None):
     return default().syr2_problem(p, A)
+
+
+def trmv(*a, **k):
+    return default().trmv(*a, **k)
+
+
+def trmv_problem(p, x=None):
+    return default().trmv_problem(p, x)

@@ -47,6 +47,13 @@
  * Re(x(j)*t1 + y(j)*t2) with a zero imaginary part.  The other triangle is
  * neither read nor written.
  *
+ * Triangular matrix-vector product (another of the Level-2 BLAS the
+ * report's §5 points to), BLAS xTRMV: x := op(T)*x with T the stored
+ * triangle of A (diagonal from A, or 1 for a unit triangle -- then the
+ * diagonal is not read), op = T, T^T or T^H.  Each output element from the
+ * definition: the sum over the inner index k ascending of op(T)(i,k)*x(k),
+ * in the working precision; all outputs are formed before x is overwritten.
+ *
  * Double-double arithmetic (report §2.2, which takes Bailey's double-double
  * format [14]: a value is the unevaluated sum hi + lo of two doubles):
  *   TwoSum (Knuth) and FastTwoSum (Dekker) give a sum and its exact error;
@@ -504,3 +511,79 @@ DEFINE_SYR2(oracle_dsyr2, double, d, 0, NO_REALPART)
 DEFINE_SYR2(oracle_cher2, ocplx_f, c, 1, c_herm_diag)
 DEFINE_SYR2(oracle_zher2, ocplx_d, z, 1, z_herm_diag)
 DEFINE_SYR2(oracle_wsyr2, odd, w, 0, NO_REALPART)
+
+/* ------------------------------------------------------------- xTRMV */
+
+/* BLAS xTRMV argument checks (xerbla positions: uplo, trans, diag, n, a, lda,
+ * x, incx). */
+static int trmv_check(char uplo, char trans, char diag, int n, const void *A,
+                      int lda, const void *x, int incx, int *upper, int *tr,
+                      int *unit)
+{
+    if (uplo == 'U' || uplo == 'u')
+        *upper = 1;
+    else if (uplo == 'L' || uplo == 'l')
+        *upper = 0;
+    else
+        return -1;
+    if (trans == 'N' || trans == 'n')
+        *tr = 0;
+    else if (trans == 'T' || trans == 't')
+        *tr = 1;
+    else if (trans == 'C' || trans == 'c')
+        *tr = 2;
+    else
+        return -2;
+    if (diag == 'U' || diag == 'u')
+        *unit = 1;
+    else if (diag == 'N' || diag == 'n')
+        *unit = 0;
+    else
+        return -3;
+    if (n < 0) return -4;
+    if (n > 0 && A == NULL) return -5;
+    if (lda < (n > 1 ? n : 1)) return -6;
+    if (n > 0 && x == NULL) return -7;
+    if (incx == 0) return -8;
+    return 0;
+}
+
+#define DEFINE_TRMV(NAME, T, P)                                                 \
+int NAME(char uplo, char trans, char diag, int n, const T *A, int lda, T *x,   \
+         int incx)                                                              \
+{                                                                               \
+    int upper, tr, unit, i, k;                                                  \
+    T *out;                                                                     \
+    int rc = trmv_check(uplo, trans, diag, n, A, lda, x, incx, &upper, &tr,     \
+                        &unit);                                                 \
+    if (rc) return rc;                                                          \
+    if (n == 0) return 0;                                                       \
+    out = (T *)malloc(sizeof(T) * (size_t)n);                                   \
+    if (out == NULL) return -100;                                               \
+    for (i = 0; i < n; ++i) {                                                   \
+        T sum = P##_zero();                                                     \
+        for (k = 0; k < n; ++k) {                                               \
+            /* op(T)(i,k): element (r, c) of the triangle */                    \
+            int r = tr == 0 ? i : k, c = tr == 0 ? k : i;                       \
+            T a;                                                                \
+            if (upper ? r > c : r < c) continue;  /* outside the triangle */    \
+            if (r == c && unit) {                                               \
+                sum = P##_add(sum, x[vpos(n, incx, k)]);                        \
+                continue;                                                       \
+            }                                                                   \
+            a = A[(long long)r + (long long)c * lda];                           \
+            if (tr == 2) a = P##_conj(a);                                       \
+            sum = P##_add(sum, P##_mul(a, x[vpos(n, incx, k)]));                \
+        }                                                                       \
+        out[i] = sum;                                                           \
+    }                                                                           \
+    for (i = 0; i < n; ++i) x[vpos(n, incx, i)] = out[i];                       \
+    free(out);                                                                  \
+    return 0;                                                                   \
+}
+
+DEFINE_TRMV(oracle_strmv, float, s)
+DEFINE_TRMV(oracle_dtrmv, double, d)
+DEFINE_TRMV(oracle_ctrmv, ocplx_f, c)
+DEFINE_TRMV(oracle_ztrmv, ocplx_d, z)
+DEFINE_TRMV(oracle_wtrmv, odd, w)

@@ -125,6 +125,23 @@ int oracle_zher2(char uplo, int n, ocplx_d alpha, const ocplx_d *x, int incx,
 int oracle_wsyr2(char uplo, int n, odd alpha, const odd *x, int incx,
                  const odd *y, int incy, odd *A, int lda);
 
+/* Triangular matrix-vector product, BLAS xTRMV: x := op(T)*x, T the stored
+ * triangle (uplo) of A, diag 'N' (diagonal from A) or 'U' (unit diagonal,
+ * not read), trans 'N', 'T' or 'C'.  Every output from the definition (inner
+ * index ascending), x overwritten after all outputs are formed.  Return
+ * codes: -1 uplo, -2 trans, -3 diag, -4 n < 0, -5 A NULL, -6 lda < max(1,n),
+ * -7 x NULL, -8 incx == 0. */
+int oracle_strmv(char uplo, char trans, char diag, int n, const float *A, int lda,
+                 float *x, int incx);
+int oracle_dtrmv(char uplo, char trans, char diag, int n, const double *A, int lda,
+                 double *x, int incx);
+int oracle_ctrmv(char uplo, char trans, char diag, int n, const ocplx_f *A, int lda,
+                 ocplx_f *x, int incx);
+int oracle_ztrmv(char uplo, char trans, char diag, int n, const ocplx_d *A, int lda,
+                 ocplx_d *x, int incx);
+int oracle_wtrmv(char uplo, char trans, char diag, int n, const odd *A, int lda,
+                 odd *x, int incx);
+
 /* The double-double primitives, exported so that the tests can pin them
  * one by one against exact rational arithmetic. */
 odd oracle_dd_add(odd a, odd b);

@@ -434,3 +434,122 @@ def gemv_integer_expected(p):
         r[:, 0] = out
         return r
     return out.astype(p.y.dtype)
+
+
+# ------------------------------------------------------------------ xTRMV
+
+def _trmv_unit(p) -> bool:
+    return p.diag in ("U", "u")
+
+
+def trmv_op_dense(p) -> np.ndarray:
+    """op(T) as a dense n x n float64/complex128 array: T the stored triangle
+    (zeros elsewhere, ones on the diagonal for a unit triangle; double-double
+    hi + lo rounded to float64)."""
+    n = p.n
+    A = p.A[:, 0].astype(np.float64) + p.A[:, 1] if p.prec == "w" else p.A
+    dt = np.complex128 if p.prec in ("c", "z") else np.float64
+    M = A[: p.lda * n].reshape(n, p.lda).T[:n, :n].astype(dt)  # [i, j]
+    keep = np.triu(np.ones((n, n), dtype=bool)) if is_upper(p.uplo) else \
+        np.tril(np.ones((n, n), dtype=bool))
+    T = np.where(keep, M, 0)
+    if _trmv_unit(p):
+        T[np.arange(n), np.arange(n)] = 1
+    if p.trans in ("N", "n"):
+        return T
+    return np.conj(T.T) if p.trans in ("C", "c") else T.T.copy()
+
+
+def trmv_exact(p):
+    """Exact op(T)*x in logical order (Fractions or (re, im) Fraction pairs)."""
+    cplx = p.prec in ("c", "z")
+    tr = p.trans not in ("N", "n")
+    conj = p.trans in ("C", "c")
+    get = exact_elements(p)
+    x = exact_vector(p, p.x, p.incx)
+    zero = (Fraction(0), Fraction(0)) if cplx else Fraction(0)
+    out = []
+    for o in range(p.n):
+        s = zero
+        for k in range(p.n):
+            r, c = (k, o) if tr else (o, k)
+            if not stored(p.uplo, r, c):
+                continue
+            if r == c and _trmv_unit(p):
+                s = _cadd(s, x[k]) if cplx else s + x[k]
+                continue
+            a = get(r, c)
+            if cplx:
+                if conj:
+                    a = (a[0], -a[1])
+                s = _cadd(s, _cmul(a, x[k]))
+            else:
+                s = s + a * x[k]
+        out.append(s)
+    return out
+
+
+def trmv_exact_errors(p, x_out, exact=None):
+    ex = trmv_exact(p) if exact is None else exact
+    idx = vec_index(p.n, p.incx)
+    errs = np.empty(p.n)
+    for k, i in enumerate(idx):
+        e = ex[k]
+        if p.prec == "w":
+            v = Fraction(float(x_out[i, 0])) + Fraction(float(x_out[i, 1]))
+            errs[k] = abs(float(v - e))
+        elif p.prec in ("c", "z"):
+            errs[k] = abs(complex(float(_frac(x_out[i].real) - e[0]),
+                                  float(_frac(x_out[i].imag) - e[1])))
+        else:
+            errs[k] = abs(float(_frac(x_out[i]) - e))
+    return errs
+
+
+def trmv_tolerance(p, rows=None):
+    """4*n*eps*(|op(T)||x|)_i for all outputs (logical order), or for the
+    outputs ``rows`` only (unit increment, read without forming op(T))."""
+    n = max(p.n, 1)
+    if rows is None:
+        x = _magnitude(p, p.x[vec_index(p.n, p.incx)])
+        t = np.abs(trmv_op_dense(p)) @ x
+    else:
+        assert p.incx == 1
+        rows = np.asarray(rows, dtype=np.int64)
+        x = _magnitude(p, p.x)
+        up = is_upper(p.uplo)
+        tr = p.trans not in ("N", "n")
+        t = np.empty(len(rows))
+        for q, o in enumerate(rows):
+            # stored entries of row o of op(T): column o of T when transposed
+            if tr:
+                ks = np.arange(0, o + 1) if up else np.arange(o, p.n)
+                idx = ks + o * p.lda
+            else:
+                ks = np.arange(o, p.n) if up else np.arange(0, o + 1)
+                idx = o + ks * p.lda
+            mag = _magnitude(p, p.A[idx])
+            if _trmv_unit(p):
+                mag[ks == o] = 1.0
+            t[q] = float(mag @ x[ks])
+    return 4.0 * n * EPS[p.prec] * t
+
+
+def trmv_integer_expected(p):
+    """Exact op(T)*x of an integer-valued TrmvProblem via int64 products, in
+    the element type (logical order)."""
+    M = trmv_op_dense(p)
+    xi = vec_index(p.n, p.incx)
+    if p.prec in ("c", "z"):
+        Mr = np.rint(M.real).astype(np.int64)
+        Mi = np.rint(M.imag).astype(np.int64)
+        xr = np.rint(p.x[xi].real).astype(np.int64)
+        xim = np.rint(p.x[xi].imag).astype(np.int64)
+        s = (Mr @ xr - Mi @ xim).astype(np.complex128) + 1j * (Mr @ xim + Mi @ xr)
+        return s.astype(p.x.dtype)
+    Mi = np.rint(M).astype(np.int64)
+    if p.prec == "w":
+        r = np.zeros((p.n, 2))
+        r[:, 0] = (Mi @ np.rint(p.x[xi, 0]).astype(np.int64)).astype(np.float64)
+        return r
+    return (Mi @ np.rint(p.x[xi]).astype(np.int64)).astype(p.x.dtype)

@@ -10,6 +10,7 @@ import pytest
 import oracle
 from tests import test_oracle_gemv as G
 from tests import test_oracle_syr2 as R2
+from tests import test_oracle_trmv as TM
 from tests import test_oracle_pins as P
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "xsymv_oracle.c")
@@ -88,6 +89,20 @@ MUTANTS = [
     ("syr2: upper update skips the diagonal",
      "int lo = upper ? 0 : j, hi = upper ? j + 1 : n;",
      "int lo = upper ? 0 : j, hi = upper ? j : n;", None),
+    ("trmv: the other triangle",
+     "if (upper ? r > c : r < c) continue;", "if (upper ? r < c : r > c) continue;", None),
+    ("trmv: diagonal skipped",
+     "if (upper ? r > c : r < c) continue;", "if (upper ? r >= c : r <= c) continue;", None),
+    ("trmv: 'N' and 'T' indices swapped",
+     "int r = tr == 0 ? i : k, c = tr == 0 ? k : i;",
+     "int r = tr == 0 ? k : i, c = tr == 0 ? i : k;", None),
+    ("trmv: 'C' without conjugate",
+     "a = A[(long long)r + (long long)c * lda];",
+     "a = A[(long long)r + (long long)c * lda]; tr = tr == 2 ? 1 : tr;", None),
+    ("trmv: unit diagonal read from A",
+     "if (r == c && unit) {", "if (0 && unit) {", None),
+    ("trmv: x overwritten while outputs are formed",
+     "out[i] = sum;", "out[i] = sum; x[vpos(n, incx, i)] = sum;", None),
     ("gemv: x walked with y's increment",
      "sum = P##_add(sum, P##_mul(a, x[vpos(lenx, incx, k)]));",
      "sum = P##_add(sum, P##_mul(a, x[vpos(lenx, 1, k)]));", None),
@@ -117,6 +132,11 @@ BATTERY = [
     (R2.test_syr2_other_triangle_and_padding_untouched, [dict(prec=pr, uplo=u)
                                                          for pr in R2.PRECS for u in "LU"]),
     (R2.test_her2_diagonal_real, [dict(prec=pr, uplo=u) for pr in "cz" for u in "LU"]),
+    (TM.test_trmv_exact_bruteforce, [dict(prec=pr, uplo=u, trans=t, diag=d, n=7, pad=2)
+                                     for pr in TM.PRECS for u in "LU" for t in TM.TRANS
+                                     for d in "NU"]),
+    (TM.test_trmv_unit_diagonal_not_read, [dict(prec=pr, uplo=u, trans=t)
+                                           for pr in TM.PRECS for u in "LU" for t in TM.TRANS]),
 ]
 
 
