@@ -20,6 +20,8 @@ Printed as one JSON line, with:
   ssyr2/dsyr2   the rank-2 update A := alpha*x*y^T + alpha*y*x^T + A on the
                 stored triangle (n = 32768), its bytes the triangle read and
                 written once;
+  s/d/z/wtrmv   the triangular product x := op(T)*x (n = 32768 real, 16384
+                complex and double-double), its bytes the triangle read once;
   symv_over_gemv_time  the symmetric call's time over the general one's on
                 the same order (GEMV detail rows: SGEMV 'N' and 'T', DGEMV
                 'N', n = 32768) -- the report's claim that SYMV, reading one
@@ -197,6 +199,55 @@ def measure_syr2_detail(name, p, reps, read_peak=None):
            "hbm_gbps_algorithmic": round(b / t_call / 1e9, 1),
            "pct_peak_hbm": round(100 * b / t_call / 1e9 / R.HBM_PEAK_GBPS, 1),
            "bytes": "triangle read + written, x and y", "calls": reps}
+    del A
+    torch.cuda.empty_cache()
+    return out
+
+
+def measure_trmv_detail(name, p, reps, read_peak=None):
+    """The triangular product: the stored triangle read once, x read and
+    overwritten (a fresh x per call, so every call does the same work)."""
+    from blas_symmetric_mat_amd import roofline as R
+    import numpy as np
+    import torch
+    import blas_symmetric_mat_amd as X
+    log(f"detail: {name}")
+    A = torch.from_numpy(np.ascontiguousarray(p.A)).to("cuda")
+    x0 = torch.from_numpy(np.ascontiguousarray(p.x)).to("cuda")
+    x = x0.clone()
+    f = getattr(X, "xtrmv_" + p.prec)
+
+    class _D:
+        def call(self):
+            x.copy_(x0)
+            f(p.uplo, p.trans, p.diag, p.n, A, p.lda, x, p.incx)
+
+    d = _D()
+    for _ in range(2):
+        d.call()
+    rec = time_kernels(d, reps)
+    main = sorted(r[0] for r in rec)
+    tot = sorted(r[0] + r[1] for r in rec)
+    t_main = main[len(main) // 2] * 1e-3
+    t_call = tot[len(tot) // 2] * 1e-3
+    unit = p.diag in ("U", "u")
+    b = R.trmv_call_bytes(p.prec, p.n, unit)
+    idx = X.trmv_current_config(p.prec, p.uplo, p.trans)
+    ci = X.trmv_config_info(p.prec, idx)
+    out = {"prec": p.prec, "uplo": p.uplo, "trans": p.trans, "diag": p.diag, "n": p.n,
+           "lda": p.lda,
+           "kernel": (f"trmv_strip<{CTYPE[p.prec]}, {'upper' if p.uplo == 'U' else 'lower'}, "
+                      f"{p.trans}, W={ci['waves']}, SW={ci['stripes_per_wave']}, "
+                      f"G={ci['cols_per_group']}, {'nt' if ci['nontemporal'] else 'cached'}> "
+                      f"(split: {'stored+height' if ci['split'] else 'height'})"),
+           "ms_per_call_median": round(t_call * 1e3, 4),
+           "ms_per_call_min": round(tot[0], 4),
+           "hbm_gbps_algorithmic": round(b / t_call / 1e9, 1),
+           "pct_peak_hbm": round(100 * b / t_call / 1e9 / R.HBM_PEAK_GBPS, 1),
+           "streaming_kernel_gbps": round((b - R.ELEM_BYTES[p.prec] * p.n) / t_main / 1e9, 1),
+           "bytes": "stored triangle once, x read and written", "calls": reps}
+    if read_peak:
+        out["pct_measured_read_peak"] = round(100 * b / t_call / 1e9 / read_peak, 1)
     del A
     torch.cuda.empty_cache()
     return out
@@ -546,6 +597,16 @@ def main():
                 ("ssyr2-L-n32768", lambda: W.make_syr2_problem("s", "L", 32768, seed=32768)),
                 ("dsyr2-U-n32768", lambda: W.make_syr2_problem("d", "U", 32768, seed=32768))]:
             detail[name] = measure_syr2_detail(name, make(), args.detail_reps, rd_med)
+        for name, make in [
+                ("strmv-L-N-n32768",
+                 lambda: W.make_trmv_problem("s", "L", "N", "N", 32768, seed=32768)),
+                ("dtrmv-U-T-n32768",
+                 lambda: W.make_trmv_problem("d", "U", "T", "N", 32768, seed=32768)),
+                ("ztrmv-L-C-n16384",
+                 lambda: W.make_trmv_problem("z", "L", "C", "N", 16384, seed=16384)),
+                ("wtrmv-U-N-n16384",
+                 lambda: W.make_trmv_problem("w", "U", "N", "N", 16384, seed=16384))]:
+            detail[name] = measure_trmv_detail(name, make(), args.detail_reps, rd_med)
         out["detail"] = detail
         # the report's point: SYMV reads half the bytes of GEMV on the same
         # order, so takes about half the time

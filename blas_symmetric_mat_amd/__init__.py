@@ -27,7 +27,9 @@ __all__ = ["xsymv_s", "xsymv_d", "xhemv_c", "xhemv_z", "xsymv_w", "XsymvError",
            "gemv_config_info", "gemv_select_config", "gemv_current_config",
            "gemv_workspace_bytes", "gemv_plan", "xsyr2_s", "xsyr2_d", "xher2_c", "xher2_z",
            "xsyr2_w", "syr2_num_configs", "syr2_config_info", "syr2_select_config",
-           "syr2_current_config"]
+           "syr2_current_config", "xtrmv_s", "xtrmv_d", "xtrmv_c", "xtrmv_z", "xtrmv_w",
+           "trmv_num_configs", "trmv_config_info", "trmv_select_config", "trmv_current_config",
+           "trmv_workspace_bytes"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libxsymv.so")
 PREC_CODE = {"s": 0, "d": 1, "c": 2, "z": 3, "w": 4}
@@ -61,6 +63,7 @@ _SCALAR = {"s": ctypes.c_float, "d": ctypes.c_double, "c": _C64, "z": _C128, "w"
 _ENTRY = {"s": "xsymv_s", "d": "xsymv_d", "c": "xhemv_c", "z": "xhemv_z", "w": "xsymv_w"}
 _GENTRY = {"s": "xgemv_s", "d": "xgemv_d", "c": "xgemv_c", "z": "xgemv_z", "w": "xgemv_w"}
 _RENTRY = {"s": "xsyr2_s", "d": "xsyr2_d", "c": "xher2_c", "z": "xher2_z", "w": "xsyr2_w"}
+_TENTRY = {"s": "xtrmv_s", "d": "xtrmv_d", "c": "xtrmv_c", "z": "xtrmv_z", "w": "xtrmv_w"}
 
 _lib = None
 _lock = threading.Lock()
@@ -91,6 +94,20 @@ def library():
                 f = getattr(lib, nm)
                 f.restype = ci
                 f.argtypes = [cc, ci, _SCALAR[p], vp, ci, vp, ci, vp, ci, vp]
+            for p, nm in _TENTRY.items():
+                f = getattr(lib, nm)
+                f.restype = ci
+                f.argtypes = [cc, cc, cc, ci, vp, ci, vp, ci, vp]
+            lib.xtrmv_num_configs.restype = ci
+            lib.xtrmv_num_configs.argtypes = [ci]
+            lib.xtrmv_config_info.restype = ci
+            lib.xtrmv_config_info.argtypes = [ci, ci] + [ctypes.POINTER(ci)] * 6
+            lib.xtrmv_select_config.restype = ci
+            lib.xtrmv_select_config.argtypes = [ci, ci]
+            lib.xtrmv_current_config.restype = ci
+            lib.xtrmv_current_config.argtypes = [ci, cc, cc]
+            lib.xtrmv_workspace_bytes.restype = ctypes.c_size_t
+            lib.xtrmv_workspace_bytes.argtypes = [ci, cc, cc, ci]
             lib.xsymv_workspace_bytes.restype = ctypes.c_size_t
             lib.xsymv_workspace_bytes.argtypes = [ci, cc, ci]
             lib.xsymv_release.restype = ci
@@ -278,6 +295,77 @@ def xher2_z(uplo, n, alpha, x, incx, y, incy, A, lda, stream=None):
 def xsyr2_w(uplo, n, alpha, x, incx, y, incy, A, lda, stream=None):
     """WSYR2: double-double; alpha is a (hi, lo) tuple."""
     _rcall("w", uplo, n, alpha, x, incx, y, incy, A, lda, stream)
+
+
+def _ch(v):
+    return v.encode()[:1] if isinstance(v, str) else v
+
+
+def _tcall(prec, uplo, trans, diag, n, A, lda, x, incx, stream):
+    f = getattr(library(), _TENTRY[prec])
+    rc = f(_ch(uplo), _ch(trans), _ch(diag), n, _addr(A), lda, _addr(x), incx, _stream(stream))
+    if rc != 0:
+        raise XsymvError(_TENTRY[prec], rc)
+
+
+def xtrmv_s(uplo, trans, diag, n, A, lda, x, incx, stream=None):
+    """STRMV: x := op(T)*x in place, T the stored triangle, float32."""
+    _tcall("s", uplo, trans, diag, n, A, lda, x, incx, stream)
+
+
+def xtrmv_d(uplo, trans, diag, n, A, lda, x, incx, stream=None):
+    """DTRMV: float64."""
+    _tcall("d", uplo, trans, diag, n, A, lda, x, incx, stream)
+
+
+def xtrmv_c(uplo, trans, diag, n, A, lda, x, incx, stream=None):
+    """CTRMV: complex64 ('C' conjugates)."""
+    _tcall("c", uplo, trans, diag, n, A, lda, x, incx, stream)
+
+
+def xtrmv_z(uplo, trans, diag, n, A, lda, x, incx, stream=None):
+    """ZTRMV: complex128."""
+    _tcall("z", uplo, trans, diag, n, A, lda, x, incx, stream)
+
+
+def xtrmv_w(uplo, trans, diag, n, A, lda, x, incx, stream=None):
+    """WTRMV: double-double (hi, lo) pairs."""
+    _tcall("w", uplo, trans, diag, n, A, lda, x, incx, stream)
+
+
+def trmv_num_configs(prec: str) -> int:
+    return library().xtrmv_num_configs(PREC_CODE[prec])
+
+
+def trmv_config_info(prec: str, idx: int) -> dict:
+    vals = [ctypes.c_int() for _ in range(6)]
+    if library().xtrmv_config_info(PREC_CODE[prec], idx, *[ctypes.byref(v) for v in vals]) != 0:
+        raise IndexError(idx)
+    w, sw, g, nt, sp, r = (v.value for v in vals)
+    return {"waves": w, "stripes_per_wave": sw, "cols_per_group": g, "nontemporal": nt,
+            "split": sp, "rows_per_strip": r}
+
+
+def trmv_select_config(prec: str, idx: int) -> None:
+    if library().xtrmv_select_config(PREC_CODE[prec], idx) != 0:
+        raise ValueError("bad trmv configuration selection")
+
+
+def trmv_current_config(prec: str, uplo: str = "L", trans: str = "N") -> int:
+    """The configuration a call (prec, uplo, trans) would use now."""
+    v = library().xtrmv_current_config(PREC_CODE[prec], _ch(uplo), _ch(trans))
+    if v < 0:
+        raise ValueError("bad trmv configuration query")
+    return v
+
+
+def trmv_workspace_bytes(prec: str, uplo: str, trans: str, n: int) -> int:
+    """Device workspace bytes of one call with the selected configuration
+    (needs the device: the split depends on resident workgroups)."""
+    v = library().xtrmv_workspace_bytes(PREC_CODE[prec], _ch(uplo), _ch(trans), n)
+    if v == ctypes.c_size_t(-1).value:
+        raise XsymvError("xtrmv_workspace_bytes", 1000)
+    return v
 
 
 def syr2_num_configs(prec: str) -> int:

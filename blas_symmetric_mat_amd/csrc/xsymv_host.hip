@@ -326,10 +326,43 @@ int check_gemv_args(char trans, int m, int n, const void* A, int lda, const void
 namespace {
 std::atomic<int> g_gemv_idx[5];
 std::atomic<int> g_syr2_idx[5];
+std::atomic<int> g_trmv_idx[5] = {-1, -1, -1, -1, -1};
 }
 
 int gemv_selected(int prec) { return g_gemv_idx[prec].load(); }
 int syr2_selected(int prec) { return g_syr2_idx[prec].load(); }
+int trmv_selected(int prec) { return g_trmv_idx[prec].load(); }
+
+int check_trmv_args(char uplo, char trans, char diag, int n, const void* A, int lda,
+                    const void* x, int incx, bool* upper, int* tr, bool* unit)
+{
+    if (uplo == 'U' || uplo == 'u')
+        *upper = true;
+    else if (uplo == 'L' || uplo == 'l')
+        *upper = false;
+    else
+        return -1;
+    if (trans == 'N' || trans == 'n')
+        *tr = 0;
+    else if (trans == 'T' || trans == 't')
+        *tr = 1;
+    else if (trans == 'C' || trans == 'c')
+        *tr = 2;
+    else
+        return -2;
+    if (diag == 'U' || diag == 'u')
+        *unit = true;
+    else if (diag == 'N' || diag == 'n')
+        *unit = false;
+    else
+        return -3;
+    if (n < 0) return -4;
+    if (n > 0 && A == nullptr) return -5;
+    if (lda < std::max(1, n)) return -6;
+    if (n > 0 && x == nullptr) return -7;
+    if (incx == 0) return -8;
+    return 0;
+}
 
 int check_syr2_args(char uplo, int n, const void* x, int incx, const void* y, int incy,
                     const void* A, int lda, bool* upper)
@@ -1120,6 +1153,82 @@ int xsyr2_current_config(int prec)
 {
     if (prec < 0 || prec > 4) return -1;
     return syr2_selected(prec);
+}
+
+int xtrmv_num_configs(int prec)
+{
+    switch (prec) {
+    case XSYMV_S: return (int)trmv_kernel_sets<float>().size();
+    case XSYMV_D: return (int)trmv_kernel_sets<double>().size();
+    case XSYMV_C: return (int)trmv_kernel_sets<cf32>().size();
+    case XSYMV_Z: return (int)trmv_kernel_sets<cf64>().size();
+    case XSYMV_W: return (int)trmv_kernel_sets<ddreal>().size();
+    default: return -1;
+    }
+}
+
+int xtrmv_config_info(int prec, int idx, int* waves, int* stripes_per_wave, int* cols_per_group,
+                      int* nontemporal, int* split, int* rows_per_strip)
+{
+    if (idx < 0 || idx >= xtrmv_num_configs(prec)) return -1;
+    int W = 0, SW = 0, G = 0, NT = 0, SP = 0, R = 0;
+    switch (prec) {
+#define XSYMV_K(T)                                                                       \
+    {                                                                                    \
+        const auto& k = trmv_kernel_sets<T>()[idx];                                      \
+        W = k.W; SW = k.SW; G = k.G; NT = k.NT; SP = k.split; R = k.R();                 \
+        break;                                                                           \
+    }
+    case XSYMV_S: XSYMV_K(float)
+    case XSYMV_D: XSYMV_K(double)
+    case XSYMV_C: XSYMV_K(cf32)
+    case XSYMV_Z: XSYMV_K(cf64)
+    default: XSYMV_K(ddreal)
+#undef XSYMV_K
+    }
+    if (waves) *waves = W;
+    if (stripes_per_wave) *stripes_per_wave = SW;
+    if (cols_per_group) *cols_per_group = G;
+    if (nontemporal) *nontemporal = NT;
+    if (split) *split = SP;
+    if (rows_per_strip) *rows_per_strip = R;
+    return 0;
+}
+
+int xtrmv_select_config(int prec, int idx)
+{
+    if (prec < 0 || prec > 4 || idx < -1 || idx >= xtrmv_num_configs(prec)) return -1;
+    g_trmv_idx[prec].store(idx);
+    return 0;
+}
+
+int xtrmv_current_config(int prec, char uplo, char trans)
+{
+    bool upper = false, unit = false;
+    int tr = 0;
+    // the argument checks of a call with n = 0
+    if (check_trmv_args(uplo, trans, 'N', 0, nullptr, 1, nullptr, 1, &upper, &tr, &unit))
+        return -1;
+    switch (prec) {
+    case XSYMV_S: return trmv_pick<float>(upper, tr);
+    case XSYMV_D: return trmv_pick<double>(upper, tr);
+    case XSYMV_C: return trmv_pick<cf32>(upper, tr);
+    case XSYMV_Z: return trmv_pick<cf64>(upper, tr);
+    case XSYMV_W: return trmv_pick<ddreal>(upper, tr);
+    default: return -1;
+    }
+}
+
+size_t xtrmv_workspace_bytes(int prec, char uplo, char trans, int n)
+{
+    switch (prec) {
+    case XSYMV_S: return trmv_ws_bytes<float>(uplo, trans, n);
+    case XSYMV_D: return trmv_ws_bytes<double>(uplo, trans, n);
+    case XSYMV_C: return trmv_ws_bytes<cf32>(uplo, trans, n);
+    case XSYMV_Z: return trmv_ws_bytes<cf64>(uplo, trans, n);
+    case XSYMV_W: return trmv_ws_bytes<ddreal>(uplo, trans, n);
+    default: return (size_t)-1;
+    }
 }
 
 const char* xsymv_version(void) { return "xsymv-gfx950 0.1"; }

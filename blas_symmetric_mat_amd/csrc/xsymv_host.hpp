@@ -26,6 +26,7 @@
 #include "xsymv_strip.hpp"
 #include "xgemv_strip.hpp"
 #include "xsyr2_strip.hpp"
+#include "xtrmv_strip.hpp"
 
 namespace xsymv {
 
@@ -585,6 +586,146 @@ int syr2_run(char uplo, int n, T alpha, const T* x, int incx, const T* y, int in
         timing_push(tc);
     }
     return 0;
+}
+
+// ------------------------------------------------------------------ xTRMV
+template <class T>
+struct TrmvKernelSet {
+    int W, SW, G, NT, split;
+    void (*k[2][3][2])(TrmvArgs<T>);  // [upper][0 'N', 1 'T', 2 'C'][unit]
+    int R() const { return W * SW * 64 * Elem<T>::VEC; }
+};
+
+template <class T, bool UP, int W, int SW, int G, bool NT>
+void fill_trmv(void (*k[3][2])(TrmvArgs<T>))
+{
+    constexpr bool cplx = std::is_same<T, cf32>::value || std::is_same<T, cf64>::value;
+    k[0][0] = &trmv_strip<T, UP, 0, false, W, SW, G, NT, STRIP_CBUF>;
+    k[0][1] = &trmv_strip<T, UP, 0, true, W, SW, G, NT, STRIP_CBUF>;
+    k[1][0] = &trmv_strip<T, UP, 1, false, W, SW, G, NT, STRIP_CBUF>;
+    k[1][1] = &trmv_strip<T, UP, 1, true, W, SW, G, NT, STRIP_CBUF>;
+    if constexpr (cplx) {
+        k[2][0] = &trmv_strip<T, UP, 2, false, W, SW, G, NT, STRIP_CBUF>;
+        k[2][1] = &trmv_strip<T, UP, 2, true, W, SW, G, NT, STRIP_CBUF>;
+    } else {  // real: T^H = T^T
+        k[2][0] = k[1][0];
+        k[2][1] = k[1][1];
+    }
+}
+
+template <class T, int W, int SW, int G, bool NT, int SPLIT>
+TrmvKernelSet<T> make_trmv()
+{
+    TrmvKernelSet<T> k{W, SW, G, NT ? 1 : 0, SPLIT, {}};
+    fill_trmv<T, false, W, SW, G, NT>(k.k[0]);
+    fill_trmv<T, true, W, SW, G, NT>(k.k[1]);
+    return k;
+}
+
+template <class T> const std::vector<TrmvKernelSet<T>>& trmv_kernel_sets();
+struct TrmvDefaults {
+    int idx[2][2];  // [upper][op = T or T^H]
+};
+template <class T> TrmvDefaults trmv_defaults();
+int trmv_selected(int prec);  // -1: the built-in choice
+
+template <class T>
+int trmv_pick(bool upper, int tr)
+{
+    const int sel = trmv_selected(prec_code<T>());
+    return sel >= 0 ? sel : trmv_defaults<T>().idx[upper ? 1 : 0][tr != 0 ? 1 : 0];
+}
+int check_trmv_args(char uplo, char trans, char diag, int n, const void* A, int lda,
+                    const void* x, int incx, bool* upper, int* tr, bool* unit);
+
+// Workspace of a TRMV call: [partials][x gathered]
+template <class T>
+size_t trmv_workspace_bytes(int tr, int nseg, int R, int NS, int n)
+{
+    const size_t part = tr == 0 ? (size_t)nseg * R : (size_t)NS * n;
+    return align_up(part * sizeof(T)) + align_up((size_t)n * sizeof(T));
+}
+
+template <class T>
+int trmv_run(char uplo, char trans, char diag, int n, const T* A, int lda, T* x, int incx,
+             hipStream_t stream, int forced_idx)
+{
+    bool upper = false, unit = false;
+    int tr = 0;
+    int rc = check_trmv_args(uplo, trans, diag, n, A, lda, x, incx, &upper, &tr, &unit);
+    if (rc) return rc;
+    if (n == 0) return 0;
+    const auto& ks = trmv_kernel_sets<T>()[forced_idx >= 0 ? forced_idx : trmv_pick<T>(upper, tr)];
+    const int R = ks.R();
+    const int threads = 64 * ks.W;
+    auto kern = ks.k[upper ? 1 : 0][tr][unit ? 1 : 0];
+    int dev = 0;
+    XSYMV_HIP(hipGetDevice(&dev));
+    DeviceState* ds = device_state(dev);
+    std::lock_guard<std::mutex> lk(device_mutex(ds));
+    int G = 0;
+    rc = resident_blocks((const void*)kern, threads, &G);
+    if (rc) return rc;
+    const StripPlan* plan = nullptr;
+    rc = get_strip_plan(ds, dev, upper, n, R, G, ks.split, stream, &plan);
+    if (rc) return rc;
+    void* ws = nullptr;
+    rc = get_workspace(ds, stream, trmv_workspace_bytes<T>(tr, plan->nseg, R, plan->NS, n), &ws);
+    if (rc) return rc;
+    char* base = static_cast<char*>(ws);
+    const size_t part_bytes = align_up((tr == 0 ? (size_t)plan->nseg * R : (size_t)plan->NS * n) *
+                                       sizeof(T));
+    T* part = reinterpret_cast<T*>(base);
+    T* xg = reinterpret_cast<T*>(base + part_bytes);
+    const long long kx = incx > 0 ? 0 : (long long)(1 - n) * incx;
+    const T* xin = x;
+    if (incx != 1) {
+        symv_gather<T><<<blocks_for(n, 256), 256, 0, stream>>>(x, incx, kx, n, xg);
+        XSYMV_HIP(hipGetLastError());
+        xin = xg;
+    }
+    TimedCall tc{};
+    const bool timing = timing_enabled();
+    if (timing) {
+        XSYMV_HIP(hipEventCreate(&tc.e0));
+        XSYMV_HIP(hipEventCreate(&tc.e1));
+        XSYMV_HIP(hipEventCreate(&tc.e2));
+        XSYMV_HIP(hipEventRecord(tc.e0, stream));
+    }
+    TrmvArgs<T> ta{A, xin, part, part, plan->d_blocks, plan->d_strip_base, (long long)lda, n};
+    kern<<<plan->G, threads, 0, stream>>>(ta);
+    XSYMV_HIP(hipGetLastError());
+    if (timing) XSYMV_HIP(hipEventRecord(tc.e1, stream));
+    TrmvMergeArgs<T> ma{part, plan->d_seg_base, xin, x, (long long)incx, kx, n, plan->NS, R,
+                        upper ? 1 : 0, tr, unit ? 1 : 0};
+    trmv_merge<T, MERGE_SPLIT><<<blocks_for(n, 64), 64 * MERGE_SPLIT, 0, stream>>>(ma);
+    XSYMV_HIP(hipGetLastError());
+    if (timing) {
+        XSYMV_HIP(hipEventRecord(tc.e2, stream));
+        timing_push(tc);
+    }
+    return 0;
+}
+
+template <class T>
+size_t trmv_ws_bytes(char uplo, char trans, int n)
+{
+    const bool upper = uplo == 'U' || uplo == 'u';
+    const int tr = (trans == 'N' || trans == 'n') ? 0 : 1;
+    if (n <= 0) return 0;
+    const auto& ks = trmv_kernel_sets<T>()[trmv_pick<T>(upper, tr)];
+    size_t most = 0;
+    for (int unit = 0; unit < 2; ++unit) {  // the larger of the two diagonal kinds
+        int G = 0;
+        if (resident_blocks((const void*)ks.k[upper ? 1 : 0][tr][unit], 64 * ks.W, &G))
+            return (size_t)-1;
+        std::vector<StripBlock> blocks;
+        std::vector<int> sb, segb;
+        int NS = 0;
+        build_strip_plan_host(upper, n, ks.R(), G, ks.split, blocks, sb, segb, NS);
+        most = std::max(most, trmv_workspace_bytes<T>(tr, segb[NS], ks.R(), NS, n));
+    }
+    return most;
 }
 
 // ---------------------------------------------------------------- autotuner

@@ -57,6 +57,24 @@ template <> const std::vector<Syr2KernelSet<cf32>>& syr2_kernel_sets<cf32>()
     };
     return v;
 }
+
+// xTRMV configurations (xtrmv_select_config forces one; otherwise
+// trmv_defaults picks per triangle and transposition)
+template <> const std::vector<TrmvKernelSet<cf32>>& trmv_kernel_sets<cf32>()
+{
+    static const std::vector<TrmvKernelSet<cf32>> v = {
+        make_trmv<cf32, 16, 1, 8, true, 1>(),              // R 2048, 16 KB runs, G 8, split by stored rows
+        make_trmv<cf32, 16, 1, 4, true, 1>(),              // R 2048, 16 KB runs, G 4, split by stored rows
+        make_trmv<cf32, 8, 2, 4, true, 0>(),               // R 2048, 16 KB runs, G 4
+        make_trmv<cf32, 16, 1, 16, true, 1>(),             // R 2048, 16 KB runs, G 16, split by stored rows
+        make_trmv<cf32, 16, 1, 8, true, 0>(),              // R 2048, 16 KB runs, G 8
+    };
+    return v;
+}
+
+// built-in choice [upper][op = T or T^H]: the fastest (median of 20 calls)
+// at n = 16384 on MI355X
+template <> TrmvDefaults trmv_defaults<cf32>() { return TrmvDefaults{{{0, 0}, {3, 3}}}; }
 }  // namespace xsymv
 
 extern "C" int xhemv_c(char uplo, int n, xcomplex64 alpha, const xcomplex64* A, int lda,
@@ -86,4 +104,12 @@ extern "C" int xher2_c(char uplo, int n, xcomplex64 alpha, const xcomplex64* x, 
     using xsymv::cf32;
     return xsymv::syr2_run<cf32>(uplo, n, cf32{alpha.re, alpha.im}, (const cf32*)x, incx,
                                (const cf32*)y, incy, (cf32*)A, lda, (hipStream_t)stream, -1);
+}
+
+extern "C" int xtrmv_c(char uplo, char trans, char diag, int n, const xcomplex64* A, int lda,
+                       xcomplex64* x, int incx, void* stream)
+{
+    using xsymv::cf32;
+    return xsymv::trmv_run<cf32>(uplo, trans, diag, n, (const cf32*)A, lda, (cf32*)x, incx,
+                               (hipStream_t)stream, -1);
 }

@@ -64,6 +64,25 @@ template <> const std::vector<Syr2KernelSet<float>>& syr2_kernel_sets<float>()
     };
     return v;
 }
+
+// xTRMV configurations (xtrmv_select_config forces one; otherwise
+// trmv_defaults picks per triangle and transposition)
+template <> const std::vector<TrmvKernelSet<float>>& trmv_kernel_sets<float>()
+{
+    static const std::vector<TrmvKernelSet<float>> v = {
+        make_trmv<float, 16, 1, 16, true, 1>(),            // R 4096, 16 KB runs, G 16, split by stored rows
+        make_trmv<float, 16, 1, 8, true, 1>(),             // R 4096, 16 KB runs, G 8, split by stored rows
+        make_trmv<float, 16, 1, 4, true, 0>(),             // R 4096, 16 KB runs, G 4
+        make_trmv<float, 16, 1, 4, true, 1>(),             // R 4096, 16 KB runs, G 4, split by stored rows
+        make_trmv<float, 8, 2, 4, true, 1>(),              // R 4096, 16 KB runs, G 4, split by stored rows
+        make_trmv<float, 16, 2, 4, true, 1>(),             // R 8192, 32 KB runs, G 4, split by stored rows
+    };
+    return v;
+}
+
+// built-in choice [upper][op = T or T^H]: the fastest (median of 20 calls)
+// at n = 32768 on MI355X
+template <> TrmvDefaults trmv_defaults<float>() { return TrmvDefaults{{{0, 3}, {0, 2}}}; }
 }  // namespace xsymv
 
 extern "C" int xsymv_s(char uplo, int n, float alpha, const float* A, int lda, const float* x,
@@ -85,4 +104,10 @@ extern "C" int xsyr2_s(char uplo, int n, float alpha, const float* x, int incx, 
 {
     return xsymv::syr2_run<float>(uplo, n, alpha, x, incx, y, incy, A, lda, (hipStream_t)stream,
                                -1);
+}
+
+extern "C" int xtrmv_s(char uplo, char trans, char diag, int n, const float* A, int lda, float* x,
+                       int incx, void* stream)
+{
+    return xsymv::trmv_run<float>(uplo, trans, diag, n, A, lda, x, incx, (hipStream_t)stream, -1);
 }

@@ -58,6 +58,24 @@ template <> const std::vector<Syr2KernelSet<ddreal>>& syr2_kernel_sets<ddreal>()
     };
     return v;
 }
+
+// xTRMV configurations (xtrmv_select_config forces one; otherwise
+// trmv_defaults picks per triangle and transposition)
+template <> const std::vector<TrmvKernelSet<ddreal>>& trmv_kernel_sets<ddreal>()
+{
+    static const std::vector<TrmvKernelSet<ddreal>> v = {
+        make_trmv<ddreal, 16, 1, 4, true, 1>(),            // R 1024, 16 KB runs, G 4, split by stored rows
+        make_trmv<ddreal, 8, 2, 4, true, 1>(),             // R 1024, 16 KB runs, G 4, split by stored rows
+        make_trmv<ddreal, 4, 2, 4, true, 0>(),             // R 512, 8 KB runs, G 4
+        make_trmv<ddreal, 16, 1, 4, true, 0>(),            // R 1024, 16 KB runs, G 4
+        make_trmv<ddreal, 16, 1, 8, true, 1>(),            // R 1024, 16 KB runs, G 8, split by stored rows
+    };
+    return v;
+}
+
+// built-in choice [upper][op = T or T^H]: the fastest (median of 20 calls)
+// at n = 16384 on MI355X
+template <> TrmvDefaults trmv_defaults<ddreal>() { return TrmvDefaults{{{4, 2}, {4, 2}}}; }
 }  // namespace xsymv
 
 extern "C" int xsymv_w(char uplo, int n, xdd alpha, const xdd* A, int lda, const xdd* x,
@@ -87,4 +105,12 @@ extern "C" int xsyr2_w(char uplo, int n, xdd alpha, const xdd* x, int incx, cons
     using xsymv::ddreal;
     return xsymv::syr2_run<ddreal>(uplo, n, ddreal{alpha.hi, alpha.lo}, (const ddreal*)x, incx,
                                (const ddreal*)y, incy, (ddreal*)A, lda, (hipStream_t)stream, -1);
+}
+
+extern "C" int xtrmv_w(char uplo, char trans, char diag, int n, const xdd* A, int lda, xdd* x,
+                       int incx, void* stream)
+{
+    using xsymv::ddreal;
+    return xsymv::trmv_run<ddreal>(uplo, trans, diag, n, (const ddreal*)A, lda, (ddreal*)x, incx,
+                                   (hipStream_t)stream, -1);
 }

@@ -57,6 +57,24 @@ template <> const std::vector<Syr2KernelSet<cf64>>& syr2_kernel_sets<cf64>()
     };
     return v;
 }
+
+// xTRMV configurations (xtrmv_select_config forces one; otherwise
+// trmv_defaults picks per triangle and transposition)
+template <> const std::vector<TrmvKernelSet<cf64>>& trmv_kernel_sets<cf64>()
+{
+    static const std::vector<TrmvKernelSet<cf64>> v = {
+        make_trmv<cf64, 16, 1, 4, true, 1>(),              // R 1024, 16 KB runs, G 4, split by stored rows
+        make_trmv<cf64, 8, 2, 4, true, 1>(),               // R 1024, 16 KB runs, G 4, split by stored rows
+        make_trmv<cf64, 4, 2, 4, true, 0>(),               // R 512, 8 KB runs, G 4
+        make_trmv<cf64, 16, 1, 4, true, 0>(),              // R 1024, 16 KB runs, G 4
+        make_trmv<cf64, 16, 1, 8, true, 1>(),              // R 1024, 16 KB runs, G 8, split by stored rows
+    };
+    return v;
+}
+
+// built-in choice [upper][op = T or T^H]: the fastest (median of 20 calls)
+// at n = 16384 on MI355X
+template <> TrmvDefaults trmv_defaults<cf64>() { return TrmvDefaults{{{4, 4}, {4, 3}}}; }
 }  // namespace xsymv
 
 extern "C" int xhemv_z(char uplo, int n, xcomplex128 alpha, const xcomplex128* A, int lda,
@@ -87,4 +105,12 @@ extern "C" int xher2_z(char uplo, int n, xcomplex128 alpha, const xcomplex128* x
     using xsymv::cf64;
     return xsymv::syr2_run<cf64>(uplo, n, cf64{alpha.re, alpha.im}, (const cf64*)x, incx,
                                (const cf64*)y, incy, (cf64*)A, lda, (hipStream_t)stream, -1);
+}
+
+extern "C" int xtrmv_z(char uplo, char trans, char diag, int n, const xcomplex128* A, int lda,
+                       xcomplex128* x, int incx, void* stream)
+{
+    using xsymv::cf64;
+    return xsymv::trmv_run<cf64>(uplo, trans, diag, n, (const cf64*)A, lda, (cf64*)x, incx,
+                               (hipStream_t)stream, -1);
 }

@@ -76,3 +76,10 @@ def syr2_call_bytes(prec: str, n: int) -> int:
     """Algorithmic bytes of one rank-2 update: the stored triangle read and
     written once, x and y read."""
     return ELEM_BYTES[prec] * (2 * stored_elements(n) + 2 * n)
+
+
+# ------------------------------------------------------------------ xTRMV
+def trmv_call_bytes(prec: str, n: int, unit: bool) -> int:
+    """Algorithmic bytes of one triangular product: the stored triangle (its
+    diagonal only when it is read) read once, x read and written."""
+    return ELEM_BYTES[prec] * (stored_elements(n) - (n if unit else 0) + 2 * n)

@@ -193,6 +193,53 @@ int xsyr2_config_info(int prec, int idx, int *waves, int *stripes_per_wave,
 int xsyr2_select_config(int prec, int idx);
 int xsyr2_current_config(int prec);
 
+/* Triangular matrix-vector product (another of the Level-2 BLAS the report's
+ * §5 carries the approach to), BLAS xTRMV:
+ *
+ *   x := op(T)*x,   op(T) = T ('N'), T^T ('T') or T^H ('C'; = 'T' for the
+ *                   real types s, d, w)
+ *
+ * T is the uplo triangle of A (DEVICE pointer, column-major, lda >=
+ * max(1, n)); diag 'N' takes the diagonal from A, 'U' takes ones and never
+ * reads it.  The other triangle and rows n..lda-1 are never read.  x: DEVICE
+ * pointer, n elements with stride incx (!= 0; negative walks backwards),
+ * overwritten in place; gaps between strided elements are left alone.  Each
+ * output is a fixed-order sum of partial sums (no atomics), so repeated calls
+ * give identical bits.  The library reads all of x before it writes any of
+ * it.  n == 0: nothing is done.  Asynchronous on `stream`; uses the
+ * per-stream workspace (xtrmv_workspace_bytes).  Return codes (BLAS xerbla
+ * positions): -1 uplo, -2 trans, -3 diag, -4 n < 0, -5 A NULL,
+ * -6 lda < max(1, n), -7 x NULL, -8 incx == 0; 1000 + hipError_t; 2000
+ * installed workspace too small. */
+int xtrmv_s(char uplo, char trans, char diag, int n, const float *A, int lda, float *x,
+            int incx, void *stream);
+int xtrmv_d(char uplo, char trans, char diag, int n, const double *A, int lda, double *x,
+            int incx, void *stream);
+int xtrmv_c(char uplo, char trans, char diag, int n, const xcomplex64 *A, int lda,
+            xcomplex64 *x, int incx, void *stream);
+int xtrmv_z(char uplo, char trans, char diag, int n, const xcomplex128 *A, int lda,
+            xcomplex128 *x, int incx, void *stream);
+int xtrmv_w(char uplo, char trans, char diag, int n, const xdd *A, int lda, xdd *x,
+            int incx, void *stream);
+
+/* Triangular product configurations, same fields as the rank-2 update's.
+ * Built in: one configuration per (precision, triangle, 'N' or a
+ * transposition), the fastest measured on MI355X at the largest size.
+ * xtrmv_select_config(prec, idx) forces configuration idx for every call of
+ * that precision; idx = -1 restores the built-in choice (0, or -1 for a bad
+ * code or index).  xtrmv_current_config: the configuration a call (prec,
+ * uplo, trans) would use now (-1 for a bad code).  xtrmv_workspace_bytes:
+ * device workspace bytes of one call (precision, uplo, trans, n) with that
+ * configuration on the current device (0 for n <= 0; -1 cast to size_t on a
+ * bad precision code or when the device cannot be queried). */
+int xtrmv_num_configs(int prec);
+int xtrmv_config_info(int prec, int idx, int *waves, int *stripes_per_wave,
+                      int *cols_per_group, int *nontemporal, int *split,
+                      int *rows_per_strip);
+int xtrmv_select_config(int prec, int idx);
+int xtrmv_current_config(int prec, char uplo, char trans);
+size_t xtrmv_workspace_bytes(int prec, char uplo, char trans, int n);
+
 /* Bytes of device workspace one call of precision `prec` and order n uses
  * with the configuration selected for it now, on the current device (0 for
  * n == 0; -1 cast to size_t for a bad precision code, or when the device

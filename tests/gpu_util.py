@@ -125,3 +125,36 @@ def run_syr2(p):
     getattr(X, RENTRY[p.prec])(p.uplo, p.n, p.alpha, x, p.incx, y, p.incy, A, p.lda)
     torch.cuda.synchronize()
     return A.cpu().numpy()
+
+
+TENTRY = {"s": "xtrmv_s", "d": "xtrmv_d", "c": "xtrmv_c", "z": "xtrmv_z", "w": "xtrmv_w"}
+
+
+class TrmvDevice:
+    """A triangular problem's A on the device; x is uploaded per call and
+    overwritten there."""
+
+    def __init__(self, p):
+        self.p = p
+        self.A = to_device(p.A)
+
+    def run(self, x_host=None):
+        import blas_symmetric_mat_amd as X
+        torch = torch_dev()
+        p = self.p
+        x = to_device(p.x if x_host is None else x_host)
+        getattr(X, TENTRY[p.prec])(p.uplo, p.trans, p.diag, p.n, self.A, p.lda, x, p.incx)
+        torch.cuda.synchronize()
+        return x.cpu().numpy()
+
+
+def assert_close_trmv(p, got, ref, label=""):
+    """|got - ref| <= 4*n*eps*(|op(T)||x|)_i on every output (logical order);
+    the bound is formed row by row (no dense op(T)) when x is contiguous."""
+    idx = H.vec_index(p.n, p.incx)
+    tol = H.trmv_tolerance(p, np.arange(p.n)) if p.incx == 1 else H.trmv_tolerance(p)
+    d = H.diff(p.prec, got[idx], ref[idx])
+    assert np.all(np.isfinite(d)), f"{label}: non-finite result"
+    bad = np.nonzero(~(d <= tol))[0]
+    assert bad.size == 0, (f"{label}: {bad.size} outputs beyond the bound, worst ratio "
+                           f"{np.max(d / np.maximum(tol, 1e-300)):.3g} at {bad[0]}")

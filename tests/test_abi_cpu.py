@@ -16,7 +16,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def declared_functions():
     text = open(os.path.join(ROOT, "include", "xsymv.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(x(?:symv|hemv|gemv|syr2|her2)_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(x(?:symv|hemv|gemv|syr2|her2|trmv)_\w+)\s*\(", text)))
 
 
 def test_exports_every_declared_function():
@@ -24,7 +24,8 @@ def test_exports_every_declared_function():
     names = declared_functions()
     assert {"xsymv_s", "xsymv_d", "xhemv_c", "xhemv_z", "xsymv_w", "xgemv_s", "xgemv_d",
             "xgemv_c", "xgemv_z", "xgemv_w", "xsymv_set_workspace", "xsyr2_s", "xsyr2_d",
-            "xher2_c", "xher2_z", "xsyr2_w"} <= set(names)
+            "xher2_c", "xher2_z", "xsyr2_w", "xtrmv_s", "xtrmv_d", "xtrmv_c", "xtrmv_z",
+            "xtrmv_w", "xtrmv_workspace_bytes"} <= set(names)
     for nm in names:
         assert hasattr(lib, nm), nm
 
@@ -295,3 +296,47 @@ def test_syr2_config_tables():
     X.syr2_select_config("s", -1)
     with pytest.raises(ValueError):
         X.syr2_select_config("s", 99)
+
+
+@pytest.mark.parametrize("prec", ["s", "d", "c", "z", "w"])
+def test_trmv_argument_errors_before_device_work(prec):
+    f = getattr(X, "xtrmv_" + prec)
+    # (uplo, trans, diag, n, A, lda, x, incx); pointers are never touched
+    cases = [(("Q", "N", "N", 4, 8, 4, 8, 1), -1), (("L", "Q", "N", 4, 8, 4, 8, 1), -2),
+             (("U", "T", "Q", 4, 8, 4, 8, 1), -3), (("u", "c", "n", -1, 8, 4, 8, 1), -4),
+             (("l", "N", "U", 4, None, 4, 8, 1), -5), (("L", "N", "u", 4, 8, 3, 8, 1), -6),
+             (("L", "t", "N", 4, 8, 4, None, 1), -7), (("U", "C", "N", 4, 8, 4, 8, 0), -8)]
+    for args, code in cases:
+        with pytest.raises(X.XsymvError) as e:
+            f(*args, stream=0)
+        assert e.value.code == code, (args, e.value.code)
+    f("L", "N", "N", 0, None, 1, None, 1, stream=0)   # n == 0
+
+
+def test_trmv_config_tables():
+    for p in "sdczw":
+        k = X.trmv_num_configs(p)
+        assert k >= 1
+        for i in range(k):
+            ci = X.trmv_config_info(p, i)
+            assert ci["split"] in (0, 1)
+            assert ci["rows_per_strip"] == ci["waves"] * ci["stripes_per_wave"] * 64 * \
+                {"s": 4, "d": 2, "c": 2, "z": 1, "w": 1}[p]
+        for uplo in "LU":
+            for trans in "NTC":
+                assert 0 <= X.trmv_current_config(p, uplo, trans) < k
+            # 'T' and 'C' share the built-in choice
+            assert X.trmv_current_config(p, uplo, "T") == X.trmv_current_config(p, uplo, "C")
+    before = {(u, t): X.trmv_current_config("d", u, t) for u in "LU" for t in "NT"}
+    X.trmv_select_config("d", 2)
+    assert all(X.trmv_current_config("d", u, t) == 2 for u in "LU" for t in "NTC")
+    X.trmv_select_config("d", -1)
+    assert before == {(u, t): X.trmv_current_config("d", u, t) for u in "LU" for t in "NT"}
+    with pytest.raises(ValueError):
+        X.trmv_select_config("d", 99)
+    with pytest.raises(IndexError):
+        X.trmv_config_info("d", 99)
+    with pytest.raises(ValueError):
+        X.trmv_current_config("d", "Q", "N")
+    with pytest.raises(ValueError):
+        X.trmv_current_config("d", "L", "Q")

@@ -1,0 +1,126 @@
+"""GPU parity of the triangular product (xTRMV: x := op(T)*x in place)
+through the C ABI against the CPU oracle: every output within
+4*n*eps*(|op(T)||x|)_i of the oracle's, integer inputs bit for bit, NaN in
+what must not be read (other triangle, padding, a unit diagonal) without
+effect, strided x with its gaps untouched, and identical bits from run to run.
+Sizes span several row strips of each configuration with ragged tails."""
+import numpy as np
+import pytest
+
+import oracle
+from blas_symmetric_mat_amd import workloads as W
+from tests import gpu_util as G
+from tests import helpers as H
+from tests import test_oracle_trmv as TM
+
+pytestmark = pytest.mark.gpu
+
+PRECS = TM.PRECS
+TRANS = TM.TRANS
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    G.torch_dev()
+
+
+def strip_rows(prec, uplo="L", trans="N"):
+    import blas_symmetric_mat_amd as X
+    return X.trmv_config_info(prec, X.trmv_current_config(prec, uplo, trans))["rows_per_strip"]
+
+
+def check(p, label):
+    got = G.TrmvDevice(p).run()
+    ref = oracle.trmv_problem(p)
+    G.assert_close_trmv(p, got, ref, label=label)
+    return got
+
+
+@pytest.mark.parametrize("prec", PRECS)
+@pytest.mark.parametrize("uplo", ["L", "U"])
+@pytest.mark.parametrize("trans", TRANS)
+@pytest.mark.parametrize("diag", ["N", "U"])
+@pytest.mark.parametrize("n,pad", [(1, 0), (2, 1), (17, 0), (65, 3), (700, 5), (2111, 2)])
+def test_trmv_parity(prec, uplo, trans, diag, n, pad):
+    G.log(f"trmv {prec} {uplo}{trans}{diag} n={n} lda={n + pad}")
+    p = TM.problem(prec, uplo, trans, diag, n, pad, seed=4000 + n)
+    check(p, f"{prec}{uplo}{trans}{diag}{n}")
+
+
+@pytest.mark.parametrize("prec", PRECS)
+@pytest.mark.parametrize("uplo", ["L", "U"])
+@pytest.mark.parametrize("trans", ["N", "C"])
+@pytest.mark.parametrize("extra", [1, 357])
+def test_trmv_several_strips(prec, uplo, trans, extra):
+    """Two full strips and a ragged third (one row, or a few hundred)."""
+    n = 2 * strip_rows(prec, uplo, trans) + extra
+    G.log(f"trmv strips {prec} {uplo}{trans} n={n}")
+    p = TM.problem(prec, uplo, trans, "N", n, 3, seed=4100 + extra)
+    check(p, f"{prec}{uplo}{trans} n={n}")
+
+
+@pytest.mark.parametrize("prec", PRECS)
+@pytest.mark.parametrize("uplo", ["L", "U"])
+@pytest.mark.parametrize("trans", TRANS)
+@pytest.mark.parametrize("diag", ["N", "U"])
+def test_trmv_integer_bitwise(prec, uplo, trans, diag):
+    """Integer T and x: every partial sum is exact in any order, so the
+    device result equals the int64 product bit for bit."""
+    G.log(f"trmv integer {prec} {uplo}{trans}{diag}")
+    p = TM.problem(prec, uplo, trans, diag, 1500, 7, seed=21, integer=(-4, 4))
+    got = G.TrmvDevice(p).run()
+    assert G.digest(got) == G.digest(H.trmv_integer_expected(p))
+
+
+@pytest.mark.parametrize("prec", PRECS)
+@pytest.mark.parametrize("uplo", ["L", "U"])
+@pytest.mark.parametrize("trans", TRANS)
+def test_trmv_nan_never_read(prec, uplo, trans):
+    """NaN in the other triangle, the padding and (diag = 'U') the diagonal:
+    the results stay finite and match the oracle."""
+    p = TM.problem(prec, uplo, trans, "U", 1029, 5, seed=22, fill=np.nan)
+    p.A[W.diag_index(p.n, p.lda)] = np.nan
+    got = check(p, f"{prec}{uplo}{trans} NaN")
+    assert np.all(np.isfinite(got))
+
+
+@pytest.mark.parametrize("prec", PRECS)
+@pytest.mark.parametrize("trans", TRANS)
+@pytest.mark.parametrize("incx", [-1, 3, -2])
+def test_trmv_increments(prec, trans, incx):
+    """Strided x (either sign): the outputs land at the strided positions and
+    the gaps keep their values."""
+    p = TM.problem(prec, "U", trans, "N", 611, 2, seed=23)
+    xs = W.empty(prec, 1 + (p.n - 1) * abs(incx))
+    xs[...] = 7.0
+    idx = H.vec_index(p.n, incx)
+    xs[idx] = p.x
+    q = W.TrmvProblem(**{**p.__dict__, "x": xs, "incx": incx})
+    got = check(q, f"{prec}{trans} inc {incx}")
+    gaps = np.ones(len(xs), dtype=bool)
+    gaps[idx] = False
+    assert np.all(got[gaps] == 7.0)
+
+
+@pytest.mark.parametrize("prec", PRECS)
+def test_trmv_every_config(prec):
+    import blas_symmetric_mat_amd as X
+    try:
+        for idx in range(X.trmv_num_configs(prec)):
+            X.trmv_select_config(prec, idx)
+            n = strip_rows(prec) + 203
+            for uplo, trans, diag in (("L", "N", "N"), ("U", "C", "U"), ("L", "T", "U"),
+                                      ("U", "N", "N")):
+                G.log(f"trmv config {prec} #{idx} {uplo}{trans}{diag} n={n}")
+                check(TM.problem(prec, uplo, trans, diag, n, 3, seed=idx),
+                      f"{prec}#{idx}{uplo}{trans}{diag}")
+    finally:
+        X.trmv_select_config(prec, -1)
+
+
+@pytest.mark.parametrize("prec", PRECS)
+@pytest.mark.parametrize("trans", ["N", "T"])
+def test_trmv_bitwise_repeatable(prec, trans):
+    p = TM.problem(prec, "L", trans, "N", 3001, 1, seed=24)
+    d = G.TrmvDevice(p)
+    assert len({G.digest(d.run()) for _ in range(10)}) == 1
