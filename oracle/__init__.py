@@ -52,6 +52,8 @@ _NAME = {"s": "ssymv", "d": "dsymv", "c": "chemv", "z": "zhemv", "w": "wsymv"}
 _GNAME = {"s": "sgemv", "d": "dgemv", "c": "cgemv", "z": "zgemv", "w": "wgemv"}
 _RNAME = {"s": "ssyr2", "d": "dsyr2", "c": "cher2", "z": "zher2", "w": "wsyr2"}
 _TNAME = {"s": "strmv", "d": "dtrmv", "c": "ctrmv", "z": "ztrmv", "w": "wtrmv"}
+_SHNAME = {"s": "ssymv_shard", "d": "dsymv_shard", "c": "chemv_shard", "z": "zhemv_shard",
+           "w": "wsymv_shard"}
 _NP = {"s": np.float32, "d": np.float64, "c": np.complex64, "z": np.complex128,
        "w": np.float64}
 
@@ -84,6 +86,15 @@ def _declare(lib):
         f = getattr(lib, "oracle_" + nm)
         f.restype = ci
         f.argtypes = [ctypes.c_char, ctypes.c_char, ctypes.c_char, ci, vp, ci, vp, ci]
+    for p, nm in _SHNAME.items():
+        f = getattr(lib, "oracle_" + nm)
+        f.restype = ci
+        f.argtypes = [ctypes.c_char, ci, ci, ci, ci, vp, ci, vp, ci, vp]
+        f = getattr(lib, f"oracle_{p}combine")
+        f.restype = ci
+        f.argtypes = [ci, ci, _SCALAR[p], vp, ci, _SCALAR[p], vp, ci]
+    lib.oracle_shard_columns.restype = ci
+    lib.oracle_shard_columns.argtypes = [ci, ci, ci, ci, vp]
     for nm in ("oracle_dd_add", "oracle_dd_mul"):
         f = getattr(lib, nm)
         f.restype = _DD
@@ -238,6 +249,31 @@ class OracleLib:
             raise ValueError(f"oracle trmv call failed with status {rc}")
         return x
 
+    def shard_columns(self, n: int, panel: int, nshards: int, shard: int) -> np.ndarray:
+        """The shard's global columns, ascending."""
+        k = self._lib.oracle_shard_columns(n, panel, nshards, shard, None)
+        if k < 0:
+            raise ValueError("bad shard arguments")
+        cols = np.zeros(max(k, 1), dtype=np.int32)
+        self._lib.oracle_shard_columns(n, panel, nshards, shard, _ptr(cols))
+        return cols[:k]
+
+    def shard(self, prec: str, uplo: str, n: int, panel: int, nshards: int, shard: int, Aloc,
+              lda: int, x, incx: int, p) -> int:
+        """p := the shard's partial product (n elements, contiguous); returns
+        the status code."""
+        _check_dtype(prec, Aloc, x, p)
+        f = getattr(self._lib, "oracle_" + _SHNAME[prec])
+        return f(_uplo(uplo), n, panel, nshards, shard, _ptr(Aloc), lda, _ptr(x), incx, _ptr(p))
+
+    def combine(self, prec: str, n: int, nshards: int, alpha, P, ldp: int, beta, y,
+                incy: int) -> int:
+        """y := beta*y + alpha*(P_0 + P_1 + ...) in place; returns the status."""
+        _check_dtype(prec, P, y)
+        f = getattr(self._lib, f"oracle_{prec}combine")
+        return f(n, nshards, scalar(prec, alpha), _ptr(P), ldp, scalar(prec, beta), _ptr(y),
+                 incy)
+
     def dd_add(self, a, b):
         r = self._lib.oracle_dd_add(_DD(*a), _DD(*b))
         return (r.hi, r.lo)
@@ -316,3 +352,15 @@ def trmv(*a, **k):
 
 def trmv_problem(p, x=None):
     return default().trmv_problem(p, x)
+
+
+def shard_columns(*a, **k):
+    return default().shard_columns(*a, **k)
+
+
+def shard(*a, **k):
+    return default().shard(*a, **k)
+
+
+def combine(*a, **k):
+    return default().combine(*a, **k)

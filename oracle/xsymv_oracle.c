@@ -54,6 +54,22 @@
  * definition: the sum over the inner index k ascending of op(T)(i,k)*x(k),
  * in the working precision; all outputs are formed before x is overwritten.
  *
+ * One GPU's share of the product (the path sharded over several GPUs with
+ * one exchange; the report's §5 points to multi-GPU SYMV, ref. [7]).  The
+ * columns are cut into panels of `panel` consecutive columns (the last one
+ * may be short); the panels are dealt to `nshards` shards round by round, in
+ * even rounds shard g taking the round's g-th panel and in odd rounds its
+ * (nshards-1-g)-th (boustrophedon order, so the shards' triangle areas stay
+ * close).  A shard keeps only its own columns, in ascending order, as a local
+ * column-major matrix.  Its partial vector is, from the definition,
+ *   p := 0; for every owned column j and every stored A(i,j):
+ *     i == j: p(j) += S(j,j)*x(j);
+ *     else:   p(i) += A(i,j)*x(j) and p(j) += conj(A(i,j))*x(i),
+ * so that the shards' partials add up to S*x.  The exchange then gives every
+ * GPU all partials, and y(i) := beta*y(i) + alpha*(p_0(i) + p_1(i) + ...),
+ * summed in rank order (the report's fixed summation order, §2.1, kept
+ * across GPUs), with the BLAS rules for beta == 0 and alpha == 0.
+ *
  * Double-double arithmetic (report §2.2, which takes Bailey's double-double
  * format [14]: a value is the unevaluated sum hi + lo of two doubles):
  *   TwoSum (Knuth) and FastTwoSum (Dekker) give a sum and its exact error;
@@ -587,3 +603,120 @@ DEFINE_TRMV(oracle_dtrmv, double, d)
 DEFINE_TRMV(oracle_ctrmv, ocplx_f, c)
 DEFINE_TRMV(oracle_ztrmv, ocplx_d, z)
 DEFINE_TRMV(oracle_wtrmv, odd, w)
+
+/* ------------------------------------------------- one shard's partial */
+
+/* Shard that owns panel q: rounds of nshards panels, boustrophedon order. */
+static int panel_owner(int q, int nshards)
+{
+    int round = q / nshards, pos = q % nshards;
+    return round % 2 == 0 ? pos : nshards - 1 - pos;
+}
+
+/* Global columns of a shard, ascending; returns their count (cols may be
+ * NULL to count only). */
+int oracle_shard_columns(int n, int panel, int nshards, int shard, int *cols)
+{
+    int j, count = 0;
+    if (n < 0 || panel <= 0 || nshards <= 0 || shard < 0 || shard >= nshards) return -1;
+    for (j = 0; j < n; ++j)
+        if (panel_owner(j / panel, nshards) == shard) {
+            if (cols) cols[count] = j;
+            ++count;
+        }
+    return count;
+}
+
+/* Argument checks: uplo, n, panel, nshards, shard, A, lda, x, incx, p. */
+static int shard_check(char uplo, int n, int panel, int nshards, int shard, const void *A,
+                       int lda, const void *x, int incx, const void *p, int *upper)
+{
+    if (uplo == 'U' || uplo == 'u')
+        *upper = 1;
+    else if (uplo == 'L' || uplo == 'l')
+        *upper = 0;
+    else
+        return -1;
+    if (n < 0) return -2;
+    if (panel <= 0) return -3;
+    if (nshards <= 0) return -4;
+    if (shard < 0 || shard >= nshards) return -5;
+    if (n > 0 && A == NULL && oracle_shard_columns(n, panel, nshards, shard, NULL) > 0)
+        return -6;
+    if (lda < (n > 1 ? n : 1)) return -7;
+    if (n > 0 && x == NULL) return -8;
+    if (incx == 0) return -9;
+    if (n > 0 && p == NULL) return -10;
+    return 0;
+}
+
+#define DEFINE_SHARD(NAME, T, P)                                                \
+int NAME(char uplo, int n, int panel, int nshards, int shard, const T *Aloc,   \
+         int lda, const T *x, int incx, T *p)                                  \
+{                                                                              \
+    int upper, i, j, l = 0;                                                    \
+    int rc = shard_check(uplo, n, panel, nshards, shard, Aloc, lda, x, incx, p, \
+                         &upper);                                              \
+    if (rc) return rc;                                                         \
+    for (i = 0; i < n; ++i) p[i] = P##_zero();                                 \
+    for (j = 0; j < n; ++j) {                                                  \
+        int lo, hi;                                                            \
+        T xj;                                                                  \
+        if (panel_owner(j / panel, nshards) != shard) continue;                \
+        xj = x[vpos(n, incx, j)];                                              \
+        lo = upper ? 0 : j;                                                    \
+        hi = upper ? j + 1 : n;                                                \
+        for (i = lo; i < hi; ++i) {                                            \
+            const T *ap = &Aloc[(long long)i + (long long)l * lda];            \
+            if (i == j) {                                                      \
+                p[j] = P##_add(p[j], P##_mul(P##_diag(ap), xj));               \
+            } else {                                                           \
+                T xi = x[vpos(n, incx, i)];                                    \
+                p[i] = P##_add(p[i], P##_mul(*ap, xj));                        \
+                p[j] = P##_add(p[j], P##_mul(P##_conj(*ap), xi));              \
+            }                                                                  \
+        }                                                                      \
+        ++l;                                                                   \
+    }                                                                          \
+    return 0;                                                                  \
+}
+
+DEFINE_SHARD(oracle_ssymv_shard, float, s)
+DEFINE_SHARD(oracle_dsymv_shard, double, d)
+DEFINE_SHARD(oracle_chemv_shard, ocplx_f, c)
+DEFINE_SHARD(oracle_zhemv_shard, ocplx_d, z)
+DEFINE_SHARD(oracle_wsymv_shard, odd, w)
+
+/* y := beta*y + alpha*(P_0 + P_1 + ... ), the partials summed in rank order.
+ * Checks: n, nshards, P, ldp, y, incy. */
+#define DEFINE_COMBINE(NAME, T, P)                                              \
+int NAME(int n, int nshards, T alpha, const T *Pp, int ldp, T beta, T *y,      \
+         int incy)                                                             \
+{                                                                              \
+    int i, g;                                                                  \
+    if (n < 0) return -1;                                                      \
+    if (nshards <= 0) return -2;                                               \
+    if (n > 0 && Pp == NULL) return -4;                                        \
+    if (ldp < (n > 1 ? n : 1)) return -5;                                      \
+    if (n > 0 && y == NULL) return -7;                                         \
+    if (incy == 0) return -8;                                                  \
+    if (n == 0 || (P##_is_zero(alpha) && P##_is_one(beta))) return 0;          \
+    for (i = 0; i < n; ++i) {                                                  \
+        T *yi = &y[vpos(n, incy, i)];                                          \
+        T r = P##_is_zero(beta) ? P##_zero() : P##_mul(beta, *yi);             \
+        if (!P##_is_zero(alpha)) {                                             \
+            T sum = Pp[i];                                                     \
+            for (g = 1; g < nshards; ++g)                                      \
+                sum = P##_add(sum, Pp[(long long)g * ldp + i]);                \
+            r = P##_add(r, P##_mul(alpha, sum));                               \
+        }                                                                      \
+        *yi = r;                                                               \
+    }                                                                          \
+    return 0;                                                                  \
+}
+
+DEFINE_COMBINE(oracle_scombine, float, s)
+DEFINE_COMBINE(oracle_dcombine, double, d)
+DEFINE_COMBINE(oracle_ccombine, ocplx_f, c)
+DEFINE_COMBINE(oracle_zcombine, ocplx_d, z)
+DEFINE_COMBINE(oracle_wcombine, odd, w)

@@ -142,6 +142,41 @@ int oracle_ztrmv(char uplo, char trans, char diag, int n, const ocplx_d *A, int 
 int oracle_wtrmv(char uplo, char trans, char diag, int n, const odd *A, int lda,
                  odd *x, int incx);
 
+/* One shard's partial product and the rank-ordered combination (the path
+ * sharded over several GPUs).  Panels of `panel` columns are dealt to
+ * `nshards` shards round by round in boustrophedon order; Aloc holds the
+ * shard's columns in ascending order (stride lda).  p (n elements,
+ * contiguous) := the shard's share of S*x: every stored element of an owned
+ * column taken in both roles, the diagonal once.  Codes: -1 uplo, -2 n,
+ * -3 panel <= 0, -4 nshards <= 0, -5 shard out of range, -6 Aloc NULL,
+ * -7 lda, -8 x NULL, -9 incx == 0, -10 p NULL.
+ * oracle_Xcombine: y := beta*y + alpha*(P[0] + P[1] + ...), partial g at
+ * P + g*ldp, summed in ascending g; codes -1 n, -2 nshards, -4 P NULL,
+ * -5 ldp, -7 y NULL, -8 incy == 0.
+ * oracle_shard_columns: the shard's global columns, ascending (cols may be
+ * NULL); returns their count, or -1 for bad arguments. */
+int oracle_shard_columns(int n, int panel, int nshards, int shard, int *cols);
+int oracle_ssymv_shard(char uplo, int n, int panel, int nshards, int shard, const float *Aloc,
+                       int lda, const float *x, int incx, float *p);
+int oracle_dsymv_shard(char uplo, int n, int panel, int nshards, int shard, const double *Aloc,
+                       int lda, const double *x, int incx, double *p);
+int oracle_chemv_shard(char uplo, int n, int panel, int nshards, int shard, const ocplx_f *Aloc,
+                       int lda, const ocplx_f *x, int incx, ocplx_f *p);
+int oracle_zhemv_shard(char uplo, int n, int panel, int nshards, int shard, const ocplx_d *Aloc,
+                       int lda, const ocplx_d *x, int incx, ocplx_d *p);
+int oracle_wsymv_shard(char uplo, int n, int panel, int nshards, int shard, const odd *Aloc,
+                       int lda, const odd *x, int incx, odd *p);
+int oracle_scombine(int n, int nshards, float alpha, const float *P, int ldp, float beta,
+                    float *y, int incy);
+int oracle_dcombine(int n, int nshards, double alpha, const double *P, int ldp, double beta,
+                    double *y, int incy);
+int oracle_ccombine(int n, int nshards, ocplx_f alpha, const ocplx_f *P, int ldp, ocplx_f beta,
+                    ocplx_f *y, int incy);
+int oracle_zcombine(int n, int nshards, ocplx_d alpha, const ocplx_d *P, int ldp, ocplx_d beta,
+                    ocplx_d *y, int incy);
+int oracle_wcombine(int n, int nshards, odd alpha, const odd *P, int ldp, odd beta, odd *y,
+                    int incy);
+
 /* The double-double primitives, exported so that the tests can pin them
  * one by one against exact rational arithmetic. */
 odd oracle_dd_add(odd a, odd b);

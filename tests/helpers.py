@@ -553,3 +553,89 @@ def trmv_integer_expected(p):
         r[:, 0] = (Mi @ np.rint(p.x[xi, 0]).astype(np.int64)).astype(np.float64)
         return r
     return (Mi @ np.rint(p.x[xi]).astype(np.int64)).astype(p.x.dtype)
+
+
+# ------------------------------------------------- sharded product (one GPU's share)
+
+def panel_owner_def(q: int, nshards: int) -> int:
+    """Shard owning panel q: rounds of nshards panels, dealt forward in even
+    rounds and backward in odd ones."""
+    rnd, pos = divmod(q, nshards)
+    return pos if rnd % 2 == 0 else nshards - 1 - pos
+
+
+def shard_columns_def(n: int, panel: int, nshards: int, shard: int) -> np.ndarray:
+    return np.array([j for j in range(n) if panel_owner_def(j // panel, nshards) == shard],
+                    dtype=np.int64)
+
+
+def local_matrix(p, cols) -> np.ndarray:
+    """The shard's local matrix: columns ``cols`` of A (all lda rows each),
+    in order."""
+    lda = p.lda
+    idx = (np.asarray(cols, dtype=np.int64)[:, None] * lda +
+           np.arange(lda, dtype=np.int64)[None, :]).reshape(-1)
+    return np.ascontiguousarray(p.A[idx])
+
+
+def shard_exact(p, nshards, panel, shard):
+    """Exact partial of a shard, row by row over the full symmetric S: entry
+    S(i,j) belongs to the shard owning the column of the stored element that
+    represents it ((i,j) if stored, else (j,i))."""
+    n = p.n
+    get = exact_elements(p)
+    cplx = p.prec in ("c", "z")
+    x = exact_vector(p, p.x, p.incx)
+    zero = (Fraction(0), Fraction(0)) if cplx else Fraction(0)
+    out = []
+    for i in range(n):
+        s = zero
+        for j in range(n):
+            col = j if stored(p.uplo, i, j) else i
+            if panel_owner_def(col // panel, nshards) != shard:
+                continue
+            if i == j:
+                a = get(i, i)
+                if cplx:
+                    a = (a[0], Fraction(0))
+            elif stored(p.uplo, i, j):
+                a = get(i, j)
+            else:
+                a = get(j, i)
+                if cplx:
+                    a = (a[0], -a[1])
+            s = _cadd(s, _cmul(a, x[j])) if cplx else s + a * x[j]
+        out.append(s)
+    return out
+
+
+def shard_mask(p, nshards, panel, shard) -> np.ndarray:
+    """0/1 mask of the entries of S that belong to the shard."""
+    n = p.n
+    i, j = np.meshgrid(np.arange(n), np.arange(n), indexing="ij")
+    st = (i <= j) if is_upper(p.uplo) else (i >= j)
+    col = np.where(st, j, i)
+    own = np.array([panel_owner_def(c // panel, nshards) for c in range(n)])
+    return own[col] == shard
+
+
+def shard_tolerance(p, nshards, panel, shard):
+    """4*n*eps*(|S_g||x|)_i, S_g the shard's entries of S."""
+    M = np.abs(dense_matrix(p)) * shard_mask(p, nshards, panel, shard)
+    x = _magnitude(p, p.x[vec_index(p.n, p.incx)])
+    return 4.0 * max(p.n, 1) * EPS[p.prec] * (M @ x)
+
+
+def exact_value_errors(prec, got, exact):
+    """|got_k - exact_k| for a contiguous vector against exact values."""
+    errs = np.empty(len(exact))
+    for k, e in enumerate(exact):
+        if prec == "w":
+            v = Fraction(float(got[k, 0])) + Fraction(float(got[k, 1]))
+            errs[k] = abs(float(v - e))
+        elif prec in ("c", "z"):
+            errs[k] = abs(complex(float(_frac(got[k].real) - e[0]),
+                                  float(_frac(got[k].imag) - e[1])))
+        else:
+            errs[k] = abs(float(_frac(got[k]) - e))
+    return errs

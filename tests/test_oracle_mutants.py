@@ -11,6 +11,7 @@ import oracle
 from tests import test_oracle_gemv as G
 from tests import test_oracle_syr2 as R2
 from tests import test_oracle_trmv as TM
+from tests import test_oracle_shard as SH
 from tests import test_oracle_pins as P
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "xsymv_oracle.c")
@@ -103,6 +104,24 @@ MUTANTS = [
      "if (r == c && unit) {", "if (0 && unit) {", None),
     ("trmv: x overwritten while outputs are formed",
      "out[i] = sum;", "out[i] = sum; x[vpos(n, incx, i)] = sum;", None),
+    ("shard: panels dealt cyclically, not back and forth",
+     "return round % 2 == 0 ? pos : nshards - 1 - pos;", "(void)round; return pos;", None),
+    ("shard: column role dropped",
+     "p[j] = P##_add(p[j], P##_mul(P##_conj(*ap), xi));", "(void)xi;", None),
+    ("shard: column role without conjugate",
+     "p[j] = P##_add(p[j], P##_mul(P##_conj(*ap), xi));",
+     "p[j] = P##_add(p[j], P##_mul(*ap, xi));", None),
+    ("shard: diagonal counted twice",
+     "p[j] = P##_add(p[j], P##_mul(P##_diag(ap), xj));",
+     "p[j] = P##_add(p[j], P##_mul(P##_add(P##_diag(ap), P##_diag(ap)), xj));", None),
+    ("shard: local column index not advanced",
+     "        ++l;                                                                   \\",
+     "                                                                               \\", None),
+    ("combine: partials summed out of rank order",
+     "for (g = 1; g < nshards; ++g)", "for (g = nshards - 1; g >= 1; --g)", None),
+    ("combine: beta = 0 multiplies y",
+     "T r = P##_is_zero(beta) ? P##_zero() : P##_mul(beta, *yi);",
+     "T r = P##_mul(beta, *yi);", None),
     ("gemv: x walked with y's increment",
      "sum = P##_add(sum, P##_mul(a, x[vpos(lenx, incx, k)]));",
      "sum = P##_add(sum, P##_mul(a, x[vpos(lenx, 1, k)]));", None),
@@ -137,6 +156,11 @@ BATTERY = [
                                      for d in "NU"]),
     (TM.test_trmv_unit_diagonal_not_read, [dict(prec=pr, uplo=u, trans=t)
                                            for pr in TM.PRECS for u in "LU" for t in TM.TRANS]),
+    (SH.test_shard_columns_definition, [dict(n=37, panel=4, nshards=3)]),
+    (SH.test_shard_exact_bruteforce, [dict(prec=pr, uplo=u, n=13, pad=1, panel=2, nshards=4)
+                                      for pr in SH.PRECS for u in "LU"]),
+    (SH.test_combine_sums_in_rank_order, [dict()]),
+    (SH.test_combine_zero_scalars, [dict(prec=pr) for pr in SH.PRECS]),
 ]
 
 
