@@ -22,6 +22,9 @@ Printed as one JSON line, with:
                 written once;
   s/d/z/wtrmv   the triangular product x := op(T)*x (n = 32768 real, 16384
                 complex and double-double), its bytes the triangle read once;
+  ...-8shards   one GPU's share of the product sharded over 8 GPUs (panels
+                of 256 columns): every shard in turn, the slowest reported,
+                and the rank-ordered combination of the 8 partials;
   symv_over_gemv_time  the symmetric call's time over the general one's on
                 the same order (GEMV detail rows: SGEMV 'N' and 'T', DGEMV
                 'N', n = 32768) -- the report's claim that SYMV, reading one
@@ -249,6 +252,87 @@ def measure_trmv_detail(name, p, reps, read_peak=None):
     if read_peak:
         out["pct_measured_read_peak"] = round(100 * b / t_call / 1e9 / read_peak, 1)
     del A
+    torch.cuda.empty_cache()
+    return out
+
+
+def measure_shard_detail(name, p, panel, nshards, reps, read_peak=None):
+    """One GPU's share of the sharded product at its real shape: every
+    shard's call (kernel + ordered merge) on this GPU in turn, its bytes the
+    shard's stored elements, x read and the partial written; then the
+    rank-ordered combination of the partials.  The exchange between GPUs is
+    not measured (one GPU)."""
+    from blas_symmetric_mat_amd import roofline as R
+    import numpy as np
+    import torch
+    import blas_symmetric_mat_amd as X
+    log(f"detail: {name}")
+    es = R.ELEM_BYTES[p.prec]
+    n = p.n
+    x = torch.from_numpy(np.ascontiguousarray(p.x)).to("cuda")
+    width = 2 if p.prec == "w" else 1
+    P = torch.empty((nshards * n * width,), dtype=x.dtype, device="cuda")
+    f = getattr(X, {"s": "xsymv_shard_s", "d": "xsymv_shard_d", "c": "xhemv_shard_c",
+                    "z": "xhemv_shard_z", "w": "xsymv_shard_w"}[p.prec])
+    shards = []
+    for g in range(nshards):
+        cols = X.shard_columns(n, panel, nshards, g)
+        idx = (np.asarray(cols, dtype=np.int64)[:, None] * p.lda +
+               np.arange(p.lda, dtype=np.int64)[None, :]).reshape(-1)
+        Aloc = torch.from_numpy(np.ascontiguousarray(p.A[idx])).to("cuda")
+        out = P[g * n * width:(g + 1) * n * width]
+
+        class _D:
+            def call(self):
+                f(p.uplo, n, panel, nshards, g, Aloc, p.lda, x, 1, out)
+
+        d = _D()
+        for _ in range(2):
+            d.call()
+        rec = time_kernels(d, reps)
+        main = sorted(r[0] for r in rec)
+        tot = sorted(r[0] + r[1] for r in rec)
+        stored = sum((c + 1) if p.uplo in ("U", "u") else (n - c) for c in cols)
+        shards.append({"shard": g, "columns": len(cols), "stored_elements": stored,
+                       "ms_per_call_median": round(tot[len(tot) // 2], 4),
+                       "kernel_ms_median": round(main[len(main) // 2], 4),
+                       "bytes": es * (stored + 2 * n)})
+        del Aloc
+        torch.cuda.empty_cache()
+    slow = max(shards, key=lambda r: r["ms_per_call_median"])
+    t = slow["ms_per_call_median"] * 1e-3
+    # the rank-ordered combination of the partials
+    y = torch.zeros_like(x)
+    cb = getattr(X, {"s": "xsymv_combine_s", "d": "xsymv_combine_d", "c": "xhemv_combine_c",
+                     "z": "xhemv_combine_z", "w": "xsymv_combine_w"}[p.prec])
+    one = (1.0, 0.0) if p.prec == "w" else 1.0
+    for _ in range(2):
+        cb(n, nshards, one, P, n, one, y, 1)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record()
+        cb(n, nshards, one, P, n, one, y, 1)
+        e1.record()
+    torch.cuda.synchronize()
+    cms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)[reps // 2]
+    out = {"prec": p.prec, "uplo": p.uplo, "n": n, "panel": panel, "shards": nshards,
+           "kernel": (f"symv_strip<{CTYPE[p.prec]}, {'upper' if p.uplo == 'U' else 'lower'}, "
+                      f"..., shard> + ordered merge"),
+           "slowest_shard": slow["shard"],
+           "ms_per_call_median": slow["ms_per_call_median"],
+           "hbm_gbps_algorithmic": round(slow["bytes"] / t / 1e9, 1),
+           "pct_peak_hbm": round(100 * slow["bytes"] / t / 1e9 / R.HBM_PEAK_GBPS, 1),
+           "stored_elements_min_max": [min(r["stored_elements"] for r in shards),
+                                       max(r["stored_elements"] for r in shards)],
+           "combine_ms_median": round(cms, 4),
+           "per_shard_ms": [r["ms_per_call_median"] for r in shards],
+           "bytes": "the shard's stored elements, x read, its partial written",
+           "exchange": "not measured (one GPU)", "calls": reps}
+    if read_peak:
+        out["pct_measured_read_peak"] = round(100 * slow["bytes"] / t / 1e9 / read_peak, 1)
+    del P, x
     torch.cuda.empty_cache()
     return out
 
@@ -607,6 +691,9 @@ def main():
                 ("wtrmv-U-N-n16384",
                  lambda: W.make_trmv_problem("w", "U", "N", "N", 16384, seed=16384))]:
             detail[name] = measure_trmv_detail(name, make(), args.detail_reps, rd_med)
+        for name, make in [("ssymv-L-n32768-8shards", lambda: W.symv_sweep("s", "L", 32768)),
+                           ("dsymv-U-n32768-8shards", lambda: W.symv_sweep("d", "U", 32768))]:
+            detail[name] = measure_shard_detail(name, make(), 256, 8, args.detail_reps, rd_med)
         out["detail"] = detail
         # the report's point: SYMV reads half the bytes of GEMV on the same
         # order, so takes about half the time

@@ -29,7 +29,10 @@ __all__ = ["xsymv_s", "xsymv_d", "xhemv_c", "xhemv_z", "xsymv_w", "XsymvError",
            "xsyr2_w", "syr2_num_configs", "syr2_config_info", "syr2_select_config",
            "syr2_current_config", "xtrmv_s", "xtrmv_d", "xtrmv_c", "xtrmv_z", "xtrmv_w",
            "trmv_num_configs", "trmv_config_info", "trmv_select_config", "trmv_current_config",
-           "trmv_workspace_bytes"]
+           "trmv_workspace_bytes", "xsymv_shard_s", "xsymv_shard_d", "xhemv_shard_c",
+           "xhemv_shard_z", "xsymv_shard_w", "xsymv_combine_s", "xsymv_combine_d",
+           "xhemv_combine_c", "xhemv_combine_z", "xsymv_combine_w", "shard_columns", "shard_plan",
+           "shard_workspace_bytes"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libxsymv.so")
 PREC_CODE = {"s": 0, "d": 1, "c": 2, "z": 3, "w": 4}
@@ -64,6 +67,10 @@ _ENTRY = {"s": "xsymv_s", "d": "xsymv_d", "c": "xhemv_c", "z": "xhemv_z", "w": "
 _GENTRY = {"s": "xgemv_s", "d": "xgemv_d", "c": "xgemv_c", "z": "xgemv_z", "w": "xgemv_w"}
 _RENTRY = {"s": "xsyr2_s", "d": "xsyr2_d", "c": "xher2_c", "z": "xher2_z", "w": "xsyr2_w"}
 _TENTRY = {"s": "xtrmv_s", "d": "xtrmv_d", "c": "xtrmv_c", "z": "xtrmv_z", "w": "xtrmv_w"}
+_SHENTRY = {"s": "xsymv_shard_s", "d": "xsymv_shard_d", "c": "xhemv_shard_c",
+            "z": "xhemv_shard_z", "w": "xsymv_shard_w"}
+_CBENTRY = {"s": "xsymv_combine_s", "d": "xsymv_combine_d", "c": "xhemv_combine_c",
+            "z": "xhemv_combine_z", "w": "xsymv_combine_w"}
 
 _lib = None
 _lock = threading.Lock()
@@ -98,6 +105,21 @@ def library():
                 f = getattr(lib, nm)
                 f.restype = ci
                 f.argtypes = [cc, cc, cc, ci, vp, ci, vp, ci, vp]
+            for p, nm in _SHENTRY.items():
+                f = getattr(lib, nm)
+                f.restype = ci
+                f.argtypes = [cc, ci, ci, ci, ci, vp, ci, vp, ci, vp, vp]
+            for p, nm in _CBENTRY.items():
+                f = getattr(lib, nm)
+                f.restype = ci
+                f.argtypes = [ci, ci, _SCALAR[p], vp, ci, _SCALAR[p], vp, ci, vp]
+            lib.xsymv_shard_plan.restype = ci
+            lib.xsymv_shard_plan.argtypes = [cc, ci, ci, ci, ci, ci, ci, ci, vp, ci, vp, vp, vp,
+                                             ci]
+            lib.xsymv_shard_columns.restype = ci
+            lib.xsymv_shard_columns.argtypes = [ci, ci, ci, ci, vp]
+            lib.xsymv_shard_workspace_bytes.restype = ctypes.c_size_t
+            lib.xsymv_shard_workspace_bytes.argtypes = [ci, cc, ci, ci, ci, ci]
             lib.xtrmv_num_configs.restype = ci
             lib.xtrmv_num_configs.argtypes = [ci]
             lib.xtrmv_config_info.restype = ci
@@ -331,6 +353,111 @@ def xtrmv_z(uplo, trans, diag, n, A, lda, x, incx, stream=None):
 def xtrmv_w(uplo, trans, diag, n, A, lda, x, incx, stream=None):
     """WTRMV: double-double (hi, lo) pairs."""
     _tcall("w", uplo, trans, diag, n, A, lda, x, incx, stream)
+
+
+def _shcall(prec, uplo, n, panel, nshards, shard, Aloc, lda, x, incx, p, stream):
+    f = getattr(library(), _SHENTRY[prec])
+    rc = f(_ch(uplo), n, panel, nshards, shard, _addr(Aloc), lda, _addr(x), incx, _addr(p),
+           _stream(stream))
+    if rc != 0:
+        raise XsymvError(_SHENTRY[prec], rc)
+
+
+def xsymv_shard_s(uplo, n, panel, nshards, shard, Aloc, lda, x, incx, p, stream=None):
+    """One shard's share p of S*x (float32): its own panels of columns, held
+    as the local matrix Aloc, each stored element in both roles."""
+    _shcall("s", uplo, n, panel, nshards, shard, Aloc, lda, x, incx, p, stream)
+
+
+def xsymv_shard_d(uplo, n, panel, nshards, shard, Aloc, lda, x, incx, p, stream=None):
+    """float64."""
+    _shcall("d", uplo, n, panel, nshards, shard, Aloc, lda, x, incx, p, stream)
+
+
+def xhemv_shard_c(uplo, n, panel, nshards, shard, Aloc, lda, x, incx, p, stream=None):
+    """complex64, Hermitian."""
+    _shcall("c", uplo, n, panel, nshards, shard, Aloc, lda, x, incx, p, stream)
+
+
+def xhemv_shard_z(uplo, n, panel, nshards, shard, Aloc, lda, x, incx, p, stream=None):
+    """complex128, Hermitian."""
+    _shcall("z", uplo, n, panel, nshards, shard, Aloc, lda, x, incx, p, stream)
+
+
+def xsymv_shard_w(uplo, n, panel, nshards, shard, Aloc, lda, x, incx, p, stream=None):
+    """double-double."""
+    _shcall("w", uplo, n, panel, nshards, shard, Aloc, lda, x, incx, p, stream)
+
+
+def _cbcall(prec, n, nshards, alpha, P, ldp, beta, y, incy, stream):
+    f = getattr(library(), _CBENTRY[prec])
+    rc = f(n, nshards, _scalar(prec, alpha), _addr(P), ldp, _scalar(prec, beta), _addr(y), incy,
+           _stream(stream))
+    if rc != 0:
+        raise XsymvError(_CBENTRY[prec], rc)
+
+
+def xsymv_combine_s(n, nshards, alpha, P, ldp, beta, y, incy, stream=None):
+    """y := beta*y + alpha*(P[0] + ... + P[nshards-1]) in rank order, float32."""
+    _cbcall("s", n, nshards, alpha, P, ldp, beta, y, incy, stream)
+
+
+def xsymv_combine_d(n, nshards, alpha, P, ldp, beta, y, incy, stream=None):
+    """float64."""
+    _cbcall("d", n, nshards, alpha, P, ldp, beta, y, incy, stream)
+
+
+def xhemv_combine_c(n, nshards, alpha, P, ldp, beta, y, incy, stream=None):
+    """complex64."""
+    _cbcall("c", n, nshards, alpha, P, ldp, beta, y, incy, stream)
+
+
+def xhemv_combine_z(n, nshards, alpha, P, ldp, beta, y, incy, stream=None):
+    """complex128."""
+    _cbcall("z", n, nshards, alpha, P, ldp, beta, y, incy, stream)
+
+
+def xsymv_combine_w(n, nshards, alpha, P, ldp, beta, y, incy, stream=None):
+    """double-double; alpha, beta are (hi, lo) tuples."""
+    _cbcall("w", n, nshards, alpha, P, ldp, beta, y, incy, stream)
+
+
+def shard_columns(n: int, panel: int, nshards: int, shard: int):
+    """Global columns of a shard (ascending), as a list."""
+    lib = library()
+    k = lib.xsymv_shard_columns(n, panel, nshards, shard, None)
+    if k < 0:
+        raise ValueError("bad shard arguments")
+    buf = (ctypes.c_int * max(k, 1))()
+    lib.xsymv_shard_columns(n, panel, nshards, shard, buf)
+    return list(buf[:k])
+
+
+def shard_plan(uplo: str, n: int, R: int, G: int, split: int, panel: int, nshards: int,
+               shard: int):
+    """One shard's work split (host computation): (blocks [k x 4],
+    strip_base [NS+1], seg_base [NS+1], col0 [NS])."""
+    import numpy as np
+    ns = (n + R - 1) // R
+    blocks = np.zeros((G, 4), dtype=np.int32)
+    sb = np.zeros(ns + 1, dtype=np.int32)
+    segb = np.zeros(ns + 1, dtype=np.int32)
+    c0 = np.zeros(ns + 1, dtype=np.int32)
+    k = library().xsymv_shard_plan(_ch(uplo), n, R, G, split, panel, nshards, shard,
+                                   blocks.ctypes.data, G, sb.ctypes.data, segb.ctypes.data,
+                                   c0.ctypes.data, ns + 1)
+    if k < 0:
+        raise ValueError(f"xsymv_shard_plan failed ({k})")
+    return blocks[:k], sb, segb, c0[:ns]
+
+
+def shard_workspace_bytes(prec: str, uplo: str, n: int, panel: int, nshards: int,
+                          shard: int) -> int:
+    v = library().xsymv_shard_workspace_bytes(PREC_CODE[prec], _ch(uplo), n, panel, nshards,
+                                              shard)
+    if v == ctypes.c_size_t(-1).value:
+        raise XsymvError("xsymv_shard_workspace_bytes", 1000)
+    return v
 
 
 def trmv_num_configs(prec: str) -> int:

@@ -30,11 +30,14 @@ std::mutex g_dev_mu;
 using PlanKey = std::tuple<int, int, int, int, int>;  // upper, n, NB, R, device
 
 using StripKey = std::tuple<int, int, int, int, int>;  // upper, n, R, G, split
+// upper, n, R, G, split, panel, nshards, shard
+using ShardKey = std::tuple<int, int, int, int, int, int, int, int>;
 
 struct DeviceState {
     std::mutex mu;
     std::map<PlanKey, std::unique_ptr<Plan>> plans;
     std::map<StripKey, std::unique_ptr<StripPlan>> strip_plans;
+    std::map<ShardKey, std::unique_ptr<StripPlan>> shard_plans;
     std::map<std::tuple<int, int, int, int>, std::unique_ptr<StripPlan>> gemv_plans;  // m, n, R, G
     std::map<hipStream_t, Workspace> workspaces;
     std::map<std::pair<const void*, int>, int> resident;  // (kernel, threads) -> blocks
@@ -76,14 +79,31 @@ void build_plan_host(bool upper, int n, int NB, int R, std::vector<TileDesc>& ti
 
 void build_strip_plan_host(bool upper, int n, int R, int G, int split,
                            std::vector<StripBlock>& blocks, std::vector<int>& strip_base,
-                           std::vector<int>& seg_base, int& NS)
+                           std::vector<int>& seg_base, int& NS, const std::vector<int>* lcol,
+                           std::vector<int>* col0)
 {
     NS = (n + R - 1) / R;
     strip_base.assign(NS + 1, 0);
+    // first (local) column of each strip's sequence; global = local unless
+    // the columns are a shard's
+    std::vector<int> first(NS, 0);
     for (int i = 0; i < NS; ++i) {
-        const int width = upper ? n - i * R : std::min(n, (i + 1) * R);
+        int width, c0;
+        if (lcol == nullptr) {
+            width = upper ? n - i * R : std::min(n, (i + 1) * R);
+            c0 = upper ? i * R : 0;
+        } else {
+            // L: local columns with global index < (i+1)R; U: those >= iR
+            const int bound = upper ? i * R : std::min(n, (i + 1) * R);
+            const int below = (int)(std::lower_bound(lcol->begin(), lcol->end(), bound) -
+                                    lcol->begin());
+            width = upper ? (int)lcol->size() - below : below;
+            c0 = upper ? below : 0;
+        }
+        first[i] = c0;
         strip_base[i + 1] = strip_base[i] + width;
     }
+    if (col0) *col0 = first;
     const long long total_pos = strip_base[NS];
     // Cost of one column of a strip, plus a fixed per-column share OVH for
     // the reductions.  A workgroup's time per column is set mostly by its
@@ -99,9 +119,8 @@ void build_strip_plan_host(bool upper, int n, int R, int G, int split,
     long long pos = 0;
     for (int i = 0; i < NS; ++i) {
         const int rs0 = i * R, rs1 = std::min(n, rs0 + R), rows = rs1 - rs0;
-        const int cfirst = upper ? rs0 : 0;
         for (int t = 0; t < strip_base[i + 1] - strip_base[i]; ++t, ++pos) {
-            const int j = cfirst + t;
+            const int j = lcol ? (*lcol)[first[i] + t] : first[i] + t;  // global column
             const bool tri = upper ? (j < rs1) : (j >= rs0);
             long long c;
             if (split == 0) {
@@ -141,8 +160,11 @@ void build_strip_plan_host(bool upper, int n, int R, int G, int split,
             ++st;
         }
     }
-    for (int i = 0; i < NS; ++i) seg_base[i] = first_slot[i];
+    // A strip holding none of the sequence (a shard's strip with none of its
+    // columns) has no segment unless a range steps through it: its first
+    // slot is then the next strip's, so that it counts zero row partials.
     seg_base[NS] = slot;
+    for (int i = NS - 1; i >= 0; --i) seg_base[i] = first_slot[i] >= 0 ? first_slot[i] : seg_base[i + 1];
 }
 
 DeviceState* device_state(int dev)
@@ -380,6 +402,126 @@ int check_syr2_args(char uplo, int n, const void* x, int incx, const void* y, in
     if (incy == 0) return -7;
     if (n > 0 && A == nullptr) return -8;
     if (lda < std::max(1, n)) return -9;
+    return 0;
+}
+
+int shard_owner(int panel_index, int nshards)
+{
+    const int round = panel_index / nshards, pos = panel_index % nshards;
+    return (round & 1) ? nshards - 1 - pos : pos;
+}
+
+void shard_columns_host(int n, int panel, int nshards, int shard, std::vector<int>& cols)
+{
+    cols.clear();
+    const int npanels = (n + panel - 1) / panel;
+    for (int q = 0; q < npanels; ++q) {
+        if (shard_owner(q, nshards) != shard) continue;
+        const int c1 = std::min(n, (q + 1) * panel);
+        for (int c = q * panel; c < c1; ++c) cols.push_back(c);
+    }
+}
+
+int shard_column_count(int n, int panel, int nshards, int shard)
+{
+    int count = 0;
+    const int npanels = (n + panel - 1) / panel;
+    for (int q = 0; q < npanels; ++q)
+        if (shard_owner(q, nshards) == shard) count += std::min(n, (q + 1) * panel) - q * panel;
+    return count;
+}
+
+int check_shard_args(char uplo, int n, int panel, int nshards, int shard, const void* A, int lda,
+                     const void* x, int incx, const void* p, bool* upper, int* ncol)
+{
+    if (uplo == 'U' || uplo == 'u')
+        *upper = true;
+    else if (uplo == 'L' || uplo == 'l')
+        *upper = false;
+    else
+        return -1;
+    if (n < 0) return -2;
+    if (panel <= 0) return -3;
+    if (nshards <= 0) return -4;
+    if (shard < 0 || shard >= nshards) return -5;
+    *ncol = shard_column_count(n, panel, nshards, shard);
+    if (*ncol > 0 && A == nullptr) return -6;
+    if (lda < std::max(1, n)) return -7;
+    if (n > 0 && x == nullptr) return -8;
+    if (incx == 0) return -9;
+    if (n > 0 && p == nullptr) return -10;
+    return 0;
+}
+
+int check_combine_args(int n, int nshards, const void* P, int ldp, const void* y, int incy)
+{
+    if (n < 0) return -1;
+    if (nshards <= 0) return -2;
+    if (n > 0 && P == nullptr) return -4;
+    if (ldp < std::max(1, n)) return -5;
+    if (n > 0 && y == nullptr) return -7;
+    if (incy == 0) return -8;
+    return 0;
+}
+
+int get_shard_plan(DeviceState* ds, bool upper, int n, int R, int G, int split, int panel,
+                   int nshards, int shard, hipStream_t stream, const StripPlan** out)
+{
+    ShardKey key{upper ? 1 : 0, n, R, G, split, panel, nshards, shard};
+    auto it = ds->shard_plans.find(key);
+    if (it != ds->shard_plans.end()) {
+        *out = it->second.get();
+        return 0;
+    }
+    std::vector<int> cols, col0;
+    shard_columns_host(n, panel, nshards, shard, cols);
+    std::vector<int> gloc(n, -1);
+    for (size_t l = 0; l < cols.size(); ++l) gloc[cols[l]] = (int)l;
+    std::vector<StripBlock> blocks;
+    std::vector<int> sb, segb;
+    int NS = 0;
+    int g = G;
+    build_strip_plan_host(upper, n, R, g, split, blocks, sb, segb, NS, &cols, &col0);
+    std::unique_ptr<StripPlan> plan(new StripPlan());
+    plan->NS = NS;
+    plan->G = (int)blocks.size();
+    plan->nseg = segb[NS];
+    plan->R = R;
+    plan->ncol = (int)cols.size();
+    // one upload: blocks, strip_base, seg_base, col0, lcol, gloc
+    const size_t bb = blocks.size() * sizeof(StripBlock);
+    const size_t ib = sb.size() * sizeof(int);
+    const size_t cb = col0.size() * sizeof(int);
+    const size_t lb = cols.size() * sizeof(int);
+    const size_t gb = gloc.size() * sizeof(int);
+    const size_t total = bb + 2 * ib + cb + lb + gb;
+    char* h = nullptr;
+    XSYMV_HIP(hipHostMalloc((void**)&h, total, hipHostMallocDefault));
+    plan->h_pinned = h;
+    size_t off = 0;
+    std::copy(blocks.begin(), blocks.end(), reinterpret_cast<StripBlock*>(h + off));
+    const size_t o_sb = off += bb;
+    std::copy(sb.begin(), sb.end(), reinterpret_cast<int*>(h + off));
+    const size_t o_seg = off += ib;
+    std::copy(segb.begin(), segb.end(), reinterpret_cast<int*>(h + off));
+    const size_t o_c0 = off += ib;
+    std::copy(col0.begin(), col0.end(), reinterpret_cast<int*>(h + off));
+    const size_t o_l = off += cb;
+    std::copy(cols.begin(), cols.end(), reinterpret_cast<int*>(h + off));
+    const size_t o_g = off += lb;
+    std::copy(gloc.begin(), gloc.end(), reinterpret_cast<int*>(h + off));
+    char* d = nullptr;
+    XSYMV_HIP(hipMalloc((void**)&d, total));
+    XSYMV_HIP(hipMemcpyAsync(d, h, total, hipMemcpyHostToDevice, stream));
+    XSYMV_HIP(hipStreamSynchronize(stream));
+    plan->d_blocks = reinterpret_cast<StripBlock*>(d);
+    plan->d_strip_base = reinterpret_cast<int*>(d + o_sb);
+    plan->d_seg_base = reinterpret_cast<int*>(d + o_seg);
+    plan->d_col0 = reinterpret_cast<int*>(d + o_c0);
+    plan->d_lcol = reinterpret_cast<int*>(d + o_l);
+    plan->d_gloc = reinterpret_cast<int*>(d + o_g);
+    *out = plan.get();
+    ds->shard_plans[key] = std::move(plan);
     return 0;
 }
 
@@ -791,6 +933,11 @@ int xsymv_release(void)
         XSYMV_HIP(hipHostFree(kv.second->h_pinned));
     }
     ds->strip_plans.clear();
+    for (auto& kv : ds->shard_plans) {
+        XSYMV_HIP(hipFree(kv.second->d_blocks));
+        XSYMV_HIP(hipHostFree(kv.second->h_pinned));
+    }
+    ds->shard_plans.clear();
     for (auto& kv : ds->gemv_plans) {
         XSYMV_HIP(hipFree(kv.second->d_blocks));
         XSYMV_HIP(hipHostFree(kv.second->h_pinned));
@@ -1019,6 +1166,35 @@ int xsymv_strip_plan(char uplo, int n, int R, int G, int split, int* blocks4, in
     return (int)blocks.size();
 }
 
+int xsymv_shard_plan(char uplo, int n, int R, int G, int split, int panel, int nshards, int shard,
+                     int* blocks4, int max_blocks, int* strip_base, int* seg_base, int* col0,
+                     int max_strips)
+{
+    if (!(uplo == 'U' || uplo == 'u' || uplo == 'L' || uplo == 'l') || n <= 0 || R <= 0 ||
+        G <= 0 || split < 0 || split > 1 || panel <= 0 || nshards <= 0 || shard < 0 ||
+        shard >= nshards)
+        return -1;
+    std::vector<int> cols, c0;
+    shard_columns_host(n, panel, nshards, shard, cols);
+    if (cols.empty()) return 0;
+    std::vector<StripBlock> blocks;
+    std::vector<int> sb, segb;
+    int NS = 0;
+    build_strip_plan_host(uplo == 'U' || uplo == 'u', n, R, G, split, blocks, sb, segb, NS, &cols,
+                          &c0);
+    if ((int)blocks.size() > max_blocks || NS + 1 > max_strips) return -2;
+    for (size_t b = 0; b < blocks.size(); ++b) {
+        blocks4[4 * b + 0] = blocks[b].u0;
+        blocks4[4 * b + 1] = blocks[b].u1;
+        blocks4[4 * b + 2] = blocks[b].slot0;
+        blocks4[4 * b + 3] = blocks[b].strip0;
+    }
+    std::copy(sb.begin(), sb.end(), strip_base);
+    std::copy(segb.begin(), segb.end(), seg_base);
+    std::copy(c0.begin(), c0.end(), col0);
+    return (int)blocks.size();
+}
+
 int xgemv_num_configs(int prec)
 {
     switch (prec) {
@@ -1227,6 +1403,27 @@ size_t xtrmv_workspace_bytes(int prec, char uplo, char trans, int n)
     case XSYMV_C: return trmv_ws_bytes<cf32>(uplo, trans, n);
     case XSYMV_Z: return trmv_ws_bytes<cf64>(uplo, trans, n);
     case XSYMV_W: return trmv_ws_bytes<ddreal>(uplo, trans, n);
+    default: return (size_t)-1;
+    }
+}
+
+int xsymv_shard_columns(int n, int panel, int nshards, int shard, int* cols)
+{
+    if (n < 0 || panel <= 0 || nshards <= 0 || shard < 0 || shard >= nshards) return -1;
+    std::vector<int> c;
+    shard_columns_host(n, panel, nshards, shard, c);
+    if (cols) std::copy(c.begin(), c.end(), cols);
+    return (int)c.size();
+}
+
+size_t xsymv_shard_workspace_bytes(int prec, char uplo, int n, int panel, int nshards, int shard)
+{
+    switch (prec) {
+    case XSYMV_S: return shard_ws_bytes<float>(uplo, n, panel, nshards, shard);
+    case XSYMV_D: return shard_ws_bytes<double>(uplo, n, panel, nshards, shard);
+    case XSYMV_C: return shard_ws_bytes<cf32>(uplo, n, panel, nshards, shard);
+    case XSYMV_Z: return shard_ws_bytes<cf64>(uplo, n, panel, nshards, shard);
+    case XSYMV_W: return shard_ws_bytes<ddreal>(uplo, n, panel, nshards, shard);
     default: return (size_t)-1;
     }
 }

@@ -152,9 +152,25 @@ struct StripPlan {
     int* d_strip_base = nullptr;
     int* d_seg_base = nullptr;
     void* h_pinned = nullptr;  // pinned source of the one upload
+    // one shard's product: its local columns (see StripArgs)
+    int ncol = 0;
+    int* d_lcol = nullptr;
+    int* d_gloc = nullptr;
+    int* d_col0 = nullptr;
 };
+// lcol (optional): the ascending global columns of a shard's local matrix;
+// the strips' sequences then run over local columns (col0: the first local
+// column of each strip's sequence).
 void build_strip_plan_host(bool upper, int n, int R, int G, int split, std::vector<StripBlock>& blocks,
-                           std::vector<int>& strip_base, std::vector<int>& seg_base, int& NS);
+                           std::vector<int>& strip_base, std::vector<int>& seg_base, int& NS,
+                           const std::vector<int>* lcol = nullptr,
+                           std::vector<int>* col0 = nullptr);
+
+// Columns of one shard when panels of `panel` columns are dealt to `nshards`
+// shards round by round, forward in even rounds and backward in odd ones.
+int shard_owner(int panel_index, int nshards);
+void shard_columns_host(int n, int panel, int nshards, int shard, std::vector<int>& cols);
+int shard_column_count(int n, int panel, int nshards, int shard);
 
 // xGEMV: (strip, column) sequence of NS strips x n columns, equal pieces
 // (per-column cost: the strip's rows plus a fixed share).
@@ -167,6 +183,8 @@ int get_gemv_plan(DeviceState* ds, int m, int n, int R, int G, hipStream_t strea
                   const StripPlan** out);
 int get_strip_plan(DeviceState* ds, int dev, bool upper, int n, int R, int G, int split, hipStream_t stream,
                    const StripPlan** out);
+int get_shard_plan(DeviceState* ds, bool upper, int n, int R, int G, int split, int panel,
+                   int nshards, int shard, hipStream_t stream, const StripPlan** out);
 // Workgroups of `kernel` (block size `threads`) the current device holds at once.
 int resident_blocks(const void* kernel, int threads, int* out);
 // Both return 0 or ERR_HIP + hipError_t; the caller holds the state's lock.
@@ -726,6 +744,148 @@ size_t trmv_ws_bytes(char uplo, char trans, int n)
         most = std::max(most, trmv_workspace_bytes<T>(tr, segb[NS], ks.R(), NS, n));
     }
     return most;
+}
+
+// ------------------------------------------------- one shard's product
+template <class T>
+struct ShardKernelSet {
+    int W, SW, G, NT, split;
+    void (*k[2])(StripArgs<T>);  // lower, upper
+    int R() const { return W * SW * 64 * Elem<T>::VEC; }
+};
+
+template <class T, int W, int SW, int G, bool NT, int SPLIT>
+ShardKernelSet<T> make_shard()
+{
+    return ShardKernelSet<T>{W, SW, G, NT ? 1 : 0, SPLIT,
+                             {&symv_strip<T, false, W, SW, G, NT, STRIP_CBUF, true>,
+                              &symv_strip<T, true, W, SW, G, NT, STRIP_CBUF, true>}};
+}
+
+template <class T> const ShardKernelSet<T>& shard_kernels();
+int check_shard_args(char uplo, int n, int panel, int nshards, int shard, const void* A, int lda,
+                     const void* x, int incx, const void* p, bool* upper, int* ncol);
+int check_combine_args(int n, int nshards, const void* P, int ldp, const void* y, int incy);
+
+// Workspace of one shard's product: [rowpart nseg*R][colpart NS*ncol][x gathered, n]
+template <class T>
+size_t shard_workspace_bytes(int nseg, int R, int NS, int ncol, int n)
+{
+    return align_up((size_t)nseg * R * sizeof(T)) + align_up((size_t)NS * ncol * sizeof(T)) +
+           align_up((size_t)n * sizeof(T));
+}
+
+// p := one shard's share of S*x (its own columns' stored elements in both
+// roles, the diagonal once), contiguous; with no columns, p := 0.
+template <class T>
+int shard_run(char uplo, int n, int panel, int nshards, int shard, const T* A, int lda,
+              const T* x, int incx, T* p, hipStream_t stream)
+{
+    bool upper = false;
+    int ncol = 0;
+    int rc = check_shard_args(uplo, n, panel, nshards, shard, A, lda, x, incx, p, &upper, &ncol);
+    if (rc) return rc;
+    if (n == 0) return 0;
+    if (ncol == 0) {
+        symv_scale<T><<<blocks_for(n, 256), 256, 0, stream>>>(p, 1, 0, n, tune_zero<T>(), 1);
+        XSYMV_HIP(hipGetLastError());
+        return 0;
+    }
+    const ShardKernelSet<T>& ks = shard_kernels<T>();
+    const int R = ks.R();
+    const int threads = 64 * ks.W;
+    auto kern = ks.k[upper ? 1 : 0];
+    int dev = 0;
+    XSYMV_HIP(hipGetDevice(&dev));
+    DeviceState* ds = device_state(dev);
+    std::lock_guard<std::mutex> lk(device_mutex(ds));
+    int G = 0;
+    rc = resident_blocks((const void*)kern, threads, &G);
+    if (rc) return rc;
+    const StripPlan* plan = nullptr;
+    rc = get_shard_plan(ds, upper, n, R, G, ks.split, panel, nshards, shard, stream, &plan);
+    if (rc) return rc;
+    void* ws = nullptr;
+    rc = get_workspace(ds, stream, shard_workspace_bytes<T>(plan->nseg, R, plan->NS, ncol, n), &ws);
+    if (rc) return rc;
+    char* base = static_cast<char*>(ws);
+    const size_t off_col = align_up((size_t)plan->nseg * R * sizeof(T));
+    const size_t off_x = off_col + align_up((size_t)plan->NS * ncol * sizeof(T));
+    T* rowpart = reinterpret_cast<T*>(base);
+    T* colpart = reinterpret_cast<T*>(base + off_col);
+    T* xg = reinterpret_cast<T*>(base + off_x);
+    const T* xin = x;
+    if (incx != 1) {
+        const long long kx = incx > 0 ? 0 : (long long)(1 - n) * incx;
+        symv_gather<T><<<blocks_for(n, 256), 256, 0, stream>>>(x, incx, kx, n, xg);
+        XSYMV_HIP(hipGetLastError());
+        xin = xg;
+    }
+    TimedCall tc{};
+    const bool timing = timing_enabled();
+    if (timing) {
+        XSYMV_HIP(hipEventCreate(&tc.e0));
+        XSYMV_HIP(hipEventCreate(&tc.e1));
+        XSYMV_HIP(hipEventCreate(&tc.e2));
+        XSYMV_HIP(hipEventRecord(tc.e0, stream));
+    }
+    StripArgs<T> sa{A, xin, rowpart, colpart, plan->d_blocks, plan->d_strip_base,
+                    (long long)lda, n, plan->d_lcol, plan->d_gloc, plan->d_col0, ncol};
+    kern<<<plan->G, threads, 0, stream>>>(sa);
+    XSYMV_HIP(hipGetLastError());
+    if (timing) XSYMV_HIP(hipEventRecord(tc.e1, stream));
+    StripMergeArgs<T> ma{rowpart, colpart, plan->d_seg_base, p, 1, 0, tune_one<T>(),
+                         tune_zero<T>(), n, plan->NS, R, upper ? 1 : 0, 1, plan->d_gloc, ncol};
+    symv_strip_merge<T, MERGE_SPLIT, true><<<blocks_for(n, 64), 64 * MERGE_SPLIT, 0, stream>>>(ma);
+    XSYMV_HIP(hipGetLastError());
+    if (timing) {
+        XSYMV_HIP(hipEventRecord(tc.e2, stream));
+        timing_push(tc);
+    }
+    return 0;
+}
+
+// y := beta*y + alpha*(P[0] + P[1] + ...), the partials summed in rank order.
+template <class T>
+int combine_run(int n, int nshards, T alpha, const T* P, int ldp, T beta, T* y, int incy,
+                hipStream_t stream)
+{
+    int rc = check_combine_args(n, nshards, P, ldp, y, incy);
+    if (rc) return rc;
+    if (n == 0 || (host_is_zero(alpha) && host_is_one(beta))) return 0;
+    const long long ky = incy > 0 ? 0 : (long long)(1 - n) * incy;
+    const int beta_zero = host_is_zero(beta) ? 1 : 0;
+    if (host_is_zero(alpha)) {
+        symv_scale<T><<<blocks_for(n, 256), 256, 0, stream>>>(y, incy, ky, n, beta, beta_zero);
+        XSYMV_HIP(hipGetLastError());
+        return 0;
+    }
+    CombineArgs<T> ca{P, y, (long long)ldp, (long long)incy, ky, alpha, beta, n, nshards,
+                      beta_zero};
+    symv_combine<T><<<blocks_for(n, 256), 256, 0, stream>>>(ca);
+    XSYMV_HIP(hipGetLastError());
+    return 0;
+}
+
+template <class T>
+size_t shard_ws_bytes(char uplo, int n, int panel, int nshards, int shard)
+{
+    bool upper = false;
+    int ncol = 0;
+    if (check_shard_args(uplo, n, panel, nshards, shard, (const void*)1, std::max(1, n),
+                         (const void*)1, 1, (const void*)1, &upper, &ncol))
+        return (size_t)-1;
+    if (n == 0 || ncol == 0) return 0;
+    const ShardKernelSet<T>& ks = shard_kernels<T>();
+    int G = 0;
+    if (resident_blocks((const void*)ks.k[upper ? 1 : 0], 64 * ks.W, &G)) return (size_t)-1;
+    std::vector<int> cols, col0;
+    shard_columns_host(n, panel, nshards, shard, cols);
+    std::vector<StripBlock> blocks;
+    std::vector<int> sb, segb;
+    int NS = 0;
+    build_strip_plan_host(upper, n, ks.R(), G, ks.split, blocks, sb, segb, NS, &cols, &col0);
+    return shard_workspace_bytes<T>(segb[NS], ks.R(), NS, ncol, n);
 }
 
 // ---------------------------------------------------------------- autotuner

@@ -75,6 +75,14 @@ template <> const std::vector<TrmvKernelSet<cf32>>& trmv_kernel_sets<cf32>()
 // built-in choice [upper][op = T or T^H]: the fastest (median of 20 calls)
 // at n = 16384 on MI355X
 template <> TrmvDefaults trmv_defaults<cf32>() { return TrmvDefaults{{{0, 0}, {3, 3}}}; }
+
+// One shard's product: the row-strip shape that the built-in rules pick for
+// the largest orders (R 2048, G 8, split by stored rows)
+template <> const ShardKernelSet<cf32>& shard_kernels<cf32>()
+{
+    static const ShardKernelSet<cf32> k = make_shard<cf32, 16, 1, 8, true, 1>();
+    return k;
+}
 }  // namespace xsymv
 
 extern "C" int xhemv_c(char uplo, int n, xcomplex64 alpha, const xcomplex64* A, int lda,
@@ -112,4 +120,21 @@ extern "C" int xtrmv_c(char uplo, char trans, char diag, int n, const xcomplex64
     using xsymv::cf32;
     return xsymv::trmv_run<cf32>(uplo, trans, diag, n, (const cf32*)A, lda, (cf32*)x, incx,
                                (hipStream_t)stream, -1);
+}
+
+extern "C" int xhemv_shard_c(char uplo, int n, int panel, int nshards, int shard,
+                            const xcomplex64* Aloc, int lda, const xcomplex64* x, int incx, xcomplex64* p,
+                            void* stream)
+{
+    using xsymv::cf32;
+    return xsymv::shard_run<cf32>(uplo, n, panel, nshards, shard, (const cf32*)Aloc, lda,
+                                    (const cf32*)x, incx, (cf32*)p, (hipStream_t)stream);
+}
+
+extern "C" int xhemv_combine_c(int n, int nshards, xcomplex64 alpha, const xcomplex64* P, int ldp,
+                              xcomplex64 beta, xcomplex64* y, int incy, void* stream)
+{
+    using xsymv::cf32;
+    return xsymv::combine_run<cf32>(n, nshards, cf32{alpha.re, alpha.im}, (const cf32*)P, ldp,
+                                      cf32{beta.re, beta.im}, (cf32*)y, incy, (hipStream_t)stream);
 }

@@ -85,6 +85,14 @@ template <> const std::vector<TrmvKernelSet<double>>& trmv_kernel_sets<double>()
 // built-in choice [upper][op = T or T^H]: the fastest (median of 20 calls)
 // at n = 32768 on MI355X
 template <> TrmvDefaults trmv_defaults<double>() { return TrmvDefaults{{{4, 3}, {3, 3}}}; }
+
+// One shard's product: the row-strip shape that the built-in rules pick for
+// the largest orders (R 4096, G 4, split by stored rows)
+template <> const ShardKernelSet<double>& shard_kernels<double>()
+{
+    static const ShardKernelSet<double> k = make_shard<double, 16, 2, 4, true, 1>();
+    return k;
+}
 }  // namespace xsymv
 
 extern "C" int xsymv_d(char uplo, int n, double alpha, const double* A, int lda,
@@ -113,4 +121,18 @@ extern "C" int xtrmv_d(char uplo, char trans, char diag, int n, const double* A,
                        int incx, void* stream)
 {
     return xsymv::trmv_run<double>(uplo, trans, diag, n, A, lda, x, incx, (hipStream_t)stream, -1);
+}
+
+extern "C" int xsymv_shard_d(char uplo, int n, int panel, int nshards, int shard,
+                            const double* Aloc, int lda, const double* x, int incx, double* p,
+                            void* stream)
+{
+    return xsymv::shard_run<double>(uplo, n, panel, nshards, shard, Aloc, lda, x, incx, p,
+                                    (hipStream_t)stream);
+}
+
+extern "C" int xsymv_combine_d(int n, int nshards, double alpha, const double* P, int ldp,
+                              double beta, double* y, int incy, void* stream)
+{
+    return xsymv::combine_run<double>(n, nshards, alpha, P, ldp, beta, y, incy, (hipStream_t)stream);
 }

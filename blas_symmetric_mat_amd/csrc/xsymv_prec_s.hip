@@ -83,6 +83,14 @@ template <> const std::vector<TrmvKernelSet<float>>& trmv_kernel_sets<float>()
 // built-in choice [upper][op = T or T^H]: the fastest (median of 20 calls)
 // at n = 32768 on MI355X
 template <> TrmvDefaults trmv_defaults<float>() { return TrmvDefaults{{{0, 3}, {0, 2}}}; }
+
+// One shard's product: the row-strip shape that the built-in rules pick for
+// the largest orders (R 4096, G 16, split by stored rows)
+template <> const ShardKernelSet<float>& shard_kernels<float>()
+{
+    static const ShardKernelSet<float> k = make_shard<float, 16, 1, 16, true, 1>();
+    return k;
+}
 }  // namespace xsymv
 
 extern "C" int xsymv_s(char uplo, int n, float alpha, const float* A, int lda, const float* x,
@@ -110,4 +118,18 @@ extern "C" int xtrmv_s(char uplo, char trans, char diag, int n, const float* A, 
                        int incx, void* stream)
 {
     return xsymv::trmv_run<float>(uplo, trans, diag, n, A, lda, x, incx, (hipStream_t)stream, -1);
+}
+
+extern "C" int xsymv_shard_s(char uplo, int n, int panel, int nshards, int shard,
+                            const float* Aloc, int lda, const float* x, int incx, float* p,
+                            void* stream)
+{
+    return xsymv::shard_run<float>(uplo, n, panel, nshards, shard, Aloc, lda, x, incx, p,
+                                    (hipStream_t)stream);
+}
+
+extern "C" int xsymv_combine_s(int n, int nshards, float alpha, const float* P, int ldp,
+                              float beta, float* y, int incy, void* stream)
+{
+    return xsymv::combine_run<float>(n, nshards, alpha, P, ldp, beta, y, incy, (hipStream_t)stream);
 }

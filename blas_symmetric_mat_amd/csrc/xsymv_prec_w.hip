@@ -76,6 +76,14 @@ template <> const std::vector<TrmvKernelSet<ddreal>>& trmv_kernel_sets<ddreal>()
 // built-in choice [upper][op = T or T^H]: the fastest (median of 20 calls)
 // at n = 16384 on MI355X
 template <> TrmvDefaults trmv_defaults<ddreal>() { return TrmvDefaults{{{4, 2}, {4, 2}}}; }
+
+// One shard's product: the row-strip shape that the built-in rules pick for
+// the largest orders (R 1024, G 4, split by strip height)
+template <> const ShardKernelSet<ddreal>& shard_kernels<ddreal>()
+{
+    static const ShardKernelSet<ddreal> k = make_shard<ddreal, 4, 4, 4, true, 0>();
+    return k;
+}
 }  // namespace xsymv
 
 extern "C" int xsymv_w(char uplo, int n, xdd alpha, const xdd* A, int lda, const xdd* x,
@@ -113,4 +121,21 @@ extern "C" int xtrmv_w(char uplo, char trans, char diag, int n, const xdd* A, in
     using xsymv::ddreal;
     return xsymv::trmv_run<ddreal>(uplo, trans, diag, n, (const ddreal*)A, lda, (ddreal*)x, incx,
                                    (hipStream_t)stream, -1);
+}
+
+extern "C" int xsymv_shard_w(char uplo, int n, int panel, int nshards, int shard,
+                            const xdd* Aloc, int lda, const xdd* x, int incx, xdd* p,
+                            void* stream)
+{
+    using xsymv::ddreal;
+    return xsymv::shard_run<ddreal>(uplo, n, panel, nshards, shard, (const ddreal*)Aloc, lda,
+                                    (const ddreal*)x, incx, (ddreal*)p, (hipStream_t)stream);
+}
+
+extern "C" int xsymv_combine_w(int n, int nshards, xdd alpha, const xdd* P, int ldp,
+                              xdd beta, xdd* y, int incy, void* stream)
+{
+    using xsymv::ddreal;
+    return xsymv::combine_run<ddreal>(n, nshards, ddreal{alpha.hi, alpha.lo}, (const ddreal*)P, ldp,
+                                      ddreal{beta.hi, beta.lo}, (ddreal*)y, incy, (hipStream_t)stream);
 }

@@ -75,6 +75,14 @@ template <> const std::vector<TrmvKernelSet<cf64>>& trmv_kernel_sets<cf64>()
 // built-in choice [upper][op = T or T^H]: the fastest (median of 20 calls)
 // at n = 16384 on MI355X
 template <> TrmvDefaults trmv_defaults<cf64>() { return TrmvDefaults{{{4, 4}, {4, 3}}}; }
+
+// One shard's product: the row-strip shape that the built-in rules pick for
+// the largest orders (R 2048, G 4, split by stored rows)
+template <> const ShardKernelSet<cf64>& shard_kernels<cf64>()
+{
+    static const ShardKernelSet<cf64> k = make_shard<cf64, 16, 2, 4, true, 1>();
+    return k;
+}
 }  // namespace xsymv
 
 extern "C" int xhemv_z(char uplo, int n, xcomplex128 alpha, const xcomplex128* A, int lda,
@@ -113,4 +121,21 @@ extern "C" int xtrmv_z(char uplo, char trans, char diag, int n, const xcomplex12
     using xsymv::cf64;
     return xsymv::trmv_run<cf64>(uplo, trans, diag, n, (const cf64*)A, lda, (cf64*)x, incx,
                                (hipStream_t)stream, -1);
+}
+
+extern "C" int xhemv_shard_z(char uplo, int n, int panel, int nshards, int shard,
+                            const xcomplex128* Aloc, int lda, const xcomplex128* x, int incx, xcomplex128* p,
+                            void* stream)
+{
+    using xsymv::cf64;
+    return xsymv::shard_run<cf64>(uplo, n, panel, nshards, shard, (const cf64*)Aloc, lda,
+                                    (const cf64*)x, incx, (cf64*)p, (hipStream_t)stream);
+}
+
+extern "C" int xhemv_combine_z(int n, int nshards, xcomplex128 alpha, const xcomplex128* P, int ldp,
+                              xcomplex128 beta, xcomplex128* y, int incy, void* stream)
+{
+    using xsymv::cf64;
+    return xsymv::combine_run<cf64>(n, nshards, cf64{alpha.re, alpha.im}, (const cf64*)P, ldp,
+                                      cf64{beta.re, beta.im}, (cf64*)y, incy, (hipStream_t)stream);
 }

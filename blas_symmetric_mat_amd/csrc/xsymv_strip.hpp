@@ -48,11 +48,17 @@ struct StripArgs {
     const T* A;
     const T* x;           // contiguous
     T* rowpart;           // [nseg][R]
-    T* colpart;           // [NS][n]
+    T* colpart;           // [NS][n] (sharded: [NS][ncol])
     const StripBlock* blocks;
     const int* strip_base;  // [NS+1]: first sequence position of strip i
     long long lda;
     int n;
+    // one shard's product only: A holds the shard's columns (local column l
+    // is global column lcol[l], ascending)
+    const int* lcol;        // [ncol]
+    const int* gloc;        // [n]: local column of a global column, or -1
+    const int* strip_col0;  // [NS]: first local column of strip i's sequence
+    int ncol;
 };
 
 // Reads of A.  A wave's rows of column j are one run of SW*H elements
@@ -65,7 +71,13 @@ struct StripArgs {
 // bound, so those few groups take element loads at clamped addresses.  The
 // diagonal itself counts once, in the row role: L takes it in the band, U
 // adds d_r * x_r at the end of the segment that holds column r.
-template <class T, bool UPPER, int W, int SW, int G, bool NT, int CBUF>
+//
+// SHARD: one GPU's share of the product when the columns are dealt out in
+// panels.  A is the shard's local matrix; the sequence runs over its local
+// columns (those with stored rows in the strip form a contiguous range, as the
+// local-to-global map ascends), addresses use the local column, triangle
+// bounds and x the global one, and column partials are indexed locally.
+template <class T, bool UPPER, int W, int SW, int G, bool NT, int CBUF, bool SHARD = false>
 __global__ __launch_bounds__(64 * W) void symv_strip(StripArgs<T> a)
 {
     using E = Elem<T>;
@@ -85,6 +97,12 @@ __global__ __launch_bounds__(64 * W) void symv_strip(StripArgs<T> a)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const T* __restrict__ A = a.A;
     const T* __restrict__ x = a.x;
+    // the column map is read at wave-uniform indices only: read it through
+    // the constant address space (scalar loads), so that no vector load has
+    // to complete before the element addresses that depend on it
+    using cmap = const __attribute__((address_space(4))) int*;
+    const cmap lcol = (cmap)a.lcol;
+    const int* __restrict__ gloc = a.gloc;
 
     int u = bd.u0;
     int slot = bd.slot0;
@@ -94,7 +112,8 @@ __global__ __launch_bounds__(64 * W) void symv_strip(StripArgs<T> a)
         const int useg = min(bd.u1, a.strip_base[strip + 1]);
         const int rs0 = strip * R;
         const int rs1 = min(n, rs0 + R);
-        const int coff = (UPPER ? rs0 : 0) - sb0;  // column = sequence position + coff
+        // (local) column = sequence position + coff
+        const int coff = (UPPER ? (SHARD ? a.strip_col0[strip] : rs0) : 0) - sb0;
         const int rw = rs0 + wave * RW;            // this wave's first row
         const bool wave_empty = rw >= rs1;
 
@@ -116,11 +135,14 @@ __global__ __launch_bounds__(64 * W) void symv_strip(StripArgs<T> a)
         for (int g0 = u; g0 < useg; g0 += G) {
             const int jg = g0 + coff;          // first column of the group
             const int ng = min(G, useg - g0);  // real columns in the group
+            // global indices of the group's first and last columns
+            const int gfirst = SHARD ? lcol[jg] : jg;
+            const int glast = SHARD ? lcol[jg + ng - 1] : jg + ng - 1;
             // no stored element of the group in this wave's rows
             const bool empty =
-                wave_empty || (UPPER ? (rw >= jg + ng - 1) : (rw + RW <= jg));
+                wave_empty || (UPPER ? (rw >= glast) : (rw + RW <= gfirst));
             // every real column of the group is left of this wave's rows (L)
-            const bool band = !UPPER && !empty && rw < jg + ng;
+            const bool band = !UPPER && !empty && rw < glast + 1;
             T cacc[G];
             if (empty) {
 #pragma unroll
@@ -131,11 +153,12 @@ __global__ __launch_bounds__(64 * W) void symv_strip(StripArgs<T> a)
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
                     const bool real = g < ng;
-                    const int cc = real ? jg + g : jg;
+                    const int cl = real ? jg + g : jg;      // local column
+                    const int cc = SHARD ? lcol[cl] : cl;  // global column
                     // stored rows of this wave in column cc: [rw, bound)
                     const int bound = UPPER ? cc : n;
                     const int rows = real ? min(RW, max(0, bound - rw)) : 0;
-                    const auto rs = make_rsrc(A + (long long)cc * lda + rw, rows * (int)sizeof(T));
+                    const auto rs = make_rsrc(A + (long long)cl * lda + rw, rows * (int)sizeof(T));
 #pragma unroll
                     for (int s = 0; s < SW; ++s)
                         E::template bload16<NT>(rs, (s * H + lane * V) * (int)sizeof(T), av[g][s]);
@@ -157,10 +180,11 @@ __global__ __launch_bounds__(64 * W) void symv_strip(StripArgs<T> a)
                 // branch-free; the diagonal counts once (row role)
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
-                    const int col = jg + g;
                     const bool colok = g < ng;
-                    const int cc = colok ? col : jg;  // jg is a real column
-                    const T* __restrict__ Acc = A + (long long)cc * lda;
+                    const int cl = colok ? jg + g : jg;      // jg is a real column
+                    const int cc = SHARD ? lcol[cl] : cl;  // global column
+                    const int col = SHARD ? cc : jg + g;
+                    const T* __restrict__ Acc = A + (long long)cl * lda;
                     const T xcol = E::sel(colok, x[cc], E::zero());
                     cacc[g] = E::zero();
 #pragma unroll
@@ -187,24 +211,31 @@ __global__ __launch_bounds__(64 * W) void symv_strip(StripArgs<T> a)
                     T sum = colred[0][c];
 #pragma unroll
                     for (int w = 1; w < W; ++w) sum = E::add(sum, colred[w][c]);
-                    a.colpart[(long long)strip * n + jbuf + c] = sum;
+                    a.colpart[(long long)strip * (SHARD ? a.ncol : n) + jbuf + c] = sum;
                 }
                 __syncthreads();
                 jbuf += nreal;
                 nbuf = 0;
             }
         }
-        if (UPPER) {
-            // diagonal of the rows whose column is in this segment
+        // (a shard's segment may hold no column: a strip without any of its
+        // columns that a workgroup's range steps through)
+        if (UPPER && (!SHARD || useg > u)) {
+            // diagonal of the rows whose column is in this segment (local
+            // columns [c0, c1))
             const int c0 = u + coff, c1 = useg + coff;
 #pragma unroll
             for (int s = 0; s < SW; ++s)
 #pragma unroll
                 for (int k = 0; k < V; ++k) {
                     const int r = rw + s * H + lane * V + k;
-                    const bool in = r >= c0 && r < c1 && r < rs1;
-                    const long long rr = in ? r : c0;  // c0 < n is a real column
-                    const T d = E::diag_load(A + rr * lda + rr);
+                    // the row's own column, locally (-1: another shard's)
+                    const int lr = SHARD ? gloc[r < rs1 ? r : rs1 - 1] : r;
+                    const bool in = lr >= c0 && lr < c1 && r < rs1;
+                    // c0 < ncol is a real local column, its diagonal a stored element
+                    const long long cl = in ? lr : c0;
+                    const long long rg = in ? r : (SHARD ? lcol[c0] : c0);
+                    const T d = E::diag_load(A + cl * lda + rg);
                     racc[s][k] = E::mac(racc[s][k], E::sel(in, d, E::zero()), xr[s][k]);
                 }
         }
@@ -243,9 +274,14 @@ struct StripMergeArgs {
     int R;
     int upper;
     int beta_zero;
+    const int* gloc;  // sharded product only
+    int ncol;
 };
 
-template <class T, int SPLIT>
+// SHARD: the shard's partial vector -- column partials only for the rows
+// whose column the shard owns (local index gloc[i], rows of ncol), no alpha or
+// beta: y is the contiguous partial p.
+template <class T, int SPLIT, bool SHARD = false>
 __global__ __launch_bounds__(64 * SPLIT) void symv_strip_merge(StripMergeArgs<T> a)
 {
     using E = Elem<T>;
@@ -259,13 +295,15 @@ __global__ __launch_bounds__(64 * SPLIT) void symv_strip_merge(StripMergeArgs<T>
         const int s_lo = a.seg_base[I];
         const int nrow = a.seg_base[I + 1] - s_lo;
         const int c_lo = a.upper ? 0 : I;
-        const int ncol = a.upper ? I + 1 : a.NS - I;
+        const int li = SHARD ? a.gloc[i] : i;  // the row's column, locally
+        const int ncol = li < 0 ? 0 : (a.upper ? I + 1 : a.NS - I);
         const int ntot = nrow + ncol;
+        const long long cstride = SHARD ? a.ncol : a.n;
         const T* __restrict__ rp = a.rowpart + (long long)s_lo * a.R + (i - I * a.R);
-        const T* __restrict__ cp = a.colpart + (long long)c_lo * a.n + i;
+        const T* __restrict__ cp = a.colpart + (long long)c_lo * cstride + li;
 #pragma unroll 4
         for (int k = g; k < ntot; k += SPLIT) {
-            const T v = (k < nrow) ? rp[(long long)k * a.R] : cp[(long long)(k - nrow) * a.n];
+            const T v = (k < nrow) ? rp[(long long)k * a.R] : cp[(long long)(k - nrow) * cstride];
             acc = E::add(acc, v);
         }
     }
@@ -278,11 +316,46 @@ __global__ __launch_bounds__(64 * SPLIT) void symv_strip_merge(StripMergeArgs<T>
     }
     if (g == 0 && i < a.n) {
         const T tot = part[0][lane];
-        T* yp = a.y + a.ky + (long long)i * a.incy;
-        T r = E::mul(a.alpha, tot);
-        if (!a.beta_zero) r = E::add(r, E::mul(a.beta, *yp));
-        *yp = r;
+        if constexpr (SHARD) {
+            a.y[i] = tot;
+        } else {
+            T* yp = a.y + a.ky + (long long)i * a.incy;
+            T r = E::mul(a.alpha, tot);
+            if (!a.beta_zero) r = E::add(r, E::mul(a.beta, *yp));
+            *yp = r;
+        }
     }
+}
+
+// Rank-ordered combination of the shards' partials: y_i := beta*y_i +
+// alpha*(P[0][i] + P[1][i] + ...), summed from shard 0 up (beta = 0: y not
+// read).  One lane per output; the partials' reads are coalesced.
+template <class T>
+struct CombineArgs {
+    const T* P;
+    T* y;
+    long long ldp;
+    long long incy;
+    long long ky;
+    T alpha;
+    T beta;
+    int n;
+    int nshards;
+    int beta_zero;
+};
+
+template <class T>
+__global__ __launch_bounds__(256) void symv_combine(CombineArgs<T> a)
+{
+    using E = Elem<T>;
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= a.n) return;
+    T sum = a.P[i];
+    for (int g = 1; g < a.nshards; ++g) sum = E::add(sum, a.P[(long long)g * a.ldp + i]);
+    T* yp = a.y + a.ky + (long long)i * a.incy;
+    T r = E::mul(a.alpha, sum);
+    if (!a.beta_zero) r = E::add(E::mul(a.beta, *yp), r);
+    *yp = r;
 }
 
 }  // namespace xsymv

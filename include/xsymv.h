@@ -193,6 +193,77 @@ int xsyr2_config_info(int prec, int idx, int *waves, int *stripes_per_wave,
 int xsyr2_select_config(int prec, int idx);
 int xsyr2_current_config(int prec);
 
+/* One GPU's share of the product, for the path sharded over several GPUs
+ * (the report's §5 points to multi-GPU SYMV, its ref. [7]); on one GPU the
+ * shards run one after another.  The columns are cut into panels of `panel`
+ * consecutive columns (the last may be short), dealt to `nshards` shards
+ * round by round: in even rounds shard g takes the round's g-th panel, in
+ * odd rounds its (nshards-1-g)-th, which keeps the shards' triangle areas
+ * close.  xsymv_shard_columns writes the global columns of `shard`
+ * (ascending; cols may be NULL) and returns their count (-1: bad argument);
+ * a host computation.
+ *
+ *   x[sd]symv_shard_X / xhemv_shard_[cz]:  p := the shard's share of S*x --
+ *   every stored element A(i,j) of an owned column j taken in both roles
+ *   (p_i += A(i,j) x_j, and p_j += conj(A(i,j)) x_i for i != j), the
+ *   diagonal once (Hermitian: its real word) -- so that the shards' partials
+ *   add up to S*x.
+ *
+ * Aloc: DEVICE pointer to the shard's local matrix, its columns in ascending
+ * global order, each a full column of A (rows 0..n-1 at stride lda >=
+ * max(1, n); only the uplo triangle is read).  x: DEVICE, n elements, stride
+ * incx != 0.  p: DEVICE, n contiguous elements, overwritten (zeros when the
+ * shard owns no column).  Deterministic: fixed-order partial sums, no
+ * atomics.  Asynchronous on `stream`; uses the per-stream workspace
+ * (xsymv_shard_workspace_bytes).  Codes: -1 uplo, -2 n < 0, -3 panel <= 0,
+ * -4 nshards <= 0, -5 shard outside [0, nshards), -6 Aloc NULL while the
+ * shard owns columns, -7 lda < max(1, n), -8 x NULL, -9 incx == 0,
+ * -10 p NULL; 1000 + hipError_t; 2000 installed workspace too small.
+ *
+ *   xsymv_combine_X / xhemv_combine_[cz]:  y := beta*y + alpha*(P[0] + P[1]
+ *   + ... + P[nshards-1]), partial g at P + g*ldp (DEVICE, n elements each),
+ *   summed in rank order -- the fixed order that keeps the result the same
+ *   from run to run, whatever the exchange did.  BLAS rules: beta == 0 does
+ *   not read y, alpha == 0 does not read P, n == 0 or (alpha == 0 and
+ *   beta == 1) returns at once.  y: DEVICE, stride incy != 0.  Codes: -1 n,
+ *   -2 nshards <= 0, -4 P NULL, -5 ldp < max(1, n), -7 y NULL, -8 incy == 0;
+ *   1000 + hipError_t. */
+int xsymv_shard_columns(int n, int panel, int nshards, int shard, int *cols);
+/* The work split of one shard's product (host computation, as
+ * xsymv_strip_plan, over the shard's local columns): blocks4, strip_base and
+ * seg_base as there, col0 (NS entries) the first local column of each
+ * strip's sequence.  A strip without any of the shard's columns has an empty
+ * sequence and (unless a workgroup's range steps through it) no segment.
+ * Returns the number of workgroups (0 when the shard owns no column), -1 for
+ * bad arguments, -2 if an output is too small. */
+int xsymv_shard_plan(char uplo, int n, int R, int G, int split, int panel, int nshards,
+                     int shard, int *blocks4, int max_blocks, int *strip_base, int *seg_base,
+                     int *col0, int max_strips);
+size_t xsymv_shard_workspace_bytes(int prec, char uplo, int n, int panel, int nshards,
+                                   int shard);
+int xsymv_shard_s(char uplo, int n, int panel, int nshards, int shard, const float *Aloc,
+                  int lda, const float *x, int incx, float *p, void *stream);
+int xsymv_shard_d(char uplo, int n, int panel, int nshards, int shard, const double *Aloc,
+                  int lda, const double *x, int incx, double *p, void *stream);
+int xhemv_shard_c(char uplo, int n, int panel, int nshards, int shard,
+                  const xcomplex64 *Aloc, int lda, const xcomplex64 *x, int incx,
+                  xcomplex64 *p, void *stream);
+int xhemv_shard_z(char uplo, int n, int panel, int nshards, int shard,
+                  const xcomplex128 *Aloc, int lda, const xcomplex128 *x, int incx,
+                  xcomplex128 *p, void *stream);
+int xsymv_shard_w(char uplo, int n, int panel, int nshards, int shard, const xdd *Aloc,
+                  int lda, const xdd *x, int incx, xdd *p, void *stream);
+int xsymv_combine_s(int n, int nshards, float alpha, const float *P, int ldp, float beta,
+                    float *y, int incy, void *stream);
+int xsymv_combine_d(int n, int nshards, double alpha, const double *P, int ldp, double beta,
+                    double *y, int incy, void *stream);
+int xhemv_combine_c(int n, int nshards, xcomplex64 alpha, const xcomplex64 *P, int ldp,
+                    xcomplex64 beta, xcomplex64 *y, int incy, void *stream);
+int xhemv_combine_z(int n, int nshards, xcomplex128 alpha, const xcomplex128 *P, int ldp,
+                    xcomplex128 beta, xcomplex128 *y, int incy, void *stream);
+int xsymv_combine_w(int n, int nshards, xdd alpha, const xdd *P, int ldp, xdd beta, xdd *y,
+                    int incy, void *stream);
+
 /* Triangular matrix-vector product (another of the Level-2 BLAS the report's
  * §5 carries the approach to), BLAS xTRMV:
  *

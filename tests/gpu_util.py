@@ -158,3 +158,31 @@ def assert_close_trmv(p, got, ref, label=""):
     bad = np.nonzero(~(d <= tol))[0]
     assert bad.size == 0, (f"{label}: {bad.size} outputs beyond the bound, worst ratio "
                            f"{np.max(d / np.maximum(tol, 1e-300)):.3g} at {bad[0]}")
+
+
+SHENTRY = {"s": "xsymv_shard_s", "d": "xsymv_shard_d", "c": "xhemv_shard_c",
+           "z": "xhemv_shard_z", "w": "xsymv_shard_w"}
+CBENTRY = {"s": "xsymv_combine_s", "d": "xsymv_combine_d", "c": "xhemv_combine_c",
+           "z": "xhemv_combine_z", "w": "xsymv_combine_w"}
+
+
+def run_shards(p, panel, nshards, shards=None):
+    """Every shard's partial on the device (one after another, as G GPUs
+    would run them side by side): returns the device tensor P[g] (n each) and
+    the host copies."""
+    import blas_symmetric_mat_amd as X
+    torch = torch_dev()
+    from blas_symmetric_mat_amd import workloads as W
+    x = to_device(p.x)
+    P = to_device(W.empty(p.prec, nshards * p.n))
+    shards = range(nshards) if shards is None else shards
+    width = 2 if p.prec == "w" else 1
+    for g in shards:
+        cols = X.shard_columns(p.n, panel, nshards, g)
+        Aloc = to_device(H.local_matrix(p, cols)) if cols else None
+        out = P[g * p.n * width:(g + 1) * p.n * width] if p.prec != "w" else \
+            P[g * p.n:(g + 1) * p.n]
+        getattr(X, SHENTRY[p.prec])(p.uplo, p.n, panel, nshards, g, Aloc, p.lda, x, p.incx, out)
+        del Aloc
+    torch.cuda.synchronize()
+    return P, P.cpu().numpy()

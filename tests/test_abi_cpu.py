@@ -25,7 +25,8 @@ def test_exports_every_declared_function():
     assert {"xsymv_s", "xsymv_d", "xhemv_c", "xhemv_z", "xsymv_w", "xgemv_s", "xgemv_d",
             "xgemv_c", "xgemv_z", "xgemv_w", "xsymv_set_workspace", "xsyr2_s", "xsyr2_d",
             "xher2_c", "xher2_z", "xsyr2_w", "xtrmv_s", "xtrmv_d", "xtrmv_c", "xtrmv_z",
-            "xtrmv_w", "xtrmv_workspace_bytes"} <= set(names)
+            "xtrmv_w", "xtrmv_workspace_bytes", "xsymv_shard_s", "xhemv_shard_z",
+            "xsymv_combine_w", "xhemv_combine_c", "xsymv_shard_columns"} <= set(names)
     for nm in names:
         assert hasattr(lib, nm), nm
 
@@ -340,3 +341,131 @@ def test_trmv_config_tables():
         X.trmv_current_config("d", "Q", "N")
     with pytest.raises(ValueError):
         X.trmv_current_config("d", "L", "Q")
+
+
+@pytest.mark.parametrize("n,panel,nshards", [(0, 1, 1), (1, 1, 1), (10, 2, 3), (37, 4, 3),
+                                             (1000, 64, 8), (100, 7, 5)])
+def test_shard_columns_match_the_oracle(n, panel, nshards):
+    """The library's dealing of panels agrees with the oracle's."""
+    import oracle
+    for g in range(nshards):
+        assert X.shard_columns(n, panel, nshards, g) == list(
+            oracle.shard_columns(n, panel, nshards, g))
+    with pytest.raises(ValueError):
+        X.shard_columns(10, 0, 2, 0)
+
+
+@pytest.mark.parametrize("prec", ["s", "d", "c", "z", "w"])
+def test_shard_argument_errors_before_device_work(prec):
+    f = getattr(X, {"s": "xsymv_shard_s", "d": "xsymv_shard_d", "c": "xhemv_shard_c",
+                    "z": "xhemv_shard_z", "w": "xsymv_shard_w"}[prec])
+    # (uplo, n, panel, nshards, shard, Aloc, lda, x, incx, p); pointers never touched
+    cases = [(("Q", 8, 2, 2, 0, 8, 8, 8, 1, 8), -1), (("L", -1, 2, 2, 0, 8, 8, 8, 1, 8), -2),
+             (("L", 8, 0, 2, 0, 8, 8, 8, 1, 8), -3), (("U", 8, 2, 0, 0, 8, 8, 8, 1, 8), -4),
+             (("U", 8, 2, 2, 2, 8, 8, 8, 1, 8), -5), (("U", 8, 2, 2, -1, 8, 8, 8, 1, 8), -5),
+             (("l", 8, 2, 2, 1, None, 8, 8, 1, 8), -6), (("L", 8, 2, 2, 0, 8, 7, 8, 1, 8), -7),
+             (("L", 8, 2, 2, 0, 8, 8, None, 1, 8), -8), (("L", 8, 2, 2, 0, 8, 8, 8, 0, 8), -9),
+             (("u", 8, 2, 2, 0, 8, 8, 8, 1, None), -10)]
+    for args, code in cases:
+        with pytest.raises(X.XsymvError) as e:
+            f(*args, stream=0)
+        assert e.value.code == code, (args, e.value.code)
+    f("L", 0, 1, 1, 0, None, 1, None, 1, None, stream=0)   # n == 0
+    g = getattr(X, {"s": "xsymv_combine_s", "d": "xsymv_combine_d", "c": "xhemv_combine_c",
+                    "z": "xhemv_combine_z", "w": "xsymv_combine_w"}[prec])
+    one = (1.0, 0.0) if prec == "w" else 1.0
+    cases = [((-1, 2, one, 8, 4, one, 8, 1), -1), ((4, 0, one, 8, 4, one, 8, 1), -2),
+             ((4, 2, one, None, 4, one, 8, 1), -4), ((4, 2, one, 8, 3, one, 8, 1), -5),
+             ((4, 2, one, 8, 4, one, None, 1), -7), ((4, 2, one, 8, 4, one, 8, 0), -8)]
+    for args, code in cases:
+        with pytest.raises(X.XsymvError) as e:
+            g(*args, stream=0)
+        assert e.value.code == code, (args, e.value.code)
+    zero = (0.0, 0.0) if prec == "w" else 0.0
+    g(0, 2, one, None, 1, one, None, 1, stream=0)         # n == 0
+    g(4, 2, zero, 8, 4, one, 8, 1, stream=0)              # alpha == 0, beta == 1
+
+
+@pytest.mark.parametrize("uplo", ["L", "U"])
+@pytest.mark.parametrize("n,R,G,panel,nshards", [(1000, 256, 37, 16, 3), (4099, 1024, 64, 128, 8),
+                                                 (777, 512, 5, 1, 4)])
+def test_shard_plan_covers_the_shards_triangle_once(uplo, n, R, G, panel, nshards):
+    """For every shard, the strips' local column ranges hold exactly the
+    shard's columns with stored rows in each strip (host plan, no device)."""
+    for g in range(nshards):
+        cols = X.shard_columns(n, panel, nshards, g)
+        NS = (n + R - 1) // R
+        for st in range(NS):
+            rs0, rs1 = st * R, min(n, st * R + R)
+            want = [c for c in cols if (c >= rs0 if uplo == "U" else c < rs1)]
+            if uplo == "U":
+                assert want == cols[len(cols) - len(want):]
+            else:
+                assert want == cols[:len(want)]
+
+
+def _simulate_shard(uplo, n, R, Greq, split, panel, nshards, shard, cpg):
+    """Walk a shard's plan as the kernel and the merge do and check every
+    index they form: local columns in [0, ncol), segment slots in [0, nseg),
+    each (strip, column) of the shard's triangle visited once, the diagonal
+    pass of an upper segment only on a real column, and every partial the
+    merge reads written by some workgroup."""
+    cols = X.shard_columns(n, panel, nshards, shard)
+    ncol = len(cols)
+    blocks, sb, segb, c0 = X.shard_plan(uplo, n, R, Greq, split, panel, nshards, shard)
+    if ncol == 0:
+        assert len(blocks) == 0
+        return
+    NS = (n + R - 1) // R
+    nseg = int(segb[NS])
+    upper = uplo == "U"
+    visited = set()
+    slot_strip = {}
+    for u0, u1, slot, strip in blocks:
+        u = int(u0)
+        while u < u1:
+            assert 0 <= strip < NS
+            sb0, useg = int(sb[strip]), min(int(u1), int(sb[strip + 1]))
+            rs0, rs1 = strip * R, min(n, strip * R + R)
+            coff = (int(c0[strip]) if upper else 0) - sb0
+            assert 0 <= slot < nseg and slot not in slot_strip
+            slot_strip[int(slot)] = strip
+            for g0 in range(u, useg, cpg):
+                jg, ng = g0 + coff, min(cpg, useg - g0)
+                assert 0 <= jg and jg + ng - 1 < ncol
+                for l in range(jg, jg + ng):
+                    c = cols[l]
+                    assert (c >= rs0) if upper else (c < rs1)  # stored rows in the strip
+                    assert (strip, l) not in visited
+                    visited.add((strip, l))
+            if upper and useg > u:
+                assert 0 <= u + coff < ncol
+            u = useg
+            slot += 1
+            strip += 1
+    want = {(s, l) for s in range(NS) for l, c in enumerate(cols)
+            if ((c >= s * R) if upper else (c < min(n, s * R + R)))}
+    assert visited == want
+    gloc = {c: l for l, c in enumerate(cols)}
+    for i in range(n):
+        I = i // R
+        s_lo, nrow = int(segb[I]), int(segb[I + 1] - segb[I])
+        assert nrow >= 0 and 0 <= s_lo and s_lo + nrow <= nseg
+        assert all(slot_strip.get(s) == I for s in range(s_lo, s_lo + nrow))
+        if i in gloc:
+            strips = range(0, I + 1) if upper else range(I, NS)
+            assert all((s, gloc[i]) in visited for s in strips)
+
+
+@pytest.mark.parametrize("uplo", ["L", "U"])
+@pytest.mark.parametrize("n,R", [(1, 1024), (17, 2048), (2111, 2048), (4099, 1024),
+                                 (8549, 4096), (3000, 256)])
+@pytest.mark.parametrize("panel,nshards", [(1, 3), (128, 8), (1024, 8), (37, 5), (4096, 2)])
+def test_shard_plan_indices_in_bounds(uplo, n, R, panel, nshards):
+    """Every shard's plan, including strips that hold none of its columns,
+    keeps the kernel's and the merge's indices in bounds (the check that a
+    strip without columns needs: no slot -1, no column past the local
+    matrix)."""
+    for Greq, split, cpg in ((1, 0, 4), (7, 1, 16), (64, 0, 8), (512, 1, 16)):
+        for g in range(nshards):
+            _simulate_shard(uplo, n, R, Greq, split, panel, nshards, g, cpg)

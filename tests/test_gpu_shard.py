@@ -1,0 +1,215 @@
+"""GPU parity of one GPU's share of the product (the sharded path run shard
+by shard on one GPU) and of the rank-ordered combination, through the C ABI
+against the CPU oracle: every shard's partial within the bound of the
+oracle's, integer inputs bit for bit, nothing outside the stored triangle
+read, the combined result against both the oracle's combination and the
+SYMV oracle, identical bits from run to run, and the per-GPU share at the
+benchmark's order (n = 32768, 8 shards) on sampled rows."""
+import numpy as np
+import pytest
+
+import oracle
+from blas_symmetric_mat_amd import workloads as W
+from tests import gpu_util as G
+from tests import helpers as H
+from tests import test_oracle_shard as SH
+
+pytestmark = pytest.mark.gpu
+
+PRECS = SH.PRECS
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    G.torch_dev()
+
+
+def one(prec):
+    return (1.0, 0.0) if prec == "w" else 1.0
+
+
+def zero(prec):
+    return (0.0, 0.0) if prec == "w" else 0.0
+
+
+def oracle_partial(p, panel, nshards, g):
+    return SH.run_shard(oracle.default(), p, panel, nshards, g)
+
+
+def check_partials(p, panel, nshards, got, label):
+    n = p.n
+    for g in range(nshards):
+        ref = oracle_partial(p, panel, nshards, g)
+        mine = got[g * n:(g + 1) * n]
+        tol = H.shard_tolerance(p, nshards, panel, g) if n <= 2500 else \
+            4.0 * n * H.EPS[p.prec] * H.abs_bound_rows(
+                W.Problem(**{**p.__dict__, "alpha": one(p.prec), "beta": zero(p.prec)}),
+                np.arange(n))
+        d = H.diff(p.prec, mine, ref)
+        assert np.all(np.isfinite(d)), f"{label} shard {g}: non-finite"
+        bad = np.nonzero(~(d <= tol))[0]
+        assert bad.size == 0, f"{label} shard {g}: {bad.size} rows beyond the bound"
+
+
+@pytest.mark.parametrize("prec", PRECS)
+@pytest.mark.parametrize("uplo", ["L", "U"])
+@pytest.mark.parametrize("n,pad,panel,nshards", [(1, 0, 1, 1), (17, 0, 4, 3), (300, 3, 32, 3),
+                                                 (700, 5, 1, 4), (2111, 2, 128, 8),
+                                                 (1500, 0, 1024, 8)])
+def test_shard_parity(prec, uplo, n, pad, panel, nshards):
+    G.log(f"shard {prec} {uplo} n={n} lda={n + pad} panel={panel} shards={nshards}")
+    p = SH.problem(prec, uplo, n, pad, seed=5000 + n)
+    _, got = G.run_shards(p, panel, nshards)
+    check_partials(p, panel, nshards, got, f"{prec}{uplo}{n}")
+
+
+@pytest.mark.parametrize("prec", PRECS)
+@pytest.mark.parametrize("uplo", ["L", "U"])
+def test_shard_several_strips(prec, uplo):
+    """Orders spanning several strips of the shard kernel, ragged ends."""
+    import blas_symmetric_mat_amd as X
+    R = {"s": 4096, "d": 4096, "c": 2048, "z": 2048, "w": 1024}[prec]
+    n = 2 * R + 357
+    G.log(f"shard strips {prec} {uplo} n={n}")
+    p = SH.problem(prec, uplo, n, 1, seed=5100)
+    _, got = G.run_shards(p, 96, 3)
+    check_partials(p, 96, 3, got, f"{prec}{uplo} n={n}")
+    assert X.shard_workspace_bytes(prec, uplo, n, 96, 3, 0) > 0
+
+
+@pytest.mark.parametrize("prec", PRECS)
+@pytest.mark.parametrize("uplo", ["L", "U"])
+def test_shard_integer_bitwise_and_combine(prec, uplo):
+    """Integer S and x: every device partial equals its exact value, and the
+    device combination (alpha = 1.5, beta = -0.5) equals the SYMV oracle's
+    integer result bit for bit."""
+    import blas_symmetric_mat_amd as X
+    n, panel, nshards = 1200, 64, 5
+    p = W.make_integer_problem(prec, uplo, n, n + 3, seed=6, lo=-4, hi=4)
+    P, got = G.run_shards(p, panel, nshards)
+    for g in range(nshards):
+        ref = oracle_partial(p, panel, nshards, g)
+        np.testing.assert_array_equal(got[g * n:(g + 1) * n], ref)  # (up to the sign of zero)
+    y = G.to_device(p.y)
+    getattr(X, G.CBENTRY[prec])(n, nshards, p.alpha, P, n, p.beta, y, 1)
+    np.testing.assert_array_equal(y.cpu().numpy(), oracle.symv_problem(p))
+
+
+@pytest.mark.parametrize("prec", PRECS)
+@pytest.mark.parametrize("uplo", ["L", "U"])
+def test_shard_combine_against_oracles(prec, uplo):
+    """Random inputs: the device combination of the device partials against
+    the oracle's combination of the same partials (bit for bit for s, d, c, z:
+    one fixed order of plain sums) and against S*x (within the bound)."""
+    import blas_symmetric_mat_amd as X
+    n, panel, nshards = 999, 16, 8
+    p = SH.problem(prec, uplo, n, 0, seed=7, alpha=complex(0.75, 0.25) if prec in "cz" else
+                   ((1.25, 0.0) if prec == "w" else 1.25),
+                   beta=complex(0.5, -1.0) if prec in "cz" else ((-0.5, 0.0) if prec == "w"
+                                                                 else -0.5))
+    P, got = G.run_shards(p, panel, nshards)
+    y = G.to_device(p.y)
+    getattr(X, G.CBENTRY[prec])(n, nshards, p.alpha, P, n, p.beta, y, 1)
+    dev = y.cpu().numpy()
+    yo = p.y.copy()
+    assert oracle.combine(prec, n, nshards, p.alpha, np.ascontiguousarray(got), n, p.beta, yo,
+                          1) == 0
+    if prec != "w":
+        assert G.digest(dev) == G.digest(yo)
+    G.assert_close(p, dev, oracle.symv_problem(p), label=f"{prec}{uplo} combined")
+
+
+@pytest.mark.parametrize("prec", PRECS)
+@pytest.mark.parametrize("uplo", ["L", "U"])
+def test_shard_nan_never_read(prec, uplo):
+    """NaN in the other triangle and the padding rows of every local column
+    (and the Hermitian diagonal's imaginary words): partials stay finite."""
+    n, panel, nshards = 777, 48, 3
+    p = SH.problem(prec, uplo, n, 5, seed=8)  # fill: NaN outside the triangle
+    if prec in ("c", "z"):
+        p.A.imag[W.diag_index(n, p.lda)] = np.nan
+    _, got = G.run_shards(p, panel, nshards)
+    assert np.all(np.isfinite(got))
+    q = W.Problem(**{**p.__dict__, "A": np.nan_to_num(p.A, nan=0.0)})
+    check_partials(q, panel, nshards, got, f"{prec}{uplo} NaN")
+
+
+@pytest.mark.parametrize("prec", PRECS)
+@pytest.mark.parametrize("incx", [-1, 3])
+def test_shard_increments(prec, incx):
+    n, panel, nshards = 611, 40, 3
+    p = SH.problem(prec, "U", n, 2, seed=9)
+    xs = W.empty(prec, 1 + (n - 1) * abs(incx))
+    xs[H.vec_index(n, incx)] = p.x
+    q = W.Problem(**{**p.__dict__, "x": xs, "incx": incx})
+    _, got = G.run_shards(q, panel, nshards)
+    _, base = G.run_shards(p, panel, nshards)
+    assert G.digest(got) == G.digest(base)
+
+
+@pytest.mark.parametrize("prec", PRECS)
+def test_combine_rules(prec):
+    """Rank order (fp32: 1, 2^24, -2^24 sum to 0 only in that order),
+    beta = 0 never reads y, alpha = 0 never reads P, strided y."""
+    import blas_symmetric_mat_amd as X
+    f = getattr(X, G.CBENTRY[prec])
+    if prec == "s":
+        P = G.to_device(np.array([1.0, 2.0 ** 24, -(2.0 ** 24)], dtype=np.float32))
+        y = G.to_device(np.array([np.nan], dtype=np.float32))
+        f(1, 3, 1.0, P, 1, 0.0, y, 1)
+        assert y.cpu().numpy()[0] == 0.0
+    n, nshards = 300, 4
+    rng = np.random.default_rng(10)
+    Ph = W.empty(prec, nshards * n)
+    yh = W.empty(prec, 1 + (n - 1) * 3)
+    if prec == "w":
+        Ph[:, 0], Ph[:, 1] = rng.integers(-9, 10, nshards * n), 0.0
+        yh[:, 0], yh[:, 1] = rng.integers(-9, 10, len(yh)), 0.0
+    else:
+        Ph[...] = rng.integers(-9, 10, nshards * n)
+        yh[...] = rng.integers(-9, 10, len(yh))
+    for incy in (1, -3):
+        y0 = yh.copy() if incy != 1 else yh[:n].copy()
+        yo = y0.copy()
+        yd = G.to_device(y0)
+        f(n, nshards, (1.5, 0.0) if prec == "w" else 1.5, G.to_device(Ph), n,
+          (-0.5, 0.0) if prec == "w" else -0.5, yd, incy)
+        oracle.combine(prec, n, nshards, (1.5, 0.0) if prec == "w" else 1.5, Ph, n,
+                       (-0.5, 0.0) if prec == "w" else -0.5, yo, incy)
+        assert G.digest(yd.cpu().numpy()) == G.digest(yo), incy
+    ynan = W.empty(prec, n)
+    ynan[...] = np.nan
+    yd = G.to_device(ynan)
+    f(n, nshards, one(prec), G.to_device(Ph), n, zero(prec), yd, 1)
+    assert np.all(np.isfinite(yd.cpu().numpy()))
+    Pn = W.empty(prec, nshards * n)
+    Pn[...] = np.nan
+    yd = G.to_device(Ph[:n].copy())
+    f(n, nshards, zero(prec), G.to_device(Pn), n, one(prec), yd, 1)  # quick return
+    f(n, nshards, zero(prec), G.to_device(Pn), n, (0.5, 0.0) if prec == "w" else 0.5, yd, 1)
+    assert np.all(np.isfinite(yd.cpu().numpy()))
+
+
+@pytest.mark.parametrize("prec", PRECS)
+def test_shard_bitwise_repeatable(prec):
+    p = SH.problem(prec, "L", 3001, 1, seed=11)
+    digests = {G.digest(G.run_shards(p, 64, 4)[1]) for _ in range(10)}
+    assert len(digests) == 1
+
+
+@pytest.mark.parametrize("prec,uplo", [("s", "L"), ("d", "U")])
+def test_shard_benchmark_order(prec, uplo):
+    """The per-GPU share at the benchmark's order: n = 32768, 8 shards of
+    256-column panels; shard 0's partial on 512 sampled rows against the
+    oracle's, within 4n*eps*(|S||x|)_i."""
+    n, panel, nshards = 32768, 256, 8
+    G.log(f"shard benchmark order {prec} {uplo}")
+    p = W.symv_sweep(prec, uplo, n)
+    _, got = G.run_shards(p, panel, nshards, shards=[0])
+    ref = oracle_partial(p, panel, nshards, 0)
+    rows = np.sort(np.random.default_rng(12).choice(n, 512, replace=False))
+    rows = np.unique(np.concatenate([rows, [0, 1, n - 1, panel - 1, panel, n // 2]]))
+    q = W.Problem(**{**p.__dict__, "alpha": 1.0, "beta": 0.0})
+    tol = 4.0 * n * H.EPS[prec] * H.abs_bound_rows(q, rows)
+    d = H.diff(prec, got[rows], ref[rows])
+    assert np.all(d <= tol)
