@@ -82,3 +82,24 @@ def quad_gemv_rows(p, rows):
            len(rows), hi.ctypes.data, lo.ctypes.data)
     assert rc == 0
     return np.stack([hi, lo], axis=1)
+
+
+ABI_CALLER = os.path.join(_HERE, "bin", "abi_caller")
+
+
+def build_abi_caller() -> str:
+    """Compile the plain host program that calls libxsymv through its C header
+    (hipcc, host code only); libxsymv and the oracle library must be built."""
+    root = os.path.dirname(os.path.dirname(_HERE))
+    os.makedirs(os.path.dirname(ABI_CALLER), exist_ok=True)
+    tmp = ABI_CALLER + f".tmp{os.getpid()}"
+    lib_dir = os.path.join(root, "blas_symmetric_mat_amd")
+    ora_dir = os.path.join(root, "oracle")
+    subprocess.run(["/opt/rocm/bin/hipcc", "-O2", "-std=c++17", "-o", tmp,
+                    os.path.join(_HERE, "abi_caller.cpp"),
+                    "-I", os.path.join(root, "include"), "-I", ora_dir,
+                    "-L", lib_dir, "-lxsymv", "-L", ora_dir, "-loracle_xsymv",
+                    "-Wl,-rpath,$ORIGIN/../../../blas_symmetric_mat_amd:$ORIGIN/../../../oracle"],
+                   check=True)
+    os.replace(tmp, ABI_CALLER)
+    return ABI_CALLER

@@ -117,3 +117,25 @@ def test_syr2_full(prec, uplo, n):
     outs = {G.digest(G.run_syr2(p)) for _ in range(3)}
     assert len(outs) == 1
     assert outs.pop() == G.digest(oracle.syr2_problem(p))
+
+
+# ------------------------------------------------------- triangular product
+
+@pytest.mark.parametrize("prec,uplo,trans,n", [("s", "L", "N", 32768), ("d", "U", "T", 32768),
+                                               ("z", "L", "C", 16384)])
+def test_trmv_full(prec, uplo, trans, n):
+    """The triangular products the benchmark times, at full size: every output
+    against the oracle within 4n*eps*(|op(T)||x|)_i on sampled rows (the
+    bound formed row by row), five identical runs."""
+    from tests import helpers as H
+    p = W.make_trmv_problem(prec, uplo, trans, "N", n, seed=n)
+    G.log(f"workload trmv {prec}{uplo}{trans} n={n}")
+    d = G.TrmvDevice(p)
+    outs = [d.run() for _ in range(5)]
+    assert len({G.digest(o) for o in outs}) == 1, "results differ between runs"
+    ref = oracle.trmv_problem(p)
+    rows = sample_rows(n, seed=n + 3)
+    tol = H.trmv_tolerance(p, rows)
+    dlt = H.diff(prec, outs[0][rows], ref[rows])
+    assert np.all(dlt <= tol), f"{np.sum(~(dlt <= tol))} sampled outputs beyond the bound"
+    G.log(f"  ok ({len(rows)} sampled outputs)")
