@@ -69,6 +69,18 @@ def test_sweep_large(prec, uplo, n):
     check(W.symv_sweep(prec, uplo, n), full=False, reps=5)
 
 
+@pytest.mark.parametrize("uplo", ["L", "U"])
+def test_element_offsets_beyond_2_31(uplo):
+    """n = lda = 46341: the last stored element's index i + j*lda exceeds
+    2^31 - 1 (46341^2 > 2^31), so every offset must be 64-bit; sampled rows
+    (those near the end included) against the oracle, three identical runs."""
+    n = 46341
+    assert (n - 1) + (n - 1) * n > 2 ** 31 - 1
+    p = W.make_problem("s", uplo, n, n, alpha=1.0, beta=1.0, seed=n,
+                       name=f"ssymv-{uplo}-n{n}")
+    check(p, full=False, reps=3)
+
+
 @pytest.mark.parametrize("prec", ["c", "z"])
 def test_hemv_lower_n16384(prec):
     p = W.hemv_lower_n16384(prec)
@@ -117,6 +129,19 @@ def test_syr2_full(prec, uplo, n):
     outs = {G.digest(G.run_syr2(p)) for _ in range(3)}
     assert len(outs) == 1
     assert outs.pop() == G.digest(oracle.syr2_problem(p))
+
+
+@pytest.mark.parametrize("uplo", ["L", "U"])
+def test_syr2_element_offsets_beyond_2_31(uplo):
+    """The rank-2 update writes A: at n = lda = 46341 (indices past 2^31 - 1)
+    the whole updated array, other triangle included, equals the oracle's
+    byte for byte."""
+    from tests import test_oracle_syr2 as R2
+    n = 46341
+    p = R2.problem("s", uplo, n, 0, seed=n, fill=-3.5)
+    G.log(f"workload syr2 s{uplo} n={n}")
+    got = G.digest(G.run_syr2(p))
+    assert got == G.digest(oracle.syr2_problem(p))
 
 
 # ------------------------------------------------------- triangular product
