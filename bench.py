@@ -96,10 +96,15 @@ class Dev:
     def __init__(self, p):
         import numpy as np
         import torch
+        def dev(a):  # host arrays are uploaded; device-drawn tensors are used as they are
+            if isinstance(a, torch.Tensor):
+                return a
+            return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
         self.p = p
-        self.A = torch.from_numpy(np.ascontiguousarray(p.A)).to("cuda")
-        self.x = torch.from_numpy(np.ascontiguousarray(p.x)).to("cuda")
-        self.y0 = torch.from_numpy(np.ascontiguousarray(p.y)).to("cuda")
+        self.A = dev(p.A)
+        self.x = dev(p.x)
+        self.y0 = dev(p.y)
         self.y = self.y0.clone()
         import blas_symmetric_mat_amd as X
         self.f = getattr(X, ENTRY[p.prec])
@@ -454,21 +459,35 @@ def summarize_trace(trace_csv: str, stats_csv: str, command: str) -> str:
     for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
         out.append(f"| `{r['Name'][:110]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                    f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
-    groups = {}
-    for r in trace:
-        key = (r["Kernel_Name"], int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
-        groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-    out += ["", "## Per (kernel, grid) launches from the trace", "",
-            "| kernel | workgroups | threads/wg | launches | mean us | median us |",
-            "|---|---|---|---|---|---|"]
-    for (k, g, wg), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+    # runs: maximal sequences of launches of one (kernel, grid) pair with no
+    # launch of another of the library's kernels between them other than
+    # merge kernels -- bench.py times its workloads one after another, so a
+    # run is one workload's calls even where two workloads share a kernel
+    # and a grid
+    runs = []
+    last = None
+    for r in sorted(trace, key=lambda r: int(r["Start_Timestamp"])):
+        k = r["Kernel_Name"]
         if "xsymv" not in k:
             continue
-        out.append(f"| `{k[:90]}` | {g // wg} | {wg} | {len(d)} | {statistics.mean(d):.1f} | "
+        key = (k, int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
+        if "merge" in k:
+            continue
+        if key != last:
+            runs.append((key, []))
+            last = key
+        runs[-1][1].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    out += ["", "## Streaming-kernel runs from the trace, in launch order", "",
+            "(merge kernels left out; bench.py's workload order: headline, then the "
+            "detail rows as listed in its output)", "",
+            "| # | kernel | workgroups | threads/wg | launches | mean us | median us |",
+            "|---|---|---|---|---|---|---|"]
+    for i, ((k, g, wg), d) in enumerate(runs):
+        out.append(f"| {i} | `{k[:90]}` | {g // wg} | {wg} | {len(d)} | {statistics.mean(d):.1f} | "
                    f"{statistics.median(d):.1f} |")
     # bench.py runs the headline first: `warmup` calls, `steps` timed calls,
     # then `steps` calls timed kernel by kernel -- the first warmup + 2*steps
-    # launches of the most launched streaming kernel (later workloads may
+    # launches of the first streaming kernel launched (later workloads may
     # launch the same kernel on the same grid)
     import re
     def flag(name, default):
@@ -481,7 +500,7 @@ def summarize_trace(trace_csv: str, stats_csv: str, command: str) -> str:
         if "xsymv::symv_" in k and "merge" not in k:
             mains.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     if mains:
-        k, d = max(mains.items(), key=lambda kv: len(kv[1]))
+        k, d = next(iter(mains.items()))  # insertion order = order of first launch
         head = d[:nhead]
         out += ["", "## Headline workload (SSYMV L n = 32768)", "",
                 f"The first {len(head)} launches of `{k[:90]}`: mean "
@@ -670,6 +689,10 @@ def main():
                  ("chemv-L-n16384", lambda: W.hemv_lower_n16384("c")),
                  ("zhemv-L-n16384", lambda: W.hemv_lower_n16384("z")),
                  ("wsymv-L-n8192", W.wsymv_lower_n8192)]
+        # every type at the metric's order n = 32768 (inputs drawn on the
+        # device: the host draw of a 17 GB triangle takes minutes)
+        cases += [(f"{k}-L-n32768-devdraw", lambda prec=prec: W.lower_on_device(prec, 32768))
+                  for prec, k in (("c", "chemv"), ("z", "zhemv"), ("w", "wsymv"))]
         for name, make in cases:
             detail[name] = measure_detail(name, make(), args.detail_reps, flush, rd_med)
         gcases = [("sgemv-N-n32768", lambda: W.gemv_square("s", "N", 32768)),

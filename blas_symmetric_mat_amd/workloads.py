@@ -189,6 +189,81 @@ def make_problem(prec: str, uplo: str, n: int, lda: int | None = None, *,
     return Problem(prec, uplo, n, lda, alpha, beta, A, x, y, name=name)
 
 
+def draw_on_device(prec: str, uplo: str, n: int, lda: int | None = None, *,
+                   alpha: Any = 1.0, beta: Any = 1.0, seed: int = 0,
+                   diag_imag_scale: float | None = None, name: str = "",
+                   device=None) -> Problem:
+    """The distributions of ``make_problem`` (uniform on [-1, 1]; NaN outside
+    the stored triangle; double-double lo = hi*u*2^-53; optional Hermitian
+    diagonal garbage) drawn on ``device`` (default: the current CUDA device)
+    with torch's seeded generator, for orders whose host draw would take
+    minutes.  The
+    values differ from ``make_problem``'s for the same seed; the returned
+    Problem holds torch device tensors in the host arrays' shapes, and
+    ``problem_to_host`` copies it back for the oracle.
+
+    Order of draws: column blocks of A left to right (each block's words,
+    then, for double-double, the blocks' u values), then x, then y, then the
+    diagonal garbage."""
+    import torch
+    if prec not in PRECISIONS:
+        raise ValueError(prec)
+    lda = n if lda is None else lda
+    if lda < max(1, n):
+        raise ValueError("lda < max(1, n)")
+    rdt = torch.float32 if prec in ("s", "c") else torch.float64
+    words = 1 if prec in ("s", "d") else 2
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None \
+        else torch.device(device)
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    upper = uplo in ("U", "u")
+    R = torch.empty((n, lda, words), dtype=rdt, device=dev)  # R[j] = column j
+    rows = torch.arange(lda, device=dev)
+    step = max(1, (1 << 26) // max(1, lda))
+    for j0 in range(0, n, step):
+        blk = R[j0:j0 + step]
+        blk.uniform_(-1.0, 1.0, generator=g)
+        if prec == "w":
+            u = torch.empty_like(blk[..., 1]).uniform_(-1.0, 1.0, generator=g)
+            blk[..., 1] = blk[..., 0] * u * 2.0 ** -53
+        cols = torch.arange(j0, j0 + blk.shape[0], device=dev)[:, None]
+        outside = (rows[None, :] < cols) if not upper else (rows[None, :] > cols)
+        blk.masked_fill_((outside | (rows[None, :] >= n))[..., None], float("nan"))
+
+    def vec():
+        v = torch.empty((n, words), dtype=rdt, device=dev).uniform_(-1.0, 1.0, generator=g)
+        if prec == "w":
+            u = torch.empty(n, dtype=rdt, device=dev).uniform_(-1.0, 1.0, generator=g)
+            v[:, 1] = v[:, 0] * u * 2.0 ** -53
+        return v
+
+    x, y = vec(), vec()
+    if diag_imag_scale is not None:
+        if prec not in ("c", "z"):
+            raise ValueError("diagonal garbage only applies to Hermitian types")
+        d = torch.arange(n, device=dev)
+        R[d, d, 1] = torch.empty(n, dtype=rdt, device=dev).uniform_(
+            -diag_imag_scale, diag_imag_scale, generator=g)
+
+    def shaped(t, count):
+        t = t.reshape(count, words)
+        if prec in ("s", "d"):
+            return t.reshape(count)
+        return torch.view_as_complex(t) if prec in ("c", "z") else t
+
+    return Problem(prec, uplo, n, lda, alpha, beta, shaped(R, lda * n), shaped(x, n),
+                   shaped(y, n), name=name)
+
+
+def problem_to_host(p: Problem) -> Problem:
+    """A copy of ``p`` whose arrays are host numpy arrays (device tensors are
+    copied back)."""
+    def host(a):
+        return a if isinstance(a, np.ndarray) else a.cpu().numpy()
+    return dataclasses.replace(p, A=host(p.A), x=host(p.x), y=host(p.y))
+
+
 def make_integer_problem(prec: str, uplo: str, n: int, lda: int | None = None, *,
                          alpha: Any = 1.5, beta: Any = -0.5, seed: int = 0,
                          lo: int = -3, hi: int = 3, fill: float = np.nan) -> Problem:
@@ -379,6 +454,18 @@ def wsymv_lower_n8192(n: int = 8192) -> Problem:
     and lo = hi*u*2^-53; alpha = beta = (1, 0); seed 4."""
     return make_problem("w", "L", n, n, alpha=(1.0, 0.0), beta=(1.0, 0.0),
                         seed=4, name=f"wsymv-L-n{n}")
+
+
+def lower_on_device(prec: str, n: int = 32768) -> Problem:
+    """uplo = L, lda = n, seed n, drawn on the device: [SD]SYMV with
+    alpha = beta = 1; [CZ]HEMV with the n = 16384 workload's scalars and
+    diagonal garbage; WSYMV with alpha = beta = (1, 0)."""
+    kw = {"s": dict(alpha=1.0, beta=1.0), "d": dict(alpha=1.0, beta=1.0),
+          "c": dict(alpha=complex(0.75, 0.25), beta=complex(0.5, -1.0), diag_imag_scale=1e3),
+          "z": dict(alpha=complex(0.75, 0.25), beta=complex(0.5, -1.0), diag_imag_scale=1e3),
+          "w": dict(alpha=(1.0, 0.0), beta=(1.0, 0.0))}[prec]
+    kind = "hemv" if prec in ("c", "z") else "symv"
+    return draw_on_device(prec, "L", n, n, seed=n, name=f"{prec}{kind}-L-n{n}-devdraw", **kw)
 
 
 def gemv_square(prec: str, trans: str, n: int) -> GemvProblem:

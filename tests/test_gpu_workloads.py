@@ -97,6 +97,33 @@ def test_wsymv_lower_n8192():
     check(W.wsymv_lower_n8192(), full=True)
 
 
+@pytest.mark.parametrize("prec", ["c", "z", "w"])
+def test_lower_n32768_device_drawn(prec):
+    """CHEMV, ZHEMV and WSYMV at n = 32768 (uplo = L, the inputs the
+    benchmark times there, drawn on the device): three identical runs, then
+    sampled rows against the oracle on the inputs copied back to the host."""
+    import torch
+    import blas_symmetric_mat_amd as X
+    G.log(f"device-drawn {prec} L n=32768")
+    p = W.lower_on_device(prec, 32768)
+    outs = set()
+    for _ in range(3):
+        y = p.y.clone()
+        getattr(X, G.ENTRY[prec])(p.uplo, p.n, p.alpha, p.A, p.lda, p.x, p.incx, p.beta, y,
+                                  p.incy)
+        torch.cuda.synchronize()
+        got = y.cpu().numpy()
+        outs.add(G.digest(got))
+    assert len(outs) == 1, "results differ between runs"
+    h = W.problem_to_host(p)
+    del p, y
+    torch.cuda.empty_cache()
+    rows = sample_rows(h.n, seed=h.n, k=100)
+    ref = oracle.rows_problem(h, rows)
+    G.assert_close(h, got[rows], ref, rows=rows, label=h.name)
+    G.log(f"  ok ({len(rows)} sampled rows)")
+
+
 # ------------------------------------------- xGEMV beside the symmetric sweep
 
 @pytest.mark.parametrize("prec,trans,n", [("s", "N", 32768), ("s", "T", 32768),
