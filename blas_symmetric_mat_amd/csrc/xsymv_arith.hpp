@@ -22,7 +22,11 @@
 // Double-double arithmetic is written from the published error-free
 // transformations: Knuth's TwoSum, Dekker's FastTwoSum, TwoProd with one
 // fused multiply-add, and the accurate double-double addition and the
-// multiplication of Hida, Li and Bailey (the report's reference [14]).
+// multiplication of Hida, Li and Bailey (the report's reference [14]).  The
+// accumulating multiply-add (mac, macc) takes that library's cheaper addition
+// instead -- one TwoSum of the high words -- which is what the report's count
+// of about 21 double operations per double-double operation (§2.2) implies;
+// merges and reductions keep the accurate addition.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -284,11 +288,31 @@ __device__ __forceinline__ ddreal dd_mul(ddreal a, ddreal b)
     return dd_fast_two_sum(p, e);
 }
 
+// Multiply-add for accumulations, acc + a*b in 15 double operations: the
+// product's error words (the fma-exact error of hi*hi plus both cross
+// products) are not renormalised but added to acc.lo, and one TwoSum joins the
+// high words before a final FastTwoSum.  With u = 2^-53, the product errs
+// by at most about 6u^2|a||b| (two fma roundings, lo*lo dropped) and the
+// addition by u^2(3|acc| + 7|a||b|): not relative to a cancelled sum, as the
+// accurate addition's error is, but a chain of k such steps stays within
+// about (3k + 13)u^2 * sum|a_j||b_j|, inside the componentwise bound
+// 4*n*2^-104*(|alpha||S||x| + |beta||y|) = 16*n*u^2*(...) that the results
+// are held to.
+__device__ __forceinline__ ddreal dd_madd(ddreal acc, ddreal a, ddreal b)
+{
+    const double p = a.hi * b.hi;
+    double e = __builtin_fma(a.hi, b.hi, -p);
+    e = __builtin_fma(a.hi, b.lo, e);
+    e = __builtin_fma(a.lo, b.hi, e);
+    const ddreal s = dd_two_sum(acc.hi, p);
+    return dd_fast_two_sum(s.hi, s.lo + (acc.lo + e));
+}
+
 template <> struct Elem<ddreal> {
     static constexpr int VEC = 1;
     __device__ static ddreal zero() { return {0.0, 0.0}; }
-    __device__ static ddreal mac(ddreal acc, ddreal a, ddreal x) { return dd_add(acc, dd_mul(a, x)); }
-    __device__ static ddreal macc(ddreal acc, ddreal a, ddreal x) { return dd_add(acc, dd_mul(a, x)); }
+    __device__ static ddreal mac(ddreal acc, ddreal a, ddreal x) { return dd_madd(acc, a, x); }
+    __device__ static ddreal macc(ddreal acc, ddreal a, ddreal x) { return dd_madd(acc, a, x); }
     __device__ static ddreal add(ddreal a, ddreal b) { return dd_add(a, b); }
     __device__ static ddreal mul(ddreal a, ddreal b) { return dd_mul(a, b); }
     __device__ static ddreal diag_load(const ddreal* p) { return *p; }

@@ -264,6 +264,73 @@ def problem_to_host(p: Problem) -> Problem:
     return dataclasses.replace(p, A=host(p.A), x=host(p.x), y=host(p.y))
 
 
+CANCEL_SCALE = {"s": 2.0 ** -12, "d": 2.0 ** -30, "c": 2.0 ** -12, "z": 2.0 ** -30,
+                "w": 2.0 ** -60}
+
+
+def make_cancelling_problem(prec: str, uplo: str, n: int, lda: int | None = None, *,
+                            seed: int = 0, alpha: Any = 1.0, beta: Any = 0.0,
+                            fill: float = np.nan, name: str = "") -> Problem:
+    """Heavy cancellation in every row: S = kron(B, [[1, 1], [1, 1]]) + c*E
+    (B, E symmetric, Hermitian for complex types, entries uniform on [-1, 1];
+    c = CANCEL_SCALE[prec]) and x made of pairs (v, -v), so that row i of S*x
+    is about c*(E*x)_i while (|S||x|)_i grows with n.  For double-double the
+    hi words hold kron(B, J) and the lo words c*E: every row's hi products
+    cancel exactly and the result comes from the lo words alone.  ``n`` must
+    be even.
+
+    Draws: B's lower triangle column by column, then E's, then v, then y
+    (B, E, v, y as make_problem draws elements; complex values take two
+    draws)."""
+    if n % 2:
+        raise ValueError("n must be even")
+    lda = n if lda is None else lda
+    rng = np.random.Generator(np.random.PCG64(seed))
+    m = n // 2
+    cplx = prec in ("c", "z")
+
+    def draw(kind, count):
+        return draw_into(rng, kind, empty(kind, count, 0.0))
+
+    def sym(k):
+        """Symmetric (Hermitian) k x k matrix from its drawn lower triangle."""
+        t = np.zeros((k, k), dtype=np.complex128 if cplx else np.float64)
+        for j in range(k):
+            col = draw("z" if cplx else "d", k - j)
+            t[j:, j] = col
+        full = np.tril(t) + np.tril(t, -1).conj().T
+        if cplx:
+            full[np.diag_indices(k)] = full.diagonal().real
+        return full
+
+    B = sym(m)
+    E = sym(n)
+    J = np.ones((2, 2))
+    c = CANCEL_SCALE[prec]
+    if prec == "w":
+        hi = np.kron(B, J)
+        lo = c * E
+        dense = np.stack([hi, lo], axis=-1)             # (n, n, 2)
+    else:
+        dense = (np.kron(B, J) + c * E).astype(_DTYPE[prec][0])
+    v = draw(prec, m)
+    if prec == "w":
+        x = np.empty((n, 2))
+        x[0::2] = v
+        x[1::2] = -v
+    else:
+        x = np.empty(n, dtype=_DTYPE[prec][0])
+        x[0::2] = v
+        x[1::2] = -v
+    y = draw(prec, n)
+    A = empty(prec, lda * n, fill)
+    upper = uplo in ("U", "u")
+    for j in range(n):
+        r0, r1 = (0, j + 1) if upper else (j, n)
+        A[j * lda + r0: j * lda + r1] = dense[r0:r1, j]
+    return Problem(prec, uplo, n, lda, alpha, beta, A, x, y, name=name or f"cancel-{prec}{uplo}{n}")
+
+
 def make_integer_problem(prec: str, uplo: str, n: int, lda: int | None = None, *,
                          alpha: Any = 1.5, beta: Any = -0.5, seed: int = 0,
                          lo: int = -3, hi: int = 3, fill: float = np.nan) -> Problem:
