@@ -1,0 +1,130 @@
+"""bench.py's host logic on the CPU: the one-GPU guard, the rocprofv3 kernel
+trace and counter summaries (on synthetic CSV files of rocprofv3's columns),
+and the digest gate that keeps a stale counter record out of the bench line."""
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+HEAD = "void xsymv::symv_strip<float, false, 16, 1, 16, true, 256, false>(xsymv::StripArgs<float>)"
+MERGE = "void xsymv::symv_strip_merge<float, 16, false>(xsymv::StripMergeArgs<float>)"
+OTHER = "void xsymv::symv_strip<double, true, 16, 1, 16, true, 256, false>(xsymv::StripArgs<double>)"
+SHARD = "void xsymv::symv_strip<float, false, 16, 1, 16, true, 256, true>(xsymv::StripArgs<float>)"
+
+
+@pytest.mark.parametrize("argv,env", [(["--gpus", "2"], {}), (["--gpus", "8"], {}),
+                                      ([], {"WORLD_SIZE": "2"})])
+def test_more_than_one_gpu_exits_with_message(argv, env):
+    r = subprocess.run([sys.executable, "bench.py", *argv], cwd=ROOT, capture_output=True,
+                       text=True, timeout=120, env={**os.environ, **env})
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+    assert r.stdout == ""
+
+
+def write_csv(path, rows):
+    with open(path, "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=list(rows[0]))
+        w.writeheader()
+        w.writerows(rows)
+
+
+def test_trace_summary_runs_and_headline(tmp_path):
+    """Launch order: the headline kernel (5 launches of 100 us, each followed
+    by a merge), another workload, the headline's kernel and grid again for a
+    later workload (3 x 200 us), then a kernel launched more often than the
+    headline's (10 x 50 us).  The runs table keeps the two runs of the same
+    kernel and grid apart, and the headline section takes the first kernel
+    launched, not the most launched one."""
+    trace, t = [], 0
+
+    def launch(name, grid, us):
+        nonlocal t
+        trace.append({"Kernel_Name": name, "Grid_Size_X": grid, "Workgroup_Size_X": 1024,
+                      "Start_Timestamp": t, "End_Timestamp": t + int(us * 1000)})
+        t += int(us * 1000) + 500
+
+    for _ in range(5):
+        launch(HEAD, 262144, 100)
+        launch(MERGE, 32768, 7)
+    for _ in range(2):
+        launch(OTHER, 262144, 600)
+    for _ in range(3):
+        launch(HEAD, 262144, 200)
+        launch(MERGE, 32768, 7)
+    for _ in range(10):
+        launch(SHARD, 262144, 50)
+    stats = []
+    for name in (HEAD, MERGE, OTHER, SHARD):
+        d = [(r["End_Timestamp"] - r["Start_Timestamp"]) for r in trace if r["Kernel_Name"] == name]
+        stats.append({"Name": name, "Calls": len(d), "TotalDurationNs": sum(d),
+                      "AverageNs": sum(d) / len(d), "MinNs": min(d), "MaxNs": max(d)})
+    write_csv(tmp_path / "trace.csv", trace)
+    write_csv(tmp_path / "stats.csv", stats)
+    md = bench.summarize_trace(str(tmp_path / "trace.csv"), str(tmp_path / "stats.csv"),
+                               "rocprofv3 ... -- python3 bench.py --steps 2 --warmup 1")
+    runs = [line for line in md.splitlines() if line.startswith("| ") and "`" in line
+            and line.split("|")[1].strip().isdigit()]
+    got = [(int(r.split("|")[1]), r.split("|")[2].strip().strip("`"), int(r.split("|")[5]),
+            float(r.split("|")[6])) for r in runs]
+    assert got == [(0, HEAD[:90], 5, 100.0), (1, OTHER[:90], 2, 600.0),
+                   (2, HEAD[:90], 3, 200.0), (3, SHARD[:90], 10, 50.0)]
+    head = md.split("## Headline workload")[1]
+    # warmup + 2 * steps = 5 launches of the first kernel launched
+    assert f"The first 5 launches of `{HEAD[:90]}`: mean 100.0 us" in head
+
+
+def test_counter_summary_scales_by_the_calibration_kernel(tmp_path):
+    """FETCH_SIZE reads 524288 KiB and WRITE_SIZE 1048576 KiB for the 1 GiB
+    calibration kernel (scales 2 and 1); the streaming kernel's readings are
+    scaled by them and the merge kernel is left out."""
+    neg = "void at::native::vectorized_elementwise_kernel<neg_kernel_cuda>(...)"
+    fetch = [{"Kernel_Name": neg, "Grid_Size": 4096, "Counter_Value": 524288.0}]
+    write = [{"Kernel_Name": neg, "Grid_Size": 4096, "Counter_Value": 1048576.0}]
+    for v in (1000000.0, 1000002.0):
+        fetch.append({"Kernel_Name": HEAD, "Grid_Size": 262144, "Counter_Value": v})
+        write.append({"Kernel_Name": HEAD, "Grid_Size": 262144, "Counter_Value": 4000.0})
+        fetch.append({"Kernel_Name": MERGE, "Grid_Size": 32768, "Counter_Value": 9.0e6})
+        write.append({"Kernel_Name": MERGE, "Grid_Size": 32768, "Counter_Value": 100.0})
+    write_csv(tmp_path / "f.csv", fetch)
+    write_csv(tmp_path / "w.csv", write)
+    rec = bench.summarize_pmc(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), "cmd",
+                              workload="ssymv-L-n32768")["ssymv-L-n32768"]
+    assert rec["kernel"] == HEAD
+    assert rec["fetch_scale"] == 2.0 and rec["write_scale"] == 1.0
+    assert rec["fetch_bytes_per_launch"] == 1000001 * 1024 * 2
+    assert rec["write_bytes_per_launch"] == 4000 * 1024
+    assert rec["bytes_per_launch"] == 1000001 * 1024 * 2 + 4000 * 1024
+    assert rec["launches"] == 2 and rec["grid_threads"] == 262144
+    assert rec["kernel_source_digest"] == bench.kernel_source_digest()
+
+
+def test_counter_summary_needs_the_calibration_kernel(tmp_path):
+    rows = [{"Kernel_Name": HEAD, "Grid_Size": 262144, "Counter_Value": 1.0}]
+    write_csv(tmp_path / "f.csv", rows)
+    write_csv(tmp_path / "w.csv", rows)
+    with pytest.raises(ValueError, match="calibration"):
+        bench.summarize_pmc(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), "cmd",
+                            workload="ssymv-L-n32768")
+
+
+def test_traffic_record_only_for_current_source_and_configuration(tmp_path, monkeypatch):
+    path = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(path))
+    assert bench.traffic_record("ssymv-L-n32768", "cfg") is None  # no file
+    rec = {"kernel_config": "cfg", "kernel_source_digest": bench.kernel_source_digest(),
+           "bytes_per_launch": 5}
+    path.write_text(json.dumps({"ssymv-L-n32768": rec}))
+    assert bench.traffic_record("ssymv-L-n32768", "cfg")["bytes_per_launch"] == 5
+    assert bench.traffic_record("ssymv-L-n32768", "another cfg") is None
+    assert bench.traffic_record("dsymv-L-n32768", "cfg") is None
+    path.write_text(json.dumps({"ssymv-L-n32768": {**rec, "kernel_source_digest": "0" * 16}}))
+    assert bench.traffic_record("ssymv-L-n32768", "cfg") is None
+
