@@ -444,7 +444,8 @@ def measure_detail(name, p, reps, flush, read_peak=None):
     return out
 
 
-def summarize_trace(trace_csv: str, stats_csv: str, command: str) -> str:
+def summarize_trace(trace_csv: str, stats_csv: str, command: str,
+                    bench_json: str | None = None) -> str:
     """Markdown summary of a rocprofv3 --kernel-trace --stats run: every
     kernel's calls and mean duration from the stats file, and the per-launch
     durations of each (kernel, grid) pair from the trace (a grid size
@@ -502,12 +503,22 @@ def summarize_trace(trace_csv: str, stats_csv: str, command: str) -> str:
     if mains:
         k, d = next(iter(mains.items()))  # insertion order = order of first launch
         head = d[:nhead]
+        timed = head[-flag("steps", 50):]
         out += ["", "## Headline workload (SSYMV L n = 32768)", "",
                 f"The first {len(head)} launches of `{k[:90]}`: mean "
                 f"{statistics.mean(head):.1f} us, median {statistics.median(head):.1f} us, "
                 f"min {min(head):.1f} us, max {max(head):.1f} us.  bench.py's "
                 "`roofline.launch_ms_mean` is the mean of the last `steps` of these, "
-                "timed with HIP events on the launch stream."]
+                "timed with HIP events on the launch stream; in the trace those "
+                f"{len(timed)} launches average {statistics.mean(timed):.1f} us."]
+        if bench_json:
+            line = open(bench_json).read().strip().splitlines()[-1]
+            roof = json.loads(line)["roofline"]
+            ev = roof["launch_ms_mean"] * 1e3
+            out += ["", f"The bench line of this profiled run: `launch_ms_mean` {ev:.1f} us "
+                        f"({100 * (ev / statistics.mean(timed) - 1):+.1f} % against the trace: "
+                        "the events also hold the gap between launches), `achieved` "
+                        f"{roof['achieved']} GB/s, `frac` {roof['frac']}."]
     return "\n".join(out) + "\n"
 
 
@@ -560,6 +571,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--summarize-trace", nargs=3, metavar=("TRACE_CSV", "STATS_CSV", "COMMAND"),
                     help="print a markdown summary of a rocprofv3 kernel trace and exit")
+    ap.add_argument("--bench-json", help="with --summarize-trace: the profiled run's bench "
+                    "output, whose launch_ms_mean the summary sets beside the trace's")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"),
                     help="write profiles/traffic_counters.json from two rocprofv3 --pmc "
                          "runs of the headline workload and exit")
@@ -568,7 +581,7 @@ def main():
                          "rocprofv3 FETCH_SIZE/WRITE_SIZE readings")
     args = ap.parse_args()
     if args.summarize_trace:
-        print(summarize_trace(*args.summarize_trace), end="")
+        print(summarize_trace(*args.summarize_trace, bench_json=args.bench_json), end="")
         return
     if args.summarize_pmc:
         rec = summarize_pmc(*args.summarize_pmc, workload="ssymv-L-n32768")
