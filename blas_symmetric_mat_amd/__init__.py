@@ -85,6 +85,14 @@ def library():
                 raise ImportError(
                     f"{LIB_PATH} is missing: build it with "
                     "`python -m blas_symmetric_mat_amd.build` (hipcc, gfx950)")
+            # torch carries its own HIP runtime: load it first, so that this
+            # library's HIP dependency resolves to the same runtime and the
+            # process holds one (two runtimes in one process do not share
+            # the device: calls through the second fail with "no device")
+            try:
+                import torch  # noqa: F401
+            except ImportError:
+                pass
             lib = ctypes.CDLL(LIB_PATH)
             vp, ci, cc = ctypes.c_void_p, ctypes.c_int, ctypes.c_char
             for p, nm in _ENTRY.items():

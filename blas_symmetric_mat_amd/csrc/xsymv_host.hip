@@ -787,8 +787,7 @@ using namespace xsymv;
 // Plain streaming read, the reference point for "% of a measured
 // stream-read peak": workgroup b reads its own contiguous chunk of `per`
 // 16-byte vectors (non-temporal loads, U in flight per lane; `per` is a
-// multiple of 256*U, so no load is guarded).  Each workgroup writes one word
-// so the loads are not removed.
+// multiple of 256*U, so no load is guarded).
 template <int U>
 static __global__ __launch_bounds__(256) void read_probe(const xsymv::u32x4* __restrict__ a,
                                                            long long per, uint32_t* out)
@@ -802,14 +801,29 @@ static __global__ __launch_bounds__(256) void read_probe(const xsymv::u32x4* __r
 #pragma unroll
         for (int k = 0; k < U; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
     }
-    __shared__ uint32_t red[256];
-    red[threadIdx.x] = acc;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t t = 0;
-        for (int k = 0; k < 256; ++k) t ^= red[k];
-        out[blockIdx.x] = t;
+    // a store that depends on every load keeps them; it almost never happens
+    // (a block-wide reduction here measurably lengthens the launch)
+    if (acc == 0x9e3779b9u) out[blockIdx.x] = acc;
+}
+
+// The same read with every resident workgroup sweeping one address window:
+// tile t (1024*U consecutive vectors) goes to workgroup t mod gridDim, so at
+// any moment the device reads neighbouring tiles (measured faster on MI355X
+// than a private chunk per workgroup).
+template <int U>
+static __global__ __launch_bounds__(1024) void read_probe_sweep(const xsymv::u32x4* __restrict__ a,
+                                                                long long ntiles, uint32_t* out)
+{
+    uint32_t acc = 0;
+    for (long long t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const xsymv::u32x4* __restrict__ p = a + t * (1024 * U) + threadIdx.x;
+        xsymv::u32x4 v[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) v[k] = __builtin_nontemporal_load(p + k * 1024);
+#pragma unroll
+        for (int k = 0; k < U; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
     }
+    if (acc == 0x9e3779b9u) out[blockIdx.x] = acc;
 }
 
 static __global__ __launch_bounds__(256) void fill_probe(uint32_t* buf, long long words)
@@ -855,31 +869,40 @@ int xsymv_read_bandwidth(size_t bytes, int reps, void* stream, float* gbps, floa
         fail(e);
         goto done;
     }
-    // a few layouts (workgroups x loads in flight per lane); the best median wins
-    for (int blocks : {2048, 8192, MAXB}) {
-        for (int u : {4, 8}) {
-            const long long per = vecs / blocks / (256 * u) * (256 * u);
-            if (per == 0) continue;
-            std::vector<float> t;
-            for (int r = 0; r < reps + 1 && rc == 0; ++r) {
-                if ((e = hipEventRecord(e0, st)) != hipSuccess) { fail(e); break; }
-                if (u == 4)
-                    read_probe<4><<<blocks, 256, 0, st>>>(a, per, out);
-                else
-                    read_probe<8><<<blocks, 256, 0, st>>>(a, per, out);
-                if ((e = hipGetLastError()) != hipSuccess) { fail(e); break; }
-                if ((e = hipEventRecord(e1, st)) != hipSuccess) { fail(e); break; }
-                if ((e = hipEventSynchronize(e1)) != hipSuccess) { fail(e); break; }
-                float ms = 0.f;
-                if ((e = hipEventElapsedTime(&ms, e0, e1)) != hipSuccess) { fail(e); break; }
-                if (r >= 1) t.push_back(ms);
-            }
-            if (rc) goto done;
-            std::sort(t.begin(), t.end());
-            const double b = (double)per * blocks * 16;
-            best_med = std::max(best_med, (float)(b / (t[t.size() / 2] * 1e-3) / 1e9));
-            best_any = std::max(best_any, (float)(b / (t[0] * 1e-3) / 1e9));
+    // a few layouts: a private chunk per workgroup (workgroups x loads in
+    // flight per lane), then tiles swept by 1024-thread workgroups (grid x
+    // loads in flight); the best median wins
+    static const int chunk_blocks[3] = {2048, 8192, MAXB};
+    for (int layout = 0; layout < 10; ++layout) {
+        const bool sweep = layout >= 6;
+        const int blocks = sweep ? (layout & 1 ? 512 : 256) : chunk_blocks[layout / 2];
+        const int u = sweep ? (layout < 8 ? 2 : 4) : (layout & 1 ? 8 : 4);
+        // private chunks: per vectors per workgroup; sweep: ntiles tiles
+        const long long per = sweep ? vecs / (1024 * u) : vecs / blocks / (256 * u) * (256 * u);
+        if (per == 0) continue;
+        std::vector<float> t;
+        for (int r = 0; r < reps + 1 && rc == 0; ++r) {
+            if ((e = hipEventRecord(e0, st)) != hipSuccess) { fail(e); break; }
+            if (sweep && u == 2)
+                read_probe_sweep<2><<<blocks, 1024, 0, st>>>(a, per, out);
+            else if (sweep)
+                read_probe_sweep<4><<<blocks, 1024, 0, st>>>(a, per, out);
+            else if (u == 4)
+                read_probe<4><<<blocks, 256, 0, st>>>(a, per, out);
+            else
+                read_probe<8><<<blocks, 256, 0, st>>>(a, per, out);
+            if ((e = hipGetLastError()) != hipSuccess) { fail(e); break; }
+            if ((e = hipEventRecord(e1, st)) != hipSuccess) { fail(e); break; }
+            if ((e = hipEventSynchronize(e1)) != hipSuccess) { fail(e); break; }
+            float ms = 0.f;
+            if ((e = hipEventElapsedTime(&ms, e0, e1)) != hipSuccess) { fail(e); break; }
+            if (r >= 1) t.push_back(ms);
         }
+        if (rc) goto done;
+        std::sort(t.begin(), t.end());
+        const double b = sweep ? (double)per * 1024 * u * 16 : (double)per * blocks * 16;
+        best_med = std::max(best_med, (float)(b / (t[t.size() / 2] * 1e-3) / 1e9));
+        best_any = std::max(best_any, (float)(b / (t[0] * 1e-3) / 1e9));
     }
     if (gbps) *gbps = best_med;
     if (best_gbps) *best_gbps = best_any;

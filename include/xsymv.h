@@ -424,10 +424,12 @@ int xsymv_strip_plan(char uplo, int n, int R, int G, int split, int *blocks4,
  * reference for "% of a measured stream-read peak" (the report puts its
  * results against both the specification and a measured bandwidth, §4).
  * Allocates `bytes` (>= 64 MiB) of device memory, fills it, then, for each
- * of a few layouts (2048, 8192 or 32768 workgroups of 256 lanes, each
- * reading its own contiguous chunk with 4 or 8 non-temporal 16-byte loads in
- * flight per lane), times `reps` launches (after one warm-up) on `stream`;
- * frees the buffer and synchronises the stream.  Writes the best layout's
+ * of ten layouts, times `reps` launches (after one warm-up) on `stream`:
+ * 2048, 8192 or 32768 workgroups of 256 lanes, each reading its own
+ * contiguous chunk with 4 or 8 non-temporal 16-byte loads in flight per
+ * lane; and 256 or 512 workgroups of 1024 lanes sweeping the buffer together
+ * in tiles of 2 or 4 such loads per lane (tile t to workgroup t mod grid).
+ * Frees the buffer and synchronises the stream.  Writes the best layout's
  * median rate and the best single launch in GB/s (either may be NULL).
  * Returns 0, -1 for bad arguments or 1000 + hipError_t. */
 int xsymv_read_bandwidth(size_t bytes, int reps, void *stream, float *gbps,

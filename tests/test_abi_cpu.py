@@ -186,6 +186,13 @@ def test_set_workspace_argument_check():
     assert X.library().xsymv_set_workspace(None, 64, None) == -2
 
 
+def test_read_bandwidth_argument_check():
+    # below 64 MiB, or no repetition: refused before any allocation
+    lib = X.library()
+    assert lib.xsymv_read_bandwidth((64 << 20) - 1, 3, None, None, None) == -1
+    assert lib.xsymv_read_bandwidth(64 << 20, 0, None, None, None) == -1
+
+
 @pytest.mark.parametrize("prec", ["s", "d", "c", "z", "w"])
 def test_gemv_argument_errors_before_device_work(prec):
     f = getattr(X, "xgemv_" + prec)

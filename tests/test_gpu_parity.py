@@ -245,3 +245,14 @@ def test_installed_workspace(prec, uplo):
         X.set_workspace(None, stream=stream)
     assert G.digest(got) == G.digest(ref)
     assert G.digest(again) == G.digest(ref)
+
+
+def test_read_bandwidth_reference():
+    """The stream-read reference the benchmark divides by: positive, below the
+    8 TB/s specification, the best launch at least the median, on a buffer of
+    4 GiB (16 times the last-level cache) whose size is not a multiple of any
+    layout's tile."""
+    import blas_symmetric_mat_amd as X
+    G.log("read bandwidth reference")
+    med, best = X.read_bandwidth((4 << 30) + 4096 * 3, reps=3)
+    assert 500.0 < med <= best and med < 8000.0, (med, best)
