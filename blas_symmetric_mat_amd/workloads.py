@@ -256,9 +256,42 @@ def draw_on_device(prec: str, uplo: str, n: int, lda: int | None = None, *,
                    shaped(y, n), name=name)
 
 
-def problem_to_host(p: Problem) -> Problem:
-    """A copy of ``p`` whose arrays are host numpy arrays (device tensors are
-    copied back)."""
+def gemv_on_device(prec: str, trans: str, m: int, n: int, *, alpha: Any = 1.0,
+                   beta: Any = 1.0, seed: int = 0, name: str = "",
+                   device=None) -> "GemvProblem":
+    """A general m x n product (lda = m) drawn on ``device`` (default: the
+    current CUDA device) with torch's seeded generator: A, x and y uniform on
+    [-1, 1] (double-double lo = hi*u*2^-53), drawn in that order -- for orders
+    whose host draw would take minutes."""
+    import torch
+    if prec not in PRECISIONS:
+        raise ValueError(prec)
+    rdt = torch.float32 if prec in ("s", "c") else torch.float64
+    words = 1 if prec in ("s", "d") else 2
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None \
+        else torch.device(device)
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+
+    def draw_elems(count):
+        t = torch.empty((count, words), dtype=rdt, device=dev).uniform_(-1.0, 1.0, generator=g)
+        if prec == "w":
+            u = torch.empty(count, dtype=rdt, device=dev).uniform_(-1.0, 1.0, generator=g)
+            t[:, 1] = t[:, 0] * u * 2.0 ** -53
+        if prec in ("s", "d"):
+            return t.reshape(count)
+        return torch.view_as_complex(t) if prec in ("c", "z") else t
+
+    lenx, leny = (n, m) if trans in ("N", "n") else (m, n)
+    A = draw_elems(m * n)
+    x = draw_elems(lenx)
+    y = draw_elems(leny)
+    return GemvProblem(prec, trans, m, n, m, alpha, beta, A, x, y, name=name)
+
+
+def problem_to_host(p):
+    """A copy of the problem ``p`` (symmetric or general) whose arrays are
+    host numpy arrays (device tensors are copied back)."""
     def host(a):
         return a if isinstance(a, np.ndarray) else a.cpu().numpy()
     return dataclasses.replace(p, A=host(p.A), x=host(p.x), y=host(p.y))

@@ -143,6 +143,34 @@ def test_gemv_square(prec, trans, n):
     G.log(f"  ok ({len(rows)} sampled outputs)")
 
 
+@pytest.mark.parametrize("trans", ["N", "T"])
+def test_gemv_element_offsets_beyond_2_31(trans):
+    """m = n = lda = 46341 (the last element's index past 2^31 - 1), inputs
+    drawn on the device: sampled outputs against the oracle on the inputs
+    copied back, three identical runs."""
+    import torch
+    import blas_symmetric_mat_amd as X
+    n = 46341
+    assert (n - 1) + (n - 1) * n > 2 ** 31 - 1
+    G.log(f"gemv s{trans} m=n={n}")
+    p = W.gemv_on_device("s", trans, n, n, seed=n, name=f"sgemv-{trans}-n{n}")
+    outs = set()
+    for _ in range(3):
+        y = p.y.clone()
+        X.xgemv_s(trans, n, n, p.alpha, p.A, n, p.x, 1, p.beta, y, 1)
+        torch.cuda.synchronize()
+        got = y.cpu().numpy()
+        outs.add(G.digest(got))
+    assert len(outs) == 1, "results differ between runs"
+    h = W.problem_to_host(p)
+    del p, y
+    torch.cuda.empty_cache()
+    rows = sample_rows(n, seed=n + 7, k=100)
+    ref = oracle.gemv_rows_problem(h, rows)
+    G.assert_close_gemv(h, got[rows], ref, rows=rows, label=h.name)
+    G.log(f"  ok ({len(rows)} sampled outputs)")
+
+
 # ------------------------------------------------------- rank-2 update
 
 @pytest.mark.parametrize("prec,uplo,n", [("s", "L", 16384), ("d", "U", 8192),
@@ -189,5 +217,32 @@ def test_trmv_full(prec, uplo, trans, n):
     rows = sample_rows(n, seed=n + 3)
     tol = H.trmv_tolerance(p, rows)
     dlt = H.diff(prec, outs[0][rows], ref[rows])
+    assert np.all(dlt <= tol), f"{np.sum(~(dlt <= tol))} sampled outputs beyond the bound"
+    G.log(f"  ok ({len(rows)} sampled outputs)")
+
+
+@pytest.mark.parametrize("uplo,trans", [("L", "N"), ("U", "T")])
+def test_trmv_element_offsets_beyond_2_31(uplo, trans):
+    """n = lda = 46341 (the last element's index past 2^31 - 1), the triangle
+    and x drawn on the device: sampled outputs against the oracle on the
+    inputs copied back."""
+    import torch
+    import blas_symmetric_mat_amd as X
+    from tests import helpers as H
+    n = 46341
+    G.log(f"trmv s{uplo}{trans} n={n}")
+    d = W.draw_on_device("s", uplo, n, n, seed=n)
+    x = d.x.clone()
+    X.xtrmv_s(uplo, trans, "N", n, d.A, n, x, 1)
+    torch.cuda.synchronize()
+    got = x.cpu().numpy()
+    h = W.problem_to_host(d)
+    del d, x
+    torch.cuda.empty_cache()
+    p = W.TrmvProblem("s", uplo, trans, "N", n, n, h.A, h.x, name=f"strmv-{uplo}{trans}-n{n}")
+    ref = oracle.trmv_problem(p)
+    rows = sample_rows(n, seed=n + 9)
+    tol = H.trmv_tolerance(p, rows)
+    dlt = H.diff("s", got[rows], ref[rows])
     assert np.all(dlt <= tol), f"{np.sum(~(dlt <= tol))} sampled outputs beyond the bound"
     G.log(f"  ok ({len(rows)} sampled outputs)")

@@ -59,3 +59,23 @@ def test_device_draw_spans_column_blocks():
     top = M[:n, :n]
     assert np.all(np.isfinite(top[i >= j])) and np.all(np.isnan(top[i < j]))
     assert np.all(np.isnan(M[n:, :]))
+
+
+@pytest.mark.parametrize("prec", W.PRECISIONS)
+@pytest.mark.parametrize("trans", ["N", "T"])
+def test_device_draw_general(prec, trans):
+    """The general-matrix drawer: A is m x n with lda = m and every element
+    drawn, x and y have op(A)'s lengths, double-double lo words at most 2^-53
+    of their hi words, and the same seed gives the same values."""
+    pytest.importorskip("torch")
+    m, n = 9, 6
+    p = W.problem_to_host(W.gemv_on_device(prec, trans, m, n, seed=4, device="cpu"))
+    assert p.lda == m and p.A.shape[0] == m * n
+    assert (p.x.shape[0], p.y.shape[0]) == ((n, m) if trans == "N" else (m, n))
+    for v in (p.A, p.x, p.y):
+        hi = v[:, 0] if prec == "w" else v
+        assert np.all(np.isfinite(hi)) and np.all(np.abs(hi.real) <= 1.0)
+        if prec == "w":
+            assert np.all(np.abs(v[:, 1]) <= np.abs(v[:, 0]) * 2.0 ** -53)
+    q = W.problem_to_host(W.gemv_on_device(prec, trans, m, n, seed=4, device="cpu"))
+    np.testing.assert_array_equal(q.A, p.A)
