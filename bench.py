@@ -576,6 +576,11 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"),
                     help="write profiles/traffic_counters.json from two rocprofv3 --pmc "
                          "runs of the headline workload and exit")
+    ap.add_argument("--profile-workload", metavar="NAME",
+                    help="for a profiler: run only NAME's call --calls times and exit, "
+                         "printing nothing else (NAME = <s|d|c|z|w>-L-n<N>: uplo L, inputs "
+                         "drawn on the device as workloads.lower_on_device draws them)")
+    ap.add_argument("--calls", type=int, default=5)
     ap.add_argument("--pmc-calibrate", action="store_true",
                     help="also run a plain 1 GiB elementwise copy, for scaling "
                          "rocprofv3 FETCH_SIZE/WRITE_SIZE readings")
@@ -605,6 +610,17 @@ def main():
     import blas_symmetric_mat_amd as X
     from blas_symmetric_mat_amd import roofline as R
     from blas_symmetric_mat_amd import workloads as W
+
+    if args.profile_workload:
+        prec, uplo, n = args.profile_workload.split("-")
+        if prec not in W.PRECISIONS or uplo != "L" or not n.startswith("n"):
+            sys.exit(f"--profile-workload: expected <s|d|c|z|w>-L-n<N>, got {args.profile_workload}")
+        d = Dev(W.lower_on_device(prec, int(n[1:])))
+        for _ in range(args.calls):
+            d.call()
+        torch.cuda.synchronize()
+        log(f"{args.profile_workload}: {args.calls} calls done")
+        return
 
     if not os.path.exists(X.LIB_PATH):
         from blas_symmetric_mat_amd import build as B
