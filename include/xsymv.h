@@ -41,6 +41,13 @@
  * beta == 1, returns without touching y.  alpha == 0 scales y by beta only
  * (A and x are not read).
  *
+ * HIP graphs: the first call of a shape (precision, uplo, n, configuration)
+ * builds its work split and uploads it with a synchronising copy, and the
+ * first call on a stream may allocate that stream's workspace; neither is
+ * allowed while a stream is being captured.  A later call of the same shape
+ * on a stream that has already run one enqueues only kernels and can be
+ * recorded into a graph and replayed (with timing off).
+ *
  * Return codes (checked before any device work; numbering follows the
  * argument positions, as BLAS xerbla does):
  *    0  success
