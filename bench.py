@@ -439,6 +439,18 @@ def measure_detail(name, p, reps, flush, read_peak=None):
         out["pct_measured_read_peak"] = round(100 * call_b / t_call / 1e9 / read_peak, 1)
     if p.prec in ("c", "z"):
         out["gflops_8n2_real"] = round(4 * R.gflops_2n2(p.n, t_call), 2)
+    if small:
+        # the same call 100 times back to back, no flush: the rate a loop of
+        # calls on warm caches sees (two events around the whole run)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(100):
+            d.call()
+        e1.record()
+        torch.cuda.synchronize()
+        out["us_per_call_back_to_back"] = round(e0.elapsed_time(e1) * 10.0, 2)
     del d
     torch.cuda.empty_cache()
     return out
