@@ -31,6 +31,22 @@ def test_exports_every_declared_function():
         assert hasattr(lib, nm), nm
 
 
+def test_exports_nothing_undeclared():
+    """Every C function the library exports is declared in include/xsymv.h
+    (the dynamic symbol table, read with nm; C++ symbols are mangled and
+    start with an underscore)."""
+    import shutil
+    import subprocess
+    if shutil.which("nm") is None:
+        pytest.skip("nm not available")
+    out = subprocess.run(["nm", "-D", "--defined-only", X.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {f[2] for f in (line.split() for line in out.splitlines())
+                if len(f) == 3 and f[1] == "T" and not f[2].startswith("_")}
+    assert exported and exported == set(declared_functions()), \
+        sorted(exported ^ set(declared_functions()))
+
+
 @pytest.mark.parametrize("prec", ["s", "d", "c", "z", "w"])
 def test_argument_errors_before_device_work(prec):
     f = getattr(X, {"s": "xsymv_s", "d": "xsymv_d", "c": "xhemv_c", "z": "xhemv_z",
