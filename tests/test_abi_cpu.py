@@ -202,6 +202,27 @@ def test_set_workspace_argument_check():
     assert X.library().xsymv_set_workspace(None, 64, None) == -2
 
 
+def test_gemv_workspace_bytes_without_a_device():
+    # empty products need no workspace; an unknown precision is refused
+    for p in "sdczw":
+        assert X.gemv_workspace_bytes(p, "N", 0, 10) == 0
+        assert X.gemv_workspace_bytes(p, "T", 10, 0) == 0
+    assert X.library().xgemv_workspace_bytes(9, b"N", 10, 10) == 2 ** 64 - 1
+
+
+def test_config_workgroups_without_a_device():
+    # families other than the row strips launch one workgroup per tile (0);
+    # out-of-range indices and precisions are refused (-1)
+    lib = X.library()
+    for p in "sdczw":
+        for i in range(X.num_configs(p)):
+            if X.config_info(p, i)["column_runs"] < 4:
+                assert X.config_workgroups(p, i, "L") == 0
+        assert X.config_workgroups(p, X.num_configs(p), "L") == -1
+        assert X.config_workgroups(p, -1, "U") == -1
+    assert lib.xsymv_config_workgroups(7, 0, b"L") == -1
+
+
 def test_read_bandwidth_argument_check():
     # below 64 MiB, or no repetition: refused before any allocation
     lib = X.library()
