@@ -99,7 +99,11 @@ int xhemv_z(char uplo, int n, xcomplex128 alpha, const xcomplex128 *A, int lda,
             int incy, void *stream);
 
 /* WSYMV: double-double symmetric (report §2.2 Fig. 4 and Fig. 5).  Inputs
- * need not be normalised; outputs are (hi, lo) with hi = RN(hi + lo). */
+ * need not be normalised; outputs are (hi, lo) with hi = RN(hi + lo).  The
+ * accumulations use double-double multiply-adds with one TwoSum of the high
+ * words (the cheaper addition of the double-double library the report
+ * builds on), merges and reductions the accurate addition; every result is
+ * within 4*n*2^-104*(|alpha|*(|S||x|)_i + |beta|*|y_i|) of the exact value. */
 int xsymv_w(char uplo, int n, xdd alpha, const xdd *A, int lda,
             const xdd *x, int incx, xdd beta, xdd *y, int incy,
             void *stream);
