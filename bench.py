@@ -590,8 +590,8 @@ def main():
                          "runs of the headline workload and exit")
     ap.add_argument("--profile-workload", metavar="NAME",
                     help="for a profiler: run only NAME's call --calls times and exit, "
-                         "printing nothing else (NAME = <s|d|c|z|w>-L-n<N>: uplo L, inputs "
-                         "drawn on the device as workloads.lower_on_device draws them)")
+                         "printing nothing else (NAME = <s|d|c|z|w>-<L|U>-n<N>: inputs drawn "
+                         "on the device as workloads.metric_order_on_device draws them)")
     ap.add_argument("--calls", type=int, default=5)
     ap.add_argument("--pmc-calibrate", action="store_true",
                     help="also run a plain 1 GiB elementwise copy, for scaling "
@@ -625,9 +625,10 @@ def main():
 
     if args.profile_workload:
         prec, uplo, n = args.profile_workload.split("-")
-        if prec not in W.PRECISIONS or uplo != "L" or not n.startswith("n"):
-            sys.exit(f"--profile-workload: expected <s|d|c|z|w>-L-n<N>, got {args.profile_workload}")
-        d = Dev(W.lower_on_device(prec, int(n[1:])))
+        if prec not in W.PRECISIONS or uplo not in ("L", "U") or not n.startswith("n"):
+            sys.exit(f"--profile-workload: expected <s|d|c|z|w>-<L|U>-n<N>, "
+                     f"got {args.profile_workload}")
+        d = Dev(W.metric_order_on_device(prec, int(n[1:]), uplo))
         for _ in range(args.calls):
             d.call()
         torch.cuda.synchronize()
@@ -732,7 +733,7 @@ def main():
                  ("wsymv-L-n8192", W.wsymv_lower_n8192)]
         # every type at the metric's order n = 32768 (inputs drawn on the
         # device: the host draw of a 17 GB triangle takes minutes)
-        cases += [(f"{k}-L-n32768-devdraw", lambda prec=prec: W.lower_on_device(prec, 32768))
+        cases += [(f"{k}-L-n32768-devdraw", lambda prec=prec: W.metric_order_on_device(prec, 32768))
                   for prec, k in (("c", "chemv"), ("z", "zhemv"), ("w", "wsymv"))]
         for name, make in cases:
             detail[name] = measure_detail(name, make(), args.detail_reps, flush, rd_med)

@@ -556,16 +556,16 @@ def wsymv_lower_n8192(n: int = 8192) -> Problem:
                         seed=4, name=f"wsymv-L-n{n}")
 
 
-def lower_on_device(prec: str, n: int = 32768) -> Problem:
-    """uplo = L, lda = n, seed n, drawn on the device: [SD]SYMV with
-    alpha = beta = 1; [CZ]HEMV with the n = 16384 workload's scalars and
-    diagonal garbage; WSYMV with alpha = beta = (1, 0)."""
+def metric_order_on_device(prec: str, n: int = 32768, uplo: str = "L") -> Problem:
+    """lda = n, seed n, drawn on the device: [SD]SYMV with alpha = beta = 1;
+    [CZ]HEMV with the n = 16384 workload's scalars and diagonal garbage;
+    WSYMV with alpha = beta = (1, 0)."""
     kw = {"s": dict(alpha=1.0, beta=1.0), "d": dict(alpha=1.0, beta=1.0),
           "c": dict(alpha=complex(0.75, 0.25), beta=complex(0.5, -1.0), diag_imag_scale=1e3),
           "z": dict(alpha=complex(0.75, 0.25), beta=complex(0.5, -1.0), diag_imag_scale=1e3),
           "w": dict(alpha=(1.0, 0.0), beta=(1.0, 0.0))}[prec]
     kind = "hemv" if prec in ("c", "z") else "symv"
-    return draw_on_device(prec, "L", n, n, seed=n, name=f"{prec}{kind}-L-n{n}-devdraw", **kw)
+    return draw_on_device(prec, uplo, n, n, seed=n, name=f"{prec}{kind}-{uplo}-n{n}-devdraw", **kw)
 
 
 def gemv_square(prec: str, trans: str, n: int) -> GemvProblem:

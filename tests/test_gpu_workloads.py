@@ -98,14 +98,15 @@ def test_wsymv_lower_n8192():
 
 
 @pytest.mark.parametrize("prec", ["c", "z", "w"])
-def test_lower_n32768_device_drawn(prec):
-    """CHEMV, ZHEMV and WSYMV at n = 32768 (uplo = L, the inputs the
-    benchmark times there, drawn on the device): three identical runs, then
-    sampled rows against the oracle on the inputs copied back to the host."""
+@pytest.mark.parametrize("uplo", ["L", "U"])
+def test_n32768_device_drawn(prec, uplo):
+    """CHEMV, ZHEMV and WSYMV at n = 32768 (uplo = L: the inputs the
+    benchmark times there; and U), drawn on the device: three identical runs,
+    then sampled rows against the oracle on the inputs copied back."""
     import torch
     import blas_symmetric_mat_amd as X
-    G.log(f"device-drawn {prec} L n=32768")
-    p = W.lower_on_device(prec, 32768)
+    G.log(f"device-drawn {prec} {uplo} n=32768")
+    p = W.metric_order_on_device(prec, 32768, uplo)
     outs = set()
     for _ in range(3):
         y = p.y.clone()
