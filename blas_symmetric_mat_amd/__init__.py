@@ -154,12 +154,16 @@ def library():
             lib.xsymv_select_config.argtypes = [ci, cc, ci, ci, ci]
             lib.xsymv_current_config.restype = ci
             lib.xsymv_current_config.argtypes = [ci, cc, ci]
+            lib.xsymv_current_config_lda.restype = ci
+            lib.xsymv_current_config_lda.argtypes = [ci, cc, ci, ci]
             lib.xsymv_timing_enable.restype = ci
             lib.xsymv_timing_enable.argtypes = [ci]
             lib.xsymv_timing_read.restype = ci
             lib.xsymv_timing_read.argtypes = [fp, fp, ci]
             lib.xsymv_autotune.restype = ci
             lib.xsymv_autotune.argtypes = [ci, cc, ci, ci, ci, ci, vp, ip, fp, ci]
+            lib.xsymv_autotune_lda.restype = ci
+            lib.xsymv_autotune_lda.argtypes = [ci, cc, ci, ci, ci, ci, ci, vp, ip, fp, ci]
             for nm in ("xsymv_save_config", "xsymv_load_config"):
                 getattr(lib, nm).restype = ci
                 getattr(lib, nm).argtypes = [ctypes.c_char_p]
@@ -590,24 +594,30 @@ def select_config(prec: str, uplo: str, n_lo: int, n_hi: int, idx: int) -> None:
         raise ValueError("bad configuration selection")
 
 
-def current_config(prec: str, uplo: str, n: int) -> int:
-    return library().xsymv_current_config(PREC_CODE[prec], uplo.encode()[:1], n)
+def current_config(prec: str, uplo: str, n: int, lda: int | None = None) -> int:
+    """The configuration a call would use now (``lda`` default: a leading
+    dimension whose columns are whole 64-byte lines)."""
+    if lda is None:
+        return library().xsymv_current_config(PREC_CODE[prec], uplo.encode()[:1], n)
+    return library().xsymv_current_config_lda(PREC_CODE[prec], uplo.encode()[:1], n, lda)
 
 
 def autotune(prec: str, uplo: str, n: int, n_lo: int | None = None, n_hi: int | None = None,
-             reps: int = 10, stream=None):
-    """Time every compiled configuration for (prec, uplo, n) on the device,
-    install the fastest for n in [n_lo, n_hi] (default: n only) and return
-    (best index, list of median milliseconds per configuration)."""
+             reps: int = 10, stream=None, lda: int | None = None):
+    """Time every compiled configuration for (prec, uplo, n) on the device
+    (on a matrix of leading dimension ``lda``, default n), install the
+    fastest for n in [n_lo, n_hi] (default: n only) and return (best index,
+    list of median milliseconds per configuration)."""
     k = num_configs(prec)
     ms = (ctypes.c_float * k)()
     best = ctypes.c_int(-1)
     n_lo = n if n_lo is None else n_lo
     n_hi = n if n_hi is None else n_hi
-    rc = library().xsymv_autotune(PREC_CODE[prec], uplo.encode()[:1], n, n_lo, n_hi, reps,
-                                  _stream(stream), ctypes.byref(best), ms, k)
+    lda = n if lda is None else lda
+    rc = library().xsymv_autotune_lda(PREC_CODE[prec], uplo.encode()[:1], n, lda, n_lo, n_hi,
+                                      reps, _stream(stream), ctypes.byref(best), ms, k)
     if rc != 0:
-        raise XsymvError("xsymv_autotune", rc)
+        raise XsymvError("xsymv_autotune_lda", rc)
     return best.value, list(ms)
 
 

@@ -665,12 +665,16 @@ int prec_of_char(char c)
 
 // Built-in selection rules measured on MI355X by the on-device autotuner over
 // a grid of orders (the counterpart of the report's per-size rules, §3
-// Table 3).  Kernels are named by shape, so the table survives reordering of
-// the configuration lists; rows whose shape is not compiled are ignored.
+// Table 3), for each stride class of the leading dimension (0: columns of
+// whole 64-byte lines, measured with lda = n; 1: any other, measured with
+// lda = n + 1).  Kernels are named by shape, so the table survives
+// reordering of the configuration lists; rows whose shape is not compiled
+// are ignored.
 struct TunedRule {
     char prec, uplo;
     int n_lo, n_hi;
     int W, CW, S, NT, XLDS, RUNS;
+    int cls;  // stride class (0 when omitted)
 };
 static const TunedRule TUNED_RULES[] = {
 #include "xsymv_tuned.inc"
@@ -678,31 +682,34 @@ static const TunedRule TUNED_RULES[] = {
 
 namespace {
 std::once_flag g_builtin_once;
-std::vector<Rule> g_builtin[5][2];
+std::vector<Rule> g_builtin[5][2][2];  // [prec][upper][stride class]
 
 void init_builtin_rules()
 {
     for (const TunedRule& t : TUNED_RULES) {
         const int prec = prec_of_char(t.prec);
-        if (prec < 0) continue;
+        if (prec < 0 || t.cls < 0 || t.cls > 1) continue;
         const int idx = find_config(prec, t.W, t.CW, t.S, t.NT, t.XLDS, t.RUNS);
         if (idx < 0) continue;
-        g_builtin[prec][t.uplo == 'U' ? 1 : 0].push_back(Rule{t.n_lo, t.n_hi, idx});
+        g_builtin[prec][t.uplo == 'U' ? 1 : 0][t.cls].push_back(Rule{t.n_lo, t.n_hi, idx});
     }
 }
 }  // namespace
 
-int builtin_config(int prec, bool upper, int n)
+// The built-in rule of the stride class for n; class 1 falls back to class
+// 0 where it has no rule; entry 0 when neither has one.
+int builtin_config(int prec, bool upper, int n, int cls)
 {
     std::call_once(g_builtin_once, init_builtin_rules);
-    for (const Rule& r : g_builtin[prec][upper ? 1 : 0])
-        if (n >= r.n_lo && n <= r.n_hi) return r.idx;
+    for (int c = cls; c >= 0; --c)
+        for (const Rule& r : g_builtin[prec][upper ? 1 : 0][c])
+            if (n >= r.n_lo && n <= r.n_hi) return r.idx;
     return 0;
 }
 
-// Caller rules first (the latest matching one; idx -1 defers to the built-in
-// choice), then the built-in rules, then entry 0.
-int pick_config(int prec, bool upper, int n)
+// Caller rules first (the latest matching one, for every stride class; idx
+// -1 defers to the built-in choice), then the built-in rules, then entry 0.
+int pick_config(int prec, bool upper, int n, int cls)
 {
     {
         std::lock_guard<std::mutex> lk(g_rules_mu);
@@ -713,7 +720,7 @@ int pick_config(int prec, bool upper, int n)
                 break;
             }
     }
-    return builtin_config(prec, upper, n);
+    return builtin_config(prec, upper, n, cls);
 }
 
 namespace {
@@ -1005,7 +1012,14 @@ int xsymv_select_config(int prec, char uplo, int n_lo, int n_hi, int idx)
 int xsymv_current_config(int prec, char uplo, int n)
 {
     if (prec < 0 || prec > 4) return -1;
-    return pick_config(prec, uplo == 'U' || uplo == 'u', n);
+    return pick_config(prec, uplo == 'U' || uplo == 'u', n, 0);
+}
+
+int xsymv_current_config_lda(int prec, char uplo, int n, int lda)
+{
+    static const size_t elem[5] = {4, 8, 8, 16, 16};
+    if (prec < 0 || prec > 4 || lda < 1) return -1;
+    return pick_config(prec, uplo == 'U' || uplo == 'u', n, stride_class(lda, elem[prec]));
 }
 
 int xsymv_timing_enable(int on)
@@ -1048,17 +1062,23 @@ int xsymv_timing_read(float* main_ms, float* merge_ms, int max)
 int xsymv_autotune(int prec, char uplo, int n, int n_lo, int n_hi, int reps, void* stream,
                    int* best_idx, float* ms, int max_cfg)
 {
-    if (prec < 0 || prec > 4 || n_lo > n_hi || n <= 0 || reps <= 0) return -1;
+    return xsymv_autotune_lda(prec, uplo, n, n, n_lo, n_hi, reps, stream, best_idx, ms, max_cfg);
+}
+
+int xsymv_autotune_lda(int prec, char uplo, int n, int lda, int n_lo, int n_hi, int reps,
+                       void* stream, int* best_idx, float* ms, int max_cfg)
+{
+    if (prec < 0 || prec > 4 || n_lo > n_hi || n <= 0 || reps <= 0 || lda < n) return -1;
     if (!(uplo == 'U' || uplo == 'u' || uplo == 'L' || uplo == 'l')) return -1;
     int best = 0;
     hipStream_t st = (hipStream_t)stream;
     int rc;
     switch (prec) {
-    case XSYMV_S: rc = autotune_for<float>(uplo, n, reps, st, &best, ms, max_cfg); break;
-    case XSYMV_D: rc = autotune_for<double>(uplo, n, reps, st, &best, ms, max_cfg); break;
-    case XSYMV_C: rc = autotune_for<cf32>(uplo, n, reps, st, &best, ms, max_cfg); break;
-    case XSYMV_Z: rc = autotune_for<cf64>(uplo, n, reps, st, &best, ms, max_cfg); break;
-    default: rc = autotune_for<ddreal>(uplo, n, reps, st, &best, ms, max_cfg); break;
+    case XSYMV_S: rc = autotune_for<float>(uplo, n, lda, reps, st, &best, ms, max_cfg); break;
+    case XSYMV_D: rc = autotune_for<double>(uplo, n, lda, reps, st, &best, ms, max_cfg); break;
+    case XSYMV_C: rc = autotune_for<cf32>(uplo, n, lda, reps, st, &best, ms, max_cfg); break;
+    case XSYMV_Z: rc = autotune_for<cf64>(uplo, n, lda, reps, st, &best, ms, max_cfg); break;
+    default: rc = autotune_for<ddreal>(uplo, n, lda, reps, st, &best, ms, max_cfg); break;
     }
     if (rc) return rc;
     if (best_idx) *best_idx = best;

@@ -124,9 +124,15 @@ template <> constexpr int prec_code<cf32>() { return XSYMV_C; }
 template <> constexpr int prec_code<cf64>() { return XSYMV_Z; }
 template <> constexpr int prec_code<ddreal>() { return XSYMV_W; }
 
-// Configuration index for (prec, upper, n): the last matching selection
-// rule, else the built-in default.
-int pick_config(int prec, bool upper, int n);
+// Stride class of a leading dimension: 0 when a column is a whole number of
+// 64-byte lines (every column starts where the previous one's lines end),
+// 1 otherwise (a wave's piece of a column then straddles one line more).
+inline int stride_class(long long lda, size_t elem) { return (lda * (long long)elem) % 64 ? 1 : 0; }
+
+// Configuration index for (prec, upper, n, stride class): the last matching
+// caller rule, else the built-in rules of that class (falling back to class
+// 0), else entry 0.
+int pick_config(int prec, bool upper, int n, int cls = 0);
 
 // --------------------------------------------------------------- tile plans
 struct Plan {
@@ -251,13 +257,13 @@ template <> inline ddreal tune_zero<ddreal>() { return {0.0, 0.0}; }
 // Autotuner per element type (specialised in the precision units, where the
 // kernels live).
 template <class T>
-int autotune_for(char uplo, int n, int reps, hipStream_t stream, int* best_idx, float* ms,
-                 int max_cfg);
-template <> int autotune_for<float>(char, int, int, hipStream_t, int*, float*, int);
-template <> int autotune_for<double>(char, int, int, hipStream_t, int*, float*, int);
-template <> int autotune_for<cf32>(char, int, int, hipStream_t, int*, float*, int);
-template <> int autotune_for<cf64>(char, int, int, hipStream_t, int*, float*, int);
-template <> int autotune_for<ddreal>(char, int, int, hipStream_t, int*, float*, int);
+int autotune_for(char uplo, int n, int lda, int reps, hipStream_t stream, int* best_idx,
+                 float* ms, int max_cfg);
+template <> int autotune_for<float>(char, int, int, int, hipStream_t, int*, float*, int);
+template <> int autotune_for<double>(char, int, int, int, hipStream_t, int*, float*, int);
+template <> int autotune_for<cf32>(char, int, int, int, hipStream_t, int*, float*, int);
+template <> int autotune_for<cf64>(char, int, int, int, hipStream_t, int*, float*, int);
+template <> int autotune_for<ddreal>(char, int, int, int, hipStream_t, int*, float*, int);
 
 // --------------------------------------------------------------- the driver
 // The strip family's half of a call (the caller holds the device lock).
@@ -332,7 +338,9 @@ int symv_run(char uplo, int n, T alpha, const T* A, int lda, const T* x, int inc
         return 0;
     }
 
-    const int idx = forced_idx >= 0 ? forced_idx : pick_config(prec_code<T>(), upper, n);
+    const int idx = forced_idx >= 0 ? forced_idx
+                                    : pick_config(prec_code<T>(), upper, n,
+                                                  stride_class(lda, sizeof(T)));
     const KernelSet<T>& ks = kernel_sets<T>()[idx];
     const int NB = ks.info.NB();
     const int R = ks.info.R();
@@ -932,17 +940,19 @@ static __global__ __launch_bounds__(256) void tune_flush(uint32_t* buf, long lon
         buf[i] = (uint32_t)i;
 }
 
-// Time every configuration of T for (uplo, n): `reps` calls each (after two
-// warm-up calls), each preceded by a cache flush when the matrix is smaller
-// than 1 GiB; the configuration with the lowest median wins, ties going to
-// the lower index.  ms[i] receives configuration i's median (up to max_cfg).
+// Time every configuration of T for (uplo, n) on a matrix of leading
+// dimension lda: `reps` calls each (after two warm-up calls), each preceded
+// by a cache flush when the matrix is smaller than 1 GiB; the configuration
+// with the lowest median wins, ties going to the lower index.  ms[i]
+// receives configuration i's median (up to max_cfg).
 template <class T>
-int autotune_impl(char uplo, int n, int reps, hipStream_t stream, int* best_idx, float* ms,
-                  int max_cfg)
+int autotune_impl(char uplo, int n, int lda_arg, int reps, hipStream_t stream, int* best_idx,
+                  float* ms, int max_cfg)
 {
-    if (n <= 0 || reps <= 0 || !(uplo == 'U' || uplo == 'u' || uplo == 'L' || uplo == 'l'))
+    if (n <= 0 || reps <= 0 || lda_arg < n ||
+        !(uplo == 'U' || uplo == 'u' || uplo == 'L' || uplo == 'l'))
         return -1;
-    const long long lda = n;
+    const long long lda = lda_arg;
     const size_t abytes = (size_t)lda * n * sizeof(T);
     T *A = nullptr, *x = nullptr, *y = nullptr;
     uint32_t* fl = nullptr;
@@ -1004,11 +1014,25 @@ done:
 }
 
 template <class T>
+size_t ws_bytes_config(bool upper, int n, int idx);
+
+template <class T>
 size_t ws_bytes(char uplo, int n)
 {
     if (n <= 0) return 0;
     const bool upper = (uplo == 'U' || uplo == 'u');
-    const KernelSet<T>& ks = kernel_sets<T>()[pick_config(prec_code<T>(), upper, n)];
+    // the leading dimension is not known here: the larger need of the two
+    // stride classes' choices
+    const int c0 = pick_config(prec_code<T>(), upper, n, 0);
+    const int c1 = pick_config(prec_code<T>(), upper, n, 1);
+    if (c0 != c1) return std::max(ws_bytes_config<T>(upper, n, c0), ws_bytes_config<T>(upper, n, c1));
+    return ws_bytes_config<T>(upper, n, c0);
+}
+
+template <class T>
+size_t ws_bytes_config(bool upper, int n, int idx)
+{
+    const KernelSet<T>& ks = kernel_sets<T>()[idx];
     const ConfigInfo& ci = ks.info;
     if (ci.strip()) {
         int G = 0;

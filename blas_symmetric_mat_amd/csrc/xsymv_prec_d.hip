@@ -34,10 +34,10 @@ template <> const std::vector<KernelSet<double>>& kernel_sets<double>()
 }
 
 template <>
-int autotune_for<double>(char uplo, int n, int reps, hipStream_t stream, int* best_idx, float* ms,
-                      int max_cfg)
+int autotune_for<double>(char uplo, int n, int lda, int reps, hipStream_t stream, int* best_idx,
+                      float* ms, int max_cfg)
 {
-    return autotune_impl<double>(uplo, n, reps, stream, best_idx, ms, max_cfg);
+    return autotune_impl<double>(uplo, n, lda, reps, stream, best_idx, ms, max_cfg);
 }
 
 // xGEMV configurations (index 0 is the default -- the fastest for both

@@ -27,15 +27,17 @@ template <> const std::vector<KernelSet<float>>& kernel_sets<float>()
         make_strip<float, 16, 1, 16, true>(),             // strip: R 4096, 16 KB runs, G 16
         make_strip<float, 16, 1, 16, true, 1>(),          // strip: R 4096, 16 KB runs, G 16, split by stored rows
         make_strip<float, 16, 1, 8, true>(),              // strip: R 4096, 16 KB runs, G 8
+        make_strip<float, 16, 2, 8, true, 1>(),           // strip: R 8192, 32 KB runs, G 8, split by stored rows
+        make_strip<float, 8, 4, 4, true, 1>(),            // strip: R 8192, 32 KB runs, G 4, split by stored rows
     };
     return v;
 }
 
 template <>
-int autotune_for<float>(char uplo, int n, int reps, hipStream_t stream, int* best_idx, float* ms,
-                      int max_cfg)
+int autotune_for<float>(char uplo, int n, int lda, int reps, hipStream_t stream, int* best_idx,
+                      float* ms, int max_cfg)
 {
-    return autotune_impl<float>(uplo, n, reps, stream, best_idx, ms, max_cfg);
+    return autotune_impl<float>(uplo, n, lda, reps, stream, best_idx, ms, max_cfg);
 }
 
 // xGEMV configurations (index 0 is the default -- the fastest for both

@@ -28,10 +28,10 @@ template <> const std::vector<KernelSet<ddreal>>& kernel_sets<ddreal>()
 }
 
 template <>
-int autotune_for<ddreal>(char uplo, int n, int reps, hipStream_t stream, int* best_idx, float* ms,
-                      int max_cfg)
+int autotune_for<ddreal>(char uplo, int n, int lda, int reps, hipStream_t stream, int* best_idx,
+                      float* ms, int max_cfg)
 {
-    return autotune_impl<ddreal>(uplo, n, reps, stream, best_idx, ms, max_cfg);
+    return autotune_impl<ddreal>(uplo, n, lda, reps, stream, best_idx, ms, max_cfg);
 }
 
 // xGEMV configurations (index 0 is the default -- the fastest for both

@@ -27,10 +27,10 @@ template <> const std::vector<KernelSet<cf64>>& kernel_sets<cf64>()
 }
 
 template <>
-int autotune_for<cf64>(char uplo, int n, int reps, hipStream_t stream, int* best_idx, float* ms,
-                      int max_cfg)
+int autotune_for<cf64>(char uplo, int n, int lda, int reps, hipStream_t stream, int* best_idx,
+                      float* ms, int max_cfg)
 {
-    return autotune_impl<cf64>(uplo, n, reps, stream, best_idx, ms, max_cfg);
+    return autotune_impl<cf64>(uplo, n, lda, reps, stream, best_idx, ms, max_cfg);
 }
 
 // xGEMV configurations (index 0 is the default -- the fastest for both

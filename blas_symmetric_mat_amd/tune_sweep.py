@@ -5,16 +5,22 @@ per-size rules (§3, Table 3).  This is the MI355X counterpart:
 
   measure:  python -m blas_symmetric_mat_amd.tune_sweep measure OUT.json
             For every precision, triangle and order of a grid, runs
-            ``xsymv_autotune`` (every compiled configuration, median of
+            ``xsymv_autotune_lda`` (every compiled configuration, median of
             ``--reps`` timed calls on device-generated data, caches flushed
             for matrices under 1 GiB) and records each configuration's median
-            time and the winner.  Needs a GPU.
+            time and the winner.  ``--stride-class 1`` measures with
+            lda = n + 1 (columns that are not whole 64-byte lines; the grid
+            orders are multiples of 64, so lda = n is class 0), ``--n-min``
+            skips the smaller orders, and ``--append`` adds the results to an
+            existing record (replacing those of the same key).  Needs a GPU.
 
   emit:     python -m blas_symmetric_mat_amd.tune_sweep emit IN.json OUT.inc
             Turns a measurement record into the rule rows compiled into the
-            library (csrc/xsymv_tuned.inc): the winner at grid order n_k
-            covers the orders between the geometric midpoints with its
-            neighbours; adjacent rows with the same kernel are merged.
+            library (csrc/xsymv_tuned.inc), per stride class: the winner at
+            grid order n_k covers the orders between the geometric midpoints
+            with its neighbours; adjacent rows with the same kernel are
+            merged.  Class 1 rows cover only the orders that class was
+            measured on; elsewhere the library falls back to class 0.
 
 Kernels are recorded by shape (waves, columns per wave, stripes,
 non-temporal loads, x in LDS, family), as the JSON rule files of
@@ -45,46 +51,70 @@ def _shape(X, prec, idx):
     return {k: ci[k] for k in SHAPE_KEYS}
 
 
-def measure(out_path: str, precs: str, reps: int, grid_max: int | None) -> None:
+def measure(out_path: str, precs: str, reps: int, grid_max: int | None, cls: int = 0,
+            n_min: int = 0, append: bool = False) -> None:
+    import os
     import torch
     import blas_symmetric_mat_amd as X
 
     torch.cuda.init()
     record = {"library": X.version(), "device": torch.cuda.get_device_name(0), "reps": reps,
               "shapes": {}, "results": []}
+    if append and os.path.exists(out_path):
+        with open(out_path) as f:
+            record = json.load(f)
     for prec in precs:
         shapes = [_shape(X, prec, i) for i in range(X.num_configs(prec))]
+        old = record["shapes"].get(prec, [])
+        # configurations are only ever appended: earlier indices keep their shapes
+        assert shapes[:len(old)] == old, f"configuration list of {prec} was reordered"
         record["shapes"][prec] = shapes
         for uplo in "LU":
             for n in GRID[prec]:
-                if grid_max and n > grid_max:
+                if (grid_max and n > grid_max) or n < n_min:
                     continue
+                lda = n + cls
                 t0 = time.time()
                 X.clear_config()
-                best, ms = X.autotune(prec, uplo, n, reps=reps)
+                best, ms = X.autotune(prec, uplo, n, reps=reps, lda=lda)
                 X.clear_config()
-                record["results"].append({"prec": prec, "uplo": uplo, "n": n, "best": best,
-                                          "ms": [round(t, 5) for t in ms]})
-                print(f"{prec}{uplo} n={n:6d}: best #{best} {ms[best] * 1e3:9.1f} us "
+                record["results"] = [r for r in record["results"] if
+                                     (r["prec"], r["uplo"], r["n"], r.get("cls", 0)) !=
+                                     (prec, uplo, n, cls)]
+                record["results"].append({"prec": prec, "uplo": uplo, "n": n, "cls": cls,
+                                          "best": best, "ms": [round(t, 5) for t in ms]})
+                print(f"{prec}{uplo} n={n:6d} lda={lda}: best #{best} {ms[best] * 1e3:9.1f} us "
                       f"(#0 {ms[0] * 1e3:9.1f} us)  [{time.time() - t0:.1f} s]", flush=True)
     with open(out_path, "w") as f:
         json.dump(record, f, indent=None, separators=(",", ":"))
 
 
 def rules_from_record(record: dict) -> list[dict]:
-    """Rule rows (prec, uplo, n_lo, n_hi, shape) from a measurement record."""
-    by_key: dict[tuple[str, str], list[dict]] = {}
+    """Rule rows (prec, uplo, cls, n_lo, n_hi, shape) from a measurement
+    record.  Class 0 rows cover every order; class 1 rows start at the
+    geometric midpoint below their smallest measured order (the library
+    falls back to class 0 below it)."""
+    by_key: dict[tuple[str, str, int], list[dict]] = {}
     for r in record["results"]:
-        by_key.setdefault((r["prec"], r["uplo"]), []).append(r)
+        by_key.setdefault((r["prec"], r["uplo"], r.get("cls", 0)), []).append(r)
     rows = []
-    for (prec, uplo), rs in sorted(by_key.items()):
+    for (prec, uplo, cls), rs in sorted(by_key.items(), key=lambda kv: (kv[0][2], kv[0][:2])):
         rs.sort(key=lambda r: r["n"])
+        ns0 = sorted(r["n"] for r in record["results"]
+                     if (r["prec"], r["uplo"], r.get("cls", 0)) == (prec, uplo, 0))
         for k, r in enumerate(rs):
-            lo = 0 if k == 0 else math.isqrt(rs[k - 1]["n"] * r["n"]) + 1
+            if k > 0:
+                lo = math.isqrt(rs[k - 1]["n"] * r["n"]) + 1
+            elif cls == 0 or not ns0 or r["n"] <= ns0[0]:
+                lo = 0
+            else:  # below the first class-1 order: the class-0 grid's midpoint
+                prev = max(m for m in ns0 if m < r["n"])
+                lo = math.isqrt(prev * r["n"]) + 1
             hi = INT_MAX if k == len(rs) - 1 else math.isqrt(r["n"] * rs[k + 1]["n"])
             shape = record["shapes"][prec][r["best"]]
-            row = {"prec": prec, "uplo": uplo, "n_lo": lo, "n_hi": hi, **shape}
-            if rows and all(rows[-1][key] == row[key] for key in ("prec", "uplo", *SHAPE_KEYS)):
+            row = {"prec": prec, "uplo": uplo, "cls": cls, "n_lo": lo, "n_hi": hi, **shape}
+            if rows and all(rows[-1][key] == row[key]
+                            for key in ("prec", "uplo", "cls", *SHAPE_KEYS)):
                 rows[-1]["n_hi"] = hi
             else:
                 rows.append(row)
@@ -99,10 +129,11 @@ def emit(in_path: str, out_path: str) -> None:
              f"// ({record.get('device', '?')}, {record.get('library', '?')}, "
              f"median of {record.get('reps', '?')} timed calls).",
              "// {prec, uplo, n_lo, n_hi, waves, cols_per_wave, stripes, nontemporal, "
-             "x_in_lds, family}"]
+             "x_in_lds, family[, stride class]}"]
     for r in rows:
-        lines.append("{'%s', '%s', %d, %d, %d, %d, %d, %d, %d, %d}," % (
-            r["prec"], r["uplo"], r["n_lo"], r["n_hi"], *[r[k] for k in SHAPE_KEYS]))
+        cls = f", {r['cls']}" if r["cls"] else ""
+        lines.append("{'%s', '%s', %d, %d, %d, %d, %d, %d, %d, %d%s}," % (
+            r["prec"], r["uplo"], r["n_lo"], r["n_hi"], *[r[k] for k in SHAPE_KEYS], cls))
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print(f"{len(rows)} rules -> {out_path}")
@@ -116,12 +147,15 @@ def main(argv=None) -> int:
     m.add_argument("--precs", default="sdczw")
     m.add_argument("--reps", type=int, default=20)
     m.add_argument("--grid-max", type=int, default=None)
+    m.add_argument("--stride-class", type=int, choices=(0, 1), default=0)
+    m.add_argument("--n-min", type=int, default=0)
+    m.add_argument("--append", action="store_true")
     e = sub.add_parser("emit")
     e.add_argument("record")
     e.add_argument("out")
     a = ap.parse_args(argv)
     if a.cmd == "measure":
-        measure(a.out, a.precs, a.reps, a.grid_max)
+        measure(a.out, a.precs, a.reps, a.grid_max, a.stride_class, a.n_min, a.append)
     else:
         emit(a.record, a.out)
     return 0

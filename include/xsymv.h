@@ -368,14 +368,20 @@ int xsymv_config_info(int prec, int idx, int *waves, int *cols_per_wave,
  * [n_lo, n_hi] (later selections take precedence).  idx = -1 restores the
  * built-in choice for that range.  Returns 0 or -1 for bad arguments.
  *
- * Built-in choice: per (precision, uplo, range of n), the configuration the
- * on-device autotuner measured fastest on MI355X over a grid of orders from
- * 64 to 32768 (the counterpart of the report's per-size rules, §3 Table 3);
- * entry 0 where no rule applies.  Caller selections (this call, autotune,
- * load_config) take precedence over it. */
+ * Built-in choice: per (precision, uplo, range of n, stride class of lda),
+ * the configuration the on-device autotuner measured fastest on MI355X over
+ * a grid of orders from 64 to 32768 (the counterpart of the report's
+ * per-size rules, §3 Table 3).  Stride class 0: lda * element size is a
+ * multiple of 64 bytes (measured with lda = n); class 1: any other lda
+ * (measured with lda = n + 1; where it has no rule, class 0's applies).
+ * Entry 0 where no rule applies.  Caller selections (this call, autotune,
+ * load_config) take precedence over it, for every lda. */
 int xsymv_select_config(int prec, char uplo, int n_lo, int n_hi, int idx);
-/* Configuration index that a call (prec, uplo, n) would use now. */
+/* Configuration index that a call (prec, uplo, n) with a class-0 leading
+ * dimension would use now; the _lda form for a given lda (-1 for a bad
+ * precision or lda < 1). */
 int xsymv_current_config(int prec, char uplo, int n);
+int xsymv_current_config_lda(int prec, char uplo, int n, int lda);
 
 /* Autotuner (the report's §3 tunes its CUDA kernels offline per GPU; this
  * is the on-device counterpart).  On the current device and `stream`, time
@@ -390,6 +396,11 @@ int xsymv_current_config(int prec, char uplo, int n);
  * bad argument, or 1000 + hipError_t. */
 int xsymv_autotune(int prec, char uplo, int n, int n_lo, int n_hi, int reps,
                    void *stream, int *best_idx, float *ms, int max_cfg);
+/* The same search on a matrix of leading dimension lda (>= n; -1 otherwise):
+ * xsymv_autotune is this call with lda = n.  The installed rule applies to
+ * every leading dimension. */
+int xsymv_autotune_lda(int prec, char uplo, int n, int lda, int n_lo, int n_hi,
+                       int reps, void *stream, int *best_idx, float *ms, int max_cfg);
 
 /* Selection rules as a JSON file: {"library": ..., "rules": [{"prec": "s",
  * "uplo": "L", "n_lo": .., "n_hi": .., "waves": .., "cols_per_wave": ..,

@@ -106,15 +106,29 @@ def test_builtin_rules_match_sweep_record():
     rows = tune_sweep.rules_from_record(record)
     assert rows
     X.clear_config()
+    size = {"s": 4, "d": 8, "c": 8, "z": 16, "w": 16}
+
+    def lda_of_class(prec, n, cls):
+        lda = max(1, n)
+        lda += (-lda * size[prec] % 64) // size[prec]  # whole 64-byte lines
+        return lda + cls
+
     for r in rows:
         for n in {r["n_lo"], r["n_hi"], (r["n_lo"] + r["n_hi"]) // 2}:
-            ci = X.config_info(r["prec"], X.current_config(r["prec"], r["uplo"], n))
+            lda = lda_of_class(r["prec"], min(n, 1 << 20), r["cls"])
+            assert (lda * size[r["prec"]] % 64 != 0) == bool(r["cls"])
+            ci = X.config_info(r["prec"], X.current_config(r["prec"], r["uplo"], n, lda))
             assert all(ci[k] == r[k] for k in tune_sweep.SHAPE_KEYS), (r, n)
     for p in "sdczw":
         for u in "LU":
-            spans = sorted((r["n_lo"], r["n_hi"]) for r in rows if r["prec"] == p and r["uplo"] == u)
-            assert spans[0][0] == 0 and spans[-1][1] == 2**31 - 1
-            assert all(a[1] + 1 == b[0] for a, b in zip(spans, spans[1:]))
+            for cls in (0, 1):
+                spans = sorted((r["n_lo"], r["n_hi"]) for r in rows
+                               if r["prec"] == p and r["uplo"] == u and r["cls"] == cls)
+                if cls == 1 and not spans:
+                    continue
+                # class 0 covers every order, class 1 a tail of them
+                assert spans[-1][1] == 2**31 - 1 and (cls or spans[0][0] == 0)
+                assert all(a[1] + 1 == b[0] for a, b in zip(spans, spans[1:]))
 
 
 def test_workspace_bytes_grow_with_n():
