@@ -91,3 +91,24 @@ def test_selection_argument_errors():
     assert lib.xsymv_autotune(0, b"Q", 64, 0, 10, 3, None, None, None, 0) == -1
     assert lib.xsymv_autotune(0, b"L", 64, 0, 10, 0, None, None, None, 0) == -1
     assert lib.xsymv_autotune(9, b"L", 64, 0, 10, 3, None, None, None, 0) == -1
+
+
+def test_stride_class_choice():
+    """A leading dimension whose columns are whole 64-byte lines (class 0)
+    and one that is not (class 1) may get different built-in choices at
+    large orders; below the orders class 1 was measured on, and for
+    precisions without class-1 rules there, the class-0 choice applies."""
+    lib = X.library()
+    assert X.current_config("s", "L", 1000, 1000) == X.current_config("s", "L", 1000, 1001)
+    for p, size in (("s", 4), ("d", 8), ("c", 8), ("z", 16), ("w", 16)):
+        for n in (5000, 20000, 32768):
+            aligned = n + (-n * size % 64) // size
+            assert X.current_config(p, "U", n, aligned) == X.current_config(p, "U", n)
+            X.current_config(p, "U", n, aligned + 1)  # a valid index either way
+    # a caller rule applies to every leading dimension
+    X.select_config("s", "U", 30000, 40000, 3)
+    assert X.current_config("s", "U", 32768, 32768) == 3
+    assert X.current_config("s", "U", 32768, 32769) == 3
+    assert lib.xsymv_current_config_lda(0, b"L", 10, 0) == -1
+    assert lib.xsymv_current_config_lda(5, b"L", 10, 10) == -1
+    assert lib.xsymv_autotune_lda(0, b"L", 64, 63, 0, 10, 3, None, None, None, 0) == -1
