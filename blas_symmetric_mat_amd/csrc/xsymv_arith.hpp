@@ -7,6 +7,10 @@
 //
 // Every type provides, for the kernels:
 //   VEC             elements per 16-byte lane load
+//   SCALAR_X        read x at a column's (wave-uniform) index with scalar
+//                   loads in the row-strip kernel for uplo = L; measured per
+//                   type: it helps the fp32 types and costs the fp64-based
+//                   ones
 //   zero()
 //   mac(acc, a, x)  acc + a*x          (the row role of a stored element)
 //   macc(acc, a, x) acc + conj(a)*x    (the column role: the mirrored element)
@@ -88,6 +92,7 @@ template <class T> struct Elem;
 // ------------------------------------------------------------------ float
 template <> struct Elem<float> {
     static constexpr int VEC = 4;
+    static constexpr bool SCALAR_X = true;
     __device__ static float zero() { return 0.0f; }
     __device__ static float mac(float acc, float a, float x) { return __builtin_fmaf(a, x, acc); }
     __device__ static float macc(float acc, float a, float x) { return __builtin_fmaf(a, x, acc); }
@@ -116,6 +121,7 @@ template <> struct Elem<float> {
 // ----------------------------------------------------------------- double
 template <> struct Elem<double> {
     static constexpr int VEC = 2;
+    static constexpr bool SCALAR_X = false;
     __device__ static double zero() { return 0.0; }
     __device__ static double mac(double acc, double a, double x) { return __builtin_fma(a, x, acc); }
     __device__ static double macc(double acc, double a, double x) { return __builtin_fma(a, x, acc); }
@@ -144,6 +150,7 @@ template <> struct Elem<double> {
 // -------------------------------------------------------- complex float
 template <> struct Elem<cf32> {
     static constexpr int VEC = 2;
+    static constexpr bool SCALAR_X = true;
     __device__ static cf32 zero() { return {0.0f, 0.0f}; }
     // acc + a*x
     __device__ static cf32 mac(cf32 acc, cf32 a, cf32 x)
@@ -202,6 +209,7 @@ template <> struct Elem<cf32> {
 // ------------------------------------------------------- complex double
 template <> struct Elem<cf64> {
     static constexpr int VEC = 1;
+    static constexpr bool SCALAR_X = false;
     __device__ static cf64 zero() { return {0.0, 0.0}; }
     __device__ static cf64 mac(cf64 acc, cf64 a, cf64 x)
     {
@@ -310,6 +318,7 @@ __device__ __forceinline__ ddreal dd_madd(ddreal acc, ddreal a, ddreal b)
 
 template <> struct Elem<ddreal> {
     static constexpr int VEC = 1;
+    static constexpr bool SCALAR_X = false;
     __device__ static ddreal zero() { return {0.0, 0.0}; }
     __device__ static ddreal mac(ddreal acc, ddreal a, ddreal x) { return dd_madd(acc, a, x); }
     __device__ static ddreal macc(ddreal acc, ddreal a, ddreal x) { return dd_madd(acc, a, x); }

@@ -67,16 +67,33 @@ struct StripArgs {
 // r > j is known, so whole groups are read with 16-byte raw-buffer loads whose
 // byte count ends at that bound: rows at or past it read as zero without a
 // memory access.  That covers the ragged last strip (L and U) and, for U, the
-// diagonal band.  For L the band (rows around the diagonal) needs a lower
-// bound, so those few groups take element loads at clamped addresses.  The
-// diagonal itself counts once, in the row role: L takes it in the band, U
-// adds d_r * x_r at the end of the segment that holds column r.
+// diagonal band.  For L the band (rows around the diagonal) also needs a lower
+// bound: a vector with no row below the diagonal is read at an offset past the
+// byte count, and in the one vector per column that straddles the diagonal the
+// rows at or above it are discarded by a select.  The diagonal itself counts
+// once, in the row role: d_r * x_r is added at the end of the segment that
+// holds column r.
 //
 // SHARD: one GPU's share of the product when the columns are dealt out in
 // panels.  A is the shard's local matrix; the sequence runs over its local
 // columns (those with stored rows in the strip form a contiguous range, as the
 // local-to-global map ascends), addresses use the local column, triangle
 // bounds and x the global one, and column partials are indexed locally.
+// Element i of an array of T read through the constant address space by a
+// wave-uniform index (scalar loads of its 32-bit words).
+template <class T>
+__device__ __forceinline__ T uniform_load(const __attribute__((address_space(4))) unsigned* p,
+                                          int i)
+{
+    constexpr int NW = sizeof(T) / 4;
+    unsigned w[NW];
+#pragma unroll
+    for (int k = 0; k < NW; ++k) w[k] = p[(long long)i * NW + k];
+    T v;
+    __builtin_memcpy(&v, w, sizeof(T));
+    return v;
+}
+
 template <class T, bool UPPER, int W, int SW, int G, bool NT, int CBUF, bool SHARD = false>
 __global__ __launch_bounds__(64 * W) void symv_strip(StripArgs<T> a)
 {
@@ -86,6 +103,7 @@ __global__ __launch_bounds__(64 * W) void symv_strip(StripArgs<T> a)
     constexpr int RW = SW * H;  // rows per wave
     constexpr int R = W * RW;
     constexpr int GROUP = 64 / G;
+    constexpr int FAR = 0x7fffff00;  // an offset past every byte count
     static_assert(CBUF % G == 0, "column buffer holds whole groups");
 
     __shared__ T colred[W][CBUF];
@@ -102,6 +120,13 @@ __global__ __launch_bounds__(64 * W) void symv_strip(StripArgs<T> a)
     // to complete before the element addresses that depend on it
     using cmap = const __attribute__((address_space(4))) int*;
     const cmap lcol = (cmap)a.lcol;
+    // x at a column's index is wave-uniform too.  Read by scalar loads it
+    // stays off the vector-memory counter, which retires in order, so that
+    // using it does not wait for the column loads issued before it; measured,
+    // that pays for the fp32 types with uplo = L only
+    constexpr bool XS = E::SCALAR_X && !UPPER;
+    using cword = const __attribute__((address_space(4))) unsigned*;
+    const cword xw = (cword)a.x;
     const int* __restrict__ gloc = a.gloc;
 
     int u = bd.u0;
@@ -162,7 +187,7 @@ __global__ __launch_bounds__(64 * W) void symv_strip(StripArgs<T> a)
 #pragma unroll
                     for (int s = 0; s < SW; ++s)
                         E::template bload16<NT>(rs, (s * H + lane * V) * (int)sizeof(T), av[g][s]);
-                    xcol[g] = E::sel(real, x[cc], E::zero());
+                    xcol[g] = E::sel(real, XS ? uniform_load<T>(xw, cc) : x[cc], E::zero());
                 }
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
@@ -176,26 +201,46 @@ __global__ __launch_bounds__(64 * W) void symv_strip(StripArgs<T> a)
                         }
                 }
             } else {
-                // L diagonal band: element loads at clamped addresses,
-                // branch-free; the diagonal counts once (row role)
+                // L diagonal band: as above, but a vector with no row below
+                // the column's diagonal is read past the byte count (zeros, no
+                // access), and in the one vector per column that straddles
+                // the diagonal the rows at or above it are replaced by zeros
+                // (a select, so a NaN stored there does not spread).  Those
+                // few bytes lie within the lda x n array, beside the diagonal
+                // element.  The diagonal itself is added with the segment's
+                // other diagonals below.
+                T av[G][SW][V];
+                T xcol[G];
+                int cg[G];
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
-                    const bool colok = g < ng;
-                    const int cl = colok ? jg + g : jg;      // jg is a real column
+                    const bool real = g < ng;
+                    const int cl = real ? jg + g : jg;      // local column
                     const int cc = SHARD ? lcol[cl] : cl;  // global column
-                    const int col = SHARD ? cc : jg + g;
-                    const T* __restrict__ Acc = A + (long long)cl * lda;
-                    const T xcol = E::sel(colok, x[cc], E::zero());
+                    const int rows = real ? min(RW, max(0, n - rw)) : 0;
+                    const auto rs = make_rsrc(A + (long long)cl * lda + rw, rows * (int)sizeof(T));
+#pragma unroll
+                    for (int s = 0; s < SW; ++s) {
+                        const int rf = rw + s * H + lane * V;  // the vector's first row
+                        E::template bload16<NT>(
+                            rs, rf + V - 1 > cc ? (s * H + lane * V) * (int)sizeof(T) : FAR,
+                            av[g][s]);
+                    }
+                    xcol[g] = E::sel(real, XS ? uniform_load<T>(xw, cc) : x[cc], E::zero());
+                    cg[g] = cc;
+                }
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
                     cacc[g] = E::zero();
 #pragma unroll
                     for (int s = 0; s < SW; ++s)
 #pragma unroll
                         for (int k = 0; k < V; ++k) {
-                            T off;
-                            const T av = masked_elem<T, false>(Acc, rw + s * H + lane * V + k,
-                                                               rs1, col, cc, colok, true, &off);
-                            racc[s][k] = E::mac(racc[s][k], av, xcol);
-                            cacc[g] = E::macc(cacc[g], off, xr[s][k]);
+                            const int r = rw + s * H + lane * V + k;
+                            const T a = V > 1 ? E::sel(r > cg[g], av[g][s][k], E::zero())
+                                              : av[g][s][k];
+                            racc[s][k] = E::mac(racc[s][k], a, xcol[g]);
+                            cacc[g] = E::macc(cacc[g], a, xr[s][k]);
                         }
                 }
             }
@@ -220,7 +265,7 @@ __global__ __launch_bounds__(64 * W) void symv_strip(StripArgs<T> a)
         }
         // (a shard's segment may hold no column: a strip without any of its
         // columns that a workgroup's range steps through)
-        if (UPPER && (!SHARD || useg > u)) {
+        if (!SHARD || useg > u) {
             // diagonal of the rows whose column is in this segment (local
             // columns [c0, c1))
             const int c0 = u + coff, c1 = useg + coff;
