@@ -16,6 +16,8 @@
 //   macc(acc, a, x) acc + conj(a)*x    (the column role: the mirrored element)
 //   add(a, b), mul(a, b)
 //   diag_load(p)    the diagonal element (Hermitian: the real word only)
+//   diag_val(a)     a loaded diagonal element's value (Hermitian: the
+//                   imaginary word replaced by zero)
 //   load16(p, out)  VEC consecutive elements, one 16-byte load, dword aligned
 //   shfl_xor(v, m)  exchange with lane ^ m inside a wave64
 //   sel(c, a, b)    c ? a : b, word by word (keeps values in registers)
@@ -99,6 +101,7 @@ template <> struct Elem<float> {
     __device__ static float add(float a, float b) { return a + b; }
     __device__ static float mul(float a, float b) { return a * b; }
     __device__ static float diag_load(const float* p) { return *p; }
+    __device__ static float diag_val(float a) { return a; }
     __device__ static void unpack(u32x4 v, float (&o)[VEC])
     {
         o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y);
@@ -128,6 +131,7 @@ template <> struct Elem<double> {
     __device__ static double add(double a, double b) { return a + b; }
     __device__ static double mul(double a, double b) { return a * b; }
     __device__ static double diag_load(const double* p) { return *p; }
+    __device__ static double diag_val(double a) { return a; }
     __device__ static void unpack(u32x4 v, double (&o)[VEC])
     {
         o[0] = __hiloint2double((int)v.y, (int)v.x);
@@ -176,6 +180,7 @@ template <> struct Elem<cf32> {
         return {a.re * b.re - a.im * b.im, a.re * b.im + a.im * b.re};
     }
     __device__ static cf32 diag_load(const cf32* p) { return {p->re, 0.0f}; }
+    __device__ static cf32 diag_val(cf32 a) { return {a.re, 0.0f}; }
     __device__ static void unpack(u32x4 v, cf32 (&o)[VEC])
     {
         o[0] = {__uint_as_float(v.x), __uint_as_float(v.y)};
@@ -233,6 +238,7 @@ template <> struct Elem<cf64> {
         return {a.re * b.re - a.im * b.im, a.re * b.im + a.im * b.re};
     }
     __device__ static cf64 diag_load(const cf64* p) { return {p->re, 0.0}; }
+    __device__ static cf64 diag_val(cf64 a) { return {a.re, 0.0}; }
     __device__ static void unpack(u32x4 v, cf64 (&o)[VEC])
     {
         o[0] = {__hiloint2double((int)v.y, (int)v.x), __hiloint2double((int)v.w, (int)v.z)};
@@ -325,6 +331,7 @@ template <> struct Elem<ddreal> {
     __device__ static ddreal add(ddreal a, ddreal b) { return dd_add(a, b); }
     __device__ static ddreal mul(ddreal a, ddreal b) { return dd_mul(a, b); }
     __device__ static ddreal diag_load(const ddreal* p) { return *p; }
+    __device__ static ddreal diag_val(ddreal a) { return a; }
     __device__ static void unpack(u32x4 v, ddreal (&o)[VEC])
     {
         o[0] = {__hiloint2double((int)v.y, (int)v.x), __hiloint2double((int)v.w, (int)v.z)};

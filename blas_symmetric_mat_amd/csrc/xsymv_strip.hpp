@@ -68,10 +68,11 @@ struct StripArgs {
 // byte count ends at that bound: rows at or past it read as zero without a
 // memory access.  That covers the ragged last strip (L and U) and, for U, the
 // diagonal band.  For L the band (rows around the diagonal) also needs a lower
-// bound: a vector with no row below the diagonal is read at an offset past the
-// byte count, and in the one vector per column that straddles the diagonal the
-// rows at or above it are discarded by a select.  The diagonal itself counts
-// once, in the row role: d_r * x_r is added at the end of the segment that
+// bound: a vector with no row at or below the diagonal is read at an offset
+// past the byte count, and in the one vector per column that holds the
+// diagonal row the rows above it are discarded by a select.  The diagonal
+// itself counts once, in the row role: for L it is taken from that vector, for
+// U (outside the byte count) d_r * x_r is added at the end of the segment that
 // holds column r.
 //
 // SHARD: one GPU's share of the product when the columns are dealt out in
@@ -201,14 +202,14 @@ __global__ __launch_bounds__(64 * W) void symv_strip(StripArgs<T> a)
                         }
                 }
             } else {
-                // L diagonal band: as above, but a vector with no row below
-                // the column's diagonal is read past the byte count (zeros, no
-                // access), and in the one vector per column that straddles
-                // the diagonal the rows at or above it are replaced by zeros
-                // (a select, so a NaN stored there does not spread).  Those
-                // few bytes lie within the lda x n array, beside the diagonal
-                // element.  The diagonal itself is added with the segment's
-                // other diagonals below.
+                // L diagonal band: as above, but a vector with no row at or
+                // below the column's diagonal is read past the byte count
+                // (zeros, no access), and in the one vector per column that
+                // holds the diagonal row the rows above it are replaced by
+                // zeros (a select, so a NaN stored there does not spread;
+                // those few bytes lie within the lda x n array, beside the
+                // diagonal element).  The diagonal element counts in the row
+                // role only (Hermitian: its real word).
                 T av[G][SW][V];
                 T xcol[G];
                 int cg[G];
@@ -223,7 +224,7 @@ __global__ __launch_bounds__(64 * W) void symv_strip(StripArgs<T> a)
                     for (int s = 0; s < SW; ++s) {
                         const int rf = rw + s * H + lane * V;  // the vector's first row
                         E::template bload16<NT>(
-                            rs, rf + V - 1 > cc ? (s * H + lane * V) * (int)sizeof(T) : FAR,
+                            rs, rf + V - 1 >= cc ? (s * H + lane * V) * (int)sizeof(T) : FAR,
                             av[g][s]);
                     }
                     xcol[g] = E::sel(real, XS ? uniform_load<T>(xw, cc) : x[cc], E::zero());
@@ -237,9 +238,9 @@ __global__ __launch_bounds__(64 * W) void symv_strip(StripArgs<T> a)
 #pragma unroll
                         for (int k = 0; k < V; ++k) {
                             const int r = rw + s * H + lane * V + k;
-                            const T a = V > 1 ? E::sel(r > cg[g], av[g][s][k], E::zero())
-                                              : av[g][s][k];
-                            racc[s][k] = E::mac(racc[s][k], a, xcol[g]);
+                            const T a = E::sel(r > cg[g], av[g][s][k], E::zero());
+                            const T ad = E::sel(r == cg[g], E::diag_val(av[g][s][k]), a);
+                            racc[s][k] = E::mac(racc[s][k], ad, xcol[g]);
                             cacc[g] = E::macc(cacc[g], a, xr[s][k]);
                         }
                 }
@@ -265,7 +266,7 @@ __global__ __launch_bounds__(64 * W) void symv_strip(StripArgs<T> a)
         }
         // (a shard's segment may hold no column: a strip without any of its
         // columns that a workgroup's range steps through)
-        if (!SHARD || useg > u) {
+        if (UPPER && (!SHARD || useg > u)) {
             // diagonal of the rows whose column is in this segment (local
             // columns [c0, c1))
             const int c0 = u + coff, c1 = useg + coff;

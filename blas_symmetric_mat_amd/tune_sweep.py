@@ -11,8 +11,9 @@ per-size rules (§3, Table 3).  This is the MI355X counterpart:
             time and the winner.  ``--stride-class 1`` measures with
             lda = n + 1 (columns that are not whole 64-byte lines; the grid
             orders are multiples of 64, so lda = n is class 0), ``--n-min``
-            skips the smaller orders, and ``--append`` adds the results to an
-            existing record (replacing those of the same key).  Needs a GPU.
+            skips the smaller orders, ``--uplos`` limits the triangles, and
+            ``--append`` adds the results to an existing record (replacing
+            those of the same key).  Needs a GPU.
 
   emit:     python -m blas_symmetric_mat_amd.tune_sweep emit IN.json OUT.inc
             Turns a measurement record into the rule rows compiled into the
@@ -52,7 +53,7 @@ def _shape(X, prec, idx):
 
 
 def measure(out_path: str, precs: str, reps: int, grid_max: int | None, cls: int = 0,
-            n_min: int = 0, append: bool = False) -> None:
+            n_min: int = 0, append: bool = False, uplos: str = "LU") -> None:
     import os
     import torch
     import blas_symmetric_mat_amd as X
@@ -69,7 +70,7 @@ def measure(out_path: str, precs: str, reps: int, grid_max: int | None, cls: int
         # configurations are only ever appended: earlier indices keep their shapes
         assert shapes[:len(old)] == old, f"configuration list of {prec} was reordered"
         record["shapes"][prec] = shapes
-        for uplo in "LU":
+        for uplo in uplos:
             for n in GRID[prec]:
                 if (grid_max and n > grid_max) or n < n_min:
                     continue
@@ -150,12 +151,13 @@ def main(argv=None) -> int:
     m.add_argument("--stride-class", type=int, choices=(0, 1), default=0)
     m.add_argument("--n-min", type=int, default=0)
     m.add_argument("--append", action="store_true")
+    m.add_argument("--uplos", default="LU", choices=("L", "U", "LU"))
     e = sub.add_parser("emit")
     e.add_argument("record")
     e.add_argument("out")
     a = ap.parse_args(argv)
     if a.cmd == "measure":
-        measure(a.out, a.precs, a.reps, a.grid_max, a.stride_class, a.n_min, a.append)
+        measure(a.out, a.precs, a.reps, a.grid_max, a.stride_class, a.n_min, a.append, a.uplos)
     else:
         emit(a.record, a.out)
     return 0
