@@ -16,8 +16,8 @@
 //   macc(acc, a, x) acc + conj(a)*x    (the column role: the mirrored element)
 //   add(a, b), mul(a, b)
 //   diag_load(p)    the diagonal element (Hermitian: the real word only)
-//   diag_val(a)     a loaded diagonal element's value (Hermitian: the
-//                   imaginary word replaced by zero)
+//   DIAG_WORDS      leading 32-bit words of an element that a diagonal
+//                   element's value uses (Hermitian: the real word only)
 //   load16(p, out)  VEC consecutive elements, one 16-byte load, dword aligned
 //   shfl_xor(v, m)  exchange with lane ^ m inside a wave64
 //   sel(c, a, b)    c ? a : b, word by word (keeps values in registers)
@@ -95,13 +95,13 @@ template <class T> struct Elem;
 template <> struct Elem<float> {
     static constexpr int VEC = 4;
     static constexpr bool SCALAR_X = true;
+    static constexpr int DIAG_WORDS = 1;
     __device__ static float zero() { return 0.0f; }
     __device__ static float mac(float acc, float a, float x) { return __builtin_fmaf(a, x, acc); }
     __device__ static float macc(float acc, float a, float x) { return __builtin_fmaf(a, x, acc); }
     __device__ static float add(float a, float b) { return a + b; }
     __device__ static float mul(float a, float b) { return a * b; }
     __device__ static float diag_load(const float* p) { return *p; }
-    __device__ static float diag_val(float a) { return a; }
     __device__ static void unpack(u32x4 v, float (&o)[VEC])
     {
         o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y);
@@ -125,13 +125,13 @@ template <> struct Elem<float> {
 template <> struct Elem<double> {
     static constexpr int VEC = 2;
     static constexpr bool SCALAR_X = false;
+    static constexpr int DIAG_WORDS = 2;
     __device__ static double zero() { return 0.0; }
     __device__ static double mac(double acc, double a, double x) { return __builtin_fma(a, x, acc); }
     __device__ static double macc(double acc, double a, double x) { return __builtin_fma(a, x, acc); }
     __device__ static double add(double a, double b) { return a + b; }
     __device__ static double mul(double a, double b) { return a * b; }
     __device__ static double diag_load(const double* p) { return *p; }
-    __device__ static double diag_val(double a) { return a; }
     __device__ static void unpack(u32x4 v, double (&o)[VEC])
     {
         o[0] = __hiloint2double((int)v.y, (int)v.x);
@@ -155,6 +155,7 @@ template <> struct Elem<double> {
 template <> struct Elem<cf32> {
     static constexpr int VEC = 2;
     static constexpr bool SCALAR_X = true;
+    static constexpr int DIAG_WORDS = 1;
     __device__ static cf32 zero() { return {0.0f, 0.0f}; }
     // acc + a*x
     __device__ static cf32 mac(cf32 acc, cf32 a, cf32 x)
@@ -180,7 +181,6 @@ template <> struct Elem<cf32> {
         return {a.re * b.re - a.im * b.im, a.re * b.im + a.im * b.re};
     }
     __device__ static cf32 diag_load(const cf32* p) { return {p->re, 0.0f}; }
-    __device__ static cf32 diag_val(cf32 a) { return {a.re, 0.0f}; }
     __device__ static void unpack(u32x4 v, cf32 (&o)[VEC])
     {
         o[0] = {__uint_as_float(v.x), __uint_as_float(v.y)};
@@ -215,6 +215,7 @@ template <> struct Elem<cf32> {
 template <> struct Elem<cf64> {
     static constexpr int VEC = 1;
     static constexpr bool SCALAR_X = false;
+    static constexpr int DIAG_WORDS = 2;
     __device__ static cf64 zero() { return {0.0, 0.0}; }
     __device__ static cf64 mac(cf64 acc, cf64 a, cf64 x)
     {
@@ -238,7 +239,6 @@ template <> struct Elem<cf64> {
         return {a.re * b.re - a.im * b.im, a.re * b.im + a.im * b.re};
     }
     __device__ static cf64 diag_load(const cf64* p) { return {p->re, 0.0}; }
-    __device__ static cf64 diag_val(cf64 a) { return {a.re, 0.0}; }
     __device__ static void unpack(u32x4 v, cf64 (&o)[VEC])
     {
         o[0] = {__hiloint2double((int)v.y, (int)v.x), __hiloint2double((int)v.w, (int)v.z)};
@@ -325,13 +325,13 @@ __device__ __forceinline__ ddreal dd_madd(ddreal acc, ddreal a, ddreal b)
 template <> struct Elem<ddreal> {
     static constexpr int VEC = 1;
     static constexpr bool SCALAR_X = false;
+    static constexpr int DIAG_WORDS = 4;
     __device__ static ddreal zero() { return {0.0, 0.0}; }
     __device__ static ddreal mac(ddreal acc, ddreal a, ddreal x) { return dd_madd(acc, a, x); }
     __device__ static ddreal macc(ddreal acc, ddreal a, ddreal x) { return dd_madd(acc, a, x); }
     __device__ static ddreal add(ddreal a, ddreal b) { return dd_add(a, b); }
     __device__ static ddreal mul(ddreal a, ddreal b) { return dd_mul(a, b); }
     __device__ static ddreal diag_load(const ddreal* p) { return *p; }
-    __device__ static ddreal diag_val(ddreal a) { return a; }
     __device__ static void unpack(u32x4 v, ddreal (&o)[VEC])
     {
         o[0] = {__hiloint2double((int)v.y, (int)v.x), __hiloint2double((int)v.w, (int)v.z)};

@@ -30,6 +30,8 @@
 //    strip in segment order + sum of colpart[i][r] in strip order).
 #pragma once
 
+#include <type_traits>
+
 #include "xsymv_kernels.hpp"
 
 namespace xsymv {
@@ -68,12 +70,14 @@ struct StripArgs {
 // byte count ends at that bound: rows at or past it read as zero without a
 // memory access.  That covers the ragged last strip (L and U) and, for U, the
 // diagonal band.  For L the band (rows around the diagonal) also needs a lower
-// bound: a vector with no row at or below the diagonal is read at an offset
-// past the byte count, and in the one vector per column that holds the
-// diagonal row the rows above it are discarded by a select.  The diagonal
-// itself counts once, in the row role: for L it is taken from that vector, for
-// U (outside the byte count) d_r * x_r is added at the end of the segment that
-// holds column r.
+// bound: a vector with no stored row is read at an offset past the byte count,
+// and the one lane per column whose vector holds the diagonal row reads its 16
+// bytes from the diagonal row instead (Hermitian: the row below it, plus the
+// diagonal's real word on its own) and moves them to its rows, so no word
+// outside the stored triangle is read.  The diagonal itself counts once, in
+// the row role: for L inside the band, for U d_r * x_r is added at the end of
+// the segment that holds column r.  For Hermitian products only the real word
+// of a diagonal element is read.
 //
 // SHARD: one GPU's share of the product when the columns are dealt out in
 // panels.  A is the shard's local matrix; the sequence runs over its local
@@ -90,6 +94,28 @@ __device__ __forceinline__ T uniform_load(const __attribute__((address_space(4))
     unsigned w[NW];
 #pragma unroll
     for (int k = 0; k < NW; ++k) w[k] = p[(long long)i * NW + k];
+    T v;
+    __builtin_memcpy(&v, w, sizeof(T));
+    return v;
+}
+
+// The value of the diagonal element at byte offset `off` of a raw buffer: its
+// first Elem<T>::DIAG_WORDS words (Hermitian: the real word; the imaginary
+// word is not read), the others zero.  Past the byte count: zero, no access.
+template <class T>
+__device__ __forceinline__ T bload_diag(__amdgpu_buffer_rsrc_t r, int off)
+{
+    constexpr int NW = Elem<T>::DIAG_WORDS;
+    unsigned w[sizeof(T) / 4] = {};
+    if constexpr (NW == 1) {
+        w[0] = __builtin_bit_cast(unsigned, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+    } else {
+        static_assert(NW == 2, "one or two words");
+        const unsigned long long d =
+            __builtin_bit_cast(unsigned long long, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+        w[0] = (unsigned)d;
+        w[1] = (unsigned)(d >> 32);
+    }
     T v;
     __builtin_memcpy(&v, w, sizeof(T));
     return v;
@@ -170,80 +196,123 @@ __global__ __launch_bounds__(64 * W) void symv_strip(StripArgs<T> a)
             // every real column of the group is left of this wave's rows (L)
             const bool band = !UPPER && !empty && rw < glast + 1;
             T cacc[G];
+            // The group's loads and multiply-adds.  FULL: every column of the
+            // group is real (all groups but a segment's last), so x is used by
+            // the multiply-adds only; a select on it would make the compiler
+            // wait for its load before issuing the next column loads.  Measured,
+            // the second copy of the body pays where a lane's vector holds
+            // several elements and costs the 16-byte types.
+            auto stream_group = [&](auto full) {
+                constexpr bool FULL = decltype(full)::value;
+                if (!band) {
+                    T av[G][SW][V];
+                    T xcol[G];
+#pragma unroll
+                    for (int g = 0; g < G; ++g) {
+                        const bool real = FULL || g < ng;
+                        const int cl = real ? jg + g : jg;      // local column
+                        const int cc = SHARD ? lcol[cl] : cl;  // global column
+                        // stored rows of this wave in column cc: [rw, bound)
+                        const int bound = UPPER ? cc : n;
+                        const int rows = real ? min(RW, max(0, bound - rw)) : 0;
+                        const auto rs =
+                            make_rsrc(A + (long long)cl * lda + rw, rows * (int)sizeof(T));
+#pragma unroll
+                        for (int s = 0; s < SW; ++s)
+                            E::template bload16<NT>(rs, (s * H + lane * V) * (int)sizeof(T),
+                                                    av[g][s]);
+                        const T xv = XS ? uniform_load<T>(xw, cc) : x[cc];
+                        xcol[g] = FULL ? xv : E::sel(real, xv, E::zero());
+                    }
+#pragma unroll
+                    for (int g = 0; g < G; ++g) {
+                        cacc[g] = E::zero();
+#pragma unroll
+                        for (int s = 0; s < SW; ++s)
+#pragma unroll
+                            for (int k = 0; k < V; ++k) {
+                                racc[s][k] = E::mac(racc[s][k], av[g][s][k], xcol[g]);
+                                cacc[g] = E::macc(cacc[g], av[g][s][k], xr[s][k]);
+                            }
+                    }
+                } else {
+                    // L diagonal band: as above, with a lower bound.  A vector
+                    // with no stored row reads past the byte count (zeros, no
+                    // access).  The lane whose vector holds the diagonal row
+                    // reads the 16 bytes that start at the diagonal (Hermitian:
+                    // one row below it, and the diagonal's real word by a load
+                    // of its own) and shifts them to its rows with selects, so
+                    // that nothing above the diagonal is read.  The diagonal
+                    // counts in the row role only.
+                    constexpr int DH = E::DIAG_WORDS * 4 < (int)sizeof(T);  // Hermitian
+                    T av[G][SW][V];
+                    T dv[G][SW];  // Hermitian: the diagonal, in the lane that holds it
+                    T xcol[G];
+                    int cg[G];
+#pragma unroll
+                    for (int g = 0; g < G; ++g) {
+                        const bool real = FULL || g < ng;
+                        const int cl = real ? jg + g : jg;      // local column
+                        const int cc = SHARD ? lcol[cl] : cl;  // global column
+                        const int rows = real ? min(RW, max(0, n - rw)) : 0;
+                        const auto rs =
+                            make_rsrc(A + (long long)cl * lda + rw, rows * (int)sizeof(T));
+#pragma unroll
+                        for (int s = 0; s < SW; ++s) {
+                            const int rf = rw + s * H + lane * V;   // the vector's first row
+                            const int r0 = rf > cc ? rf : cc + DH;  // first row it reads
+                            E::template bload16<NT>(
+                                rs, r0 < rf + V ? (r0 - rw) * (int)sizeof(T) : FAR, av[g][s]);
+                            if constexpr (DH)
+                                dv[g][s] = bload_diag<T>(
+                                    rs, rf <= cc && cc < rf + V ? (cc - rw) * (int)sizeof(T) : FAR);
+                        }
+                        const T xv = XS ? uniform_load<T>(xw, cc) : x[cc];
+                        xcol[g] = FULL ? xv : E::sel(real, xv, E::zero());
+                        cg[g] = real ? cc : -1;
+                    }
+#pragma unroll
+                    for (int g = 0; g < G; ++g) {
+                        cacc[g] = E::zero();
+#pragma unroll
+                        for (int s = 0; s < SW; ++s) {
+                            const int rf = rw + s * H + lane * V;
+                            // rows the loaded vector starts below this lane's
+                            // first row (0 except in the lane with the diagonal)
+                            const int sh = rf > cg[g] ? 0 : cg[g] + DH - rf;
+#pragma unroll
+                            for (int k = 0; k < V; ++k) {
+                                // row rf + k is element k - sh of the loaded vector
+                                T v = av[g][s][k];
+                                if constexpr (V > 1) {
+                                    v = E::sel(sh == 0, v, E::zero());
+#pragma unroll
+                                    for (int j = 0; j < k; ++j)
+                                        v = E::sel(sh == k - j, av[g][s][j], v);
+                                }
+                                const bool dg = rf + k == cg[g];
+                                T ac, ar;  // column role (off-diagonal only), row role
+                                if constexpr (DH) {
+                                    ac = v;
+                                    ar = E::sel(dg, dv[g][s], v);
+                                } else {
+                                    ac = E::sel(dg, E::zero(), v);
+                                    ar = v;
+                                }
+                                racc[s][k] = E::mac(racc[s][k], ar, xcol[g]);
+                                cacc[g] = E::macc(cacc[g], ac, xr[s][k]);
+                            }
+                        }
+                    }
+                }
+            };
             if (empty) {
 #pragma unroll
                 for (int g = 0; g < G; ++g) cacc[g] = E::zero();
-            } else if (!band) {
-                T av[G][SW][V];
-                T xcol[G];
-#pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    const bool real = g < ng;
-                    const int cl = real ? jg + g : jg;      // local column
-                    const int cc = SHARD ? lcol[cl] : cl;  // global column
-                    // stored rows of this wave in column cc: [rw, bound)
-                    const int bound = UPPER ? cc : n;
-                    const int rows = real ? min(RW, max(0, bound - rw)) : 0;
-                    const auto rs = make_rsrc(A + (long long)cl * lda + rw, rows * (int)sizeof(T));
-#pragma unroll
-                    for (int s = 0; s < SW; ++s)
-                        E::template bload16<NT>(rs, (s * H + lane * V) * (int)sizeof(T), av[g][s]);
-                    xcol[g] = E::sel(real, XS ? uniform_load<T>(xw, cc) : x[cc], E::zero());
-                }
-#pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    cacc[g] = E::zero();
-#pragma unroll
-                    for (int s = 0; s < SW; ++s)
-#pragma unroll
-                        for (int k = 0; k < V; ++k) {
-                            racc[s][k] = E::mac(racc[s][k], av[g][s][k], xcol[g]);
-                            cacc[g] = E::macc(cacc[g], av[g][s][k], xr[s][k]);
-                        }
-                }
+            } else if (V > 1 && ng == G) {
+                stream_group(std::integral_constant<bool, (V > 1)>{});
             } else {
-                // L diagonal band: as above, but a vector with no row at or
-                // below the column's diagonal is read past the byte count
-                // (zeros, no access), and in the one vector per column that
-                // holds the diagonal row the rows above it are replaced by
-                // zeros (a select, so a NaN stored there does not spread;
-                // those few bytes lie within the lda x n array, beside the
-                // diagonal element).  The diagonal element counts in the row
-                // role only (Hermitian: its real word).
-                T av[G][SW][V];
-                T xcol[G];
-                int cg[G];
-#pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    const bool real = g < ng;
-                    const int cl = real ? jg + g : jg;      // local column
-                    const int cc = SHARD ? lcol[cl] : cl;  // global column
-                    const int rows = real ? min(RW, max(0, n - rw)) : 0;
-                    const auto rs = make_rsrc(A + (long long)cl * lda + rw, rows * (int)sizeof(T));
-#pragma unroll
-                    for (int s = 0; s < SW; ++s) {
-                        const int rf = rw + s * H + lane * V;  // the vector's first row
-                        E::template bload16<NT>(
-                            rs, rf + V - 1 >= cc ? (s * H + lane * V) * (int)sizeof(T) : FAR,
-                            av[g][s]);
-                    }
-                    xcol[g] = E::sel(real, XS ? uniform_load<T>(xw, cc) : x[cc], E::zero());
-                    cg[g] = cc;
-                }
-#pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    cacc[g] = E::zero();
-#pragma unroll
-                    for (int s = 0; s < SW; ++s)
-#pragma unroll
-                        for (int k = 0; k < V; ++k) {
-                            const int r = rw + s * H + lane * V + k;
-                            const T a = E::sel(r > cg[g], av[g][s][k], E::zero());
-                            const T ad = E::sel(r == cg[g], E::diag_val(av[g][s][k]), a);
-                            racc[s][k] = E::mac(racc[s][k], ad, xcol[g]);
-                            cacc[g] = E::macc(cacc[g], a, xr[s][k]);
-                        }
-                }
+                stream_group(std::false_type{});
             }
             wave_transpose_reduce<T, G>(cacc, lane);
             if ((lane & (GROUP - 1)) == 0)
