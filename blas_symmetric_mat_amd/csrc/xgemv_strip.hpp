@@ -59,6 +59,12 @@ __global__ __launch_bounds__(64 * W) void gemv_strip(GemvArgs<T> a)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const T* __restrict__ A = a.A;
     const T* __restrict__ x = a.x;
+    // 'N': x at a column's index is wave-uniform; for the fp32 types it is
+    // read by scalar loads, off the in-order vector-memory counter (as in the
+    // symmetric kernels' lower triangle)
+    constexpr bool XS = E::SCALAR_X && TR == 0;
+    using cword = const __attribute__((address_space(4))) unsigned*;
+    const cword xw = (cword)a.x;
 
     int u = bd.u0;
     int slot = bd.slot0;
@@ -96,19 +102,27 @@ __global__ __launch_bounds__(64 * W) void gemv_strip(GemvArgs<T> a)
             T cacc[G];
 #pragma unroll
             for (int g = 0; g < G; ++g) cacc[g] = E::zero();
-            if (!wave_empty) {
+            // FULL ('N'): every column of the group is real (all groups but a
+            // segment's last), so x needs no select and is used by the
+            // multiply-adds only; compiled twice where a lane's vector holds
+            // several elements
+            auto stream_group = [&](auto full) {
+                constexpr bool FULL = decltype(full)::value;
                 T av[G][SW][V];
                 T xcol[G];
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
-                    const bool real = g < ng;
+                    const bool real = FULL || g < ng;
                     const int cc = real ? jg + g : jg;
                     const auto rs = make_rsrc(A + (long long)cc * lda + rw,
                                               (real ? rows : 0) * (int)sizeof(T));
 #pragma unroll
                     for (int s = 0; s < SW; ++s)
                         E::template bload16<NT>(rs, (s * H + lane * V) * (int)sizeof(T), av[g][s]);
-                    if (TR == 0) xcol[g] = E::sel(real, x[cc], E::zero());
+                    if (TR == 0) {
+                        const T xv = XS ? uniform_load<T>(xw, cc) : x[cc];
+                        xcol[g] = FULL ? xv : E::sel(real, xv, E::zero());
+                    }
                 }
 #pragma unroll
                 for (int g = 0; g < G; ++g)
@@ -123,6 +137,12 @@ __global__ __launch_bounds__(64 * W) void gemv_strip(GemvArgs<T> a)
                             else
                                 cacc[g] = E::macc(cacc[g], av[g][s][k], xr[s][k]);
                         }
+            };
+            if (!wave_empty) {
+                if (TR == 0 && V > 1 && ng == G)
+                    stream_group(std::integral_constant<bool, (TR == 0 && V > 1)>{});
+                else
+                    stream_group(std::false_type{});
             }
             if (TR != 0) {
                 wave_transpose_reduce<T, G>(cacc, lane);
