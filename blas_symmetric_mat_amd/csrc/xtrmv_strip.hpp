@@ -110,34 +110,51 @@ __global__ __launch_bounds__(64 * W) void trmv_strip(TrmvArgs<T> a)
             if (empty) {
                 // nothing stored in this wave's rows
             } else if (!band) {
-                T av[G][SW][V];
-                T xcol[G];
+                // FULL ('N'): every column of the group is real, so x needs no
+                // select and is used by the multiply-adds only; compiled twice
+                // where a lane's vector holds several elements.  For the fp32
+                // types x at the column index is read by scalar loads (x is
+                // the call's copy of the input, which no kernel writes).
+                auto stream_group = [&](auto full) {
+                    constexpr bool FULL = decltype(full)::value;
+                    constexpr bool XS = E::SCALAR_X && TR == 0;
+                    using cword = const __attribute__((address_space(4))) unsigned*;
+                    T av[G][SW][V];
+                    T xcol[G];
 #pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    const bool real = g < ng;
-                    const int cc = real ? jg + g : jg;
-                    // stored rows of this wave in column cc: [rw, bound)
-                    const int bound = UPPER ? cc + 1 - DU : n;
-                    const int rows = real ? min(RW, max(0, bound - rw)) : 0;
-                    const auto rs = make_rsrc(A + (long long)cc * lda + rw, rows * ES);
+                    for (int g = 0; g < G; ++g) {
+                        const bool real = FULL || g < ng;
+                        const int cc = real ? jg + g : jg;
+                        // stored rows of this wave in column cc: [rw, bound)
+                        const int bound = UPPER ? cc + 1 - DU : n;
+                        const int rows = real ? min(RW, max(0, bound - rw)) : 0;
+                        const auto rs = make_rsrc(A + (long long)cc * lda + rw, rows * ES);
 #pragma unroll
-                    for (int s = 0; s < SW; ++s)
-                        E::template bload16<NT>(rs, (s * H + lane * V) * ES, av[g][s]);
-                    if (TR == 0) xcol[g] = E::sel(real, x[cc], E::zero());
-                }
-#pragma unroll
-                for (int g = 0; g < G; ++g)
-#pragma unroll
-                    for (int s = 0; s < SW; ++s)
-#pragma unroll
-                        for (int k = 0; k < V; ++k) {
-                            if (TR == 0)
-                                racc[s][k] = E::mac(racc[s][k], av[g][s][k], xcol[g]);
-                            else if (TR == 1)
-                                cacc[g] = E::mac(cacc[g], av[g][s][k], xr[s][k]);
-                            else
-                                cacc[g] = E::macc(cacc[g], av[g][s][k], xr[s][k]);
+                        for (int s = 0; s < SW; ++s)
+                            E::template bload16<NT>(rs, (s * H + lane * V) * ES, av[g][s]);
+                        if (TR == 0) {
+                            const T xv = XS ? uniform_load<T>((cword)x, cc) : x[cc];
+                            xcol[g] = FULL ? xv : E::sel(real, xv, E::zero());
                         }
+                    }
+#pragma unroll
+                    for (int g = 0; g < G; ++g)
+#pragma unroll
+                        for (int s = 0; s < SW; ++s)
+#pragma unroll
+                            for (int k = 0; k < V; ++k) {
+                                if (TR == 0)
+                                    racc[s][k] = E::mac(racc[s][k], av[g][s][k], xcol[g]);
+                                else if (TR == 1)
+                                    cacc[g] = E::mac(cacc[g], av[g][s][k], xr[s][k]);
+                                else
+                                    cacc[g] = E::macc(cacc[g], av[g][s][k], xr[s][k]);
+                            }
+                };
+                if (TR == 0 && V > 1 && ng == G)
+                    stream_group(std::integral_constant<bool, (TR == 0 && V > 1)>{});
+                else
+                    stream_group(std::false_type{});
             } else {
                 // L diagonal band: element loads; rows above a column's first
                 // stored row, or past n, read as zero without an access
