@@ -21,7 +21,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "xsymv_oracle.c")
 LIB_PATH = os.path.join(_HERE, "liboracle_xsymv.so")
-CFLAGS = ["-O2", "-ffp-contract=off", "-std=c99", "-fPIC", "-shared", "-Wall"]
+CFLAGS = ["-O2", "-ffp-contract=off", "-std=c99", "-fPIC", "-shared", "-Wall", "-fopenmp"]
 
 
 def build(force: bool = True) -> str:
@@ -93,6 +93,10 @@ def _declare(lib):
         f = getattr(lib, f"oracle_{p}combine")
         f.restype = ci
         f.argtypes = [ci, ci, _SCALAR[p], vp, ci, _SCALAR[p], vp, ci]
+    lib.oracle_set_threads.restype = ci
+    lib.oracle_set_threads.argtypes = [ci]
+    lib.oracle_get_threads.restype = ci
+    lib.oracle_get_threads.argtypes = []
     lib.oracle_shard_columns.restype = ci
     lib.oracle_shard_columns.argtypes = [ci, ci, ci, ci, vp]
     for nm in ("oracle_dd_add", "oracle_dd_mul"):
@@ -142,7 +146,8 @@ class OracleLib:
 
     def symv(self, prec: str, uplo: str, n: int, alpha, A, lda: int, x,
              incx: int, beta, y, incy: int) -> int:
-        """y := alpha*S*x + beta*y in place, by the three-part algorithm.
+        """y := alpha*S*x + beta*y in place, from the definition (one
+        output at a time, inner index ascending).
         Returns the status code (0 = ok, negative = bad argument)."""
         _check_dtype(prec, A, x, y)
         f = getattr(self._lib, "oracle_" + _NAME[prec])
@@ -274,6 +279,14 @@ class OracleLib:
         return f(n, nshards, scalar(prec, alpha), _ptr(P), ldp, scalar(prec, beta), _ptr(y),
                  incy)
 
+    def set_threads(self, nthreads: int) -> int:
+        """Threads of the full-product calls (outputs are independent, so
+        every count gives the same bits); returns 0 or a negative code."""
+        return self._lib.oracle_set_threads(int(nthreads))
+
+    def get_threads(self) -> int:
+        return self._lib.oracle_get_threads()
+
     def dd_add(self, a, b):
         r = self._lib.oracle_dd_add(_DD(*a), _DD(*b))
         return (r.hi, r.lo)
@@ -316,6 +329,14 @@ def rows_problem(p, rows=None):
 
 def dd_add(a, b):
     return default().dd_add(a, b)
+
+
+def set_threads(nthreads):
+    return default().set_threads(nthreads)
+
+
+def get_threads():
+    return default().get_threads()
 
 
 def dd_mul(a, b):

@@ -18,17 +18,15 @@
  *   diagonal element is never read).  conj() is the identity for the real
  *   and double-double types.
  *
- * How.  The report's sequential algorithm (§2.1 Fig. 1), taken step by step:
- *   v := 0 and y := beta*y;
- *   part one: for every column j, every stored off-diagonal a = A(i,j) is
- *     used twice -- v(i) += a*x(j) (its row's share) and t += conj(a)*x(i)
- *     (its column's share, the transpose) -- and then y(j) += alpha*t;
- *   part two: y(i) += alpha*S(i,i)*x(i);
- *   part three: y += alpha*v.
- * Fig. 1 prints the U case; for L only the range of i within a column
- * changes (i > j instead of i < j).  Scaling y by beta follows BLAS: with
- * beta == 0 the old y is not read (it may hold NaN), and alpha == 0 leaves
- * y := beta*y without touching A or x.
+ * How.  The definition written out, one output element at a time:
+ *   y(i) := beta*y(i) + alpha * sum over j = 0, 1, ..., n-1 of S(i,j)*x(j),
+ * the inner index ascending, in the working precision.  Each output reads
+ * only its own y(i), so y is overwritten in place.  The BLAS rules hold:
+ * with beta == 0 the old y is not read (it may hold NaN), alpha == 0 leaves
+ * y := beta*y without touching A or x, and n == 0 or (alpha == 0 and
+ * beta == 1) returns at once.  Outputs are independent, so the full product
+ * may be spread over threads (oracle_set_threads; OpenMP) with the same bits
+ * for any thread count.
  *
  * General matrix-vector product (the report's point of comparison: SYMV
  * reads one triangle, GEMV the whole matrix, §1 and §2.1), BLAS xGEMV:
@@ -61,11 +59,11 @@
  * even rounds shard g taking the round's g-th panel and in odd rounds its
  * (nshards-1-g)-th (boustrophedon order, so the shards' triangle areas stay
  * close).  A shard keeps only its own columns, in ascending order, as a local
- * column-major matrix.  Its partial vector is, from the definition,
- *   p := 0; for every owned column j and every stored A(i,j):
- *     i == j: p(j) += S(j,j)*x(j);
- *     else:   p(i) += A(i,j)*x(j) and p(j) += conj(A(i,j))*x(i),
- * so that the shards' partials add up to S*x.  The exchange then gives every
+ * column-major matrix.  Its partial vector holds, for every output i, the
+ * terms S(i,j)*x(j) (j ascending) whose element S(i,j) is stored in one of
+ * its columns -- column j when (i,j) is in the stored triangle, column i
+ * otherwise -- so that every term of S*x belongs to exactly one shard and the
+ * shards' partials add up to S*x.  The exchange then gives every
  * GPU all partials, and y(i) := beta*y(i) + alpha*(p_0(i) + p_1(i) + ...),
  * summed in rank order (the report's fixed summation order, §2.1, kept
  * across GPUs), with the BLAS rules for beta == 0 and alpha == 0.
@@ -262,54 +260,69 @@ static odd w_zero(void)
 
 /* ------------------------------------------------------------ algorithm */
 
-/* One definition per element type; P is the prefix of its operations. */
+/* Threads the full-product entry points use (rows are independent, so any
+ * count gives the same bits); 1 unless set. */
+static int g_threads = 1;
+
+int oracle_set_threads(int nthreads)
+{
+    if (nthreads < 1) return -1;
+#ifdef _OPENMP
+    g_threads = nthreads;
+#else
+    if (nthreads > 1) return -2;
+#endif
+    return 0;
+}
+
+int oracle_get_threads(void) { return g_threads; }
+
+/* One definition per element type; P is the prefix of its operations.
+ *
+ * elem: S(i,j), the element of the full matrix that the stored triangle
+ *   implies -- A(i,j) where (i,j) is stored, conj(A(j,i)) across the
+ *   diagonal, and on the diagonal its stored value (Hermitian: the real word
+ *   alone).
+ * row: output i of eq.(1), beta*Y(i) + alpha * sum over j = 0, 1, ..., n-1
+ *   (ascending) of S(i,j)*X(j); with beta == 0 the old Y(i) is not read,
+ *   with alpha == 0 neither A nor x is. */
 #define DEFINE_ORACLE(NAME, ROWS_NAME, T, P)                                   \
+static T P##_elem(int upper, const T *A, int lda, long long i, long long j)    \
+{                                                                              \
+    if (i == j) return P##_diag(&A[i + i * lda]);                              \
+    if (upper ? (i < j) : (i > j)) return A[i + j * lda];                      \
+    return P##_conj(A[j + i * lda]);                                           \
+}                                                                              \
+                                                                               \
+static T P##_row(int upper, int n, T alpha, const T *A, int lda, const T *x,   \
+                 int incx, T beta, const T *yi, long long i)                   \
+{                                                                              \
+    int j;                                                                     \
+    T res = P##_is_zero(beta) ? P##_zero() : P##_mul(beta, *yi);               \
+    if (!P##_is_zero(alpha)) {                                                 \
+        T sum = P##_zero();                                                    \
+        for (j = 0; j < n; ++j) {                                              \
+            T s = P##_elem(upper, A, lda, i, j);                               \
+            sum = P##_add(sum, P##_mul(s, x[vpos(n, incx, j)]));               \
+        }                                                                      \
+        res = P##_add(res, P##_mul(alpha, sum));                               \
+    }                                                                          \
+    return res;                                                                \
+}                                                                              \
+                                                                               \
 int NAME(char uplo, int n, T alpha, const T *A, int lda, const T *x,           \
          int incx, T beta, T *y, int incy)                                     \
 {                                                                              \
-    int upper, i, j;                                                           \
+    int upper, i;                                                              \
     int rc = check_args(uplo, n, A, lda, x, incx, y, incy, &upper);            \
-    T *v;                                                                      \
     if (rc) return rc;                                                         \
     if (n == 0 || (P##_is_zero(alpha) && P##_is_one(beta))) return 0;          \
-    /* y := beta*y (BLAS: beta == 0 writes zeros without reading y) */         \
-    if (!P##_is_one(beta)) {                                                   \
-        for (i = 0; i < n; ++i) {                                              \
-            T *yi = &y[vpos(n, incy, i)];                                      \
-            *yi = P##_is_zero(beta) ? P##_zero() : P##_mul(beta, *yi);         \
-        }                                                                      \
-    }                                                                          \
-    if (P##_is_zero(alpha)) return 0;                                          \
-    v = (T *)malloc(sizeof(T) * (size_t)n);                                    \
-    if (v == NULL) return -100;                                                \
-    for (i = 0; i < n; ++i) v[i] = P##_zero();                                 \
-    /* part one: each stored off-diagonal element, read once, used twice */    \
-    for (j = 0; j < n; ++j) {                                                  \
-        T xj = x[vpos(n, incx, j)];                                            \
-        T t = P##_zero();                                                      \
-        int lo = upper ? 0 : j + 1;                                            \
-        int hi = upper ? j : n;                                                \
-        T *yj = &y[vpos(n, incy, j)];                                          \
-        for (i = lo; i < hi; ++i) {                                            \
-            T a = A[(long long)i + (long long)j * lda];                        \
-            T xi = x[vpos(n, incx, i)];                                        \
-            v[i] = P##_add(v[i], P##_mul(a, xj));                              \
-            t = P##_add(t, P##_mul(P##_conj(a), xi));                          \
-        }                                                                      \
-        *yj = P##_add(*yj, P##_mul(alpha, t));                                 \
-    }                                                                          \
-    /* part two: the diagonal */                                               \
-    for (i = 0; i < n; ++i) {                                                  \
-        T d = P##_diag(&A[(long long)i + (long long)i * lda]);                 \
-        T *yi = &y[vpos(n, incy, i)];                                          \
-        *yi = P##_add(*yi, P##_mul(P##_mul(alpha, d), x[vpos(n, incx, i)]));   \
-    }                                                                          \
-    /* part three: y += alpha*v */                                             \
+    /* output i reads Y(i) alone, so y is updated in place row by row */       \
+    _Pragma("omp parallel for schedule(dynamic, 16) num_threads(g_threads)")   \
     for (i = 0; i < n; ++i) {                                                  \
         T *yi = &y[vpos(n, incy, i)];                                          \
-        *yi = P##_add(*yi, P##_mul(alpha, v[i]));                              \
+        *yi = P##_row(upper, n, alpha, A, lda, x, incx, beta, yi, i);          \
     }                                                                          \
-    free(v);                                                                   \
     return 0;                                                                  \
 }                                                                              \
                                                                                \
@@ -317,35 +330,17 @@ int ROWS_NAME(char uplo, int n, T alpha, const T *A, int lda, const T *x,      \
               int incx, T beta, const T *y, int incy, const long long *rows,   \
               int nrows, T *out)                                               \
 {                                                                              \
-    int upper, r, j;                                                           \
+    int upper, r;                                                              \
     int rc = check_args(uplo, n, A, lda, x, incx, y, incy, &upper);            \
     if (rc) return rc;                                                         \
     for (r = 0; r < nrows; ++r)                                                \
         if (rows[r] < 0 || rows[r] >= n) return -11;                           \
     for (r = 0; r < nrows; ++r) {                                              \
-        long long i = rows[r];                                                 \
-        T yi = y[vpos(n, incy, (int)i)];                                       \
-        T sum = P##_zero();                                                    \
-        T res;                                                                 \
-        if (P##_is_zero(alpha) && P##_is_one(beta)) {                          \
-            out[r] = yi;                                                       \
-            continue;                                                          \
-        }                                                                      \
-        res = P##_is_zero(beta) ? P##_zero() : P##_mul(beta, yi);              \
-        if (!P##_is_zero(alpha)) {                                             \
-            for (j = 0; j < n; ++j) {                                          \
-                T s;                                                           \
-                if (i == j)                                                    \
-                    s = P##_diag(&A[i + (long long)i * lda]);                  \
-                else if (upper ? (i < j) : (i > j))                            \
-                    s = A[i + (long long)j * lda];                             \
-                else                                                           \
-                    s = P##_conj(A[(long long)j + i * lda]);                   \
-                sum = P##_add(sum, P##_mul(s, x[vpos(n, incx, j)]));           \
-            }                                                                  \
-            res = P##_add(res, P##_mul(alpha, sum));                           \
-        }                                                                      \
-        out[r] = res;                                                          \
+        const T *yi = &y[vpos(n, incy, (int)rows[r])];                         \
+        out[r] = (P##_is_zero(alpha) && P##_is_one(beta))                      \
+                     ? *yi                                                     \
+                     : P##_row(upper, n, alpha, A, lda, x, incx, beta, yi,     \
+                               rows[r]);                                       \
     }                                                                          \
     return 0;                                                                  \
 }
@@ -650,34 +645,46 @@ static int shard_check(char uplo, int n, int panel, int nshards, int shard, cons
     return 0;
 }
 
+/* The shard's share of S*x, from the definition: output i is the sum over
+ * j ascending of S(i,j)*X(j) over the j whose S(i,j) is stored in a column
+ * the shard owns -- the stored copy of S(i,j) is A(i,j) in column j when
+ * (i,j) lies in the stored triangle (the diagonal included), else A(j,i) in
+ * column i (conjugated for Hermitian matrices).  Aloc holds owned column c
+ * as its local column loc[c], the number of owned columns left of c.  The
+ * outputs are independent and may be spread over oracle_set_threads()
+ * threads (same bits for any count). */
 #define DEFINE_SHARD(NAME, T, P)                                                \
 int NAME(char uplo, int n, int panel, int nshards, int shard, const T *Aloc,   \
          int lda, const T *x, int incx, T *p)                                  \
 {                                                                              \
-    int upper, i, j, l = 0;                                                    \
+    int upper, i, j, c, l = 0;                                                 \
+    int *loc;                                                                  \
     int rc = shard_check(uplo, n, panel, nshards, shard, Aloc, lda, x, incx, p, \
                          &upper);                                              \
     if (rc) return rc;                                                         \
-    for (i = 0; i < n; ++i) p[i] = P##_zero();                                 \
-    for (j = 0; j < n; ++j) {                                                  \
-        int lo, hi;                                                            \
-        T xj;                                                                  \
-        if (panel_owner(j / panel, nshards) != shard) continue;                \
-        xj = x[vpos(n, incx, j)];                                              \
-        lo = upper ? 0 : j;                                                    \
-        hi = upper ? j + 1 : n;                                                \
-        for (i = lo; i < hi; ++i) {                                            \
-            const T *ap = &Aloc[(long long)i + (long long)l * lda];            \
-            if (i == j) {                                                      \
-                p[j] = P##_add(p[j], P##_mul(P##_diag(ap), xj));               \
-            } else {                                                           \
-                T xi = x[vpos(n, incx, i)];                                    \
-                p[i] = P##_add(p[i], P##_mul(*ap, xj));                        \
-                p[j] = P##_add(p[j], P##_mul(P##_conj(*ap), xi));              \
-            }                                                                  \
+    loc = (int *)malloc(sizeof(int) * (size_t)(n > 0 ? n : 1));                \
+    if (loc == NULL) return -100;                                              \
+    for (c = 0; c < n; ++c)                                                    \
+        loc[c] = panel_owner(c / panel, nshards) == shard ? l++ : -1;          \
+    _Pragma("omp parallel for schedule(dynamic, 16) num_threads(g_threads)")   \
+    for (i = 0; i < n; ++i) {                                                  \
+        T sum = P##_zero();                                                    \
+        for (j = 0; j < n; ++j) {                                              \
+            int stored_here = upper ? (i <= j) : (i >= j);                     \
+            int col = stored_here ? j : i, row = stored_here ? i : j;          \
+            const T *ap;                                                       \
+            T s;                                                               \
+            if (loc[col] < 0) continue;  /* another shard's column */          \
+            ap = &Aloc[(long long)row + (long long)loc[col] * lda];            \
+            if (i == j)                                                        \
+                s = P##_diag(ap);                                              \
+            else                                                               \
+                s = stored_here ? *ap : P##_conj(*ap);                         \
+            sum = P##_add(sum, P##_mul(s, x[vpos(n, incx, j)]));               \
         }                                                                      \
-        ++l;                                                                   \
+        p[i] = sum;                                                            \
     }                                                                          \
+    free(loc);                                                                 \
     return 0;                                                                  \
 }
 

@@ -9,8 +9,8 @@
  * Source of the method: Imamura, Mukunoki, Yamada, Machida, "CUDA-xSYMV no
  * jisso to hyoka" (Implementation and evaluation of CUDA-xSYMV), IPSJ SIG
  * Technical Report 2014-HPC-146 No.14 -- cited below as "the CUDA-xSYMV
- * report".  Problem statement: §1 eq.(1); sequential three-part algorithm:
- * §2.1 Fig. 1; BLAS-style argument list: §2.2 Fig. 5; element types
+ * report".  Problem statement: §1 eq.(1), which the product follows as
+ * written; BLAS-style argument list: §2.2 Fig. 5; element types
  * (float2 / double2 complex, double2 double-double): §2.2.
  *
  * Matrices are column-major: element (i, j) of A lives at A[i + j*lda],
@@ -32,10 +32,13 @@ typedef struct { float re, im; } ocplx_f;    /* interleaved, like float2  */
 typedef struct { double re, im; } ocplx_d;   /* interleaved, like double2 */
 typedef struct { double hi, lo; } odd;       /* value = hi + lo exactly   */
 
-/* Full result by the three-part algorithm of §2.1 Fig. 1 (part one: the
- * off-diagonal elements used twice; part two: the diagonal; part three:
- * the row-role vector v added in), extended to uplo = 'L', to Hermitian
- * matrices and to BLAS increments. */
+/* Full result from the definition of eq.(1), output by output:
+ *   y(i) := beta*y(i) + alpha * sum_{j ascending} S(i,j)*x(j)
+ * where S is the full matrix implied by the stored triangle (the mirrored
+ * element conjugated for Hermitian matrices, whose diagonal is its real
+ * word); BLAS rules for beta == 0 (y not read), alpha == 0 and increments.
+ * The outputs are independent: the rows are spread over
+ * oracle_set_threads() threads, with the same bits for any count. */
 int oracle_ssymv(char uplo, int n, float alpha, const float *A, int lda,
                  const float *x, int incx, float beta, float *y, int incy);
 int oracle_dsymv(char uplo, int n, double alpha, const double *A, int lda,
@@ -47,7 +50,12 @@ int oracle_zhemv(char uplo, int n, ocplx_d alpha, const ocplx_d *A, int lda,
 int oracle_wsymv(char uplo, int n, odd alpha, const odd *A, int lda,
                  const odd *x, int incx, odd beta, odd *y, int incy);
 
-/* Selected rows only, straight from the definition of eq.(1):
+/* Threads of the full-product calls (default 1): 0, -1 for nthreads < 1,
+ * -2 when built without OpenMP and nthreads > 1.  get: the current count. */
+int oracle_set_threads(int nthreads);
+int oracle_get_threads(void);
+
+/* Selected rows only, the same definition of eq.(1):
  *   out[r] = beta*y(rows[r]) + alpha * sum_{j ascending} S(rows[r], j)*x(j)
  * where S is the full matrix implied by the stored triangle.  y is read
  * (not written); results go to out[0..nrows).  Used to check very large
@@ -146,8 +154,9 @@ int oracle_wtrmv(char uplo, char trans, char diag, int n, const odd *A, int lda,
  * sharded over several GPUs).  Panels of `panel` columns are dealt to
  * `nshards` shards round by round in boustrophedon order; Aloc holds the
  * shard's columns in ascending order (stride lda).  p (n elements,
- * contiguous) := the shard's share of S*x: every stored element of an owned
- * column taken in both roles, the diagonal once.  Codes: -1 uplo, -2 n,
+ * contiguous) := the shard's share of S*x: output i sums, j ascending, the
+ * terms S(i,j)*x(j) whose element is stored in an owned column (column j
+ * when (i,j) is in the stored triangle, column i otherwise).  Codes: -1 uplo, -2 n,
  * -3 panel <= 0, -4 nshards <= 0, -5 shard out of range, -6 Aloc NULL,
  * -7 lda, -8 x NULL, -9 incx == 0, -10 p NULL.
  * oracle_Xcombine: y := beta*y + alpha*(P[0] + P[1] + ...), partial g at

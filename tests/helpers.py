@@ -159,11 +159,57 @@ def abs_bound_terms(p):
     return t
 
 
+def _scalar_magnitudes(p):
+    if p.prec == "w":
+        return abs(p.alpha[0] + p.alpha[1]), abs(p.beta[0] + p.beta[1])
+    return abs(complex(p.alpha)), abs(complex(p.beta))
+
+
+def abs_bound_blocked(p, block: int = 512):
+    """(|alpha|*(|S||x|)_i + |beta|*|y_i|) for every logical row, read from
+    the stored triangle one block of columns at a time (no n x n array), so
+    that it serves the largest orders: a stored element A(r, c) adds
+    |A(r, c)||x_c| to row r and, off the diagonal, |A(r, c)||x_r| to row c
+    (|S| is symmetric).  A Hermitian diagonal counts its real word only."""
+    n, lda = p.n, p.lda
+    ax = _magnitude(p, p.x[vec_index(n, p.incx)])
+    ay = _magnitude(p, p.y[vec_index(n, p.incy)])
+    al, be = _scalar_magnitudes(p)
+    up = is_upper(p.uplo)
+    t = np.zeros(n)
+    for c0 in range(0, n, block):
+        c1 = min(n, c0 + block)
+        # rows holding stored elements of these columns: U [0, c1), L [c0, n)
+        r0, r1 = (0, c1) if up else (c0, n)
+        blk = p.A[c0 * lda:c1 * lda]
+        blk = blk.reshape(c1 - c0, lda, 2)[:, r0:r1] if p.prec == "w" else \
+            blk.reshape(c1 - c0, lda)[:, r0:r1]
+        if p.prec == "w":
+            M = np.abs(blk[..., 0] + blk[..., 1])    # M[c - c0, r - r0] = |A(r, c)|
+        else:
+            M = np.abs(blk.astype(np.complex128 if p.prec in ("c", "z") else np.float64))
+        # the diagonal square [c0, c1): keep the stored side only
+        k = np.arange(c1 - c0)
+        sq = M[:, c0 - r0:c1 - r0]
+        keep = (k[None, :] <= k[:, None]) if up else (k[None, :] >= k[:, None])
+        sq[~keep] = 0.0
+        if p.prec in ("c", "z"):
+            sq[k, k] = np.abs(blk[k, c0 - r0 + k].real.astype(np.float64))
+        t[r0:r1] += ax[c0:c1] @ M                     # row role, diagonal included
+        sq[k, k] = 0.0
+        t[c0:c1] += M @ ax[r0:r1]                     # mirrored role
+    t = al * t
+    if be != 0:
+        t = t + be * np.where(np.isfinite(ay), ay, 0.0)
+    return t
+
+
 def tolerance(p, rows=None):
     """Componentwise bound 4*n*eps*(|alpha|*(|S||x|)_i + |beta|*|y_i|), for all
-    rows or for the logical rows ``rows`` only (then without forming S)."""
+    rows (read block by block from the stored triangle) or for the logical
+    rows ``rows`` only."""
     if rows is None:
-        return 4.0 * max(p.n, 1) * EPS[p.prec] * abs_bound_terms(p)
+        return 4.0 * max(p.n, 1) * EPS[p.prec] * abs_bound_blocked(p)
     return 4.0 * max(p.n, 1) * EPS[p.prec] * abs_bound_rows(p, rows)
 
 

@@ -20,7 +20,7 @@ PRECS = SH.PRECS
 
 
 @pytest.fixture(scope="module", autouse=True)
-def _gpu():
+def _gpu(oracle_threads):
     G.torch_dev()
 
 

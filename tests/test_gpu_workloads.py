@@ -1,10 +1,12 @@
 """GPU parity at the benchmark workloads' full sizes, in the launch
 configuration the benchmark times (default tile configuration, the caller's
-stream).  Problems the oracle finishes in seconds are compared on every row;
-the largest are compared on a sample of rows (first and last rows, rows
-around panel and tile boundaries, random rows), which the oracle computes one
-by one from the definition.  Every workload is also run ten times and must
-give identical bytes."""
+stream).  Every symmetric / Hermitian workload is compared on every row with
+the oracle (run over the host's cores: its outputs are independent, so the
+thread count does not change its bytes), within the componentwise bound
+formed block by block from the stored triangle.  The general, rank-2 and
+triangular products past the symmetric ones are compared on sampled outputs
+(first and last, around tile boundaries, random).  Every symmetric workload is
+also run ten times and must give identical bytes."""
 import numpy as np
 import pytest
 
@@ -13,6 +15,11 @@ from blas_symmetric_mat_amd import workloads as W
 from tests import gpu_util as G
 
 pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _threads(oracle_threads):
+    yield
 
 
 def sample_rows(n, seed=0, k=160):
@@ -29,62 +36,58 @@ def sample_rows(n, seed=0, k=160):
     return np.unique(rows[(rows >= 0) & (rows < n)])
 
 
-def check(p, full: bool, reps: int = 10):
+def check(p, reps: int = 10):
+    """``reps`` runs with identical bytes, then every row against the oracle."""
     G.log(f"workload {p.name}: n={p.n} lda={p.lda}")
     dp = G.DeviceProblem(p)
     outs = [dp.run() for _ in range(reps)]
     assert len({G.digest(o) for o in outs}) == 1, "results differ between runs"
-    got = outs[0]
-    if full:
-        ref = oracle.symv_problem(p)
-        G.assert_close(p, got, ref, label=p.name)
-    else:
-        rows = sample_rows(p.n, seed=p.n)
-        ref = oracle.rows_problem(p, rows)
-        G.assert_close(p, got[rows], ref, rows=rows, label=p.name)
-    G.log(f"  ok ({'all rows' if full else f'{len(np.atleast_1d(ref))} sampled rows'})")
+    del dp
+    ref = oracle.symv_problem(p)
+    G.assert_close(p, outs[0], ref, label=p.name)
+    G.log(f"  ok (all {p.n} rows, {reps} identical runs)")
 
 
 def test_ssymv_lower_n1024():
-    check(W.ssymv_lower_n1024(), full=True)
+    check(W.ssymv_lower_n1024())
 
 
 def test_dsymv_upper_n8192_lda8200_beta0():
     p = W.dsymv_upper_n8192_lda8200_beta0()
     p.y[:] = np.nan  # beta = 0: y must be ignored
-    check(p, full=True)
+    check(p)
 
 
 @pytest.mark.parametrize("prec", ["s", "d"])
 @pytest.mark.parametrize("uplo", ["L", "U"])
 @pytest.mark.parametrize("n", [2048, 4096, 8192])
 def test_sweep_small(prec, uplo, n):
-    check(W.symv_sweep(prec, uplo, n), full=True)
+    check(W.symv_sweep(prec, uplo, n))
 
 
 @pytest.mark.parametrize("prec", ["s", "d"])
 @pytest.mark.parametrize("uplo", ["L", "U"])
 @pytest.mark.parametrize("n", [10007, 16384, 24576, 32767, 32768])
 def test_sweep_large(prec, uplo, n):
-    check(W.symv_sweep(prec, uplo, n), full=False, reps=5)
+    check(W.symv_sweep(prec, uplo, n))
 
 
 @pytest.mark.parametrize("uplo", ["L", "U"])
 def test_element_offsets_beyond_2_31(uplo):
     """n = lda = 46341: the last stored element's index i + j*lda exceeds
-    2^31 - 1 (46341^2 > 2^31), so every offset must be 64-bit; sampled rows
-    (those near the end included) against the oracle, three identical runs."""
+    2^31 - 1 (46341^2 > 2^31), so every offset must be 64-bit; every row
+    against the oracle, ten identical runs."""
     n = 46341
     assert (n - 1) + (n - 1) * n > 2 ** 31 - 1
     p = W.make_problem("s", uplo, n, n, alpha=1.0, beta=1.0, seed=n,
                        name=f"ssymv-{uplo}-n{n}")
-    check(p, full=False, reps=3)
+    check(p)
 
 
 @pytest.mark.parametrize("prec", ["c", "z"])
 def test_hemv_lower_n16384(prec):
     p = W.hemv_lower_n16384(prec)
-    check(p, full=False)
+    check(p)
     # the diagonal's imaginary words (garbage here) are ignored: NaN there too
     q = W.hemv_lower_n16384(prec)
     q.A.imag[W.diag_index(q.n, q.lda)] = np.nan
@@ -94,21 +97,21 @@ def test_hemv_lower_n16384(prec):
 
 
 def test_wsymv_lower_n8192():
-    check(W.wsymv_lower_n8192(), full=True)
+    check(W.wsymv_lower_n8192())
 
 
 @pytest.mark.parametrize("prec", ["c", "z", "w"])
 @pytest.mark.parametrize("uplo", ["L", "U"])
 def test_n32768_device_drawn(prec, uplo):
     """CHEMV, ZHEMV and WSYMV at n = 32768 (uplo = L: the inputs the
-    benchmark times there; and U), drawn on the device: three identical runs,
-    then sampled rows against the oracle on the inputs copied back."""
+    benchmark times there; and U), drawn on the device: ten identical runs,
+    then every row against the oracle on the inputs copied back."""
     import torch
     import blas_symmetric_mat_amd as X
     G.log(f"device-drawn {prec} {uplo} n=32768")
     p = W.metric_order_on_device(prec, 32768, uplo)
     outs = set()
-    for _ in range(3):
+    for _ in range(10):
         y = p.y.clone()
         getattr(X, G.ENTRY[prec])(p.uplo, p.n, p.alpha, p.A, p.lda, p.x, p.incx, p.beta, y,
                                   p.incy)
@@ -119,10 +122,9 @@ def test_n32768_device_drawn(prec, uplo):
     h = W.problem_to_host(p)
     del p, y
     torch.cuda.empty_cache()
-    rows = sample_rows(h.n, seed=h.n, k=100)
-    ref = oracle.rows_problem(h, rows)
-    G.assert_close(h, got[rows], ref, rows=rows, label=h.name)
-    G.log(f"  ok ({len(rows)} sampled rows)")
+    ref = oracle.symv_problem(h)
+    G.assert_close(h, got, ref, label=h.name)
+    G.log(f"  ok (all {h.n} rows)")
 
 
 # ------------------------------------------- xGEMV beside the symmetric sweep

@@ -18,28 +18,27 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "xsymv_oracle.c")
 
 # (name, text in the oracle, replacement, occurrence to change or None = all)
 MUTANTS = [
-    ("column role without conjugate",
-     "t = P##_add(t, P##_mul(P##_conj(a), xi));",
-     "t = P##_add(t, P##_mul(a, xi));", None),
-    ("row role with x(i)",
-     "v[i] = P##_add(v[i], P##_mul(a, xj));",
-     "v[i] = P##_add(v[i], P##_mul(a, xi));", None),
-    ("part two dropped",
-     "*yi = P##_add(*yi, P##_mul(P##_mul(alpha, d), x[vpos(n, incx, i)]));",
-     "(void)d;", None),
-    ("part three dropped",
-     "*yi = P##_add(*yi, P##_mul(alpha, v[i]));",
-     "(void)yi;", None),
-    ("upper loop includes the diagonal",
-     "int hi = upper ? j : n;", "int hi = upper ? j + 1 : n;", None),
-    ("lower loop includes the diagonal",
-     "int lo = upper ? 0 : j + 1;", "int lo = upper ? 0 : j;", None),
-    ("transposed read",
-     "T a = A[(long long)i + (long long)j * lda];",
-     "T a = A[(long long)j + (long long)i * lda];", None),
+    ("mirrored element not conjugated",
+     "return P##_conj(A[j + i * lda]);", "return A[j + i * lda];", None),
+    ("mirrored element read from the unstored triangle",
+     "return P##_conj(A[j + i * lda]);", "return P##_conj(A[i + j * lda]);", None),
+    ("stored element read transposed",
+     "if (upper ? (i < j) : (i > j)) return A[i + j * lda];",
+     "if (upper ? (i < j) : (i > j)) return A[j + i * lda];", None),
+    ("triangles swapped",
+     "if (upper ? (i < j) : (i > j)) return", "if (upper ? (i > j) : (i < j)) return", None),
+    ("diagonal dropped",
+     "if (i == j) return P##_diag(&A[i + i * lda]);", "if (i == j) return P##_zero();", None),
+    ("x(i) in place of x(j)",
+     "sum = P##_add(sum, P##_mul(s, x[vpos(n, incx, j)]));",
+     "sum = P##_add(sum, P##_mul(s, x[vpos(n, incx, (int)i)]));", 1),
+    ("inner sum one term short",
+     "for (j = 0; j < n; ++j) {", "for (j = 0; j < n - 1; ++j) {", 1),
     ("beta = 0 multiplies y",
-     "*yi = P##_is_zero(beta) ? P##_zero() : P##_mul(beta, *yi);",
-     "*yi = P##_mul(beta, *yi);", None),
+     "T res = P##_is_zero(beta) ? P##_zero() : P##_mul(beta, *yi);",
+     "T res = P##_mul(beta, *yi);", 1),
+    ("alpha dropped",
+     "res = P##_add(res, P##_mul(alpha, sum));", "res = P##_add(res, sum);", None),
     ("Hermitian diagonal keeps the imaginary word (single)",
      "r.im = 0.0f;", "r.im = p->im;", 1),
     ("Hermitian diagonal keeps the imaginary word (double)",
@@ -58,11 +57,6 @@ MUTANTS = [
      "r.lo = fma(a, b, -p);", "r.lo = 0.0;", None),
     ("increments ignored",
      "return start + (long long)k * inc;", "return (long long)k;", None),
-    ("rows: mirrored element not conjugated",
-     "s = P##_conj(A[(long long)j + i * lda]);",
-     "s = A[(long long)j + i * lda];", None),
-    ("rows: alpha dropped",
-     "res = P##_add(res, P##_mul(alpha, sum));", "res = P##_add(res, sum);", None),
     ("gemv: 'N' reads the transposed element",
      "T a = tr == 0 ? A[(long long)o + (long long)k * lda]",
      "T a = tr == 0 ? A[(long long)k + (long long)o * lda]", None),
@@ -70,7 +64,7 @@ MUTANTS = [
      "if (tr == 2) a = P##_conj(a);", "(void)0;", None),
     ("gemv: beta = 0 multiplies y",
      "T res = P##_is_zero(beta) ? P##_zero() : P##_mul(beta, *yi);",
-     "T res = P##_mul(beta, *yi);", None),
+     "T res = P##_mul(beta, *yi);", 2),
     ("gemv: alpha dropped",
      "res = P##_add(res, P##_mul(alpha, P##_gemv_dot(",
      "res = P##_add(res, (P##_gemv_dot(", 1),
@@ -106,17 +100,17 @@ MUTANTS = [
      "out[i] = sum;", "out[i] = sum; x[vpos(n, incx, i)] = sum;", None),
     ("shard: panels dealt cyclically, not back and forth",
      "return round % 2 == 0 ? pos : nshards - 1 - pos;", "(void)round; return pos;", None),
-    ("shard: column role dropped",
-     "p[j] = P##_add(p[j], P##_mul(P##_conj(*ap), xi));", "(void)xi;", None),
-    ("shard: column role without conjugate",
-     "p[j] = P##_add(p[j], P##_mul(P##_conj(*ap), xi));",
-     "p[j] = P##_add(p[j], P##_mul(*ap, xi));", None),
+    ("shard: mirrored terms dropped",
+     "s = stored_here ? *ap : P##_conj(*ap);",
+     "if (!stored_here) continue; s = *ap;", None),
+    ("shard: mirrored terms without conjugate",
+     "s = stored_here ? *ap : P##_conj(*ap);", "s = *ap;", None),
     ("shard: diagonal counted twice",
-     "p[j] = P##_add(p[j], P##_mul(P##_diag(ap), xj));",
-     "p[j] = P##_add(p[j], P##_mul(P##_add(P##_diag(ap), P##_diag(ap)), xj));", None),
+     "s = P##_diag(ap);", "s = P##_add(P##_diag(ap), P##_diag(ap));", None),
     ("shard: local column index not advanced",
-     "        ++l;                                                                   \\",
-     "                                                                               \\", None),
+     "== shard ? l++ : -1;", "== shard ? l : -1;", None),
+    ("shard: mirrored term owned by column j",
+     "int col = stored_here ? j : i, row", "int col = j, row", None),
     ("combine: partials summed out of rank order",
      "for (g = 1; g < nshards; ++g)", "for (g = nshards - 1; g >= 1; --g)", None),
     ("combine: beta = 0 multiplies y",
