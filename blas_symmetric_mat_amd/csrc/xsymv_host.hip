@@ -40,7 +40,10 @@ struct DeviceState {
     std::map<ShardKey, std::unique_ptr<StripPlan>> shard_plans;
     std::map<std::tuple<int, int, int, int>, std::unique_ptr<StripPlan>> gemv_plans;  // m, n, R, G
     std::map<hipStream_t, Workspace> workspaces;
-    std::map<std::pair<const void*, int>, int> resident;  // (kernel, threads) -> blocks
+    // (kernel, threads) -> blocks.  Guarded by its own lock: size queries
+    // reach it without `mu`, product calls with `mu` held.
+    std::mutex resident_mu;
+    std::map<std::pair<const void*, int>, int> resident;
 };
 
 namespace {
@@ -219,6 +222,7 @@ int resident_blocks(const void* kernel, int threads, int* out)
     XSYMV_HIP(hipGetDevice(&dev));
     DeviceState* ds = device_state(dev);
     auto key = std::make_pair(kernel, threads);
+    std::lock_guard<std::mutex> lk(ds->resident_mu);
     auto it = ds->resident.find(key);
     if (it != ds->resident.end()) {
         *out = it->second;
@@ -944,36 +948,45 @@ int xsymv_release(void)
 {
     int dev = 0;
     XSYMV_HIP(hipGetDevice(&dev));
-    XSYMV_HIP(hipDeviceSynchronize());
     DeviceState* ds = device_state(dev);
+    // Lock first, so that no call can enqueue work on a buffer between the
+    // synchronisation and the frees.
     std::lock_guard<std::mutex> lk(ds->mu);
+    XSYMV_HIP(hipDeviceSynchronize());
+    // Every entry is dropped from its map whether or not its free succeeded,
+    // so a later call or release never reuses or frees it again; the first
+    // error is returned after all frees were attempted.
+    hipError_t first = hipSuccess;
+    auto note = [&](hipError_t e) {
+        if (e != hipSuccess && first == hipSuccess) first = e;
+    };
     for (auto& kv : ds->workspaces)
-        if (kv.second.owned && kv.second.ptr) XSYMV_HIP(hipFree(kv.second.ptr));
+        if (kv.second.owned && kv.second.ptr) note(hipFree(kv.second.ptr));
     ds->workspaces.clear();
     for (auto& kv : ds->plans) {
         Plan* p = kv.second.get();
-        XSYMV_HIP(hipFree(p->d_tiles));
-        XSYMV_HIP(hipFree(p->d_slot_base));
-        XSYMV_HIP(hipHostFree(p->h_tiles));
-        XSYMV_HIP(hipHostFree(p->h_slot_base));
+        note(hipFree(p->d_tiles));
+        note(hipFree(p->d_slot_base));
+        note(hipHostFree(p->h_tiles));
+        note(hipHostFree(p->h_slot_base));
     }
     ds->plans.clear();
     for (auto& kv : ds->strip_plans) {
-        XSYMV_HIP(hipFree(kv.second->d_blocks));
-        XSYMV_HIP(hipHostFree(kv.second->h_pinned));
+        note(hipFree(kv.second->d_blocks));
+        note(hipHostFree(kv.second->h_pinned));
     }
     ds->strip_plans.clear();
     for (auto& kv : ds->shard_plans) {
-        XSYMV_HIP(hipFree(kv.second->d_blocks));
-        XSYMV_HIP(hipHostFree(kv.second->h_pinned));
+        note(hipFree(kv.second->d_blocks));
+        note(hipHostFree(kv.second->h_pinned));
     }
     ds->shard_plans.clear();
     for (auto& kv : ds->gemv_plans) {
-        XSYMV_HIP(hipFree(kv.second->d_blocks));
-        XSYMV_HIP(hipHostFree(kv.second->h_pinned));
+        note(hipFree(kv.second->d_blocks));
+        note(hipHostFree(kv.second->h_pinned));
     }
     ds->gemv_plans.clear();
-    return 0;
+    return first == hipSuccess ? 0 : ERR_HIP + (int)first;
 }
 
 int xsymv_num_configs(int prec) { return num_configs(prec); }

@@ -100,3 +100,59 @@ def test_one_stream_growing_and_shrinking_workspace():
     for _ in range(2):
         for d, r in zip(devs, ref):
             assert G.digest(d.run()) == r
+
+
+def test_size_queries_beside_running_calls():
+    """Workspace-size queries (which fill the per-device cache of resident
+    workgroup counts) from one thread while products run on other threads'
+    streams: the queries answer consistently and the products keep their
+    bytes."""
+    import torch
+    import blas_symmetric_mat_amd as X
+    X.release()
+    jobs = [_jobs(7000 + 100 * t) for t in range(2)]
+    devs = [[(k, _device(k, p)) for k, p in js] for js in jobs]
+    want = [[G.digest(_run_uploaded(k, d)) for k, d in ds] for ds in devs]
+    queries = [lambda: X.workspace_bytes("s", "L", 3001),
+               lambda: X.workspace_bytes("w", "U", 777),
+               lambda: X.gemv_workspace_bytes("d", "T", 2000, 1500),
+               lambda: X.trmv_workspace_bytes("c", "U", "N", 1500),
+               lambda: X.shard_workspace_bytes("z", "L", 4000, 64, 4, 1),
+               lambda: X.config_workgroups("d", 0, "U")]
+    first = [q() for q in queries]
+    errors = []
+    stop = threading.Event()
+
+    def runner(t):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for r in range(4):
+                    for j, (k, d) in enumerate(devs[t]):
+                        if G.digest(_run_uploaded(k, d)) != want[t][j]:
+                            errors.append(("product", t, r, j))
+        except Exception as e:  # reported below
+            errors.append((t, repr(e)))
+
+    def asker():
+        try:
+            while not stop.is_set():
+                got = [q() for q in queries]
+                if got != first:
+                    errors.append(("query", got, first))
+                    return
+        except Exception as e:  # reported below
+            errors.append(("asker", repr(e)))
+
+    G.log("concurrency: size queries beside 2 product threads")
+    ths = [threading.Thread(target=runner, args=(t,)) for t in range(2)]
+    ask = threading.Thread(target=asker)
+    ask.start()
+    for th in ths:
+        th.start()
+    for th in ths:
+        th.join(timeout=240)
+    stop.set()
+    ask.join(timeout=60)
+    assert not any(th.is_alive() for th in ths + [ask]), "a thread did not finish"
+    assert not errors, errors[:5]
