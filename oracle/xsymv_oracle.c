@@ -654,10 +654,31 @@ static int shard_check(char uplo, int n, int panel, int nshards, int shard, cons
  * outputs are independent and may be spread over oracle_set_threads()
  * threads (same bits for any count). */
 #define DEFINE_SHARD(NAME, T, P)                                                \
+static T P##_shard_row(int upper, int n, const int *loc, const T *Aloc,        \
+                       int lda, const T *x, int incx, int i)                   \
+{                                                                              \
+    int j;                                                                     \
+    T sum = P##_zero();                                                        \
+    for (j = 0; j < n; ++j) {                                                  \
+        int stored_here = upper ? (i <= j) : (i >= j);                         \
+        int col = stored_here ? j : i, row = stored_here ? i : j;              \
+        const T *ap;                                                           \
+        T s;                                                                   \
+        if (loc[col] < 0) continue;  /* another shard's column */              \
+        ap = &Aloc[(long long)row + (long long)loc[col] * lda];                \
+        if (i == j)                                                            \
+            s = P##_diag(ap);                                                  \
+        else                                                                   \
+            s = stored_here ? *ap : P##_conj(*ap);                             \
+        sum = P##_add(sum, P##_mul(s, x[vpos(n, incx, j)]));                   \
+    }                                                                          \
+    return sum;                                                                \
+}                                                                              \
+                                                                               \
 int NAME(char uplo, int n, int panel, int nshards, int shard, const T *Aloc,   \
          int lda, const T *x, int incx, T *p)                                  \
 {                                                                              \
-    int upper, i, j, c, l = 0;                                                 \
+    int upper, i, c, l = 0;                                                    \
     int *loc;                                                                  \
     int rc = shard_check(uplo, n, panel, nshards, shard, Aloc, lda, x, incx, p, \
                          &upper);                                              \
@@ -667,23 +688,8 @@ int NAME(char uplo, int n, int panel, int nshards, int shard, const T *Aloc,   \
     for (c = 0; c < n; ++c)                                                    \
         loc[c] = panel_owner(c / panel, nshards) == shard ? l++ : -1;          \
     _Pragma("omp parallel for schedule(dynamic, 16) num_threads(g_threads)")   \
-    for (i = 0; i < n; ++i) {                                                  \
-        T sum = P##_zero();                                                    \
-        for (j = 0; j < n; ++j) {                                              \
-            int stored_here = upper ? (i <= j) : (i >= j);                     \
-            int col = stored_here ? j : i, row = stored_here ? i : j;          \
-            const T *ap;                                                       \
-            T s;                                                               \
-            if (loc[col] < 0) continue;  /* another shard's column */          \
-            ap = &Aloc[(long long)row + (long long)loc[col] * lda];            \
-            if (i == j)                                                        \
-                s = P##_diag(ap);                                              \
-            else                                                               \
-                s = stored_here ? *ap : P##_conj(*ap);                         \
-            sum = P##_add(sum, P##_mul(s, x[vpos(n, incx, j)]));               \
-        }                                                                      \
-        p[i] = sum;                                                            \
-    }                                                                          \
+    for (i = 0; i < n; ++i)                                                    \
+        p[i] = P##_shard_row(upper, n, loc, Aloc, lda, x, incx, i);            \
     free(loc);                                                                 \
     return 0;                                                                  \
 }

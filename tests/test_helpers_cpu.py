@@ -66,3 +66,20 @@ def test_oracle_set_threads_errors():
     lib = oracle.default()
     assert lib.set_threads(0) == -1
     assert lib.get_threads() == 1
+
+
+@pytest.mark.parametrize("prec", W.PRECISIONS)
+@pytest.mark.parametrize("uplo", ["L", "U"])
+def test_shard_oracle_threads_same_bytes(prec, uplo):
+    """The shard partial is the same for any thread count."""
+    from tests import test_oracle_shard as SH
+    lib = oracle.default()
+    p = SH.problem(prec, uplo, 257, 3, seed=21)
+    try:
+        outs = []
+        for t in (1, 4, 8):
+            assert lib.set_threads(t) == 0
+            outs.append(b"".join(SH.run_shard(lib, p, 16, 3, g).tobytes() for g in range(3)))
+        assert outs[0] == outs[1] == outs[2]
+    finally:
+        lib.set_threads(1)
