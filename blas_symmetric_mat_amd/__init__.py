@@ -32,10 +32,12 @@ __all__ = ["xsymv_s", "xsymv_d", "xhemv_c", "xhemv_z", "xsymv_w", "XsymvError",
            "trmv_workspace_bytes", "xsymv_shard_s", "xsymv_shard_d", "xhemv_shard_c",
            "xhemv_shard_z", "xsymv_shard_w", "xsymv_combine_s", "xsymv_combine_d",
            "xhemv_combine_c", "xhemv_combine_z", "xsymv_combine_w", "shard_columns", "shard_plan",
-           "shard_workspace_bytes"]
+           "shard_workspace_bytes", "xsymv_s_noalloc", "STATIC_SCRATCH_BYTES"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libxsymv.so")
 PREC_CODE = {"s": 0, "d": 1, "c": 2, "z": 3, "w": 4}
+# XSYMV_STATIC_SCRATCH_BYTES of include/xsymv.h: the static array of xsymv_s_noalloc
+STATIC_SCRATCH_BYTES = 32 << 20
 
 
 class XsymvError(RuntimeError):
@@ -43,6 +45,12 @@ class XsymvError(RuntimeError):
         self.code = code
         if code == 2000:
             msg = f"{name}: the workspace installed for this stream is too small"
+        elif code == 3000:
+            msg = f"{name}: the call needs more than the static array's {STATIC_SCRATCH_BYTES} bytes"
+        elif code == 3001:
+            msg = f"{name}: the selected configuration is not a row-strip one"
+        elif code == 3002:
+            msg = f"{name}: device index beyond the static table"
         elif code >= 1000:
             msg = f"{name}: HIP runtime error {code - 1000}"
         else:
@@ -167,6 +175,9 @@ def library():
             for nm in ("xsymv_save_config", "xsymv_load_config"):
                 getattr(lib, nm).restype = ci
                 getattr(lib, nm).argtypes = [ctypes.c_char_p]
+            lib.xsymv_s_noalloc.restype = ci
+            lib.xsymv_s_noalloc.argtypes = [cc, ci, ctypes.c_float, vp, ci, vp, ci,
+                                            ctypes.c_float, vp, ci, vp]
             lib.xsymv_clear_config.restype = ci
             lib.xsymv_clear_config.argtypes = []
             lib.xsymv_config_workgroups.restype = ci
@@ -240,6 +251,18 @@ def _call(prec, uplo, n, alpha, A, lda, x, incx, beta, y, incy, stream):
 def xsymv_s(uplo, n, alpha, A, lda, x, incx, beta, y, incy, stream=None):
     """SSYMV: y := alpha*S*x + beta*y, float32, S symmetric (one triangle)."""
     _call("s", uplo, n, alpha, A, lda, x, incx, beta, y, incy, stream)
+
+
+def xsymv_s_noalloc(uplo, n, alpha, A, lda, x, incx, beta, y, incy, stream=None):
+    """SSYMV without device allocation: xsymv_s's product and bytes, its
+    partial sums in the library's static array (shared by every call on the
+    GPU: calls that overlap in time race)."""
+    f = library().xsymv_s_noalloc
+    u = uplo.encode()[:1] if isinstance(uplo, str) else uplo
+    rc = f(u, n, _scalar("s", alpha), _addr(A), lda, _addr(x), incx, _scalar("s", beta),
+           _addr(y), incy, _stream(stream))
+    if rc != 0:
+        raise XsymvError("xsymv_s_noalloc", rc)
 
 
 def xsymv_d(uplo, n, alpha, A, lda, x, incx, beta, y, incy, stream=None):

@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libxsymv.so")
 UNITS = ["xsymv_host", "xsymv_prec_s", "xsymv_prec_d", "xsymv_prec_c", "xsymv_prec_z",
-         "xsymv_prec_w"]
+         "xsymv_prec_w", "xsymv_static"]
 ARCH = os.environ.get("XSYMV_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",

@@ -32,6 +32,9 @@ namespace xsymv {
 
 constexpr int ERR_HIP = 1000;
 constexpr int ERR_WORKSPACE = 2000;  // a caller-installed workspace is too small
+constexpr int ERR_STATIC_SIZE = 3000;    // the static array is too small for the call
+constexpr int ERR_STATIC_CONFIG = 3001;  // the selected configuration is not a row strip
+constexpr int ERR_STATIC_DEVICE = 3002;  // device index beyond the static table
 
 // Device workspace of one (device, stream): library-owned (grown with
 // hipMalloc on demand) or installed by the caller (never freed here).

@@ -342,6 +342,32 @@ size_t xsymv_workspace_bytes(int prec, char uplo, int n);
  * (a few KB per order and configuration) are still allocated by the library. */
 int xsymv_set_workspace(void *dev_ptr, size_t bytes, void *stream);
 
+/* SSYMV for callers that cannot allocate device memory -- code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * same product, arguments, return codes, configuration choice, kernels and
+ * work split as xsymv_s, hence the same bytes; but no device memory is ever
+ * allocated (no hipMalloc, hipFree or pinned host memory, and no timing
+ * events: xsymv_timing_* does not see these calls).  The partial sums and the
+ * work split live in one static device array of XSYMV_STATIC_SCRATCH_BYTES
+ * per GPU, part of the library's code object (every GPU the library runs on
+ * holds it until the process ends).
+ *
+ * The first call of a shape (uplo, n, configuration) on a GPU writes the work
+ * split into the array with a copy from host memory and waits for `stream`
+ * (so it cannot be captured); later calls of that shape enqueue kernels only.
+ * Calls on one GPU share the array: calls on one stream are ordered, but calls
+ * that overlap in time on one GPU (other streams, other threads) race on it
+ * and must not be issued.  Extra return codes, checked before any device work:
+ *   3000  the call needs more than XSYMV_STATIC_SCRATCH_BYTES (partials of
+ *         the configuration chosen for n, plus x gathered when incx != 1);
+ *   3001  the configuration selected for (uplo, n) by a caller rule is not a
+ *         row-strip one (column_runs 4 or 5) -- only those are supported;
+ *   3002  the current device index is 64 or more. */
+#define XSYMV_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+int xsymv_s_noalloc(char uplo, int n, float alpha, const float *A, int lda,
+                    const float *x, int incx, float beta, float *y, int incy,
+                    void *stream);
+
 /* Release every library-owned workspace and cached tile plan of the current
  * device and forget installed workspaces (synchronises the device first).
  * Returns 0 or 1000 + hipError_t. */
