@@ -7,33 +7,36 @@ alpha = beta = 1, seed 32768 (the largest size of the [SD]SYMV sweep).  The
 inputs are resident in HBM before timing starts.  `value` is GFLOPS counted
 as 2n^2 per call, over K timed steps between two device synchronisations.
 
-Printed as one JSON line, with:
+Printed as one JSON line (kept short), with:
   roofline      the streaming kernel's algorithmic bytes (stored triangle + x)
                 over its average duration, timed with HIP events recorded by
                 the library on the launch stream, against the 8 TB/s HBM peak;
-                `traffic` comes from committed rocprofv3 counter summaries when
-                they were taken on the current kernel source, else null;
-  stream_read_gbps  a plain streaming read of 4 GiB on the same device
-                (xsymv_read_bandwidth), the secondary reference: every rate
-                is also given as % of it (`pct_measured_read_peak`);
-  cpu_baseline  the CPU oracle (single thread) on the same problem;
-  ssyr2/dsyr2   the rank-2 update A := alpha*x*y^T + alpha*y*x^T + A on the
-                stored triangle (n = 32768), its bytes the triangle read and
-                written once;
-  s/d/z/wtrmv   the triangular product x := op(T)*x (n = 32768 real, 16384
-                complex and double-double), its bytes the triangle read once;
-  ...-8shards   one GPU's share of the product sharded over 8 GPUs (panels
-                of 256 columns): every shard in turn, the slowest reported,
-                and the rank-ordered combination of the 8 partials;
-  symv_over_gemv_time  the symmetric call's time over the general one's on
-                the same order (GEMV detail rows: SGEMV 'N' and 'T', DGEMV
-                'N', n = 32768) -- the report's claim that SYMV, reading one
-                triangle, takes about half of GEMV's time;
-  detail        the other workloads (fp64 n = 32768, both triangles, the small
-                and padded cases, CHEMV/ZHEMV n = 16384, WSYMV n = 8192), each
-                timed per call (20 calls, median and min) with the library's
-                events and a cache flush between calls when the matrix is
-                below 1 GiB.
+                `traffic` and `traffic_ratio` come from the committed
+                rocprofv3 counter record when it was taken on the current
+                kernel source and configuration, else null;
+  stream_read_gbps / copy_gbps  a plain streaming read of 4 GiB, and a plain
+                read + write (copy, and update in place) of 2 GiB, on the same
+                device: the measured references beside the specification;
+  cpu_baseline  the CPU oracle on the same inputs, on 1 core and on every
+                core the process may use (its outputs are independent, so the
+                threads change no bit), per workload;
+  configs       one row per benchmark workload, [us per call, % of 8 TB/s
+                for the call's algorithmic bytes, % for the streaming kernel's
+                own bytes over its time, counter traffic / algorithmic bytes or
+                null]: C1 SSYMV L n = 1024; C2 DSYMV U n = 8192, lda = 8200,
+                beta = 0; C3 the [SD]SYMV sweep, s/d x L/U x n in {2048, 4096,
+                8192, 16384, 24576, 32768, 10007, 32767}; C4 CHEMV/ZHEMV L
+                n = 16384; C5 WSYMV L n = 8192; CHEMV/ZHEMV/WSYMV L at
+                n = 32768 (inputs drawn on the device).  Each is timed per
+                call (library events around its two kernels, median of 20),
+                with the caches flushed before every call (1 GiB written and
+                read back) when the matrix is below 1 GiB;
+  rule_check    at the sweep's odd orders (10007, 32767) the built-in
+                configuration's time over the on-device autotuner's best;
+  other         SGEMV/DGEMV (the report's SYMV-vs-GEMV comparison),
+                SSYR2/DSYR2 (against the in-place copy rate), S/D/Z/WTRMV and
+                one GPU's share of the product sharded over 8 GPUs.
+--detail-json FILE writes every row's full record.
 
 Only one GPU is used: --gpus N with N > 1 exits with a message.
 """
@@ -68,8 +71,8 @@ def kernel_label(X, prec: str, uplo: str, idx: int) -> str:
     tri = "upper" if uplo == "U" else "lower"
     load = "nt" if ci["nontemporal"] else "cached"
     fam = ci["column_runs"]
-    if fam in (4, 5):
-        split = "height" if fam == 4 else "stored+height"
+    if fam in (4, 5, 6):
+        split = {4: "height", 5: "stored+height", 6: "height only"}[fam]
         return (f"symv_strip<{CTYPE[prec]}, {tri}, W={ci['waves']}, "
                 f"SW={ci['stripes'] // ci['waves']}, G={ci['cols_per_wave']}, {load}> "
                 f"(split: {split})")
@@ -366,23 +369,47 @@ def time_kernels(d: Dev, reps: int, flush=None):
     return rec
 
 
-def cpu_baseline(p, seconds: float):
-    """The oracle (plain C, one thread) on the same problem, repeated until
-    about ``seconds`` of CPU work."""
+def host_cores() -> int:
+    """Cores this process may run on (at most 16, the share of one GPU)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def cpu_time(p, threads: int, min_seconds: float) -> tuple[float, int]:
+    """Seconds per oracle call on the problem with ``threads`` threads, over
+    as many calls as take ``min_seconds`` (at least one)."""
     import oracle
+    lib = oracle.default()
+    assert lib.set_threads(threads) == 0
+    try:
+        reps, total = 0, 0.0
+        while total < min_seconds or reps == 0:
+            t0 = time.perf_counter()
+            lib.symv_problem(p)
+            total += time.perf_counter() - t0
+            reps += 1
+    finally:
+        lib.set_threads(1)
+    return total / reps, reps
+
+
+def cpu_baselines(problems: dict, headline: str, min_seconds: float) -> dict:
+    """The oracle (plain C) on the same inputs as the GPU rows, on 1 core and
+    on every core this process may use, per workload; the headline's 1-core
+    figure is `value`."""
     from blas_symmetric_mat_amd import roofline as R
-    reps, t_total = 0, 0.0
-    while t_total < seconds or reps == 0:
-        t0 = time.perf_counter()
-        oracle.symv_problem(p)
-        t_total += time.perf_counter() - t0
-        reps += 1
-    t = t_total / reps
-    return {"value": round(R.gflops_2n2(p.n, t), 3), "unit": "GFLOPS", "cores": 1,
-            "kind": "oracle",
-            "sample": f"the full {p.name} problem (same inputs as the GPU run), "
-                      f"{reps} calls, {t:.3f} s each, single-threaded C",
-            "cpu": cpu_model()}
+    cores = host_cores()
+    per = {}
+    for name, p in problems.items():
+        t1, r1 = cpu_time(p, 1, min_seconds)
+        tn, rn = cpu_time(p, cores, min_seconds)
+        per[name] = [round(R.gflops_2n2(p.n, t1), 3), round(R.gflops_2n2(p.n, tn), 3)]
+        log(f"cpu {name}: 1 core {t1:.3f} s, {cores} cores {tn:.3f} s")
+    h = per[headline]
+    return {"value": h[0], "unit": "GFLOPS", "cores": 1, "kind": "oracle",
+            "sample": f"full calls on the GPU rows' own inputs, repeated to >= {min_seconds} s; "
+                      f"per_config = [GFLOPS on 1 core, on {cores} cores] (OpenMP over rows)",
+            "n_cores": {"value": h[1], "cores": cores},
+            "per_config": per, "cpu": cpu_model()}
 
 
 def cpu_model():
@@ -393,6 +420,17 @@ def cpu_model():
     except OSError:
         pass
     return None
+
+
+def workload_key(p) -> str:
+    """Name of a symmetric problem in the counter record and in
+    --profile-workload: <prec>-<uplo>-n<N>[-lda<L>][-beta0]."""
+    k = f"{p.prec}-{p.uplo}-n{p.n}"
+    if p.lda != p.n:
+        k += f"-lda{p.lda}"
+    if beta_is_zero(p):
+        k += "-beta0"
+    return k
 
 
 def traffic_record(workload: str, kernel: str):
@@ -408,10 +446,22 @@ def traffic_record(workload: str, kernel: str):
     return rec
 
 
-def measure_detail(name, p, reps, flush, read_peak=None):
+def compact(row: dict) -> list:
+    """[us per call, % of 8 TB/s for the call, % for the streaming kernel,
+    counter traffic / algorithmic kernel bytes or None]"""
+    return [round(row["ms_per_call_median"] * 1e3, 1), row["pct_peak_hbm"],
+            row.get("kernel_pct_peak_hbm"), row.get("traffic_ratio")]
+
+
+def measure_detail(name, p, reps, flush, read_peak=None, quiet=False):
+    """One symmetric workload timed per call: the library's events around its
+    streaming kernel and its merge, median of `reps` calls, the caches
+    flushed before each call when the matrix is below 1 GiB."""
     from blas_symmetric_mat_amd import roofline as R
     import torch
-    log(f"detail: {name}")
+    import blas_symmetric_mat_amd as X
+    if not quiet:
+        log(f"detail: {name}")
     d = Dev(p)
     for _ in range(2):
         d.call()
@@ -424,17 +474,24 @@ def measure_detail(name, p, reps, flush, read_peak=None):
     t_call = tot[len(tot) // 2] * 1e-3
     bz = beta_is_zero(p)
     call_b = R.call_bytes(p.prec, p.n, bz)
-    import blas_symmetric_mat_amd as X
+    kb = R.tile_kernel_bytes(p.prec, p.n)
+    label = kernel_label(X, p.prec, p.uplo, X.current_config(p.prec, p.uplo, p.n, p.lda))
     out = {"prec": p.prec, "uplo": p.uplo, "n": p.n, "lda": p.lda,
-           "kernel": kernel_label(X, p.prec, p.uplo, X.current_config(p.prec, p.uplo, p.n)),
+           "kernel": label,
            "ms_per_call_median": round(t_call * 1e3, 4),
            "ms_per_call_min": round(tot[0], 4),
+           "kernel_ms_median": round(t_main * 1e3, 4),
+           "merge_ms_median": round(sorted(r[1] for r in rec)[len(rec) // 2], 4),
            "gflops_2n2": round(R.gflops_2n2(p.n, t_call), 2),
            "hbm_gbps_algorithmic": round(call_b / t_call / 1e9, 1),
            "pct_peak_hbm": round(100 * call_b / t_call / 1e9 / R.HBM_PEAK_GBPS, 1),
-           "tile_kernel_gbps": round(R.tile_kernel_bytes(p.prec, p.n) / t_main / 1e9, 1),
+           "tile_kernel_gbps": round(kb / t_main / 1e9, 1),
+           "kernel_pct_peak_hbm": round(100 * kb / t_main / 1e9 / R.HBM_PEAK_GBPS, 1),
            "flushed_between_calls": small,
            "calls": reps}
+    tr = traffic_record(workload_key(p), label)
+    out["traffic_bytes"] = tr["bytes_per_launch"] if tr else None
+    out["traffic_ratio"] = round(tr["bytes_per_launch"] / kb, 4) if tr else None
     if read_peak:
         out["pct_measured_read_peak"] = round(100 * call_b / t_call / 1e9 / read_peak, 1)
     if p.prec in ("c", "z"):
@@ -453,6 +510,21 @@ def measure_detail(name, p, reps, flush, read_peak=None):
         out["us_per_call_back_to_back"] = round(e0.elapsed_time(e1) * 10.0, 2)
     del d
     torch.cuda.empty_cache()
+    return out
+
+
+def rule_check(cases, reps: int = 10) -> dict:
+    """For each (prec, uplo, n) with lda = n: the built-in configuration's
+    median over the on-device autotuner's best (both as the autotuner times
+    them: flushed caches, events around the call), and both indices."""
+    import blas_symmetric_mat_amd as X
+    out = {}
+    for prec, uplo, n in cases:
+        X.clear_config()
+        builtin = X.current_config(prec, uplo, n, n)
+        best, ms = X.autotune(prec, uplo, n, reps=reps, lda=n)
+        X.clear_config()
+        out[f"{prec}-{uplo}-n{n}"] = [round(ms[builtin] / ms[best], 4), builtin, best]
     return out
 
 
@@ -534,41 +606,132 @@ def summarize_trace(trace_csv: str, stats_csv: str, command: str,
     return "\n".join(out) + "\n"
 
 
-def summarize_pmc(fetch_csv: str, write_csv: str, command: str, workload: str) -> dict:
-    """Per-launch HBM traffic of the streaming kernel from two rocprofv3 --pmc
-    runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what
-    the same counter reads for the plain 1 GiB elementwise kernel that
-    `--pmc-calibrate` runs (1 GiB read + 1 GiB written)."""
+# Workloads of the counter runs (--pmc-workloads), in launch order, drawn on
+# the device: C1, C2, C3 at n = 32768 (both triangles, fp32 and fp64), C4,
+# C5, and CHEMV/ZHEMV/WSYMV at n = 32768.
+PMC_WORKLOADS = ["s-L-n32768", "s-L-n1024", "d-U-n8192-lda8200-beta0", "s-U-n32768",
+                 "d-L-n32768", "d-U-n32768", "c-L-n16384", "z-L-n16384", "w-L-n8192",
+                 "c-L-n32768", "z-L-n32768", "w-L-n32768"]
+PMC_CALLS = 3
+
+
+def run_pmc_workloads(calls: int) -> None:
+    """Every PMC workload `calls` times, one after another, then a plain
+    1 GiB elementwise kernel of known traffic (1 GiB read, 1 GiB written)
+    that scales the counters."""
+    import torch
+    for name in PMC_WORKLOADS:
+        d = Dev(profile_problem(name))
+        for _ in range(calls):
+            d.call()
+        torch.cuda.synchronize()
+        del d
+        torch.cuda.empty_cache()
+        log(f"pmc workload {name}: {calls} calls")
+    a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    torch.neg(a, out=b)
+    torch.cuda.synchronize()
+
+
+def summarize_pmc(fetch_csv: str, write_csv: str, command: str, calls: int = PMC_CALLS) -> dict:
+    """Per-launch HBM traffic of the streaming kernel of every PMC workload
+    from two rocprofv3 --pmc runs of `--pmc-workloads` (FETCH_SIZE, then
+    WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads
+    for the plain 1 GiB elementwise kernel at the end of the run.  The
+    streaming-kernel dispatches come in PMC_WORKLOADS order, `calls` each."""
     import csv
     import statistics
-
-    def per_kernel(path):
-        agg = {}
-        for r in csv.DictReader(open(path)):
-            agg.setdefault((r["Kernel_Name"], int(r["Grid_Size"])), []).append(
-                float(r["Counter_Value"]))
-        return agg
-
-    f, w = per_kernel(fetch_csv), per_kernel(write_csv)
-    calib = [k for k in f if "neg_kernel" in k[0]]
-    if len(calib) != 1:
-        raise ValueError("calibration kernel not found exactly once")
-    gib = float(1 << 30)
-    fetch_scale = gib / (statistics.mean(f[calib[0]]) * 1024)
-    write_scale = gib / (statistics.mean(w[calib[0]]) * 1024)
-    mains = [k for k in f if "xsymv::symv_" in k[0] and "merge" not in k[0]]
-    main = max(mains, key=lambda k: statistics.mean(f[k]))
-    fb = statistics.mean(f[main]) * 1024 * fetch_scale
-    wb = statistics.mean(w[main]) * 1024 * write_scale
     import blas_symmetric_mat_amd as X
-    prec, uplo, n = workload[0], workload.split("-")[1], int(workload.split("-n")[-1])
-    kcfg = kernel_label(X, prec, uplo, X.current_config(prec, uplo, n))
-    return {workload: {"kernel": main[0], "kernel_config": kcfg, "grid_threads": main[1],
-                       "fetch_bytes_per_launch": round(fb), "write_bytes_per_launch": round(wb),
-                       "bytes_per_launch": round(fb + wb),
-                       "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4),
-                       "launches": len(f[main]), "kernel_source_digest": kernel_source_digest(),
-                       "command": command}}
+
+    def dispatches(path):
+        rows = list(csv.DictReader(open(path)))
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        return rows
+
+    f, w = dispatches(fetch_csv), dispatches(write_csv)
+    gib = float(1 << 30)
+    calf = [float(r["Counter_Value"]) for r in f if "neg_kernel" in r["Kernel_Name"]]
+    calw = [float(r["Counter_Value"]) for r in w if "neg_kernel" in r["Kernel_Name"]]
+    if len(calf) != 1 or len(calw) != 1:
+        raise ValueError("calibration kernel not found exactly once")
+    fetch_scale = gib / (calf[0] * 1024)
+    write_scale = gib / (calw[0] * 1024)
+
+    def mains(rows):
+        return [r for r in rows if "xsymv::symv_strip<" in r["Kernel_Name"]]
+
+    mf, mw = mains(f), mains(w)
+    if len(mf) != len(PMC_WORKLOADS) * calls or len(mw) != len(mf):
+        raise ValueError(f"expected {len(PMC_WORKLOADS) * calls} streaming launches, "
+                         f"got {len(mf)} / {len(mw)}")
+    out = {}
+    digest = kernel_source_digest()
+    for k, name in enumerate(PMC_WORKLOADS):
+        fr, wr = mf[k * calls:(k + 1) * calls], mw[k * calls:(k + 1) * calls]
+        fb = statistics.mean(float(r["Counter_Value"]) for r in fr) * 1024 * fetch_scale
+        wb = statistics.mean(float(r["Counter_Value"]) for r in wr) * 1024 * write_scale
+        parts = name.split("-")
+        prec, uplo, n = parts[0], parts[1], int(parts[2][1:])
+        lda = next((int(x[3:]) for x in parts[3:] if x.startswith("lda")), n)
+        kcfg = kernel_label(X, prec, uplo, X.current_config(prec, uplo, n, lda))
+        from blas_symmetric_mat_amd import roofline as R
+        kb = R.tile_kernel_bytes(prec, n)
+        out[name] = {"kernel": fr[0]["Kernel_Name"], "kernel_config": kcfg,
+                     "grid_threads": int(fr[0]["Grid_Size"]),
+                     "fetch_bytes_per_launch": round(fb), "write_bytes_per_launch": round(wb),
+                     "bytes_per_launch": round(fb + wb),
+                     "algorithmic_bytes_per_launch": kb,
+                     "traffic_ratio": round((fb + wb) / kb, 4),
+                     "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4),
+                     "launches": calls, "kernel_source_digest": digest, "command": command}
+    return out
+
+
+def profile_problem(name: str):
+    """The problem a profiler run times: <s|d|c|z|w>-<L|U>-n<N>[-lda<L>][-beta0],
+    drawn on the device (lda = n and the scalars of
+    workloads.metric_order_on_device unless given)."""
+    from blas_symmetric_mat_amd import workloads as W
+    parts = name.split("-")
+    ok = len(parts) >= 3 and parts[0] in W.PRECISIONS and parts[1] in ("L", "U") and \
+        parts[2].startswith("n") and parts[2][1:].isdigit()
+    lda, beta0 = None, False
+    for extra in parts[3:] if ok else []:
+        if extra.startswith("lda") and extra[3:].isdigit():
+            lda = int(extra[3:])
+        elif extra == "beta0":
+            beta0 = True
+        else:
+            ok = False
+    if not ok:
+        sys.exit(f"--profile-workload: expected <s|d|c|z|w>-<L|U>-n<N>[-lda<L>][-beta0], "
+                 f"got {name}")
+    prec, uplo, n = parts[0], parts[1], int(parts[2][1:])
+    p = W.metric_order_on_device(prec, n, uplo)
+    if lda is not None or beta0:
+        kw = {"alpha": p.alpha, "beta": p.beta}
+        if beta0:
+            kw["beta"] = (0.0, 0.0) if prec == "w" else 0.0
+        del p
+        p = W.draw_on_device(prec, uplo, n, lda, seed=n, name=name, **kw)
+    return p
+
+
+C3_ORDERS = [2048, 4096, 8192, 16384, 24576, 32768, 10007, 32767]
+
+
+def make_flush():
+    """Flush the caches (4 MB L2 per XCD, 256 MB MALL) before a timed call:
+    write a 1 GiB buffer, then read it back, so that they hold clean lines
+    of the buffer and the call pays no write-back of dirty ones."""
+    import torch
+    buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+
+    def flush():
+        buf.fill_(1.0)
+        buf.sum()
+    return flush, buf
 
 
 def main():
@@ -579,35 +742,37 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-detail", action="store_true", help="headline workload only")
     ap.add_argument("--detail-reps", type=int, default=20)
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--detail-json", metavar="FILE",
+                    help="also write every workload's full record to FILE")
+    ap.add_argument("--cpu-seconds", type=float, default=1.0,
+                    help="minimum CPU time per oracle timing (per workload and core count)")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-rule-check", action="store_true")
     ap.add_argument("--summarize-trace", nargs=3, metavar=("TRACE_CSV", "STATS_CSV", "COMMAND"),
                     help="print a markdown summary of a rocprofv3 kernel trace and exit")
     ap.add_argument("--bench-json", help="with --summarize-trace: the profiled run's bench "
                     "output, whose launch_ms_mean the summary sets beside the trace's")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"),
                     help="write profiles/traffic_counters.json from two rocprofv3 --pmc "
-                         "runs of the headline workload and exit")
+                         "runs of --pmc-workloads and exit")
+    ap.add_argument("--pmc-workloads", action="store_true",
+                    help="for rocprofv3 --pmc: run every counter workload a few times, "
+                         "then the calibration kernel, and exit")
     ap.add_argument("--profile-workload", metavar="NAME",
                     help="for a profiler: run only NAME's call --calls times and exit, "
-                         "printing nothing else (NAME = <s|d|c|z|w>-<L|U>-n<N>: inputs drawn "
-                         "on the device as workloads.metric_order_on_device draws them)")
+                         "printing nothing else (NAME = <s|d|c|z|w>-<L|U>-n<N>[-lda<L>]"
+                         "[-beta0]: inputs drawn on the device)")
     ap.add_argument("--calls", type=int, default=5)
-    ap.add_argument("--pmc-calibrate", action="store_true",
-                    help="also run a plain 1 GiB elementwise copy, for scaling "
-                         "rocprofv3 FETCH_SIZE/WRITE_SIZE readings")
     args = ap.parse_args()
     if args.summarize_trace:
         print(summarize_trace(*args.summarize_trace, bench_json=args.bench_json), end="")
         return
     if args.summarize_pmc:
-        rec = summarize_pmc(*args.summarize_pmc, workload="ssymv-L-n32768")
-        old = json.load(open(TRAFFIC_FILE)) if os.path.exists(TRAFFIC_FILE) else {}
-        old.update(rec)
+        rec = summarize_pmc(*args.summarize_pmc)
         with open(TRAFFIC_FILE, "w") as fh:
-            json.dump(old, fh, indent=1)
+            json.dump(rec, fh, indent=1)
             fh.write("\n")
-        print(json.dumps(rec, indent=1))
+        print(json.dumps({k: v["traffic_ratio"] for k, v in rec.items()}, indent=1))
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -624,15 +789,14 @@ def main():
     from blas_symmetric_mat_amd import workloads as W
 
     if args.profile_workload:
-        prec, uplo, n = args.profile_workload.split("-")
-        if prec not in W.PRECISIONS or uplo not in ("L", "U") or not n.startswith("n"):
-            sys.exit(f"--profile-workload: expected <s|d|c|z|w>-<L|U>-n<N>, "
-                     f"got {args.profile_workload}")
-        d = Dev(W.metric_order_on_device(prec, int(n[1:]), uplo))
+        d = Dev(profile_problem(args.profile_workload))
         for _ in range(args.calls):
             d.call()
         torch.cuda.synchronize()
         log(f"{args.profile_workload}: {args.calls} calls done")
+        return
+    if args.pmc_workloads:
+        run_pmc_workloads(PMC_CALLS)
         return
 
     if not os.path.exists(X.LIB_PATH):
@@ -676,10 +840,11 @@ def main():
     achieved = kb / (main_ms * 1e-3) / 1e9
     workload = f"ssymv-L-n{p.n}"
     kname = kernel_label(X, "s", "L", cfg_idx)
-    tr = traffic_record(workload, kname)
+    tr = traffic_record(workload_key(p), kname)
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": R.HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": round(achieved / R.HBM_PEAK_GBPS, 4),
             "traffic": tr["bytes_per_launch"] if tr else None,
+            "traffic_ratio": round(tr["bytes_per_launch"] / kb, 4) if tr else None,
             "kernel": kname, "launch_ms_mean": round(main_ms, 4),
             "merge_ms_mean": round(merge_ms, 4),
             "algorithmic_bytes_per_launch": kb}
@@ -691,61 +856,62 @@ def main():
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": "f32", "data": "synthetic",
            "config": {"workload": workload, "n": p.n, "lda": p.lda, "uplo": "L",
-                      "alpha": 1.0, "beta": 1.0, "seed": p.n, "distribution": "uniform[-1,1]",
-                      "tile_config": X.config_info("s", cfg_idx)},
+                      "alpha": 1.0, "beta": 1.0, "seed": p.n, "distribution": "uniform[-1,1]"},
            "hbm_gbps_algorithmic": round(call_b / (ms_per_step * 1e-3) / 1e9, 1),
            "pct_peak_hbm": round(100 * call_b / (ms_per_step * 1e-3) / 1e9 / R.HBM_PEAK_GBPS, 2),
            "roofline": roof}
 
-    # measured stream-read reference (secondary figure next to the spec peak)
+    # measured references beside the specification
     rd_med, rd_best = X.read_bandwidth(4 << 30, reps=10)
-    out["stream_read_gbps"] = {"median": round(rd_med, 1), "best": round(rd_best, 1),
-                               "bytes": 4 << 30, "kernel": "non-temporal 16-byte loads, best of 10 "
-                               "layouts: a private chunk per workgroup, or tiles swept "
-                               "by all workgroups together (xsymv_read_bandwidth)"}
+    cp_med, ip_med = X.copy_bandwidth(2 << 30, reps=10)
+    out["stream_read_gbps"] = round(rd_med, 1)
+    out["copy_gbps"] = {"copy": round(cp_med, 1), "in_place": round(ip_med, 1)}
     out["pct_measured_read_peak"] = round(100 * out["hbm_gbps_algorithmic"] / rd_med, 2)
     roof["frac_of_measured_read"] = round(achieved / rd_med, 4)
-    log(f"stream read: {rd_med:.0f} GB/s median, {rd_best:.0f} best")
+    log(f"references: read {rd_med:.0f} GB/s, copy {cp_med:.0f}, in place {ip_med:.0f}")
 
-    # -------------------------------------------------------------- CPU leg
-    if not args.no_cpu:
-        log("cpu baseline (oracle) ...")
-        out["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
-    else:
-        out["cpu_baseline"] = None
-    del p
-
-    # ------------------------------------------------------------ the rest
+    cpu_problems = {"C3 s-L-n32768": p}
+    detail = {}
     if not args.no_detail:
-        flush_buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+        flush, flush_buf = make_flush()
+        configs = {}
 
-        def flush():
-            flush_buf.fill_(1.0)
+        def sym(key, prob, keep_for_cpu=False):
+            row = measure_detail(key, prob, args.detail_reps, flush, rd_med, quiet=True)
+            detail[key] = row
+            configs[key] = compact(row)
+            if keep_for_cpu:
+                cpu_problems[key] = prob
 
-        detail = {}
-        cases = [("ssymv-U-n32768", lambda: W.symv_sweep("s", "U", 32768)),
-                 ("dsymv-L-n32768", lambda: W.symv_sweep("d", "L", 32768)),
-                 ("dsymv-U-n32768", lambda: W.symv_sweep("d", "U", 32768)),
-                 ("ssymv-L-n1024", W.ssymv_lower_n1024),
-                 ("dsymv-U-n8192-lda8200-beta0", W.dsymv_upper_n8192_lda8200_beta0),
-                 ("chemv-L-n16384", lambda: W.hemv_lower_n16384("c")),
-                 ("zhemv-L-n16384", lambda: W.hemv_lower_n16384("z")),
-                 ("wsymv-L-n8192", W.wsymv_lower_n8192)]
-        # every type at the metric's order n = 32768 (inputs drawn on the
-        # device: the host draw of a 17 GB triangle takes minutes)
-        cases += [(f"{k}-L-n32768-devdraw", lambda prec=prec: W.metric_order_on_device(prec, 32768))
-                  for prec, k in (("c", "chemv"), ("z", "zhemv"), ("w", "wsymv"))]
-        for name, make in cases:
-            detail[name] = measure_detail(name, make(), args.detail_reps, flush, rd_med)
-        gcases = [("sgemv-N-n32768", lambda: W.gemv_square("s", "N", 32768)),
-                  ("sgemv-T-n32768", lambda: W.gemv_square("s", "T", 32768)),
-                  ("dgemv-N-n32768", lambda: W.gemv_square("d", "N", 32768))]
-        for name, make in gcases:
+        t0 = time.perf_counter()
+        sym("C1 s-L-n1024", W.ssymv_lower_n1024(), True)
+        sym("C2 d-U-n8192-lda8200-beta0", W.dsymv_upper_n8192_lda8200_beta0(), True)
+        for prec in "sd":
+            for uplo in "LU":
+                for n in C3_ORDERS:
+                    key = f"C3 {prec}-{uplo}-n{n}"
+                    sym(key, p if key == "C3 s-L-n32768" else W.symv_sweep(prec, uplo, n))
+                log(f"C3 {prec}{uplo}: {len(C3_ORDERS)} orders [{time.perf_counter() - t0:.0f} s]")
+        del p
+        sym("C4 c-L-n16384", W.hemv_lower_n16384("c"), True)
+        sym("C4 z-L-n16384", W.hemv_lower_n16384("z"), True)
+        sym("C5 w-L-n8192", W.wsymv_lower_n8192(), True)
+        for prec in "czw":
+            sym(f"{prec}-L-n32768-devdraw", W.metric_order_on_device(prec, 32768))
+        log(f"C1-C5: {len(configs)} workloads [{time.perf_counter() - t0:.0f} s]")
+        out["configs"] = configs
+
+        other = {}
+        for name, make in [("sgemv-N-n32768", lambda: W.gemv_square("s", "N", 32768)),
+                           ("sgemv-T-n32768", lambda: W.gemv_square("s", "T", 32768)),
+                           ("dgemv-N-n32768", lambda: W.gemv_square("d", "N", 32768))]:
             detail[name] = measure_gemv_detail(name, make(), args.detail_reps, rd_med)
         for name, make in [
                 ("ssyr2-L-n32768", lambda: W.make_syr2_problem("s", "L", 32768, seed=32768)),
                 ("dsyr2-U-n32768", lambda: W.make_syr2_problem("d", "U", 32768, seed=32768))]:
-            detail[name] = measure_syr2_detail(name, make(), args.detail_reps, rd_med)
+            row = measure_syr2_detail(name, make(), args.detail_reps, rd_med)
+            row["pct_of_in_place_copy"] = round(100 * row["hbm_gbps_algorithmic"] / ip_med, 1)
+            detail[name] = row
         for name, make in [
                 ("strmv-L-N-n32768",
                  lambda: W.make_trmv_problem("s", "L", "N", "N", 32768, seed=32768)),
@@ -759,27 +925,44 @@ def main():
         for name, make in [("ssymv-L-n32768-8shards", lambda: W.symv_sweep("s", "L", 32768)),
                            ("dsymv-U-n32768-8shards", lambda: W.symv_sweep("d", "U", 32768))]:
             detail[name] = measure_shard_detail(name, make(), 256, 8, args.detail_reps, rd_med)
-        out["detail"] = detail
+        for name in ("sgemv-N-n32768", "sgemv-T-n32768", "dgemv-N-n32768", "ssyr2-L-n32768",
+                     "dsyr2-U-n32768", "strmv-L-N-n32768", "dtrmv-U-T-n32768",
+                     "ztrmv-L-C-n16384", "wtrmv-U-N-n16384"):
+            r = detail[name]
+            other[name] = [round(r["ms_per_call_median"] * 1e3, 1), r["pct_peak_hbm"]]
+        for name in ("ssyr2-L-n32768", "dsyr2-U-n32768"):
+            other[name].append(detail[name]["pct_of_in_place_copy"])
+        for name in ("ssymv-L-n32768-8shards", "dsymv-U-n32768-8shards"):
+            r = detail[name]
+            other[name] = [round(r["ms_per_call_median"] * 1e3, 1), r["pct_peak_hbm"],
+                           round(r["combine_ms_median"] * 1e3, 1)]
         # the report's point: SYMV reads half the bytes of GEMV on the same
         # order, so takes about half the time
-        out["symv_over_gemv_time"] = {
-            "sgemv-N-n32768": round(ms_per_step / detail["sgemv-N-n32768"]["ms_per_call_median"],
-                                    3),
-            "dsymv-L/dgemv-N-n32768": round(detail["dsymv-L-n32768"]["ms_per_call_median"] /
-                                            detail["dgemv-N-n32768"]["ms_per_call_median"], 3)}
+        other["symv_over_gemv_time"] = {
+            "s-L/sgemv-N": round(ms_per_step / detail["sgemv-N-n32768"]["ms_per_call_median"], 3),
+            "d-L/dgemv-N": round(detail["C3 d-L-n32768"]["ms_per_call_median"] /
+                                 detail["dgemv-N-n32768"]["ms_per_call_median"], 3)}
+        out["other"] = other
         del flush_buf
+        torch.cuda.empty_cache()
+        if not args.no_rule_check:
+            t0 = time.perf_counter()
+            out["rule_check"] = rule_check([(pr, u, n) for pr in "sd" for u in "LU"
+                                            for n in (10007, 32767)])
+            log(f"rule check [{time.perf_counter() - t0:.0f} s]")
+    else:
+        del p
 
-    if args.pmc_calibrate:
-        # a plain elementwise kernel of known traffic: reads 1 GiB, writes 1 GiB
-        a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
-        b = torch.empty_like(a)
-        torch.neg(a, out=b)
-        torch.cuda.synchronize()
-        out["pmc_calibration"] = {"kernel": "torch.neg float32", "bytes_read": a.nbytes,
-                                  "bytes_written": b.nbytes}
-
+    # -------------------------------------------------------------- CPU leg
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baselines(cpu_problems, "C3 s-L-n32768", args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
     out["kernel_source_digest"] = kernel_source_digest()
-    print(json.dumps(out))
+    if args.detail_json:
+        with open(args.detail_json, "w") as fh:
+            json.dump({"detail": detail, "line": out}, fh, indent=1)
+    print(json.dumps(out, separators=(",", ":")))
 
 
 if __name__ == "__main__":

@@ -32,7 +32,7 @@ __all__ = ["xsymv_s", "xsymv_d", "xhemv_c", "xhemv_z", "xsymv_w", "XsymvError",
            "trmv_workspace_bytes", "xsymv_shard_s", "xsymv_shard_d", "xhemv_shard_c",
            "xhemv_shard_z", "xsymv_shard_w", "xsymv_combine_s", "xsymv_combine_d",
            "xhemv_combine_c", "xhemv_combine_z", "xsymv_combine_w", "shard_columns", "shard_plan",
-           "shard_workspace_bytes", "xsymv_s_noalloc", "STATIC_SCRATCH_BYTES"]
+           "shard_workspace_bytes", "copy_bandwidth", "xsymv_s_noalloc", "STATIC_SCRATCH_BYTES"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libxsymv.so")
 PREC_CODE = {"s": 0, "d": 1, "c": 2, "z": 3, "w": 4}
@@ -206,6 +206,8 @@ def library():
             lib.xgemv_plan.argtypes = [ci, ci, ci, ci, ip, ci, ip, ci]
             lib.xsymv_read_bandwidth.restype = ci
             lib.xsymv_read_bandwidth.argtypes = [ctypes.c_size_t, ci, vp, fp, fp]
+            lib.xsymv_copy_bandwidth.restype = ci
+            lib.xsymv_copy_bandwidth.argtypes = [ctypes.c_size_t, ci, vp, fp, fp]
             lib.xsymv_version.restype = ctypes.c_char_p
             lib.xsymv_version.argtypes = []
             _lib = lib
@@ -686,7 +688,7 @@ def config_workgroups(prec: str, idx: int, uplo: str = "L") -> int:
 def strip_plan(uplo: str, n: int, R: int, G: int, split: int = 0):
     """The row-strip work split (host computation) under cost model `split`
     (0: strip height per column, doubled in the triangle; 1: stored rows plus
-    strip height): (blocks [G x 4]: first, end, first slot, first strip),
+    strip height; 2: strip height alone): (blocks [G x 4]: first, end, first slot, first strip),
     strip_base [NS+1], seg_base [NS+1]."""
     import numpy as np
     ns = (n + R - 1) // R
@@ -725,6 +727,18 @@ def read_bandwidth(nbytes: int = 4 << 30, reps: int = 10, stream=None):
     if rc != 0:
         raise XsymvError("xsymv_read_bandwidth", rc)
     return med.value, best.value
+
+
+def copy_bandwidth(nbytes: int = 2 << 30, reps: int = 10, stream=None):
+    """(copy, in-place update) GB/s, bytes read plus bytes written, of a plain
+    read + write of ``nbytes`` on the device."""
+    cp = ctypes.c_float()
+    ip_ = ctypes.c_float()
+    rc = library().xsymv_copy_bandwidth(nbytes, reps, _stream(stream), ctypes.byref(cp),
+                                        ctypes.byref(ip_))
+    if rc != 0:
+        raise XsymvError("xsymv_copy_bandwidth", rc)
+    return cp.value, ip_.value
 
 
 def release() -> None:

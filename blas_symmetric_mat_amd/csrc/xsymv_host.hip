@@ -116,7 +116,10 @@ void build_strip_plan_host(bool upper, int n, int R, int G, int split,
     //            triangle (the wave holding the diagonal takes element loads
     //            there, up to VEC of them per 16 bytes);
     //   split 1: the stored rows of the column plus R (suits element types of
-    //            one or two elements per 16 bytes, whose band costs less).
+    //            one or two elements per 16 bytes, whose band costs less);
+    //   split 2: R per column, band or not (suits the double-double type,
+    //            whose arithmetic, done for every row of a wave whether stored
+    //            or not, sets the time of a band column as of any other).
     const long long OVH = 16;
     std::vector<long long> prefix(total_pos + 1, 0);
     long long pos = 0;
@@ -128,6 +131,8 @@ void build_strip_plan_host(bool upper, int n, int R, int G, int split,
             long long c;
             if (split == 0) {
                 c = tri ? 2ll * rows : rows;
+            } else if (split == 2) {
+                c = rows;
             } else {
                 const long long stored = !tri ? rows : (upper ? (j - rs0 + 1) : (rs1 - j));
                 c = stored + R;
@@ -837,6 +842,29 @@ static __global__ __launch_bounds__(1024) void read_probe_sweep(const xsymv::u32
     if (acc == 0x9e3779b9u) out[blockIdx.x] = acc;
 }
 
+// Plain read + write, the reference for the rank-2 update (which reads the
+// stored triangle and writes it back): workgroup b copies its own chunk of
+// `per` 16-byte vectors from src to dst (INPLACE: dst = src, each vector
+// written back where it was read, as the update does), U vectors in flight
+// per lane, non-temporal loads and stores.
+template <int U, bool INPLACE>
+static __global__ __launch_bounds__(256) void copy_probe(xsymv::u32x4* src, xsymv::u32x4* dst,
+                                                         long long per)
+{
+    xsymv::u32x4* __restrict__ p = src + (long long)blockIdx.x * per;
+    xsymv::u32x4* __restrict__ q = (INPLACE ? src : dst) + (long long)blockIdx.x * per;
+    for (long long i = threadIdx.x; i < per; i += 256 * U) {
+        xsymv::u32x4 v[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) v[k] = __builtin_nontemporal_load(p + i + k * 256);
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            if (INPLACE) v[k].x ^= 1u;  // an update, not a plain store of what was read
+            __builtin_nontemporal_store(v[k], q + i + k * 256);
+        }
+    }
+}
+
 static __global__ __launch_bounds__(256) void fill_probe(uint32_t* buf, long long words)
 {
     for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < words;
@@ -917,6 +945,69 @@ int xsymv_read_bandwidth(size_t bytes, int reps, void* stream, float* gbps, floa
     }
     if (gbps) *gbps = best_med;
     if (best_gbps) *best_gbps = best_any;
+done:
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    (void)hipStreamSynchronize(st);
+    (void)hipFree(buf);
+    return rc;
+}
+
+int xsymv_copy_bandwidth(size_t bytes, int reps, void* stream, float* copy_gbps,
+                         float* inplace_gbps)
+{
+    if (bytes < ((size_t)64 << 20) || reps <= 0) return -1;
+    const hipStream_t st = (hipStream_t)stream;
+    const long long vecs = (long long)(bytes / 16);
+    char* buf = nullptr;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    int rc = 0;
+    float best[2] = {0.f, 0.f};  // [copy, in place]
+    auto fail = [&](hipError_t e) { rc = ERR_HIP + (int)e; };
+    hipError_t e;
+    if ((e = hipMalloc((void**)&buf, (size_t)vecs * 32)) != hipSuccess) return ERR_HIP + (int)e;
+    auto* src = reinterpret_cast<xsymv::u32x4*>(buf);
+    auto* dst = src + vecs;
+    fill_probe<<<4096, 256, 0, st>>>(reinterpret_cast<uint32_t*>(buf), vecs * 8);
+    if ((e = hipGetLastError()) != hipSuccess) { fail(e); goto done; }
+    if ((e = hipEventCreate(&e0)) != hipSuccess || (e = hipEventCreate(&e1)) != hipSuccess) {
+        fail(e);
+        goto done;
+    }
+    // layouts: {2048, 8192} workgroups x {4, 8} vectors in flight per lane,
+    // for the copy and for the in-place update; the best median of each kind
+    for (int layout = 0; layout < 8; ++layout) {
+        const bool inplace = layout >= 4;
+        const int blocks = (layout & 2) ? 8192 : 2048;
+        const int u = (layout & 1) ? 8 : 4;
+        const long long per = vecs / blocks / (256 * u) * (256 * u);
+        if (per == 0) continue;
+        std::vector<float> t;
+        for (int r = 0; r < reps + 1 && rc == 0; ++r) {
+            if ((e = hipEventRecord(e0, st)) != hipSuccess) { fail(e); break; }
+            if (inplace && u == 4)
+                copy_probe<4, true><<<blocks, 256, 0, st>>>(src, dst, per);
+            else if (inplace)
+                copy_probe<8, true><<<blocks, 256, 0, st>>>(src, dst, per);
+            else if (u == 4)
+                copy_probe<4, false><<<blocks, 256, 0, st>>>(src, dst, per);
+            else
+                copy_probe<8, false><<<blocks, 256, 0, st>>>(src, dst, per);
+            if ((e = hipGetLastError()) != hipSuccess) { fail(e); break; }
+            if ((e = hipEventRecord(e1, st)) != hipSuccess) { fail(e); break; }
+            if ((e = hipEventSynchronize(e1)) != hipSuccess) { fail(e); break; }
+            float ms = 0.f;
+            if ((e = hipEventElapsedTime(&ms, e0, e1)) != hipSuccess) { fail(e); break; }
+            if (r >= 1) t.push_back(ms);
+        }
+        if (rc) goto done;
+        std::sort(t.begin(), t.end());
+        const double b = 2.0 * (double)per * blocks * 16;  // read + written
+        float& slot = best[inplace ? 1 : 0];
+        slot = std::max(slot, (float)(b / (t[t.size() / 2] * 1e-3) / 1e9));
+    }
+    if (copy_gbps) *copy_gbps = best[0];
+    if (inplace_gbps) *inplace_gbps = best[1];
 done:
     if (e0) (void)hipEventDestroy(e0);
     if (e1) (void)hipEventDestroy(e1);
@@ -1204,7 +1295,7 @@ int xsymv_strip_plan(char uplo, int n, int R, int G, int split, int* blocks4, in
                      int* strip_base, int* seg_base, int max_strips)
 {
     if (!(uplo == 'U' || uplo == 'u' || uplo == 'L' || uplo == 'l') || n <= 0 || R <= 0 ||
-        G <= 0 || split < 0 || split > 1)
+        G <= 0 || split < 0 || split > 2)
         return -1;
     std::vector<StripBlock> blocks;
     std::vector<int> sb, segb;
@@ -1227,7 +1318,7 @@ int xsymv_shard_plan(char uplo, int n, int R, int G, int split, int panel, int n
                      int max_strips)
 {
     if (!(uplo == 'U' || uplo == 'u' || uplo == 'L' || uplo == 'l') || n <= 0 || R <= 0 ||
-        G <= 0 || split < 0 || split > 1 || panel <= 0 || nshards <= 0 || shard < 0 ||
+        G <= 0 || split < 0 || split > 2 || panel <= 0 || nshards <= 0 || shard < 0 ||
         shard >= nshards)
         return -1;
     std::vector<int> cols, c0;

@@ -935,7 +935,9 @@ __global__ __launch_bounds__(256) void tune_fill(T* a, long long count, unsigned
         a[i] = tune_elem<T>(seed + (unsigned long long)i);
 }
 
-// Flush the caches (L2, MALL) between timed calls: write a 1 GiB buffer.
+// Flush the caches (L2, MALL) between timed calls: write a 1 GiB buffer,
+// then read it back, so that the caches hold clean lines of the buffer and
+// the timed call pays no write-back of dirty ones.
 static __global__ __launch_bounds__(256) void tune_flush(uint32_t* buf, long long words)
 {
     for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < words;
@@ -943,9 +945,21 @@ static __global__ __launch_bounds__(256) void tune_flush(uint32_t* buf, long lon
         buf[i] = (uint32_t)i;
 }
 
+static __global__ __launch_bounds__(256) void tune_flush_read(uint32_t* buf, long long words)
+{
+    uint32_t acc = 0;
+    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < words;
+         i += (long long)gridDim.x * 256)
+        acc ^= buf[i];
+    // never true for what tune_flush wrote (values below 2^28, so their XOR
+    // is too), but it keeps the loads from being dropped
+    if (acc == 0xffffffffu) buf[0] = acc;
+}
+
 // Time every configuration of T for (uplo, n) on a matrix of leading
 // dimension lda: `reps` calls each (after two warm-up calls), each preceded
-// by a cache flush when the matrix is smaller than 1 GiB; the configuration
+// by a cache flush (1 GiB written and read back) when the matrix is smaller
+// than 1 GiB; the configuration
 // with the lowest median wins, ties going to the lower index.  ms[i]
 // receives configuration i's median (up to max_cfg).
 template <class T>
@@ -981,7 +995,10 @@ int autotune_impl(char uplo, int n, int lda_arg, int reps, hipStream_t stream, i
     for (size_t ci = 0; ci < sets.size(); ++ci) {
         std::vector<float> t;
         for (int r = 0; r < reps + 2 && rc == 0; ++r) {
-            if (flush) tune_flush<<<2048, 256, 0, stream>>>(fl, flush_words);
+            if (flush) {
+                tune_flush<<<2048, 256, 0, stream>>>(fl, flush_words);
+                tune_flush_read<<<2048, 256, 0, stream>>>(fl, flush_words);
+            }
             if ((e = hipEventRecord(e0, stream)) != hipSuccess) { fail(e); break; }
             // alpha = 1, beta = 0: y is overwritten, never grows
             rc = symv_run<T>(uplo, n, tune_one<T>(), A, (int)lda, x, 1, tune_zero<T>(), y, 1,

@@ -22,6 +22,7 @@ template <> const std::vector<KernelSet<cf32>>& kernel_sets<cf32>()
         make_strip<cf32, 8, 2, 4, true, 1>(),             // strip: R 2048, 16 KB runs, G 4, split by stored rows
         make_strip<cf32, 16, 2, 8, true, 1>(),            // strip: R 4096, 32 KB runs, G 8, split by stored rows
         make_strip<cf32, 16, 1, 8, true, 1>(),            // strip: R 2048, 16 KB runs, G 8, split by stored rows
+        make_strip<cf32, 16, 1, 8, true, 2>(),            // strip: R 2048, 16 KB runs, G 8, split by height alone
     };
     return v;
 }

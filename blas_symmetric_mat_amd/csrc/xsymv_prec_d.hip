@@ -29,6 +29,8 @@ template <> const std::vector<KernelSet<double>>& kernel_sets<double>()
         make_strip<double, 16, 2, 8, true, 1>(),          // strip: R 4096, 32 KB runs, G 8, split by stored rows
         make_strip<double, 16, 1, 16, true, 1>(),         // strip: R 2048, 16 KB runs, G 16, split by stored rows
         make_strip<double, 16, 1, 8, true, 1>(),          // strip: R 2048, 16 KB runs, G 8, split by stored rows
+        make_strip<double, 8, 1, 8, true, 2>(),           // strip: R 1024, 8 KB runs, G 8, split by height alone
+        make_strip<double, 16, 1, 8, true, 2>(),          // strip: R 2048, 16 KB runs, G 8, split by height alone
     };
     return v;
 }

@@ -29,6 +29,7 @@ template <> const std::vector<KernelSet<float>>& kernel_sets<float>()
         make_strip<float, 16, 1, 8, true>(),              // strip: R 4096, 16 KB runs, G 8
         make_strip<float, 16, 2, 8, true, 1>(),           // strip: R 8192, 32 KB runs, G 8, split by stored rows
         make_strip<float, 8, 4, 4, true, 1>(),            // strip: R 8192, 32 KB runs, G 4, split by stored rows
+        make_strip<float, 16, 1, 16, true, 2>(),          // strip: R 4096, 16 KB runs, G 16, split by height alone
     };
     return v;
 }

@@ -23,6 +23,9 @@ template <> const std::vector<KernelSet<ddreal>>& kernel_sets<ddreal>()
         make_strip<ddreal, 4, 4, 4, true, 1>(),           // strip: R 1024, 16 KB runs, G 4, split by stored rows
         make_strip<ddreal, 16, 1, 4, true, 1>(),          // strip: R 1024, 16 KB runs, G 4, split by stored rows
         make_strip<ddreal, 8, 2, 4, true>(),              // strip: R 1024, 16 KB runs, G 4
+        make_strip<ddreal, 4, 4, 4, true, 2>(),           // strip: R 1024, 16 KB runs, G 4, split by height alone
+        make_strip<ddreal, 4, 2, 4, true, 2>(),           // strip: R 512, 8 KB runs, G 4, split by height alone
+        make_strip<ddreal, 16, 1, 4, true, 2>(),          // strip: R 1024, 16 KB runs, G 4, split by height alone
     };
     return v;
 }

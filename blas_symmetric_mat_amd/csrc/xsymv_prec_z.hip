@@ -22,6 +22,8 @@ template <> const std::vector<KernelSet<cf64>>& kernel_sets<cf64>()
         make_strip<cf64, 16, 2, 4, true, 1>(),            // strip: R 2048, 32 KB runs, G 4, split by stored rows
         make_strip<cf64, 8, 2, 4, true, 1>(),             // strip: R 1024, 16 KB runs, G 4, split by stored rows
         make_strip<cf64, 16, 1, 8, true, 1>(),            // strip: R 1024, 16 KB runs, G 8, split by stored rows
+        make_strip<cf64, 16, 2, 4, true, 2>(),            // strip: R 2048, 32 KB runs, G 4, split by height alone
+        make_strip<cf64, 16, 1, 8, true, 2>(),            // strip: R 1024, 16 KB runs, G 8, split by height alone
     };
     return v;
 }

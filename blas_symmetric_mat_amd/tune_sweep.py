@@ -10,7 +10,9 @@ per-size rules (§3, Table 3).  This is the MI355X counterpart:
             for matrices under 1 GiB) and records each configuration's median
             time and the winner.  ``--stride-class 1`` measures with
             lda = n + 1 (columns that are not whole 64-byte lines; the grid
-            orders are multiples of 64, so lda = n is class 0), ``--n-min``
+            orders are multiples of 64, so lda = n is class 0), and adds the
+            size sweep's odd orders (10007 and 32767 for s and d) with
+            lda = n, ``--n-min``
             skips the smaller orders, ``--uplos`` limits the triangles, and
             ``--append`` adds the results to an existing record (replacing
             those of the same key).  Needs a GPU.
@@ -43,6 +45,10 @@ GRID = {
     "z": [64, 128, 256, 512, 1024, 2048, 4096, 8192, 12288, 16384, 24576],
     "w": [64, 128, 256, 512, 1024, 2048, 4096, 8192, 12288, 16384, 24576],
 }
+# orders measured for stride class 1 only, with lda = n: the odd orders of
+# the [SD]SYMV size-sweep workload, whose columns are not whole 64-byte lines
+EXTRA_CLASS1 = {"s": [10007, 32767], "d": [10007, 32767]}
+ELEM_BYTES = {"s": 4, "d": 8, "c": 8, "z": 16, "w": 16}
 SHAPE_KEYS = ("waves", "cols_per_wave", "stripes", "nontemporal", "x_in_lds", "column_runs")
 INT_MAX = 2**31 - 1
 
@@ -70,11 +76,14 @@ def measure(out_path: str, precs: str, reps: int, grid_max: int | None, cls: int
         # configurations are only ever appended: earlier indices keep their shapes
         assert shapes[:len(old)] == old, f"configuration list of {prec} was reordered"
         record["shapes"][prec] = shapes
+        orders = sorted(set(GRID[prec]) | (set(EXTRA_CLASS1.get(prec, [])) if cls else set()))
         for uplo in uplos:
-            for n in GRID[prec]:
+            for n in orders:
                 if (grid_max and n > grid_max) or n < n_min:
                     continue
-                lda = n + cls
+                # class 1: lda = n where its columns are already not whole
+                # 64-byte lines (odd orders), else n + 1
+                lda = n if cls and (n * ELEM_BYTES[prec]) % 64 else n + cls
                 t0 = time.time()
                 X.clear_config()
                 best, ms = X.autotune(prec, uplo, n, reps=reps, lda=lda)

@@ -361,7 +361,7 @@ int xsymv_set_workspace(void *dev_ptr, size_t bytes, void *stream);
  *   3000  the call needs more than XSYMV_STATIC_SCRATCH_BYTES (partials of
  *         the configuration chosen for n, plus x gathered when incx != 1);
  *   3001  the configuration selected for (uplo, n) by a caller rule is not a
- *         row-strip one (column_runs 4 or 5) -- only those are supported;
+ *         row-strip one (column_runs 4, 5 or 6) -- only those are supported;
  *   3002  the current device index is 64 or more. */
 #define XSYMV_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
 int xsymv_s_noalloc(char uplo, int n, float alpha, const float *A, int lda,
@@ -382,8 +382,9 @@ int xsymv_release(void);
  * the kernel family: 0 tiles, whole tile unrolled; 1 tiles, each wave walks
  * its columns one contiguous run at a time; 2 the same with the next run
  * prefetched; 3 tiles, all waves of a workgroup on one column; 4 row strips,
- * work split by strip height; 5 row strips, work split by stored rows plus
- * strip height.  Any output pointer may be NULL.  Returns 0, or -1 for a bad
+ * work split by strip height, doubled in the diagonal triangle; 5 row strips,
+ * work split by stored rows plus strip height; 6 row strips, work split by
+ * strip height alone.  Any output pointer may be NULL.  Returns 0, or -1 for a bad
  * index. */
 int xsymv_num_configs(int prec);
 int xsymv_config_info(int prec, int idx, int *waves, int *cols_per_wave,
@@ -448,7 +449,7 @@ int xsymv_clear_config(void);
 int xsymv_timing_enable(int on);
 int xsymv_timing_read(float *main_ms, float *merge_ms, int max);
 
-/* Workgroups a row-strip configuration (column_runs 4 or 5) is launched with
+/* Workgroups a row-strip configuration (column_runs 4, 5 or 6) is launched with
  * on the current device: the number of its workgroups the device holds at
  * once.  0 for other families, -1 for a bad index, -(1000 + hipError_t) on a
  * runtime error. */
@@ -457,7 +458,8 @@ int xsymv_config_workgroups(int prec, int idx, char uplo);
 /* The row-strip work split the library uses for order n, strips of R rows,
  * G workgroups and cost model `split` (0: every column of a strip costs the
  * strip's height, doubled in its diagonal triangle -- family 4; 1: a column
- * costs its stored rows plus the strip's height -- family 5), a host
+ * costs its stored rows plus the strip's height -- family 5; 2: every column
+ * costs the strip's height -- family 6), a host
  * computation with no device work: writes per workgroup
  * {first, end} of its range in the strips' concatenated column sequence,
  * its first segment slot and the strip of `first` into blocks4 (4 ints per
@@ -482,6 +484,22 @@ int xsymv_strip_plan(char uplo, int n, int R, int G, int split, int *blocks4,
  * Returns 0, -1 for bad arguments or 1000 + hipError_t. */
 int xsymv_read_bandwidth(size_t bytes, int reps, void *stream, float *gbps,
                          float *best_gbps);
+
+/* Measurement helper: the device's plain read + write bandwidth, the
+ * reference for the rank-2 update, which reads the stored triangle and
+ * writes it back (the report sets its results beside a measured copy rate as
+ * well as the specification, §4).  Allocates 2 * `bytes` (bytes >= 64 MiB),
+ * fills them, then for each of four layouts (2048 or 8192 workgroups of 256
+ * lanes, each moving its own contiguous chunk with 4 or 8 non-temporal
+ * 16-byte loads and stores in flight per lane) times `reps` launches after
+ * one warm-up: a copy from one buffer to the other, and an update in place
+ * (each vector written back where it was read).  Rates count the bytes read
+ * plus the bytes written.  Writes the best layout's median rate of the copy
+ * and of the in-place update in GB/s (either may be NULL); frees the buffer
+ * and synchronises the stream.  Returns 0, -1 for bad arguments or
+ * 1000 + hipError_t. */
+int xsymv_copy_bandwidth(size_t bytes, int reps, void *stream, float *copy_gbps,
+                         float *inplace_gbps);
 
 /* Library version string. */
 const char *xsymv_version(void);

@@ -81,38 +81,83 @@ def test_trace_summary_runs_and_headline(tmp_path):
     assert f"The first 5 launches of `{HEAD[:90]}`: mean 100.0 us" in head
 
 
+def pmc_rows(values):
+    """Dispatch rows of a --pmc-workloads run: per workload `calls` streaming
+    launches (each followed by a merge, whose readings must be ignored), then
+    the calibration kernel; values[k] = the k-th workload's streaming
+    readings (FETCH, WRITE)."""
+    neg = "void at::native::vectorized_elementwise_kernel<neg_kernel_cuda>(...)"
+    fetch, write, did = [], [], 0
+    for (fv, wv) in values:
+        for _ in range(bench.PMC_CALLS):
+            for name, f, w in ((HEAD, fv, wv), (MERGE, 9.0e6, 100.0)):
+                did += 1
+                fetch.append({"Dispatch_Id": did, "Kernel_Name": name, "Grid_Size": 262144,
+                              "Counter_Value": f})
+                write.append({"Dispatch_Id": did, "Kernel_Name": name, "Grid_Size": 262144,
+                              "Counter_Value": w})
+    did += 1
+    fetch.append({"Dispatch_Id": did, "Kernel_Name": neg, "Grid_Size": 4096,
+                  "Counter_Value": 524288.0})
+    write.append({"Dispatch_Id": did, "Kernel_Name": neg, "Grid_Size": 4096,
+                  "Counter_Value": 1048576.0})
+    return fetch, write
+
+
 def test_counter_summary_scales_by_the_calibration_kernel(tmp_path):
     """FETCH_SIZE reads 524288 KiB and WRITE_SIZE 1048576 KiB for the 1 GiB
-    calibration kernel (scales 2 and 1); the streaming kernel's readings are
-    scaled by them and the merge kernel is left out."""
-    neg = "void at::native::vectorized_elementwise_kernel<neg_kernel_cuda>(...)"
-    fetch = [{"Kernel_Name": neg, "Grid_Size": 4096, "Counter_Value": 524288.0}]
-    write = [{"Kernel_Name": neg, "Grid_Size": 4096, "Counter_Value": 1048576.0}]
-    for v in (1000000.0, 1000002.0):
-        fetch.append({"Kernel_Name": HEAD, "Grid_Size": 262144, "Counter_Value": v})
-        write.append({"Kernel_Name": HEAD, "Grid_Size": 262144, "Counter_Value": 4000.0})
-        fetch.append({"Kernel_Name": MERGE, "Grid_Size": 32768, "Counter_Value": 9.0e6})
-        write.append({"Kernel_Name": MERGE, "Grid_Size": 32768, "Counter_Value": 100.0})
+    calibration kernel (scales 2 and 1); each workload's streaming launches
+    are scaled by them, in launch order, and the merge kernels are left out."""
+    from blas_symmetric_mat_amd import roofline as R
+    vals = [(1000000.0 + k, 4000.0 + k) for k in range(len(bench.PMC_WORKLOADS))]
+    fetch, write = pmc_rows(vals)
+    fetch.reverse()  # the summary orders dispatches by id
     write_csv(tmp_path / "f.csv", fetch)
     write_csv(tmp_path / "w.csv", write)
-    rec = bench.summarize_pmc(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), "cmd",
-                              workload="ssymv-L-n32768")["ssymv-L-n32768"]
-    assert rec["kernel"] == HEAD
-    assert rec["fetch_scale"] == 2.0 and rec["write_scale"] == 1.0
-    assert rec["fetch_bytes_per_launch"] == 1000001 * 1024 * 2
-    assert rec["write_bytes_per_launch"] == 4000 * 1024
-    assert rec["bytes_per_launch"] == 1000001 * 1024 * 2 + 4000 * 1024
-    assert rec["launches"] == 2 and rec["grid_threads"] == 262144
-    assert rec["kernel_source_digest"] == bench.kernel_source_digest()
+    out = bench.summarize_pmc(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), "cmd")
+    assert list(out) == bench.PMC_WORKLOADS
+    for k, name in enumerate(bench.PMC_WORKLOADS):
+        rec = out[name]
+        assert rec["kernel"] == HEAD
+        assert rec["fetch_scale"] == 2.0 and rec["write_scale"] == 1.0
+        assert rec["fetch_bytes_per_launch"] == (1000000 + k) * 1024 * 2
+        assert rec["write_bytes_per_launch"] == (4000 + k) * 1024
+        assert rec["bytes_per_launch"] == (1000000 + k) * 2048 + (4000 + k) * 1024
+        prec, n = name[0], int(name.split("-")[2][1:])
+        assert rec["algorithmic_bytes_per_launch"] == R.tile_kernel_bytes(prec, n)
+        assert rec["launches"] == bench.PMC_CALLS and rec["grid_threads"] == 262144
+        assert rec["kernel_source_digest"] == bench.kernel_source_digest()
 
 
-def test_counter_summary_needs_the_calibration_kernel(tmp_path):
-    rows = [{"Kernel_Name": HEAD, "Grid_Size": 262144, "Counter_Value": 1.0}]
-    write_csv(tmp_path / "f.csv", rows)
-    write_csv(tmp_path / "w.csv", rows)
+def test_counter_summary_needs_every_launch_and_the_calibration_kernel(tmp_path):
+    vals = [(1.0, 1.0)] * len(bench.PMC_WORKLOADS)
+    fetch, write = pmc_rows(vals)
+    write_csv(tmp_path / "f.csv", fetch[:-1])
+    write_csv(tmp_path / "w.csv", write[:-1])
     with pytest.raises(ValueError, match="calibration"):
-        bench.summarize_pmc(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), "cmd",
-                            workload="ssymv-L-n32768")
+        bench.summarize_pmc(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), "cmd")
+    write_csv(tmp_path / "f.csv", fetch[2:])
+    write_csv(tmp_path / "w.csv", write[2:])
+    with pytest.raises(ValueError, match="streaming launches"):
+        bench.summarize_pmc(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), "cmd")
+
+
+def test_profile_workload_names():
+    from blas_symmetric_mat_amd import workloads as W
+
+    class P:
+        pass
+    for name in bench.PMC_WORKLOADS:
+        parts = name.split("-")
+        q = P()
+        q.prec, q.uplo, q.n = parts[0], parts[1], int(parts[2][1:])
+        q.lda = next((int(x[3:]) for x in parts[3:] if x.startswith("lda")), q.n)
+        q.beta = 0.0 if "beta0" in parts else 1.0
+        assert bench.workload_key(q) == name
+    assert bench.workload_key(W.dsymv_upper_n8192_lda8200_beta0()) == "d-U-n8192-lda8200-beta0"
+    for bad in ("x-L-n10", "s-Q-n10", "s-L-10", "s-L-n10-foo"):
+        with pytest.raises(SystemExit):
+            bench.profile_problem(bad)
 
 
 def test_traffic_record_only_for_current_source_and_configuration(tmp_path, monkeypatch):
