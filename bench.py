@@ -15,8 +15,8 @@ Printed as one JSON line (kept short), with:
                 rocprofv3 counter record when it was taken on the current
                 kernel source and configuration, else null;
   stream_read_gbps / copy_gbps  a plain streaming read of 4 GiB, and a plain
-                read + write (copy, and update in place) of 2 GiB, on the same
-                device: the measured references beside the specification;
+                copy of 2 GiB (bytes read plus written), on the same device:
+                the measured references beside the specification;
   cpu_baseline  the CPU oracle on the same inputs, on 1 core and on every
                 core the process may use (its outputs are independent, so the
                 threads change no bit), per workload;
@@ -34,7 +34,7 @@ Printed as one JSON line (kept short), with:
   rule_check    at the sweep's odd orders (10007, 32767) the built-in
                 configuration's time over the on-device autotuner's best;
   other         SGEMV/DGEMV (the report's SYMV-vs-GEMV comparison),
-                SSYR2/DSYR2 (against the in-place copy rate), S/D/Z/WTRMV and
+                SSYR2/DSYR2 (against the copy rate), S/D/Z/WTRMV and
                 one GPU's share of the product sharded over 8 GPUs.
 --detail-json FILE writes every row's full record.
 
@@ -863,12 +863,12 @@ def main():
 
     # measured references beside the specification
     rd_med, rd_best = X.read_bandwidth(4 << 30, reps=10)
-    cp_med, ip_med = X.copy_bandwidth(2 << 30, reps=10)
+    cp_med, _ = X.copy_bandwidth(2 << 30, reps=10)
     out["stream_read_gbps"] = round(rd_med, 1)
-    out["copy_gbps"] = {"copy": round(cp_med, 1), "in_place": round(ip_med, 1)}
+    out["copy_gbps"] = round(cp_med, 1)
     out["pct_measured_read_peak"] = round(100 * out["hbm_gbps_algorithmic"] / rd_med, 2)
     roof["frac_of_measured_read"] = round(achieved / rd_med, 4)
-    log(f"references: read {rd_med:.0f} GB/s, copy {cp_med:.0f}, in place {ip_med:.0f}")
+    log(f"references: read {rd_med:.0f} GB/s, copy {cp_med:.0f}")
 
     cpu_problems = {"C3 s-L-n32768": p}
     detail = {}
@@ -910,7 +910,7 @@ def main():
                 ("ssyr2-L-n32768", lambda: W.make_syr2_problem("s", "L", 32768, seed=32768)),
                 ("dsyr2-U-n32768", lambda: W.make_syr2_problem("d", "U", 32768, seed=32768))]:
             row = measure_syr2_detail(name, make(), args.detail_reps, rd_med)
-            row["pct_of_in_place_copy"] = round(100 * row["hbm_gbps_algorithmic"] / ip_med, 1)
+            row["pct_of_copy"] = round(100 * row["hbm_gbps_algorithmic"] / cp_med, 1)
             detail[name] = row
         for name, make in [
                 ("strmv-L-N-n32768",
@@ -931,7 +931,7 @@ def main():
             r = detail[name]
             other[name] = [round(r["ms_per_call_median"] * 1e3, 1), r["pct_peak_hbm"]]
         for name in ("ssyr2-L-n32768", "dsyr2-U-n32768"):
-            other[name].append(detail[name]["pct_of_in_place_copy"])
+            other[name].append(detail[name]["pct_of_copy"])
         for name in ("ssymv-L-n32768-8shards", "dsymv-U-n32768-8shards"):
             r = detail[name]
             other[name] = [round(r["ms_per_call_median"] * 1e3, 1), r["pct_peak_hbm"],

@@ -730,15 +730,15 @@ def read_bandwidth(nbytes: int = 4 << 30, reps: int = 10, stream=None):
 
 
 def copy_bandwidth(nbytes: int = 2 << 30, reps: int = 10, stream=None):
-    """(copy, in-place update) GB/s, bytes read plus bytes written, of a plain
-    read + write of ``nbytes`` on the device."""
-    cp = ctypes.c_float()
-    ip_ = ctypes.c_float()
-    rc = library().xsymv_copy_bandwidth(nbytes, reps, _stream(stream), ctypes.byref(cp),
-                                        ctypes.byref(ip_))
+    """(median, best) GB/s, bytes read plus bytes written, of a plain copy of
+    ``nbytes`` on the device."""
+    med = ctypes.c_float()
+    best = ctypes.c_float()
+    rc = library().xsymv_copy_bandwidth(nbytes, reps, _stream(stream), ctypes.byref(med),
+                                        ctypes.byref(best))
     if rc != 0:
         raise XsymvError("xsymv_copy_bandwidth", rc)
-    return cp.value, ip_.value
+    return med.value, best.value
 
 
 def release() -> None:

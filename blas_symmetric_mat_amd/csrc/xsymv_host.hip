@@ -844,24 +844,21 @@ static __global__ __launch_bounds__(1024) void read_probe_sweep(const xsymv::u32
 
 // Plain read + write, the reference for the rank-2 update (which reads the
 // stored triangle and writes it back): workgroup b copies its own chunk of
-// `per` 16-byte vectors from src to dst (INPLACE: dst = src, each vector
-// written back where it was read, as the update does), U vectors in flight
-// per lane, non-temporal loads and stores.
-template <int U, bool INPLACE>
-static __global__ __launch_bounds__(256) void copy_probe(xsymv::u32x4* src, xsymv::u32x4* dst,
+// `per` 16-byte vectors from src to dst, U vectors in flight per lane,
+// non-temporal loads and stores.
+template <int U>
+static __global__ __launch_bounds__(256) void copy_probe(const xsymv::u32x4* __restrict__ src,
+                                                         xsymv::u32x4* __restrict__ dst,
                                                          long long per)
 {
-    xsymv::u32x4* __restrict__ p = src + (long long)blockIdx.x * per;
-    xsymv::u32x4* __restrict__ q = (INPLACE ? src : dst) + (long long)blockIdx.x * per;
+    const xsymv::u32x4* __restrict__ p = src + (long long)blockIdx.x * per;
+    xsymv::u32x4* __restrict__ q = dst + (long long)blockIdx.x * per;
     for (long long i = threadIdx.x; i < per; i += 256 * U) {
         xsymv::u32x4 v[U];
 #pragma unroll
         for (int k = 0; k < U; ++k) v[k] = __builtin_nontemporal_load(p + i + k * 256);
 #pragma unroll
-        for (int k = 0; k < U; ++k) {
-            if (INPLACE) v[k].x ^= 1u;  // an update, not a plain store of what was read
-            __builtin_nontemporal_store(v[k], q + i + k * 256);
-        }
+        for (int k = 0; k < U; ++k) __builtin_nontemporal_store(v[k], q + i + k * 256);
     }
 }
 
@@ -953,8 +950,7 @@ done:
     return rc;
 }
 
-int xsymv_copy_bandwidth(size_t bytes, int reps, void* stream, float* copy_gbps,
-                         float* inplace_gbps)
+int xsymv_copy_bandwidth(size_t bytes, int reps, void* stream, float* gbps, float* best_gbps)
 {
     if (bytes < ((size_t)64 << 20) || reps <= 0) return -1;
     const hipStream_t st = (hipStream_t)stream;
@@ -962,7 +958,7 @@ int xsymv_copy_bandwidth(size_t bytes, int reps, void* stream, float* copy_gbps,
     char* buf = nullptr;
     hipEvent_t e0 = nullptr, e1 = nullptr;
     int rc = 0;
-    float best[2] = {0.f, 0.f};  // [copy, in place]
+    float best_med = 0.f, best_any = 0.f;
     auto fail = [&](hipError_t e) { rc = ERR_HIP + (int)e; };
     hipError_t e;
     if ((e = hipMalloc((void**)&buf, (size_t)vecs * 32)) != hipSuccess) return ERR_HIP + (int)e;
@@ -974,10 +970,8 @@ int xsymv_copy_bandwidth(size_t bytes, int reps, void* stream, float* copy_gbps,
         fail(e);
         goto done;
     }
-    // layouts: {2048, 8192} workgroups x {4, 8} vectors in flight per lane,
-    // for the copy and for the in-place update; the best median of each kind
-    for (int layout = 0; layout < 8; ++layout) {
-        const bool inplace = layout >= 4;
+    // layouts: {2048, 8192} workgroups x {4, 8} vectors in flight per lane
+    for (int layout = 0; layout < 4; ++layout) {
         const int blocks = (layout & 2) ? 8192 : 2048;
         const int u = (layout & 1) ? 8 : 4;
         const long long per = vecs / blocks / (256 * u) * (256 * u);
@@ -985,14 +979,10 @@ int xsymv_copy_bandwidth(size_t bytes, int reps, void* stream, float* copy_gbps,
         std::vector<float> t;
         for (int r = 0; r < reps + 1 && rc == 0; ++r) {
             if ((e = hipEventRecord(e0, st)) != hipSuccess) { fail(e); break; }
-            if (inplace && u == 4)
-                copy_probe<4, true><<<blocks, 256, 0, st>>>(src, dst, per);
-            else if (inplace)
-                copy_probe<8, true><<<blocks, 256, 0, st>>>(src, dst, per);
-            else if (u == 4)
-                copy_probe<4, false><<<blocks, 256, 0, st>>>(src, dst, per);
+            if (u == 4)
+                copy_probe<4><<<blocks, 256, 0, st>>>(src, dst, per);
             else
-                copy_probe<8, false><<<blocks, 256, 0, st>>>(src, dst, per);
+                copy_probe<8><<<blocks, 256, 0, st>>>(src, dst, per);
             if ((e = hipGetLastError()) != hipSuccess) { fail(e); break; }
             if ((e = hipEventRecord(e1, st)) != hipSuccess) { fail(e); break; }
             if ((e = hipEventSynchronize(e1)) != hipSuccess) { fail(e); break; }
@@ -1003,11 +993,11 @@ int xsymv_copy_bandwidth(size_t bytes, int reps, void* stream, float* copy_gbps,
         if (rc) goto done;
         std::sort(t.begin(), t.end());
         const double b = 2.0 * (double)per * blocks * 16;  // read + written
-        float& slot = best[inplace ? 1 : 0];
-        slot = std::max(slot, (float)(b / (t[t.size() / 2] * 1e-3) / 1e9));
+        best_med = std::max(best_med, (float)(b / (t[t.size() / 2] * 1e-3) / 1e9));
+        best_any = std::max(best_any, (float)(b / (t[0] * 1e-3) / 1e9));
     }
-    if (copy_gbps) *copy_gbps = best[0];
-    if (inplace_gbps) *inplace_gbps = best[1];
+    if (gbps) *gbps = best_med;
+    if (best_gbps) *best_gbps = best_any;
 done:
     if (e0) (void)hipEventDestroy(e0);
     if (e1) (void)hipEventDestroy(e1);

@@ -314,7 +314,7 @@ int strip_run(const KernelSet<T>& ks, bool upper, int n, T alpha, const T* A, in
     if (timing) XSYMV_HIP(hipEventRecord(tc.e1, stream));
     StripMergeArgs<T> ma{rowpart, colpart, plan->d_seg_base, y, (long long)incy, ky, alpha, beta,
                          n, plan->NS, R, upper ? 1 : 0, beta_zero};
-    symv_strip_merge<T, MERGE_SPLIT><<<blocks_for(n, 64), 64 * MERGE_SPLIT, 0, stream>>>(ma);
+    launch_strip_merge<T, MERGE_SPLIT>(ma, n, stream);
     XSYMV_HIP(hipGetLastError());
     if (timing) {
         XSYMV_HIP(hipEventRecord(tc.e2, stream));
@@ -847,7 +847,7 @@ int shard_run(char uplo, int n, int panel, int nshards, int shard, const T* A, i
     if (timing) XSYMV_HIP(hipEventRecord(tc.e1, stream));
     StripMergeArgs<T> ma{rowpart, colpart, plan->d_seg_base, p, 1, 0, tune_one<T>(),
                          tune_zero<T>(), n, plan->NS, R, upper ? 1 : 0, 1, plan->d_gloc, ncol};
-    symv_strip_merge<T, MERGE_SPLIT, true><<<blocks_for(n, 64), 64 * MERGE_SPLIT, 0, stream>>>(ma);
+    launch_strip_merge<T, MERGE_SPLIT, true>(ma, n, stream);
     XSYMV_HIP(hipGetLastError());
     if (timing) {
         XSYMV_HIP(hipEventRecord(tc.e2, stream));

@@ -372,8 +372,12 @@ __global__ __launch_bounds__(64 * W) void symv_strip(StripArgs<T> a)
 // Ordered merge for the strip decomposition: row r of strip I adds its row
 // partials slot by slot (segments of strip I in order), then the column
 // partials colpart[i][r] of the strips that hold column r (L: i >= I,
-// U: i <= I) in ascending i.  SPLIT waves share 64 rows; wave g takes the
-// terms k with k % SPLIT == g; the subtotals meet in a fixed pairwise tree.
+// U: i <= I) in ascending i.  A workgroup of SPLIT waves takes ROWS
+// consecutive rows (64 or 32); the 64 / ROWS lane groups of a wave and the
+// waves give SPLIT * 64 / ROWS streams, stream v taking the terms k with
+// k % streams == v; the subtotals meet in a fixed pairwise tree.  ROWS = 32
+// runs twice as many workgroups, for orders whose 64-row blocks would leave
+// CUs idle.
 template <class T>
 struct StripMergeArgs {
     const T* rowpart;
@@ -396,14 +400,18 @@ struct StripMergeArgs {
 // SHARD: the shard's partial vector -- column partials only for the rows
 // whose column the shard owns (local index gloc[i], rows of ncol), no alpha or
 // beta: y is the contiguous partial p.
-template <class T, int SPLIT, bool SHARD = false>
+template <class T, int SPLIT, bool SHARD = false, int ROWS = 64>
 __global__ __launch_bounds__(64 * SPLIT) void symv_strip_merge(StripMergeArgs<T> a)
 {
     using E = Elem<T>;
-    __shared__ T part[SPLIT][64];
+    constexpr int GROUPS = 64 / ROWS;      // lane groups per wave
+    constexpr int V = SPLIT * GROUPS;      // streams
+    static_assert(ROWS == 64 || ROWS == 32, "64 or 32 rows per workgroup");
+    __shared__ T part[V][ROWS];
     const int lane = threadIdx.x & 63;
-    const int g = threadIdx.x >> 6;
-    const int i = blockIdx.x * 64 + lane;
+    const int v = (threadIdx.x >> 6) * GROUPS + lane / ROWS;  // this lane's stream
+    const int rl = lane % ROWS;
+    const int i = blockIdx.x * ROWS + rl;
     T acc = E::zero();
     if (i < a.n) {
         const int I = i / a.R;
@@ -417,20 +425,20 @@ __global__ __launch_bounds__(64 * SPLIT) void symv_strip_merge(StripMergeArgs<T>
         const T* __restrict__ rp = a.rowpart + (long long)s_lo * a.R + (i - I * a.R);
         const T* __restrict__ cp = a.colpart + (long long)c_lo * cstride + li;
 #pragma unroll 4
-        for (int k = g; k < ntot; k += SPLIT) {
-            const T v = (k < nrow) ? rp[(long long)k * a.R] : cp[(long long)(k - nrow) * cstride];
-            acc = E::add(acc, v);
+        for (int k = v; k < ntot; k += V) {
+            const T t = (k < nrow) ? rp[(long long)k * a.R] : cp[(long long)(k - nrow) * cstride];
+            acc = E::add(acc, t);
         }
     }
-    part[g][lane] = acc;
+    part[v][rl] = acc;
     __syncthreads();
 #pragma unroll
-    for (int w = SPLIT / 2; w >= 1; w >>= 1) {
-        if (g < w) part[g][lane] = E::add(part[g][lane], part[g + w][lane]);
+    for (int w = V / 2; w >= 1; w >>= 1) {
+        if (v < w) part[v][rl] = E::add(part[v][rl], part[v + w][rl]);
         __syncthreads();
     }
-    if (g == 0 && i < a.n) {
-        const T tot = part[0][lane];
+    if (v == 0 && i < a.n) {
+        const T tot = part[0][rl];
         if constexpr (SHARD) {
             a.y[i] = tot;
         } else {
@@ -440,6 +448,19 @@ __global__ __launch_bounds__(64 * SPLIT) void symv_strip_merge(StripMergeArgs<T>
             *yp = r;
         }
     }
+}
+
+// Rows per merge workgroup for order n: 32 below 16384 (twice the
+// workgroups), else 64.
+constexpr int MERGE_ROWS_SMALL_BELOW = 16384;
+
+template <class T, int SPLIT, bool SHARD = false>
+void launch_strip_merge(const StripMergeArgs<T>& ma, int n, hipStream_t stream)
+{
+    if (n < MERGE_ROWS_SMALL_BELOW)
+        symv_strip_merge<T, SPLIT, SHARD, 32><<<(n + 31) / 32, 64 * SPLIT, 0, stream>>>(ma);
+    else
+        symv_strip_merge<T, SPLIT, SHARD, 64><<<(n + 63) / 64, 64 * SPLIT, 0, stream>>>(ma);
 }
 
 // Rank-ordered combination of the shards' partials: y_i := beta*y_i +
@@ -465,8 +486,18 @@ __global__ __launch_bounds__(256) void symv_combine(CombineArgs<T> a)
     using E = Elem<T>;
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i >= a.n) return;
+    // the partials are loaded 8 at a time (all in flight together) and added
+    // in rank order
     T sum = a.P[i];
-    for (int g = 1; g < a.nshards; ++g) sum = E::add(sum, a.P[(long long)g * a.ldp + i]);
+    for (int g0 = 1; g0 < a.nshards; g0 += 8) {
+        T v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            v[k] = g0 + k < a.nshards ? a.P[(long long)(g0 + k) * a.ldp + i] : E::zero();
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            if (g0 + k < a.nshards) sum = E::add(sum, v[k]);
+    }
     T* yp = a.y + a.ky + (long long)i * a.incy;
     T r = E::mul(a.alpha, sum);
     if (!a.beta_zero) r = E::add(E::mul(a.beta, *yp), r);

@@ -490,16 +490,13 @@ int xsymv_read_bandwidth(size_t bytes, int reps, void *stream, float *gbps,
  * writes it back (the report sets its results beside a measured copy rate as
  * well as the specification, §4).  Allocates 2 * `bytes` (bytes >= 64 MiB),
  * fills them, then for each of four layouts (2048 or 8192 workgroups of 256
- * lanes, each moving its own contiguous chunk with 4 or 8 non-temporal
- * 16-byte loads and stores in flight per lane) times `reps` launches after
- * one warm-up: a copy from one buffer to the other, and an update in place
- * (each vector written back where it was read).  Rates count the bytes read
- * plus the bytes written.  Writes the best layout's median rate of the copy
- * and of the in-place update in GB/s (either may be NULL); frees the buffer
- * and synchronises the stream.  Returns 0, -1 for bad arguments or
- * 1000 + hipError_t. */
-int xsymv_copy_bandwidth(size_t bytes, int reps, void *stream, float *copy_gbps,
-                         float *inplace_gbps);
+ * lanes, each copying its own contiguous chunk from one buffer to the other
+ * with 4 or 8 non-temporal 16-byte loads and stores in flight per lane) times
+ * `reps` launches after one warm-up.  Rates count the bytes read plus the
+ * bytes written.  Writes the best layout's median rate and the best single
+ * launch in GB/s (either may be NULL); frees the buffer and synchronises the
+ * stream.  Returns 0, -1 for bad arguments or 1000 + hipError_t. */
+int xsymv_copy_bandwidth(size_t bytes, int reps, void *stream, float *gbps, float *best_gbps);
 
 /* Library version string. */
 const char *xsymv_version(void);
