@@ -88,11 +88,12 @@ template <> const std::vector<TrmvKernelSet<double>>& trmv_kernel_sets<double>()
 // at n = 32768 on MI355X
 template <> TrmvDefaults trmv_defaults<double>() { return TrmvDefaults{{{4, 3}, {3, 3}}}; }
 
-// One shard's product: the row-strip shape that the built-in rules pick for
-// the largest orders (R 4096, G 4, split by stored rows)
+// One shard's product (537 MB at n = 32768 with 8 shards): R 2048, G 8,
+// split by strip height alone -- the fastest of five shapes measured on the
+// per-GPU share at that order
 template <> const ShardKernelSet<double>& shard_kernels<double>()
 {
-    static const ShardKernelSet<double> k = make_shard<double, 16, 2, 4, true, 1>();
+    static const ShardKernelSet<double> k = make_shard<double, 16, 1, 8, true, 2>();
     return k;
 }
 }  // namespace xsymv

@@ -87,11 +87,12 @@ template <> const std::vector<TrmvKernelSet<float>>& trmv_kernel_sets<float>()
 // at n = 32768 on MI355X
 template <> TrmvDefaults trmv_defaults<float>() { return TrmvDefaults{{{0, 3}, {0, 2}}}; }
 
-// One shard's product: the row-strip shape that the built-in rules pick for
-// the largest orders (R 4096, G 16, split by stored rows)
+// One shard's product (268 MB at n = 32768 with 8 shards): R 4096, G 16,
+// split by strip height alone -- the fastest of five shapes measured on the
+// per-GPU share at that order
 template <> const ShardKernelSet<float>& shard_kernels<float>()
 {
-    static const ShardKernelSet<float> k = make_shard<float, 16, 1, 16, true, 1>();
+    static const ShardKernelSet<float> k = make_shard<float, 16, 1, 16, true, 2>();
     return k;
 }
 }  // namespace xsymv
