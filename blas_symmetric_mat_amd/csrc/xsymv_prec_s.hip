@@ -55,15 +55,18 @@ template <> const std::vector<GemvKernelSet<float>>& gemv_kernel_sets<float>()
     return v;
 }
 
-// xSYR2 / xHER2 configurations (index 0 is the default; xsyr2_select_config
-// chooses another)
+// xSYR2 configurations (index 0 is the default -- the fastest, or level with
+// the fastest, of ten shapes for both triangles at n = 32768 on MI355X;
+// xsyr2_select_config chooses another)
 template <> const std::vector<Syr2KernelSet<float>>& syr2_kernel_sets<float>()
 {
     static const std::vector<Syr2KernelSet<float>> v = {
+        make_syr2<float, 16, 1, 16, true, 1>(),            // R 4096, 16 KB runs, G 16
         make_syr2<float, 16, 1, 8, true, 1>(),             // R 4096, 16 KB runs, G 8
         make_syr2<float, 16, 1, 4, true, 1>(),             // R 4096, 16 KB runs, G 4
         make_syr2<float, 8, 2, 4, true, 1>(),              // R 4096, 16 KB runs, G 4
         make_syr2<float, 4, 2, 4, true, 0>(),              // R 2048, 8 KB runs, G 4
+        make_syr2<float, 16, 1, 8, true, 2>(),             // R 4096, 16 KB runs, G 8, split by height alone
     };
     return v;
 }

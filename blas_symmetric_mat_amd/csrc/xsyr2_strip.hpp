@@ -19,8 +19,12 @@
 // (L: row n; U: the diagonal, inclusive), so the ragged last strip and the
 // whole upper band are 16-byte operations and nothing outside the triangle
 // is read or written.  The lower band (rows around the diagonal) needs a
-// lower bound: those groups go element by element, with the offset of an
-// unstored row moved past the byte count (no access).
+// lower bound as well.  For fp32 there the one lane per column whose vector
+// holds both unstored rows and the diagonal reads and writes the 16 bytes
+// that start at the diagonal instead (rows of the next lane's vector among
+// them get, from both lanes, the same bytes), and vectors with no stored row
+// are moved past the byte count (no access); the other types go element by
+// element, with the offset of an unstored row moved past the byte count.
 #pragma once
 
 #include "xsymv_strip.hpp"
@@ -67,6 +71,10 @@ __global__ __launch_bounds__(64 * W) void syr2_strip(Syr2Args<T> a)
     constexpr int R = W * RW;
     constexpr int ES = (int)sizeof(T);
     constexpr int FAR = 0x7fffff00;  // an offset past every byte count
+    // L band in whole vectors: measured, it pays for the four-element vectors
+    // of fp32 (SSYR2 L n = 32768 942 -> 856 us) and costs the two-element
+    // ones about 1 % (DSYR2 L), so those keep the element-wise band
+    constexpr bool VBAND = !UPPER && V >= 4;
 
     const StripBlock bd = a.blocks[blockIdx.x];
     const int n = a.n;
@@ -89,8 +97,12 @@ __global__ __launch_bounds__(64 * W) void syr2_strip(Syr2Args<T> a)
         const int rw = rs0 + wave * RW;            // this wave's first row
         if (rw < rs1) {                            // wave-uniform
             T xr[SW][V], yr[SW][V];
+            // L: x and y at the next lane's rows (the rows a vector moved to
+            // the diagonal reaches; past n they are never stored)
+            constexpr int NV = VBAND ? V : 1;
+            T xn[SW][NV], yn[SW][NV];
 #pragma unroll
-            for (int s = 0; s < SW; ++s)
+            for (int s = 0; s < SW; ++s) {
 #pragma unroll
                 for (int k = 0; k < V; ++k) {
                     const int r = rw + s * H + lane * V + k;
@@ -98,6 +110,16 @@ __global__ __launch_bounds__(64 * W) void syr2_strip(Syr2Args<T> a)
                     xr[s][k] = x[rc];
                     yr[s][k] = y[rc];
                 }
+                if constexpr (VBAND) {
+#pragma unroll
+                    for (int k = 0; k < V; ++k) {
+                        const int r = rw + s * H + lane * V + V + k;
+                        const int rc = r < n ? r : n - 1;
+                        xn[s][k] = x[rc];
+                        yn[s][k] = y[rc];
+                    }
+                }
+            }
 #pragma unroll 1
             for (int g0 = u; g0 < useg; g0 += G) {
                 const int jg = g0 + coff;
@@ -140,9 +162,58 @@ __global__ __launch_bounds__(64 * W) void syr2_strip(Syr2Args<T> a)
                             }
                             bstore16<T, NT>(rsr[g], (s * H + lane * V) * ES, av[g][s]);
                         }
+                } else if constexpr (VBAND) {
+                    // lower band, whole vectors: a vector with no stored row
+                    // goes past the byte count; the vector that holds the
+                    // diagonal and rows above it is replaced by the V rows
+                    // starting at the diagonal (4- or 8-byte aligned), whose
+                    // rows past the lane's own are the next lane's, updated
+                    // to the same bytes there
+                    __amdgpu_buffer_rsrc_t rsr[G];
+                    T av[G][SW][V];
+                    int off[G][SW];
+                    int sh[G][SW];  // rows the vector starts below the lane's first row
+#pragma unroll
+                    for (int g = 0; g < G; ++g) {
+                        const int col = g < ng ? jg + g : jg;
+                        const int rows = g < ng ? min(RW, max(0, n - rw)) : 0;
+                        rsr[g] = make_rsrc(A + (long long)col * lda + rw, rows * ES);
+#pragma unroll
+                        for (int s = 0; s < SW; ++s) {
+                            const int rf = rw + s * H + lane * V;  // the lane's first row
+                            const bool whole = rf >= col;
+                            const bool moved = !whole && rf + V > col;
+                            sh[g][s] = moved ? col - rf : 0;
+                            off[g][s] = whole ? (rf - rw) * ES : moved ? (col - rw) * ES : FAR;
+                            E::template bload16<NT>(rsr[g], off[g][s], av[g][s]);
+                        }
+                    }
+#pragma unroll
+                    for (int g = 0; g < G; ++g)
+#pragma unroll
+                        for (int s = 0; s < SW; ++s) {
+                            const int rf = rw + s * H + lane * V;
+#pragma unroll
+                            for (int k = 0; k < V; ++k) {
+                                // element k is row rf + sh + k
+                                T xi = xr[s][k], yi = yr[s][k];
+#pragma unroll
+                                for (int d = 1; d < V; ++d) {
+                                    const int q = k + d;
+                                    const T xs = q < V ? xr[s][q % V] : xn[s][q % V];
+                                    const T ys = q < V ? yr[s][q % V] : yn[s][q % V];
+                                    xi = E::sel(sh[g][s] == d, xs, xi);
+                                    yi = E::sel(sh[g][s] == d, ys, yi);
+                                }
+                                const int col = jg + g;
+                                av[g][s][k] = syr2_elem<T, HERM>(av[g][s][k], xi, yi, t1[g], t2[g],
+                                                                 rf + sh[g][s] + k == col);
+                            }
+                            bstore16<T, NT>(rsr[g], off[g][s], av[g][s]);
+                        }
                 } else {
-                    // lower band: element by element, unstored rows (above the
-                    // diagonal or past n) moved out of range
+                    // lower band, one element per vector: unstored rows
+                    // (above the diagonal or past n) moved out of range
 #pragma unroll
                     for (int g = 0; g < G; ++g) {
                         const int col = jg + g;

@@ -195,8 +195,9 @@ int xsyr2_w(char uplo, int n, xdd alpha, const xdd *x, int incx, const xdd *y, i
 
 /* Rank-2 update configurations (entry 0 the default): waves per workgroup,
  * stripes per wave, columns per group, non-temporal access (0/1), work split
- * (0: strip height per column, 1: stored rows plus strip height) and rows per
- * strip.  Same conventions as the xGEMV configuration calls. */
+ * (the cost models of xsymv_strip_plan: 0 strip height, doubled in the
+ * diagonal triangle; 1 stored rows plus strip height; 2 strip height alone)
+ * and rows per strip.  Same conventions as the xGEMV configuration calls. */
 int xsyr2_num_configs(int prec);
 int xsyr2_config_info(int prec, int idx, int *waves, int *stripes_per_wave,
                       int *cols_per_group, int *nontemporal, int *split,
