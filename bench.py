@@ -9,8 +9,9 @@ as 2n^2 per call, over K timed steps between two device synchronisations.
 
 Printed as one JSON line (kept short), with:
   roofline      the streaming kernel's algorithmic bytes (stored triangle + x)
-                over its average duration, timed with HIP events recorded by
-                the library on the launch stream, against the 8 TB/s HBM peak;
+                over its average duration, timed with HIP events that the
+                library binds to the launch (hipExtLaunchKernel: the kernel's
+                own start and end), against the 8 TB/s HBM peak;
                 `traffic` and `traffic_ratio` come from the committed
                 rocprofv3 counter record when it was taken on the current
                 kernel source and configuration, else null;
@@ -27,10 +28,14 @@ Printed as one JSON line (kept short), with:
                 beta = 0; C3 the [SD]SYMV sweep, s/d x L/U x n in {2048, 4096,
                 8192, 16384, 24576, 32768, 10007, 32767}; C4 CHEMV/ZHEMV L
                 n = 16384; C5 WSYMV L n = 8192; CHEMV/ZHEMV/WSYMV L at
-                n = 32768 (inputs drawn on the device).  Each is timed per
-                call (library events around its two kernels, median of 20),
-                with the caches flushed before every call (1 GiB written and
-                read back) when the matrix is below 1 GiB;
+                n = 32768 (inputs drawn on the device).  "us per call" is
+                what one call adds to a stream, with nothing recorded inside
+                the call: below 1 GiB of matrix, the median of (cache flush +
+                call) minus the median of (flush alone), 20 of each,
+                interleaved, each between a pair of events (the flush: 1 GiB
+                written and read back); from 1 GiB, 20 calls back to back
+                over 20.  The kernel's own time comes from the library's
+                events bound to its launch, on the same caches;
   rule_check    at the sweep's odd orders (10007, 32767) the built-in
                 configuration's time over the on-device autotuner's best;
   other         SGEMV/DGEMV (the report's SYMV-vs-GEMV comparison),
@@ -149,11 +154,9 @@ def measure_gemv_detail(name, p, reps, read_peak=None):
     d = GemvDev(p)
     for _ in range(2):
         d.call()
-    rec = time_kernels(d, reps)
-    main = sorted(r[0] for r in rec)
-    tot = sorted(r[0] + r[1] for r in rec)
+    main = sorted(r[0] for r in time_kernels(d, reps))
     t_main = main[len(main) // 2] * 1e-3
-    t_call = tot[len(tot) // 2] * 1e-3
+    t_call = call_ms(d, reps)[0] * 1e-3
     bz = beta_is_zero(p)
     call_b = R.gemv_call_bytes(p.prec, p.m, p.n, p.trans, bz)
     ci = X.gemv_config_info(p.prec, X.gemv_current_config(p.prec))
@@ -162,7 +165,6 @@ def measure_gemv_detail(name, p, reps, read_peak=None):
                       f"SW={ci['stripes_per_wave']}, G={ci['cols_per_group']}, "
                       f"{'nt' if ci['nontemporal'] else 'cached'}>"),
            "ms_per_call_median": round(t_call * 1e3, 4),
-           "ms_per_call_min": round(tot[0], 4),
            "gflops_2mn": round(2.0 * p.m * p.n / t_call / 1e9, 2),
            "hbm_gbps_algorithmic": round(call_b / t_call / 1e9, 1),
            "pct_peak_hbm": round(100 * call_b / t_call / 1e9 / R.HBM_PEAK_GBPS, 1),
@@ -196,9 +198,7 @@ def measure_syr2_detail(name, p, reps, read_peak=None):
     d = _D()
     for _ in range(2):
         d.call()
-    rec = time_kernels(d, reps)
-    tot = sorted(r[0] + r[1] for r in rec)
-    t_call = tot[len(tot) // 2] * 1e-3
+    t_call = call_ms(d, reps)[0] * 1e-3
     b = R.syr2_call_bytes(p.prec, p.n)
     ci = X.syr2_config_info(p.prec, X.syr2_current_config(p.prec))
     out = {"prec": p.prec, "uplo": p.uplo, "n": p.n, "lda": p.lda,
@@ -206,7 +206,6 @@ def measure_syr2_detail(name, p, reps, read_peak=None):
                       f"W={ci['waves']}, SW={ci['stripes_per_wave']}, G={ci['cols_per_group']}, "
                       f"{'nt' if ci['nontemporal'] else 'cached'}>"),
            "ms_per_call_median": round(t_call * 1e3, 4),
-           "ms_per_call_min": round(tot[0], 4),
            "hbm_gbps_algorithmic": round(b / t_call / 1e9, 1),
            "pct_peak_hbm": round(100 * b / t_call / 1e9 / R.HBM_PEAK_GBPS, 1),
            "bytes": "triangle read + written, x and y", "calls": reps}
@@ -236,11 +235,9 @@ def measure_trmv_detail(name, p, reps, read_peak=None):
     d = _D()
     for _ in range(2):
         d.call()
-    rec = time_kernels(d, reps)
-    main = sorted(r[0] for r in rec)
-    tot = sorted(r[0] + r[1] for r in rec)
+    main = sorted(r[0] for r in time_kernels(d, reps))
     t_main = main[len(main) // 2] * 1e-3
-    t_call = tot[len(tot) // 2] * 1e-3
+    t_call = call_ms(d, reps)[0] * 1e-3
     unit = p.diag in ("U", "u")
     b = R.trmv_call_bytes(p.prec, p.n, unit)
     idx = X.trmv_current_config(p.prec, p.uplo, p.trans)
@@ -252,7 +249,6 @@ def measure_trmv_detail(name, p, reps, read_peak=None):
                       f"G={ci['cols_per_group']}, {'nt' if ci['nontemporal'] else 'cached'}> "
                       f"(split: {'stored+height' if ci['split'] else 'height'})"),
            "ms_per_call_median": round(t_call * 1e3, 4),
-           "ms_per_call_min": round(tot[0], 4),
            "hbm_gbps_algorithmic": round(b / t_call / 1e9, 1),
            "pct_peak_hbm": round(100 * b / t_call / 1e9 / R.HBM_PEAK_GBPS, 1),
            "streaming_kernel_gbps": round((b - R.ELEM_BYTES[p.prec] * p.n) / t_main / 1e9, 1),
@@ -264,12 +260,14 @@ def measure_trmv_detail(name, p, reps, read_peak=None):
     return out
 
 
-def measure_shard_detail(name, p, panel, nshards, reps, read_peak=None):
+def measure_shard_detail(name, p, panel, nshards, reps, read_peak=None, flush=None):
     """One GPU's share of the sharded product at its real shape: every
     shard's call (kernel + ordered merge) on this GPU in turn, its bytes the
     shard's stored elements, x read and the partial written; then the
-    rank-ordered combination of the partials.  The exchange between GPUs is
-    not measured (one GPU)."""
+    rank-ordered combination of the partials.  Each shard's call is timed
+    with call_ms, the caches flushed before every call (a shard's share is
+    below 1 GiB); the combination back to back.  The exchange between GPUs
+    is not measured (one GPU)."""
     from blas_symmetric_mat_amd import roofline as R
     import numpy as np
     import torch
@@ -297,12 +295,10 @@ def measure_shard_detail(name, p, panel, nshards, reps, read_peak=None):
         d = _D()
         for _ in range(2):
             d.call()
-        rec = time_kernels(d, reps)
-        main = sorted(r[0] for r in rec)
-        tot = sorted(r[0] + r[1] for r in rec)
+        main = sorted(r[0] for r in time_kernels(d, reps, flush))
         stored = sum((c + 1) if p.uplo in ("U", "u") else (n - c) for c in cols)
         shards.append({"shard": g, "columns": len(cols), "stored_elements": stored,
-                       "ms_per_call_median": round(tot[len(tot) // 2], 4),
+                       "ms_per_call_median": round(call_ms(d, reps, flush)[0], 4),
                        "kernel_ms_median": round(main[len(main) // 2], 4),
                        "bytes": es * (stored + 2 * n)})
         del Aloc
@@ -314,17 +310,13 @@ def measure_shard_detail(name, p, panel, nshards, reps, read_peak=None):
     cb = getattr(X, {"s": "xsymv_combine_s", "d": "xsymv_combine_d", "c": "xhemv_combine_c",
                      "z": "xhemv_combine_z", "w": "xsymv_combine_w"}[p.prec])
     one = (1.0, 0.0) if p.prec == "w" else 1.0
+    class _C:
+        def call(self):
+            cb(n, nshards, one, P, n, one, y, 1)
+
     for _ in range(2):
-        cb(n, nshards, one, P, n, one, y, 1)
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(reps)]
-    for e0, e1 in ev:
-        e0.record()
-        cb(n, nshards, one, P, n, one, y, 1)
-        e1.record()
-    torch.cuda.synchronize()
-    cms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)[reps // 2]
+        _C().call()
+    cms = call_ms(_C(), reps)[0]  # back to back: the partials (n x shards) stay cached
     out = {"prec": p.prec, "uplo": p.uplo, "n": n, "panel": panel, "shards": nshards,
            "kernel": (f"symv_strip<{CTYPE[p.prec]}, {'upper' if p.uplo == 'U' else 'lower'}, "
                       f"..., shard> + ordered merge"),
@@ -350,13 +342,15 @@ def beta_is_zero(p):
     return (b[0] == 0 and b[1] == 0) if isinstance(b, tuple) else complex(b) == 0
 
 
-def time_kernels(d: Dev, reps: int, flush=None):
-    """Per-call (main kernel ms, merge kernel ms) from the library's events."""
+def time_kernels(d: Dev, reps: int, flush=None, mode: int = 1):
+    """Per-call (main kernel ms, merge ms) from the library's events bound to
+    the launches (mode 1), or (call span ms, 0) with no event between the
+    call's kernels (mode 2)."""
     import torch
     import blas_symmetric_mat_amd as X
     torch.cuda.synchronize()
     X.timing_read()  # drop stale records
-    X.timing_enable(True)
+    X.timing_enable(mode)
     try:
         for _ in range(reps):
             if flush is not None:
@@ -367,6 +361,54 @@ def time_kernels(d: Dev, reps: int, flush=None):
     finally:
         X.timing_enable(False)
     return rec
+
+
+def time_split_and_call(d, reps, flush=None):
+    """(sorted main-kernel ms, sorted merge ms, sorted call ms): mode-1 calls
+    for the kernels, then as many mode-2 calls for the whole call."""
+    rec = time_kernels(d, reps, flush)
+    whole = time_kernels(d, reps, flush, mode=2)
+    return (sorted(r[0] for r in rec), sorted(r[1] for r in rec), sorted(r[0] for r in whole))
+
+
+def call_ms(d, reps, flush=None):
+    """(ms one call adds to a stream, ms of the flush alone or None), with
+    nothing recorded inside the call: events placed in a call put a gap of a
+    few microseconds between its kernels.  With a flush: the median of
+    (flush + call) minus the median of (flush alone), each between a pair of
+    events, the two interleaved, so each call starts on flushed caches right
+    after other work.  Without: `reps` calls back to back between one pair of
+    events, over `reps`."""
+    import statistics
+    import torch
+    torch.cuda.synchronize()
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+    if flush is None:
+        e0, e1 = ev(), ev()
+        e0.record()
+        for _ in range(reps):
+            d.call()
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1) / reps, None
+    pairs = []
+    for _ in range(reps):
+        row = []
+        for with_call in (False, True):
+            e0, e1 = ev(), ev()
+            e0.record()
+            flush()
+            if with_call:
+                d.call()
+            e1.record()
+            row.append((e0, e1))
+        pairs.append(row)
+    torch.cuda.synchronize()
+    f_only = statistics.median(a.elapsed_time(b) for (a, b), _ in pairs)
+    f_call = statistics.median(a.elapsed_time(b) for _, (a, b) in pairs)
+    return f_call - f_only, f_only
 
 
 def host_cores() -> int:
@@ -454,9 +496,10 @@ def compact(row: dict) -> list:
 
 
 def measure_detail(name, p, reps, flush, read_peak=None, quiet=False):
-    """One symmetric workload timed per call: the library's events around its
-    streaming kernel and its merge, median of `reps` calls, the caches
-    flushed before each call when the matrix is below 1 GiB."""
+    """One symmetric workload: the call's cost on the stream (call_ms; the
+    caches flushed before each call when the matrix is below 1 GiB, else
+    calls back to back), and its streaming kernel and merge from the
+    library's events bound to them (median of `reps` calls, same caches)."""
     from blas_symmetric_mat_amd import roofline as R
     import torch
     import blas_symmetric_mat_amd as X
@@ -469,9 +512,10 @@ def measure_detail(name, p, reps, flush, read_peak=None, quiet=False):
     small = p.A.nbytes < (1 << 30)
     rec = time_kernels(d, reps, flush if small else None)
     main = sorted(r[0] for r in rec)
-    tot = sorted(r[0] + r[1] for r in rec)
+    merge = sorted(r[1] for r in rec)
+    c_ms, f_ms = call_ms(d, reps, flush if small else None)
     t_main = main[len(main) // 2] * 1e-3
-    t_call = tot[len(tot) // 2] * 1e-3
+    t_call = c_ms * 1e-3
     bz = beta_is_zero(p)
     call_b = R.call_bytes(p.prec, p.n, bz)
     kb = R.tile_kernel_bytes(p.prec, p.n)
@@ -479,9 +523,9 @@ def measure_detail(name, p, reps, flush, read_peak=None, quiet=False):
     out = {"prec": p.prec, "uplo": p.uplo, "n": p.n, "lda": p.lda,
            "kernel": label,
            "ms_per_call_median": round(t_call * 1e3, 4),
-           "ms_per_call_min": round(tot[0], 4),
+           "flush_ms_median": round(f_ms, 4) if f_ms is not None else None,
            "kernel_ms_median": round(t_main * 1e3, 4),
-           "merge_ms_median": round(sorted(r[1] for r in rec)[len(rec) // 2], 4),
+           "merge_ms_median": round(merge[len(merge) // 2], 4),
            "gflops_2n2": round(R.gflops_2n2(p.n, t_call), 2),
            "hbm_gbps_algorithmic": round(call_b / t_call / 1e9, 1),
            "pct_peak_hbm": round(100 * call_b / t_call / 1e9 / R.HBM_PEAK_GBPS, 1),
@@ -593,15 +637,16 @@ def summarize_trace(trace_csv: str, stats_csv: str, command: str,
                 f"{statistics.mean(head):.1f} us, median {statistics.median(head):.1f} us, "
                 f"min {min(head):.1f} us, max {max(head):.1f} us.  bench.py's "
                 "`roofline.launch_ms_mean` is the mean of the last `steps` of these, "
-                "timed with HIP events on the launch stream; in the trace those "
+                "timed with HIP events bound to the launches (hipExtLaunchKernel) on the "
+                "launch stream; in the trace those "
                 f"{len(timed)} launches average {statistics.mean(timed):.1f} us."]
         if bench_json:
             line = open(bench_json).read().strip().splitlines()[-1]
             roof = json.loads(line)["roofline"]
             ev = roof["launch_ms_mean"] * 1e3
             out += ["", f"The bench line of this profiled run: `launch_ms_mean` {ev:.1f} us "
-                        f"({100 * (ev / statistics.mean(timed) - 1):+.1f} % against the trace: "
-                        "the events also hold the gap between launches), `achieved` "
+                        f"({100 * (ev / statistics.mean(timed) - 1):+.1f} % against the "
+                        "trace), `achieved` "
                         f"{roof['achieved']} GB/s, `frac` {roof['frac']}."]
     return "\n".join(out) + "\n"
 
@@ -688,6 +733,131 @@ def summarize_pmc(fetch_csv: str, write_csv: str, command: str, calls: int = PMC
     return out
 
 
+def summarize_calls(trace_csv: str, name: str, command: str, events_json: str | None = None) -> str:
+    """Markdown breakdown of a `--profile-workload NAME --calls N --flush
+    [--read-probe]` run under rocprofv3 --kernel-trace.  That run makes 2
+    warm-up calls, N flushed calls timed with the library's events in mode 1
+    (bound to each kernel), N in mode 2 (bound to the call's first start and
+    last end) and N with no library events (bench.py's per-call protocol:
+    flush + call against flush alone); per group, the medians of the
+    streaming kernel, the gap to its merge, the merge and the span from the
+    kernel's start to the merge's end, against the algorithmic bytes; then
+    the plain streaming read of the matrix's size (xsymv_read_bandwidth,
+    every layout) and, when the run wrote it, what the timings measured."""
+    import csv
+    import re
+    import statistics
+    from blas_symmetric_mat_amd import roofline as R
+    rows = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Start_Timestamp"]))
+    lib = [r for r in rows if "xsymv::" in r["Kernel_Name"]]
+    first = next(r["Kernel_Name"] for r in lib if "merge" not in r["Kernel_Name"])
+    calls = []
+    for i, r in enumerate(lib):
+        if r["Kernel_Name"] == first and i + 1 < len(lib) and "merge" in lib[i + 1]["Kernel_Name"]:
+            m = lib[i + 1]
+            s0, e0 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+            s1, e1 = int(m["Start_Timestamp"]), int(m["End_Timestamp"])
+            calls.append(((e0 - s0) / 1e3, (s1 - e0) / 1e3, (e1 - s1) / 1e3, (e1 - s0) / 1e3,
+                          m["Kernel_Name"]))
+    if not calls:
+        raise ValueError(f"no streaming launch followed by a merge for {first}")
+    mc = re.search(r"--calls[ =](\d+)", command)
+    nc = int(mc.group(1)) if mc else (len(calls) - 2) // 3
+    groups = [("warm-up, no timing, no flush", calls[:2]),
+              ("flushed, events bound to each kernel (mode 1)", calls[2:2 + nc]),
+              ("flushed, events bound to the call (mode 2)", calls[2 + nc:2 + 2 * nc]),
+              ("flushed, no library events (per-call protocol)", calls[2 + 2 * nc:2 + 3 * nc])]
+    groups = [(g, c) for g, c in groups if c]
+    parts = name.split("-")
+    prec, n = parts[0], int(parts[2][1:])
+    kb = R.tile_kernel_bytes(prec, n)
+    cb = R.call_bytes(prec, n, "beta0" in parts)
+
+    def med(cs, k):
+        return statistics.median(c[k] for c in cs)
+    out = [f"# Per-call breakdown, {name}", "", "Command (run from the repository root):", "",
+           "```", command, "```", "",
+           f"Streaming kernel `{first}`, merge `{calls[0][4]}`.  Medians from the kernel trace, "
+           "us; the flush writes 1 GiB and reads it back.", "",
+           "| calls | n | streaming kernel | gap to the merge | merge | span |",
+           "|---|---|---|---|---|---|"]
+    for g, cs in groups:
+        out.append(f"| {g} | {len(cs)} | {med(cs, 0):.1f} | {med(cs, 1):.1f} | {med(cs, 2):.1f} | "
+                   f"{med(cs, 3):.1f} |")
+    last = groups[-1][1]
+    out += ["", f"Algorithmic bytes: kernel {kb:,} (stored triangle + x), call {cb:,}.  In the "
+                f"last group the kernel moves {kb / med(last, 0) / 1e3:.0f} GB/s "
+                f"({100 * kb / med(last, 0) / 1e3 / R.HBM_PEAK_GBPS:.1f} % of 8 TB/s) and the "
+                f"call span {cb / med(last, 3) / 1e3:.0f} GB/s "
+                f"({100 * cb / med(last, 3) / 1e3 / R.HBM_PEAK_GBPS:.1f} %)."]
+    probes = {}
+    for r in rows:
+        k = r["Kernel_Name"]
+        if k.startswith("void read_probe"):
+            key = (k.split("(")[0][5:], int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"]),
+                   int(r["Workgroup_Size_X"]))
+            probes.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    if probes:
+        pb = max(kb, 64 << 20)  # the probe reads at least 64 MiB
+        where = ("larger than the 256 MB last-level cache" if pb > (256 << 20) else
+                 "it fits in the 256 MB last-level cache, so these reads are served from there")
+        out += ["", f"Plain streaming read of {pb:,} B (the matrix's bytes, at least 64 MiB), every "
+                    "layout of xsymv_read_bandwidth, same process, no flush between launches "
+                    f"({where}):", "",
+                "| kernel | workgroups | threads/wg | launches | median us |", "|---|---|---|---|---|"]
+        best = None
+        for (k, g, wg), d in probes.items():
+            m = statistics.median(d)
+            best = m if best is None or m < best else best
+            out.append(f"| `{k}` | {g} | {wg} | {len(d)} | {m:.1f} |")
+        if pb == kb:
+            out += ["", f"Fastest layout: {best:.1f} us; the streaming kernel (last group) takes "
+                        f"{med(last, 0) / best:.3f} x that."]
+        else:
+            out += ["", f"Fastest layout: {best:.1f} us (more bytes than the call reads: no ratio)."]
+    if events_json and os.path.exists(events_json):
+        ev = json.load(open(events_json))
+        out += ["", "What the timings measured in the same run: mode-1 events, streaming "
+                    f"kernel {ev['kernel_us_median']:.1f} us; mode-2 events, whole call "
+                    f"{ev['call_us_median']:.1f} us"]
+        if "call_us_differential" in ev:
+            out[-1] += (f"; flush + call minus flush alone (medians of {ev['calls']}, flush "
+                        f"{ev['flush_us_median']:.1f} us), {ev['call_us_differential']:.1f} us")
+        out[-1] += "."
+    return "\n".join(out) + "\n"
+
+
+def traffic_markdown(rec: dict) -> str:
+    """Markdown table of a counter record (profiles/traffic_counters.json)."""
+    any_rec = next(iter(rec.values()))
+    out = ["# HBM traffic of the streaming kernel, per workload", "",
+           "Commands (repository root; one counter per run, then the summary):", "", "```",
+           any_rec["command"].replace("<COUNTER>", "FETCH_SIZE"),
+           any_rec["command"].replace("<COUNTER>", "WRITE_SIZE"),
+           "python3 bench.py --summarize-pmc gpurun_out/pmc_FETCH_SIZE/run_counter_collection.csv "
+           "gpurun_out/pmc_WRITE_SIZE/run_counter_collection.csv \"<command>\"",
+           "python3 bench.py --traffic-md > profiles/symv_strip_traffic_by_workload.md", "```", "",
+           f"`--pmc-workloads` runs each workload {any_rec['launches']} times (inputs drawn on "
+           "the device), then one plain elementwise kernel (torch.neg, float32) that reads "
+           "1 GiB and writes 1 GiB.  On this MI355X FETCH_SIZE reads half of the bytes it "
+           f"fetches (scale {any_rec['fetch_scale']}) and WRITE_SIZE all of them (scale "
+           f"{any_rec['write_scale']}); every reading is scaled so.  Algorithmic bytes: the "
+           "stored triangle once plus x.  Kernel source digest when measured: "
+           f"{any_rec['kernel_source_digest']} (bench.py reports `traffic` only while the "
+           "sources still have it and the same configuration is chosen).", "",
+           "| workload | kernel configuration | fetched B | written B | total / algorithmic |",
+           "|---|---|---|---|---|"]
+    for name, r in rec.items():
+        out.append(f"| {name} | `{r['kernel_config']}` | {r['fetch_bytes_per_launch']:,} | "
+                   f"{r['write_bytes_per_launch']:,} | {r['traffic_ratio']:.4f} |")
+    out += ["", "The writes are the row partials (one slice of a strip per segment) and the "
+                "column partials (one per strip and column) that the merge reads back; the "
+                "fetches above the algorithmic bytes are x re-read per segment, the row-strip "
+                "x slices and lines shared by neighbouring columns or cut by the leading "
+                "dimension."]
+    return "\n".join(out) + "\n"
+
+
 def profile_problem(name: str):
     """The problem a profiler run times: <s|d|c|z|w>-<L|U>-n<N>[-lda<L>][-beta0],
     drawn on the device (lda = n and the scalars of
@@ -755,6 +925,8 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"),
                     help="write profiles/traffic_counters.json from two rocprofv3 --pmc "
                          "runs of --pmc-workloads and exit")
+    ap.add_argument("--traffic-md", action="store_true",
+                    help="print profiles/traffic_counters.json as a markdown table and exit")
     ap.add_argument("--pmc-workloads", action="store_true",
                     help="for rocprofv3 --pmc: run every counter workload a few times, "
                          "then the calibration kernel, and exit")
@@ -763,9 +935,24 @@ def main():
                          "printing nothing else (NAME = <s|d|c|z|w>-<L|U>-n<N>[-lda<L>]"
                          "[-beta0]: inputs drawn on the device)")
     ap.add_argument("--calls", type=int, default=5)
+    ap.add_argument("--flush", action="store_true",
+                    help="with --profile-workload: flush the caches before each call and time "
+                         "the calls with the library's events (written to --events-json)")
+    ap.add_argument("--read-probe", action="store_true",
+                    help="with --profile-workload: then a plain streaming read of the "
+                         "matrix's algorithmic bytes (every layout)")
+    ap.add_argument("--events-json", metavar="FILE")
+    ap.add_argument("--summarize-calls", nargs=3, metavar=("TRACE_CSV", "NAME", "COMMAND"),
+                    help="per-call breakdown of a --profile-workload run and exit")
     args = ap.parse_args()
     if args.summarize_trace:
         print(summarize_trace(*args.summarize_trace, bench_json=args.bench_json), end="")
+        return
+    if args.traffic_md:
+        print(traffic_markdown(json.load(open(TRAFFIC_FILE))), end="")
+        return
+    if args.summarize_calls:
+        print(summarize_calls(*args.summarize_calls, events_json=args.events_json), end="")
         return
     if args.summarize_pmc:
         rec = summarize_pmc(*args.summarize_pmc)
@@ -789,10 +976,31 @@ def main():
     from blas_symmetric_mat_amd import workloads as W
 
     if args.profile_workload:
-        d = Dev(profile_problem(args.profile_workload))
-        for _ in range(args.calls):
-            d.call()
+        p = profile_problem(args.profile_workload)
+        d = Dev(p)
+        if args.flush:
+            flush, _buf = make_flush()
+            for _ in range(2):
+                d.call()
+            ks, _, cs = time_split_and_call(d, args.calls, flush)
+            diff, f_only = call_ms(d, args.calls, flush)
+            ev = {"calls": len(cs), "kernel_us_median": ks[len(ks) // 2] * 1e3,
+                  "call_us_median": cs[len(cs) // 2] * 1e3,
+                  "call_us_differential": diff * 1e3, "flush_us_median": f_only * 1e3}
+            log(f"{args.profile_workload}: {args.calls} flushed calls, events {ev}")
+            if args.events_json:
+                with open(args.events_json, "w") as fh:
+                    json.dump(ev, fh)
+            del _buf
+        else:
+            for _ in range(args.calls):
+                d.call()
         torch.cuda.synchronize()
+        if args.read_probe:
+            nb = R.tile_kernel_bytes(p.prec, p.n)
+            del d
+            torch.cuda.empty_cache()
+            log(f"read probe of {nb} B: {X.read_bandwidth(max(nb, 64 << 20), 10)}")
         log(f"{args.profile_workload}: {args.calls} calls done")
         return
     if args.pmc_workloads:
@@ -924,7 +1132,8 @@ def main():
             detail[name] = measure_trmv_detail(name, make(), args.detail_reps, rd_med)
         for name, make in [("ssymv-L-n32768-8shards", lambda: W.symv_sweep("s", "L", 32768)),
                            ("dsymv-U-n32768-8shards", lambda: W.symv_sweep("d", "U", 32768))]:
-            detail[name] = measure_shard_detail(name, make(), 256, 8, args.detail_reps, rd_med)
+            detail[name] = measure_shard_detail(name, make(), 256, 8, args.detail_reps, rd_med,
+                                                flush)
         for name in ("sgemv-N-n32768", "sgemv-T-n32768", "dgemv-N-n32768", "ssyr2-L-n32768",
                      "dsyr2-U-n32768", "strmv-L-N-n32768", "dtrmv-U-T-n32768",
                      "ztrmv-L-C-n16384", "wtrmv-U-N-n16384"):

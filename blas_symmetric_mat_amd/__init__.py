@@ -665,13 +665,18 @@ def clear_config() -> None:
     library().xsymv_clear_config()
 
 
-def timing_enable(on: bool) -> None:
-    library().xsymv_timing_enable(1 if on else 0)
+def timing_enable(mode) -> None:
+    """Timing mode: False/0 off, True/1 main kernel and merge per call, 2 each
+    call whole (no event bound between its kernels)."""
+    m = int(mode)
+    if library().xsymv_timing_enable(m) != 0:
+        raise ValueError(f"timing mode {mode!r}: 0, 1 or 2")
 
 
 def timing_read(max_calls: int = 4096):
-    """List of (main_kernel_ms, merge_kernel_ms) for the calls recorded since
-    timing was enabled or last read."""
+    """List of (main_ms, merge_ms) for the calls recorded since timing was
+    enabled or last read: mode 1 the main kernel and, from its end, the
+    merge; mode 2 (call span, 0)."""
     a = (ctypes.c_float * max_calls)()
     b = (ctypes.c_float * max_calls)()
     k = library().xsymv_timing_read(a, b, max_calls)

@@ -21,7 +21,7 @@ std::mutex g_rules_mu;
 std::vector<Rule> g_rules[5][2];
 
 std::mutex g_time_mu;
-bool g_timing = false;
+int g_timing = 0;  // 0 off, 1 main kernel and merge, 2 whole call
 std::vector<TimedCall> g_timed;
 
 std::mutex g_dev_mu;
@@ -594,7 +594,7 @@ int get_workspace(DeviceState* ds, hipStream_t stream, size_t bytes, void** out)
     return 0;
 }
 
-bool timing_enabled()
+int timing_enabled()
 {
     std::lock_guard<std::mutex> tl(g_time_mu);
     return g_timing;
@@ -1119,7 +1119,8 @@ int xsymv_current_config_lda(int prec, char uplo, int n, int lda)
 int xsymv_timing_enable(int on)
 {
     std::lock_guard<std::mutex> tl(g_time_mu);
-    g_timing = on != 0;
+    if (on < 0 || on > 2) return -1;
+    g_timing = on;
     return 0;
 }
 
@@ -1134,10 +1135,11 @@ int xsymv_timing_read(float* main_ms, float* merge_ms, int max)
     int err = 0;
     for (auto& c : calls) {
         if (!err) {
-            hipError_t e = hipEventSynchronize(c.e2);
+            // the last event of the call; whole-call records have no e1
+            hipError_t e = hipEventSynchronize(c.e2 ? c.e2 : c.e1);
             float a = 0.f, b = 0.f;
-            if (e == hipSuccess) e = hipEventElapsedTime(&a, c.e0, c.e1);
-            if (e == hipSuccess) e = hipEventElapsedTime(&b, c.e1, c.e2);
+            if (e == hipSuccess) e = hipEventElapsedTime(&a, c.e0, c.e1 ? c.e1 : c.e2);
+            if (e == hipSuccess && c.e1 && c.e2) e = hipEventElapsedTime(&b, c.e1, c.e2);
             if (e != hipSuccess) {
                 err = ERR_HIP + (int)e;
             } else if (k < max) {
@@ -1147,8 +1149,8 @@ int xsymv_timing_read(float* main_ms, float* merge_ms, int max)
             }
         }
         (void)hipEventDestroy(c.e0);
-        (void)hipEventDestroy(c.e1);
-        (void)hipEventDestroy(c.e2);
+        if (c.e1) (void)hipEventDestroy(c.e1);
+        if (c.e2) (void)hipEventDestroy(c.e2);
     }
     return err ? err : k;
 }

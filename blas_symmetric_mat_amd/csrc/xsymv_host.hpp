@@ -12,6 +12,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <algorithm>
 #include <map>
@@ -221,11 +222,43 @@ size_t workspace_bytes_for(int P, int n, int nslots, int NB)
 }
 
 // ------------------------------------------------------------------- timing
+// One timed call: e0 takes the main kernel's own start, e1 its end, e2 the
+// end of the merge.  Null events are not taken: all while timing is off; e2
+// for a call of one kernel; e1 in whole-call mode (timing mode 2), where no
+// event is bound between the two kernels.
 struct TimedCall {
-    hipEvent_t e0, e1, e2;
+    hipEvent_t e0 = nullptr, e1 = nullptr, e2 = nullptr;
 };
-bool timing_enabled();
+int timing_enabled();  // the timing mode: 0 off, 1 main kernel and merge, 2 whole call
 void timing_push(const TimedCall& c);
+
+// Creates the events of a timed call in timing mode `mode`; `merge`: the call
+// has a second kernel.
+inline hipError_t timed_call_create(TimedCall& tc, int mode, bool merge = true)
+{
+    hipError_t e = hipEventCreate(&tc.e0);
+    if (e == hipSuccess && (mode == 1 || !merge)) e = hipEventCreate(&tc.e1);
+    if (e == hipSuccess && merge) e = hipEventCreate(&tc.e2);
+    return e;
+}
+
+// Launches kernel `k` (one argument struct) on `stream`.  Given events, they
+// take the kernel's own start and end times from its dispatch (HIP's extended
+// launch), so that timing puts no marker packet between the kernels of a
+// call: a marker between the streaming kernel and its merge delays the merge
+// by several microseconds.
+template <class A>
+hipError_t launch_k(void (*k)(A), dim3 grid, dim3 block, hipStream_t stream, A args,
+                    hipEvent_t start = nullptr, hipEvent_t stop = nullptr)
+{
+    if (start == nullptr && stop == nullptr) {
+        k<<<grid, block, 0, stream>>>(args);
+        return hipGetLastError();
+    }
+    void* p[] = {&args};
+    return hipExtLaunchKernel(reinterpret_cast<const void*>(k), grid, block, p, 0, stream, start,
+                              stop, 0);
+}
 
 // ---------------------------------------------------------------- checking
 int check_args(char uplo, int n, const void* A, int lda, const void* x, int incx,
@@ -300,26 +333,17 @@ int strip_run(const KernelSet<T>& ks, bool upper, int n, T alpha, const T* A, in
         xin = xg;
     }
     TimedCall tc{};
-    const bool timing = timing_enabled();
+    const int timing = timing_enabled();
     if (timing) {
-        XSYMV_HIP(hipEventCreate(&tc.e0));
-        XSYMV_HIP(hipEventCreate(&tc.e1));
-        XSYMV_HIP(hipEventCreate(&tc.e2));
-        XSYMV_HIP(hipEventRecord(tc.e0, stream));
+        XSYMV_HIP(timed_call_create(tc, timing));
     }
     StripArgs<T> sa{A, xin, rowpart, colpart, plan->d_blocks, plan->d_strip_base,
                     (long long)lda, n};
-    kern<<<plan->G, threads, 0, stream>>>(sa);
-    XSYMV_HIP(hipGetLastError());
-    if (timing) XSYMV_HIP(hipEventRecord(tc.e1, stream));
+    XSYMV_HIP(launch_k(kern, plan->G, threads, stream, sa, tc.e0, tc.e1));
     StripMergeArgs<T> ma{rowpart, colpart, plan->d_seg_base, y, (long long)incy, ky, alpha, beta,
                          n, plan->NS, R, upper ? 1 : 0, beta_zero};
-    launch_strip_merge<T, MERGE_SPLIT>(ma, n, stream);
-    XSYMV_HIP(hipGetLastError());
-    if (timing) {
-        XSYMV_HIP(hipEventRecord(tc.e2, stream));
-        timing_push(tc);
-    }
+    XSYMV_HIP((launch_strip_merge<T, MERGE_SPLIT>(ma, n, stream, tc.e2)));
+    if (timing) timing_push(tc);
     return 0;
 }
 
@@ -376,31 +400,21 @@ int symv_run(char uplo, int n, T alpha, const T* A, int lda, const T* x, int inc
     }
 
     TimedCall tc{};
-    const bool timing = timing_enabled();
+    const int timing = timing_enabled();
     if (timing) {
-        XSYMV_HIP(hipEventCreate(&tc.e0));
-        XSYMV_HIP(hipEventCreate(&tc.e1));
-        XSYMV_HIP(hipEventCreate(&tc.e2));
-        XSYMV_HIP(hipEventRecord(tc.e0, stream));
+        XSYMV_HIP(timed_call_create(tc, timing));
     }
 
     SymvArgs<T> sa{A, xin, rowpart, colpart, plan->d_tiles, (long long)lda, n};
     const int threads = 64 * ks.info.W;
-    if (upper)
-        ks.upper<<<plan->ntiles, threads, 0, stream>>>(sa);
-    else
-        ks.lower<<<plan->ntiles, threads, 0, stream>>>(sa);
-    XSYMV_HIP(hipGetLastError());
-    if (timing) XSYMV_HIP(hipEventRecord(tc.e1, stream));
+    XSYMV_HIP(launch_k(upper ? ks.upper : ks.lower, plan->ntiles, threads, stream, sa, tc.e0,
+                       tc.e1));
 
     MergeArgs<T> ma{rowpart, colpart, plan->d_slot_base, y, (long long)incy, ky, alpha, beta,
                     n, plan->P, NB, upper ? 1 : 0, beta_zero};
-    symv_merge<T, MERGE_SPLIT><<<blocks_for(n, 64), 64 * MERGE_SPLIT, 0, stream>>>(ma);
-    XSYMV_HIP(hipGetLastError());
-    if (timing) {
-        XSYMV_HIP(hipEventRecord(tc.e2, stream));
-        timing_push(tc);
-    }
+    XSYMV_HIP(launch_k(&symv_merge<T, MERGE_SPLIT>, blocks_for(n, 64), 64 * MERGE_SPLIT, stream,
+                       ma, nullptr, tc.e2));
+    if (timing) timing_push(tc);
     return 0;
 }
 
@@ -495,25 +509,17 @@ int gemv_run(char trans, int m, int n, T alpha, const T* A, int lda, const T* x,
         xin = xg;
     }
     TimedCall tc{};
-    const bool timing = timing_enabled();
+    const int timing = timing_enabled();
     if (timing) {
-        XSYMV_HIP(hipEventCreate(&tc.e0));
-        XSYMV_HIP(hipEventCreate(&tc.e1));
-        XSYMV_HIP(hipEventCreate(&tc.e2));
-        XSYMV_HIP(hipEventRecord(tc.e0, stream));
+        XSYMV_HIP(timed_call_create(tc, timing));
     }
     GemvArgs<T> ga{A, xin, part, part, plan->d_blocks, (long long)lda, m, n};
-    kern<<<plan->G, threads, 0, stream>>>(ga);
-    XSYMV_HIP(hipGetLastError());
-    if (timing) XSYMV_HIP(hipEventRecord(tc.e1, stream));
+    XSYMV_HIP(launch_k(kern, plan->G, threads, stream, ga, tc.e0, tc.e1));
     GemvMergeArgs<T> ma{part, plan->d_seg_base, y, (long long)incy, ky, alpha, beta, leny,
                         plan->NS, R, n, tr, beta_zero};
-    gemv_merge<T, MERGE_SPLIT><<<blocks_for(leny, 64), 64 * MERGE_SPLIT, 0, stream>>>(ma);
-    XSYMV_HIP(hipGetLastError());
-    if (timing) {
-        XSYMV_HIP(hipEventRecord(tc.e2, stream));
-        timing_push(tc);
-    }
+    XSYMV_HIP(launch_k(&gemv_merge<T, MERGE_SPLIT>, blocks_for(leny, 64), 64 * MERGE_SPLIT,
+                       stream, ma, nullptr, tc.e2));
+    if (timing) timing_push(tc);
     return 0;
 }
 
@@ -599,21 +605,13 @@ int syr2_run(char uplo, int n, T alpha, const T* x, int incx, const T* y, int in
         }
     }
     TimedCall tc{};
-    const bool timing = timing_enabled();
+    const int timing = timing_enabled();
     if (timing) {
-        XSYMV_HIP(hipEventCreate(&tc.e0));
-        XSYMV_HIP(hipEventCreate(&tc.e1));
-        XSYMV_HIP(hipEventCreate(&tc.e2));
-        XSYMV_HIP(hipEventRecord(tc.e0, stream));
+        XSYMV_HIP(timed_call_create(tc, timing, false));  // no merge step
     }
     Syr2Args<T> sa{A, xin, yin, plan->d_blocks, plan->d_strip_base, (long long)lda, alpha, n};
-    kern<<<plan->G, threads, 0, stream>>>(sa);
-    XSYMV_HIP(hipGetLastError());
-    if (timing) {
-        XSYMV_HIP(hipEventRecord(tc.e1, stream));
-        XSYMV_HIP(hipEventRecord(tc.e2, stream));  // no merge step
-        timing_push(tc);
-    }
+    XSYMV_HIP(launch_k(kern, plan->G, threads, stream, sa, tc.e0, tc.e1));
+    if (timing) timing_push(tc);
     return 0;
 }
 
@@ -714,25 +712,17 @@ int trmv_run(char uplo, char trans, char diag, int n, const T* A, int lda, T* x,
         xin = xg;
     }
     TimedCall tc{};
-    const bool timing = timing_enabled();
+    const int timing = timing_enabled();
     if (timing) {
-        XSYMV_HIP(hipEventCreate(&tc.e0));
-        XSYMV_HIP(hipEventCreate(&tc.e1));
-        XSYMV_HIP(hipEventCreate(&tc.e2));
-        XSYMV_HIP(hipEventRecord(tc.e0, stream));
+        XSYMV_HIP(timed_call_create(tc, timing));
     }
     TrmvArgs<T> ta{A, xin, part, part, plan->d_blocks, plan->d_strip_base, (long long)lda, n};
-    kern<<<plan->G, threads, 0, stream>>>(ta);
-    XSYMV_HIP(hipGetLastError());
-    if (timing) XSYMV_HIP(hipEventRecord(tc.e1, stream));
+    XSYMV_HIP(launch_k(kern, plan->G, threads, stream, ta, tc.e0, tc.e1));
     TrmvMergeArgs<T> ma{part, plan->d_seg_base, xin, x, (long long)incx, kx, n, plan->NS, R,
                         upper ? 1 : 0, tr, unit ? 1 : 0};
-    trmv_merge<T, MERGE_SPLIT><<<blocks_for(n, 64), 64 * MERGE_SPLIT, 0, stream>>>(ma);
-    XSYMV_HIP(hipGetLastError());
-    if (timing) {
-        XSYMV_HIP(hipEventRecord(tc.e2, stream));
-        timing_push(tc);
-    }
+    XSYMV_HIP(launch_k(&trmv_merge<T, MERGE_SPLIT>, blocks_for(n, 64), 64 * MERGE_SPLIT, stream,
+                       ma, nullptr, tc.e2));
+    if (timing) timing_push(tc);
     return 0;
 }
 
@@ -833,26 +823,17 @@ int shard_run(char uplo, int n, int panel, int nshards, int shard, const T* A, i
         xin = xg;
     }
     TimedCall tc{};
-    const bool timing = timing_enabled();
+    const int timing = timing_enabled();
     if (timing) {
-        XSYMV_HIP(hipEventCreate(&tc.e0));
-        XSYMV_HIP(hipEventCreate(&tc.e1));
-        XSYMV_HIP(hipEventCreate(&tc.e2));
-        XSYMV_HIP(hipEventRecord(tc.e0, stream));
+        XSYMV_HIP(timed_call_create(tc, timing));
     }
     StripArgs<T> sa{A, xin, rowpart, colpart, plan->d_blocks, plan->d_strip_base,
                     (long long)lda, n, plan->d_lcol, plan->d_gloc, plan->d_col0, ncol};
-    kern<<<plan->G, threads, 0, stream>>>(sa);
-    XSYMV_HIP(hipGetLastError());
-    if (timing) XSYMV_HIP(hipEventRecord(tc.e1, stream));
+    XSYMV_HIP(launch_k(kern, plan->G, threads, stream, sa, tc.e0, tc.e1));
     StripMergeArgs<T> ma{rowpart, colpart, plan->d_seg_base, p, 1, 0, tune_one<T>(),
                          tune_zero<T>(), n, plan->NS, R, upper ? 1 : 0, 1, plan->d_gloc, ncol};
-    launch_strip_merge<T, MERGE_SPLIT, true>(ma, n, stream);
-    XSYMV_HIP(hipGetLastError());
-    if (timing) {
-        XSYMV_HIP(hipEventRecord(tc.e2, stream));
-        timing_push(tc);
-    }
+    XSYMV_HIP((launch_strip_merge<T, MERGE_SPLIT, true>(ma, n, stream, tc.e2)));
+    if (timing) timing_push(tc);
     return 0;
 }
 
@@ -873,8 +854,11 @@ int combine_run(int n, int nshards, T alpha, const T* P, int ldp, T beta, T* y, 
     }
     CombineArgs<T> ca{P, y, (long long)ldp, (long long)incy, ky, alpha, beta, n, nshards,
                       beta_zero};
-    symv_combine<T><<<blocks_for(n, 256), 256, 0, stream>>>(ca);
-    XSYMV_HIP(hipGetLastError());
+    TimedCall tc{};
+    const int timing = timing_enabled();
+    if (timing) XSYMV_HIP(timed_call_create(tc, timing, false));  // one kernel
+    XSYMV_HIP(launch_k(&symv_combine<T>, blocks_for(n, 256), 256, stream, ca, tc.e0, tc.e1));
+    if (timing) timing_push(tc);
     return 0;
 }
 

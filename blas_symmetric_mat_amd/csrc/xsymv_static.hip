@@ -152,8 +152,7 @@ int symv_static(char uplo, int n, T alpha, const T* A, int lda, const T* x, int 
     XSYMV_HIP(hipGetLastError());
     StripMergeArgs<T> ma{rowpart, colpart, d_seg_base, y, (long long)incy, ky, alpha, beta,
                          n, st.NS, R, upper ? 1 : 0, beta_zero};
-    launch_strip_merge<T, MERGE_SPLIT>(ma, n, stream);
-    XSYMV_HIP(hipGetLastError());
+    XSYMV_HIP((launch_strip_merge<T, MERGE_SPLIT>(ma, n, stream)));
     return 0;
 }
 

@@ -30,6 +30,8 @@
 //    strip in segment order + sum of colpart[i][r] in strip order).
 #pragma once
 
+#include <hip/hip_ext.h>
+
 #include <type_traits>
 
 #include "xsymv_kernels.hpp"
@@ -454,13 +456,23 @@ __global__ __launch_bounds__(64 * SPLIT) void symv_strip_merge(StripMergeArgs<T>
 // workgroups), else 64.
 constexpr int MERGE_ROWS_SMALL_BELOW = 16384;
 
+// Launches the merge for order n; `stop` (timing only) takes the merge's own
+// end time from its dispatch.  Returns the launch's error.
 template <class T, int SPLIT, bool SHARD = false>
-void launch_strip_merge(const StripMergeArgs<T>& ma, int n, hipStream_t stream)
+hipError_t launch_strip_merge(StripMergeArgs<T> ma, int n, hipStream_t stream,
+                              hipEvent_t stop = nullptr)
 {
-    if (n < MERGE_ROWS_SMALL_BELOW)
-        symv_strip_merge<T, SPLIT, SHARD, 32><<<(n + 31) / 32, 64 * SPLIT, 0, stream>>>(ma);
-    else
-        symv_strip_merge<T, SPLIT, SHARD, 64><<<(n + 63) / 64, 64 * SPLIT, 0, stream>>>(ma);
+    const bool small = n < MERGE_ROWS_SMALL_BELOW;
+    auto k = small ? &symv_strip_merge<T, SPLIT, SHARD, 32> : &symv_strip_merge<T, SPLIT, SHARD, 64>;
+    const int rows = small ? 32 : 64;
+    const dim3 grid((n + rows - 1) / rows), block(64 * SPLIT);
+    if (stop == nullptr) {
+        k<<<grid, block, 0, stream>>>(ma);
+        return hipGetLastError();
+    }
+    void* p[] = {&ma};
+    return hipExtLaunchKernel(reinterpret_cast<const void*>(k), grid, block, p, 0, stream, nullptr,
+                              stop, 0);
 }
 
 // Rank-ordered combination of the shards' partials: y_i := beta*y_i +

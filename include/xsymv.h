@@ -442,12 +442,22 @@ int xsymv_save_config(const char *path);
 int xsymv_load_config(const char *path);
 int xsymv_clear_config(void);
 
-/* Kernel timing for measurement: while enabled, every call records HIP
- * events around its main (tile streaming) kernel and its merge kernel on
- * its stream.  xsymv_timing_read waits for the recorded events, writes up to
- * `max` (main_ms, merge_ms) pairs, clears the record and returns how many it
- * wrote (or 1000 + hipError_t on failure). */
-int xsymv_timing_enable(int on);
+/* Kernel timing for measurement.  xsymv_timing_enable(mode): 0 off (the
+ * default); 1 every call times its main (streaming) kernel and its merge
+ * kernel; 2 every call times itself whole.  The HIP events are bound to the
+ * launches (hipExtLaunchKernel's start and stop events), so they take the
+ * kernels' own start and end times.  Mode 1: main_ms runs from the main
+ * kernel's start to its end, merge_ms from there to the merge's end (the
+ * launch gap included).  Mode 2: no event is bound between the two kernels
+ * (binding one there delays the merge by a few microseconds); main_ms is the
+ * call's span, from the main kernel's start to the merge's end, and merge_ms
+ * is 0.  Calls of one kernel (the rank-2 update, the shard combination)
+ * record that kernel as main_ms and 0 in either mode.  xsymv_timing_read
+ * waits for the recorded events, writes up to `max` (main_ms, merge_ms)
+ * pairs, clears the record and returns how many it wrote (or
+ * 1000 + hipError_t on failure).  xsymv_timing_enable returns 0, or -1 for
+ * a mode other than 0, 1, 2. */
+int xsymv_timing_enable(int mode);
 int xsymv_timing_read(float *main_ms, float *merge_ms, int max);
 
 /* Workgroups a row-strip configuration (column_runs 4, 5 or 6) is launched with

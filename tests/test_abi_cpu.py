@@ -527,3 +527,14 @@ def test_shard_plan_indices_in_bounds(uplo, n, R, panel, nshards):
     for Greq, split, cpg in ((1, 0, 4), (7, 1, 16), (64, 0, 8), (512, 1, 16)):
         for g in range(nshards):
             _simulate_shard(uplo, n, R, Greq, split, panel, nshards, g, cpg)
+
+
+def test_timing_modes():
+    """Modes 0, 1 and 2 are accepted (host state only, nothing launched);
+    any other is refused."""
+    for m in (1, 2, 0, True, False):
+        X.timing_enable(m)
+    for bad in (3, -1):
+        with pytest.raises(ValueError):
+            X.timing_enable(bad)
+    assert X.library().xsymv_timing_enable(0) == 0

@@ -173,3 +173,56 @@ def test_traffic_record_only_for_current_source_and_configuration(tmp_path, monk
     path.write_text(json.dumps({"ssymv-L-n32768": {**rec, "kernel_source_digest": "0" * 16}}))
     assert bench.traffic_record("ssymv-L-n32768", "cfg") is None
 
+
+
+def test_call_breakdown(tmp_path):
+    """A --profile-workload --calls 3 --flush run: 2 warm-up calls (no gap),
+    3 mode-1 calls and 3 mode-2 calls (a 5 us gap before the merge) and 3
+    calls of the per-call protocol (no gap), flush kernels between them, then
+    two layouts of the read probe.  The breakdown keeps the four groups
+    apart, takes kernel, gap, merge and span per group, the fastest probe
+    layout, and quotes what the timings measured."""
+    from blas_symmetric_mat_amd import roofline as R
+    kern = "void xsymv::symv_strip<double, true, 16, 1, 8, true, 256, false>(xsymv::StripArgs<double>)"
+    merge = "void xsymv::symv_strip_merge<double, 16, false, 32>(xsymv::StripMergeArgs<double>)"
+    fill = "void at::native::vectorized_elementwise_kernel<4, at::native::FillFunctor<float>>(...)"
+    probe4 = "void read_probe<4>(unsigned int __vector(4) const*, long long, unsigned int*)"
+    probe8 = "void read_probe<8>(unsigned int __vector(4) const*, long long, unsigned int*)"
+    trace, t = [], 0
+
+    def launch(name, grid, wg, us, gap=0.0):
+        nonlocal t
+        trace.append({"Kernel_Name": name, "Grid_Size_X": grid, "Workgroup_Size_X": wg,
+                      "Start_Timestamp": t, "End_Timestamp": t + int(us * 1000)})
+        t += int(us * 1000) + int(gap * 1000)
+
+    for _ in range(2):
+        launch(kern, 262144, 1024, 54.0)
+        launch(merge, 262144, 1024, 5.0)
+    for gap in (5.0, 5.0, 0.0):
+        for _ in range(3):
+            launch(fill, 1 << 26, 256, 150.0)
+            launch(kern, 262144, 1024, 47.0, gap=gap)
+            launch(merge, 262144, 1024, 4.0)
+        if gap == 0.0:
+            launch(fill, 1 << 26, 256, 150.0)  # flush alone
+    for _ in range(4):
+        launch(probe4, 2048 * 256, 256, 42.0)
+        launch(probe8, 2048 * 256, 256, 40.0)
+    write_csv(tmp_path / "trace.csv", trace)
+    (tmp_path / "ev.json").write_text(json.dumps({
+        "calls": 3, "kernel_us_median": 51.0, "call_us_median": 58.5,
+        "call_us_differential": 51.5, "flush_us_median": 450.0}))
+    name = "d-U-n8192-lda8200-beta0"
+    md = bench.summarize_calls(str(tmp_path / "trace.csv"), name,
+                               f"rocprofv3 ... -- python3 bench.py --profile-workload {name} "
+                               "--calls 3 --flush --read-probe",
+                               events_json=str(tmp_path / "ev.json"))
+    assert "| warm-up, no timing, no flush | 2 | 54.0 | 0.0 | 5.0 | 59.0 |" in md
+    assert "| flushed, events bound to each kernel (mode 1) | 3 | 47.0 | 5.0 | 4.0 | 56.0 |" in md
+    assert "| flushed, events bound to the call (mode 2) | 3 | 47.0 | 5.0 | 4.0 | 56.0 |" in md
+    assert "| flushed, no library events (per-call protocol) | 3 | 47.0 | 0.0 | 4.0 | 51.0 |" in md
+    kb = R.tile_kernel_bytes("d", 8192)
+    assert f"the kernel moves {kb / 47.0 / 1e3:.0f} GB/s" in md
+    assert "Fastest layout: 40.0 us; the streaming kernel (last group) takes 1.175 x that." in md
+    assert "flush 450.0 us), 51.5 us." in md

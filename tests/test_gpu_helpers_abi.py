@@ -35,6 +35,31 @@ def test_timing_records_one_entry_per_call():
     d.run_device(y)
     torch.cuda.synchronize()
     assert X.timing_read() == []  # disabled: nothing recorded
+    # whole-call mode: (span, 0) per call, the span longer than the main
+    # kernel alone takes
+    X.timing_enable(2)
+    try:
+        for _ in range(3):
+            d.run_device(y)
+        torch.cuda.synchronize()
+        whole = X.timing_read()
+    finally:
+        X.timing_enable(False)
+    assert len(whole) == 3
+    assert all(span > 0 and merge == 0 for span, merge in whole)
+    assert sorted(s for s, _ in whole)[1] > sorted(m for m, _ in rec)[1]
+    # one-kernel calls: the rank-2 update records (kernel, 0) in both modes
+    A = torch.zeros(500 * 500, dtype=torch.float64, device="cuda")
+    v = torch.ones(500, dtype=torch.float64, device="cuda")
+    for mode in (1, 2):
+        X.timing_enable(mode)
+        try:
+            X.xsyr2_d("L", 500, 1.0, v, 1, v, 1, A, 500)
+            torch.cuda.synchronize()
+            one = X.timing_read()
+        finally:
+            X.timing_enable(False)
+        assert len(one) == 1 and one[0][0] > 0 and one[0][1] == 0
 
 
 def test_strip_configurations_fill_every_cu():
