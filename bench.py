@@ -266,8 +266,8 @@ def measure_shard_detail(name, p, panel, nshards, reps, read_peak=None, flush=No
     shard's stored elements, x read and the partial written; then the
     rank-ordered combination of the partials.  Each shard's call is timed
     with call_ms, the caches flushed before every call (a shard's share is
-    below 1 GiB); the combination back to back.  The exchange between GPUs
-    is not measured (one GPU)."""
+    below 1 GiB); the combination's kernel by the events bound to it.  The
+    exchange between GPUs is not measured (one GPU)."""
     from blas_symmetric_mat_amd import roofline as R
     import numpy as np
     import torch
@@ -316,7 +316,9 @@ def measure_shard_detail(name, p, panel, nshards, reps, read_peak=None, flush=No
 
     for _ in range(2):
         _C().call()
-    cms = call_ms(_C(), reps)[0]  # back to back: the partials (n x shards) stay cached
+    # the combination's kernel alone (events bound to its launch): timed back
+    # to back, a kernel this short measures the host's launch rate instead
+    cms = sorted(r[0] for r in time_kernels(_C(), reps))[reps // 2]
     out = {"prec": p.prec, "uplo": p.uplo, "n": n, "panel": panel, "shards": nshards,
            "kernel": (f"symv_strip<{CTYPE[p.prec]}, {'upper' if p.uplo == 'U' else 'lower'}, "
                       f"..., shard> + ordered merge"),
