@@ -30,12 +30,12 @@ Printed as one JSON line (kept short), with:
                 n = 16384; C5 WSYMV L n = 8192; CHEMV/ZHEMV/WSYMV L at
                 n = 32768 (inputs drawn on the device).  "us per call" is
                 what one call adds to a stream, with nothing recorded inside
-                the call: below 1 GiB of matrix, the median of (cache flush +
-                call) minus the median of (flush alone), 20 of each,
-                interleaved, each between a pair of events (the flush: 1 GiB
-                written and read back); from 1 GiB, 20 calls back to back
-                over 20.  The kernel's own time comes from the library's
-                events bound to its launch, on the same caches;
+                the call: the median of (cache flush + call) minus the median
+                of (flush alone), 20 of each, interleaved, each between a
+                pair of events (the flush: 1 GiB written and read back).  The
+                kernel's own time comes from the library's events bound to
+                its launch, on flushed calls too; the detail record adds the
+                rate of calls back to back;
   rule_check    at the sweep's odd orders (10007, 32767) the built-in
                 configuration's time over the on-device autotuner's best;
   other         SGEMV/DGEMV (the report's SYMV-vs-GEMV comparison),
@@ -144,7 +144,7 @@ class GemvDev:
                p.incy)
 
 
-def measure_gemv_detail(name, p, reps, read_peak=None):
+def measure_gemv_detail(name, p, reps, read_peak=None, flush=None):
     """The general product beside the symmetric one (the report's comparison:
     same streaming machinery, twice the bytes)."""
     from blas_symmetric_mat_amd import roofline as R
@@ -154,9 +154,9 @@ def measure_gemv_detail(name, p, reps, read_peak=None):
     d = GemvDev(p)
     for _ in range(2):
         d.call()
-    main = sorted(r[0] for r in time_kernels(d, reps))
+    main = sorted(r[0] for r in time_kernels(d, reps, flush))
     t_main = main[len(main) // 2] * 1e-3
-    t_call = call_ms(d, reps)[0] * 1e-3
+    t_call = call_ms(d, reps, flush)[0] * 1e-3
     bz = beta_is_zero(p)
     call_b = R.gemv_call_bytes(p.prec, p.m, p.n, p.trans, bz)
     ci = X.gemv_config_info(p.prec, X.gemv_current_config(p.prec))
@@ -170,7 +170,7 @@ def measure_gemv_detail(name, p, reps, read_peak=None):
            "pct_peak_hbm": round(100 * call_b / t_call / 1e9 / R.HBM_PEAK_GBPS, 1),
            "tile_kernel_gbps": round(R.gemv_kernel_bytes(p.prec, p.m, p.n, p.trans) / t_main
                                      / 1e9, 1),
-           "flushed_between_calls": False, "calls": reps}
+           "flushed_between_calls": flush is not None, "calls": reps}
     if read_peak:
         out["pct_measured_read_peak"] = round(100 * call_b / t_call / 1e9 / read_peak, 1)
     del d
@@ -178,7 +178,7 @@ def measure_gemv_detail(name, p, reps, read_peak=None):
     return out
 
 
-def measure_syr2_detail(name, p, reps, read_peak=None):
+def measure_syr2_detail(name, p, reps, read_peak=None, flush=None):
     """The rank-2 update: the stored triangle read and written once."""
     from blas_symmetric_mat_amd import roofline as R
     import numpy as np
@@ -198,7 +198,7 @@ def measure_syr2_detail(name, p, reps, read_peak=None):
     d = _D()
     for _ in range(2):
         d.call()
-    t_call = call_ms(d, reps)[0] * 1e-3
+    t_call = call_ms(d, reps, flush)[0] * 1e-3
     b = R.syr2_call_bytes(p.prec, p.n)
     ci = X.syr2_config_info(p.prec, X.syr2_current_config(p.prec))
     out = {"prec": p.prec, "uplo": p.uplo, "n": p.n, "lda": p.lda,
@@ -214,7 +214,7 @@ def measure_syr2_detail(name, p, reps, read_peak=None):
     return out
 
 
-def measure_trmv_detail(name, p, reps, read_peak=None):
+def measure_trmv_detail(name, p, reps, read_peak=None, flush=None):
     """The triangular product: the stored triangle read once, x read and
     overwritten (a fresh x per call, so every call does the same work)."""
     from blas_symmetric_mat_amd import roofline as R
@@ -229,15 +229,20 @@ def measure_trmv_detail(name, p, reps, read_peak=None):
 
     class _D:
         def call(self):
-            x.copy_(x0)
             f(p.uplo, p.trans, p.diag, p.n, A, p.lda, x, p.incx)
+
+    def fresh():  # before every call, outside what is timed: x restored
+        if flush is not None:
+            flush()
+        x.copy_(x0)
 
     d = _D()
     for _ in range(2):
+        fresh()
         d.call()
-    main = sorted(r[0] for r in time_kernels(d, reps))
+    main = sorted(r[0] for r in time_kernels(d, reps, fresh))
     t_main = main[len(main) // 2] * 1e-3
-    t_call = call_ms(d, reps)[0] * 1e-3
+    t_call = call_ms(d, reps, fresh)[0] * 1e-3
     unit = p.diag in ("U", "u")
     b = R.trmv_call_bytes(p.prec, p.n, unit)
     idx = X.trmv_current_config(p.prec, p.uplo, p.trans)
@@ -498,10 +503,10 @@ def compact(row: dict) -> list:
 
 
 def measure_detail(name, p, reps, flush, read_peak=None, quiet=False):
-    """One symmetric workload: the call's cost on the stream (call_ms; the
-    caches flushed before each call when the matrix is below 1 GiB, else
-    calls back to back), and its streaming kernel and merge from the
-    library's events bound to them (median of `reps` calls, same caches)."""
+    """One symmetric workload: the call's cost on the stream (call_ms, the
+    caches flushed before each call), its streaming kernel and merge from
+    the library's events bound to them (median of `reps` flushed calls), and
+    the rate of calls back to back without a flush."""
     from blas_symmetric_mat_amd import roofline as R
     import torch
     import blas_symmetric_mat_amd as X
@@ -512,10 +517,10 @@ def measure_detail(name, p, reps, flush, read_peak=None, quiet=False):
         d.call()
     torch.cuda.synchronize()
     small = p.A.nbytes < (1 << 30)
-    rec = time_kernels(d, reps, flush if small else None)
+    rec = time_kernels(d, reps, flush)
     main = sorted(r[0] for r in rec)
     merge = sorted(r[1] for r in rec)
-    c_ms, f_ms = call_ms(d, reps, flush if small else None)
+    c_ms, f_ms = call_ms(d, reps, flush)
     t_main = main[len(main) // 2] * 1e-3
     t_call = c_ms * 1e-3
     bz = beta_is_zero(p)
@@ -533,7 +538,7 @@ def measure_detail(name, p, reps, flush, read_peak=None, quiet=False):
            "pct_peak_hbm": round(100 * call_b / t_call / 1e9 / R.HBM_PEAK_GBPS, 1),
            "tile_kernel_gbps": round(kb / t_main / 1e9, 1),
            "kernel_pct_peak_hbm": round(100 * kb / t_main / 1e9 / R.HBM_PEAK_GBPS, 1),
-           "flushed_between_calls": small,
+           "flushed_between_calls": True,
            "calls": reps}
     tr = traffic_record(workload_key(p), label)
     out["traffic_bytes"] = tr["bytes_per_launch"] if tr else None
@@ -542,34 +547,31 @@ def measure_detail(name, p, reps, flush, read_peak=None, quiet=False):
         out["pct_measured_read_peak"] = round(100 * call_b / t_call / 1e9 / read_peak, 1)
     if p.prec in ("c", "z"):
         out["gflops_8n2_real"] = round(4 * R.gflops_2n2(p.n, t_call), 2)
-    if small:
-        # the same call 100 times back to back, no flush: the rate a loop of
-        # calls on warm caches sees (two events around the whole run)
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(100):
-            d.call()
-        e1.record()
-        torch.cuda.synchronize()
-        out["us_per_call_back_to_back"] = round(e0.elapsed_time(e1) * 10.0, 2)
+    # the same call back to back, no flush (100 calls below 1 GiB of matrix,
+    # else 20): the rate a loop of calls sustains
+    nb = 100 if small else 20
+    out["us_per_call_back_to_back"] = round(call_ms(d, nb)[0] * 1e3, 2)
     del d
     torch.cuda.empty_cache()
     return out
 
 
-def rule_check(cases, reps: int = 10) -> dict:
+def rule_check(cases, reps: int = 20) -> dict:
     """For each (prec, uplo, n) with lda = n: the built-in configuration's
-    median over the on-device autotuner's best (both as the autotuner times
-    them: flushed caches, events around the call), and both indices."""
+    time over the best configuration's, as the on-device autotuner times
+    them (flushed caches, events around the call, median of `reps` calls);
+    two autotuner passes, each configuration's two medians averaged (one
+    pass alone favours whichever configuration a noisy run flatters); and
+    both indices."""
     import blas_symmetric_mat_amd as X
     out = {}
     for prec, uplo, n in cases:
         X.clear_config()
         builtin = X.current_config(prec, uplo, n, n)
-        best, ms = X.autotune(prec, uplo, n, reps=reps, lda=n)
+        runs = [X.autotune(prec, uplo, n, reps=reps, lda=n)[1] for _ in range(2)]
         X.clear_config()
+        ms = [(a + b) / 2 for a, b in zip(*runs)]
+        best = min(range(len(ms)), key=lambda i: ms[i])
         out[f"{prec}-{uplo}-n{n}"] = [round(ms[builtin] / ms[best], 4), builtin, best]
     return out
 
@@ -1115,11 +1117,11 @@ def main():
         for name, make in [("sgemv-N-n32768", lambda: W.gemv_square("s", "N", 32768)),
                            ("sgemv-T-n32768", lambda: W.gemv_square("s", "T", 32768)),
                            ("dgemv-N-n32768", lambda: W.gemv_square("d", "N", 32768))]:
-            detail[name] = measure_gemv_detail(name, make(), args.detail_reps, rd_med)
+            detail[name] = measure_gemv_detail(name, make(), args.detail_reps, rd_med, flush)
         for name, make in [
                 ("ssyr2-L-n32768", lambda: W.make_syr2_problem("s", "L", 32768, seed=32768)),
                 ("dsyr2-U-n32768", lambda: W.make_syr2_problem("d", "U", 32768, seed=32768))]:
-            row = measure_syr2_detail(name, make(), args.detail_reps, rd_med)
+            row = measure_syr2_detail(name, make(), args.detail_reps, rd_med, flush)
             row["pct_of_copy"] = round(100 * row["hbm_gbps_algorithmic"] / cp_med, 1)
             detail[name] = row
         for name, make in [
@@ -1131,7 +1133,7 @@ def main():
                  lambda: W.make_trmv_problem("z", "L", "C", "N", 16384, seed=16384)),
                 ("wtrmv-U-N-n16384",
                  lambda: W.make_trmv_problem("w", "U", "N", "N", 16384, seed=16384))]:
-            detail[name] = measure_trmv_detail(name, make(), args.detail_reps, rd_med)
+            detail[name] = measure_trmv_detail(name, make(), args.detail_reps, rd_med, flush)
         for name, make in [("ssymv-L-n32768-8shards", lambda: W.symv_sweep("s", "L", 32768)),
                            ("dsymv-U-n32768-8shards", lambda: W.symv_sweep("d", "U", 32768))]:
             detail[name] = measure_shard_detail(name, make(), 256, 8, args.detail_reps, rd_med,
