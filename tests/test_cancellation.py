@@ -70,3 +70,27 @@ def test_device_oracle_under_cancellation(prec, uplo):
     outs = [d.run() for _ in range(10)]
     assert len({G.digest(o) for o in outs}) == 1
     G.assert_close(p, outs[0], oracle.symv_problem(p), label=p.name)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("uplo", ["L", "U"])
+def test_device_every_dd_strip_config_under_cancellation(uplo):
+    """Every double-double row-strip configuration under heavy cancellation
+    (the built-in rules reach only some of them at the sizes above): n = 258
+    against the exact result, n = 1500 (several strips, a ragged last one)
+    against the oracle, both within the componentwise bound."""
+    import blas_symmetric_mat_amd as X
+    from tests import gpu_util as G
+    strips = [i for i in range(X.num_configs("w")) if X.config_info("w", i)["column_runs"] >= 4]
+    assert strips
+    small = problem("w", uplo, 258, 3, seed=54)
+    big = problem("w", uplo, 1500, 1, seed=55)
+    ref = oracle.symv_problem(big)
+    try:
+        for idx in strips:
+            G.log(f"cancellation dd strip config #{idx} {uplo}")
+            X.select_config("w", uplo, 0, 1 << 30, idx)
+            exact_ok(small, G.DeviceProblem(small).run())
+            G.assert_close(big, G.DeviceProblem(big).run(), ref, label=f"#{idx}")
+    finally:
+        X.select_config("w", uplo, 0, 1 << 30, -1)
