@@ -226,3 +226,48 @@ def test_call_breakdown(tmp_path):
     assert f"the kernel moves {kb / 47.0 / 1e3:.0f} GB/s" in md
     assert "Fastest layout: 40.0 us; the streaming kernel (last group) takes 1.175 x that." in md
     assert "flush 450.0 us), 51.5 us." in md
+
+
+def test_call_ms_differential_protocol(monkeypatch):
+    """call_ms on a simulated clock: (flush + call) - (flush alone) gives the
+    call's own time; without a flush, calls back to back over their count; a
+    call lost in the flush falls back to more pairs, then to the events'
+    whole-call span."""
+    import torch
+    clock = {"t": 0.0}
+
+    class Ev:
+        def __init__(self, enable_timing=True):
+            self.t = None
+
+        def record(self):
+            self.t = clock["t"]
+
+        def synchronize(self):
+            pass
+
+        def elapsed_time(self, other):
+            return other.t - self.t
+
+    monkeypatch.setattr(torch.cuda, "Event", Ev)
+    monkeypatch.setattr(torch.cuda, "synchronize", lambda: None)
+
+    def flush():
+        clock["t"] += 0.45
+
+    class D:
+        def __init__(self, ms):
+            self.ms = ms
+
+        def call(self):
+            clock["t"] += self.ms
+
+    c, f = bench.call_ms(D(0.054), 20, flush)
+    assert abs(c - 0.054) < 1e-9 and abs(f - 0.45) < 1e-9
+    c, f = bench.call_ms(D(0.33), 20)
+    assert abs(c - 0.33) < 1e-9 and f is None
+    seen = []
+    monkeypatch.setattr(bench, "time_kernels",
+                        lambda d, reps, fl=None, mode=1: seen.append(mode) or [(0.06, 0.0)] * reps)
+    c, f = bench.call_ms(D(0.0), 20, flush)
+    assert seen == [2] and abs(c - 0.06) < 1e-9
