@@ -182,6 +182,34 @@ __global__ __launch_bounds__(64 * W) void symv_strip(StripArgs<T> a)
                 const T v = x[r < rs1 ? r : rs1 - 1];
                 xr[s][k] = E::sel(r < rs1, v, E::zero());
             }
+        // U: the diagonal of the rows whose column is in this segment (local
+        // columns [c0, c1)), loaded now and added at the segment's end, so
+        // that the end waits on no load (a segment of the diagonal triangle
+        // holds several of them, each in its own cache line).  A shard's
+        // segment may hold no column: a strip without any of its columns
+        // that a workgroup's range steps through.
+        constexpr int NDG = UPPER ? SW : 1;
+        T dg[NDG][V];
+        bool din[NDG][V];
+        const bool has_diag = UPPER && (!SHARD || useg > u);
+        if constexpr (UPPER) {
+            const int c0 = u + coff, c1 = useg + coff;
+#pragma unroll
+            for (int s = 0; s < SW; ++s)
+#pragma unroll
+                for (int k = 0; k < V; ++k) {
+                    const int r = rw + s * H + lane * V + k;
+                    // the row's own column, locally (-1: another shard's)
+                    const int lr = has_diag ? (SHARD ? gloc[r < rs1 ? r : rs1 - 1] : r) : -1;
+                    const bool in = has_diag && lr >= c0 && lr < c1 && r < rs1;
+                    // c0 < ncol is a real local column, its diagonal a stored
+                    // element (no load at all when the segment holds none)
+                    const long long cl = in ? lr : c0;
+                    const long long rg = in ? r : (SHARD ? (has_diag ? lcol[c0] : 0) : c0);
+                    din[s][k] = in;
+                    dg[s][k] = has_diag ? E::diag_load(A + cl * lda + rg) : E::zero();
+                }
+        }
 
         int jbuf = u + coff;  // first column held in colred
         int nbuf = 0;         // columns held in colred
@@ -335,26 +363,15 @@ __global__ __launch_bounds__(64 * W) void symv_strip(StripArgs<T> a)
                 nbuf = 0;
             }
         }
-        // (a shard's segment may hold no column: a strip without any of its
-        // columns that a workgroup's range steps through)
-        if (UPPER && (!SHARD || useg > u)) {
-            // diagonal of the rows whose column is in this segment (local
-            // columns [c0, c1))
-            const int c0 = u + coff, c1 = useg + coff;
+        if constexpr (UPPER) {
+            if (has_diag) {
 #pragma unroll
-            for (int s = 0; s < SW; ++s)
+                for (int s = 0; s < SW; ++s)
 #pragma unroll
-                for (int k = 0; k < V; ++k) {
-                    const int r = rw + s * H + lane * V + k;
-                    // the row's own column, locally (-1: another shard's)
-                    const int lr = SHARD ? gloc[r < rs1 ? r : rs1 - 1] : r;
-                    const bool in = lr >= c0 && lr < c1 && r < rs1;
-                    // c0 < ncol is a real local column, its diagonal a stored element
-                    const long long cl = in ? lr : c0;
-                    const long long rg = in ? r : (SHARD ? lcol[c0] : c0);
-                    const T d = E::diag_load(A + cl * lda + rg);
-                    racc[s][k] = E::mac(racc[s][k], E::sel(in, d, E::zero()), xr[s][k]);
-                }
+                    for (int k = 0; k < V; ++k)
+                        racc[s][k] = E::mac(racc[s][k], E::sel(din[s][k], dg[s][k], E::zero()),
+                                            xr[s][k]);
+            }
         }
         // this wave's row partials for the segment
         T* __restrict__ rp = a.rowpart + (long long)slot * R;
