@@ -142,7 +142,7 @@ void build_strip_plan_host(bool upper, int n, int R, int G, int split,
     }
     const long long C = prefix[total_pos];
     G = std::max(1, (int)std::min<long long>(G, total_pos));
-    blocks.assign(G, StripBlock{0, 0, 0, 0});
+    blocks.assign(G, StripBlock{});
     std::vector<long long> bound(G + 1, 0);
     bound[G] = total_pos;
     for (int b = 1; b < G; ++b) {
@@ -159,7 +159,8 @@ void build_strip_plan_host(bool upper, int n, int R, int G, int split,
     for (int b = 0; b < G; ++b) {
         const int u0 = (int)bound[b], u1 = (int)bound[b + 1];
         while (strip < NS - 1 && strip_base[strip + 1] <= u0) ++strip;
-        blocks[b] = StripBlock{u0, u1, slot, strip};
+        blocks[b] = StripBlock{u0, u1, slot, strip, strip_base[strip], strip_base[strip + 1],
+                               first[strip], 0};
         int u = u0, st = strip;
         while (u < u1) {
             if (first_slot[st] < 0) first_slot[st] = slot;
@@ -260,7 +261,7 @@ void build_gemv_plan_host(int m, int n, int R, int G, std::vector<StripBlock>& b
     };
     const long long C = cost_before(total);
     G = std::max(1, (int)std::min<long long>(G, total));
-    blocks.assign(G, StripBlock{0, 0, 0, 0});
+    blocks.assign(G, StripBlock{});
     std::vector<long long> bound(G + 1, 0);
     bound[G] = total;
     for (int b = 1; b < G; ++b) {
@@ -281,7 +282,7 @@ void build_gemv_plan_host(int m, int n, int R, int G, std::vector<StripBlock>& b
     for (int b = 0; b < G; ++b) {
         const int u0 = (int)bound[b], u1 = (int)bound[b + 1];
         const int strip = std::min(NS - 1, u0 / std::max(n, 1));
-        blocks[b] = StripBlock{u0, u1, slot, strip};
+        blocks[b] = StripBlock{u0, u1, slot, strip, strip * n, (strip + 1) * n, 0, 0};
         int u = u0, st = strip;
         while (u < u1) {
             if (first_slot[st] < 0) first_slot[st] = slot;

@@ -39,12 +39,19 @@
 namespace xsymv {
 
 // Per workgroup: [u0, u1) in the column sequence, first segment slot, strip
-// of u0.
+// of u0, and that strip's entries of the plan's tables (where its sequence
+// starts and ends, its first local column), so that a workgroup's first
+// column loads depend on this one descriptor load alone.  32 bytes: read by
+// one scalar load.
 struct StripBlock {
     int u0;
     int u1;
     int slot0;
     int strip0;
+    int sb0;   // strip_base[strip0]
+    int sb1;   // strip_base[strip0 + 1]
+    int col0;  // strip_col0[strip0] (a shard's product), else 0
+    int pad;
 };
 
 template <class T>
@@ -137,7 +144,11 @@ __global__ __launch_bounds__(64 * W) void symv_strip(StripArgs<T> a)
 
     __shared__ T colred[W][CBUF];
 
-    const StripBlock bd = a.blocks[blockIdx.x];
+    // the descriptor through the constant address space: one scalar load
+    // of its 32 bytes
+    using cblock = const __attribute__((address_space(4))) StripBlock*;
+    const cblock bp = (cblock)a.blocks + blockIdx.x;
+    const StripBlock bd{bp->u0, bp->u1, bp->slot0, bp->strip0, bp->sb0, bp->sb1, bp->col0, 0};
     const int n = a.n;
     const long long lda = a.lda;
     const int lane = threadIdx.x & 63;
@@ -161,13 +172,16 @@ __global__ __launch_bounds__(64 * W) void symv_strip(StripArgs<T> a)
     int u = bd.u0;
     int slot = bd.slot0;
     int strip = bd.strip0;
+    // this strip's table entries: from the descriptor for the first segment,
+    // from the tables for a later one
+    int sb_lo = bd.sb0, sb_hi = bd.sb1, scol0 = bd.col0;
     while (u < bd.u1) {  // workgroup-uniform: one segment per iteration
-        const int sb0 = a.strip_base[strip];
-        const int useg = min(bd.u1, a.strip_base[strip + 1]);
+        const int sb0 = sb_lo;
+        const int useg = min(bd.u1, sb_hi);
         const int rs0 = strip * R;
         const int rs1 = min(n, rs0 + R);
         // (local) column = sequence position + coff
-        const int coff = (UPPER ? (SHARD ? a.strip_col0[strip] : rs0) : 0) - sb0;
+        const int coff = (UPPER ? (SHARD ? scol0 : rs0) : 0) - sb0;
         const int rw = rs0 + wave * RW;            // this wave's first row
         const bool wave_empty = rw >= rs1;
 
@@ -385,6 +399,11 @@ __global__ __launch_bounds__(64 * W) void symv_strip(StripArgs<T> a)
         u = useg;
         ++slot;
         ++strip;
+        if (u < bd.u1) {  // another strip follows (strip < NS)
+            sb_lo = sb_hi;
+            sb_hi = a.strip_base[strip + 1];
+            if constexpr (SHARD && UPPER) scol0 = a.strip_col0[strip];
+        }
     }
 }
 

@@ -94,7 +94,7 @@ def _partials_bytes(X, uplo, n):
     G_ = X.config_workgroups("s", idx, uplo)
     blocks, sb, seg = X.strip_plan(uplo, n, R, G_, ci["column_runs"] - 4)
     NS = len(sb) - 1
-    return (up(len(blocks) * 16) + 2 * up((NS + 1) * 4) + up(seg[-1] * R * 4) + up(NS * n * 4))
+    return (up(len(blocks) * 32) + 2 * up((NS + 1) * 4) + up(seg[-1] * R * 4) + up(NS * n * 4))
 
 
 def test_too_large_refused():
