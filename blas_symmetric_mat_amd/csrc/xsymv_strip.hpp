@@ -450,11 +450,21 @@ __global__ __launch_bounds__(64 * SPLIT) void symv_strip_merge(StripMergeArgs<T>
     const int v = (threadIdx.x >> 6) * GROUPS + lane / ROWS;  // this lane's stream
     const int rl = lane % ROWS;
     const int i = blockIdx.x * ROWS + rl;
+    // the workgroup's rows lie in one strip (R is a multiple of ROWS): its
+    // segment range is read by scalar loads, and y_i (when beta != 0) is
+    // loaded now, so that neither waits at the end
+    const int I = (int)(((long long)blockIdx.x * ROWS) / a.R);
+    using cint = const __attribute__((address_space(4))) int*;
+    const int s_lo = ((cint)a.seg_base)[I];
+    const int nrow = ((cint)a.seg_base)[I + 1] - s_lo;
+    T* yp = nullptr;
+    T yv = E::zero();
+    if constexpr (!SHARD) {
+        yp = a.y + a.ky + (long long)i * a.incy;
+        if (v == 0 && i < a.n && !a.beta_zero) yv = *yp;
+    }
     T acc = E::zero();
     if (i < a.n) {
-        const int I = i / a.R;
-        const int s_lo = a.seg_base[I];
-        const int nrow = a.seg_base[I + 1] - s_lo;
         const int c_lo = a.upper ? 0 : I;
         const int li = SHARD ? a.gloc[i] : i;  // the row's column, locally
         const int ncol = li < 0 ? 0 : (a.upper ? I + 1 : a.NS - I);
@@ -480,9 +490,8 @@ __global__ __launch_bounds__(64 * SPLIT) void symv_strip_merge(StripMergeArgs<T>
         if constexpr (SHARD) {
             a.y[i] = tot;
         } else {
-            T* yp = a.y + a.ky + (long long)i * a.incy;
             T r = E::mul(a.alpha, tot);
-            if (!a.beta_zero) r = E::add(r, E::mul(a.beta, *yp));
+            if (!a.beta_zero) r = E::add(r, E::mul(a.beta, yv));
             *yp = r;
         }
     }
