@@ -315,6 +315,7 @@ int get_gemv_plan(DeviceState* ds, int m, int n, int R, int G, hipStream_t strea
     plan->G = (int)blocks.size();
     plan->nseg = segb[NS];
     plan->R = R;
+    plan->h_seg_base = segb;
     const size_t bb = blocks.size() * sizeof(StripBlock);
     const size_t ib = segb.size() * sizeof(int);
     char* h = nullptr;
@@ -497,6 +498,7 @@ int get_shard_plan(DeviceState* ds, bool upper, int n, int R, int G, int split, 
     plan->G = (int)blocks.size();
     plan->nseg = segb[NS];
     plan->R = R;
+    plan->h_seg_base = segb;
     plan->ncol = (int)cols.size();
     // one upload: blocks, strip_base, seg_base, col0, lcol, gloc
     const size_t bb = blocks.size() * sizeof(StripBlock);
@@ -555,6 +557,7 @@ int get_strip_plan(DeviceState* ds, int dev, bool upper, int n, int R, int G, in
     plan->G = (int)blocks.size();
     plan->nseg = segb[NS];
     plan->R = R;
+    plan->h_seg_base = segb;
     const size_t bb = blocks.size() * sizeof(StripBlock);
     const size_t ib = sb.size() * sizeof(int);
     char* h = nullptr;

@@ -161,6 +161,7 @@ struct StripPlan {
     StripBlock* d_blocks = nullptr;
     int* d_strip_base = nullptr;
     int* d_seg_base = nullptr;
+    std::vector<int> h_seg_base;  // host copy (the merge takes it as arguments)
     void* h_pinned = nullptr;  // pinned source of the one upload
     // one shard's product: its local columns (see StripArgs)
     int ncol = 0;
@@ -342,7 +343,7 @@ int strip_run(const KernelSet<T>& ks, bool upper, int n, T alpha, const T* A, in
     XSYMV_HIP(launch_k(kern, plan->G, threads, stream, sa, tc.e0, tc.e1));
     StripMergeArgs<T> ma{rowpart, colpart, plan->d_seg_base, y, (long long)incy, ky, alpha, beta,
                          n, plan->NS, R, upper ? 1 : 0, beta_zero};
-    XSYMV_HIP((launch_strip_merge<T, MERGE_SPLIT>(ma, n, stream, tc.e2)));
+    XSYMV_HIP((launch_strip_merge<T, MERGE_SPLIT>(ma, n, stream, tc.e2, plan->h_seg_base.data())));
     if (timing) timing_push(tc);
     return 0;
 }
@@ -832,7 +833,8 @@ int shard_run(char uplo, int n, int panel, int nshards, int shard, const T* A, i
     XSYMV_HIP(launch_k(kern, plan->G, threads, stream, sa, tc.e0, tc.e1));
     StripMergeArgs<T> ma{rowpart, colpart, plan->d_seg_base, p, 1, 0, tune_one<T>(),
                          tune_zero<T>(), n, plan->NS, R, upper ? 1 : 0, 1, plan->d_gloc, ncol};
-    XSYMV_HIP((launch_strip_merge<T, MERGE_SPLIT, true>(ma, n, stream, tc.e2)));
+    XSYMV_HIP((launch_strip_merge<T, MERGE_SPLIT, true>(ma, n, stream, tc.e2,
+                                                         plan->h_seg_base.data())));
     if (timing) timing_push(tc);
     return 0;
 }

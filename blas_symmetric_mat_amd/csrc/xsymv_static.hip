@@ -39,6 +39,7 @@ struct StaticState {
     // shape of the work split the array holds
     int upper = 0, n = 0, R = 0, G = 0, split = 0;
     int NS = 0, nblocks = 0, nseg = 0;
+    std::vector<int> seg;  // host copy of seg_base (passed to the merge as arguments)
 };
 
 std::mutex g_static_mu;
@@ -129,6 +130,7 @@ int symv_static(char uplo, int n, T alpha, const T* A, int lda, const T* x, int 
         st.NS = NS;
         st.nblocks = nblocks;
         st.nseg = segb[NS];
+        st.seg = segb;
     } else {
         const size_t need = static_layout<T>(st.nblocks, st.NS, st.nseg, R, n, gather, &o_sb,
                                              &o_seg, &o_row, &o_col, &o_x);
@@ -152,7 +154,7 @@ int symv_static(char uplo, int n, T alpha, const T* A, int lda, const T* x, int 
     XSYMV_HIP(hipGetLastError());
     StripMergeArgs<T> ma{rowpart, colpart, d_seg_base, y, (long long)incy, ky, alpha, beta,
                          n, st.NS, R, upper ? 1 : 0, beta_zero};
-    XSYMV_HIP((launch_strip_merge<T, MERGE_SPLIT>(ma, n, stream)));
+    XSYMV_HIP((launch_strip_merge<T, MERGE_SPLIT>(ma, n, stream, nullptr, st.seg.data())));
     return 0;
 }
 

@@ -416,6 +416,8 @@ __global__ __launch_bounds__(64 * W) void symv_strip(StripArgs<T> a)
 // k % streams == v; the subtotals meet in a fixed pairwise tree.  ROWS = 32
 // runs twice as many workgroups, for orders whose 64-row blocks would leave
 // CUs idle.
+constexpr int MERGE_SEG_INLINE = 256;
+
 template <class T>
 struct StripMergeArgs {
     const T* rowpart;
@@ -433,12 +435,16 @@ struct StripMergeArgs {
     int beta_zero;
     const int* gloc;  // sharded product only
     int ncol;
+    // seg_base itself (NS + 1 entries) when it fits: the kernel arguments
+    // come with the first scalar load, so the partials' addresses wait on no
+    // table in memory
+    int seg_inline[MERGE_SEG_INLINE];
 };
 
 // SHARD: the shard's partial vector -- column partials only for the rows
 // whose column the shard owns (local index gloc[i], rows of ncol), no alpha or
-// beta: y is the contiguous partial p.
-template <class T, int SPLIT, bool SHARD = false, int ROWS = 64>
+// beta: y is the contiguous partial p.  INL: seg_base from the arguments.
+template <class T, int SPLIT, bool SHARD = false, int ROWS = 64, bool INL = false>
 __global__ __launch_bounds__(64 * SPLIT) void symv_strip_merge(StripMergeArgs<T> a)
 {
     using E = Elem<T>;
@@ -455,8 +461,8 @@ __global__ __launch_bounds__(64 * SPLIT) void symv_strip_merge(StripMergeArgs<T>
     // loaded now, so that neither waits at the end
     const int I = (int)(((long long)blockIdx.x * ROWS) / a.R);
     using cint = const __attribute__((address_space(4))) int*;
-    const int s_lo = ((cint)a.seg_base)[I];
-    const int nrow = ((cint)a.seg_base)[I + 1] - s_lo;
+    const int s_lo = INL ? a.seg_inline[I] : ((cint)a.seg_base)[I];
+    const int nrow = (INL ? a.seg_inline[I + 1] : ((cint)a.seg_base)[I + 1]) - s_lo;
     T* yp = nullptr;
     T yv = E::zero();
     if constexpr (!SHARD) {
@@ -502,13 +508,22 @@ __global__ __launch_bounds__(64 * SPLIT) void symv_strip_merge(StripMergeArgs<T>
 constexpr int MERGE_ROWS_SMALL_BELOW = 16384;
 
 // Launches the merge for order n; `stop` (timing only) takes the merge's own
-// end time from its dispatch.  Returns the launch's error.
+// end time from its dispatch.  h_seg (host copy of seg_base, NS + 1 entries)
+// given and short enough: the table goes in the arguments.  Returns the
+// launch's error.
 template <class T, int SPLIT, bool SHARD = false>
 hipError_t launch_strip_merge(StripMergeArgs<T> ma, int n, hipStream_t stream,
-                              hipEvent_t stop = nullptr)
+                              hipEvent_t stop = nullptr, const int* h_seg = nullptr)
 {
     const bool small = n < MERGE_ROWS_SMALL_BELOW;
-    auto k = small ? &symv_strip_merge<T, SPLIT, SHARD, 32> : &symv_strip_merge<T, SPLIT, SHARD, 64>;
+    const bool inl = h_seg != nullptr && ma.NS + 1 <= MERGE_SEG_INLINE;
+    if (inl) {
+        for (int i = 0; i <= ma.NS; ++i) ma.seg_inline[i] = h_seg[i];
+    }
+    auto k = small ? (inl ? &symv_strip_merge<T, SPLIT, SHARD, 32, true>
+                          : &symv_strip_merge<T, SPLIT, SHARD, 32, false>)
+                   : (inl ? &symv_strip_merge<T, SPLIT, SHARD, 64, true>
+                          : &symv_strip_merge<T, SPLIT, SHARD, 64, false>);
     const int rows = small ? 32 : 64;
     const dim3 grid((n + rows - 1) / rows), block(64 * SPLIT);
     if (stop == nullptr) {
