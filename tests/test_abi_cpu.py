@@ -148,7 +148,7 @@ def test_workspace_bytes_grow_with_n():
         X.clear_config()
 
 
-@pytest.mark.parametrize("split", [0, 1])
+@pytest.mark.parametrize("split", [0, 1, 2])
 @pytest.mark.parametrize("uplo", ["L", "U"])
 @pytest.mark.parametrize("n,R,G", [(1, 64, 7), (100, 64, 3), (1000, 256, 37), (1031, 128, 200),
                                    (4096, 1024, 1792), (10007, 2048, 1792), (5000, 512, 1)])
