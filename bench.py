@@ -564,11 +564,11 @@ def measure_detail(name, p, reps, flush, read_peak=None, quiet=False):
     return out
 
 
-def rule_check(cases, reps: int = 20) -> dict:
+def rule_check(cases, reps: int = 20, passes: int = 3) -> dict:
     """For each (prec, uplo, n) with lda = n: the built-in configuration's
     time over the best configuration's, as the on-device autotuner times
     them (flushed caches, events around the call, median of `reps` calls);
-    two autotuner passes, each configuration's two medians averaged (one
+    `passes` autotuner passes, each configuration's medians averaged (one
     pass alone favours whichever configuration a noisy run flatters); and
     both indices."""
     import blas_symmetric_mat_amd as X
@@ -576,7 +576,7 @@ def rule_check(cases, reps: int = 20) -> dict:
     for prec, uplo, n in cases:
         X.clear_config()
         builtin = X.current_config(prec, uplo, n, n)
-        runs = [X.autotune(prec, uplo, n, reps=reps, lda=n)[1] for _ in range(2)]
+        runs = [X.autotune(prec, uplo, n, reps=reps, lda=n)[1] for _ in range(passes)]
         X.clear_config()
         ms = [(a + b) / 2 for a, b in zip(*runs)]
         best = min(range(len(ms)), key=lambda i: ms[i])

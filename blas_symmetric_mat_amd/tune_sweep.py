@@ -15,7 +15,9 @@ per-size rules (§3, Table 3).  This is the MI355X counterpart:
             lda = n, ``--n-min``
             skips the smaller orders, ``--uplos`` limits the triangles, and
             ``--append`` adds the results to an existing record (replacing
-            those of the same key).  Needs a GPU.
+            those of the same key), ``--passes`` averages each
+            configuration's median over several autotuner passes.  Needs a
+            GPU.
 
   emit:     python -m blas_symmetric_mat_amd.tune_sweep emit IN.json OUT.inc
             Turns a measurement record into the rule rows compiled into the
@@ -59,14 +61,14 @@ def _shape(X, prec, idx):
 
 
 def measure(out_path: str, precs: str, reps: int, grid_max: int | None, cls: int = 0,
-            n_min: int = 0, append: bool = False, uplos: str = "LU") -> None:
+            n_min: int = 0, append: bool = False, uplos: str = "LU", passes: int = 1) -> None:
     import os
     import torch
     import blas_symmetric_mat_amd as X
 
     torch.cuda.init()
     record = {"library": X.version(), "device": torch.cuda.get_device_name(0), "reps": reps,
-              "shapes": {}, "results": []}
+              "passes": passes, "shapes": {}, "results": []}
     if append and os.path.exists(out_path):
         with open(out_path) as f:
             record = json.load(f)
@@ -85,9 +87,16 @@ def measure(out_path: str, precs: str, reps: int, grid_max: int | None, cls: int
                 # 64-byte lines (odd orders), else n + 1
                 lda = n if cls and (n * ELEM_BYTES[prec]) % 64 else n + cls
                 t0 = time.time()
+                # each configuration's median averaged over `passes` autotuner
+                # passes: shapes within a per cent of one another are common, and
+                # one pass names whichever a noisy run flatters
+                runs = []
+                for _ in range(passes):
+                    X.clear_config()
+                    runs.append(X.autotune(prec, uplo, n, reps=reps, lda=lda)[1])
                 X.clear_config()
-                best, ms = X.autotune(prec, uplo, n, reps=reps, lda=lda)
-                X.clear_config()
+                ms = [sum(t) / len(t) for t in zip(*runs)]
+                best = min(range(len(ms)), key=lambda i: ms[i])
                 record["results"] = [r for r in record["results"] if
                                      (r["prec"], r["uplo"], r["n"], r.get("cls", 0)) !=
                                      (prec, uplo, n, cls)]
@@ -137,7 +146,8 @@ def emit(in_path: str, out_path: str) -> None:
     rows = rules_from_record(record)
     lines = [f"// Generated by blas_symmetric_mat_amd/tune_sweep.py from {in_path.split('/')[-1]}",
              f"// ({record.get('device', '?')}, {record.get('library', '?')}, "
-             f"median of {record.get('reps', '?')} timed calls).",
+             f"median of {record.get('reps', '?')} timed calls, averaged over "
+             f"{record.get('passes', 1)} autotuner pass(es)).",
              "// {prec, uplo, n_lo, n_hi, waves, cols_per_wave, stripes, nontemporal, "
              "x_in_lds, family[, stride class]}"]
     for r in rows:
@@ -161,12 +171,14 @@ def main(argv=None) -> int:
     m.add_argument("--n-min", type=int, default=0)
     m.add_argument("--append", action="store_true")
     m.add_argument("--uplos", default="LU", choices=("L", "U", "LU"))
+    m.add_argument("--passes", type=int, default=1)
     e = sub.add_parser("emit")
     e.add_argument("record")
     e.add_argument("out")
     a = ap.parse_args(argv)
     if a.cmd == "measure":
-        measure(a.out, a.precs, a.reps, a.grid_max, a.stride_class, a.n_min, a.append, a.uplos)
+        measure(a.out, a.precs, a.reps, a.grid_max, a.stride_class, a.n_min, a.append, a.uplos,
+                a.passes)
     else:
         emit(a.record, a.out)
     return 0
