@@ -416,7 +416,7 @@ __global__ __launch_bounds__(64 * W) void symv_strip(StripArgs<T> a)
 // k % streams == v; the subtotals meet in a fixed pairwise tree.  ROWS = 32
 // runs twice as many workgroups, for orders whose 64-row blocks would leave
 // CUs idle.
-constexpr int MERGE_SEG_INLINE = 256;
+constexpr int MERGE_SEG_INLINE = 64;
 
 template <class T>
 struct StripMergeArgs {

@@ -249,3 +249,34 @@ def test_trmv_element_offsets_beyond_2_31(uplo, trans):
     dlt = H.diff("s", got[rows], ref[rows])
     assert np.all(dlt <= tol), f"{np.sum(~(dlt <= tol))} sampled outputs beyond the bound"
     G.log(f"  ok ({len(rows)} sampled outputs)")
+
+
+@pytest.mark.parametrize("prec,n", [("w", 16640), ("d", 33280)])
+@pytest.mark.parametrize("uplo", ["L", "U"])
+def test_merge_segment_table_in_memory(prec, uplo, n):
+    """The merge reads its segment table from memory when the strips are too
+    many for its arguments (65 or more): the strip configuration of the
+    shortest strips at an order with 65 of them (WSYMV R = 256, DSYMV
+    R = 512), drawn on the device, every row against the oracle."""
+    import torch
+    import blas_symmetric_mat_amd as X
+    cfgs = [i for i in range(X.num_configs(prec)) if X.config_info(prec, i)["column_runs"] >= 4]
+    idx = min(cfgs, key=lambda i: X.config_info(prec, i)["stripes"])
+    ci = X.config_info(prec, idx)
+    R = ci["stripes"] * ci["rows_per_stripe"]
+    assert (n + R - 1) // R >= 65
+    G.log(f"merge table in memory: {prec} {uplo} n={n} config #{idx} (R {R})")
+    p = W.metric_order_on_device(prec, n, uplo)
+    X.select_config(prec, uplo, n, n, idx)
+    try:
+        y = p.y.clone()
+        getattr(X, G.ENTRY[prec])(p.uplo, p.n, p.alpha, p.A, p.lda, p.x, p.incx, p.beta, y,
+                                  p.incy)
+        torch.cuda.synchronize()
+        got = y.cpu().numpy()
+    finally:
+        X.select_config(prec, uplo, n, n, -1)
+    h = W.problem_to_host(p)
+    del p, y
+    torch.cuda.empty_cache()
+    G.assert_close(h, got, oracle.symv_problem(h), label=h.name)
