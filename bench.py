@@ -578,7 +578,7 @@ def rule_check(cases, reps: int = 20, passes: int = 3) -> dict:
         builtin = X.current_config(prec, uplo, n, n)
         runs = [X.autotune(prec, uplo, n, reps=reps, lda=n)[1] for _ in range(passes)]
         X.clear_config()
-        ms = [(a + b) / 2 for a, b in zip(*runs)]
+        ms = [sum(v) / len(v) for v in zip(*runs)]
         best = min(range(len(ms)), key=lambda i: ms[i])
         out[f"{prec}-{uplo}-n{n}"] = [round(ms[builtin] / ms[best], 4), builtin, best]
     return out

@@ -271,3 +271,27 @@ def test_call_ms_differential_protocol(monkeypatch):
                         lambda d, reps, fl=None, mode=1: seen.append(mode) or [(0.06, 0.0)] * reps)
     c, f = bench.call_ms(D(0.0), 20, flush)
     assert seen == [2] and abs(c - 0.06) < 1e-9
+
+
+@pytest.mark.parametrize("passes", [1, 2, 3])
+def test_rule_check_averages_every_pass(monkeypatch, passes):
+    """The rule check averages each configuration's medians over all the
+    autotuner passes it asked for, whatever their number."""
+    import blas_symmetric_mat_amd as X
+    # configuration 1 is the built-in choice; per pass, configuration 0 is
+    # faster in the first pass only, configuration 2 on average
+    times = [[1.0, 2.0, 1.5], [3.0, 2.0, 1.5], [3.0, 2.0, 1.5]]
+    calls = []
+
+    def autotune(prec, uplo, n, reps=20, lda=None):
+        calls.append((prec, uplo, n, reps, lda))
+        return 0, list(times[len(calls) - 1])
+
+    monkeypatch.setattr(X, "clear_config", lambda: None)
+    monkeypatch.setattr(X, "current_config", lambda prec, uplo, n, lda: 1)
+    monkeypatch.setattr(X, "autotune", autotune)
+    out = bench.rule_check([("s", "L", 4096)], reps=7, passes=passes)
+    assert calls == [("s", "L", 4096, 7, 4096)] * passes
+    avg = [sum(t[i] for t in times[:passes]) / passes for i in range(3)]
+    best = min(range(3), key=lambda i: avg[i])
+    assert out == {"s-L-n4096": [round(avg[1] / avg[best], 4), 1, best]}
