@@ -581,6 +581,7 @@ def rule_check(cases, reps: int = 20, passes: int = 3) -> dict:
         ms = [sum(v) / len(v) for v in zip(*runs)]
         best = min(range(len(ms)), key=lambda i: ms[i])
         out[f"{prec}-{uplo}-n{n}"] = [round(ms[builtin] / ms[best], 4), builtin, best]
+        log(f"rule check {prec}-{uplo}-n{n}: built-in #{builtin}, fastest #{best}")
     return out
 
 
