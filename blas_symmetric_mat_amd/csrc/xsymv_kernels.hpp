@@ -296,6 +296,37 @@ __global__ __launch_bounds__(64 * W) void symv_tiles(SymvArgs<T> args)
 }
 
 // ---------------------------------------------------------------------------
+// One lane's share of a merge: acc + t(k0) + t(k0 + step) + ... over k < kend,
+// added in that order.  The terms are loaded NB at a time, all NB issued
+// before the first is added, so a lane whose share is at most NB terms waits
+// for one memory round trip (a loop that loads and adds term by term waits
+// once per term).  Indices past kend load the batch's first term again (an
+// address already in use, no branch) and are not added.  addr(k) is the
+// address of term k.
+template <class T, int NB, class Addr>
+__device__ __forceinline__ T ordered_batch_sum(T acc, int k0, int kend, int step, Addr addr)
+{
+    using E = Elem<T>;
+    for (int kb = k0; kb < kend; kb += NB * step) {
+        T t[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const int k = kb + b * step;
+            t[b] = *addr(k < kend ? k : kb);
+        }
+        // keep the scheduler from moving each load down to its addition
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+            if (kb + b * step < kend) acc = E::add(acc, t[b]);
+    }
+    return acc;
+}
+
+// Terms per batch of the merges' ordered sums.
+constexpr int MERGE_BATCH = 8;
+
+// ---------------------------------------------------------------------------
 // Column-run kernel: the same tiles and partials as symv_tiles, organised so
 // that registers do not grow with the panel width.  Each wave walks its CW
 // columns one at a time; a column's R tile rows are one contiguous run of S
@@ -627,11 +658,9 @@ __global__ __launch_bounds__(64 * SPLIT) void symv_merge(MergeArgs<T> a)
         const int ci = i - pi * a.NB;
         const T* __restrict__ rp = a.rowpart + (long long)p_lo * a.n + i;
         const T* __restrict__ cp = a.colpart + (long long)s_lo * a.NB + ci;
-#pragma unroll 4
-        for (int k = g; k < ntot; k += SPLIT) {
-            const T v = (k < nrow) ? rp[(long long)k * a.n] : cp[(long long)(k - nrow) * a.NB];
-            acc = E::add(acc, v);
-        }
+        acc = ordered_batch_sum<T, MERGE_BATCH>(acc, g, ntot, SPLIT, [&](int k) {
+            return k < nrow ? rp + (long long)k * a.n : cp + (long long)(k - nrow) * a.NB;
+        });
     }
     part[g][lane] = acc;
     __syncthreads();

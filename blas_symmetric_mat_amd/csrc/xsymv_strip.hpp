@@ -459,7 +459,7 @@ __global__ __launch_bounds__(64 * SPLIT) void symv_strip_merge(StripMergeArgs<T>
     // the workgroup's rows lie in one strip (R is a multiple of ROWS): its
     // segment range is read by scalar loads, and y_i (when beta != 0) is
     // loaded now, so that neither waits at the end
-    const int I = (int)(((long long)blockIdx.x * ROWS) / a.R);
+    const int I = (int)((blockIdx.x * (unsigned)ROWS) / (unsigned)a.R);  // below n: 32 bits
     using cint = const __attribute__((address_space(4))) int*;
     const int s_lo = INL ? a.seg_inline[I] : ((cint)a.seg_base)[I];
     const int nrow = (INL ? a.seg_inline[I + 1] : ((cint)a.seg_base)[I + 1]) - s_lo;
@@ -478,11 +478,9 @@ __global__ __launch_bounds__(64 * SPLIT) void symv_strip_merge(StripMergeArgs<T>
         const long long cstride = SHARD ? a.ncol : a.n;
         const T* __restrict__ rp = a.rowpart + (long long)s_lo * a.R + (i - I * a.R);
         const T* __restrict__ cp = a.colpart + (long long)c_lo * cstride + li;
-#pragma unroll 4
-        for (int k = v; k < ntot; k += V) {
-            const T t = (k < nrow) ? rp[(long long)k * a.R] : cp[(long long)(k - nrow) * cstride];
-            acc = E::add(acc, t);
-        }
+        acc = ordered_batch_sum<T, MERGE_BATCH>(acc, v, ntot, V, [&](int k) {
+            return k < nrow ? rp + (long long)k * a.R : cp + (long long)(k - nrow) * cstride;
+        });
     }
     part[v][rl] = acc;
     __syncthreads();

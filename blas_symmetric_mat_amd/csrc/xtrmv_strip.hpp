@@ -265,8 +265,8 @@ __global__ __launch_bounds__(64 * SPLIT) void trmv_merge(TrmvMergeArgs<T> a)
             stride = a.n;
         }
         const T* __restrict__ p = a.part + base;
-#pragma unroll 4
-        for (int k = g; k < K; k += SPLIT) acc = E::add(acc, p[(long long)k * stride]);
+        acc = ordered_batch_sum<T, MERGE_BATCH>(acc, g, K, SPLIT,
+                                                [&](int k) { return p + (long long)k * stride; });
     }
     part[g][lane] = acc;
     __syncthreads();
