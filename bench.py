@@ -159,7 +159,7 @@ def measure_gemv_detail(name, p, reps, read_peak=None, flush=None):
     t_call = call_ms(d, reps, flush)[0] * 1e-3
     bz = beta_is_zero(p)
     call_b = R.gemv_call_bytes(p.prec, p.m, p.n, p.trans, bz)
-    ci = X.gemv_config_info(p.prec, X.gemv_current_config(p.prec))
+    ci = X.gemv_config_info(p.prec, X.gemv_current_config(p.prec, p.trans, p.m, p.n))
     out = {"prec": p.prec, "trans": p.trans, "m": p.m, "n": p.n, "lda": p.lda,
            "kernel": (f"gemv_strip<{CTYPE[p.prec]}, {p.trans}, W={ci['waves']}, "
                       f"SW={ci['stripes_per_wave']}, G={ci['cols_per_group']}, "

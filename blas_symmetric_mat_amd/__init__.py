@@ -199,7 +199,7 @@ def library():
             lib.xgemv_select_config.restype = ci
             lib.xgemv_select_config.argtypes = [ci, ci]
             lib.xgemv_current_config.restype = ci
-            lib.xgemv_current_config.argtypes = [ci]
+            lib.xgemv_current_config.argtypes = [ci, ctypes.c_char, ci, ci]
             lib.xgemv_workspace_bytes.restype = ctypes.c_size_t
             lib.xgemv_workspace_bytes.argtypes = [ci, cc, ci, ci]
             lib.xgemv_plan.restype = ci
@@ -568,12 +568,15 @@ def gemv_config_info(prec: str, idx: int) -> dict:
 
 
 def gemv_select_config(prec: str, idx: int) -> None:
+    """Force configuration idx for every xGEMV call of `prec`; -1 restores
+    the built-in choice per transposition and size."""
     if library().xgemv_select_config(PREC_CODE[prec], idx) != 0:
         raise ValueError("bad gemv configuration selection")
 
 
-def gemv_current_config(prec: str) -> int:
-    return library().xgemv_current_config(PREC_CODE[prec])
+def gemv_current_config(prec: str, trans: str, m: int, n: int) -> int:
+    """The configuration an xGEMV call (prec, trans, m, n) runs."""
+    return library().xgemv_current_config(PREC_CODE[prec], trans.encode()[:1], m, n)
 
 
 def gemv_workspace_bytes(prec: str, trans: str, m: int, n: int) -> int:

@@ -357,7 +357,7 @@ int check_gemv_args(char trans, int m, int n, const void* A, int lda, const void
 }
 
 namespace {
-std::atomic<int> g_gemv_idx[5];
+std::atomic<int> g_gemv_idx[5] = {-1, -1, -1, -1, -1};
 std::atomic<int> g_syr2_idx[5];
 std::atomic<int> g_trmv_idx[5] = {-1, -1, -1, -1, -1};
 }
@@ -1380,14 +1380,24 @@ int xgemv_config_info(int prec, int idx, int* waves, int* stripes_per_wave, int*
 int xgemv_select_config(int prec, int idx)
 {
     if (prec < 0 || prec > 4 || idx < -1 || idx >= xgemv_num_configs(prec)) return -1;
-    g_gemv_idx[prec].store(idx < 0 ? 0 : idx);
+    g_gemv_idx[prec].store(idx);
     return 0;
 }
 
-int xgemv_current_config(int prec)
+int xgemv_current_config(int prec, char trans, int m, int n)
 {
-    if (prec < 0 || prec > 4) return -1;
-    return gemv_selected(prec);
+    int tr = 0;
+    // the argument checks of a call (transposition only; no data)
+    if (check_gemv_args(trans, 0, 0, nullptr, 1, nullptr, 1, nullptr, 1, &tr)) return -1;
+    if (m < 0 || n < 0) return -1;
+    switch (prec) {
+    case XSYMV_S: return gemv_pick<float>(tr, m, n);
+    case XSYMV_D: return gemv_pick<double>(tr, m, n);
+    case XSYMV_C: return gemv_pick<cf32>(tr, m, n);
+    case XSYMV_Z: return gemv_pick<cf64>(tr, m, n);
+    case XSYMV_W: return gemv_pick<ddreal>(tr, m, n);
+    default: return -1;
+    }
 }
 
 size_t xgemv_workspace_bytes(int prec, char trans, int m, int n)

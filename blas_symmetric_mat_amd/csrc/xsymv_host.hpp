@@ -446,7 +446,29 @@ GemvKernelSet<T> make_gemv()
 }
 
 template <class T> const std::vector<GemvKernelSet<T>>& gemv_kernel_sets();
-int gemv_selected(int prec);
+int gemv_selected(int prec);  // -1: the built-in choice
+
+// Built-in xGEMV choice per element type: [0 'N', 1 'T' or 'C'][size
+// class], the size class from the matrix's element count m*n: below
+// 12288^2, below 20000^2, then larger (the orders 8192, 16384 and 32768 --
+// 23170 for the 16-byte types -- fall one in each).
+struct GemvDefaults {
+    int idx[2][3];
+};
+template <class T> GemvDefaults gemv_defaults();
+
+inline int gemv_size_class(int m, int n)
+{
+    const long long e = (long long)m * n;
+    return e < 12288LL * 12288 ? 0 : e < 20000LL * 20000 ? 1 : 2;
+}
+
+template <class T>
+int gemv_pick(int tr, int m, int n)
+{
+    const int sel = gemv_selected(prec_code<T>());
+    return sel >= 0 ? sel : gemv_defaults<T>().idx[tr != 0 ? 1 : 0][gemv_size_class(m, n)];
+}
 
 int check_gemv_args(char trans, int m, int n, const void* A, int lda, const void* x, int incx,
                     const void* y, int incy, int* tr);
@@ -478,7 +500,7 @@ int gemv_run(char trans, int m, int n, T alpha, const T* A, int lda, const T* x,
         return 0;
     }
     const auto& sets = gemv_kernel_sets<T>();
-    const int idx = forced_idx >= 0 ? forced_idx : gemv_selected(prec_code<T>());
+    const int idx = forced_idx >= 0 ? forced_idx : gemv_pick<T>(tr, m, n);
     const GemvKernelSet<T>& ks = sets[idx];
     const int R = ks.R();
     const int threads = 64 * ks.W;
@@ -529,7 +551,7 @@ size_t gemv_ws_bytes(char trans, int m, int n)
 {
     const int tr = (trans == 'N' || trans == 'n') ? 0 : 1;
     if (m <= 0 || n <= 0) return 0;
-    const auto& ks = gemv_kernel_sets<T>()[gemv_selected(prec_code<T>())];
+    const auto& ks = gemv_kernel_sets<T>()[gemv_pick<T>(tr, m, n)];
     int G = 0;
     if (resident_blocks((const void*)ks.k[tr], 64 * ks.W, &G)) return (size_t)-1;
     std::vector<StripBlock> blocks;

@@ -34,9 +34,8 @@ int autotune_for<cf32>(char uplo, int n, int lda, int reps, hipStream_t stream, 
     return autotune_impl<cf32>(uplo, n, lda, reps, stream, best_idx, ms, max_cfg);
 }
 
-// xGEMV configurations (index 0 is the default -- the fastest for both
-// 'N' and 'T' at the largest size measured on MI355X; xgemv_select_config
-// chooses another)
+// xGEMV configurations (the built-in choice per transposition and size is
+// gemv_defaults below; xgemv_select_config forces one)
 template <> const std::vector<GemvKernelSet<cf32>>& gemv_kernel_sets<cf32>()
 {
     static const std::vector<GemvKernelSet<cf32>> v = {
@@ -45,6 +44,13 @@ template <> const std::vector<GemvKernelSet<cf32>>& gemv_kernel_sets<cf32>()
         make_gemv<cf32, 16, 2, 4, true>(),                 // R 4096, 32 KB runs, G 4
     };
     return v;
+}
+
+// built-in choice [0 'N', 1 'T' or 'C'][size class]: the fastest (two passes of
+// 20 flushed calls) at the orders 8192, 16384, 32768 on MI355X
+template <> GemvDefaults gemv_defaults<cf32>()
+{
+    return GemvDefaults{{{1, 2, 1}, {1, 0, 0}}};
 }
 
 // xSYR2 / xHER2 configurations (index 0 is the default; xsyr2_select_config

@@ -42,9 +42,8 @@ int autotune_for<double>(char uplo, int n, int lda, int reps, hipStream_t stream
     return autotune_impl<double>(uplo, n, lda, reps, stream, best_idx, ms, max_cfg);
 }
 
-// xGEMV configurations (index 0 is the default -- the fastest for both
-// 'N' and 'T' at the largest size measured on MI355X; xgemv_select_config
-// chooses another)
+// xGEMV configurations (the built-in choice per transposition and size is
+// gemv_defaults below; xgemv_select_config forces one)
 template <> const std::vector<GemvKernelSet<double>>& gemv_kernel_sets<double>()
 {
     static const std::vector<GemvKernelSet<double>> v = {
@@ -54,6 +53,13 @@ template <> const std::vector<GemvKernelSet<double>>& gemv_kernel_sets<double>()
         make_gemv<double, 8, 2, 8, true>(),                // R 2048, 16 KB runs, G 8
     };
     return v;
+}
+
+// built-in choice [0 'N', 1 'T'][size class]: the fastest (two passes of
+// 20 flushed calls) at the orders 8192, 16384, 32768 on MI355X
+template <> GemvDefaults gemv_defaults<double>()
+{
+    return GemvDefaults{{{2, 3, 2}, {0, 1, 2}}};
 }
 
 // xSYR2 / xHER2 configurations (index 0 is the default; xsyr2_select_config

@@ -41,9 +41,8 @@ int autotune_for<float>(char uplo, int n, int lda, int reps, hipStream_t stream,
     return autotune_impl<float>(uplo, n, lda, reps, stream, best_idx, ms, max_cfg);
 }
 
-// xGEMV configurations (index 0 is the default -- the fastest for both
-// 'N' and 'T' at the largest size measured on MI355X; xgemv_select_config
-// chooses another)
+// xGEMV configurations (the built-in choice per transposition and size is
+// gemv_defaults below; xgemv_select_config forces one)
 template <> const std::vector<GemvKernelSet<float>>& gemv_kernel_sets<float>()
 {
     static const std::vector<GemvKernelSet<float>> v = {
@@ -53,6 +52,13 @@ template <> const std::vector<GemvKernelSet<float>>& gemv_kernel_sets<float>()
         make_gemv<float, 8, 2, 8, true>(),                 // R 4096, 16 KB runs, G 8
     };
     return v;
+}
+
+// built-in choice [0 'N', 1 'T'][size class]: the fastest (two passes of
+// 20 flushed calls) at the orders 8192, 16384, 32768 on MI355X
+template <> GemvDefaults gemv_defaults<float>()
+{
+    return GemvDefaults{{{1, 1, 2}, {1, 1, 0}}};
 }
 
 // xSYR2 configurations (index 0 is the default -- the fastest, or level with

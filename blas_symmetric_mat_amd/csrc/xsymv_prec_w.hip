@@ -37,9 +37,8 @@ int autotune_for<ddreal>(char uplo, int n, int lda, int reps, hipStream_t stream
     return autotune_impl<ddreal>(uplo, n, lda, reps, stream, best_idx, ms, max_cfg);
 }
 
-// xGEMV configurations (index 0 is the default -- the fastest for both
-// 'N' and 'T' at the largest size measured on MI355X; xgemv_select_config
-// chooses another)
+// xGEMV configurations (the built-in choice per transposition and size is
+// gemv_defaults below; xgemv_select_config forces one)
 template <> const std::vector<GemvKernelSet<ddreal>>& gemv_kernel_sets<ddreal>()
 {
     static const std::vector<GemvKernelSet<ddreal>> v = {
@@ -48,6 +47,13 @@ template <> const std::vector<GemvKernelSet<ddreal>>& gemv_kernel_sets<ddreal>()
         make_gemv<ddreal, 16, 1, 4, true>(),               // R 1024, 16 KB runs, G 4
     };
     return v;
+}
+
+// built-in choice [0 'N', 1 'T'][size class]: the fastest (two passes of
+// 20 flushed calls) at the orders 8192, 16384, 23170 on MI355X
+template <> GemvDefaults gemv_defaults<ddreal>()
+{
+    return GemvDefaults{{{2, 2, 1}, {1, 1, 1}}};
 }
 
 // xSYR2 / xHER2 configurations (index 0 is the default; xsyr2_select_config

@@ -142,21 +142,25 @@ int xgemv_z(char trans, int m, int n, xcomplex128 alpha, const xcomplex128 *A, i
 int xgemv_w(char trans, int m, int n, xdd alpha, const xdd *A, int lda, const xdd *x,
             int incx, xdd beta, xdd *y, int incy, void *stream);
 
-/* xGEMV configurations: each precision has a compiled list (entry 0 the
- * default); info gives waves per workgroup, stripes per wave, columns per
- * group, non-temporal loads (0/1) and rows per strip (outputs may be NULL;
- * returns 0 or -1 for a bad index).  select installs entry idx (-1: entry 0)
- * for every later call of that precision (0 or -1); current returns it.
- * workspace_bytes: device workspace of one call on the current device with
- * the selected entry (-1 cast to size_t on a bad code or when the device
- * cannot be queried).  xgemv_plan: the work split for m x n, strips of R
+/* xGEMV configurations: each precision has a compiled list; info gives
+ * waves per workgroup, stripes per wave, columns per group, non-temporal
+ * loads (0/1) and rows per strip (outputs may be NULL; returns 0 or -1 for
+ * a bad index).  Built in: one configuration per (precision, 'N' or a
+ * transposition, size class of m*n: below 12288^2, below 20000^2, larger),
+ * the fastest measured on MI355X at one order in each class.  select forces
+ * entry idx for every later call of that precision; idx = -1 restores the
+ * built-in choice (0 or -1 for a bad code or index).  current: the
+ * configuration a call (prec, trans, m, n) runs (-1 for a bad code, trans,
+ * m or n).  workspace_bytes: device workspace of one call on the current
+ * device with that configuration (-1 cast to size_t on a bad code or when
+ * the device cannot be queried).  xgemv_plan: the work split for m x n, strips of R
  * rows and G workgroups (host computation; blocks4 as for xsymv_strip_plan,
  * seg_base[NS+1]); returns the number of workgroups, -1 or -2. */
 int xgemv_num_configs(int prec);
 int xgemv_config_info(int prec, int idx, int *waves, int *stripes_per_wave,
                       int *cols_per_group, int *nontemporal, int *rows_per_strip);
 int xgemv_select_config(int prec, int idx);
-int xgemv_current_config(int prec);
+int xgemv_current_config(int prec, char trans, int m, int n);
 size_t xgemv_workspace_bytes(int prec, char trans, int m, int n);
 int xgemv_plan(int m, int n, int R, int G, int *blocks4, int max_blocks, int *seg_base,
                int max_strips);

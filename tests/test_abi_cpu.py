@@ -280,13 +280,47 @@ def test_gemv_config_tables():
                 {"s": 4, "d": 2, "c": 2, "z": 1, "w": 1}[p]
         with pytest.raises(IndexError):
             X.gemv_config_info(p, k)
-        assert X.gemv_current_config(p) == 0
     X.gemv_select_config("d", 1)
-    assert X.gemv_current_config("d") == 1
+    for trans, m, n in (("N", 8, 8), ("T", 40000, 40000), ("C", 1, 1 << 20)):
+        assert X.gemv_current_config("d", trans, m, n) == 1
     X.gemv_select_config("d", -1)
-    assert X.gemv_current_config("d") == 0
+    assert X.gemv_current_config("d", "N", 16384, 16384) == 3
     with pytest.raises(ValueError):
         X.gemv_select_config("s", 99)
+
+
+# The built-in xGEMV choice [0 'N', 1 'T'/'C'][size class of m*n]
+GEMV_BUILTIN = {"s": ((1, 1, 2), (1, 1, 0)), "d": ((2, 3, 2), (0, 1, 2)),
+                "c": ((1, 2, 1), (1, 0, 0)), "z": ((2, 0, 1), (2, 1, 2)),
+                "w": ((2, 2, 1), (1, 1, 1))}
+
+
+def test_gemv_builtin_choice_by_transposition_and_size():
+    """Size classes by the element count m*n (below 12288^2, below 20000^2,
+    larger) and 'T' and 'C' sharing a column; every entry a valid index;
+    a forced index applies to every shape; bad arguments give -1."""
+    for p, tab in GEMV_BUILTIN.items():
+        k = X.gemv_num_configs(p)
+        X.gemv_select_config(p, -1)
+        for trans in "NTCntc":
+            row = tab[0 if trans in "Nn" else 1]
+            # class edges: 12288^2 - 1, 12288^2, 20000^2 - 1, 20000^2
+            for m, n, cls in ((0, 0, 0), (8192, 8192, 0), (1, 12288 * 12288 - 1, 0),
+                              (12288, 12288, 1), (3, 50331648, 1), (16384, 16384, 1),
+                              (19999, 20000, 1), (20000, 20000, 2), (32768, 32768, 2),
+                              (1, 1 << 30, 2)):
+                got = X.gemv_current_config(p, trans, m, n)
+                assert got == row[cls], (p, trans, m, n)
+                assert 0 <= got < k
+        X.gemv_select_config(p, k - 1)
+        assert X.gemv_current_config(p, "N", 8, 8) == k - 1
+        assert X.gemv_current_config(p, "T", 32768, 32768) == k - 1
+        X.gemv_select_config(p, -1)
+    lib = X.library()
+    assert lib.xgemv_current_config(0, b"X", 8, 8) == -1
+    assert lib.xgemv_current_config(0, b"N", -1, 8) == -1
+    assert lib.xgemv_current_config(0, b"N", 8, -1) == -1
+    assert lib.xgemv_current_config(7, b"N", 8, 8) == -1
 
 
 @pytest.mark.parametrize("m,n,R,G", [(1, 1, 64, 5), (100, 7, 64, 3), (1000, 77, 256, 37),
