@@ -245,7 +245,7 @@ def measure_trmv_detail(name, p, reps, read_peak=None, flush=None):
     t_call = call_ms(d, reps, fresh)[0] * 1e-3
     unit = p.diag in ("U", "u")
     b = R.trmv_call_bytes(p.prec, p.n, unit)
-    idx = X.trmv_current_config(p.prec, p.uplo, p.trans)
+    idx = X.trmv_current_config(p.prec, p.uplo, p.trans, p.n)
     ci = X.trmv_config_info(p.prec, idx)
     out = {"prec": p.prec, "uplo": p.uplo, "trans": p.trans, "diag": p.diag, "n": p.n,
            "lda": p.lda,

@@ -143,7 +143,7 @@ def library():
             lib.xtrmv_select_config.restype = ci
             lib.xtrmv_select_config.argtypes = [ci, ci]
             lib.xtrmv_current_config.restype = ci
-            lib.xtrmv_current_config.argtypes = [ci, cc, cc]
+            lib.xtrmv_current_config.argtypes = [ci, cc, cc, ci]
             lib.xtrmv_workspace_bytes.restype = ctypes.c_size_t
             lib.xtrmv_workspace_bytes.argtypes = [ci, cc, cc, ci]
             lib.xsymv_workspace_bytes.restype = ctypes.c_size_t
@@ -515,9 +515,9 @@ def trmv_select_config(prec: str, idx: int) -> None:
         raise ValueError("bad trmv configuration selection")
 
 
-def trmv_current_config(prec: str, uplo: str = "L", trans: str = "N") -> int:
-    """The configuration a call (prec, uplo, trans) would use now."""
-    v = library().xtrmv_current_config(PREC_CODE[prec], _ch(uplo), _ch(trans))
+def trmv_current_config(prec: str, uplo: str, trans: str, n: int) -> int:
+    """The configuration a call (prec, uplo, trans, n) would use now."""
+    v = library().xtrmv_current_config(PREC_CODE[prec], _ch(uplo), _ch(trans), n)
     if v < 0:
         raise ValueError("bad trmv configuration query")
     return v

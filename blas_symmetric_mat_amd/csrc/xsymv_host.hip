@@ -1531,19 +1531,20 @@ int xtrmv_select_config(int prec, int idx)
     return 0;
 }
 
-int xtrmv_current_config(int prec, char uplo, char trans)
+int xtrmv_current_config(int prec, char uplo, char trans, int n)
 {
     bool upper = false, unit = false;
     int tr = 0;
     // the argument checks of a call with n = 0
     if (check_trmv_args(uplo, trans, 'N', 0, nullptr, 1, nullptr, 1, &upper, &tr, &unit))
         return -1;
+    if (n < 0) return -1;
     switch (prec) {
-    case XSYMV_S: return trmv_pick<float>(upper, tr);
-    case XSYMV_D: return trmv_pick<double>(upper, tr);
-    case XSYMV_C: return trmv_pick<cf32>(upper, tr);
-    case XSYMV_Z: return trmv_pick<cf64>(upper, tr);
-    case XSYMV_W: return trmv_pick<ddreal>(upper, tr);
+    case XSYMV_S: return trmv_pick<float>(upper, tr, n);
+    case XSYMV_D: return trmv_pick<double>(upper, tr, n);
+    case XSYMV_C: return trmv_pick<cf32>(upper, tr, n);
+    case XSYMV_Z: return trmv_pick<cf64>(upper, tr, n);
+    case XSYMV_W: return trmv_pick<ddreal>(upper, tr, n);
     default: return -1;
     }
 }

@@ -673,17 +673,22 @@ TrmvKernelSet<T> make_trmv()
 }
 
 template <class T> const std::vector<TrmvKernelSet<T>>& trmv_kernel_sets();
+// Built-in xTRMV choice per element type: [upper][0 'N', 1 'T' or 'C'][size
+// class of n: below 12288, below 20000, then larger].
 struct TrmvDefaults {
-    int idx[2][2];  // [upper][op = T or T^H]
+    int idx[2][2][3];
 };
 template <class T> TrmvDefaults trmv_defaults();
 int trmv_selected(int prec);  // -1: the built-in choice
 
+inline int trmv_size_class(int n) { return n < 12288 ? 0 : n < 20000 ? 1 : 2; }
+
 template <class T>
-int trmv_pick(bool upper, int tr)
+int trmv_pick(bool upper, int tr, int n)
 {
     const int sel = trmv_selected(prec_code<T>());
-    return sel >= 0 ? sel : trmv_defaults<T>().idx[upper ? 1 : 0][tr != 0 ? 1 : 0];
+    return sel >= 0 ? sel
+                    : trmv_defaults<T>().idx[upper ? 1 : 0][tr != 0 ? 1 : 0][trmv_size_class(n)];
 }
 int check_trmv_args(char uplo, char trans, char diag, int n, const void* A, int lda,
                     const void* x, int incx, bool* upper, int* tr, bool* unit);
@@ -705,7 +710,7 @@ int trmv_run(char uplo, char trans, char diag, int n, const T* A, int lda, T* x,
     int rc = check_trmv_args(uplo, trans, diag, n, A, lda, x, incx, &upper, &tr, &unit);
     if (rc) return rc;
     if (n == 0) return 0;
-    const auto& ks = trmv_kernel_sets<T>()[forced_idx >= 0 ? forced_idx : trmv_pick<T>(upper, tr)];
+    const auto& ks = trmv_kernel_sets<T>()[forced_idx >= 0 ? forced_idx : trmv_pick<T>(upper, tr, n)];
     const int R = ks.R();
     const int threads = 64 * ks.W;
     auto kern = ks.k[upper ? 1 : 0][tr][unit ? 1 : 0];
@@ -755,7 +760,7 @@ size_t trmv_ws_bytes(char uplo, char trans, int n)
     const bool upper = uplo == 'U' || uplo == 'u';
     const int tr = (trans == 'N' || trans == 'n') ? 0 : 1;
     if (n <= 0) return 0;
-    const auto& ks = trmv_kernel_sets<T>()[trmv_pick<T>(upper, tr)];
+    const auto& ks = trmv_kernel_sets<T>()[trmv_pick<T>(upper, tr, n)];
     size_t most = 0;
     for (int unit = 0; unit < 2; ++unit) {  // the larger of the two diagonal kinds
         int G = 0;

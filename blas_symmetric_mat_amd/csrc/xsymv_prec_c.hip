@@ -66,7 +66,7 @@ template <> const std::vector<Syr2KernelSet<cf32>>& syr2_kernel_sets<cf32>()
 }
 
 // xTRMV configurations (xtrmv_select_config forces one; otherwise
-// trmv_defaults picks per triangle and transposition)
+// trmv_defaults picks per triangle, transposition and size)
 template <> const std::vector<TrmvKernelSet<cf32>>& trmv_kernel_sets<cf32>()
 {
     static const std::vector<TrmvKernelSet<cf32>> v = {
@@ -79,9 +79,13 @@ template <> const std::vector<TrmvKernelSet<cf32>>& trmv_kernel_sets<cf32>()
     return v;
 }
 
-// built-in choice [upper][op = T or T^H]: the fastest (median of 20 calls)
-// at n = 16384 on MI355X
-template <> TrmvDefaults trmv_defaults<cf32>() { return TrmvDefaults{{{0, 0}, {3, 3}}}; }
+// built-in choice [upper][0 'N', 1 'T' or 'C'][size class]: the fastest (two
+// passes of 20 flushed calls; 'T' and 'C' by their summed time) at the
+// orders 8192, 16384 and 32768 on MI355X
+template <> TrmvDefaults trmv_defaults<cf32>()
+{
+    return TrmvDefaults{{{{1, 1, 1}, {1, 0, 1}}, {{1, 3, 3}, {1, 3, 0}}}};
+}
 
 // One shard's product: the row-strip shape that the built-in rules pick for
 // the largest orders (R 2048, G 8, split by stored rows)

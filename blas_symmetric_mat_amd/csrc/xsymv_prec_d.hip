@@ -76,7 +76,7 @@ template <> const std::vector<Syr2KernelSet<double>>& syr2_kernel_sets<double>()
 }
 
 // xTRMV configurations (xtrmv_select_config forces one; otherwise
-// trmv_defaults picks per triangle and transposition)
+// trmv_defaults picks per triangle, transposition and size)
 template <> const std::vector<TrmvKernelSet<double>>& trmv_kernel_sets<double>()
 {
     static const std::vector<TrmvKernelSet<double>> v = {
@@ -90,9 +90,13 @@ template <> const std::vector<TrmvKernelSet<double>>& trmv_kernel_sets<double>()
     return v;
 }
 
-// built-in choice [upper][op = T or T^H]: the fastest (median of 20 calls)
-// at n = 32768 on MI355X
-template <> TrmvDefaults trmv_defaults<double>() { return TrmvDefaults{{{4, 3}, {3, 3}}}; }
+// built-in choice [upper][0 'N', 1 'T'][size class]: the fastest (two
+// passes of 20 flushed calls; 'T' and 'C' by their summed time) at the
+// orders 8192, 16384 and 32768 on MI355X
+template <> TrmvDefaults trmv_defaults<double>()
+{
+    return TrmvDefaults{{{{0, 1, 5}, {1, 0, 1}}, {{1, 1, 0}, {0, 0, 3}}}};
+}
 
 // One shard's product (537 MB at n = 32768 with 8 shards): R 2048, G 8,
 // split by strip height alone -- the fastest of five shapes measured on the

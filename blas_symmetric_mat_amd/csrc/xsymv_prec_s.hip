@@ -78,7 +78,7 @@ template <> const std::vector<Syr2KernelSet<float>>& syr2_kernel_sets<float>()
 }
 
 // xTRMV configurations (xtrmv_select_config forces one; otherwise
-// trmv_defaults picks per triangle and transposition)
+// trmv_defaults picks per triangle, transposition and size)
 template <> const std::vector<TrmvKernelSet<float>>& trmv_kernel_sets<float>()
 {
     static const std::vector<TrmvKernelSet<float>> v = {
@@ -92,9 +92,13 @@ template <> const std::vector<TrmvKernelSet<float>>& trmv_kernel_sets<float>()
     return v;
 }
 
-// built-in choice [upper][op = T or T^H]: the fastest (median of 20 calls)
-// at n = 32768 on MI355X
-template <> TrmvDefaults trmv_defaults<float>() { return TrmvDefaults{{{0, 3}, {0, 2}}}; }
+// built-in choice [upper][0 'N', 1 'T'][size class]: the fastest (two
+// passes of 20 flushed calls; 'T' and 'C' by their summed time) at the
+// orders 8192, 16384 and 32768 on MI355X
+template <> TrmvDefaults trmv_defaults<float>()
+{
+    return TrmvDefaults{{{{0, 0, 0}, {2, 3, 3}}, {{0, 0, 0}, {4, 4, 1}}}};
+}
 
 // One shard's product (268 MB at n = 32768 with 8 shards): R 4096, G 16,
 // split by strip height alone -- the fastest of five shapes measured on the

@@ -69,7 +69,7 @@ template <> const std::vector<Syr2KernelSet<ddreal>>& syr2_kernel_sets<ddreal>()
 }
 
 // xTRMV configurations (xtrmv_select_config forces one; otherwise
-// trmv_defaults picks per triangle and transposition)
+// trmv_defaults picks per triangle, transposition and size)
 template <> const std::vector<TrmvKernelSet<ddreal>>& trmv_kernel_sets<ddreal>()
 {
     static const std::vector<TrmvKernelSet<ddreal>> v = {
@@ -82,9 +82,13 @@ template <> const std::vector<TrmvKernelSet<ddreal>>& trmv_kernel_sets<ddreal>()
     return v;
 }
 
-// built-in choice [upper][op = T or T^H]: the fastest (median of 20 calls)
-// at n = 16384 on MI355X
-template <> TrmvDefaults trmv_defaults<ddreal>() { return TrmvDefaults{{{4, 2}, {4, 2}}}; }
+// built-in choice [upper][0 'N', 1 'T'][size class]: the fastest (two
+// passes of 20 flushed calls; 'T' and 'C' by their summed time) at the
+// orders 8192, 16384 and 23170 on MI355X
+template <> TrmvDefaults trmv_defaults<ddreal>()
+{
+    return TrmvDefaults{{{{4, 4, 4}, {2, 2, 4}}, {{4, 4, 4}, {1, 1, 1}}}};
+}
 
 // One shard's product: the row-strip shape that the built-in rules pick for
 // the largest orders (R 1024, G 4, split by strip height)

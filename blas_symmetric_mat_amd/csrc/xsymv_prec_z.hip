@@ -67,7 +67,7 @@ template <> const std::vector<Syr2KernelSet<cf64>>& syr2_kernel_sets<cf64>()
 }
 
 // xTRMV configurations (xtrmv_select_config forces one; otherwise
-// trmv_defaults picks per triangle and transposition)
+// trmv_defaults picks per triangle, transposition and size)
 template <> const std::vector<TrmvKernelSet<cf64>>& trmv_kernel_sets<cf64>()
 {
     static const std::vector<TrmvKernelSet<cf64>> v = {
@@ -80,9 +80,13 @@ template <> const std::vector<TrmvKernelSet<cf64>>& trmv_kernel_sets<cf64>()
     return v;
 }
 
-// built-in choice [upper][op = T or T^H]: the fastest (median of 20 calls)
-// at n = 16384 on MI355X
-template <> TrmvDefaults trmv_defaults<cf64>() { return TrmvDefaults{{{4, 4}, {4, 3}}}; }
+// built-in choice [upper][0 'N', 1 'T' or 'C'][size class]: the fastest (two
+// passes of 20 flushed calls; 'T' and 'C' by their summed time) at the
+// orders 8192, 16384 and 23170 on MI355X
+template <> TrmvDefaults trmv_defaults<cf64>()
+{
+    return TrmvDefaults{{{{4, 4, 0}, {4, 4, 0}}, {{4, 4, 1}, {1, 3, 1}}}};
+}
 
 // One shard's product: the row-strip shape that the built-in rules pick for
 // the largest orders (R 2048, G 4, split by stored rows)

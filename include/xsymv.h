@@ -311,11 +311,12 @@ int xtrmv_w(char uplo, char trans, char diag, int n, const xdd *A, int lda, xdd 
 
 /* Triangular product configurations, same fields as the rank-2 update's.
  * Built in: one configuration per (precision, triangle, 'N' or a
- * transposition), the fastest measured on MI355X at the largest size.
+ * transposition, size class of n: below 12288, below 20000, larger), the
+ * fastest measured on MI355X at one order in each class.
  * xtrmv_select_config(prec, idx) forces configuration idx for every call of
  * that precision; idx = -1 restores the built-in choice (0, or -1 for a bad
  * code or index).  xtrmv_current_config: the configuration a call (prec,
- * uplo, trans) would use now (-1 for a bad code).  xtrmv_workspace_bytes:
+ * uplo, trans, n) would use now (-1 for a bad code, uplo, trans or n).  xtrmv_workspace_bytes:
  * device workspace bytes of one call (precision, uplo, trans, n) with that
  * configuration on the current device (0 for n <= 0; -1 cast to size_t on a
  * bad precision code or when the device cannot be queried). */
@@ -324,7 +325,7 @@ int xtrmv_config_info(int prec, int idx, int *waves, int *stripes_per_wave,
                       int *cols_per_group, int *nontemporal, int *split,
                       int *rows_per_strip);
 int xtrmv_select_config(int prec, int idx);
-int xtrmv_current_config(int prec, char uplo, char trans);
+int xtrmv_current_config(int prec, char uplo, char trans, int n);
 size_t xtrmv_workspace_bytes(int prec, char uplo, char trans, int n);
 
 /* Bytes of device workspace one call of precision `prec` and order n uses

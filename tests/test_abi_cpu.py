@@ -417,22 +417,49 @@ def test_trmv_config_tables():
                 {"s": 4, "d": 2, "c": 2, "z": 1, "w": 1}[p]
         for uplo in "LU":
             for trans in "NTC":
-                assert 0 <= X.trmv_current_config(p, uplo, trans) < k
+                for n in (0, 1000, 16384, 32768):
+                    assert 0 <= X.trmv_current_config(p, uplo, trans, n) < k
             # 'T' and 'C' share the built-in choice
-            assert X.trmv_current_config(p, uplo, "T") == X.trmv_current_config(p, uplo, "C")
-    before = {(u, t): X.trmv_current_config("d", u, t) for u in "LU" for t in "NT"}
+            for n in (1000, 16384, 32768):
+                assert X.trmv_current_config(p, uplo, "T", n) == \
+                    X.trmv_current_config(p, uplo, "C", n)
+    keys = [(u, t, n) for u in "LU" for t in "NT" for n in (8192, 16384, 32768)]
+    before = {key: X.trmv_current_config("d", *key) for key in keys}
     X.trmv_select_config("d", 2)
-    assert all(X.trmv_current_config("d", u, t) == 2 for u in "LU" for t in "NTC")
+    assert all(X.trmv_current_config("d", *key) == 2 for key in keys)
     X.trmv_select_config("d", -1)
-    assert before == {(u, t): X.trmv_current_config("d", u, t) for u in "LU" for t in "NT"}
+    assert before == {key: X.trmv_current_config("d", *key) for key in keys}
     with pytest.raises(ValueError):
         X.trmv_select_config("d", 99)
     with pytest.raises(IndexError):
         X.trmv_config_info("d", 99)
     with pytest.raises(ValueError):
-        X.trmv_current_config("d", "Q", "N")
+        X.trmv_current_config("d", "Q", "N", 8)
     with pytest.raises(ValueError):
-        X.trmv_current_config("d", "L", "Q")
+        X.trmv_current_config("d", "L", "Q", 8)
+    with pytest.raises(ValueError):
+        X.trmv_current_config("d", "L", "N", -1)
+
+
+# The built-in xTRMV choice [upper][0 'N', 1 'T'/'C'][size class of n]
+TRMV_BUILTIN = {"s": (((0, 0, 0), (2, 3, 3)), ((0, 0, 0), (4, 4, 1))),
+                "d": (((0, 1, 5), (1, 0, 1)), ((1, 1, 0), (0, 0, 3))),
+                "c": (((1, 1, 1), (1, 0, 1)), ((1, 3, 3), (1, 3, 0))),
+                "z": (((4, 4, 0), (4, 4, 0)), ((4, 4, 1), (1, 3, 1))),
+                "w": (((4, 4, 4), (2, 2, 4)), ((4, 4, 4), (1, 1, 1)))}
+
+
+def test_trmv_builtin_choice_by_triangle_transposition_and_size():
+    """Size classes by n (below 12288, below 20000, larger), their edges,
+    and 'T' and 'C' sharing a column."""
+    for p, tab in TRMV_BUILTIN.items():
+        X.trmv_select_config(p, -1)
+        for ui, uplo in enumerate("LU"):
+            for trans in "NTC":
+                row = tab[ui][0 if trans == "N" else 1]
+                for n, cls in ((0, 0), (1, 0), (8192, 0), (12287, 0), (12288, 1), (19999, 1),
+                               (20000, 2), (32768, 2), (46341, 2)):
+                    assert X.trmv_current_config(p, uplo, trans, n) == row[cls], (p, uplo, trans, n)
 
 
 @pytest.mark.parametrize("n,panel,nshards", [(0, 1, 1), (1, 1, 1), (10, 2, 3), (37, 4, 3),

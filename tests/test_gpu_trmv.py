@@ -24,9 +24,12 @@ def _gpu():
     G.torch_dev()
 
 
-def strip_rows(prec, uplo="L", trans="N"):
+def strip_rows(prec, uplo="L", trans="N", n=8192):
+    """Rows per strip of the configuration a call at order n runs (the
+    built-in choice depends on n's size class: 8192 stands for orders below
+    12288)."""
     import blas_symmetric_mat_amd as X
-    return X.trmv_config_info(prec, X.trmv_current_config(prec, uplo, trans))["rows_per_strip"]
+    return X.trmv_config_info(prec, X.trmv_current_config(prec, uplo, trans, n))["rows_per_strip"]
 
 
 def check(p, label):
@@ -53,7 +56,10 @@ def test_trmv_parity(prec, uplo, trans, diag, n, pad):
 @pytest.mark.parametrize("extra", [1, 357])
 def test_trmv_several_strips(prec, uplo, trans, extra):
     """Two full strips and a ragged third (one row, or a few hundred)."""
+    import blas_symmetric_mat_amd as X
     n = 2 * strip_rows(prec, uplo, trans) + extra
+    # the same configuration at this order as at the one queried
+    assert X.trmv_current_config(prec, uplo, trans, n) == X.trmv_current_config(prec, uplo, trans, 8192)
     G.log(f"trmv strips {prec} {uplo}{trans} n={n}")
     p = TM.problem(prec, uplo, trans, "N", n, 3, seed=4100 + extra)
     check(p, f"{prec}{uplo}{trans} n={n}")
