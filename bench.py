@@ -200,7 +200,7 @@ def measure_syr2_detail(name, p, reps, read_peak=None, flush=None):
         d.call()
     t_call = call_ms(d, reps, flush)[0] * 1e-3
     b = R.syr2_call_bytes(p.prec, p.n)
-    ci = X.syr2_config_info(p.prec, X.syr2_current_config(p.prec))
+    ci = X.syr2_config_info(p.prec, X.syr2_current_config(p.prec, p.uplo, p.n))
     out = {"prec": p.prec, "uplo": p.uplo, "n": p.n, "lda": p.lda,
            "kernel": (f"syr2_strip<{CTYPE[p.prec]}, {'upper' if p.uplo == 'U' else 'lower'}, "
                       f"W={ci['waves']}, SW={ci['stripes_per_wave']}, G={ci['cols_per_group']}, "

@@ -191,7 +191,7 @@ def library():
             lib.xsyr2_select_config.restype = ci
             lib.xsyr2_select_config.argtypes = [ci, ci]
             lib.xsyr2_current_config.restype = ci
-            lib.xsyr2_current_config.argtypes = [ci]
+            lib.xsyr2_current_config.argtypes = [ci, cc, ci]
             lib.xgemv_num_configs.restype = ci
             lib.xgemv_num_configs.argtypes = [ci]
             lib.xgemv_config_info.restype = ci
@@ -546,12 +546,18 @@ def syr2_config_info(prec: str, idx: int) -> dict:
 
 
 def syr2_select_config(prec: str, idx: int) -> None:
+    """Force configuration idx for every rank-2 update of `prec`; -1 restores
+    the built-in choice per triangle and size."""
     if library().xsyr2_select_config(PREC_CODE[prec], idx) != 0:
         raise ValueError("bad syr2 configuration selection")
 
 
-def syr2_current_config(prec: str) -> int:
-    return library().xsyr2_current_config(PREC_CODE[prec])
+def syr2_current_config(prec: str, uplo: str, n: int) -> int:
+    """The configuration a rank-2 update (prec, uplo, n) runs."""
+    v = library().xsyr2_current_config(PREC_CODE[prec], _ch(uplo), n)
+    if v < 0:
+        raise ValueError("bad syr2 configuration query")
+    return v
 
 
 def gemv_num_configs(prec: str) -> int:

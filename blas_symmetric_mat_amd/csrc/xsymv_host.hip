@@ -358,7 +358,7 @@ int check_gemv_args(char trans, int m, int n, const void* A, int lda, const void
 
 namespace {
 std::atomic<int> g_gemv_idx[5] = {-1, -1, -1, -1, -1};
-std::atomic<int> g_syr2_idx[5];
+std::atomic<int> g_syr2_idx[5] = {-1, -1, -1, -1, -1};
 std::atomic<int> g_trmv_idx[5] = {-1, -1, -1, -1, -1};
 }
 
@@ -1474,14 +1474,26 @@ int xsyr2_config_info(int prec, int idx, int* waves, int* stripes_per_wave, int*
 int xsyr2_select_config(int prec, int idx)
 {
     if (prec < 0 || prec > 4 || idx < -1 || idx >= xsyr2_num_configs(prec)) return -1;
-    g_syr2_idx[prec].store(idx < 0 ? 0 : idx);
+    g_syr2_idx[prec].store(idx);
     return 0;
 }
 
-int xsyr2_current_config(int prec)
+int xsyr2_current_config(int prec, char uplo, int n)
 {
-    if (prec < 0 || prec > 4) return -1;
-    return syr2_selected(prec);
+    bool upper = false;
+    if (uplo == 'U' || uplo == 'u')
+        upper = true;
+    else if (uplo != 'L' && uplo != 'l')
+        return -1;
+    if (n < 0) return -1;
+    switch (prec) {
+    case XSYMV_S: return syr2_pick<float>(upper, n);
+    case XSYMV_D: return syr2_pick<double>(upper, n);
+    case XSYMV_C: return syr2_pick<cf32>(upper, n);
+    case XSYMV_Z: return syr2_pick<cf64>(upper, n);
+    case XSYMV_W: return syr2_pick<ddreal>(upper, n);
+    default: return -1;
+    }
 }
 
 int xtrmv_num_configs(int prec)

@@ -579,7 +579,22 @@ Syr2KernelSet<T> make_syr2()
 }
 
 template <class T> const std::vector<Syr2KernelSet<T>>& syr2_kernel_sets();
-int syr2_selected(int prec);
+int syr2_selected(int prec);  // -1: the built-in choice
+
+// Built-in xSYR2 / xHER2 choice per element type: [upper][size class of n,
+// as for xTRMV: below 12288, below 20000, then larger].
+struct Syr2Defaults {
+    int idx[2][3];
+};
+template <class T> Syr2Defaults syr2_defaults();
+
+template <class T>
+int syr2_pick(bool upper, int n)
+{
+    const int sel = syr2_selected(prec_code<T>());
+    return sel >= 0 ? sel
+                    : syr2_defaults<T>().idx[upper ? 1 : 0][n < 12288 ? 0 : n < 20000 ? 1 : 2];
+}
 int check_syr2_args(char uplo, int n, const void* x, int incx, const void* y, int incy,
                     const void* A, int lda, bool* upper);
 
@@ -592,7 +607,7 @@ int syr2_run(char uplo, int n, T alpha, const T* x, int incx, const T* y, int in
     if (rc) return rc;
     if (n == 0 || host_is_zero(alpha)) return 0;
     const auto& ks = syr2_kernel_sets<T>()[forced_idx >= 0 ? forced_idx
-                                                              : syr2_selected(prec_code<T>())];
+                                                              : syr2_pick<T>(upper, n)];
     const int R = ks.R();
     const int threads = 64 * ks.W;
     auto kern = ks.k[upper ? 1 : 0];

@@ -53,8 +53,8 @@ template <> GemvDefaults gemv_defaults<cf32>()
     return GemvDefaults{{{1, 2, 1}, {1, 0, 0}}};
 }
 
-// xSYR2 / xHER2 configurations (index 0 is the default; xsyr2_select_config
-// chooses another)
+// xSYR2 / xHER2 configurations (the built-in choice per triangle and size is
+// syr2_defaults below; xsyr2_select_config forces one)
 template <> const std::vector<Syr2KernelSet<cf32>>& syr2_kernel_sets<cf32>()
 {
     static const std::vector<Syr2KernelSet<cf32>> v = {
@@ -64,6 +64,10 @@ template <> const std::vector<Syr2KernelSet<cf32>>& syr2_kernel_sets<cf32>()
     };
     return v;
 }
+
+// built-in choice [upper][size class]: the fastest (two passes of 20 flushed
+// calls) at the orders 8192, 16384 and 32768 on MI355X
+template <> Syr2Defaults syr2_defaults<cf32>() { return Syr2Defaults{{{2, 0, 0}, {0, 0, 1}}}; }
 
 // xTRMV configurations (xtrmv_select_config forces one; otherwise
 // trmv_defaults picks per triangle, transposition and size)

@@ -62,8 +62,8 @@ template <> GemvDefaults gemv_defaults<double>()
     return GemvDefaults{{{2, 3, 2}, {0, 1, 2}}};
 }
 
-// xSYR2 / xHER2 configurations (index 0 is the default; xsyr2_select_config
-// chooses another)
+// xSYR2 / xHER2 configurations (the built-in choice per triangle and size is
+// syr2_defaults below; xsyr2_select_config forces one)
 template <> const std::vector<Syr2KernelSet<double>>& syr2_kernel_sets<double>()
 {
     static const std::vector<Syr2KernelSet<double>> v = {
@@ -74,6 +74,10 @@ template <> const std::vector<Syr2KernelSet<double>>& syr2_kernel_sets<double>()
     };
     return v;
 }
+
+// built-in choice [upper][size class]: the fastest (two passes of 20 flushed
+// calls) at the orders 8192, 16384 and 32768 on MI355X
+template <> Syr2Defaults syr2_defaults<double>() { return Syr2Defaults{{{0, 0, 0}, {1, 1, 2}}}; }
 
 // xTRMV configurations (xtrmv_select_config forces one; otherwise
 // trmv_defaults picks per triangle, transposition and size)

@@ -61,9 +61,8 @@ template <> GemvDefaults gemv_defaults<float>()
     return GemvDefaults{{{1, 1, 2}, {1, 1, 0}}};
 }
 
-// xSYR2 configurations (index 0 is the default -- the fastest, or level with
-// the fastest, of ten shapes for both triangles at n = 32768 on MI355X;
-// xsyr2_select_config chooses another)
+// xSYR2 / xHER2 configurations (the built-in choice per triangle and size is
+// syr2_defaults below; xsyr2_select_config forces one)
 template <> const std::vector<Syr2KernelSet<float>>& syr2_kernel_sets<float>()
 {
     static const std::vector<Syr2KernelSet<float>> v = {
@@ -76,6 +75,10 @@ template <> const std::vector<Syr2KernelSet<float>>& syr2_kernel_sets<float>()
     };
     return v;
 }
+
+// built-in choice [upper][size class]: the fastest (two passes of 20 flushed
+// calls) at the orders 8192, 16384 and 32768 on MI355X
+template <> Syr2Defaults syr2_defaults<float>() { return Syr2Defaults{{{2, 5, 5}, {0, 0, 0}}}; }
 
 // xTRMV configurations (xtrmv_select_config forces one; otherwise
 // trmv_defaults picks per triangle, transposition and size)

@@ -197,17 +197,22 @@ int xher2_z(char uplo, int n, xcomplex128 alpha, const xcomplex128 *x, int incx,
 int xsyr2_w(char uplo, int n, xdd alpha, const xdd *x, int incx, const xdd *y, int incy,
             xdd *A, int lda, void *stream);
 
-/* Rank-2 update configurations (entry 0 the default): waves per workgroup,
- * stripes per wave, columns per group, non-temporal access (0/1), work split
- * (the cost models of xsymv_strip_plan: 0 strip height, doubled in the
- * diagonal triangle; 1 stored rows plus strip height; 2 strip height alone)
- * and rows per strip.  Same conventions as the xGEMV configuration calls. */
+/* Rank-2 update configurations: waves per workgroup, stripes per wave,
+ * columns per group, non-temporal access (0/1), work split (the cost models
+ * of xsymv_strip_plan: 0 strip height, doubled in the diagonal triangle; 1
+ * stored rows plus strip height; 2 strip height alone) and rows per strip.
+ * Built in: one configuration per (precision, triangle, size class of n:
+ * below 12288, below 20000, larger), the fastest measured on MI355X at one
+ * order in each class.  select forces entry idx for every later call of
+ * that precision; idx = -1 restores the built-in choice (0 or -1 for a bad
+ * code or index).  current: the configuration a call (prec, uplo, n) runs
+ * (-1 for a bad code, uplo or n). */
 int xsyr2_num_configs(int prec);
 int xsyr2_config_info(int prec, int idx, int *waves, int *stripes_per_wave,
                       int *cols_per_group, int *nontemporal, int *split,
                       int *rows_per_strip);
 int xsyr2_select_config(int prec, int idx);
-int xsyr2_current_config(int prec);
+int xsyr2_current_config(int prec, char uplo, int n);
 
 /* One GPU's share of the product, for the path sharded over several GPUs
  * (the report's §5 points to multi-GPU SYMV, its ref. [7]); on one GPU the

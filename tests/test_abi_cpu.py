@@ -383,12 +383,35 @@ def test_syr2_config_tables():
         for i in range(k):
             ci = X.syr2_config_info(p, i)
             assert ci["split"] in (0, 1, 2)
-        assert X.syr2_current_config(p) == 0
+        for uplo in "LUlu":
+            for n in (0, 1000, 16384, 32768):
+                assert 0 <= X.syr2_current_config(p, uplo, n) < k
     X.syr2_select_config("s", 1)
-    assert X.syr2_current_config("s") == 1
+    assert all(X.syr2_current_config("s", u, n) == 1 for u in "LU" for n in (8, 40000))
     X.syr2_select_config("s", -1)
+    assert X.syr2_current_config("s", "L", 8192) == 2
     with pytest.raises(ValueError):
         X.syr2_select_config("s", 99)
+    with pytest.raises(ValueError):
+        X.syr2_current_config("s", "Q", 8)
+    with pytest.raises(ValueError):
+        X.syr2_current_config("s", "L", -1)
+
+
+# The built-in rank-2 choice [upper][size class of n]
+SYR2_BUILTIN = {"s": ((2, 5, 5), (0, 0, 0)), "d": ((0, 0, 0), (1, 1, 2)),
+                "c": ((2, 0, 0), (0, 0, 1)), "z": ((0, 0, 1), (1, 1, 1)),
+                "w": ((0, 0, 1), (0, 1, 1))}
+
+
+def test_syr2_builtin_choice_by_triangle_and_size():
+    """Size classes by n (below 12288, below 20000, larger) and their edges."""
+    for p, tab in SYR2_BUILTIN.items():
+        X.syr2_select_config(p, -1)
+        for ui, uplo in enumerate("LU"):
+            for n, cls in ((0, 0), (8192, 0), (12287, 0), (12288, 1), (19999, 1), (20000, 2),
+                           (32768, 2)):
+                assert X.syr2_current_config(p, uplo, n) == tab[ui][cls], (p, uplo, n)
 
 
 @pytest.mark.parametrize("prec", ["s", "d", "c", "z", "w"])
