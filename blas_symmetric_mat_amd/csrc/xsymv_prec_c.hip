@@ -46,11 +46,12 @@ template <> const std::vector<GemvKernelSet<cf32>>& gemv_kernel_sets<cf32>()
     return v;
 }
 
-// built-in choice [0 'N', 1 'T' or 'C'][size class]: the fastest (two passes of
-// 20 flushed calls) at the orders 8192, 16384, 32768 on MI355X
+// built-in choice [0 'N', 1 'T' or 'C'][size class]: the fastest (four passes
+// of 20 flushed calls, tuned/mi355x_level2.json) at the orders 8192, 16384,
+// 32768 on MI355X
 template <> GemvDefaults gemv_defaults<cf32>()
 {
-    return GemvDefaults{{{1, 2, 1}, {1, 0, 0}}};
+    return GemvDefaults{{{1, 0, 1}, {1, 0, 1}}};
 }
 
 // xSYR2 / xHER2 configurations (the built-in choice per triangle and size is
@@ -65,8 +66,9 @@ template <> const std::vector<Syr2KernelSet<cf32>>& syr2_kernel_sets<cf32>()
     return v;
 }
 
-// built-in choice [upper][size class]: the fastest (two passes of 20 flushed
-// calls) at the orders 8192, 16384 and 32768 on MI355X
+// built-in choice [upper][size class]: the fastest (four passes of 20 flushed
+// calls, tuned/mi355x_level2.json) at the orders 8192, 16384 and 32768 on
+// MI355X
 template <> Syr2Defaults syr2_defaults<cf32>() { return Syr2Defaults{{{2, 0, 0}, {0, 0, 1}}}; }
 
 // xTRMV configurations (xtrmv_select_config forces one; otherwise
@@ -83,12 +85,12 @@ template <> const std::vector<TrmvKernelSet<cf32>>& trmv_kernel_sets<cf32>()
     return v;
 }
 
-// built-in choice [upper][0 'N', 1 'T' or 'C'][size class]: the fastest (two
-// passes of 20 flushed calls; 'T' and 'C' by their summed time) at the
-// orders 8192, 16384 and 32768 on MI355X
+// built-in choice [upper][0 'N', 1 'T' or 'C'][size class]: the fastest (four
+// passes of 20 flushed calls, tuned/mi355x_level2.json; 'T' and 'C' by their
+// summed time) at the orders 8192, 16384 and 32768 on MI355X
 template <> TrmvDefaults trmv_defaults<cf32>()
 {
-    return TrmvDefaults{{{{1, 1, 1}, {1, 0, 1}}, {{1, 3, 3}, {1, 3, 0}}}};
+    return TrmvDefaults{{{{1, 1, 1}, {1, 0, 3}}, {{3, 3, 3}, {1, 3, 3}}}};
 }
 
 // One shard's product: the row-strip shape that the built-in rules pick for

@@ -55,11 +55,12 @@ template <> const std::vector<GemvKernelSet<double>>& gemv_kernel_sets<double>()
     return v;
 }
 
-// built-in choice [0 'N', 1 'T'][size class]: the fastest (two passes of
-// 20 flushed calls) at the orders 8192, 16384, 32768 on MI355X
+// built-in choice [0 'N', 1 'T'][size class]: the fastest (four passes of 20
+// flushed calls, tuned/mi355x_level2.json) at the orders 8192, 16384, 32768 on
+// MI355X
 template <> GemvDefaults gemv_defaults<double>()
 {
-    return GemvDefaults{{{2, 3, 2}, {0, 1, 2}}};
+    return GemvDefaults{{{2, 3, 2}, {0, 3, 2}}};
 }
 
 // xSYR2 / xHER2 configurations (the built-in choice per triangle and size is
@@ -75,9 +76,10 @@ template <> const std::vector<Syr2KernelSet<double>>& syr2_kernel_sets<double>()
     return v;
 }
 
-// built-in choice [upper][size class]: the fastest (two passes of 20 flushed
-// calls) at the orders 8192, 16384 and 32768 on MI355X
-template <> Syr2Defaults syr2_defaults<double>() { return Syr2Defaults{{{0, 0, 0}, {1, 1, 2}}}; }
+// built-in choice [upper][size class]: the fastest (four passes of 20 flushed
+// calls, tuned/mi355x_level2.json) at the orders 8192, 16384 and 32768 on
+// MI355X
+template <> Syr2Defaults syr2_defaults<double>() { return Syr2Defaults{{{0, 0, 0}, {0, 1, 2}}}; }
 
 // xTRMV configurations (xtrmv_select_config forces one; otherwise
 // trmv_defaults picks per triangle, transposition and size)
@@ -94,12 +96,12 @@ template <> const std::vector<TrmvKernelSet<double>>& trmv_kernel_sets<double>()
     return v;
 }
 
-// built-in choice [upper][0 'N', 1 'T'][size class]: the fastest (two
-// passes of 20 flushed calls; 'T' and 'C' by their summed time) at the
-// orders 8192, 16384 and 32768 on MI355X
+// built-in choice [upper][0 'N', 1 'T'][size class]: the fastest (four passes
+// of 20 flushed calls, tuned/mi355x_level2.json; 'T' and 'C' by their summed
+// time) at the orders 8192, 16384 and 32768 on MI355X
 template <> TrmvDefaults trmv_defaults<double>()
 {
-    return TrmvDefaults{{{{0, 1, 5}, {1, 0, 1}}, {{1, 1, 0}, {0, 0, 3}}}};
+    return TrmvDefaults{{{{0, 1, 0}, {1, 1, 3}}, {{0, 1, 0}, {5, 3, 3}}}};
 }
 
 // One shard's product (537 MB at n = 32768 with 8 shards): R 2048, G 8,

@@ -54,8 +54,9 @@ template <> const std::vector<GemvKernelSet<float>>& gemv_kernel_sets<float>()
     return v;
 }
 
-// built-in choice [0 'N', 1 'T'][size class]: the fastest (two passes of
-// 20 flushed calls) at the orders 8192, 16384, 32768 on MI355X
+// built-in choice [0 'N', 1 'T'][size class]: the fastest (four passes of 20
+// flushed calls, tuned/mi355x_level2.json) at the orders 8192, 16384, 32768 on
+// MI355X
 template <> GemvDefaults gemv_defaults<float>()
 {
     return GemvDefaults{{{1, 1, 2}, {1, 1, 0}}};
@@ -76,9 +77,10 @@ template <> const std::vector<Syr2KernelSet<float>>& syr2_kernel_sets<float>()
     return v;
 }
 
-// built-in choice [upper][size class]: the fastest (two passes of 20 flushed
-// calls) at the orders 8192, 16384 and 32768 on MI355X
-template <> Syr2Defaults syr2_defaults<float>() { return Syr2Defaults{{{2, 5, 5}, {0, 0, 0}}}; }
+// built-in choice [upper][size class]: the fastest (four passes of 20 flushed
+// calls, tuned/mi355x_level2.json) at the orders 8192, 16384 and 32768 on
+// MI355X
+template <> Syr2Defaults syr2_defaults<float>() { return Syr2Defaults{{{5, 5, 5}, {0, 0, 0}}}; }
 
 // xTRMV configurations (xtrmv_select_config forces one; otherwise
 // trmv_defaults picks per triangle, transposition and size)
@@ -95,12 +97,12 @@ template <> const std::vector<TrmvKernelSet<float>>& trmv_kernel_sets<float>()
     return v;
 }
 
-// built-in choice [upper][0 'N', 1 'T'][size class]: the fastest (two
-// passes of 20 flushed calls; 'T' and 'C' by their summed time) at the
-// orders 8192, 16384 and 32768 on MI355X
+// built-in choice [upper][0 'N', 1 'T'][size class]: the fastest (four passes
+// of 20 flushed calls, tuned/mi355x_level2.json; 'T' and 'C' by their summed
+// time) at the orders 8192, 16384 and 32768 on MI355X
 template <> TrmvDefaults trmv_defaults<float>()
 {
-    return TrmvDefaults{{{{0, 0, 0}, {2, 3, 3}}, {{0, 0, 0}, {4, 4, 1}}}};
+    return TrmvDefaults{{{{0, 0, 0}, {2, 3, 3}}, {{0, 0, 0}, {4, 4, 5}}}};
 }
 
 // One shard's product (268 MB at n = 32768 with 8 shards): R 4096, G 16,

@@ -47,11 +47,12 @@ template <> const std::vector<GemvKernelSet<cf64>>& gemv_kernel_sets<cf64>()
     return v;
 }
 
-// built-in choice [0 'N', 1 'T' or 'C'][size class]: the fastest (two passes of
-// 20 flushed calls) at the orders 8192, 16384, 23170 on MI355X
+// built-in choice [0 'N', 1 'T' or 'C'][size class]: the fastest (four passes
+// of 20 flushed calls, tuned/mi355x_level2.json) at the orders 8192, 16384,
+// 23170 on MI355X
 template <> GemvDefaults gemv_defaults<cf64>()
 {
-    return GemvDefaults{{{2, 0, 1}, {2, 1, 2}}};
+    return GemvDefaults{{{2, 0, 2}, {2, 0, 2}}};
 }
 
 // xSYR2 / xHER2 configurations (the built-in choice per triangle and size is
@@ -66,9 +67,10 @@ template <> const std::vector<Syr2KernelSet<cf64>>& syr2_kernel_sets<cf64>()
     return v;
 }
 
-// built-in choice [upper][size class]: the fastest (two passes of 20 flushed
-// calls) at the orders 8192, 16384 and 23170 on MI355X
-template <> Syr2Defaults syr2_defaults<cf64>() { return Syr2Defaults{{{0, 0, 1}, {1, 1, 1}}}; }
+// built-in choice [upper][size class]: the fastest (four passes of 20 flushed
+// calls, tuned/mi355x_level2.json) at the orders 8192, 16384 and 23170 on
+// MI355X
+template <> Syr2Defaults syr2_defaults<cf64>() { return Syr2Defaults{{{0, 0, 1}, {0, 1, 1}}}; }
 
 // xTRMV configurations (xtrmv_select_config forces one; otherwise
 // trmv_defaults picks per triangle, transposition and size)
@@ -84,12 +86,12 @@ template <> const std::vector<TrmvKernelSet<cf64>>& trmv_kernel_sets<cf64>()
     return v;
 }
 
-// built-in choice [upper][0 'N', 1 'T' or 'C'][size class]: the fastest (two
-// passes of 20 flushed calls; 'T' and 'C' by their summed time) at the
-// orders 8192, 16384 and 23170 on MI355X
+// built-in choice [upper][0 'N', 1 'T' or 'C'][size class]: the fastest (four
+// passes of 20 flushed calls, tuned/mi355x_level2.json; 'T' and 'C' by their
+// summed time) at the orders 8192, 16384 and 23170 on MI355X
 template <> TrmvDefaults trmv_defaults<cf64>()
 {
-    return TrmvDefaults{{{{4, 4, 0}, {4, 4, 0}}, {{4, 4, 1}, {1, 3, 1}}}};
+    return TrmvDefaults{{{{4, 4, 0}, {4, 4, 0}}, {{0, 4, 1}, {1, 3, 1}}}};
 }
 
 // One shard's product: the row-strip shape that the built-in rules pick for

@@ -284,15 +284,22 @@ def test_gemv_config_tables():
     for trans, m, n in (("N", 8, 8), ("T", 40000, 40000), ("C", 1, 1 << 20)):
         assert X.gemv_current_config("d", trans, m, n) == 1
     X.gemv_select_config("d", -1)
-    assert X.gemv_current_config("d", "N", 16384, 16384) == 3
+    assert X.gemv_current_config("d", "N", 16384, 16384) == _level2_tables()["gemv"]["d"][0][1]
     with pytest.raises(ValueError):
         X.gemv_select_config("s", 99)
 
 
+def _level2_tables():
+    """The built-in tables of xGEMV, xTRMV and the rank-2 update, as the
+    committed measurement record gives them (tune_level2 emit)."""
+    import json
+    from blas_symmetric_mat_amd import tune_level2
+    path = os.path.join(os.path.dirname(X.__file__), "tuned", "mi355x_level2.json")
+    return tune_level2.tables_from_record(json.load(open(path)))
+
+
 # The built-in xGEMV choice [0 'N', 1 'T'/'C'][size class of m*n]
-GEMV_BUILTIN = {"s": ((1, 1, 2), (1, 1, 0)), "d": ((2, 3, 2), (0, 1, 2)),
-                "c": ((1, 2, 1), (1, 0, 0)), "z": ((2, 0, 1), (2, 1, 2)),
-                "w": ((2, 2, 1), (1, 1, 1))}
+GEMV_BUILTIN = _level2_tables()["gemv"]
 
 
 def test_gemv_builtin_choice_by_transposition_and_size():
@@ -389,7 +396,7 @@ def test_syr2_config_tables():
     X.syr2_select_config("s", 1)
     assert all(X.syr2_current_config("s", u, n) == 1 for u in "LU" for n in (8, 40000))
     X.syr2_select_config("s", -1)
-    assert X.syr2_current_config("s", "L", 8192) == 2
+    assert X.syr2_current_config("s", "L", 8192) == _level2_tables()["syr2"]["s"][0][0]
     with pytest.raises(ValueError):
         X.syr2_select_config("s", 99)
     with pytest.raises(ValueError):
@@ -399,9 +406,7 @@ def test_syr2_config_tables():
 
 
 # The built-in rank-2 choice [upper][size class of n]
-SYR2_BUILTIN = {"s": ((2, 5, 5), (0, 0, 0)), "d": ((0, 0, 0), (1, 1, 2)),
-                "c": ((2, 0, 0), (0, 0, 1)), "z": ((0, 0, 1), (1, 1, 1)),
-                "w": ((0, 0, 1), (0, 1, 1))}
+SYR2_BUILTIN = _level2_tables()["syr2"]
 
 
 def test_syr2_builtin_choice_by_triangle_and_size():
@@ -465,11 +470,7 @@ def test_trmv_config_tables():
 
 
 # The built-in xTRMV choice [upper][0 'N', 1 'T'/'C'][size class of n]
-TRMV_BUILTIN = {"s": (((0, 0, 0), (2, 3, 3)), ((0, 0, 0), (4, 4, 1))),
-                "d": (((0, 1, 5), (1, 0, 1)), ((1, 1, 0), (0, 0, 3))),
-                "c": (((1, 1, 1), (1, 0, 1)), ((1, 3, 3), (1, 3, 0))),
-                "z": (((4, 4, 0), (4, 4, 0)), ((4, 4, 1), (1, 3, 1))),
-                "w": (((4, 4, 4), (2, 2, 4)), ((4, 4, 4), (1, 1, 1)))}
+TRMV_BUILTIN = _level2_tables()["trmv"]
 
 
 def test_trmv_builtin_choice_by_triangle_transposition_and_size():
