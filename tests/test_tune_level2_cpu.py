@@ -65,3 +65,26 @@ def test_emit_prints_initialisers(tmp_path, capsys):
     assert "template <> Syr2Defaults syr2_defaults<ddreal>() " \
            "{ return Syr2Defaults{{{0, 0, 1}, {0, 1, 1}}}; }" in out
     assert "orders 8192, 16384, 23170" in out
+
+
+def test_committed_record_matches_the_compiled_lists():
+    """The record behind the built-in tables covers every product, precision,
+    variant and order, with one time per compiled configuration of that
+    precision, in every pass: a configuration added to or removed from a
+    list makes this fail until the record is measured again."""
+    import os
+    import blas_symmetric_mat_amd as X
+    path = os.path.join(os.path.dirname(X.__file__), "tuned", "mi355x_level2.json")
+    rec = json.load(open(path))
+    count = {"gemv": X.gemv_num_configs, "trmv": X.trmv_num_configs, "syr2": X.syr2_num_configs}
+    assert rec["passes"] >= 2 and rec["reps"] >= 10
+    for op in T.OPS:
+        for prec in "sdczw":
+            times = rec["times"][op][prec]
+            assert sorted(times) == sorted(T.variants(op, prec)), (op, prec)
+            for var, by_order in times.items():
+                assert sorted(by_order, key=int) == [str(n) for n in T.ORDERS[prec]]
+                for passes in by_order.values():
+                    assert len(passes) == rec["passes"]
+                    assert all(len(row) == count[op](prec) for row in passes), (op, prec, var)
+                    assert all(t > 0 for row in passes for t in row)
